@@ -1,0 +1,41 @@
+"""CPU oracle for one Hy3 MoE layer forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls, links or
+executes this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, headers, tables
+or helpers with the HIP path (``sparse_moe_layer_wave_amd/``) and imports
+nothing from it.
+
+What it computes is the plain definition of the layer, in NumPy float64 except
+where the pages fix a precision (the router's scores are fp32, the FP8 variant
+quantises to OCP e4m3):
+
+* router: logits = x . W_gate^T (fp32 weights), sigmoid scores, top-k with ties
+  to the lower expert index, the k scores divided by their sum and multiplied by
+  router_scaling_factor -- "Tencent Hy3-295B architecture teardown", section 4.1
+  (router flow steps 1, 3, 4, 5) and "Tencent Hy3-Flash Q&A", Q4.2;
+* expert: SwiGLU with the fused gate_up projection, SiLU on the gate half --
+  "Tencent Hy3-295B architecture teardown", section 2.3 (parameter breakdown)
+  and "DeepSeek V4-Flash architecture Q&A", Q4.5;
+* combine: per-expert loop adding weight * expert output into the token's row
+  -- "DeepSeek V4-Flash architecture Q&A", Q8.4 (the MoE forward sketch and
+  the index_add_ note), done in float64 so the fp32-combine requirement
+  (wmrh.cn Hy3 assembly blog, section 2.3) is met with margin.
+
+Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
+invariants, library routines and brute force.  Parity unpinned: the value 2.826
+itself, and anything that would need the real model's weights.
+"""
+
+from .codecs import (bf16_bits_to_f64, f32_to_bf16_bits, e4m3_bits_to_f64,
+                     f32_to_e4m3_bits, E4M3_MAX)
+from .moe import (route, expert_swiglu, forward, forward_tokens, quant_row_e4m3,
+                  quant_rows_e4m3, forward_fp8, forward_fp8_tokens,
+                  expert_param_count, flops_per_token, NEAR_TIE)
+
+__all__ = [
+    "bf16_bits_to_f64", "f32_to_bf16_bits", "e4m3_bits_to_f64", "f32_to_e4m3_bits",
+    "E4M3_MAX", "route", "expert_swiglu", "forward", "forward_tokens",
+    "quant_row_e4m3", "quant_rows_e4m3", "forward_fp8", "forward_fp8_tokens",
+    "expert_param_count", "flops_per_token", "NEAR_TIE",
+]

@@ -1,0 +1,214 @@
+"""The Hy3 MoE layer forward pass, written out as its plain definition.
+
+Test infrastructure only (see the package docstring).  Float64 throughout
+except where the pages fix a precision:
+
+* The router's scores are float32.  The Hy3 router casts hidden states and the
+  gate weight to float before the linear map and the sigmoid ("Tencent
+  Hy3-295B architecture teardown", section 4.1; "Tencent Hy3-Flash Q&A", Q6.2).
+  The oracle computes the logit in float64 (closer to the exact value than any
+  float32 summation order), applies the sigmoid in float64 and rounds the score
+  once to float32.  Selection compares those float32 scores.
+* The FP8 variant quantises activations to e4m3 with one float32 scale per row
+  ("DeepSeek V4-Flash architecture Q&A", Q7.2 for the format, Q7.4 for
+  per-channel scales), computing the scale and the scaled values in float32.
+"""
+
+from collections import namedtuple
+
+import numpy as np
+
+from .codecs import bf16_bits_to_f64, e4m3_bits_to_f64, f32_to_e4m3_bits, E4M3_MAX
+
+# Tokens whose k-th and (k+1)-th float32 scores differ by less than this are
+# flagged: a float32 GPU router may legitimately pick either expert there.
+NEAR_TIE = 1e-6
+
+Route = namedtuple("Route", "idx w scores near_tie order_tie gap")
+
+
+def _sigmoid64(z):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def route(x_bits, W_gate, k, scale, logit_bias=None, block=4096):
+    """Sigmoid top-k router ("Tencent Hy3-295B architecture teardown", section
+    4.1, router flow steps 1, 3, 4 and 5; "Tencent Hy3-Flash Q&A", Q4.2).
+
+    x_bits      uint16 [T, d]  bf16 hidden states
+    W_gate      float32 [E, d] router weight
+    k, scale    experts per token, router_scaling_factor (use float32(2.826))
+    logit_bias  float32 [E] or None: added to each logit before the sigmoid
+                (the gate linear map's per-expert bias term)
+
+    Returns Route(idx int64 [T,k], w float64 [T,k], scores float32 [T,E],
+    near_tie bool [T], order_tie bool [T], gap float64 [T]).
+
+    * scores = float32(sigmoid(x . W_gate^T + b)), logits summed in float64;
+    * idx[t] = the first k experts when all E are ordered by score descending,
+      equal scores by ascending expert index (slot j holds the j-th);
+    * w[t, j] = scale * s[idx_j] / sum_j s[idx_j]  (float64);
+    * near_tie: k < E and s_(k) - s_(k+1) < NEAR_TIE (the chosen set may differ
+      on a float32 GPU router); order_tie: some adjacent pair among the first
+      k+1 ranked scores is that close (the slot order may differ).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    W = np.asarray(W_gate, dtype=np.float32).astype(np.float64)
+    T = x_bits.shape[0]
+    E = W.shape[0]
+    if not (1 <= k <= E):
+        raise ValueError("need 1 <= k <= E")
+    b = None if logit_bias is None else np.asarray(logit_bias, dtype=np.float32).astype(np.float64)
+    scores = np.empty((T, E), dtype=np.float32)
+    for t0 in range(0, T, block):
+        xb = bf16_bits_to_f64(x_bits[t0:t0 + block])
+        logits = xb @ W.T
+        if b is not None:
+            logits = logits + b
+        scores[t0:t0 + block] = _sigmoid64(logits).astype(np.float32)
+    # stable sort on the negated score: equal scores keep ascending expert order
+    order = np.argsort(-scores, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int64)
+    ranked = np.take_along_axis(scores, order[:, :min(k + 1, E)], axis=1).astype(np.float64)
+    sel = ranked[:, :k]
+    w = np.float64(np.float32(scale)) * sel / sel.sum(axis=1, keepdims=True) if T else sel.copy()
+    if k < E:
+        gap = ranked[:, k - 1] - ranked[:, k]
+    else:
+        gap = np.full(T, np.inf)
+    near_tie = gap < NEAR_TIE
+    adj = ranked[:, :-1] - ranked[:, 1:] if ranked.shape[1] > 1 else np.zeros((T, 0))
+    order_tie = near_tie | (np.any(adj < NEAR_TIE, axis=1) if adj.shape[1] else np.zeros(T, bool))
+    return Route(idx, w, scores, near_tie, order_tie, gap)
+
+
+def expert_swiglu(x, W_gu, W_dn):
+    """One SwiGLU expert on rows x [n, d] (float64).
+
+    W_gu [2F, d]: rows [0, F) are the gate projection, rows [F, 2F) the up
+    projection (the fused gate_up_proj of "Tencent Hy3-295B architecture
+    teardown", section 2.3).  W_dn [d, F] is down_proj.  No bias.
+    a = SiLU(x W_gate^T) * (x W_up^T), y = a W_dn^T ("DeepSeek V4-Flash
+    architecture Q&A", Q4.5)."""
+    F = W_dn.shape[1]
+    g = x @ W_gu[:F].T
+    u = x @ W_gu[F:].T
+    a = g * _sigmoid64(g) * u
+    return a @ W_dn.T
+
+
+def forward(x_bits, W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias=None):
+    """Routed MoE output with bf16 experts, float64 combine.
+
+    x_bits uint16 [T,d]; W_gate float32 [E,d]; W_gu_bits uint16 [E,2F,d];
+    W_dn_bits uint16 [E,d,F].  Returns (out float64 [T,d], Route).
+
+    The combine is the per-expert loop of "DeepSeek V4-Flash architecture Q&A",
+    Q8.4: for each expert, run it on the tokens that chose it and add
+    weight * output into those tokens' rows.  The shared expert and the
+    residual are not part of this output."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, d = x_bits.shape
+    r = route(x_bits, W_gate, k, scale, logit_bias)
+    out = np.zeros((T, d), dtype=np.float64)
+    if T == 0:
+        return out, r
+    x = bf16_bits_to_f64(x_bits)
+    for e in np.unique(r.idx):
+        t, j = np.nonzero(r.idx == e)          # a token picks an expert at most once
+        y = expert_swiglu(x[t], bf16_bits_to_f64(W_gu_bits[e]), bf16_bits_to_f64(W_dn_bits[e]))
+        out[t] += r.w[t, j][:, None] * y
+    return out, r
+
+
+def forward_tokens(tokens, x_bits, W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias=None):
+    """Output rows of ``forward`` for the listed tokens only.  Tokens are
+    independent through the whole layer, so this is forward() on those rows."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    return forward(np.asarray(x_bits)[tokens], W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias)
+
+
+# ----------------------------------------------------------------------------- FP8
+
+def quant_row_e4m3(v):
+    """Per-row e4m3 quantisation of a float32 vector.
+
+    amax = max |v|.  amax = 0 gives codes 0 and scale 1.  Otherwise
+    r = float32(448 / amax), codes = e4m3(float32(v * r)) (nearest, ties to
+    even, saturating) and scale s = float32(amax / 448); the dequantised row is
+    codes * s.  Returns (uint8 codes, float32 scale)."""
+    v = np.asarray(v, dtype=np.float32)
+    amax = np.max(np.abs(v)) if v.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(v.shape, dtype=np.uint8), np.float32(1.0)
+    r = np.float32(E4M3_MAX) / np.float32(amax)
+    q = f32_to_e4m3_bits(v * r)
+    return q, np.float32(amax) / np.float32(E4M3_MAX)
+
+
+def quant_rows_e4m3(M):
+    """quant_row_e4m3 applied to every row of a float32 matrix."""
+    M = np.asarray(M, dtype=np.float32)
+    q = np.empty(M.shape, dtype=np.uint8)
+    s = np.empty(M.shape[0], dtype=np.float32)
+    for i in range(M.shape[0]):
+        q[i], s[i] = quant_row_e4m3(M[i])
+    return q, s
+
+
+def forward_fp8(x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale, logit_bias=None):
+    """Routed MoE output with e4m3 experts.
+
+    Wq_gu uint8 [E,2F,d] with float32 per-output-row scales s_gu [E,2F];
+    Wq_dn uint8 [E,d,F] with s_dn [E,d].  Routing is the float32 router of
+    ``route``.  Each token's bf16 row is quantised with quant_row_e4m3 before
+    the gate_up product; each (token, slot) SwiGLU activation row, rounded to
+    float32, is quantised the same way before the down product.  Products use
+    the dequantised operands in float64; the combine is as in ``forward``."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, d = x_bits.shape
+    r = route(x_bits, W_gate, k, scale, logit_bias)
+    out = np.zeros((T, d), dtype=np.float64)
+    if T == 0:
+        return out, r
+    qx, sx = quant_rows_e4m3(bf16_bits_to_f64(x_bits).astype(np.float32))
+    xd = e4m3_bits_to_f64(qx) * sx.astype(np.float64)[:, None]
+    F = Wq_dn.shape[2]
+    for e in np.unique(r.idx):
+        t, j = np.nonzero(r.idx == e)
+        Wgu = e4m3_bits_to_f64(Wq_gu[e]) * np.asarray(s_gu[e], np.float64)[:, None]
+        Wdn = e4m3_bits_to_f64(Wq_dn[e]) * np.asarray(s_dn[e], np.float64)[:, None]
+        g = xd[t] @ Wgu[:F].T
+        u = xd[t] @ Wgu[F:].T
+        a = g * _sigmoid64(g) * u
+        qa, sa = quant_rows_e4m3(a.astype(np.float32))
+        ad = e4m3_bits_to_f64(qa) * sa.astype(np.float64)[:, None]
+        out[t] += r.w[t, j][:, None] * (ad @ Wdn.T)
+    return out, r
+
+
+def forward_fp8_tokens(tokens, x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale, logit_bias=None):
+    """Output rows of ``forward_fp8`` for the listed tokens only."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    return forward_fp8(np.asarray(x_bits)[tokens], W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale,
+                       logit_bias)
+
+
+# ----------------------------------------------------------------------------- accounting
+
+def expert_param_count(d, d_ff):
+    """Parameters of one routed expert: the fused gate_up matrix [2*d_ff, d]
+    plus the down matrix [d, d_ff] (no bias)."""
+    gate_up = (2 * d_ff) * d
+    down = d * d_ff
+    return gate_up + down
+
+
+def flops_per_token(d, d_ff, k, E):
+    """Useful FLOPs per token of the routed layer: for each of the k experts a
+    [1,d]x[d,2F] and a [1,F]x[F,d] product (2 FLOPs per multiply-add), plus
+    the [1,d]x[d,E] router product.  The sigmoid, SiLU and combine are not
+    counted."""
+    per_expert = 2 * (d * 2 * d_ff) + 2 * (d_ff * d)
+    return k * per_expert + 2 * d * E
