@@ -1,0 +1,146 @@
+/*
+ * hy3moe.h -- C ABI of the Hy3 MoE layer forward pass on MI355X (gfx950).
+ *
+ * The layer (one MoE FFN block of Hy3, routed experts only):
+ *   router   logits = x . W_gate^T (+ per-expert logit bias), computed in fp32;
+ *            s = sigmoid(logits); the k experts with the largest s are chosen
+ *            (equal scores: lower expert index first; slot j = j-th largest);
+ *            w_j = scale * s_j / sum_j s_j
+ *            ["Tencent Hy3-295B architecture teardown", section 4.1, router
+ *             flow steps 1, 3, 4, 5; "Tencent Hy3-Flash Q&A", Q4.2 and Q6.2]
+ *   experts  SwiGLU: h = SiLU(x . Wg^T) * (x . Wu^T), y = h . Wd^T, where the
+ *            fused gate_up matrix holds Wg in rows [0, d_ff) and Wu in rows
+ *            [d_ff, 2 d_ff)  ["Tencent Hy3-295B architecture teardown",
+ *             section 2.3; "DeepSeek V4-Flash architecture Q&A", Q4.5]
+ *   combine  out[t] = sum_j w_j * y_{t,j}, accumulated in fp32 in slot order
+ *            ["DeepSeek V4-Flash architecture Q&A", Q8.4; wmrh.cn Hy3 assembly
+ *             blog, section 2.3 (enable_moe_fp32_combine)]
+ *
+ * Conventions for every call:
+ *   - Every pointer argument is DEVICE memory owned by the caller, except the
+ *     size_t* out-parameter of hy3moe_workspace_size (host).  The library never
+ *     allocates, frees or synchronises; it keeps no state between calls apart
+ *     from a thread-local copy of the last HIP error.
+ *   - Layouts are dense and row-major.  bf16 = uint16_t bit patterns;
+ *     e4m3 = uint8_t codes of the OCP E4M3FN format (bias 7, max 448, no inf).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on it; results are ready once the stream has
+ *     reached that point.  Device faults surface at the caller's next sync.
+ *   - Arguments are checked on the host before anything is enqueued; a
+ *     negative status means nothing was enqueued.  T == 0 is a successful
+ *     no-op.  Supported shapes: 1 <= k <= min(E, 16), 1 <= E <= 1024,
+ *     d and d_ff multiples of 64, T <= 2^24.
+ *     Every pointer must be 16-byte aligned.
+ *   - The workspace is scratch device memory of at least the size that
+ *     hy3moe_workspace_size reports; its contents on entry do not matter and
+ *     are undefined on return.  Calls that share a workspace must not overlap.
+ */
+#ifndef HY3MOE_H
+#define HY3MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HY3MOE_OK = 0,
+    HY3MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+    HY3MOE_ERR_SHAPE = -2,       /* T < 0, k < 1, k > E, or a non-positive size */
+    HY3MOE_ERR_UNSUPPORTED = -3, /* outside the supported shapes listed above, or unknown dtype */
+    HY3MOE_ERR_WORKSPACE = -4,   /* workspace smaller than required */
+    HY3MOE_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+    HY3MOE_ERR_HIP = -6          /* a HIP launch failed; see hy3moe_last_hip_error() */
+} hy3moe_status;
+
+enum { HY3MOE_WEIGHTS_BF16 = 0, HY3MOE_WEIGHTS_FP8_E4M3 = 1 };
+
+/* Bytes of workspace hy3moe_forward (weight_dtype BF16) or hy3moe_forward_fp8
+ * (FP8_E4M3) needs for these sizes; it also covers hy3moe_route and
+ * hy3moe_permute.  Writes *bytes (host pointer).  Grows monotonically with T. */
+int hy3moe_workspace_size(int T, int d, int E, int k, int d_ff, int weight_dtype, size_t* bytes);
+
+/* Router alone ("Tencent Hy3-295B architecture teardown", section 4.1).
+ *   x          bf16 [T, d]
+ *   W_gate     fp32 [E, d]
+ *   logit_bias fp32 [E], added to every token's logits before the sigmoid, or NULL
+ *   scale      router_scaling_factor (Hy3: 2.826)
+ *   topk_idx   int32 [T, k] out: chosen experts, slot order = descending score,
+ *              equal scores by ascending expert index
+ *   topk_w     fp32 [T, k] out: scale * s_j / sum of the k chosen scores
+ * The logits are fp32 sums of exact products (x is bf16, W_gate is split into
+ * three bf16 parts that add up to it exactly); the scores are fp32. */
+int hy3moe_route(const uint16_t* x, const float* W_gate, const float* logit_bias,
+                 int T, int d, int E, int k, float scale,
+                 int32_t* topk_idx, float* topk_w,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Dispatch order alone: a stable counting sort of the T*k (token, slot) pairs by
+ * expert, i.e. expert-contiguous rows, ascending token inside an expert (the
+ * grouping the per-expert loop of "DeepSeek V4-Flash architecture Q&A", Q8.4,
+ * performs, laid out for grouped GEMMs).
+ *   topk_idx  int32 [T, k] in (every entry in [0, E); a token lists an expert at most once)
+ *   counts    int32 [E] out: pairs per expert
+ *   offsets   int32 [E+1] out: exclusive prefix sum of counts (offsets[E] = T*k)
+ *   row_of    int32 [T, k] out: row of pair (t, j) in expert-contiguous order
+ *   token_of  int32 [T*k] out: token of each row
+ * Entries outside [0, E) are not detected and give undefined results. */
+int hy3moe_permute(const int32_t* topk_idx, int T, int E, int k,
+                   int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* token_of,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole layer with bf16 experts.
+ *   x          bf16 [T, d];  W_gate fp32 [E, d]
+ *   W_gate_up  bf16 [E, 2*d_ff, d] (rows [0,d_ff) gate, [d_ff,2*d_ff) up)
+ *   W_down     bf16 [E, d, d_ff]
+ *   out        fp32 [T, d] out, overwritten (not accumulated): the routed
+ *              experts' weighted sum; shared expert and residual are not added
+ *   logit_bias fp32 [E] or NULL (as in hy3moe_route)
+ *   topk_idx, topk_w  NULL, or [T, k] outputs receiving the routing
+ * Expert products run on bf16 MFMA with fp32 accumulation; SiLU(gate)*up is
+ * computed in fp32 and stored as bf16; each expert output row is stored as
+ * bf16 and the combine accumulates in fp32 in slot order (deterministic). */
+int hy3moe_forward(const uint16_t* x, const float* W_gate,
+                   const uint16_t* W_gate_up, const uint16_t* W_down, float* out,
+                   int T, int d, int E, int k, int d_ff, float scale, void* stream,
+                   const float* logit_bias, int32_t* topk_idx, float* topk_w,
+                   void* workspace, size_t workspace_bytes);
+
+/* The whole layer with e4m3 experts and per-output-channel fp32 scales
+ * (formats: "DeepSeek V4-Flash architecture Q&A", Q7.2 and Q7.4).
+ *   Wq_gate_up e4m3 [E, 2*d_ff, d], s_gate_up fp32 [E, 2*d_ff]
+ *   Wq_down    e4m3 [E, d, d_ff],   s_down    fp32 [E, d]
+ * Routing is the fp32 router above.  Each token's x row and each (token, slot)
+ * SwiGLU activation row are quantised to e4m3 with one fp32 scale per row, as
+ * hy3moe_quantize_rows_e4m3 does; the products run on fp8 MFMA with fp32
+ * accumulation and are rescaled by row scale * channel scale.  Other
+ * arguments as for hy3moe_forward. */
+int hy3moe_forward_fp8(const uint16_t* x, const float* W_gate,
+                       const uint8_t* Wq_gate_up, const float* s_gate_up,
+                       const uint8_t* Wq_down, const float* s_down, float* out,
+                       int T, int d, int E, int k, int d_ff, float scale, void* stream,
+                       const float* logit_bias, int32_t* topk_idx, float* topk_w,
+                       void* workspace, size_t workspace_bytes);
+
+/* Per-row e4m3 quantisation used by hy3moe_forward_fp8 for x:
+ *   amax = max |x[r, :]|;  amax == 0 -> q = 0, s = 1;  otherwise
+ *   r = fp32(448 / amax), q = e4m3(fp32(x * r)) rounded to nearest even and
+ *   saturated to +-448, s = fp32(amax / 448); the row dequantises as q * s.
+ *   x bf16 [rows, cols] in; q e4m3 [rows, cols] out; s fp32 [rows] out.
+ * cols must be a multiple of 64 and at most 65536. */
+int hy3moe_quantize_rows_e4m3(const uint16_t* x, int rows, int cols,
+                              uint8_t* q, float* s, void* stream);
+
+/* Static text for a status code. */
+const char* hy3moe_status_string(int status);
+
+/* hipError_t of the last call on this thread that returned HY3MOE_ERR_HIP (0 if none). */
+int hy3moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HY3MOE_H */

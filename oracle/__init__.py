@@ -20,21 +20,28 @@ quantises to OCP e4m3):
 * combine: per-expert loop adding weight * expert output into the token's row
   -- "DeepSeek V4-Flash architecture Q&A", Q8.4 (the MoE forward sketch and
   the index_add_ note), done in float64 so the fp32-combine requirement
-  (wmrh.cn Hy3 assembly blog, section 2.3) is met with margin.
+  (wmrh.cn Hy3 assembly blog, section 2.3) is met with margin;
+* activation precision: the model's activations are bf16 tensors, and the
+  fp32 combine widens bf16 expert outputs before adding them (wmrh.cn Hy3
+  assembly blog, section 2.3; "Tencent Hy3-Flash Q&A", Q6.2 describes the
+  bf16 sum used when that option is off).  So by default the SwiGLU
+  activation h and each expert output y are rounded once to bf16 (from
+  float64) where the layer stores them; ``bf16_activations=False`` gives the
+  all-float64 expression.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 invariants, library routines and brute force.  Parity unpinned: the value 2.826
 itself, and anything that would need the real model's weights.
 """
 
-from .codecs import (bf16_bits_to_f64, f32_to_bf16_bits, e4m3_bits_to_f64,
+from .codecs import (bf16_bits_to_f64, f32_to_bf16_bits, round_to_bf16, e4m3_bits_to_f64,
                      f32_to_e4m3_bits, E4M3_MAX)
 from .moe import (route, expert_swiglu, forward, forward_tokens, quant_row_e4m3,
                   quant_rows_e4m3, forward_fp8, forward_fp8_tokens,
                   expert_param_count, flops_per_token, NEAR_TIE)
 
 __all__ = [
-    "bf16_bits_to_f64", "f32_to_bf16_bits", "e4m3_bits_to_f64", "f32_to_e4m3_bits",
+    "bf16_bits_to_f64", "f32_to_bf16_bits", "round_to_bf16", "e4m3_bits_to_f64", "f32_to_e4m3_bits",
     "E4M3_MAX", "route", "expert_swiglu", "forward", "forward_tokens",
     "quant_row_e4m3", "quant_rows_e4m3", "forward_fp8", "forward_fp8_tokens",
     "expert_param_count", "flops_per_token", "NEAR_TIE",

@@ -27,6 +27,20 @@ def bf16_bits_to_f64(bits):
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def round_to_bf16(a):
+    """float64 values -> the nearest bf16 values (ties to even), as float64.
+
+    One rounding straight from float64 (no float32 step): keep the top 8
+    significant bits of the binary64 pattern.  Valid for finite values in
+    bf16's normal range, which is all the layer produces."""
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    u = a.view(np.uint64)
+    drop = np.uint64(45)                          # 52 - 7 stored mantissa bits
+    lsb = (u >> drop) & np.uint64(1)
+    r = (u + np.uint64((1 << 44) - 1) + lsb) & ~np.uint64((1 << 45) - 1)
+    return r.view(np.float64)
+
+
 def f32_to_bf16_bits(x):
     """float32 values -> uint16 bf16 bit patterns, round to nearest even.
 

@@ -9,6 +9,10 @@ except where the pages fix a precision:
   The oracle computes the logit in float64 (closer to the exact value than any
   float32 summation order), applies the sigmoid in float64 and rounds the score
   once to float32.  Selection compares those float32 scores.
+* The SwiGLU activation and each expert output are bf16 tensors in the model
+  (its activations are bf16; the fp32 combine widens bf16 expert outputs:
+  wmrh.cn Hy3 assembly blog, section 2.3), so ``bf16_activations=True`` (the
+  default) rounds each once from float64 to bf16 where the layer stores it.
 * The FP8 variant quantises activations to e4m3 with one float32 scale per row
   ("DeepSeek V4-Flash architecture Q&A", Q7.2 for the format, Q7.4 for
   per-channel scales), computing the scale and the scaled values in float32.
@@ -18,7 +22,7 @@ from collections import namedtuple
 
 import numpy as np
 
-from .codecs import bf16_bits_to_f64, e4m3_bits_to_f64, f32_to_e4m3_bits, E4M3_MAX
+from .codecs import bf16_bits_to_f64, e4m3_bits_to_f64, f32_to_e4m3_bits, round_to_bf16, E4M3_MAX
 
 # Tokens whose k-th and (k+1)-th float32 scores differ by less than this are
 # flagged: a float32 GPU router may legitimately pick either expert there.
@@ -83,22 +87,26 @@ def route(x_bits, W_gate, k, scale, logit_bias=None, block=4096):
     return Route(idx, w, scores, near_tie, order_tie, gap)
 
 
-def expert_swiglu(x, W_gu, W_dn):
+def expert_swiglu(x, W_gu, W_dn, bf16_activations=True):
     """One SwiGLU expert on rows x [n, d] (float64).
 
     W_gu [2F, d]: rows [0, F) are the gate projection, rows [F, 2F) the up
     projection (the fused gate_up_proj of "Tencent Hy3-295B architecture
     teardown", section 2.3).  W_dn [d, F] is down_proj.  No bias.
     a = SiLU(x W_gate^T) * (x W_up^T), y = a W_dn^T ("DeepSeek V4-Flash
-    architecture Q&A", Q4.5)."""
+    architecture Q&A", Q4.5).  With bf16_activations, a and y are rounded to
+    bf16 (the tensors a bf16 model stores); the products stay float64."""
     F = W_dn.shape[1]
     g = x @ W_gu[:F].T
     u = x @ W_gu[F:].T
     a = g * _sigmoid64(g) * u
+    if bf16_activations:
+        return round_to_bf16(round_to_bf16(a) @ W_dn.T)
     return a @ W_dn.T
 
 
-def forward(x_bits, W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias=None):
+def forward(x_bits, W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias=None,
+            bf16_activations=True):
     """Routed MoE output with bf16 experts, float64 combine.
 
     x_bits uint16 [T,d]; W_gate float32 [E,d]; W_gu_bits uint16 [E,2F,d];
@@ -117,16 +125,19 @@ def forward(x_bits, W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias=None):
     x = bf16_bits_to_f64(x_bits)
     for e in np.unique(r.idx):
         t, j = np.nonzero(r.idx == e)          # a token picks an expert at most once
-        y = expert_swiglu(x[t], bf16_bits_to_f64(W_gu_bits[e]), bf16_bits_to_f64(W_dn_bits[e]))
+        y = expert_swiglu(x[t], bf16_bits_to_f64(W_gu_bits[e]), bf16_bits_to_f64(W_dn_bits[e]),
+                          bf16_activations)
         out[t] += r.w[t, j][:, None] * y
     return out, r
 
 
-def forward_tokens(tokens, x_bits, W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias=None):
+def forward_tokens(tokens, x_bits, W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias=None,
+                   bf16_activations=True):
     """Output rows of ``forward`` for the listed tokens only.  Tokens are
     independent through the whole layer, so this is forward() on those rows."""
     tokens = np.asarray(tokens, dtype=np.int64)
-    return forward(np.asarray(x_bits)[tokens], W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias)
+    return forward(np.asarray(x_bits)[tokens], W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias,
+                   bf16_activations)
 
 
 # ----------------------------------------------------------------------------- FP8
@@ -165,7 +176,8 @@ def forward_fp8(x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale, logit_bias=N
     ``route``.  Each token's bf16 row is quantised with quant_row_e4m3 before
     the gate_up product; each (token, slot) SwiGLU activation row, rounded to
     float32, is quantised the same way before the down product.  Products use
-    the dequantised operands in float64; the combine is as in ``forward``."""
+    the dequantised operands in float64; each expert output row is rounded to
+    bf16 (as in ``forward``) and the combine is as in ``forward``."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     T, d = x_bits.shape
     r = route(x_bits, W_gate, k, scale, logit_bias)
@@ -184,7 +196,7 @@ def forward_fp8(x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale, logit_bias=N
         a = g * _sigmoid64(g) * u
         qa, sa = quant_rows_e4m3(a.astype(np.float32))
         ad = e4m3_bits_to_f64(qa) * sa.astype(np.float64)[:, None]
-        out[t] += r.w[t, j][:, None] * (ad @ Wdn.T)
+        out[t] += r.w[t, j][:, None] * round_to_bf16(ad @ Wdn.T)
     return out, r
 
 

@@ -1,0 +1,239 @@
+// C ABI of libhy3moe (declared in include/hy3moe.h): argument checks,
+// workspace carving and the launch sequence of the layer.  Every check runs on
+// the host before anything is enqueued; the library never allocates, frees or
+// synchronises.
+
+#include "../../include/hy3moe.h"
+#include "internal.h"
+
+namespace {
+
+using hy3::Layout;
+using hy3::Tile;
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Regions used by hy3moe_route and hy3moe_permute come first, so their needs
+// are prefixes of the forward layout and do not depend on d or d_ff.
+Layout make_layout(int T, int d, int E, int k, int F, int dtype) {
+    Layout L{};
+    const size_t Tk = static_cast<size_t>(T) * k;
+    L.nb = (T + hy3::kRouteBlock - 1) / hy3::kRouteBlock;
+    const int bm_gu = dtype == HY3MOE_WEIGHTS_FP8_E4M3 ? hy3::gemm_bm_fp8(T, k) : hy3::gemm_bm_gate_up(T, k);
+    const int bm_dn = dtype == HY3MOE_WEIGHTS_FP8_E4M3 ? hy3::gemm_bm_fp8(T, k) : hy3::gemm_bm_down(T, k);
+    L.max_tiles_gu = static_cast<int>(Tk / bm_gu) + E;
+    L.max_tiles_dn = static_cast<int>(Tk / bm_dn) + E;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    L.scores = take(static_cast<size_t>(T) * E * sizeof(float));
+    L.blk_counts = take(static_cast<size_t>(E) * L.nb * sizeof(int32_t));
+    L.blk_base = take(static_cast<size_t>(E) * L.nb * sizeof(int32_t));
+    L.counts = take(static_cast<size_t>(E) * sizeof(int32_t));
+    L.offsets = take(static_cast<size_t>(E + 1) * sizeof(int32_t));
+    L.tiles_gu = take(static_cast<size_t>(L.max_tiles_gu) * sizeof(Tile));
+    L.ntiles_gu = take(sizeof(int32_t));
+    L.tiles_dn = take(static_cast<size_t>(L.max_tiles_dn) * sizeof(Tile));
+    L.ntiles_dn = take(sizeof(int32_t));
+    L.idx = take(Tk * sizeof(int32_t));
+    L.w = take(Tk * sizeof(float));
+    L.row_of = take(Tk * sizeof(int32_t));
+    L.tok_of = take(Tk * sizeof(int32_t));
+    if (dtype == HY3MOE_WEIGHTS_FP8_E4M3) {
+        L.h = take(Tk * F * sizeof(float));            // fp32 SwiGLU activations
+        L.hq = take(Tk * F);                           // their e4m3 codes
+        L.hs = take(Tk * sizeof(float));               // per-row scale / amax
+        L.xq = take(static_cast<size_t>(T) * d);
+        L.xs = take(static_cast<size_t>(T) * sizeof(float));
+    } else {
+        L.h = take(Tk * F * sizeof(uint16_t));
+        L.hq = L.hs = L.xq = L.xs = 0;
+    }
+    L.y = take(Tk * d * sizeof(uint16_t));
+    L.total = off;
+    return L;
+}
+
+size_t route_bytes(const Layout& L) { return L.blk_counts; }
+size_t permute_bytes(const Layout& L) { return L.idx; }
+
+int check_shape(int T, int d, int E, int k, int F) {
+    if (T < 0 || d <= 0 || E <= 0 || F <= 0 || k < 1 || k > E) return HY3MOE_ERR_SHAPE;
+    if (k > 16 || E > 1024 || (d % 64) != 0 || (F % 64) != 0 || T > (1 << 24))
+        return HY3MOE_ERR_UNSUPPORTED;
+    return HY3MOE_OK;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return HY3MOE_OK;
+    g_last_hip_error = static_cast<int>(e);
+    return HY3MOE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hy3moe_workspace_size(int T, int d, int E, int k, int d_ff, int weight_dtype, size_t* bytes) {
+    if (!bytes) return HY3MOE_ERR_NULL;
+    const int st = check_shape(T, d, E, k, d_ff);
+    if (st != HY3MOE_OK) return st;
+    if (weight_dtype != HY3MOE_WEIGHTS_BF16 && weight_dtype != HY3MOE_WEIGHTS_FP8_E4M3)
+        return HY3MOE_ERR_UNSUPPORTED;
+    *bytes = make_layout(T, d, E, k, d_ff, weight_dtype).total;
+    return HY3MOE_OK;
+}
+
+int hy3moe_route(const uint16_t* x, const float* W_gate, const float* logit_bias, int T, int d,
+                 int E, int k, float scale, int32_t* topk_idx, float* topk_w, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    int st = check_shape(T, d, E, k, 64);
+    if (st != HY3MOE_OK) return st;
+    if (T == 0) return HY3MOE_OK;
+    if (!x || !W_gate || !topk_idx || !topk_w || !workspace) return HY3MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(W_gate) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+        !aligned16(workspace) || (logit_bias && !aligned16(logit_bias)))
+        return HY3MOE_ERR_ALIGN;
+    const Layout L = make_layout(T, d, E, k, 64, HY3MOE_WEIGHTS_BF16);
+    if (workspace_bytes < route_bytes(L)) return HY3MOE_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    return hip_status(hy3::launch_router(x, W_gate, logit_bias, T, d, E, k, scale,
+                                         reinterpret_cast<float*>(ws + L.scores), topk_idx, topk_w,
+                                         nullptr, L.nb, static_cast<hipStream_t>(stream)));
+}
+
+int hy3moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
+                   int32_t* offsets, int32_t* row_of, int32_t* token_of, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    int st = check_shape(T, 64, E, k, 64);
+    if (st != HY3MOE_OK) return st;
+    if (T == 0) return HY3MOE_OK;
+    if (!topk_idx || !counts || !offsets || !row_of || !token_of || !workspace)
+        return HY3MOE_ERR_NULL;
+    if (!aligned16(topk_idx) || !aligned16(counts) || !aligned16(offsets) || !aligned16(row_of) ||
+        !aligned16(token_of) || !aligned16(workspace))
+        return HY3MOE_ERR_ALIGN;
+    const Layout L = make_layout(T, 64, E, k, 64, HY3MOE_WEIGHTS_BF16);
+    if (workspace_bytes < permute_bytes(L)) return HY3MOE_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* blk_counts = reinterpret_cast<int32_t*>(ws + L.blk_counts);
+    hipError_t e = hy3::launch_block_counts(topk_idx, T, E, k, L.nb, blk_counts, s);
+    if (e != hipSuccess) return hip_status(e);
+    e = hy3::launch_dispatch(topk_idx, T, E, k, L.nb, blk_counts,
+                             reinterpret_cast<int32_t*>(ws + L.blk_base), counts, offsets,
+                             reinterpret_cast<Tile*>(ws + L.tiles_gu),
+                             reinterpret_cast<int32_t*>(ws + L.ntiles_gu), hy3::gemm_bm_gate_up(T, k),
+                             reinterpret_cast<Tile*>(ws + L.tiles_dn),
+                             reinterpret_cast<int32_t*>(ws + L.ntiles_dn), hy3::gemm_bm_down(T, k),
+                             row_of, token_of, s);
+    return hip_status(e);
+}
+
+int hy3moe_forward(const uint16_t* x, const float* W_gate, const uint16_t* W_gate_up,
+                   const uint16_t* W_down, float* out, int T, int d, int E, int k, int d_ff,
+                   float scale, void* stream, const float* logit_bias, int32_t* topk_idx,
+                   float* topk_w, void* workspace, size_t workspace_bytes) {
+    int st = check_shape(T, d, E, k, d_ff);
+    if (st != HY3MOE_OK) return st;
+    if (T == 0) return HY3MOE_OK;
+    if (!x || !W_gate || !W_gate_up || !W_down || !out || !workspace) return HY3MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_gate_up) || !aligned16(W_down) ||
+        !aligned16(out) || !aligned16(workspace) || (logit_bias && !aligned16(logit_bias)) ||
+        (topk_idx && !aligned16(topk_idx)) || (topk_w && !aligned16(topk_w)))
+        return HY3MOE_ERR_ALIGN;
+    const Layout L = make_layout(T, d, E, k, d_ff, HY3MOE_WEIGHTS_BF16);
+    if (workspace_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + L.idx);
+    float* w = topk_w ? topk_w : reinterpret_cast<float*>(ws + L.w);
+    int32_t* blk_counts = reinterpret_cast<int32_t*>(ws + L.blk_counts);
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+    Tile* tiles_gu = reinterpret_cast<Tile*>(ws + L.tiles_gu);
+    Tile* tiles_dn = reinterpret_cast<Tile*>(ws + L.tiles_dn);
+    int32_t* ntiles_gu = reinterpret_cast<int32_t*>(ws + L.ntiles_gu);
+    int32_t* ntiles_dn = reinterpret_cast<int32_t*>(ws + L.ntiles_dn);
+    int32_t* row_of = reinterpret_cast<int32_t*>(ws + L.row_of);
+    int32_t* tok_of = reinterpret_cast<int32_t*>(ws + L.tok_of);
+    uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+    uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
+
+    hipError_t e = hy3::launch_router(x, W_gate, logit_bias, T, d, E, k, scale,
+                                      reinterpret_cast<float*>(ws + L.scores), idx, w, blk_counts,
+                                      L.nb, s);
+    if (e != hipSuccess) return hip_status(e);
+    e = hy3::launch_dispatch(idx, T, E, k, L.nb, blk_counts,
+                             reinterpret_cast<int32_t*>(ws + L.blk_base),
+                             reinterpret_cast<int32_t*>(ws + L.counts), offsets, tiles_gu, ntiles_gu,
+                             hy3::gemm_bm_gate_up(T, k), tiles_dn, ntiles_dn,
+                             hy3::gemm_bm_down(T, k), row_of, tok_of, s);
+    if (e != hipSuccess) return hip_status(e);
+    e = hy3::launch_gate_up_bf16(x, tok_of, W_gate_up, tiles_gu, ntiles_gu, L.max_tiles_gu, offsets,
+                                 h, T, d, d_ff, k, s);
+    if (e != hipSuccess) return hip_status(e);
+    e = hy3::launch_down_bf16(h, W_down, tiles_dn, ntiles_dn, L.max_tiles_dn, offsets, y, T, d, d_ff,
+                              k, s);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(hy3::launch_combine(y, row_of, w, out, T, d, k, s));
+}
+
+int hy3moe_forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gate_up,
+                       const float* s_gate_up, const uint8_t* Wq_down, const float* s_down,
+                       float* out, int T, int d, int E, int k, int d_ff, float scale, void* stream,
+                       const float* logit_bias, int32_t* topk_idx, float* topk_w, void* workspace,
+                       size_t workspace_bytes) {
+    int st = check_shape(T, d, E, k, d_ff);
+    if (st != HY3MOE_OK) return st;
+    if (T == 0) return HY3MOE_OK;
+    if (!x || !W_gate || !Wq_gate_up || !s_gate_up || !Wq_down || !s_down || !out || !workspace)
+        return HY3MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(W_gate) || !aligned16(Wq_gate_up) || !aligned16(s_gate_up) ||
+        !aligned16(Wq_down) || !aligned16(s_down) || !aligned16(out) || !aligned16(workspace) ||
+        (logit_bias && !aligned16(logit_bias)) || (topk_idx && !aligned16(topk_idx)) ||
+        (topk_w && !aligned16(topk_w)))
+        return HY3MOE_ERR_ALIGN;
+    const Layout L = make_layout(T, d, E, k, d_ff, HY3MOE_WEIGHTS_FP8_E4M3);
+    if (workspace_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
+    (void)scale;
+    (void)stream;
+    return HY3MOE_ERR_UNSUPPORTED;
+}
+
+int hy3moe_quantize_rows_e4m3(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,
+                              void* stream) {
+    if (rows < 0 || cols <= 0) return HY3MOE_ERR_SHAPE;
+    if ((cols % 64) != 0 || cols > 65536) return HY3MOE_ERR_UNSUPPORTED;
+    if (rows == 0) return HY3MOE_OK;
+    if (!x || !q || !s) return HY3MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return HY3MOE_ERR_ALIGN;
+    return hip_status(hy3::launch_quant_rows(x, rows, cols, q, s, static_cast<hipStream_t>(stream)));
+}
+
+const char* hy3moe_status_string(int status) {
+    switch (status) {
+        case HY3MOE_OK: return "ok";
+        case HY3MOE_ERR_NULL: return "a required pointer is NULL";
+        case HY3MOE_ERR_SHAPE: return "invalid shape (T < 0, k < 1, k > E or a non-positive size)";
+        case HY3MOE_ERR_UNSUPPORTED:
+            return "unsupported shape or dtype (k <= 16, E <= 1024, d and d_ff multiples of 64, "
+                   "T <= 2^24)";
+        case HY3MOE_ERR_WORKSPACE: return "workspace smaller than hy3moe_workspace_size reports";
+        case HY3MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case HY3MOE_ERR_HIP: return "a HIP launch failed (see hy3moe_last_hip_error)";
+        default: return "unknown status";
+    }
+}
+
+int hy3moe_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,186 @@
+// Dispatch order: a stable counting sort of the T*k (token, slot) pairs by
+// expert.  Rows of one expert are contiguous, in ascending token order, which
+// is the grouping the per-expert loop of "DeepSeek V4-Flash architecture Q&A"
+// (Q8.4) performs, laid out so one grouped GEMM launch covers every expert.
+//
+// Tokens are cut into routing blocks of 64.  The router's top-k kernel already
+// counted, per block, the pairs of every expert (popcount of a 64-bit token
+// mask held in LDS).  Here:
+//   k_block_scan   one workgroup per expert: exclusive scan of its per-block
+//                  counts -> base of each block inside the expert; total count;
+//   k_offsets      one workgroup: exclusive scan of the counts -> offsets, and
+//                  the M-tile lists of both expert GEMMs;
+//   k_scatter      one workgroup per routing block: rebuilds the token masks
+//                  and gives pair (t, j) of expert e the row
+//                  offsets[e] + base[e, block] + #(tokens of the block before t
+//                  that chose e).
+// All of it is integer work with no atomics whose order matters, so the
+// result is the same on every run.
+
+#include "internal.h"
+
+namespace hy3 {
+namespace {
+
+// Exclusive scan over one workgroup of 256 threads; returns the total.
+__device__ int block_exclusive_scan(int v, int* lds /* >= 256 + 1 ints */, int& excl) {
+    const int tid = threadIdx.x;
+    lds[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int add = tid >= off ? lds[tid - off] : 0;
+        __syncthreads();
+        lds[tid] += add;
+        __syncthreads();
+    }
+    const int incl = lds[tid];
+    const int total = lds[255];
+    __syncthreads();
+    excl = incl - v;
+    return total;
+}
+
+__global__ __launch_bounds__(256) void k_block_scan(const int32_t* __restrict__ blk_counts,
+                                                   int32_t* __restrict__ blk_base,
+                                                   int32_t* __restrict__ counts, int nb) {
+    __shared__ int lds[256];
+    const int e = blockIdx.x;
+    const int32_t* c = blk_counts + static_cast<size_t>(e) * nb;
+    int32_t* b = blk_base + static_cast<size_t>(e) * nb;
+    int running = 0;
+    for (int base = 0; base < nb; base += 256 * 4) {
+        int v[4];
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = base + threadIdx.x * 4 + i;
+            v[i] = p < nb ? c[p] : 0;
+            sum += v[i];
+        }
+        int excl;
+        const int total = block_exclusive_scan(sum, lds, excl);
+        int acc = running + excl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = base + threadIdx.x * 4 + i;
+            if (p < nb) b[p] = acc;
+            acc += v[i];
+        }
+        running += total;
+    }
+    if (threadIdx.x == 0) counts[e] = running;
+}
+
+// One workgroup of 1024 threads; E <= 1024.
+__global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ counts, int E,
+                                                  int32_t* __restrict__ offsets,
+                                                  Tile* __restrict__ tiles_gu,
+                                                  int32_t* __restrict__ ntiles_gu, int bm_gu,
+                                                  Tile* __restrict__ tiles_dn,
+                                                  int32_t* __restrict__ ntiles_dn, int bm_dn) {
+    __shared__ int s_cnt[1024];
+    __shared__ int s_t1[1024];
+    __shared__ int s_t2[1024];
+    const int tid = threadIdx.x;
+    const int c = tid < E ? counts[tid] : 0;
+    s_cnt[tid] = c;
+    s_t1[tid] = (c + bm_gu - 1) / bm_gu;
+    s_t2[tid] = (c + bm_dn - 1) / bm_dn;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int a0 = tid >= off ? s_cnt[tid - off] : 0;
+        const int a1 = tid >= off ? s_t1[tid - off] : 0;
+        const int a2 = tid >= off ? s_t2[tid - off] : 0;
+        __syncthreads();
+        s_cnt[tid] += a0;
+        s_t1[tid] += a1;
+        s_t2[tid] += a2;
+        __syncthreads();
+    }
+    const int off_e = s_cnt[tid] - c;
+    if (tid < E) offsets[tid] = off_e;
+    if (tid == 0) {
+        offsets[E] = s_cnt[1023];
+        *ntiles_gu = s_t1[1023];
+        *ntiles_dn = s_t2[1023];
+    }
+    if (tid < E) {
+        const int n1 = (c + bm_gu - 1) / bm_gu;
+        const int start1 = s_t1[tid] - n1;
+        for (int i = 0; i < n1; ++i) tiles_gu[start1 + i] = Tile{tid, off_e + i * bm_gu};
+        const int n2 = (c + bm_dn - 1) / bm_dn;
+        const int start2 = s_t2[tid] - n2;
+        for (int i = 0; i < n2; ++i) tiles_dn[start2 + i] = Tile{tid, off_e + i * bm_dn};
+    }
+}
+
+__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, int T, int E,
+                                                int k, int nb,
+                                                const int32_t* __restrict__ blk_base,
+                                                const int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ row_of,
+                                                int32_t* __restrict__ tok_of) {
+    __shared__ unsigned long long mask[1024];
+    for (int e = threadIdx.x; e < E; e += 256) mask[e] = 0ull;
+    __syncthreads();
+    const int b = blockIdx.x;
+    const int npairs = kRouteBlock * k;
+    for (int p = threadIdx.x; p < npairs; p += 256) {
+        const int tl = p / k;
+        const int t = b * kRouteBlock + tl;
+        if (t < T) atomicOr(&mask[idx[static_cast<size_t>(t) * k + (p - tl * k)]], 1ull << tl);
+    }
+    __syncthreads();
+    for (int p = threadIdx.x; p < npairs; p += 256) {
+        const int tl = p / k;
+        const int t = b * kRouteBlock + tl;
+        if (t < T) {
+            const size_t pair = static_cast<size_t>(t) * k + (p - tl * k);
+            const int e = idx[pair];
+            const int rank = __popcll(mask[e] & ((1ull << tl) - 1ull));
+            const int row = offsets[e] + blk_base[static_cast<size_t>(e) * nb + b] + rank;
+            row_of[pair] = row;
+            tok_of[row] = t;
+        }
+    }
+}
+
+// Per-block counts when the routing comes from the caller (hy3moe_permute).
+__global__ __launch_bounds__(256) void k_block_counts(const int32_t* __restrict__ idx, int T,
+                                                     int E, int k, int nb,
+                                                     int32_t* __restrict__ blk_counts) {
+    __shared__ int cnt[1024];
+    for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+    __syncthreads();
+    const int b = blockIdx.x;
+    for (int p = threadIdx.x; p < kRouteBlock * k; p += 256) {
+        const int t = b * kRouteBlock + p / k;
+        if (t < T) atomicAdd(&cnt[idx[static_cast<size_t>(t) * k + (p % k)]], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256)
+        blk_counts[static_cast<size_t>(e) * nb + b] = cnt[e];
+}
+
+}  // namespace
+
+hipError_t launch_block_counts(const int32_t* idx, int T, int E, int k, int nb,
+                               int32_t* blk_counts, hipStream_t s) {
+    hipLaunchKernelGGL(k_block_counts, dim3(nb), dim3(256), 0, s, idx, T, E, k, nb, blk_counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
+                           const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,
+                           int32_t* offsets, Tile* tiles_gu, int32_t* ntiles_gu, int bm_gu,
+                           Tile* tiles_dn, int32_t* ntiles_dn, int bm_dn, int32_t* row_of,
+                           int32_t* tok_of, hipStream_t s) {
+    hipLaunchKernelGGL(k_block_scan, dim3(E), dim3(256), 0, s, blk_counts, blk_base, counts, nb);
+    hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, s, counts, E, offsets, tiles_gu,
+                       ntiles_gu, bm_gu, tiles_dn, ntiles_dn, bm_dn);
+    hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(256), 0, s, idx, T, E, k, nb, blk_base, offsets,
+                       row_of, tok_of);
+    return hipGetLastError();
+}
+
+}  // namespace hy3

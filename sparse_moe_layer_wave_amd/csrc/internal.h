@@ -1,0 +1,103 @@
+// Internal declarations shared by the HIP translation units of libhy3moe.
+// Not part of the public ABI (that is include/hy3moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hy3 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// Tokens per routing block: one bit per token in a 64-bit LDS mask.
+constexpr int kRouteBlock = 64;
+
+// One M-tile of a grouped GEMM: expert and first row (in expert-contiguous
+// row order); the tile ends at min(row0 + BM, offsets[expert + 1]).
+struct Tile {
+    int expert;
+    int row0;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g / (1.0f + __expf(-g)) * u;
+}
+
+// Workspace carving, computed identically on the host for every entry point.
+struct Layout {
+    size_t scores, blk_counts, blk_base, counts, offsets, tiles_gu, ntiles_gu, tiles_dn,
+        ntiles_dn, idx, w, row_of, tok_of, h, y, xq, xs, hq, hs, total;
+    int nb;              // routing blocks
+    int max_tiles_gu;    // upper bound on M-tiles of the gate_up GEMM
+    int max_tiles_dn;
+};
+
+// ---- launchers (each returns hipGetLastError() after enqueueing) ----
+hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bias, int T, int d,
+                         int E, int k, float scale, float* scores, int32_t* idx, float* w,
+                         int32_t* blk_counts, int nb, hipStream_t s);
+
+hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
+                           const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,
+                           int32_t* offsets, Tile* tiles_gu, int32_t* ntiles_gu, int bm_gu,
+                           Tile* tiles_dn, int32_t* ntiles_dn, int bm_dn, int32_t* row_of,
+                           int32_t* tok_of, hipStream_t s);
+
+// bf16 expert GEMMs; the M-tile size they need in the tile lists
+int gemm_bm_gate_up(int T, int k);
+int gemm_bm_down(int T, int k);
+hipError_t launch_gate_up_bf16(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
+                               const Tile* tiles, const int32_t* ntiles, int max_tiles,
+                               const int32_t* offsets, uint16_t* h, int T, int d, int F, int k,
+                               hipStream_t s);
+hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* W_dn, const Tile* tiles,
+                            const int32_t* ntiles, int max_tiles, const int32_t* offsets,
+                            uint16_t* y, int T, int d, int F, int k, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* row_of, const float* w, float* out,
+                          int T, int d, int k, hipStream_t s);
+
+// fp8 path
+__device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
+    // OCP E4M3FN, round to nearest even, finite values saturate to +-448.
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (!(a == a)) return static_cast<uint8_t>(sign | 0x7fu);
+    if (a >= 448.0f) return static_cast<uint8_t>(sign | 0x7eu);
+    if (a < 0.015625f) {                       // below 2^-6: multiples of 2^-9
+        const float m = rintf(a * 512.0f);     // exact scaling, ties to even
+        return static_cast<uint8_t>(sign | static_cast<uint32_t>(m));
+    }
+    uint32_t ua = __float_as_uint(a);          // keep 3 of 23 mantissa bits, ties to even
+    ua += 0x7ffffu + ((ua >> 20) & 1u);
+    const int e = static_cast<int>(ua >> 23) - 127;
+    uint32_t code = (static_cast<uint32_t>(e + 7) << 3) | ((ua >> 20) & 7u);
+    if (code > 0x7eu) code = 0x7eu;
+    return static_cast<uint8_t>(sign | code);
+}
+
+hipError_t launch_block_counts(const int32_t* idx, int T, int E, int k, int nb,
+                               int32_t* blk_counts, hipStream_t s);
+hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,
+                             hipStream_t st);
+int gemm_bm_fp8(int T, int k);
+
+}  // namespace hy3

@@ -1,0 +1,206 @@
+"""ctypes binding of libhy3moe (include/hy3moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch tensors supply device memory and the current HIP stream; the
+functions check dtype, shape, device and contiguity, pass raw pointers, and
+raise Hy3MoeError on a negative status.  There is no fallback: if the library
+is not built, lib() raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhy3moe.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+WEIGHTS_BF16, WEIGHTS_FP8_E4M3 = 0, 1
+
+EXPORTS = (
+    "hy3moe_workspace_size", "hy3moe_route", "hy3moe_permute", "hy3moe_forward",
+    "hy3moe_forward_fp8", "hy3moe_quantize_rows_e4m3", "hy3moe_status_string",
+    "hy3moe_last_hip_error",
+)
+
+_lib = None
+
+
+class Hy3MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = lib().hy3moe_status_string(status).decode()
+        if status == ERR_HIP:
+            msg += f" (hipError {lib().hy3moe_last_hip_error()})"
+        super().__init__(f"{where}: status {status}: {msg}")
+
+
+def lib():
+    """The loaded library (loads it on first use; raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(python -m sparse_moe_layer_wave_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F, S, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    L.hy3moe_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(Z)]
+    L.hy3moe_route.argtypes = [P, P, P, I, I, I, I, F, P, P, P, Z, S]
+    L.hy3moe_permute.argtypes = [P, I, I, I, P, P, P, P, P, Z, S]
+    L.hy3moe_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z]
+    L.hy3moe_forward_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z]
+    L.hy3moe_quantize_rows_e4m3.argtypes = [P, I, I, P, P, S]
+    L.hy3moe_status_string.argtypes = [I]
+    L.hy3moe_status_string.restype = ctypes.c_char_p
+    L.hy3moe_last_hip_error.argtypes = []
+    for name in EXPORTS:
+        if name not in ("hy3moe_status_string",):
+            getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status, where):
+    if status != OK:
+        raise Hy3MoeError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def workspace_size(T, d, E, k, d_ff, weight_dtype=WEIGHTS_BF16):
+    n = ctypes.c_size_t(0)
+    _check(lib().hy3moe_workspace_size(T, d, E, k, d_ff, weight_dtype, ctypes.byref(n)),
+           "hy3moe_workspace_size")
+    return n.value
+
+
+def alloc_workspace(T, d, E, k, d_ff, weight_dtype=WEIGHTS_BF16, device="cuda"):
+    return torch.empty(max(workspace_size(T, d, E, k, d_ff, weight_dtype), 1), dtype=torch.uint8,
+                       device=device)
+
+
+def route(x, W_gate, k, scale, bias=None, workspace=None):
+    """hy3moe_route: returns (topk_idx int32 [T,k], topk_w fp32 [T,k])."""
+    T, d = x.shape
+    E = W_gate.shape[0]
+    _need(x, torch.bfloat16, (T, d), "x")
+    _need(W_gate, torch.float32, (E, d), "W_gate")
+    if bias is not None:
+        _need(bias, torch.float32, (E,), "bias")
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(T, d, E, k, 64, device=x.device) if T else None
+    _check(lib().hy3moe_route(_ptr(x), _ptr(W_gate), _ptr(bias), T, d, E, k, float(scale),
+                              _ptr(idx), _ptr(w), _ptr(workspace),
+                              0 if workspace is None else workspace.numel(), _stream()),
+           "hy3moe_route")
+    return idx, w
+
+
+def permute(topk_idx, E, workspace=None):
+    """hy3moe_permute: returns (counts [E], offsets [E+1], row_of [T,k], token_of [T*k])."""
+    T, k = topk_idx.shape
+    _need(topk_idx, torch.int32, (T, k), "topk_idx")
+    dev = topk_idx.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_of = torch.empty((T, k), dtype=torch.int32, device=dev)
+    token_of = torch.empty(T * k, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = alloc_workspace(T, 64, E, k, 64, device=dev) if T else None
+    _check(lib().hy3moe_permute(_ptr(topk_idx), T, E, k, _ptr(counts), _ptr(offsets), _ptr(row_of),
+                                _ptr(token_of), _ptr(workspace),
+                                0 if workspace is None else workspace.numel(), _stream()),
+           "hy3moe_permute")
+    return counts, offsets, row_of, token_of
+
+
+def forward(x, W_gate, W_gate_up, W_down, k, scale, bias=None, out=None, workspace=None,
+            return_routing=False):
+    """hy3moe_forward: returns out fp32 [T,d] (and (idx, w) if return_routing)."""
+    T, d = x.shape
+    E = W_gate.shape[0]
+    F = W_down.shape[2]
+    _need(x, torch.bfloat16, (T, d), "x")
+    _need(W_gate, torch.float32, (E, d), "W_gate")
+    _need(W_gate_up, torch.bfloat16, (E, 2 * F, d), "W_gate_up")
+    _need(W_down, torch.bfloat16, (E, d, F), "W_down")
+    if bias is not None:
+        _need(bias, torch.float32, (E,), "bias")
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, (T, d), "out")
+    idx = w = None
+    if return_routing:
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(T, d, E, k, F, device=x.device) if T else None
+    _check(lib().hy3moe_forward(_ptr(x), _ptr(W_gate), _ptr(W_gate_up), _ptr(W_down), _ptr(out),
+                                T, d, E, k, F, float(scale), _stream(), _ptr(bias), _ptr(idx),
+                                _ptr(w), _ptr(workspace),
+                                0 if workspace is None else workspace.numel()),
+           "hy3moe_forward")
+    return (out, idx, w) if return_routing else out
+
+
+def forward_fp8(x, W_gate, Wq_gate_up, s_gate_up, Wq_down, s_down, k, scale, bias=None, out=None,
+                workspace=None, return_routing=False):
+    """hy3moe_forward_fp8: e4m3 experts (uint8 codes) with fp32 per-channel scales."""
+    T, d = x.shape
+    E = W_gate.shape[0]
+    F = Wq_down.shape[2]
+    _need(x, torch.bfloat16, (T, d), "x")
+    _need(W_gate, torch.float32, (E, d), "W_gate")
+    _need(Wq_gate_up, torch.uint8, (E, 2 * F, d), "Wq_gate_up")
+    _need(s_gate_up, torch.float32, (E, 2 * F), "s_gate_up")
+    _need(Wq_down, torch.uint8, (E, d, F), "Wq_down")
+    _need(s_down, torch.float32, (E, d), "s_down")
+    if bias is not None:
+        _need(bias, torch.float32, (E,), "bias")
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, (T, d), "out")
+    idx = w = None
+    if return_routing:
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(T, d, E, k, F, WEIGHTS_FP8_E4M3, device=x.device) if T else None
+    _check(lib().hy3moe_forward_fp8(_ptr(x), _ptr(W_gate), _ptr(Wq_gate_up), _ptr(s_gate_up),
+                                    _ptr(Wq_down), _ptr(s_down), _ptr(out), T, d, E, k, F,
+                                    float(scale), _stream(), _ptr(bias), _ptr(idx), _ptr(w),
+                                    _ptr(workspace), 0 if workspace is None else workspace.numel()),
+           "hy3moe_forward_fp8")
+    return (out, idx, w) if return_routing else out
+
+
+def quantize_rows_e4m3(x):
+    """hy3moe_quantize_rows_e4m3: returns (codes uint8 [rows, cols], scales fp32 [rows])."""
+    rows, cols = x.shape
+    _need(x, torch.bfloat16, (rows, cols), "x")
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    s = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(lib().hy3moe_quantize_rows_e4m3(_ptr(x), rows, cols, _ptr(q), _ptr(s), _stream()),
+           "hy3moe_quantize_rows_e4m3")
+    return q, s

@@ -1,0 +1,86 @@
+"""Comparison helpers shared by the GPU parity tests (routing, permutation,
+outputs).  The tolerances and their reasons:
+
+* routing indices: bit-exact, except tokens the oracle flags -- a k-th/(k+1)-th
+  score gap below 1e-6 may change the chosen set, and any adjacent gap below
+  1e-6 among the first k+1 may change the slot order.  The GPU's fp32 logits
+  differ from the oracle's float64 ones by a few 1e-7 (fp32 accumulation over
+  d terms), which moves a score by at most a quarter of that.
+* routing weights: |dw| <= 1e-5 * scale (the same score error divided by a
+  sum of k scores, plus fp32 rounding of the division and scaling).
+* outputs: max |out_gpu - out_ref| <= tol * rms(out_ref), tol = 1e-2 with bf16
+  experts and 3e-2 with e4m3 experts, over the tokens whose chosen expert set
+  equals the oracle's.
+"""
+
+import numpy as np
+
+
+def check_routing(idx_gpu, w_gpu, r, scale):
+    idx_gpu = np.asarray(idx_gpu, dtype=np.int64)
+    w_gpu = np.asarray(w_gpu, dtype=np.float64)
+    T = idx_gpu.shape[0]
+    set_eq = np.array([set(a) == set(b) for a, b in zip(idx_gpu.tolist(), r.idx.tolist())],
+                      dtype=bool) if T else np.zeros(0, bool)
+    slot_eq = np.all(idx_gpu == r.idx, axis=1)
+    bad_set = ~set_eq & ~r.near_tie
+    bad_slot = ~slot_eq & ~r.order_tie
+    assert not bad_set.any(), f"routing sets differ on unflagged tokens {np.nonzero(bad_set)[0][:10]}"
+    assert not bad_slot.any(), f"slot order differs on unflagged tokens {np.nonzero(bad_slot)[0][:10]}"
+    # every GPU row: k distinct experts in range, weights sum to scale
+    assert np.all((idx_gpu >= 0) & (idx_gpu < r.scores.shape[1]))
+    assert all(len(set(row)) == len(row) for row in idx_gpu.tolist())
+    if T:
+        assert np.max(np.abs(w_gpu.sum(axis=1) - scale)) < 1e-5 * scale
+    dw = np.abs(w_gpu[slot_eq] - r.w[slot_eq])
+    assert dw.size == 0 or dw.max() <= 1e-5 * scale, f"weights differ by {dw.max()}"
+    return dict(tokens=T, near_tie=int(r.near_tie.sum()), set_diff=int((~set_eq).sum()),
+                slot_diff=int((~slot_eq).sum()), max_dw=float(dw.max()) if dw.size else 0.0)
+
+
+def expected_permutation(idx, E):
+    """Stable counting sort of the (token, slot) pairs by expert, via NumPy's
+    stable argsort: rows of one expert contiguous, ascending token inside."""
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    flat = idx.reshape(-1)
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    row_of = np.empty(T * k, dtype=np.int64)
+    row_of[order] = np.arange(T * k)
+    token_of = order // k
+    return counts, offsets, row_of.reshape(T, k), token_of
+
+
+def check_permutation(idx, E, counts, offsets, row_of, token_of):
+    c, o, r, t = expected_permutation(idx, E)
+    assert np.array_equal(np.asarray(counts), c)
+    assert np.array_equal(np.asarray(offsets), o)
+    assert np.array_equal(np.asarray(row_of), r)
+    assert np.array_equal(np.asarray(token_of), t)
+
+
+def check_output(out_gpu, out_ref, tol, valid=None):
+    out_gpu = np.asarray(out_gpu, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(out_ref ** 2))) if out_ref.size else 0.0
+    if valid is None:
+        valid = np.ones(out_ref.shape[0], dtype=bool)
+    err = float(np.max(np.abs(out_gpu[valid] - out_ref[valid]))) if valid.any() else 0.0
+    assert np.all(np.isfinite(out_gpu))
+    assert err <= tol * rms, f"max|d| {err:.3e} > {tol} * rms {rms:.3e}"
+    return dict(max_abs=err, rms_ref=rms, ratio=err / rms if rms else 0.0)
+
+
+class LazyExperts:
+    """Expert weights left on the GPU; the oracle pulls each expert it needs
+    (as host bit patterns) when it indexes this object."""
+
+    def __init__(self, tensor):
+        from sparse_moe_layer_wave_amd import inputs
+        self._t = tensor
+        self._bits = inputs.bits
+        self.shape = tuple(tensor.shape)
+
+    def __getitem__(self, e):
+        return self._bits(self._t[int(e)])

@@ -1,0 +1,126 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments before touching the GPU.  Pointer
+arguments here are fake addresses that the library never dereferences,
+because argument checks run on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_layer_wave_amd import hy3moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hy3moe.h")
+
+A = ctypes.c_void_p(0x10000)       # aligned fake device address
+MIS = ctypes.c_void_p(0x10004)     # misaligned
+NUL = None
+
+
+@pytest.fixture(scope="module")
+def L():
+    return hy3moe.lib()
+
+
+def test_every_declared_function_is_exported(L):
+    decl = set(re.findall(r"\b(hy3moe_\w+)\s*\(", open(HEADER).read()))
+    assert decl == set(hy3moe.EXPORTS)
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert len(L.hy3moe_status_string(code)) > 0
+    assert L.hy3moe_status_string(-99) == b"unknown status"
+    assert L.hy3moe_last_hip_error() == 0
+
+
+def _ws(L, T, d=4096, E=192, k=8, F=1536, dt=0):
+    n = ctypes.c_size_t(0)
+    st = L.hy3moe_workspace_size(T, d, E, k, F, dt, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_monotone_and_checked(L):
+    prev = -1
+    for T in (1, 2, 63, 64, 65, 1000, 8192, 65536):
+        for dt in (0, 1):
+            st, n = _ws(L, T, dt=dt)
+            assert st == 0 and n > 0
+        st, n = _ws(L, T)
+        assert n > prev
+        prev = n
+    # bf16 y [T*k, d] alone is part of the requirement
+    assert _ws(L, 65536)[1] >= 65536 * 8 * 4096 * 2
+    assert _ws(L, 8, dt=2)[0] == hy3moe.ERR_UNSUPPORTED
+    assert L.hy3moe_workspace_size(8, 4096, 192, 8, 1536, 0, None) == hy3moe.ERR_NULL
+
+
+def _fwd(L, T=16, d=512, E=32, k=8, F=128, x=A, wg=A, gu=A, dn=A, out=A, ws=A, nws=1 << 40,
+         bias=NUL, idx=NUL, w=NUL):
+    return L.hy3moe_forward(x, wg, gu, dn, out, T, d, E, k, F, 2.826, NUL, bias, idx, w, ws, nws)
+
+
+def test_forward_argument_checks(L):
+    assert _fwd(L, T=-1) == hy3moe.ERR_SHAPE
+    assert _fwd(L, k=0) == hy3moe.ERR_SHAPE
+    assert _fwd(L, k=33, E=32) == hy3moe.ERR_SHAPE
+    assert _fwd(L, d=0) == hy3moe.ERR_SHAPE
+    assert _fwd(L, k=17, E=64) == hy3moe.ERR_UNSUPPORTED
+    assert _fwd(L, E=1025) == hy3moe.ERR_UNSUPPORTED
+    assert _fwd(L, d=520) == hy3moe.ERR_UNSUPPORTED
+    assert _fwd(L, F=100) == hy3moe.ERR_UNSUPPORTED
+    assert _fwd(L, T=(1 << 24) + 1) == hy3moe.ERR_UNSUPPORTED
+    assert _fwd(L, x=NUL) == hy3moe.ERR_NULL
+    assert _fwd(L, dn=NUL) == hy3moe.ERR_NULL
+    assert _fwd(L, ws=NUL) == hy3moe.ERR_NULL
+    assert _fwd(L, x=MIS) == hy3moe.ERR_ALIGN
+    assert _fwd(L, out=MIS) == hy3moe.ERR_ALIGN
+    assert _fwd(L, bias=MIS) == hy3moe.ERR_ALIGN
+    assert _fwd(L, idx=MIS) == hy3moe.ERR_ALIGN
+    st, need = _ws(L, 16, 512, 32, 8, 128)
+    assert _fwd(L, nws=need - 1) == hy3moe.ERR_WORKSPACE
+    # T == 0 is a no-op that needs no pointers at all
+    assert _fwd(L, T=0, x=NUL, wg=NUL, gu=NUL, dn=NUL, out=NUL, ws=NUL, nws=0) == hy3moe.OK
+
+
+def test_forward_fp8_argument_checks(L):
+    def f(T=16, sgu=A, sdn=A, ws=A, nws=1 << 40, k=8):
+        return L.hy3moe_forward_fp8(A, A, A, sgu, A, sdn, A, T, 512, 32, k, 128, 2.826, NUL, NUL,
+                                    NUL, NUL, ws, nws)
+    assert f(T=-3) == hy3moe.ERR_SHAPE
+    assert f(sgu=NUL) == hy3moe.ERR_NULL
+    assert f(sdn=MIS) == hy3moe.ERR_ALIGN
+    assert f(nws=10) == hy3moe.ERR_WORKSPACE
+    assert f(T=0, ws=NUL, nws=0) == hy3moe.OK
+
+
+def test_route_and_permute_argument_checks(L):
+    def r(T=16, d=512, E=32, k=8, x=A, idx=A, ws=A, nws=1 << 40):
+        return L.hy3moe_route(x, A, NUL, T, d, E, k, 2.826, idx, A, ws, nws, NUL)
+    assert r(k=40) == hy3moe.ERR_SHAPE
+    assert r(x=NUL) == hy3moe.ERR_NULL
+    assert r(idx=MIS) == hy3moe.ERR_ALIGN
+    assert r(nws=0) == hy3moe.ERR_WORKSPACE
+    assert r(d=96) == hy3moe.ERR_UNSUPPORTED
+    assert r(T=0, x=NUL, ws=NUL, nws=0) == hy3moe.OK
+
+    def p(T=16, E=32, k=8, idx=A, row=A, ws=A, nws=1 << 40):
+        return L.hy3moe_permute(idx, T, E, k, A, A, row, A, ws, nws, NUL)
+    assert p(k=0) == hy3moe.ERR_SHAPE
+    assert p(idx=NUL) == hy3moe.ERR_NULL
+    assert p(row=MIS) == hy3moe.ERR_ALIGN
+    assert p(nws=4) == hy3moe.ERR_WORKSPACE
+    assert p(T=0, idx=NUL, ws=NUL, nws=0) == hy3moe.OK
+
+
+def test_quantize_rows_argument_checks(L):
+    q = L.hy3moe_quantize_rows_e4m3
+    assert q(A, -1, 64, A, A, NUL) == hy3moe.ERR_SHAPE
+    assert q(A, 4, 100, A, A, NUL) == hy3moe.ERR_UNSUPPORTED
+    assert q(NUL, 4, 64, A, A, NUL) == hy3moe.ERR_NULL
+    assert q(A, 4, 64, MIS, A, NUL) == hy3moe.ERR_ALIGN
+    assert q(NUL, 0, 64, NUL, NUL, NUL) == hy3moe.OK

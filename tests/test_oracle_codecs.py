@@ -91,3 +91,41 @@ def test_e4m3_saturates():
     got = codecs.f32_to_e4m3_bits(v)
     assert np.array_equal(got, np.uint8([0x7E] * 8 + [0xFE] * 2))
     assert codecs.f32_to_e4m3_bits(np.float32([np.nan]))[0] == 0x7F
+
+
+def _exact_bf16_round(v):
+    """Nearest bf16 value to a float64, ties to even, by exact rational
+    comparison of the two bf16 neighbours obtained by truncation."""
+    from fractions import Fraction
+    u = np.float64(v).view(np.uint64)
+    lo = (u & ~np.uint64((1 << 45) - 1)).view(np.float64)         # toward zero
+    step = np.uint64(1 << 45)
+    hi = (u & ~np.uint64((1 << 45) - 1)) + step
+    hi = hi.view(np.float64)
+    fv, flo, fhi = Fraction(float(v)), Fraction(float(lo)), Fraction(float(hi))
+    dlo, dhi = abs(fv - flo), abs(fhi - fv)
+    if dlo < dhi:
+        return float(lo)
+    if dhi < dlo:
+        return float(hi)
+    lo_even = ((np.float64(lo).view(np.uint64) >> np.uint64(45)) & np.uint64(1)) == 0
+    return float(lo) if lo_even else float(hi)
+
+
+def test_round_to_bf16_exact_on_random_float64():
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-20, 20, 3000),
+                        -rng.standard_normal(1000)])
+    got = codecs.round_to_bf16(v)
+    ref = np.array([_exact_bf16_round(a) for a in v])
+    assert np.array_equal(got, ref)
+
+
+def test_round_to_bf16_matches_torch_on_float32_values():
+    rng = np.random.default_rng(4)
+    v = (rng.standard_normal(100_000) * 5).astype(np.float32)
+    mids = (rng.integers(0x0080, 0x7F00, 5000, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    v = np.concatenate([v, mids, -mids])
+    got = codecs.round_to_bf16(v.astype(np.float64))
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, ref)

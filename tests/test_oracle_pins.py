@@ -104,7 +104,7 @@ def _brute_force_set(s32_row, k):
 def test_brute_force_subsets(E, k, d, F, T):
     rng = np.random.default_rng(5 + E)
     x, Wg, Wgu, Wdn = _rand_layer(rng, T, d, E, F, w_std=0.2)
-    out, r = oracle.forward(x, Wg, Wgu, Wdn, k, SCALE)
+    out, r = oracle.forward(x, Wg, Wgu, Wdn, k, SCALE, bf16_activations=False)
     x64 = codecs.bf16_bits_to_f64(x)
     logits = torch.from_numpy(x64) @ torch.from_numpy(Wg.astype(np.float64)).T
     s32 = torch.sigmoid(logits).numpy().astype(np.float32)
@@ -132,17 +132,26 @@ def test_identical_experts_reduce_to_dense_swiglu():
     x, Wg, Wgu, Wdn = _rand_layer(rng, T, d, E, F)
     Wgu[:] = Wgu[0]
     Wdn[:] = Wdn[0]
-    out, _ = oracle.forward(x, Wg, Wgu, Wdn, 4, SCALE)
-    ref = SCALE * _torch_swiglu(codecs.bf16_bits_to_f64(x), codecs.bf16_bits_to_f64(Wgu[0]),
-                                codecs.bf16_bits_to_f64(Wdn[0]))
+    out, _ = oracle.forward(x, Wg, Wgu, Wdn, 4, SCALE, bf16_activations=False)
+    x64 = codecs.bf16_bits_to_f64(x)
+    Wgu0, Wdn0 = codecs.bf16_bits_to_f64(Wgu[0]), codecs.bf16_bits_to_f64(Wdn[0])
+    ref = SCALE * _torch_swiglu(x64, Wgu0, Wdn0)
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+    # with bf16 activations: h and y rounded once, the weights still sum to scale
+    out_b, _ = oracle.forward(x, Wg, Wgu, Wdn, 4, SCALE)
+    F = Wdn0.shape[1]
+    g = torch.from_numpy(x64) @ torch.from_numpy(Wgu0[:F]).T
+    u = torch.from_numpy(x64) @ torch.from_numpy(Wgu0[F:]).T
+    h = codecs.round_to_bf16((Fn.silu(g) * u).numpy())
+    y = codecs.round_to_bf16((torch.from_numpy(h) @ torch.from_numpy(Wdn0).T).numpy())
+    np.testing.assert_allclose(out_b, SCALE * y, rtol=1e-12, atol=1e-15)
 
 
 def test_k1_is_scaled_argmax_expert():
     rng = np.random.default_rng(7)
     T, d, E, F = 30, 32, 9, 8
     x, Wg, Wgu, Wdn = _rand_layer(rng, T, d, E, F)
-    out, r = oracle.forward(x, Wg, Wgu, Wdn, 1, SCALE)
+    out, r = oracle.forward(x, Wg, Wgu, Wdn, 1, SCALE, bf16_activations=False)
     x64 = codecs.bf16_bits_to_f64(x)
     logits = torch.from_numpy(x64) @ torch.from_numpy(Wg.astype(np.float64)).T
     top = torch.argmax(logits, dim=1).numpy()
@@ -158,7 +167,7 @@ def test_k_equals_E_uses_every_expert():
     rng = np.random.default_rng(8)
     T, d, E, F = 10, 32, 6, 8
     x, Wg, Wgu, Wdn = _rand_layer(rng, T, d, E, F)
-    out, r = oracle.forward(x, Wg, Wgu, Wdn, E, SCALE)
+    out, r = oracle.forward(x, Wg, Wgu, Wdn, E, SCALE, bf16_activations=False)
     x64 = codecs.bf16_bits_to_f64(x)
     s = 1.0 / (1.0 + np.exp(-(x64 @ Wg.astype(np.float64).T)))
     s = s.astype(np.float32).astype(np.float64)
