@@ -1,0 +1,207 @@
+"""Throughput of the Hy3 MoE layer forward pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-prefill]
+
+One step = one hy3moe_forward call (router, dispatch order, gate_up, down,
+fp32 combine) over one batch of synthetic Hy3-shaped input already resident
+in HBM.  The main line is the decode batch (T=64 tokens, d=4096, 192 experts,
+top-8, d_ff=1536, bf16 experts); the prefill batch (T=8192) is reported in the
+same JSON line under "prefill".  Per-kernel durations come from HIP events
+recorded on the launch stream between the stages (hy3moe_forward_timed).
+
+Prints one JSON line.  Only one GPU is used; --gpus N > 1 exits with a message.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from sparse_moe_layer_wave_amd import hy3moe, inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+
+
+def _events(n):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()                 # creates the underlying hipEvent
+    return evs
+
+
+def algorithmic(c, n_touched):
+    """Bytes and FLOPs a kernel must move/compute, counting only touched
+    experts' weights, each tensor once, and no padding."""
+    T, d, E, k, F = c["T"], c["d"], c["E"], c["k"], c["F"]
+    rows = T * k
+    wb = 1 if c.get("weights") == "fp8" else 2
+    return {
+        "gate_up": dict(bytes=n_touched * 2 * F * d * wb + T * d * 2 + rows * F * 2,
+                        flops=2 * rows * d * 2 * F),
+        "down": dict(bytes=n_touched * d * F * wb + rows * F * 2 + rows * d * 2,
+                     flops=2 * rows * F * d),
+        "router": dict(bytes=E * d * 4 + T * d * 2 + rows * 8, flops=2 * T * d * E),
+        "combine": dict(bytes=rows * d * 2 + rows * 8 + T * d * 4, flops=2 * rows * d),
+        "layer_flops": T * (k * 6 * d * F + 2 * d * E),
+    }
+
+
+def run_workload(cfg, steps, warmup):
+    inp = inputs.make_inputs(cfg, device="cuda")
+    c = inp["cfg"]
+    T, d, E, k, F = c["T"], c["d"], c["E"], c["k"], c["F"]
+    ws = hy3moe.alloc_workspace(T, d, E, k, F)
+    out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+
+    def step(evs=None):
+        hy3moe.forward(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], k, inp["scale"],
+                       bias=inp["bias"], out=out, workspace=ws, stage_events=evs)
+
+    for _ in range(warmup):
+        step()
+    _, idx_r, _ = hy3moe.forward(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], k,
+                                 inp["scale"], bias=inp["bias"], workspace=ws, return_routing=True)
+    torch.cuda.synchronize()
+    load = np.bincount(idx_r.cpu().numpy().reshape(-1), minlength=E)
+    n_touched = int((load > 0).sum())
+    evs = [_events(6) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms = {name: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)]))
+                for i, name in enumerate(hy3moe.STAGES)}
+    alg = algorithmic(c, n_touched)
+    res = dict(cfg=c, ms_per_step=elapsed / steps * 1e3, tokens_per_s=T * steps / elapsed,
+               stage_ms=stage_ms, n_touched=n_touched, alg=alg,
+               layer_tflops=alg["layer_flops"] * steps / elapsed / 1e12,
+               hottest_over_mean=float(load.max() / load.mean()))
+    del inp, ws, out
+    torch.cuda.empty_cache()
+    return res, idx
+
+
+def roofline(res, kernel, bound):
+    ms = res["stage_ms"][kernel]
+    a = res["alg"][kernel]
+    if bound == "hbm":
+        achieved = a["bytes"] / (ms * 1e-3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = a["flops"] / (ms * 1e-3) / 1e12
+        peak, unit = BF16_PEAK_TFLOPS, "TFLOP/s"
+    return {"bound": bound, "kernel": kernel, "achieved": round(achieved, 2), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic(kernel, res),
+            "avg_kernel_ms": round(ms, 5)}
+
+
+def traffic(kernel, res):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when
+    it was taken on the current kernel source; otherwise null."""
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel}_{res['cfg']['name']}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "sparse_moe_layer_wave_amd", "csrc", rec["source"])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if sha != rec.get("source_sha"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, max_seconds=25.0):
+    """The oracle, as it stands, on the first tokens of the same workload."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    class Lazy:                         # expert weights stay in HBM until the oracle needs one
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, e):
+            return inputs.bits(self.t[int(e)])
+
+    inp = inputs.make_inputs(cfg, device="cuda")
+    c = inp["cfg"]
+    x_bits, W = inputs.bits(inp["x"]), inputs.bits(inp["W_gate"])
+    b = None if inp["bias"] is None else inputs.bits(inp["bias"])
+    gu, dn = Lazy(inp["W_gu"]), Lazy(inp["W_dn"])
+    n = 0
+    t0 = time.perf_counter()
+    chunk = 4
+    while n < c["T"] and time.perf_counter() - t0 < max_seconds:
+        toks = np.arange(n, min(n + chunk, c["T"]))
+        oracle.forward_tokens(toks, x_bits, W, gu, dn, c["k"], inputs.ROUTER_SCALE, b)
+        n += len(toks)
+    el = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(n / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of the {c['T']} decode tokens, oracle.forward_tokens in chunks of "
+                      f"{chunk} (NumPy float64, OpenBLAS), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the layer is not sharded "
+              "across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    dec, _ = run_workload(1, args.steps, args.warmup)
+    line = {
+        "metric": "MoE-layer tokens/s at T=64 & T=8192; % of HBM BW / % of MFMA peak",
+        "value": round(dec["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, Hy3 MoE layer shapes; random-init weights)",
+        "config": {"workload": dec["cfg"]["name"], "T": 64, "d": 4096, "E": 192, "k": 8,
+                   "d_ff": 1536, "experts_touched": dec["n_touched"]},
+        "roofline": roofline(dec, "gate_up", "hbm"),
+        "kernel_ms": {k: round(v, 5) for k, v in dec["stage_ms"].items()},
+        "layer_tflops": round(dec["layer_tflops"], 3),
+    }
+    if not args.no_prefill:
+        pre, _ = run_workload(2, max(5, args.steps // 5), args.warmup)
+        line["prefill"] = {
+            "workload": pre["cfg"]["name"], "tokens_per_s": round(pre["tokens_per_s"], 1),
+            "ms_per_step": round(pre["ms_per_step"], 4),
+            "layer_tflops": round(pre["layer_tflops"], 2),
+            "layer_frac_of_bf16_peak": round(pre["layer_tflops"] / BF16_PEAK_TFLOPS, 4),
+            "roofline": roofline(pre, "gate_up", "mfma"),
+            "roofline_down": roofline(pre, "down", "mfma"),
+            "kernel_ms": {k: round(v, 5) for k, v in pre["stage_ms"].items()},
+        }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

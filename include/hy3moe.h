@@ -108,6 +108,17 @@ int hy3moe_forward(const uint16_t* x, const float* W_gate,
                    const float* logit_bias, int32_t* topk_idx, float* topk_w,
                    void* workspace, size_t workspace_bytes);
 
+/* hy3moe_forward with instrumentation: stage_events is a HOST array of 6
+ * hipEvent_t handles (any may be NULL) recorded on `stream` before the router,
+ * after the router, after the dispatch order, after gate_up, after down and
+ * after the combine.  The caller creates the events and reads them with
+ * hipEventElapsedTime; the work enqueued is that of hy3moe_forward. */
+int hy3moe_forward_timed(const uint16_t* x, const float* W_gate,
+                         const uint16_t* W_gate_up, const uint16_t* W_down, float* out,
+                         int T, int d, int E, int k, int d_ff, float scale, void* stream,
+                         const float* logit_bias, int32_t* topk_idx, float* topk_w,
+                         void* workspace, size_t workspace_bytes, void* const* stage_events);
+
 /* The whole layer with e4m3 experts and per-output-channel fp32 scales
  * (formats: "DeepSeek V4-Flash architecture Q&A", Q7.2 and Q7.4).
  *   Wq_gate_up e4m3 [E, 2*d_ff, d], s_gate_up fp32 [E, 2*d_ff]

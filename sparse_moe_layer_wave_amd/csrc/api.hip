@@ -35,7 +35,8 @@ Layout make_layout(int T, int d, int E, int k, int F, int dtype) {
         off = align_up(off + bytes);
         return at;
     };
-    L.scores = take(static_cast<size_t>(T) * E * sizeof(float));
+    L.nsplit = hy3::router_nsplit(T, d, E);
+    L.scores = take(static_cast<size_t>(L.nsplit) * T * E * sizeof(float));
     L.blk_counts = take(static_cast<size_t>(E) * L.nb * sizeof(int32_t));
     L.blk_base = take(static_cast<size_t>(E) * L.nb * sizeof(int32_t));
     L.counts = take(static_cast<size_t>(E) * sizeof(int32_t));
@@ -73,6 +74,12 @@ int check_shape(int T, int d, int E, int k, int F) {
     return HY3MOE_OK;
 }
 
+// Records stage_events[i] on the stream when the caller supplied it.
+hipError_t mark(void* const* ev, int i, hipStream_t s) {
+    if (!ev || !ev[i]) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
+}
+
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return HY3MOE_OK;
     g_last_hip_error = static_cast<int>(e);
@@ -107,8 +114,8 @@ int hy3moe_route(const uint16_t* x, const float* W_gate, const float* logit_bias
     if (workspace_bytes < route_bytes(L)) return HY3MOE_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
     return hip_status(hy3::launch_router(x, W_gate, logit_bias, T, d, E, k, scale,
-                                         reinterpret_cast<float*>(ws + L.scores), topk_idx, topk_w,
-                                         nullptr, L.nb, static_cast<hipStream_t>(stream)));
+                                         reinterpret_cast<float*>(ws + L.scores), L.nsplit, topk_idx,
+                                         topk_w, nullptr, L.nb, static_cast<hipStream_t>(stream)));
 }
 
 int hy3moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
@@ -139,10 +146,15 @@ int hy3moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts
     return hip_status(e);
 }
 
-int hy3moe_forward(const uint16_t* x, const float* W_gate, const uint16_t* W_gate_up,
-                   const uint16_t* W_down, float* out, int T, int d, int E, int k, int d_ff,
-                   float scale, void* stream, const float* logit_bias, int32_t* topk_idx,
-                   float* topk_w, void* workspace, size_t workspace_bytes) {
+}  // extern "C"
+
+namespace {
+
+static int forward_bf16(const uint16_t* x, const float* W_gate, const uint16_t* W_gate_up,
+                        const uint16_t* W_down, float* out, int T, int d, int E, int k, int d_ff,
+                        float scale, void* stream, const float* logit_bias, int32_t* topk_idx,
+                        float* topk_w, void* workspace, size_t workspace_bytes,
+                        void* const* ev) {
     int st = check_shape(T, d, E, k, d_ff);
     if (st != HY3MOE_OK) return st;
     if (T == 0) return HY3MOE_OK;
@@ -168,24 +180,62 @@ int hy3moe_forward(const uint16_t* x, const float* W_gate, const uint16_t* W_gat
     uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
     uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
 
-    hipError_t e = hy3::launch_router(x, W_gate, logit_bias, T, d, E, k, scale,
-                                      reinterpret_cast<float*>(ws + L.scores), idx, w, blk_counts,
-                                      L.nb, s);
+    hipError_t e = mark(ev, 0, s);
+    if (e != hipSuccess) return hip_status(e);
+    e = hy3::launch_router(x, W_gate, logit_bias, T, d, E, k, scale,
+                                      reinterpret_cast<float*>(ws + L.scores), L.nsplit, idx, w,
+                                      blk_counts, L.nb, s);
+    if (e == hipSuccess) e = mark(ev, 1, s);
     if (e != hipSuccess) return hip_status(e);
     e = hy3::launch_dispatch(idx, T, E, k, L.nb, blk_counts,
                              reinterpret_cast<int32_t*>(ws + L.blk_base),
                              reinterpret_cast<int32_t*>(ws + L.counts), offsets, tiles_gu, ntiles_gu,
                              hy3::gemm_bm_gate_up(T, k), tiles_dn, ntiles_dn,
                              hy3::gemm_bm_down(T, k), row_of, tok_of, s);
+    if (e == hipSuccess) e = mark(ev, 2, s);
     if (e != hipSuccess) return hip_status(e);
-    e = hy3::launch_gate_up_bf16(x, tok_of, W_gate_up, tiles_gu, ntiles_gu, L.max_tiles_gu, offsets,
-                                 h, T, d, d_ff, k, s);
+    const bool decode = hy3::use_decode_path(T, d, E, k);
+    if (decode)
+        e = hy3::launch_gate_up_decode(x, tok_of, W_gate_up, offsets, h, E, d, d_ff, s);
+    else
+        e = hy3::launch_gate_up_bf16(x, tok_of, W_gate_up, tiles_gu, ntiles_gu, L.max_tiles_gu,
+                                     offsets, h, T, d, d_ff, k, s);
+    if (e == hipSuccess) e = mark(ev, 3, s);
     if (e != hipSuccess) return hip_status(e);
-    e = hy3::launch_down_bf16(h, W_down, tiles_dn, ntiles_dn, L.max_tiles_dn, offsets, y, T, d, d_ff,
-                              k, s);
+    if (decode)
+        e = hy3::launch_down_decode(h, W_down, offsets, y, E, d, d_ff, s);
+    else
+        e = hy3::launch_down_bf16(h, W_down, tiles_dn, ntiles_dn, L.max_tiles_dn, offsets, y, T, d,
+                                  d_ff, k, s);
+    if (e == hipSuccess) e = mark(ev, 4, s);
     if (e != hipSuccess) return hip_status(e);
-    return hip_status(hy3::launch_combine(y, row_of, w, out, T, d, k, s));
+    e = hy3::launch_combine(y, row_of, w, out, T, d, k, s);
+    if (e == hipSuccess) e = mark(ev, 5, s);
+    return hip_status(e);
 }
+
+}  // namespace
+
+extern "C" {
+
+int hy3moe_forward(const uint16_t* x, const float* W_gate, const uint16_t* W_gate_up,
+                   const uint16_t* W_down, float* out, int T, int d, int E, int k, int d_ff,
+                   float scale, void* stream, const float* logit_bias, int32_t* topk_idx,
+                   float* topk_w, void* workspace, size_t workspace_bytes) {
+    return forward_bf16(x, W_gate, W_gate_up, W_down, out, T, d, E, k, d_ff, scale, stream,
+                        logit_bias, topk_idx, topk_w, workspace, workspace_bytes, nullptr);
+}
+
+int hy3moe_forward_timed(const uint16_t* x, const float* W_gate, const uint16_t* W_gate_up,
+                         const uint16_t* W_down, float* out, int T, int d, int E, int k, int d_ff,
+                         float scale, void* stream, const float* logit_bias, int32_t* topk_idx,
+                         float* topk_w, void* workspace, size_t workspace_bytes,
+                         void* const* stage_events) {
+    return forward_bf16(x, W_gate, W_gate_up, W_down, out, T, d, E, k, d_ff, scale, stream,
+                        logit_bias, topk_idx, topk_w, workspace, workspace_bytes, stage_events);
+}
+
+
 
 int hy3moe_forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gate_up,
                        const float* s_gate_up, const uint8_t* Wq_down, const float* s_down,

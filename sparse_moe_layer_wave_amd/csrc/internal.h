@@ -37,7 +37,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
-    return g / (1.0f + __expf(-g)) * u;
+    return g / (1.0f + expf(-g)) * u;
 }
 
 // Workspace carving, computed identically on the host for every entry point.
@@ -45,14 +45,17 @@ struct Layout {
     size_t scores, blk_counts, blk_base, counts, offsets, tiles_gu, ntiles_gu, tiles_dn,
         ntiles_dn, idx, w, row_of, tok_of, h, y, xq, xs, hq, hs, total;
     int nb;              // routing blocks
+    int nsplit;          // router d-chunks
     int max_tiles_gu;    // upper bound on M-tiles of the gate_up GEMM
     int max_tiles_dn;
 };
 
 // ---- launchers (each returns hipGetLastError() after enqueueing) ----
+// Router: partial logits [nsplit, T, E] in `partial`, then selection.
+int router_nsplit(int T, int d, int E);
 hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bias, int T, int d,
-                         int E, int k, float scale, float* scores, int32_t* idx, float* w,
-                         int32_t* blk_counts, int nb, hipStream_t s);
+                         int E, int k, float scale, float* partial, int nsplit, int32_t* idx,
+                         float* w, int32_t* blk_counts, int nb, hipStream_t s);
 
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
                            const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,
@@ -70,6 +73,14 @@ hipError_t launch_gate_up_bf16(const uint16_t* x, const int32_t* tok_of, const u
 hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* W_dn, const Tile* tiles,
                             const int32_t* ntiles, int max_tiles, const int32_t* offsets,
                             uint16_t* y, int T, int d, int F, int k, hipStream_t s);
+
+// decode-sized batches: weight streaming, one workgroup per (expert, weight slice)
+bool use_decode_path(int T, int d, int E, int k);
+hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
+                                 const int32_t* offsets, uint16_t* h, int E, int d, int F,
+                                 hipStream_t s);
+hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const int32_t* offsets,
+                              uint16_t* y, int E, int d, int F, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of, const float* w, float* out,
                           int T, int d, int k, hipStream_t s);

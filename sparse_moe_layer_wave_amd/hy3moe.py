@@ -20,7 +20,7 @@ WEIGHTS_BF16, WEIGHTS_FP8_E4M3 = 0, 1
 
 EXPORTS = (
     "hy3moe_workspace_size", "hy3moe_route", "hy3moe_permute", "hy3moe_forward",
-    "hy3moe_forward_fp8", "hy3moe_quantize_rows_e4m3", "hy3moe_status_string",
+    "hy3moe_forward_timed", "hy3moe_forward_fp8", "hy3moe_quantize_rows_e4m3", "hy3moe_status_string",
     "hy3moe_last_hip_error",
 )
 
@@ -50,6 +50,7 @@ def lib():
     L.hy3moe_route.argtypes = [P, P, P, I, I, I, I, F, P, P, P, Z, S]
     L.hy3moe_permute.argtypes = [P, I, I, I, P, P, P, P, P, Z, S]
     L.hy3moe_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z]
+    L.hy3moe_forward_timed.argtypes = [P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z, P]
     L.hy3moe_forward_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z]
     L.hy3moe_quantize_rows_e4m3.argtypes = [P, I, I, P, P, S]
     L.hy3moe_status_string.argtypes = [I]
@@ -135,9 +136,15 @@ def permute(topk_idx, E, workspace=None):
     return counts, offsets, row_of, token_of
 
 
+STAGES = ("router", "dispatch", "gate_up", "down", "combine")
+
+
 def forward(x, W_gate, W_gate_up, W_down, k, scale, bias=None, out=None, workspace=None,
-            return_routing=False):
-    """hy3moe_forward: returns out fp32 [T,d] (and (idx, w) if return_routing)."""
+            return_routing=False, stage_events=None):
+    """hy3moe_forward: returns out fp32 [T,d] (and (idx, w) if return_routing).
+
+    stage_events: optional list of 6 torch.cuda.Event (enable_timing=True);
+    hy3moe_forward_timed records them around the five stages (STAGES)."""
     T, d = x.shape
     E = W_gate.shape[0]
     F = W_down.shape[2]
@@ -156,11 +163,19 @@ def forward(x, W_gate, W_gate_up, W_down, k, scale, bias=None, out=None, workspa
         w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = alloc_workspace(T, d, E, k, F, device=x.device) if T else None
-    _check(lib().hy3moe_forward(_ptr(x), _ptr(W_gate), _ptr(W_gate_up), _ptr(W_down), _ptr(out),
-                                T, d, E, k, F, float(scale), _stream(), _ptr(bias), _ptr(idx),
-                                _ptr(w), _ptr(workspace),
-                                0 if workspace is None else workspace.numel()),
-           "hy3moe_forward")
+    args = (_ptr(x), _ptr(W_gate), _ptr(W_gate_up), _ptr(W_down), _ptr(out), T, d, E, k, F,
+            float(scale), _stream(), _ptr(bias), _ptr(idx), _ptr(w), _ptr(workspace),
+            0 if workspace is None else workspace.numel())
+    if stage_events is None:
+        _check(lib().hy3moe_forward(*args), "hy3moe_forward")
+    else:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events: need 6 events")
+        for ev in stage_events:
+            if not ev.cuda_event:       # torch creates the hipEvent on first record
+                ev.record()
+        arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(ev.cuda_event) for ev in stage_events])
+        _check(lib().hy3moe_forward_timed(*args, arr), "hy3moe_forward_timed")
     return (out, idx, w) if return_routing else out
 
 

@@ -111,6 +111,21 @@ def test_all_tokens_one_expert(gpu_lib):
     assert torch.all(idx[:, 0] == 5)
 
 
+@pytest.mark.parametrize("T,E,k,hot", [(64, 192, 8, True), (96, 192, 8, False), (16, 32, 8, True),
+                                       (3, 40, 5, False)])
+def test_decode_path_shapes(gpu_lib, T, E, k, hot):
+    """Small batches (T*k <= 4E) take the weight-streaming kernels; a hot
+    expert with more than 16 rows exercises their multi-pass loop."""
+    c = dict(inputs.CONFIGS[0], T=T, E=E, k=k, F=128, seed=200 + T)
+    inp = _cpu_case(c)
+    if hot:
+        b = torch.zeros(E, dtype=torch.float32)
+        b[E - 1] = 30.0
+        inp["bias"] = b
+    stats, _, idx = _full_compare(inp)
+    print(T, E, k, hot, stats)
+
+
 def test_empty_batch(gpu_lib):
     from sparse_moe_layer_wave_amd import hy3moe as hy
     inp = _to("cuda", _cpu_case(0, T=0))
