@@ -9,7 +9,6 @@
 namespace {
 
 using hy3::Layout;
-using hy3::Tile;
 
 thread_local int g_last_hip_error = 0;
 
@@ -25,10 +24,7 @@ Layout make_layout(int T, int d, int E, int k, int F, int dtype) {
     Layout L{};
     const size_t Tk = static_cast<size_t>(T) * k;
     L.nb = (T + hy3::kRouteBlock - 1) / hy3::kRouteBlock;
-    const int bm_gu = dtype == HY3MOE_WEIGHTS_FP8_E4M3 ? hy3::gemm_bm_fp8(T, k) : hy3::gemm_bm_gate_up(T, k);
-    const int bm_dn = dtype == HY3MOE_WEIGHTS_FP8_E4M3 ? hy3::gemm_bm_fp8(T, k) : hy3::gemm_bm_down(T, k);
-    L.max_tiles_gu = static_cast<int>(Tk / bm_gu) + E;
-    L.max_tiles_dn = static_cast<int>(Tk / bm_dn) + E;
+    L.max_mtiles = static_cast<int>(Tk / hy3::prefill_bm()) + E;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -41,10 +37,7 @@ Layout make_layout(int T, int d, int E, int k, int F, int dtype) {
     L.blk_base = take(static_cast<size_t>(E) * L.nb * sizeof(int32_t));
     L.counts = take(static_cast<size_t>(E) * sizeof(int32_t));
     L.offsets = take(static_cast<size_t>(E + 1) * sizeof(int32_t));
-    L.tiles_gu = take(static_cast<size_t>(L.max_tiles_gu) * sizeof(Tile));
-    L.ntiles_gu = take(sizeof(int32_t));
-    L.tiles_dn = take(static_cast<size_t>(L.max_tiles_dn) * sizeof(Tile));
-    L.ntiles_dn = take(sizeof(int32_t));
+    L.tile_off = take(static_cast<size_t>(E + 1) * sizeof(int32_t));
     L.idx = take(Tk * sizeof(int32_t));
     L.w = take(Tk * sizeof(float));
     L.row_of = take(Tk * sizeof(int32_t));
@@ -138,11 +131,8 @@ int hy3moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts
     if (e != hipSuccess) return hip_status(e);
     e = hy3::launch_dispatch(topk_idx, T, E, k, L.nb, blk_counts,
                              reinterpret_cast<int32_t*>(ws + L.blk_base), counts, offsets,
-                             reinterpret_cast<Tile*>(ws + L.tiles_gu),
-                             reinterpret_cast<int32_t*>(ws + L.ntiles_gu), hy3::gemm_bm_gate_up(T, k),
-                             reinterpret_cast<Tile*>(ws + L.tiles_dn),
-                             reinterpret_cast<int32_t*>(ws + L.ntiles_dn), hy3::gemm_bm_down(T, k),
-                             row_of, token_of, s);
+                             reinterpret_cast<int32_t*>(ws + L.tile_off), hy3::prefill_bm(), row_of,
+                             token_of, s);
     return hip_status(e);
 }
 
@@ -171,10 +161,7 @@ static int forward_bf16(const uint16_t* x, const float* W_gate, const uint16_t* 
     float* w = topk_w ? topk_w : reinterpret_cast<float*>(ws + L.w);
     int32_t* blk_counts = reinterpret_cast<int32_t*>(ws + L.blk_counts);
     int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
-    Tile* tiles_gu = reinterpret_cast<Tile*>(ws + L.tiles_gu);
-    Tile* tiles_dn = reinterpret_cast<Tile*>(ws + L.tiles_dn);
-    int32_t* ntiles_gu = reinterpret_cast<int32_t*>(ws + L.ntiles_gu);
-    int32_t* ntiles_dn = reinterpret_cast<int32_t*>(ws + L.ntiles_dn);
+    int32_t* tile_off = reinterpret_cast<int32_t*>(ws + L.tile_off);
     int32_t* row_of = reinterpret_cast<int32_t*>(ws + L.row_of);
     int32_t* tok_of = reinterpret_cast<int32_t*>(ws + L.tok_of);
     uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
@@ -189,24 +176,22 @@ static int forward_bf16(const uint16_t* x, const float* W_gate, const uint16_t* 
     if (e != hipSuccess) return hip_status(e);
     e = hy3::launch_dispatch(idx, T, E, k, L.nb, blk_counts,
                              reinterpret_cast<int32_t*>(ws + L.blk_base),
-                             reinterpret_cast<int32_t*>(ws + L.counts), offsets, tiles_gu, ntiles_gu,
-                             hy3::gemm_bm_gate_up(T, k), tiles_dn, ntiles_dn,
-                             hy3::gemm_bm_down(T, k), row_of, tok_of, s);
+                             reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
+                             hy3::prefill_bm(), row_of, tok_of, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
     if (e != hipSuccess) return hip_status(e);
     const bool decode = hy3::use_decode_path(T, d, E, k);
     if (decode)
         e = hy3::launch_gate_up_decode(x, tok_of, W_gate_up, offsets, h, E, d, d_ff, s);
     else
-        e = hy3::launch_gate_up_bf16(x, tok_of, W_gate_up, tiles_gu, ntiles_gu, L.max_tiles_gu,
-                                     offsets, h, T, d, d_ff, k, s);
+        e = hy3::launch_gate_up_prefill(x, tok_of, W_gate_up, offsets, tile_off, L.max_mtiles, h, E,
+                                        d, d_ff, s);
     if (e == hipSuccess) e = mark(ev, 3, s);
     if (e != hipSuccess) return hip_status(e);
     if (decode)
         e = hy3::launch_down_decode(h, W_down, offsets, y, E, d, d_ff, s);
     else
-        e = hy3::launch_down_bf16(h, W_down, tiles_dn, ntiles_dn, L.max_tiles_dn, offsets, y, T, d,
-                                  d_ff, k, s);
+        e = hy3::launch_down_prefill(h, W_down, offsets, tile_off, L.max_mtiles, y, E, d, d_ff, s);
     if (e == hipSuccess) e = mark(ev, 4, s);
     if (e != hipSuccess) return hip_status(e);
     e = hy3::launch_combine(y, row_of, w, out, T, d, k, s);

@@ -9,7 +9,7 @@
 //   k_block_scan   one workgroup per expert: exclusive scan of its per-block
 //                  counts -> base of each block inside the expert; total count;
 //   k_offsets      one workgroup: exclusive scan of the counts -> offsets, and
-//                  the M-tile lists of both expert GEMMs;
+//                  of the per-expert M-tile counts of the grouped GEMMs;
 //   k_scatter      one workgroup per routing block: rebuilds the token masks
 //                  and gives pair (t, j) of expert e the row
 //                  offsets[e] + base[e, block] + #(tokens of the block before t
@@ -71,46 +71,35 @@ __global__ __launch_bounds__(256) void k_block_scan(const int32_t* __restrict__ 
     if (threadIdx.x == 0) counts[e] = running;
 }
 
-// One workgroup of 1024 threads; E <= 1024.
+// One workgroup of 1024 threads; E <= 1024.  offsets = exclusive scan of the
+// counts; tile_off = exclusive scan of ceil(count / bm), the M-tiles of the
+// grouped GEMMs.
 __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ counts, int E,
                                                   int32_t* __restrict__ offsets,
-                                                  Tile* __restrict__ tiles_gu,
-                                                  int32_t* __restrict__ ntiles_gu, int bm_gu,
-                                                  Tile* __restrict__ tiles_dn,
-                                                  int32_t* __restrict__ ntiles_dn, int bm_dn) {
+                                                  int32_t* __restrict__ tile_off, int bm) {
     __shared__ int s_cnt[1024];
-    __shared__ int s_t1[1024];
-    __shared__ int s_t2[1024];
+    __shared__ int s_til[1024];
     const int tid = threadIdx.x;
     const int c = tid < E ? counts[tid] : 0;
+    const int nt = (c + bm - 1) / bm;
     s_cnt[tid] = c;
-    s_t1[tid] = (c + bm_gu - 1) / bm_gu;
-    s_t2[tid] = (c + bm_dn - 1) / bm_dn;
+    s_til[tid] = nt;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
         const int a0 = tid >= off ? s_cnt[tid - off] : 0;
-        const int a1 = tid >= off ? s_t1[tid - off] : 0;
-        const int a2 = tid >= off ? s_t2[tid - off] : 0;
+        const int a1 = tid >= off ? s_til[tid - off] : 0;
         __syncthreads();
         s_cnt[tid] += a0;
-        s_t1[tid] += a1;
-        s_t2[tid] += a2;
+        s_til[tid] += a1;
         __syncthreads();
     }
-    const int off_e = s_cnt[tid] - c;
-    if (tid < E) offsets[tid] = off_e;
+    if (tid < E) {
+        offsets[tid] = s_cnt[tid] - c;
+        tile_off[tid] = s_til[tid] - nt;
+    }
     if (tid == 0) {
         offsets[E] = s_cnt[1023];
-        *ntiles_gu = s_t1[1023];
-        *ntiles_dn = s_t2[1023];
-    }
-    if (tid < E) {
-        const int n1 = (c + bm_gu - 1) / bm_gu;
-        const int start1 = s_t1[tid] - n1;
-        for (int i = 0; i < n1; ++i) tiles_gu[start1 + i] = Tile{tid, off_e + i * bm_gu};
-        const int n2 = (c + bm_dn - 1) / bm_dn;
-        const int start2 = s_t2[tid] - n2;
-        for (int i = 0; i < n2; ++i) tiles_dn[start2 + i] = Tile{tid, off_e + i * bm_dn};
+        tile_off[E] = s_til[1023];
     }
 }
 
@@ -172,12 +161,10 @@ hipError_t launch_block_counts(const int32_t* idx, int T, int E, int k, int nb,
 
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
                            const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,
-                           int32_t* offsets, Tile* tiles_gu, int32_t* ntiles_gu, int bm_gu,
-                           Tile* tiles_dn, int32_t* ntiles_dn, int bm_dn, int32_t* row_of,
+                           int32_t* offsets, int32_t* tile_off, int bm, int32_t* row_of,
                            int32_t* tok_of, hipStream_t s) {
     hipLaunchKernelGGL(k_block_scan, dim3(E), dim3(256), 0, s, blk_counts, blk_base, counts, nb);
-    hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, s, counts, E, offsets, tiles_gu,
-                       ntiles_gu, bm_gu, tiles_dn, ntiles_dn, bm_dn);
+    hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, s, counts, E, offsets, tile_off, bm);
     hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(256), 0, s, idx, T, E, k, nb, blk_base, offsets,
                        row_of, tok_of);
     return hipGetLastError();

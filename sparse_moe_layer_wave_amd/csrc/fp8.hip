@@ -62,8 +62,6 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_bf16(const uint16_t* _
 
 }  // namespace
 
-int gemm_bm_fp8(int, int) { return 64; }
-
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,
                              hipStream_t st) {
     hipLaunchKernelGGL(k_quant_rows_bf16, dim3(rows), dim3(kQThreads), 0, st, x, cols, q, s);

@@ -17,13 +17,6 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 // Tokens per routing block: one bit per token in a 64-bit LDS mask.
 constexpr int kRouteBlock = 64;
 
-// One M-tile of a grouped GEMM: expert and first row (in expert-contiguous
-// row order); the tile ends at min(row0 + BM, offsets[expert + 1]).
-struct Tile {
-    int expert;
-    int row0;
-};
-
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
@@ -42,12 +35,11 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 
 // Workspace carving, computed identically on the host for every entry point.
 struct Layout {
-    size_t scores, blk_counts, blk_base, counts, offsets, tiles_gu, ntiles_gu, tiles_dn,
-        ntiles_dn, idx, w, row_of, tok_of, h, y, xq, xs, hq, hs, total;
+    size_t scores, blk_counts, blk_base, counts, offsets, tile_off, idx, w, row_of, tok_of, h, y,
+        xq, xs, hq, hs, total;
     int nb;              // routing blocks
     int nsplit;          // router d-chunks
-    int max_tiles_gu;    // upper bound on M-tiles of the gate_up GEMM
-    int max_tiles_dn;
+    int max_mtiles;      // upper bound on M-tiles of the grouped GEMMs
 };
 
 // ---- launchers (each returns hipGetLastError() after enqueueing) ----
@@ -59,20 +51,17 @@ hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bi
 
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
                            const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,
-                           int32_t* offsets, Tile* tiles_gu, int32_t* ntiles_gu, int bm_gu,
-                           Tile* tiles_dn, int32_t* ntiles_dn, int bm_dn, int32_t* row_of,
+                           int32_t* offsets, int32_t* tile_off, int bm, int32_t* row_of,
                            int32_t* tok_of, hipStream_t s);
 
-// bf16 expert GEMMs; the M-tile size they need in the tile lists
-int gemm_bm_gate_up(int T, int k);
-int gemm_bm_down(int T, int k);
-hipError_t launch_gate_up_bf16(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
-                               const Tile* tiles, const int32_t* ntiles, int max_tiles,
-                               const int32_t* offsets, uint16_t* h, int T, int d, int F, int k,
-                               hipStream_t s);
-hipError_t launch_down_bf16(const uint16_t* h, const uint16_t* W_dn, const Tile* tiles,
-                            const int32_t* ntiles, int max_tiles, const int32_t* offsets,
-                            uint16_t* y, int T, int d, int F, int k, hipStream_t s);
+// prefill-sized batches: MFMA grouped GEMMs over M-tiles of prefill_bm() rows
+int prefill_bm();
+hipError_t launch_gate_up_prefill(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
+                                  const int32_t* offsets, const int32_t* tile_off, int max_mtiles,
+                                  uint16_t* h, int E, int d, int F, hipStream_t s);
+hipError_t launch_down_prefill(const uint16_t* h, const uint16_t* W_dn, const int32_t* offsets,
+                               const int32_t* tile_off, int max_mtiles, uint16_t* y, int E, int d,
+                               int F, hipStream_t s);
 
 // decode-sized batches: weight streaming, one workgroup per (expert, weight slice)
 bool use_decode_path(int T, int d, int E, int k);
@@ -109,6 +98,5 @@ hipError_t launch_block_counts(const int32_t* idx, int T, int E, int k, int nb,
                                int32_t* blk_counts, hipStream_t s);
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,
                              hipStream_t st);
-int gemm_bm_fp8(int T, int k);
 
 }  // namespace hy3
