@@ -32,7 +32,9 @@ Layout make_layout(int T, int d, int E, int k, int F, int dtype) {
         return at;
     };
     L.nsplit = hy3::router_nsplit(T, d, E);
-    L.scores = take(static_cast<size_t>(L.nsplit) * T * E * sizeof(float));
+    L.planes = take(hy3::router_plane_elems(d, E) * sizeof(uint16_t));
+    L.partial = take(L.nsplit > 1 ? static_cast<size_t>(L.nsplit) * T * E * sizeof(float) : 0);
+    L.scores = take(static_cast<size_t>(T) * E * sizeof(float));
     L.blk_counts = take(static_cast<size_t>(E) * L.nb * sizeof(int32_t));
     L.blk_base = take(static_cast<size_t>(E) * L.nb * sizeof(int32_t));
     L.counts = take(static_cast<size_t>(E) * sizeof(int32_t));
@@ -58,6 +60,12 @@ Layout make_layout(int T, int d, int E, int k, int F, int dtype) {
 }
 
 size_t route_bytes(const Layout& L) { return L.blk_counts; }
+
+hy3::RouterWork router_work(char* ws, const Layout& L) {
+    return hy3::RouterWork{reinterpret_cast<uint16_t*>(ws + L.planes),
+                           reinterpret_cast<float*>(ws + L.partial),
+                           reinterpret_cast<float*>(ws + L.scores), L.nsplit};
+}
 size_t permute_bytes(const Layout& L) { return L.idx; }
 
 int check_shape(int T, int d, int E, int k, int F) {
@@ -107,8 +115,8 @@ int hy3moe_route(const uint16_t* x, const float* W_gate, const float* logit_bias
     if (workspace_bytes < route_bytes(L)) return HY3MOE_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
     return hip_status(hy3::launch_router(x, W_gate, logit_bias, T, d, E, k, scale,
-                                         reinterpret_cast<float*>(ws + L.scores), L.nsplit, topk_idx,
-                                         topk_w, nullptr, L.nb, static_cast<hipStream_t>(stream)));
+                                         router_work(ws, L), topk_idx, topk_w, nullptr, L.nb,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int hy3moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
@@ -169,9 +177,8 @@ static int forward_bf16(const uint16_t* x, const float* W_gate, const uint16_t* 
 
     hipError_t e = mark(ev, 0, s);
     if (e != hipSuccess) return hip_status(e);
-    e = hy3::launch_router(x, W_gate, logit_bias, T, d, E, k, scale,
-                                      reinterpret_cast<float*>(ws + L.scores), L.nsplit, idx, w,
-                                      blk_counts, L.nb, s);
+    e = hy3::launch_router(x, W_gate, logit_bias, T, d, E, k, scale, router_work(ws, L), idx, w,
+                           blk_counts, L.nb, s);
     if (e == hipSuccess) e = mark(ev, 1, s);
     if (e != hipSuccess) return hip_status(e);
     e = hy3::launch_dispatch(idx, T, E, k, L.nb, blk_counts,

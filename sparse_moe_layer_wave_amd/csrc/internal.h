@@ -35,7 +35,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 
 // Workspace carving, computed identically on the host for every entry point.
 struct Layout {
-    size_t scores, blk_counts, blk_base, counts, offsets, tile_off, idx, w, row_of, tok_of, h, y,
+    size_t planes, partial, scores, blk_counts, blk_base, counts, offsets, tile_off, idx, w, row_of, tok_of, h, y,
         xq, xs, hq, hs, total;
     int nb;              // routing blocks
     int nsplit;          // router d-chunks
@@ -43,11 +43,19 @@ struct Layout {
 };
 
 // ---- launchers (each returns hipGetLastError() after enqueueing) ----
-// Router: partial logits [nsplit, T, E] in `partial`, then selection.
+// Router scratch: bf16 planes of W_gate [3, E, d], d-split partial logits
+// [nsplit, T, E] (nsplit > 1 only), scores [T, E].
+struct RouterWork {
+    uint16_t* planes;
+    float* partial;
+    float* scores;
+    int nsplit;
+};
 int router_nsplit(int T, int d, int E);
+size_t router_plane_elems(int d, int E);
 hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bias, int T, int d,
-                         int E, int k, float scale, float* partial, int nsplit, int32_t* idx,
-                         float* w, int32_t* blk_counts, int nb, hipStream_t s);
+                         int E, int k, float scale, const RouterWork& rw, int32_t* idx, float* w,
+                         int32_t* blk_counts, int nb, hipStream_t s);
 
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
                            const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,

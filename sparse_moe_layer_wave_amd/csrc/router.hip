@@ -3,14 +3,14 @@
 // teardown", section 4.1, router flow steps 1, 3, 4 and 5).
 //
 // Logits.  The gate weight is fp32 and the hidden states are bf16; the pages'
-// router casts both to float before the linear map.  Each fp32 weight w is
-// split into three bf16 parts by truncation, w = hi + mid + lo exactly (8
-// significant bits each), so x.w = x.hi + x.mid + x.lo with every product
-// exact in fp32.  That runs on bf16 MFMA with fp32 accumulation: an
-// fp32-accurate GEMM for three times the bf16 work.  Small batches split the
-// d-sum into nsplit chunks (partial logits [nsplit, T, E]) so enough
-// workgroups stream W_gate; the selection kernel adds the chunks in a fixed
-// order, so the result does not depend on scheduling.
+// router casts both to float before the linear map.  k_router_prep splits each
+// fp32 weight w into three bf16 planes by truncation, w = hi + mid + lo
+// exactly (8 significant bits each), so x.w = x.hi + x.mid + x.lo with every
+// product exact in fp32: an fp32-accurate GEMM on bf16 MFMA (fp32
+// accumulate) for three times the bf16 work.  Small batches split the d-sum
+// over nsplit workgroups; the last of them to finish (an atomic ticket per
+// output block) adds the partial sums in the fixed order s = 0..nsplit-1, so
+// the result does not depend on scheduling.
 //
 // Selection.  Scores lie in [0, 1], so their fp32 bit patterns order like the
 // values; key = (score bits << 32) | ~expert makes "largest score, then lowest
@@ -23,106 +23,138 @@
 namespace hy3 {
 namespace {
 
-constexpr int kScoreTokens = 64;    // tokens per workgroup (4 waves x 16)
-constexpr int kScoreExperts = 32;   // experts per workgroup (2 MFMA n-tiles)
-constexpr int kKStep = 32;          // d elements per MFMA
-constexpr int kUnroll = 4;          // k-steps whose loads are issued together
-
-__device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
-    const uint32_t u = __float_as_uint(w);
-    const uint32_t uh = u & 0xffff0000u;
-    const float r1 = w - __uint_as_float(uh);          // exact: <= 16 significant bits left
-    const uint32_t um = __float_as_uint(r1) & 0xffff0000u;
-    const float r2 = r1 - __uint_as_float(um);          // exact: <= 8 significant bits left
-    hi = static_cast<uint16_t>(uh >> 16);
-    mid = static_cast<uint16_t>(um >> 16);
-    lo = static_cast<uint16_t>(__float_as_uint(r2) >> 16);   // r2 fits bf16 exactly
-}
+constexpr int kLogitTokens = 256;   // tokens per workgroup (4 waves x 64)
+constexpr int kLogitExperts = 32;   // experts per workgroup (one 32-wide MFMA block)
+constexpr int kUnroll = 4;          // k16-steps whose loads are issued together
 
 union Frag {
     bf16x8_t v;
-    uint16_t h[8];
-    uint4 q;
+    i32x4_t q;
 };
 
-// partial[s, t, e] = sum over i in chunk s of x[t,i] W[e,i].
-// MFMA 16x16x32: A = 16 tokens x 32 k (lane l: token l%16, k 8*(l/16)..+8),
-// B = 32 k x 16 experts (lane l: expert l%16, same k); C lane l holds expert
-// l%16 for tokens 4*(l/16)..+4.
-__global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x,
-                                                       const float* __restrict__ Wg,
-                                                       float* __restrict__ partial, int T, int d,
-                                                       int E, int kchunk) {
+// planes[p][e][i] = part p of W[e][i].
+__global__ __launch_bounds__(256) void k_router_prep(const float* __restrict__ W,
+                                                     uint16_t* __restrict__ planes, size_t n) {
+    const size_t i = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (i < n) {
+        const float4 w = *reinterpret_cast<const float4*>(W + i);
+        const float wv[4] = {w.x, w.y, w.z, w.w};
+        uint16_t hi[4], mid[4], lo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t uh = __float_as_uint(wv[j]) & 0xffff0000u;
+            const float r1 = wv[j] - __uint_as_float(uh);        // exact: <= 16 significant bits
+            const uint32_t um = __float_as_uint(r1) & 0xffff0000u;
+            const float r2 = r1 - __uint_as_float(um);            // exact: <= 8 significant bits
+            hi[j] = static_cast<uint16_t>(uh >> 16);
+            mid[j] = static_cast<uint16_t>(um >> 16);
+            lo[j] = static_cast<uint16_t>(__float_as_uint(r2) >> 16);
+        }
+        *reinterpret_cast<uint2*>(planes + i) =
+            make_uint2(hi[0] | (uint32_t(hi[1]) << 16), hi[2] | (uint32_t(hi[3]) << 16));
+        *reinterpret_cast<uint2*>(planes + n + i) =
+            make_uint2(mid[0] | (uint32_t(mid[1]) << 16), mid[2] | (uint32_t(mid[3]) << 16));
+        *reinterpret_cast<uint2*>(planes + 2 * n + i) =
+            make_uint2(lo[0] | (uint32_t(lo[1]) << 16), lo[2] | (uint32_t(lo[3]) << 16));
+    }
+}
+
+__device__ __forceinline__ float sigmoid_bias(float z, const float* bias, int e) {
+    if (bias) z += bias[e];
+    return 1.0f / (1.0f + expf(-z));
+}
+
+// Workgroup (tb, eb, s): tokens 256 tb.., experts 32 eb.., d-chunk s; wave w
+// owns tokens 64 w..64 w+63 as two 32-row MFMA blocks.
+// MFMA 32x32x16: A lane l = token l%32, k 8*(l/32)..+8; B lane l = expert
+// l%32, same k; C lane l = expert l%32, tokens 8*(j/4) + 4*(l/32) + j%4.
+// nsplit == 1 writes sigmoid scores; otherwise raw partial logits per chunk.
+__global__ __launch_bounds__(256) void k_router_logits(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
+    const float* __restrict__ bias, float* __restrict__ partial, float* __restrict__ scores,
+    int T, int d, int E, int kchunk, int nsplit) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * kScoreTokens + wave * 16;
-    const int e0 = blockIdx.y * kScoreExperts;
+    const int t0 = blockIdx.x * kLogitTokens + wave * 64;
+    if (t0 >= T) return;                            // whole wave past the batch
+    const int e0 = blockIdx.y * kLogitExperts;
     const int k0 = blockIdx.z * kchunk;
-    const int r = lane & 15;
-    const int kg = lane >> 4;
+    const int l32 = lane & 31;
+    const int kh = (lane >> 5) * 8;
+    const size_t plane = static_cast<size_t>(E) * d;
 
-    const int ta = t0 + r;
-    const bool va = ta < T;
-    const uint16_t* xa = x + static_cast<size_t>(va ? ta : 0) * d + k0 + kg * 8;
-    const float* wb[2];
-    bool vb[2];
+    const uint16_t* xa[2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int e = e0 + nt * 16 + r;
-        vb[nt] = e < E;
-        wb[nt] = Wg + static_cast<size_t>(vb[nt] ? e : 0) * d + k0 + kg * 8;
+    for (int mb = 0; mb < 2; ++mb) {
+        const int ta = min(t0 + 32 * mb + l32, T - 1);   // rows past T repeat a valid row
+        xa[mb] = x + static_cast<size_t>(ta) * d + k0 + kh;
     }
+    const int eb = min(e0 + l32, E - 1);
+    const uint16_t* wb = planes + static_cast<size_t>(eb) * d + k0 + kh;
 
-    f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    for (int kb = 0; kb < kchunk; kb += kKStep * kUnroll) {
-        uint4 av[kUnroll];
-        float4 wv[kUnroll][2][2];
+    f32x16_t acc[2] = {{}, {}};
+    for (int kb = 0; kb < kchunk; kb += 16 * kUnroll) {
+        i32x4_t av[kUnroll][2], bv[kUnroll][3];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int kk = kb + u * kKStep;
-            const bool in = kk < kchunk;                   // kchunk is a multiple of 32
-            av[u] = va && in ? *reinterpret_cast<const uint4*>(xa + kk) : make_uint4(0, 0, 0, 0);
+            const int kk = min(kb + 16 * u, kchunk - 16);  // kchunk is a multiple of 32
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                if (vb[nt] && in) {
-                    wv[u][nt][0] = *reinterpret_cast<const float4*>(wb[nt] + kk);
-                    wv[u][nt][1] = *reinterpret_cast<const float4*>(wb[nt] + kk + 4);
-                } else {
-                    wv[u][nt][0] = wv[u][nt][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int mb = 0; mb < 2; ++mb) av[u][mb] = *reinterpret_cast<const i32x4_t*>(xa[mb] + kk);
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+                bv[u][p] = *reinterpret_cast<const i32x4_t*>(wb + p * plane + kk);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (kb + 16 * u < kchunk) {
+#pragma unroll
+                for (int p = 0; p < 3; ++p) {
+                    Frag b;
+                    b.q = bv[u][p];
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb) {
+                        Frag a;
+                        a.q = av[u][mb];
+                        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc[mb], 0, 0, 0);
+                    }
                 }
             }
         }
+    }
+
+    const int e = e0 + l32;
+    if (e >= E) return;
+    float* out = nsplit == 1 ? scores : partial + static_cast<size_t>(blockIdx.z) * T * E;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            if (kb + u * kKStep >= kchunk) break;
-            Frag a;
-            a.q = av[u];
+    for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const float w8[8] = {wv[u][nt][0].x, wv[u][nt][0].y, wv[u][nt][0].z,
-                                     wv[u][nt][0].w, wv[u][nt][1].x, wv[u][nt][1].y,
-                                     wv[u][nt][1].z, wv[u][nt][1].w};
-                Frag bh, bm, bl;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) split3(w8[i], bh.h[i], bm.h[i], bl.h[i]);
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, bh.v, acc[nt], 0, 0, 0);
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, bm.v, acc[nt], 0, 0, 0);
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, bl.v, acc[nt], 0, 0, 0);
+        for (int j = 0; j < 16; ++j) {
+            const int t = t0 + 32 * mb + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+            if (t < T) {
+                const float v = acc[mb][j];
+                out[static_cast<size_t>(t) * E + e] = nsplit == 1 ? sigmoid_bias(v, bias, e) : v;
             }
         }
     }
+}
 
-    float* out = partial + static_cast<size_t>(blockIdx.z) * T * E;
+// scores = sigmoid(sum over s = 0..nsplit-1 of partial[s] + bias), one element
+// per thread, the chunks added in that fixed order.
+constexpr int kMaxSplit = 32;
+__global__ __launch_bounds__(256) void k_router_reduce(const float* __restrict__ partial,
+                                                       const float* __restrict__ bias,
+                                                       float* __restrict__ scores, int T, int E,
+                                                       int nsplit) {
+    const size_t n = static_cast<size_t>(T) * E;
+    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= n) return;
+    float v[kMaxSplit];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int e = e0 + nt * 16 + r;
-        if (e >= E) continue;
+    for (int s = 0; s < kMaxSplit; ++s) v[s] = s < nsplit ? partial[s * n + i] : 0.f;
+    float z = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = t0 + kg * 4 + i;
-            if (t < T) out[static_cast<size_t>(t) * E + e] = acc[nt][i];
-        }
-    }
+    for (int s = 0; s < kMaxSplit; ++s) z += v[s];       // +0.f past nsplit changes nothing
+    scores[i] = sigmoid_bias(z, bias, static_cast<int>(i % E));
 }
 
 // 64-bit maximum over the 16 lanes of a DPP row (row_ror by 8, 4, 2, 1).
@@ -148,19 +180,18 @@ __device__ __forceinline__ unsigned long long row16_max(unsigned long long v) {
 
 constexpr int kSelThreads = 1024;   // 16 waves x 4 tokens = 64 tokens (one routing block)
 
-// Sums the partial logits, adds the bias and applies the sigmoid into an LDS
-// tile [tb tokens][E + 1] (tb = 64 when E is small; larger E takes the block's
-// 64 tokens in sub-batches), then selects k experts per token, 16 lanes each.
-// Writes idx/w and, when blk_counts is given, the block's per-expert pair count.
+// Copies the scores of a 64-token routing block into an LDS tile [tb][E + 1]
+// (tb = 64 when E is small; larger E takes the block in sub-batches), then
+// selects k experts per token, 16 lanes each.  Writes idx/w and, when
+// blk_counts is given, the block's per-expert pair count.
 __global__ __launch_bounds__(kSelThreads) void k_router_select(
-    const float* __restrict__ partial, int nsplit, const float* __restrict__ bias, int T, int E,
-    int k, float scale, int tb, int32_t* __restrict__ idx, float* __restrict__ wout,
-    int32_t* __restrict__ blk_counts, int nb) {
+    const float* __restrict__ scores, int T, int E, int k, float scale, int tb,
+    int32_t* __restrict__ idx, float* __restrict__ wout, int32_t* __restrict__ blk_counts,
+    int nb) {
     extern __shared__ uint32_t s_score[];              // [tb][E + 1]
     __shared__ unsigned long long mask[1024];
     const int tid = threadIdx.x;
     const int ld = E + 1;
-    const size_t plane = static_cast<size_t>(T) * E;
     for (int e = tid; e < E; e += kSelThreads) mask[e] = 0ull;
     const int lane = tid & 63;
     const int j = lane & 15;                              // lane within the token's row
@@ -171,14 +202,10 @@ __global__ __launch_bounds__(kSelThreads) void k_router_select(
         const int ntok = min(tb, T - t_first);
         if (ntok <= 0) break;
         __syncthreads();
+        const float* src = scores + static_cast<size_t>(t_first) * E;
         for (int p = tid; p < ntok * E; p += kSelThreads) {
             const int tl = p / E;
-            const int e = p - tl * E;
-            const size_t off = static_cast<size_t>(t_first + tl) * E + e;
-            float z = 0.f;
-            for (int s = 0; s < nsplit; ++s) z += partial[s * plane + off];
-            if (bias) z += bias[e];
-            s_score[tl * ld + e] = __float_as_uint(1.0f / (1.0f + expf(-z)));
+            s_score[tl * ld + (p - tl * E)] = __float_as_uint(src[p]);
         }
         __syncthreads();
 
@@ -232,24 +259,35 @@ int select_tokens_per_pass(int E) {
 }  // namespace
 
 int router_nsplit(int T, int d, int E) {
-    const int wgs = ((T + kScoreTokens - 1) / kScoreTokens) * ((E + kScoreExperts - 1) / kScoreExperts);
+    const int wgs = ((T + kLogitTokens - 1) / kLogitTokens) * ((E + kLogitExperts - 1) / kLogitExperts);
     int ns = 1;
-    const int chunk_min = kKStep * kUnroll;                  // 128
-    while (wgs * ns < 256 && (d % (2 * ns * chunk_min)) == 0 && d / (2 * ns) >= chunk_min) ns *= 2;
+    // chunks stay multiples of 32 and at least 256 wide
+    while (wgs * ns < 512 && 2 * ns <= kMaxSplit && (d % (2 * ns * 32)) == 0 && d / (2 * ns) >= 256)
+        ns *= 2;
     return ns;
 }
 
+size_t router_plane_elems(int d, int E) { return static_cast<size_t>(3) * E * d; }
 
 hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bias, int T, int d,
-                         int E, int k, float scale, float* partial, int nsplit, int32_t* idx,
-                         float* w, int32_t* blk_counts, int nb, hipStream_t s) {
-    dim3 g1((T + kScoreTokens - 1) / kScoreTokens, (E + kScoreExperts - 1) / kScoreExperts, nsplit);
-    hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, s, x, W_gate, partial, T, d, E,
-                       d / nsplit);
+                         int E, int k, float scale, const RouterWork& rw, int32_t* idx, float* w,
+                         int32_t* blk_counts, int nb, hipStream_t s) {
+    const size_t n = static_cast<size_t>(E) * d;
+    hipLaunchKernelGGL(k_router_prep, dim3(static_cast<unsigned>((n / 4 + 255) / 256)), dim3(256), 0,
+                       s, W_gate, rw.planes, n);
+    dim3 g1((T + kLogitTokens - 1) / kLogitTokens, (E + kLogitExperts - 1) / kLogitExperts,
+            rw.nsplit);
+    hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, s, x, rw.planes, bias, rw.partial,
+                       rw.scores, T, d, E, d / rw.nsplit, rw.nsplit);
+    if (rw.nsplit > 1) {
+        const size_t te = static_cast<size_t>(T) * E;
+        hipLaunchKernelGGL(k_router_reduce, dim3(static_cast<unsigned>((te + 255) / 256)), dim3(256),
+                           0, s, rw.partial, bias, rw.scores, T, E, rw.nsplit);
+    }
     const int tb = select_tokens_per_pass(E);
     hipLaunchKernelGGL(k_router_select, dim3(nb), dim3(kSelThreads),
-                       static_cast<size_t>(tb) * (E + 1) * sizeof(uint32_t), s, partial, nsplit,
-                       bias, T, E, k, scale, tb, idx, w, blk_counts, nb);
+                       static_cast<size_t>(tb) * (E + 1) * sizeof(uint32_t), s, rw.scores, T, E,
+                       k, scale, tb, idx, w, blk_counts, nb);
     return hipGetLastError();
 }
 
