@@ -125,15 +125,27 @@ int hy3moe_forward_timed(const uint16_t* x, const float* W_gate,
  *   Wq_down    e4m3 [E, d, d_ff],   s_down    fp32 [E, d]
  * Routing is the fp32 router above.  Each token's x row and each (token, slot)
  * SwiGLU activation row are quantised to e4m3 with one fp32 scale per row, as
- * hy3moe_quantize_rows_e4m3 does; the products run on fp8 MFMA with fp32
- * accumulation and are rescaled by row scale * channel scale.  Other
- * arguments as for hy3moe_forward. */
+ * hy3moe_quantize_rows_e4m3 does (the activation row from its fp32 value);
+ * the products run on fp8 MFMA with fp32 accumulation and are rescaled by row
+ * scale * channel scale; expert outputs are stored as bf16 and combined in
+ * fp32 as in hy3moe_forward.  d and d_ff must be multiples of 128 here
+ * (HY3MOE_ERR_UNSUPPORTED otherwise).  Other arguments as for hy3moe_forward. */
 int hy3moe_forward_fp8(const uint16_t* x, const float* W_gate,
                        const uint8_t* Wq_gate_up, const float* s_gate_up,
                        const uint8_t* Wq_down, const float* s_down, float* out,
                        int T, int d, int E, int k, int d_ff, float scale, void* stream,
                        const float* logit_bias, int32_t* topk_idx, float* topk_w,
                        void* workspace, size_t workspace_bytes);
+
+/* hy3moe_forward_fp8 with the six stage events of hy3moe_forward_timed; the
+ * e4m3 quantisation of x and of the SwiGLU activations falls in the gate_up
+ * stage. */
+int hy3moe_forward_fp8_timed(const uint16_t* x, const float* W_gate,
+                             const uint8_t* Wq_gate_up, const float* s_gate_up,
+                             const uint8_t* Wq_down, const float* s_down, float* out,
+                             int T, int d, int E, int k, int d_ff, float scale, void* stream,
+                             const float* logit_bias, int32_t* topk_idx, float* topk_w,
+                             void* workspace, size_t workspace_bytes, void* const* stage_events);
 
 /* Per-row e4m3 quantisation used by hy3moe_forward_fp8 for x:
  *   amax = max |x[r, :]|;  amax == 0 -> q = 0, s = 1;  otherwise

@@ -47,12 +47,13 @@ Layout make_layout(int T, int d, int E, int k, int F, int dtype) {
     if (dtype == HY3MOE_WEIGHTS_FP8_E4M3) {
         L.h = take(Tk * F * sizeof(float));            // fp32 SwiGLU activations
         L.hq = take(Tk * F);                           // their e4m3 codes
-        L.hs = take(Tk * sizeof(float));               // per-row scale / amax
+        L.hs = take(Tk * sizeof(float));               // per-row scale
+        L.amax = take(Tk * sizeof(uint32_t));          // per-row max |h| (bit pattern)
         L.xq = take(static_cast<size_t>(T) * d);
         L.xs = take(static_cast<size_t>(T) * sizeof(float));
     } else {
         L.h = take(Tk * F * sizeof(uint16_t));
-        L.hq = L.hs = L.xq = L.xs = 0;
+        L.hq = L.hs = L.xq = L.xs = L.amax = 0;
     }
     L.y = take(Tk * d * sizeof(uint16_t));
     L.total = off;
@@ -206,6 +207,54 @@ static int forward_bf16(const uint16_t* x, const float* W_gate, const uint16_t* 
     return hip_status(e);
 }
 
+int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, const float* s_gu,
+                const uint8_t* Wq_dn, const float* s_dn, float* out, int T, int d, int E, int k,
+                int d_ff, float scale, void* stream, const float* logit_bias, int32_t* topk_idx,
+                float* topk_w, void* workspace, const Layout& L, void* const* ev) {
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t Tk = static_cast<size_t>(T) * k;
+    int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + L.idx);
+    float* w = topk_w ? topk_w : reinterpret_cast<float*>(ws + L.w);
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+    int32_t* tile_off = reinterpret_cast<int32_t*>(ws + L.tile_off);
+    int32_t* row_of = reinterpret_cast<int32_t*>(ws + L.row_of);
+    int32_t* tok_of = reinterpret_cast<int32_t*>(ws + L.tok_of);
+    float* h32 = reinterpret_cast<float*>(ws + L.h);
+    uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
+    float* hs = reinterpret_cast<float*>(ws + L.hs);
+    uint32_t* amax = reinterpret_cast<uint32_t*>(ws + L.amax);
+    uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
+    float* xs = reinterpret_cast<float*>(ws + L.xs);
+    uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
+
+    hipError_t e = mark(ev, 0, s);
+    if (e == hipSuccess)
+        e = hy3::launch_router(x, W_gate, logit_bias, T, d, E, k, scale, router_work(ws, L), idx, w,
+                               reinterpret_cast<int32_t*>(ws + L.blk_counts), L.nb, s);
+    if (e == hipSuccess) e = mark(ev, 1, s);
+    if (e == hipSuccess)
+        e = hy3::launch_dispatch(idx, T, E, k, L.nb, reinterpret_cast<int32_t*>(ws + L.blk_counts),
+                                 reinterpret_cast<int32_t*>(ws + L.blk_base),
+                                 reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
+                                 hy3::prefill_bm(), row_of, tok_of, s);
+    if (e == hipSuccess) e = mark(ev, 2, s);
+    if (e == hipSuccess) e = hy3::launch_quant_rows(x, T, d, xq, xs, s);
+    if (e == hipSuccess) e = hy3::launch_fill_u32(amax, Tk, 0u, s);
+    if (e == hipSuccess)
+        e = hy3::launch_gate_up_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, L.max_mtiles,
+                                    h32, amax, E, d, d_ff, s);
+    if (e == hipSuccess) e = hy3::launch_quant_rows_f32(h32, amax, static_cast<int>(Tk), d_ff, hq, hs, s);
+    if (e == hipSuccess) e = mark(ev, 3, s);
+    if (e == hipSuccess)
+        e = hy3::launch_down_fp8(hq, hs, Wq_dn, s_dn, offsets, tile_off, L.max_mtiles, y, E, d, d_ff,
+                                 s);
+    if (e == hipSuccess) e = mark(ev, 4, s);
+    if (e == hipSuccess) e = hy3::launch_combine(y, row_of, w, out, T, d, k, s);
+    if (e == hipSuccess) e = mark(ev, 5, s);
+    return hip_status(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -244,11 +293,34 @@ int hy3moe_forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq
         (logit_bias && !aligned16(logit_bias)) || (topk_idx && !aligned16(topk_idx)) ||
         (topk_w && !aligned16(topk_w)))
         return HY3MOE_ERR_ALIGN;
+    if ((d % 128) != 0 || (d_ff % 128) != 0) return HY3MOE_ERR_UNSUPPORTED;
     const Layout L = make_layout(T, d, E, k, d_ff, HY3MOE_WEIGHTS_FP8_E4M3);
     if (workspace_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
-    (void)scale;
-    (void)stream;
-    return HY3MOE_ERR_UNSUPPORTED;
+    return forward_fp8(x, W_gate, Wq_gate_up, s_gate_up, Wq_down, s_down, out, T, d, E, k, d_ff,
+                       scale, stream, logit_bias, topk_idx, topk_w, workspace, L, nullptr);
+}
+
+int hy3moe_forward_fp8_timed(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gate_up,
+                             const float* s_gate_up, const uint8_t* Wq_down, const float* s_down,
+                             float* out, int T, int d, int E, int k, int d_ff, float scale,
+                             void* stream, const float* logit_bias, int32_t* topk_idx,
+                             float* topk_w, void* workspace, size_t workspace_bytes,
+                             void* const* stage_events) {
+    int st = check_shape(T, d, E, k, d_ff);
+    if (st != HY3MOE_OK) return st;
+    if (T == 0) return HY3MOE_OK;
+    if (!x || !W_gate || !Wq_gate_up || !s_gate_up || !Wq_down || !s_down || !out || !workspace)
+        return HY3MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(W_gate) || !aligned16(Wq_gate_up) || !aligned16(s_gate_up) ||
+        !aligned16(Wq_down) || !aligned16(s_down) || !aligned16(out) || !aligned16(workspace) ||
+        (logit_bias && !aligned16(logit_bias)) || (topk_idx && !aligned16(topk_idx)) ||
+        (topk_w && !aligned16(topk_w)))
+        return HY3MOE_ERR_ALIGN;
+    if ((d % 128) != 0 || (d_ff % 128) != 0) return HY3MOE_ERR_UNSUPPORTED;
+    const Layout L = make_layout(T, d, E, k, d_ff, HY3MOE_WEIGHTS_FP8_E4M3);
+    if (workspace_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
+    return forward_fp8(x, W_gate, Wq_gate_up, s_gate_up, Wq_down, s_down, out, T, d, E, k, d_ff,
+                       scale, stream, logit_bias, topk_idx, topk_w, workspace, L, stage_events);
 }
 
 int hy3moe_quantize_rows_e4m3(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,

@@ -1,5 +1,5 @@
-// FP8 (OCP e4m3) path: per-row activation quantisation and the grouped
-// expert GEMMs on fp8 MFMA.  Formats: "DeepSeek V4-Flash architecture Q&A",
+// FP8 (OCP e4m3) path: per-row activation quantisation (the grouped expert
+// GEMMs on fp8 MFMA are in gemm_prefill.hip).  Formats: "DeepSeek V4-Flash architecture Q&A",
 // Q7.2 (E4M3, range +-448) and Q7.4 (one scale per output channel).
 //
 // Row quantiser: amax = max|v|; amax == 0 -> codes 0, scale 1; otherwise
@@ -60,7 +60,46 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_bf16(const uint16_t* _
     if (threadIdx.x == 0) s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
 }
 
+// h rows (fp32) with their max |h| already reduced into amax (bit patterns):
+// the same quantiser as above, one workgroup per row.
+__global__ __launch_bounds__(kQThreads) void k_quant_rows_f32(const float* __restrict__ h,
+                                                             const uint32_t* __restrict__ amax_bits,
+                                                             int cols, uint8_t* __restrict__ q,
+                                                             float* __restrict__ s) {
+    const size_t row = blockIdx.x;
+    const float amax = __uint_as_float(amax_bits[row]);
+    const float r = amax > 0.f ? 448.0f / amax : 0.f;
+    const float* hr = h + row * cols;
+    for (int c = threadIdx.x * 4; c < cols; c += kQThreads * 4) {
+        const float4 v = *reinterpret_cast<const float4*>(hr + c);
+        const uint32_t packed = static_cast<uint32_t>(f32_to_e4m3(v.x * r)) |
+                                (static_cast<uint32_t>(f32_to_e4m3(v.y * r)) << 8) |
+                                (static_cast<uint32_t>(f32_to_e4m3(v.z * r)) << 16) |
+                                (static_cast<uint32_t>(f32_to_e4m3(v.w * r)) << 24);
+        *reinterpret_cast<uint32_t*>(q + row * cols + c) = packed;
+    }
+    if (threadIdx.x == 0) s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+}
+
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, size_t n, uint32_t v) {
+    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * 256)
+        p[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, int rows, int cols,
+                                 uint8_t* q, float* s, hipStream_t st) {
+    hipLaunchKernelGGL(k_quant_rows_f32, dim3(rows), dim3(kQThreads), 0, st, h, amax_bits, cols, q, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
+    const unsigned blocks = static_cast<unsigned>(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096);
+    hipLaunchKernelGGL(k_fill_u32, dim3(blocks), dim3(256), 0, st, p, n, v);
+    return hipGetLastError();
+}
 
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,
                              hipStream_t st) {

@@ -1,13 +1,23 @@
-// Grouped expert GEMMs for prefill-sized batches on CDNA4 MFMA (bf16 in,
-// fp32 accumulate).  Expert e's rows form M-tiles of 128 rows; each workgroup
-// computes one M-tile against 256 weight rows:
+// Grouped expert GEMMs for prefill-sized batches on CDNA4 MFMA, fp32
+// accumulate, with bf16 or e4m3 operands.  Expert e's rows form M-tiles of 128
+// rows; each workgroup computes one M-tile against 256 weight rows:
 //
 //   gate_up: weight rows = 128 gate rows c0..c0+127 and the matching 128 up
-//            rows F+c0..; writes h[r, c] = bf16(SiLU(G) * U) for 128 columns
-//            ("DeepSeek V4-Flash architecture Q&A", Q4.5: SiLU on the gate
-//            branch; "Tencent Hy3-295B architecture teardown", section 2.3:
-//            the fused gate_up projection);
-//   down:    weight rows = output columns n0..n0+255; writes y[r, n] = bf16.
+//            rows F+c0..; h[r, c] = SiLU(G) * U for 128 columns ("DeepSeek
+//            V4-Flash architecture Q&A", Q4.5: SiLU on the gate branch;
+//            "Tencent Hy3-295B architecture teardown", section 2.3: the fused
+//            gate_up projection).  bf16: h stored as bf16.  e4m3: G and U are
+//            rescaled by the row's activation scale and the channel's weight
+//            scale, h is stored as fp32 and the row's max |h| is folded into
+//            amax[r] (an integer atomic max on the bit pattern of |h|), for
+//            the per-row quantisation of h that follows;
+//   down:    weight rows = output columns n0..n0+255; y[r, n] stored as bf16
+//            (e4m3: rescaled by the row and channel scales first).
+//
+// Both formats use 128-byte K-tiles (64 bf16 or 128 e4m3 values per row), so
+// the LDS layout and the producers are byte-identical; the consumers issue
+// v_mfma_f32_32x32x16_bf16 (4 per K-tile and block) or
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales (2 per K-tile and block).
 //
 // Eight waves with two roles.  Waves 4-7 are producers: they move K-tiles
 // from global memory straight into a 3-stage LDS ring (global_load_lds_dwordx4,
@@ -34,10 +44,12 @@ namespace {
 
 constexpr int BM = 128;
 constexpr int BNW = 256;                   // weight rows per tile
-constexpr int BK = 64;
-constexpr int TILE_A = BM * BK;            // bf16 elements
-constexpr int TILE_B = BNW * BK;
+constexpr int ROWB = 128;                  // bytes of one row of a K-tile
+constexpr int TILE_A = BM * ROWB;          // bytes
+constexpr int TILE_B = BNW * ROWB;
 constexpr int STAGE = TILE_A + TILE_B;     // 48 KB
+
+enum Mode { GU_BF16 = 0, DN_BF16 = 1, GU_FP8 = 2, DN_FP8 = 3 };
 constexpr int kStages = 3;
 constexpr int kXcds = 8;
 constexpr int kChunks = 12;                // 1 KB LDS blocks per producer wave per K-tile
@@ -45,6 +57,11 @@ constexpr int kChunks = 12;                // 1 KB LDS blocks per producer wave 
 union Frag {
     bf16x8_t v;
     i32x4_t q;
+};
+
+union Frag8 {                              // 32 e4m3 values
+    i32x8_t v;
+    i32x4_t q[2];
 };
 
 // Element offset of 16-byte chunk `chunk` of LDS row `row` (64 bf16 = 128 B per
@@ -55,11 +72,11 @@ union Frag {
 __device__ __forceinline__ int lchunk(int row, int chunk) {   // logical <-> physical, an involution
     return chunk ^ (row & 7) ^ ((row >> 3) & 1);
 }
-__device__ __forceinline__ int swz(int row, int chunk) {
-    return row * BK + (lchunk(row, chunk) << 3);
+__device__ __forceinline__ int swz(int row, int chunk) {   // byte offset
+    return row * ROWB + (lchunk(row, chunk) << 4);
 }
 
-__device__ __forceinline__ __attribute__((address_space(3))) void* as_lds(uint16_t* p) {
+__device__ __forceinline__ __attribute__((address_space(3))) void* as_lds(uint8_t* p) {
     return reinterpret_cast<__attribute__((address_space(3))) void*>(
         static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
 }
@@ -77,16 +94,23 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <bool GATE_UP>
+template <int MODE>
 __global__ __launch_bounds__(512, 1) void k_prefill_gemm(
-    const uint16_t* __restrict__ A,        // gate_up: x [T, K]; down: h [rows, K]
+    const uint8_t* __restrict__ A,         // gate_up: x [T, K]; down: h [rows, K]
     const int32_t* __restrict__ tok_of,    // gate_up only
-    const uint16_t* __restrict__ W,        // gate_up: [E, 2N, K]; down: [E, N, K]
+    const uint8_t* __restrict__ W,         // gate_up: [E, 2N, K]; down: [E, N, K]
     const int32_t* __restrict__ offsets,   // [E+1] row offsets
     const int32_t* __restrict__ tile_off,  // [E+1] M-tile offsets (tiles of BM rows)
-    uint16_t* __restrict__ C,              // gate_up: h [rows, N]; down: y [rows, N]
+    uint16_t* __restrict__ C,              // bf16 out: gate_up h [rows, N] (bf16 mode); y [rows, N]
+    const float* __restrict__ a_scale,     // e4m3: per token (gate_up) or per row (down)
+    const float* __restrict__ w_scale,     // e4m3: [E, 2N] (gate_up) or [E, N] (down)
+    float* __restrict__ h32,               // e4m3 gate_up: h [rows, N] fp32
+    uint32_t* __restrict__ amax,           // e4m3 gate_up: [rows] bits of max |h|
     int K, int N, int E, int n_tiles_n) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[kStages * STAGE];
+    constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8;
+    constexpr bool FP8 = MODE == GU_FP8 || MODE == DN_FP8;
+    constexpr int ESZ = FP8 ? 1 : 2;                // bytes per element
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * STAGE];
 
     // XCD-aware remap of the block index onto the logical tile order
     const int G = gridDim.x;                       // a multiple of kXcds
@@ -108,7 +132,8 @@ __global__ __launch_bounds__(512, 1) void k_prefill_gemm(
     const int mt = local - nt * mt_e;
     const int row0 = offsets[e] + mt * BM;
     const int rows = min(BM, offsets[e + 1] - row0);
-    const int nk = K / BK;
+    const size_t kbytes = static_cast<size_t>(K) * ESZ;   // bytes of one A or weight row
+    const int nk = static_cast<int>(kbytes / ROWB);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -122,7 +147,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_gemm(
         // lane i's 16 bytes at block + 16 i: lane i fetches the logical chunk
         // that the swizzle maps to physical chunk i % 8 of row i / 8.
         const int p = wave - 4;
-        const uint16_t* src[kChunks];
+        const uint8_t* src[kChunks];
 #pragma unroll
         for (int j = 0; j < kChunks; ++j) {
             const int b = p * kChunks + j;
@@ -131,7 +156,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_gemm(
                 const int row = 8 * b + (lane >> 3);
                 const int r = min(row, rows - 1);           // rows past the tile end repeat a valid row
                 const size_t arow = GATE_UP ? static_cast<size_t>(tok_of[row0 + r]) : static_cast<size_t>(row0 + r);
-                src[j] = A + arow * K + (lchunk(row, pc) << 3);
+                src[j] = A + arow * kbytes + (lchunk(row, pc) << 4);
             } else {
                 const int row = 8 * (b - 16) + (lane >> 3);  // 0..255
                 int wrow;
@@ -142,8 +167,8 @@ __global__ __launch_bounds__(512, 1) void k_prefill_gemm(
                     wrow = nt * BNW + row;
                     wrow = wrow < N ? wrow : 0;
                 }
-                src[j] = W + static_cast<size_t>(e) * (GATE_UP ? 2 * N : N) * K +
-                         static_cast<size_t>(wrow) * K + (lchunk(row, pc) << 3);
+                src[j] = W + static_cast<size_t>(e) * (GATE_UP ? 2 * N : N) * kbytes +
+                         static_cast<size_t>(wrow) * kbytes + (lchunk(row, pc) << 4);
             }
         }
         // Every iteration issues one K-tile (tiles past the end re-read the last
@@ -151,10 +176,10 @@ __global__ __launch_bounds__(512, 1) void k_prefill_gemm(
         // tile are outstanding and the vmcnt waits below are exact.
 #define HY3_ISSUE(KT, STG)                                                                         \
         {                                                                                          \
-            const int ko_ = (KT) * BK;                                                             \
-            uint16_t* stage_ = lds + (STG) * STAGE + p * kChunks * 512;                            \
+            const int ko_ = (KT) * ROWB;                                                           \
+            uint8_t* stage_ = lds + (STG) * STAGE + p * kChunks * 1024;                            \
             _Pragma("unroll") for (int j = 0; j < kChunks; ++j)                                    \
-                __builtin_amdgcn_global_load_lds(src[j] + ko_, as_lds(stage_ + j * 512), 16, 0, 0); \
+                __builtin_amdgcn_global_load_lds(src[j] + ko_, as_lds(stage_ + j * 1024), 16, 0, 0); \
         }
         HY3_ISSUE(0, 0);
         HY3_ISSUE(min(1, nk - 1), 1);
@@ -199,7 +224,11 @@ __global__ __launch_bounds__(512, 1) void k_prefill_gemm(
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16_t{};
 
     lds_barrier();
-    // fragments of k-slice ks+1 are read while the MFMAs of slice ks run
+    // fragments of k-step ks+1 are read while the MFMAs of step ks run.
+    // bf16: 4 k-steps of 16 per K-tile, a lane's 8 values = chunk 2 ks + khalf;
+    // e4m3: 2 k-steps of 64, a lane's 32 values = chunks 4 ks + 2 khalf, +1.
+    constexpr int KSTEPS = FP8 ? 2 : 4;
+    if constexpr (!FP8) {
 #define HY3_FRAGS(SET, KS)                                                                         \
     {                                                                                              \
         const int chunk_ = 2 * (KS) + khalf;                                                       \
@@ -210,12 +239,12 @@ __global__ __launch_bounds__(512, 1) void k_prefill_gemm(
     }
 #define HY3_CITER(IT, STG)                                                                         \
     if ((IT) < nk) {                                                                               \
-        const uint16_t* As = lds + (STG) * STAGE;                                                  \
-        const uint16_t* Bs = As + TILE_A;                                                          \
+        const uint8_t* As = lds + (STG) * STAGE;                                                   \
+        const uint8_t* Bs = As + TILE_A;                                                           \
         Frag fa[2][2], fb[2][4];                                                                   \
         HY3_FRAGS(0, 0);                                                                           \
-        _Pragma("unroll") for (int ks = 0; ks < BK / 16; ++ks) {                                   \
-            if (ks + 1 < BK / 16) HY3_FRAGS((ks + 1) & 1, ks + 1);                                 \
+        _Pragma("unroll") for (int ks = 0; ks < KSTEPS; ++ks) {                                    \
+            if (ks + 1 < KSTEPS) HY3_FRAGS((ks + 1) & 1, ks + 1);                                  \
             _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                       \
                 _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                                   \
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                         \
@@ -223,34 +252,95 @@ __global__ __launch_bounds__(512, 1) void k_prefill_gemm(
         }                                                                                          \
     }                                                                                              \
     lds_barrier();
-    // the same number of barriers as the producer: ceil(nk / 3) * 3 iterations
-    for (int it = 0; it < nk; it += 3) {
-        HY3_CITER(it, 0);
-        HY3_CITER(it + 1, 1);
-        HY3_CITER(it + 2, 2);
-    }
+        for (int it = 0; it < nk; it += 3) {   // ceil(nk / 3) * 3 barriers, as the producer
+            HY3_CITER(it, 0);
+            HY3_CITER(it + 1, 1);
+            HY3_CITER(it + 2, 2);
+        }
 #undef HY3_CITER
 #undef HY3_FRAGS
+    } else {
+#define HY3_FRAGS8(SET, KS)                                                                        \
+    {                                                                                              \
+        const int chunk_ = 4 * (KS) + 2 * khalf;                                                   \
+        _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                                         \
+            fa[SET][mb].q[0] = *reinterpret_cast<const i32x4_t*>(As + swz(a_row[mb], chunk_));     \
+            fa[SET][mb].q[1] = *reinterpret_cast<const i32x4_t*>(As + swz(a_row[mb], chunk_ + 1)); \
+        }                                                                                          \
+        _Pragma("unroll") for (int nb = 0; nb < 4; ++nb) {                                         \
+            fb[SET][nb].q[0] = *reinterpret_cast<const i32x4_t*>(Bs + swz(b_row[nb], chunk_));     \
+            fb[SET][nb].q[1] = *reinterpret_cast<const i32x4_t*>(Bs + swz(b_row[nb], chunk_ + 1)); \
+        }                                                                                          \
+    }
+#define HY3_CITER8(IT, STG)                                                                        \
+    if ((IT) < nk) {                                                                               \
+        const uint8_t* As = lds + (STG) * STAGE;                                                   \
+        const uint8_t* Bs = As + TILE_A;                                                           \
+        Frag8 fa[2][2], fb[2][4];                                                                  \
+        HY3_FRAGS8(0, 0);                                                                          \
+        _Pragma("unroll") for (int ks = 0; ks < KSTEPS; ++ks) {                                    \
+            if (ks + 1 < KSTEPS) HY3_FRAGS8((ks + 1) & 1, ks + 1);                                 \
+            _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                                       \
+                _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                                   \
+                    acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                 \
+                        fa[ks & 1][mb].v, fb[ks & 1][nb].v, acc[mb][nb], 0, 0, 0, 127, 0, 127);    \
+        }                                                                                          \
+    }                                                                                              \
+    lds_barrier();
+        for (int it = 0; it < nk; it += 3) {
+            HY3_CITER8(it, 0);
+            HY3_CITER8(it + 1, 1);
+            HY3_CITER8(it + 2, 2);
+        }
+#undef HY3_CITER8
+#undef HY3_FRAGS8
+    }
 
     // epilogue
+    const float* ws_e = FP8 ? w_scale + static_cast<size_t>(e) * (GATE_UP ? 2 * N : N) : nullptr;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int r = 64 * wm + 32 * mb + 8 * (j >> 2) + 4 * khalf + (j & 3);
             if (r >= rows) continue;
-            uint16_t* crow = C + static_cast<size_t>(row0 + r) * N;
-            if (GATE_UP) {
+            const size_t grow = static_cast<size_t>(row0 + r);
+            if constexpr (MODE == GU_BF16) {
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb) {
                     const int c = nt * (BNW / 2) + 64 * wn + 32 * nb + l32;
-                    if (c < N) crow[c] = f32_to_bf16(silu_mul(acc[mb][nb][j], acc[mb][nb + 2][j]));
+                    if (c < N) C[grow * N + c] = f32_to_bf16(silu_mul(acc[mb][nb][j], acc[mb][nb + 2][j]));
                 }
-            } else {
+            } else if constexpr (MODE == DN_BF16) {
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) {
                     const int c = nt * BNW + 128 * wn + 32 * nb + l32;
-                    if (c < N) crow[c] = f32_to_bf16(acc[mb][nb][j]);
+                    if (c < N) C[grow * N + c] = f32_to_bf16(acc[mb][nb][j]);
+                }
+            } else if constexpr (MODE == GU_FP8) {
+                const float sx = a_scale[tok_of[grow]];
+                float hmax = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const int c = nt * (BNW / 2) + 64 * wn + 32 * nb + l32;
+                    if (c < N) {
+                        const float g = acc[mb][nb][j] * sx * ws_e[c];
+                        const float u = acc[mb][nb + 2][j] * sx * ws_e[N + c];
+                        const float hv = silu_mul(g, u);
+                        h32[grow * N + c] = hv;
+                        hmax = fmaxf(hmax, fabsf(hv));
+                    }
+                }
+                // row max over the 32 lanes that share this row (same khalf)
+#pragma unroll
+                for (int off = 16; off >= 1; off >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, off, 32));
+                if (l32 == 0) atomicMax(&amax[grow], __float_as_uint(hmax));
+            } else {
+                const float sh = a_scale[grow];
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const int c = nt * BNW + 128 * wn + 32 * nb + l32;
+                    if (c < N) C[grow * N + c] = f32_to_bf16(acc[mb][nb][j] * sh * ws_e[c]);
                 }
             }
         }
@@ -270,8 +360,10 @@ hipError_t launch_gate_up_prefill(const uint16_t* x, const int32_t* tok_of, cons
                                   const int32_t* offsets, const int32_t* tile_off, int max_mtiles,
                                   uint16_t* h, int E, int d, int F, hipStream_t s) {
     const int ntn = (F + BNW / 2 - 1) / (BNW / 2);
-    hipLaunchKernelGGL(k_prefill_gemm<true>, dim3(grid_for(max_mtiles, ntn)), dim3(512), 0, s, x,
-                       tok_of, W_gu, offsets, tile_off, h, d, F, E, ntn);
+    hipLaunchKernelGGL(k_prefill_gemm<GU_BF16>, dim3(grid_for(max_mtiles, ntn)), dim3(512), 0, s,
+                       reinterpret_cast<const uint8_t*>(x), tok_of,
+                       reinterpret_cast<const uint8_t*>(W_gu), offsets, tile_off, h, nullptr,
+                       nullptr, nullptr, nullptr, d, F, E, ntn);
     return hipGetLastError();
 }
 
@@ -279,8 +371,29 @@ hipError_t launch_down_prefill(const uint16_t* h, const uint16_t* W_dn, const in
                                const int32_t* tile_off, int max_mtiles, uint16_t* y, int E, int d,
                                int F, hipStream_t s) {
     const int ntn = (d + BNW - 1) / BNW;
-    hipLaunchKernelGGL(k_prefill_gemm<false>, dim3(grid_for(max_mtiles, ntn)), dim3(512), 0, s, h,
-                       nullptr, W_dn, offsets, tile_off, y, F, d, E, ntn);
+    hipLaunchKernelGGL(k_prefill_gemm<DN_BF16>, dim3(grid_for(max_mtiles, ntn)), dim3(512), 0, s,
+                       reinterpret_cast<const uint8_t*>(h), nullptr,
+                       reinterpret_cast<const uint8_t*>(W_dn), offsets, tile_off, y, nullptr,
+                       nullptr, nullptr, nullptr, F, d, E, ntn);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
+                              const uint8_t* Wq, const float* ws, const int32_t* offsets,
+                              const int32_t* tile_off, int max_mtiles, float* h32, uint32_t* amax,
+                              int E, int d, int F, hipStream_t s) {
+    const int ntn = (F + BNW / 2 - 1) / (BNW / 2);
+    hipLaunchKernelGGL(k_prefill_gemm<GU_FP8>, dim3(grid_for(max_mtiles, ntn)), dim3(512), 0, s, xq,
+                       tok_of, Wq, offsets, tile_off, nullptr, xs, ws, h32, amax, d, F, E, ntn);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq, const float* ws,
+                           const int32_t* offsets, const int32_t* tile_off, int max_mtiles,
+                           uint16_t* y, int E, int d, int F, hipStream_t s) {
+    const int ntn = (d + BNW - 1) / BNW;
+    hipLaunchKernelGGL(k_prefill_gemm<DN_FP8>, dim3(grid_for(max_mtiles, ntn)), dim3(512), 0, s, hq,
+                       nullptr, Wq, offsets, tile_off, y, hs, ws, nullptr, nullptr, F, d, E, ntn);
     return hipGetLastError();
 }
 

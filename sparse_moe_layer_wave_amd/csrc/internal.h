@@ -36,7 +36,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // Workspace carving, computed identically on the host for every entry point.
 struct Layout {
     size_t planes, partial, scores, blk_counts, blk_base, counts, offsets, tile_off, idx, w, row_of, tok_of, h, y,
-        xq, xs, hq, hs, total;
+        xq, xs, hq, hs, amax, total;
     int nb;              // routing blocks
     int nsplit;          // router d-chunks
     int max_mtiles;      // upper bound on M-tiles of the grouped GEMMs
@@ -106,5 +106,15 @@ hipError_t launch_block_counts(const int32_t* idx, int T, int E, int k, int nb,
                                int32_t* blk_counts, hipStream_t s);
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,
                              hipStream_t st);
+hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, int rows, int cols,
+                                 uint8_t* q, float* s, hipStream_t st);
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
+hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
+                              const uint8_t* Wq, const float* ws, const int32_t* offsets,
+                              const int32_t* tile_off, int max_mtiles, float* h32, uint32_t* amax,
+                              int E, int d, int F, hipStream_t s);
+hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq, const float* ws,
+                           const int32_t* offsets, const int32_t* tile_off, int max_mtiles,
+                           uint16_t* y, int E, int d, int F, hipStream_t s);
 
 }  // namespace hy3

@@ -20,7 +20,8 @@ WEIGHTS_BF16, WEIGHTS_FP8_E4M3 = 0, 1
 
 EXPORTS = (
     "hy3moe_workspace_size", "hy3moe_route", "hy3moe_permute", "hy3moe_forward",
-    "hy3moe_forward_timed", "hy3moe_forward_fp8", "hy3moe_quantize_rows_e4m3", "hy3moe_status_string",
+    "hy3moe_forward_timed", "hy3moe_forward_fp8", "hy3moe_forward_fp8_timed",
+    "hy3moe_quantize_rows_e4m3", "hy3moe_status_string",
     "hy3moe_last_hip_error",
 )
 
@@ -52,6 +53,7 @@ def lib():
     L.hy3moe_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z]
     L.hy3moe_forward_timed.argtypes = [P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z, P]
     L.hy3moe_forward_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z]
+    L.hy3moe_forward_fp8_timed.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z, P]
     L.hy3moe_quantize_rows_e4m3.argtypes = [P, I, I, P, P, S]
     L.hy3moe_status_string.argtypes = [I]
     L.hy3moe_status_string.restype = ctypes.c_char_p
@@ -169,18 +171,21 @@ def forward(x, W_gate, W_gate_up, W_down, k, scale, bias=None, out=None, workspa
     if stage_events is None:
         _check(lib().hy3moe_forward(*args), "hy3moe_forward")
     else:
-        if len(stage_events) != 6:
-            raise ValueError("stage_events: need 6 events")
-        for ev in stage_events:
-            if not ev.cuda_event:       # torch creates the hipEvent on first record
-                ev.record()
-        arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(ev.cuda_event) for ev in stage_events])
-        _check(lib().hy3moe_forward_timed(*args, arr), "hy3moe_forward_timed")
+        _check(lib().hy3moe_forward_timed(*args, _event_array(stage_events)), "hy3moe_forward_timed")
     return (out, idx, w) if return_routing else out
 
 
+def _event_array(stage_events):
+    if len(stage_events) != 6:
+        raise ValueError("stage_events: need 6 events")
+    for ev in stage_events:
+        if not ev.cuda_event:           # torch creates the hipEvent on first record
+            ev.record()
+    return (ctypes.c_void_p * 6)(*[ctypes.c_void_p(ev.cuda_event) for ev in stage_events])
+
+
 def forward_fp8(x, W_gate, Wq_gate_up, s_gate_up, Wq_down, s_down, k, scale, bias=None, out=None,
-                workspace=None, return_routing=False):
+                workspace=None, return_routing=False, stage_events=None):
     """hy3moe_forward_fp8: e4m3 experts (uint8 codes) with fp32 per-channel scales."""
     T, d = x.shape
     E = W_gate.shape[0]
@@ -202,11 +207,14 @@ def forward_fp8(x, W_gate, Wq_gate_up, s_gate_up, Wq_down, s_down, k, scale, bia
         w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = alloc_workspace(T, d, E, k, F, WEIGHTS_FP8_E4M3, device=x.device) if T else None
-    _check(lib().hy3moe_forward_fp8(_ptr(x), _ptr(W_gate), _ptr(Wq_gate_up), _ptr(s_gate_up),
-                                    _ptr(Wq_down), _ptr(s_down), _ptr(out), T, d, E, k, F,
-                                    float(scale), _stream(), _ptr(bias), _ptr(idx), _ptr(w),
-                                    _ptr(workspace), 0 if workspace is None else workspace.numel()),
-           "hy3moe_forward_fp8")
+    args = (_ptr(x), _ptr(W_gate), _ptr(Wq_gate_up), _ptr(s_gate_up), _ptr(Wq_down), _ptr(s_down),
+            _ptr(out), T, d, E, k, F, float(scale), _stream(), _ptr(bias), _ptr(idx), _ptr(w),
+            _ptr(workspace), 0 if workspace is None else workspace.numel())
+    if stage_events is None:
+        _check(lib().hy3moe_forward_fp8(*args), "hy3moe_forward_fp8")
+    else:
+        _check(lib().hy3moe_forward_fp8_timed(*args, _event_array(stage_events)),
+               "hy3moe_forward_fp8_timed")
     return (out, idx, w) if return_routing else out
 
 

@@ -84,3 +84,25 @@ class LazyExperts:
 
     def __getitem__(self, e):
         return self._bits(self._t[int(e)])
+
+
+def check_output_fp8_small(out_gpu, out_ref, valid=None, tol_max=3e-2):
+    """Small-d_ff e4m3 cases.  One SwiGLU activation whose fp32 value falls on
+    the other side of an e4m3 rounding boundary than the oracle's (the two
+    differ in their last bits) moves by one e4m3 step, 1/8 of its size; with
+    only d_ff terms per output, that one step can move an output by several
+    percent of rms.  So here: rms error <= 1e-2 * rms(ref), at most 1e-4 of the
+    elements beyond tol_max * rms(ref), none beyond 5 * tol_max * rms(ref)."""
+    out_gpu = np.asarray(out_gpu, dtype=np.float64)
+    if valid is None:
+        valid = np.ones(out_ref.shape[0], dtype=bool)
+    d = np.abs(out_gpu[valid] - out_ref[valid])
+    rms = float(np.sqrt(np.mean(out_ref ** 2)))
+    rms_err = float(np.sqrt(np.mean(d ** 2)))
+    frac = float(np.mean(d > tol_max * rms))
+    assert np.all(np.isfinite(out_gpu))
+    assert rms_err <= 1e-2 * rms, f"rms error {rms_err:.3e} > 1e-2 * rms {rms:.3e}"
+    assert frac <= 1e-4, f"{frac:.2e} of elements beyond {tol_max} * rms"
+    assert d.max() <= 5 * tol_max * rms, f"max|d| {d.max():.3e} > {5 * tol_max} * rms"
+    return dict(max_abs=float(d.max()), rms_ref=rms, ratio=float(d.max()) / rms,
+                rms_err_ratio=rms_err / rms, frac_beyond=frac)
