@@ -60,18 +60,23 @@ def run_workload(cfg, steps, warmup):
     inp = inputs.make_inputs(cfg, device="cuda")
     c = inp["cfg"]
     T, d, E, k, F = c["T"], c["d"], c["E"], c["k"], c["F"]
-    ws = hy3moe.alloc_workspace(T, d, E, k, F)
+    fp8 = c.get("weights") == "fp8"
+    ws = hy3moe.alloc_workspace(T, d, E, k, F, hy3moe.WEIGHTS_FP8_E4M3 if fp8 else hy3moe.WEIGHTS_BF16)
     out = torch.empty((T, d), dtype=torch.float32, device="cuda")
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
 
-    def step(evs=None):
-        hy3moe.forward(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], k, inp["scale"],
-                       bias=inp["bias"], out=out, workspace=ws, stage_events=evs)
+    def step(evs=None, return_routing=False):
+        if fp8:
+            return hy3moe.forward_fp8(inp["x"], inp["W_gate"], inp["Wq_gu"], inp["s_gu"], inp["Wq_dn"],
+                                      inp["s_dn"], k, inp["scale"], bias=inp["bias"], out=out,
+                                      workspace=ws, stage_events=evs, return_routing=return_routing)
+        return hy3moe.forward(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], k, inp["scale"],
+                              bias=inp["bias"], out=out, workspace=ws, stage_events=evs,
+                              return_routing=return_routing)
 
     for _ in range(warmup):
         step()
-    _, idx_r, _ = hy3moe.forward(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], k,
-                                 inp["scale"], bias=inp["bias"], workspace=ws, return_routing=True)
+    _, idx_r, _ = step(return_routing=True)
     torch.cuda.synchronize()
     load = np.bincount(idx_r.cpu().numpy().reshape(-1), minlength=E)
     n_touched = int((load > 0).sum())
@@ -102,7 +107,8 @@ def roofline(res, kernel, bound):
         peak, unit = HBM_PEAK_GBS, "GB/s"
     else:
         achieved = a["flops"] / (ms * 1e-3) / 1e12
-        peak, unit = BF16_PEAK_TFLOPS, "TFLOP/s"
+        fp8 = res["cfg"].get("weights") == "fp8"
+        peak, unit = (FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS), "TFLOP/s"
     return {"bound": bound, "kernel": kernel, "achieved": round(achieved, 2), "peak": peak,
             "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic(kernel, res),
             "avg_kernel_ms": round(ms, 5)}
@@ -159,13 +165,25 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 prefill line")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the skewed T=65536 and FP8 T=8192 lines")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one 1 GiB device-to-device copy (outside every timed region), "
+                         "a known byte count for scaling HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the layer is not sharded "
               "across GPUs in this build", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        torch.cuda.empty_cache()
 
     dec, _ = run_workload(1, args.steps, args.warmup)
     line = {
@@ -198,6 +216,18 @@ def main():
             "roofline_down": roofline(pre, "down", "mfma"),
             "kernel_ms": {k: round(v, 5) for k, v in pre["stage_ms"].items()},
         }
+    if not args.no_extra:
+        for key, cfg in (("skewed", 3), ("fp8", 4)):
+            res, _ = run_workload(cfg, max(3, args.steps // 10), min(args.warmup, 2))
+            line[key] = {
+                "workload": res["cfg"]["name"], "tokens_per_s": round(res["tokens_per_s"], 1),
+                "ms_per_step": round(res["ms_per_step"], 4),
+                "layer_tflops": round(res["layer_tflops"], 2),
+                "hottest_over_mean": round(res["hottest_over_mean"], 2),
+                "roofline": roofline(res, "gate_up", "mfma"),
+                "roofline_down": roofline(res, "down", "mfma"),
+                "kernel_ms": {k: round(v, 5) for k, v in res["stage_ms"].items()},
+            }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(1)
     print(json.dumps(line), flush=True)

@@ -188,7 +188,7 @@ static int forward_bf16(const uint16_t* x, const float* W_gate, const uint16_t* 
                              hy3::prefill_bm(), row_of, tok_of, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
     if (e != hipSuccess) return hip_status(e);
-    const bool decode = hy3::use_decode_path(T, d, E, k);
+    const bool decode = hy3::use_decode_path(T, d, d_ff, E, k);
     if (decode)
         e = hy3::launch_gate_up_decode(x, tok_of, W_gate_up, offsets, h, E, d, d_ff, s);
     else

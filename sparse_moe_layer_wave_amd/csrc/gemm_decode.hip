@@ -5,9 +5,15 @@
 // 32 weight rows over the full K and the expert's rows 16 at a time
 // (v_mfma_f32_16x16x32_bf16: A = 16 token rows x 32 k, B = 32 k x 16 weight
 // rows; lane l holds row l%16 and k 8*(l/16)..+8 of both; C lane l holds
-// column l%16, rows 4*(l/16)..+4).  Weights go straight from global memory to
-// registers (no reuse, so no LDS): each wave keeps kDepth k-steps of weight
-// fragments in flight, 8 KB per k-step group per wave.
+// column l%16, rows 4*(l/16)..+4).
+//
+// Weights are read in the order HBM streams best: each load instruction
+// covers 4 weight rows x 256 contiguous bytes (a whole-row run of 128 k),
+// the next batch already in flight in registers while the current one is
+// used.  The MFMA wants each lane on a single row, so every batch goes through
+// a wave-private 8 KB LDS slab [32 rows][128 k] whose 16-byte chunks are XOR-
+// swizzled by (row & 15): the 16-row fragment reads then hit 16 different
+// bank groups.  Only the owning wave touches its slab, so no barrier is needed.
 //
 // gate_up: wave w of block (e, c0) owns gate rows c0+16w..+16 and the matching
 //          up rows F+c0+16w..+16, and writes h[r, c] = bf16(SiLU(g) * u)
@@ -21,12 +27,17 @@
 namespace hy3 {
 namespace {
 
-constexpr int kDepth = 8;       // k-steps (of 32) loaded before their MFMAs
+constexpr int kBatchK = 128;            // k per batch (4 MFMA k-steps of 32)
+constexpr int kSlab = 32 * kBatchK;     // bf16 elements of one wave's LDS slab (8 KB)
 
 union Frag {
     bf16x8_t v;
     i32x4_t q;
 };
+
+__device__ __forceinline__ int slab_off(int row, int chunk) {   // element offset, 16 chunks per row
+    return row * kBatchK + ((chunk ^ (row & 15)) << 3);
+}
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) void k_decode_gemm(
@@ -36,6 +47,7 @@ __global__ __launch_bounds__(256) void k_decode_gemm(
     const int32_t* __restrict__ offsets,
     uint16_t* __restrict__ C,              // gate_up: h [rows, N]; down: y [rows, N]
     int K, int N) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kSlab];
     const int e = blockIdx.x;
     const int rbeg = offsets[e];
     const int rend = offsets[e + 1];
@@ -44,26 +56,28 @@ __global__ __launch_bounds__(256) void k_decode_gemm(
     const int wave = threadIdx.x >> 6;
     const int r16 = lane & 15;
     const int kq = (lane >> 4) * 8;
+    uint16_t* slab = lds + wave * kSlab;
 
-    // this lane's two weight rows (one per n-tile) and its output column(s)
-    int wrow0, wrow1, col0, col1;
-    if (GATE_UP) {
-        const int c = blockIdx.y * 64 + wave * 16 + r16;
-        wrow0 = c;
-        wrow1 = N + c;
-        col0 = blockIdx.y * 64 + wave * 16;
-        col1 = col0;
-    } else {
-        const int n = blockIdx.y * 128 + wave * 32;
-        wrow0 = n + r16;
-        wrow1 = n + 16 + r16;
-        col0 = n;
-        col1 = n + 16;
-    }
+    // weight row of slab row sr (0..31): n-tile sr/16, row sr%16 of it
+    int col0;
+    size_t wrow_base;   // element offset of slab row 0's weight row; others via wrow_of
     const size_t wbase = static_cast<size_t>(e) * (GATE_UP ? 2 * N : N) * K;
-    const uint16_t* w0 = W + wbase + static_cast<size_t>(wrow0) * K + kq;
-    const uint16_t* w1 = W + wbase + static_cast<size_t>(wrow1) * K + kq;
+    auto wrow_of = [&](int sr) -> int {
+        if (GATE_UP) return (sr < 16 ? 0 : N) + blockIdx.y * 64 + wave * 16 + (sr & 15);
+        return blockIdx.y * 128 + wave * 32 + sr;
+    };
+    (void)wrow_base;
+    col0 = GATE_UP ? blockIdx.y * 64 + wave * 16 : blockIdx.y * 128 + wave * 32;
+    // load instruction i (0..7) of a batch: slab rows 4i + lane/16, bytes (lane%16)*16
+    const uint16_t* wsrc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        wsrc[i] = W + wbase + static_cast<size_t>(wrow_of(4 * i + (lane >> 4))) * K + (lane & 15) * 8;
+    int wdst[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wdst[i] = slab_off(4 * i + (lane >> 4), lane & 15);
 
+    const int nb = K / kBatchK;
     for (int p0 = rbeg; p0 < rend; p0 += 16) {
         const int prow = p0 + r16;                    // A row this lane loads
         const bool va = prow < rend;
@@ -73,28 +87,33 @@ __global__ __launch_bounds__(256) void k_decode_gemm(
 
         f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
         f32x4_t acc1 = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = 0; kb < K; kb += 32 * kDepth) {
-            i32x4_t b0[kDepth], b1[kDepth], av[kDepth];
+        i32x4_t cur[8], nxt[8];
 #pragma unroll
-            for (int u = 0; u < kDepth; ++u) {
-                const int kk = kb + 32 * u;
-                if (kk < K) {
-                    b0[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(w0 + kk));
-                    b1[u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(w1 + kk));
-                    av[u] = va ? *reinterpret_cast<const i32x4_t*>(a + kk) : i32x4_t{0, 0, 0, 0};
-                }
+        for (int i = 0; i < 8; ++i) cur[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(wsrc[i]));
+        for (int b = 0; b < nb; ++b) {
+            const int kb = b * kBatchK;
+            const int kn = (b + 1 < nb ? b + 1 : b) * kBatchK;   // last batch re-reads itself
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                nxt[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(wsrc[i] + kn));
+            i32x4_t av[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                av[s] = va ? *reinterpret_cast<const i32x4_t*>(a + kb + 32 * s) : i32x4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) *reinterpret_cast<i32x4_t*>(slab + wdst[i]) = cur[i];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                // lane l: slab row (nt*16 + l%16), logical chunk 4 s + l/16
+                Frag fa, f0, f1;
+                fa.q = av[s];
+                f0.q = *reinterpret_cast<const i32x4_t*>(slab + slab_off(r16, 4 * s + (lane >> 4)));
+                f1.q = *reinterpret_cast<const i32x4_t*>(slab + slab_off(16 + r16, 4 * s + (lane >> 4)));
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.v, f0.v, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.v, f1.v, acc1, 0, 0, 0);
             }
 #pragma unroll
-            for (int u = 0; u < kDepth; ++u) {
-                if (kb + 32 * u < K) {
-                    Frag fa, f0, f1;
-                    fa.q = av[u];
-                    f0.q = b0[u];
-                    f1.q = b1[u];
-                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.v, f0.v, acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.v, f1.v, acc1, 0, 0, 0);
-                }
-            }
+            for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
         }
         // C lane l: column l%16, rows 4*(l/16)+i
 #pragma unroll
@@ -105,7 +124,7 @@ __global__ __launch_bounds__(256) void k_decode_gemm(
                     C[static_cast<size_t>(row) * N + col0 + r16] = f32_to_bf16(silu_mul(acc0[i], acc1[i]));
                 } else {
                     C[static_cast<size_t>(row) * N + col0 + r16] = f32_to_bf16(acc0[i]);
-                    C[static_cast<size_t>(row) * N + col1 + r16] = f32_to_bf16(acc1[i]);
+                    C[static_cast<size_t>(row) * N + col0 + 16 + r16] = f32_to_bf16(acc1[i]);
                 }
             }
         }
@@ -115,9 +134,9 @@ __global__ __launch_bounds__(256) void k_decode_gemm(
 }  // namespace
 
 // Decode path while the average expert gets at most 4 rows (so nearly every
-// expert fits one 16-row pass); needs d to be a multiple of 128.
-bool use_decode_path(int T, int d, int E, int k) {
-    return static_cast<long long>(T) * k <= 4LL * E && (d % 128) == 0;
+// expert fits one 16-row pass); needs d and d_ff to be multiples of 128.
+bool use_decode_path(int T, int d, int F, int E, int k) {
+    return static_cast<long long>(T) * k <= 4LL * E && (d % 128) == 0 && (F % 128) == 0;
 }
 
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,

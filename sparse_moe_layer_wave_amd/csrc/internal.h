@@ -72,7 +72,7 @@ hipError_t launch_down_prefill(const uint16_t* h, const uint16_t* W_dn, const in
                                int F, hipStream_t s);
 
 // decode-sized batches: weight streaming, one workgroup per (expert, weight slice)
-bool use_decode_path(int T, int d, int E, int k);
+bool use_decode_path(int T, int d, int F, int E, int k);
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
                                  const int32_t* offsets, uint16_t* h, int E, int d, int F,
                                  hipStream_t s);

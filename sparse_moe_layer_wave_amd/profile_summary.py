@@ -1,0 +1,122 @@
+"""Summarise rocprofv3 output of a bench.py run into a short text table.
+
+    python -m sparse_moe_layer_wave_amd.profile_summary --trace T.csv \
+        [--fetch F.csv --write W.csv] --command "..." --out profiles/NAME.md \
+        [--traffic-json profiles/counters_gate_up_hy3_decode_T64.json --kernel k_decode_gemm \
+         --grid-x 49152 --grid-y 24 --source gemm_decode.hip]
+
+--trace is rocprofv3's kernel_trace.csv (--kernel-trace --output-format csv);
+--fetch / --write are counter_collection.csv files of two --pmc runs
+(FETCH_SIZE, WRITE_SIZE: KiB per dispatch).  The counters are scaled by what
+they read for the largest device copy in the same run (bench.py
+--copy-calibration copies 1 GiB), so "bytes" means bytes as a plain copy of
+known size counts them.  The traffic JSON is what bench.py reports as
+roofline.traffic while the kernel's source file is unchanged (sha256 prefix).
+"""
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30
+
+
+def _short(name):
+    n = name.split("(")[0].replace("void ", "")
+    return n.replace("hy3::(anonymous namespace)::", "")
+
+
+def _trace(path):
+    out = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]),
+               int(r["Grid_Size_Z"]), int(r["Workgroup_Size_X"]))
+        out[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return out
+
+
+def _counters(path, counter):
+    per = collections.defaultdict(list)
+    copies = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        name = _short(r["Kernel_Name"])
+        v = float(r["Counter_Value"])
+        per[(name, int(r["Grid_Size"]))].append(v)
+        if "copy" in name.lower():
+            copies.append((int(r["Grid_Size"]), v))
+    scale = None
+    if copies:
+        grid, v = max(copies)
+        scale = COPY_BYTES / (v * 1024.0) if v > 0 else None
+    return per, scale
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--command", required=True, help="the command lines that produced the inputs")
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--traffic-json")
+    ap.add_argument("--kernel", help="kernel name (substring) for the traffic JSON")
+    ap.add_argument("--grid-x", type=int)
+    ap.add_argument("--grid-y", type=int, default=1)
+    ap.add_argument("--source", help="source file (under csrc/) of that kernel")
+    ap.add_argument("--workload", default="hy3_decode_T64")
+    args = ap.parse_args()
+
+    trace = _trace(args.trace)
+    fetch = write = None
+    fscale = wscale = None
+    if args.fetch:
+        fetch, fscale = _counters(args.fetch, "FETCH_SIZE")
+    if args.write:
+        write, wscale = _counters(args.write, "WRITE_SIZE")
+
+    lines = ["# rocprofv3 summary", "", "Commands:", "", "```", args.command.strip(), "```", ""]
+    if fscale:
+        lines.append(f"Counter scale (1 GiB device copy): FETCH x{fscale:.3f}, WRITE x{wscale:.3f}")
+        lines.append("")
+    lines.append("| kernel | grid (threads) | block | calls | avg us | min us | fetch MB/call | write MB/call |")
+    lines.append("|---|---|---|---|---|---|---|---|")
+    rows = sorted(trace.items(), key=lambda kv: -sum(kv[1]))
+    traffic = None
+    for (name, gx, gy, gz, bx), durs in rows:
+        if "hy3" not in name and "k_" not in name:
+            continue
+        fmb = wmb = ""
+        gsize = gx * gy * gz
+        if fetch is not None:
+            fv = fetch.get((name, gsize))
+            wv = write.get((name, gsize)) if write else None
+            if fv and fscale:
+                fmb = f"{sum(fv) / len(fv) * 1024 * fscale / 1e6:.1f}"
+            if wv and wscale:
+                wmb = f"{sum(wv) / len(wv) * 1024 * wscale / 1e6:.1f}"
+            if (args.kernel and args.kernel in name and gx == args.grid_x and gy == args.grid_y
+                    and fv and wv and fscale and wscale):
+                traffic = (sum(fv) / len(fv) * 1024 * fscale + sum(wv) / len(wv) * 1024 * wscale)
+        lines.append(f"| {name} | ({gx},{gy},{gz}) | {bx} | {len(durs)} | "
+                     f"{sum(durs) / len(durs) / 1e3:.1f} | {min(durs) / 1e3:.1f} | {fmb} | {wmb} |")
+    os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    if args.traffic_json and traffic is not None:
+        src = os.path.join(PKG, "csrc", args.source)
+        rec = {"kernel": args.kernel, "workload": args.workload, "source": args.source,
+               "source_sha": hashlib.sha256(open(src, "rb").read()).hexdigest()[:16],
+               "bytes_per_launch": round(traffic),
+               "how": "FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by a 1 GiB copy"}
+        json.dump(rec, open(args.traffic_json, "w"), indent=1)
+        print("traffic", rec)
+
+
+if __name__ == "__main__":
+    main()
