@@ -32,9 +32,10 @@
 // slice; B the same for a weight row; C lane l holds column l%32 and rows
 // 8*(j/4) + 4*(l/32) + j%4, j = 0..15.
 //
-// Work order: a 1-D grid over (expert, n-tile, m-tile) with the m-tiles of
-// one (expert, n-tile) adjacent, so the weight slice they share is fetched
-// once into L2.  Workgroups are dealt round-robin over the 8 XCDs, so the
+// Work order: a 1-D grid over (expert, m-tile group, n-tile, m-tile): the up
+// to 8 m-tiles of a group are adjacent for each n-tile, so the weight slice
+// they share is fetched once into L2, and a group's A rows (at most 8 MB) are
+// reused across all n-tiles before the next group starts.  Workgroups are dealt round-robin over the 8 XCDs, so the
 // block index is remapped to give each XCD a contiguous run of that order.
 
 #include "internal.h"
@@ -52,6 +53,7 @@ constexpr int STAGE = TILE_A + TILE_B;     // 48 KB
 enum Mode { GU_BF16 = 0, DN_BF16 = 1, GU_FP8 = 2, DN_FP8 = 3 };
 constexpr int kStages = 3;
 constexpr int kXcds = 8;
+constexpr int kGroupM = 8;                 // m-tiles visited together (see the tile order)
 constexpr int kChunks = 12;                // 1 KB LDS blocks per producer wave per K-tile
 
 union Frag {
@@ -128,8 +130,23 @@ __global__ __launch_bounds__(512, 1) void k_prefill_gemm(
     const int e = lo;
     const int mt_e = tile_off[e + 1] - tile_off[e];
     const int local = L - tile_off[e] * n_tiles_n;
-    const int nt = local / mt_e;
-    const int mt = local - nt * mt_e;
+    // within the expert: groups of kGroupM m-tiles; each group runs every
+    // n-tile with its m-tiles adjacent, so a group's A rows and the weight
+    // slice in use both stay in L2 however many rows the expert has
+    const int full = mt_e / kGroupM;
+    const int span = kGroupM * n_tiles_n;
+    int nt, mt;
+    if (local < full * span) {
+        const int g = local / span;
+        const int r = local - g * span;
+        nt = r / kGroupM;
+        mt = g * kGroupM + (r - nt * kGroupM);
+    } else {
+        const int rem = mt_e - full * kGroupM;
+        const int r = local - full * span;
+        nt = r / rem;
+        mt = full * kGroupM + (r - nt * rem);
+    }
     const int row0 = offsets[e] + mt * BM;
     const int rows = min(BM, offsets[e + 1] - row0);
     const size_t kbytes = static_cast<size_t>(K) * ESZ;   // bytes of one A or weight row

@@ -26,8 +26,8 @@ COPY_BYTES = 1 << 30
 
 
 def _short(name):
-    n = name.split("(")[0].replace("void ", "")
-    return n.replace("hy3::(anonymous namespace)::", "")
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0].replace("hy3::", "")
 
 
 def _trace(path):
