@@ -192,14 +192,14 @@ static int forward_bf16(const uint16_t* x, const float* W_gate, const uint16_t* 
     if (decode)
         e = hy3::launch_gate_up_decode(x, tok_of, W_gate_up, offsets, h, E, d, d_ff, s);
     else
-        e = hy3::launch_gate_up_prefill(x, tok_of, W_gate_up, offsets, tile_off, L.max_mtiles, h, E,
+        e = hy3::launch_gate_up_grouped(x, tok_of, W_gate_up, offsets, tile_off, L.max_mtiles, h, E,
                                         d, d_ff, s);
     if (e == hipSuccess) e = mark(ev, 3, s);
     if (e != hipSuccess) return hip_status(e);
     if (decode)
         e = hy3::launch_down_decode(h, W_down, offsets, y, E, d, d_ff, s);
     else
-        e = hy3::launch_down_prefill(h, W_down, offsets, tile_off, L.max_mtiles, y, E, d, d_ff, s);
+        e = hy3::launch_down_grouped(h, W_down, offsets, tile_off, L.max_mtiles, y, E, d, d_ff, s);
     if (e == hipSuccess) e = mark(ev, 4, s);
     if (e != hipSuccess) return hip_status(e);
     e = hy3::launch_combine(y, row_of, w, out, T, d, k, s);

@@ -1,5 +1,5 @@
 // FP8 (OCP e4m3) path: per-row activation quantisation (the grouped expert
-// GEMMs on fp8 MFMA are in gemm_prefill.hip).  Formats: "DeepSeek V4-Flash architecture Q&A",
+// GEMMs on fp8 MFMA are in gemm_grouped.hip).  Formats: "DeepSeek V4-Flash architecture Q&A",
 // Q7.2 (E4M3, range +-448) and Q7.4 (one scale per output channel).
 //
 // Row quantiser: amax = max|v|; amax == 0 -> codes 0, scale 1; otherwise

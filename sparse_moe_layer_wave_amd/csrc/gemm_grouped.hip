@@ -1,0 +1,436 @@
+// Grouped expert GEMMs for prefill-sized batches on CDNA4 MFMA with fp32
+// accumulation, on bf16 or e4m3 operands:
+//
+//   gate_up: h[r, c] = SiLU(x_t . Wg[e][c]) * (x_t . Wu[e][c]) for the rows r
+//            of expert e (t = token of r) ("DeepSeek V4-Flash architecture
+//            Q&A", Q4.5: SiLU on the gate branch; "Tencent Hy3-295B
+//            architecture teardown", section 2.3: the fused gate_up
+//            projection, gate rows first).  bf16: h stored as bf16.  e4m3:
+//            the two products are first rescaled by the token's activation
+//            scale and the channel's weight scale ("DeepSeek V4-Flash
+//            architecture Q&A", Q7.4: one scale per output channel); h is
+//            stored as fp32 and the row's max |h| is folded into amax[r] (an
+//            integer atomic max on the bit pattern of |h|) for the per-row
+//            quantisation of h that follows;
+//   down:    y[r, n] = h[r] . Wd[e][n] (e4m3: rescaled by the row's and the
+//            channel's scales), stored as bf16.
+//
+// Four waves per workgroup, every one both a loader and an MFMA wave, each
+// owning a 128 x 128 block of the output tile (4 x 4 blocks of 32 x 32 MFMA
+// outputs in AGPRs, so each fragment read from LDS feeds four MFMAs).  Two
+// tile shapes share the code:
+//   square: 256 rows x 256 weight rows, waves in a 2 x 2 grid;
+//   wide:   128 rows x 512 weight rows, waves in a 1 x 4 grid.
+// An expert's rows are split into 128-row blocks; pairs of blocks run as
+// square tiles and an odd last block as a wide tile, so no tile carries more
+// than 127 padding rows and both shapes do the same MFMA work.
+//
+// K advances in slices of 64 bytes per row (32 bf16 = two steps of
+// v_mfma_f32_32x32x16_bf16, or 64 e4m3 = one step of
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales).  A slice of a tile is
+// 32 or 40 one-kilobyte copies (16 rows each), issued as
+// global_load_lds_dwordx4 straight into a 4-slot LDS ring, three slices
+// ahead of use; every wave issues its own share.  The copies are written in
+// inline assembly: the compiler does not see them as LDS stores and so does
+// not wait for all of them before each LDS read; the loop instead waits
+// (s_waitcnt vmcnt) for exactly the slice it needs and then meets the other
+// waves at a barrier.  Fragments of slice k+1 are read from LDS while the
+// MFMAs of slice k run, and the copies and reads are spread between the
+// MFMAs so that neither memory queue stalls the wave.
+//
+// LDS row r keeps logical 16-byte chunk c at physical chunk c ^ ((r >> 2) & 3):
+// the 16 lanes of one phase of a fragment read (16 rows at one logical chunk)
+// then hit 16 distinct 4-bank groups, all 64 banks once.
+// MFMA lane layout: A lane l holds row l%32 and 16 bytes (bf16: k 8*(l/32)..+8
+// of a 16-wide step; e4m3: 32 bytes, k 32*(l/32)..+32 of a 64-wide step); B
+// the same for a weight row; C lane l holds column l%32 and rows
+// 8*(j/4) + 4*(l/32) + j%4, j = 0..15.
+//
+// Work order: a 1-D grid over units (expert, chunk of up to 8 row blocks,
+// 512-row weight panel, tile).  The tiles of one chunk that read the same
+// weight panel are adjacent, so the panel streams into L2 once for all of
+// them; workgroups are dealt round-robin over the 8 XCDs, so the block index is
+// remapped to give each XCD a contiguous run of units.
+
+#include "internal.h"
+
+namespace hy3 {
+namespace {
+
+enum Mode { GU_BF16 = 0, DN_BF16 = 1, GU_FP8 = 2, DN_FP8 = 3 };
+
+constexpr int kRowB = 64;                      // bytes per LDS row (one K slice)
+constexpr int kLdsBytes = 160 * 1024;          // the whole LDS of a CU
+constexpr int kSlots = 4;                      // LDS ring depth
+constexpr int kXcds = 8;
+constexpr int kChunkBlocks = 8;                // row blocks of 128 per chunk (see work order)
+
+__device__ __forceinline__ int pchunk(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// 16 bytes per lane from global memory into LDS: lane i's bytes land at
+// lds_base + 16 i (lds_base is wave-uniform, passed in M0; one wait state
+// between the M0 write and the copy).  M0 is listed as clobbered although
+// the compiler reserves it: nothing else in this file's device code uses M0
+// (the compiler sets it only for its own LDS-DMA builtins and for indirect
+// register indexing, neither of which appears here).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy_to_lds(const uint8_t* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Barrier after this wave's LDS reads have completed; copies in flight are
+// not waited for.  Compiler fences keep memory operations on their side.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+struct Unit {
+    int e, row0, rows, n;                          // n: column tile index of this shape
+};
+
+struct Args {
+    const uint8_t* A;                              // gate_up: x [T, K]; down: h [rows, K]
+    const int32_t* tok_of;                         // gate_up: token of each row
+    const uint8_t* W;                              // gate_up: [E, 2N, K]; down: [E, N, K]
+    const int32_t* offsets;                        // [E+1] row offsets
+    const int32_t* tile_off;                       // [E+1] offsets in 128-row blocks
+    uint16_t* C;                                   // bf16 out: gate_up h (bf16 mode) or y [rows, N]
+    const float* a_scale;                          // e4m3: per token (gate_up) or per row (down)
+    const float* w_scale;                          // e4m3: [E, 2N] (gate_up) or [E, N] (down)
+    float* h32;                                    // e4m3 gate_up: h [rows, N] fp32
+    uint32_t* amax;                                // e4m3 gate_up: [rows] bits of max |h|
+    int K, N, E, npanel;                           // K in elements; npanel: 512-row panels per expert
+};
+
+// One tile.  SQUARE: 256 rows x 256 weight rows; else 128 x 512.
+template <int MODE, bool SQUARE>
+__device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u) {
+    constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8;
+    constexpr bool FP8 = MODE == GU_FP8 || MODE == DN_FP8;
+    constexpr int RA = SQUARE ? 256 : 128;         // A rows per slice
+    constexpr int NPW = SQUARE ? 8 : 10;           // 1 KB copies per wave per slice
+    constexpr int WCOLS = SQUARE ? 128 : 256;      // gate_up: h columns of the tile
+    constexpr int NCOLS = SQUARE ? 256 : 512;      // down: output columns of the tile
+    constexpr int kSlotBytes = (RA + NCOLS) * kRowB;   // one slice: 32 or 40 KB
+    static_assert(kSlots * kSlotBytes <= kLdsBytes, "LDS");
+    constexpr int NMFMA = FP8 ? 16 : 32;           // MFMAs per slice and wave
+    const int N = g.N;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = SQUARE ? (wave & 1) : 0;
+    const int wn = SQUARE ? (wave >> 1) : wave;
+    const size_t rowbytes = static_cast<size_t>(g.K) * (FP8 ? 1 : 2);
+    const int nk = static_cast<int>(rowbytes / kRowB);
+
+    // ---- copy sources: copy j of this wave fills LDS rows 16 i .. 16 i + 15,
+    // i = wave * NPW + j; lane -> row 16 i + lane / 4, physical chunk lane % 4
+    const uint8_t* src[NPW];
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+        const int row = 16 * (wave * NPW + j) + (lane >> 2);
+        const int lc = pchunk(row, lane & 3);
+        if (row < RA) {
+            const int r = min(row, u.rows - 1);                // padding rows repeat a valid row
+            const size_t ar = GATE_UP ? static_cast<size_t>(g.tok_of[u.row0 + r]) : static_cast<size_t>(u.row0 + r);
+            src[j] = g.A + ar * rowbytes + lc * 16;
+        } else {
+            const int p = row - RA;                            // weight panel row
+            int wr;
+            if (GATE_UP) {
+                const int col = u.n * WCOLS + (p >> 7) * 64 + (p & 63);
+                wr = col < N ? ((p & 64) ? N + col : col) : 0;
+            } else {
+                wr = u.n * NCOLS + p;
+                wr = wr < N ? wr : 0;
+            }
+            src[j] = g.W + (static_cast<size_t>(u.e) * (GATE_UP ? 2 * N : N) + wr) * rowbytes + lc * 16;
+        }
+    }
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+    const uint32_t my_copies = lds0 + static_cast<uint32_t>(wave * NPW) * 1024u;
+
+    // ---- fragment addresses: rows a0 + 32 mb + l32 and b0 + 32 nb + l32; the
+    // physical chunk only depends on l32 (block offsets are multiples of 32).
+    // Half-fragment h of a block is one 16-byte read: bf16: the lane's 8
+    // values of k step h (chunk 2 h + khalf); e4m3: bytes 16 h.. of the lane's
+    // 32 (chunk 2 khalf + h).
+    const int l32 = lane & 31;
+    const int khalf = lane >> 5;
+    const int a0 = wm * 128;
+    const int b0 = RA + wn * 128;
+    int off[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) off[h] = l32 * kRowB + pchunk(l32, FP8 ? 2 * khalf + h : 2 * h + khalf) * 16;
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16_t{};
+
+    // read r of a slice (16 per slice): half h = r / 8; r % 8 < 4: A block r % 4,
+    // else B block r % 4
+    i32x4_t fa[2][2][4], fb[2][2][4];                  // [set][half][block]
+    auto read_frag = [&](int set, const uint8_t* base, int r) {
+        const int h = r >> 3, b = r & 3;
+        if ((r & 4) == 0) fa[set][h][b] = *reinterpret_cast<const i32x4_t*>(base + (a0 + 32 * b) * kRowB + off[h]);
+        else fb[set][h][b] = *reinterpret_cast<const i32x4_t*>(base + (b0 + 32 * b) * kRowB + off[h]);
+    };
+    auto mfma = [&](int set, int i) {
+        if constexpr (FP8) {
+            const int mb = i >> 2, nb = i & 3;
+            const i32x8_t a = __builtin_shufflevector(fa[set][0][mb], fa[set][1][mb], 0, 1, 2, 3, 4, 5, 6, 7);
+            const i32x8_t b = __builtin_shufflevector(fb[set][0][nb], fb[set][1][nb], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[mb][nb], 0, 0, 0, 127, 0, 127);
+        } else {
+            const int h = i >> 4, mb = (i >> 2) & 3, nb = i & 3;
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, fa[set][h][mb]), __builtin_bit_cast(bf16x8_t, fb[set][h][nb]),
+                acc[mb][nb], 0, 0, 0);
+        }
+    };
+
+    // ---- prologue: slices 0 .. kSlots-1 in flight (clamped: a short K
+    // re-reads its last slice), slice 0 read
+#pragma unroll
+    for (int s = 0; s < kSlots; ++s) {
+        const int kt = min(s, nk - 1);
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) copy_to_lds(src[j] + kt * kRowB, my_copies + s * kSlotBytes + j * 1024);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kSlots - 1) * NPW));
+    lds_barrier();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) read_frag(0, lds, r);
+
+    // ---- main loop, two slices per trip (fragment sets 0 and 1).  Every
+    // slice issues exactly NPW copies (slices past the end re-read the last
+    // one into a slot nobody reads again), so the waits are exact: at the top
+    // of slice kt, slices up to kt + kSlots - 1 are issued and kt + 1 must
+    // have landed.  Copy j of slice kt + kSlots follows MFMA j * NMFMA / NPW and
+    // the 16 fragment reads of slice kt + 1 are spread evenly over the MFMAs.
+    auto step = [&](int kt, int set) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kSlots - 2) * NPW));
+        lds_barrier();                                 // everyone: slice kt in registers, kt+1 landed
+        const int kin = min(kt + kSlots, nk - 1);
+        const uint32_t islot = my_copies + (kt & (kSlots - 1)) * kSlotBytes;
+        const uint8_t* rbase = lds + ((kt + 1) & (kSlots - 1)) * kSlotBytes;
+#pragma unroll
+        for (int i = 0; i < NMFMA; ++i) {
+            mfma(set, i);
+#pragma unroll
+            for (int j = 0; j < NPW; ++j)
+                if (i == j * NMFMA / NPW) copy_to_lds(src[j] + kin * kRowB, islot + j * 1024);
+            if constexpr (FP8) {
+                read_frag(set ^ 1, rbase, i);
+            } else {
+                if (i & 1) read_frag(set ^ 1, rbase, i >> 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        step(kt, 0);
+        step(kt + 1, 1);
+    }
+    if (kt < nk) step(kt, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));          // no copy may land after the tile ends
+
+    // ---- epilogue.  Each wave stages its output block in LDS (row-major,
+    // rows padded by 16 bytes so the two half-waves of a write, 4 rows apart,
+    // use different banks) and then stores it as 16-byte chunks, whole rows
+    // per group of lanes: 8x fewer store instructions than storing the MFMA
+    // layout (one column per lane) directly.  e4m3: the tile's row scales are
+    // staged in LDS as well (one load per thread, all in flight together) and
+    // the lane's column scales are loaded once, ahead of the loops.
+    constexpr int OCOLS = GATE_UP ? 64 : 128;          // output columns per wave
+    constexpr int OESZ = MODE == GU_FP8 ? 4 : 2;       // bytes per output element
+    constexpr int OPITCH = OCOLS * OESZ + 16;
+    static_assert(4 * 128 * OPITCH + RA * 4 <= kLdsBytes, "LDS");
+    uint8_t* ow = lds + wave * (128 * OPITCH);
+    float* srow = reinterpret_cast<float*>(lds + 4 * 128 * OPITCH);
+    lds_barrier();                                     // every wave is done with the ring
+    if constexpr (FP8) {
+        const int t = threadIdx.x;
+        if (t < RA) {
+            const int r = min(t, u.rows - 1);
+            srow[t] = GATE_UP ? g.a_scale[g.tok_of[u.row0 + r]] : g.a_scale[u.row0 + r];
+        }
+        __syncthreads();
+    }
+    float wsc[4] = {0.f, 0.f, 0.f, 0.f};              // gate_up: gate nb 0,1 then up nb 0,1; down: nb 0..3
+    if constexpr (FP8) {
+        const float* ws_e = g.w_scale + static_cast<size_t>(u.e) * (GATE_UP ? 2 * N : N);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int c = GATE_UP ? u.n * WCOLS + wn * 64 + 32 * (nb & 1) + l32
+                                  : u.n * NCOLS + wn * 128 + 32 * nb + l32;
+            if (c < N) wsc[nb] = ws_e[(GATE_UP && nb >= 2) ? N + c : c];
+        }
+    }
+    const int col0 = GATE_UP ? u.n * WCOLS + wn * 64 : u.n * NCOLS + wn * 128;   // the wave's first output column
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int rl = 32 * mb + 8 * (j >> 2) + 4 * khalf + (j & 3);   // row within the wave's block
+            uint8_t* orow = ow + rl * OPITCH;
+            if constexpr (MODE == GU_BF16) {
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    *reinterpret_cast<uint16_t*>(orow + (32 * nb + l32) * 2) =
+                        f32_to_bf16(silu_mul(acc[mb][nb][j], acc[mb][nb + 2][j]));
+            } else if constexpr (MODE == DN_BF16) {
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    *reinterpret_cast<uint16_t*>(orow + (32 * nb + l32) * 2) = f32_to_bf16(acc[mb][nb][j]);
+            } else if constexpr (MODE == GU_FP8) {
+                const float sx = srow[a0 + rl];
+                float hmax = 0.f;
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const float gv = acc[mb][nb][j] * sx * wsc[nb];
+                    const float uv = acc[mb][nb + 2][j] * sx * wsc[nb + 2];
+                    const float hv = silu_mul(gv, uv);             // 0 for columns >= N (zero scales)
+                    *reinterpret_cast<float*>(orow + (32 * nb + l32) * 4) = hv;
+                    hmax = fmaxf(hmax, fabsf(hv));
+                }
+                // row max over the 32 lanes that share this row (same khalf)
+#pragma unroll
+                for (int o = 16; o >= 1; o >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, o, 32));
+                if (l32 == 0 && a0 + rl < u.rows) atomicMax(&g.amax[u.row0 + a0 + rl], __float_as_uint(hmax));
+            } else {
+                const float sh = srow[a0 + rl];
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    *reinterpret_cast<uint16_t*>(orow + (32 * nb + l32) * 2) = f32_to_bf16(acc[mb][nb][j] * sh * wsc[nb]);
+            }
+        }
+    }
+    // a wave's LDS accesses complete in order, so it can read its block back
+    // without a barrier
+    constexpr int CPR = OCOLS * OESZ / 16;             // 16-byte chunks per row: 8 or 16
+    constexpr int EPC = 16 / OESZ;                     // elements per chunk
+#pragma unroll
+    for (int it = 0; it < 128 * CPR / 64; ++it) {
+        const int q = it * 64 + lane;
+        const int rl = q / CPR, cc = q % CPR;
+        const int r = a0 + rl;
+        const int c = col0 + cc * EPC;
+        const i32x4_t v = *reinterpret_cast<const i32x4_t*>(ow + rl * OPITCH + cc * 16);
+        if (r < u.rows && c < N) {
+            const size_t grow = static_cast<size_t>(u.row0 + r);
+            if constexpr (MODE == GU_FP8) *reinterpret_cast<i32x4_t*>(g.h32 + grow * N + c) = v;
+            else *reinterpret_cast<i32x4_t*>(g.C + grow * N + c) = v;
+        }
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void k_grouped(Args g) {
+    constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+
+    const int E = g.E, npanel = g.npanel;
+    const int G = gridDim.x;                       // a multiple of kXcds
+    const int L = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
+    if (L >= g.tile_off[E] * npanel) return;
+    int lo = 0, hi = E - 1;                        // expert: last e with tile_off[e] * npanel <= L
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (g.tile_off[mid] * npanel <= L) lo = mid;
+        else hi = mid - 1;
+    }
+    Unit u;
+    u.e = lo;
+    const int nb_e = g.tile_off[lo + 1] - g.tile_off[lo];
+    int v = L - g.tile_off[lo] * npanel;
+    // chunks of kChunkBlocks row blocks; a chunk of m blocks has m * npanel
+    // units: for each weight panel, its square tiles (two column tiles per
+    // panel, pairs of blocks) and then its wide tile (odd last block)
+    const int full = nb_e / kChunkBlocks;
+    int c, m;
+    if (v < full * kChunkBlocks * npanel) {
+        c = v / (kChunkBlocks * npanel);
+        m = kChunkBlocks;
+    } else {
+        c = full;
+        m = nb_e - full * kChunkBlocks;
+    }
+    v -= c * kChunkBlocks * npanel;
+    const int pairs = m >> 1;
+    const int panel = v / m;
+    const int w = v - panel * m;
+    int blk;
+    const bool square = w < 2 * pairs;
+    if (square) {
+        u.n = 2 * panel + w / pairs;
+        blk = c * kChunkBlocks + 2 * (w % pairs);
+    } else {
+        u.n = panel;
+        blk = c * kChunkBlocks + 2 * pairs;
+    }
+    u.row0 = g.offsets[lo] + blk * 128;
+    u.rows = min(square ? 256 : 128, g.offsets[lo + 1] - u.row0);
+    const int cols_sq = GATE_UP ? 128 : 256;       // output columns of a square tile
+    if (square && u.n * cols_sq >= g.N) return;    // second column tile of a partial last panel
+
+    if (square) tile<MODE, true>(g, lds, u);
+    else tile<MODE, false>(g, lds, u);
+}
+
+template <int MODE>
+hipError_t launch(Args g, int max_blocks, hipStream_t s) {
+    constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8;
+    g.npanel = GATE_UP ? (g.N + 255) / 256 : (g.N + 511) / 512;   // 512 weight rows per panel
+    const long long units = static_cast<long long>(max_blocks) * g.npanel;
+    const int grid = static_cast<int>((units + kXcds - 1) / kXcds * kXcds);
+    hipLaunchKernelGGL(k_grouped<MODE>, dim3(grid), dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_bm() { return 128; }
+
+hipError_t launch_gate_up_grouped(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
+                                  const int32_t* offsets, const int32_t* tile_off, int max_blocks,
+                                  uint16_t* h, int E, int d, int F, hipStream_t s) {
+    Args g{reinterpret_cast<const uint8_t*>(x), tok_of, reinterpret_cast<const uint8_t*>(W_gu), offsets,
+           tile_off, h, nullptr, nullptr, nullptr, nullptr, d, F, E, 0};
+    return launch<GU_BF16>(g, max_blocks, s);
+}
+
+hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const int32_t* offsets,
+                               const int32_t* tile_off, int max_blocks, uint16_t* y, int E, int d,
+                               int F, hipStream_t s) {
+    Args g{reinterpret_cast<const uint8_t*>(h), nullptr, reinterpret_cast<const uint8_t*>(W_dn), offsets,
+           tile_off, y, nullptr, nullptr, nullptr, nullptr, F, d, E, 0};
+    return launch<DN_BF16>(g, max_blocks, s);
+}
+
+hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
+                              const uint8_t* Wq, const float* ws, const int32_t* offsets,
+                              const int32_t* tile_off, int max_blocks, float* h32, uint32_t* amax,
+                              int E, int d, int F, hipStream_t s) {
+    Args g{xq, tok_of, Wq, offsets, tile_off, nullptr, xs, ws, h32, amax, d, F, E, 0};
+    return launch<GU_FP8>(g, max_blocks, s);
+}
+
+hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq, const float* ws,
+                           const int32_t* offsets, const int32_t* tile_off, int max_blocks,
+                           uint16_t* y, int E, int d, int F, hipStream_t s) {
+    Args g{hq, nullptr, Wq, offsets, tile_off, y, hs, ws, nullptr, nullptr, F, d, E, 0};
+    return launch<DN_FP8>(g, max_blocks, s);
+}
+
+}  // namespace hy3

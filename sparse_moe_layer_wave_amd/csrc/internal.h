@@ -62,13 +62,14 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
                            int32_t* offsets, int32_t* tile_off, int bm, int32_t* row_of,
                            int32_t* tok_of, hipStream_t s);
 
-// prefill-sized batches: MFMA grouped GEMMs over M-tiles of prefill_bm() rows
+// prefill-sized batches: MFMA grouped GEMMs over row blocks of prefill_bm() rows
+// (max_blocks bounds the number of row blocks, tile_off[E])
 int prefill_bm();
-hipError_t launch_gate_up_prefill(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
-                                  const int32_t* offsets, const int32_t* tile_off, int max_mtiles,
+hipError_t launch_gate_up_grouped(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
+                                  const int32_t* offsets, const int32_t* tile_off, int max_blocks,
                                   uint16_t* h, int E, int d, int F, hipStream_t s);
-hipError_t launch_down_prefill(const uint16_t* h, const uint16_t* W_dn, const int32_t* offsets,
-                               const int32_t* tile_off, int max_mtiles, uint16_t* y, int E, int d,
+hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const int32_t* offsets,
+                               const int32_t* tile_off, int max_blocks, uint16_t* y, int E, int d,
                                int F, hipStream_t s);
 
 // decode-sized batches: weight streaming, one workgroup per (expert, weight slice)
