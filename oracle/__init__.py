@@ -17,6 +17,11 @@ quantises to OCP e4m3):
 * expert: SwiGLU with the fused gate_up projection, SiLU on the gate half --
   "Tencent Hy3-295B architecture teardown", section 2.3 (parameter breakdown)
   and "DeepSeek V4-Flash architecture Q&A", Q4.5;
+* full block (``forward_block``): the shared expert's output added to the
+  routed sum -- "Tencent Hy3-Flash Q&A", Q4.7; the router fed an RMSNorm'd
+  copy of x (route_norm, Q4.9) and choosing with the selection-only
+  e_score_correction_bias (Q4.3; "Tencent Hy3-295B architecture teardown",
+  section 4.1, router flow step 2);
 * combine: per-expert loop adding weight * expert output into the token's row
   -- "DeepSeek V4-Flash architecture Q&A", Q8.4 (the MoE forward sketch and
   the index_add_ note), done in float64 so the fp32-combine requirement
@@ -37,12 +42,14 @@ itself, and anything that would need the real model's weights.
 from .codecs import (bf16_bits_to_f64, f32_to_bf16_bits, round_to_bf16, e4m3_bits_to_f64,
                      f32_to_e4m3_bits, E4M3_MAX)
 from .moe import (route, expert_swiglu, forward, forward_tokens, quant_row_e4m3,
-                  quant_rows_e4m3, forward_fp8, forward_fp8_tokens,
-                  expert_param_count, flops_per_token, NEAR_TIE)
+                  quant_rows_e4m3, forward_fp8, forward_fp8_tokens, rms_norm_bf16,
+                  forward_block, forward_block_tokens, expert_param_count, flops_per_token,
+                  NEAR_TIE)
 
 __all__ = [
     "bf16_bits_to_f64", "f32_to_bf16_bits", "round_to_bf16", "e4m3_bits_to_f64", "f32_to_e4m3_bits",
     "E4M3_MAX", "route", "expert_swiglu", "forward", "forward_tokens",
     "quant_row_e4m3", "quant_rows_e4m3", "forward_fp8", "forward_fp8_tokens",
+    "rms_norm_bf16", "forward_block", "forward_block_tokens",
     "expert_param_count", "flops_per_token", "NEAR_TIE",
 ]

@@ -22,13 +22,14 @@ from collections import namedtuple
 
 import numpy as np
 
-from .codecs import bf16_bits_to_f64, e4m3_bits_to_f64, f32_to_e4m3_bits, round_to_bf16, E4M3_MAX
+from .codecs import (bf16_bits_to_f64, e4m3_bits_to_f64, f32_to_bf16_bits, f32_to_e4m3_bits,
+                     round_to_bf16, E4M3_MAX)
 
 # Tokens whose k-th and (k+1)-th float32 scores differ by less than this are
 # flagged: a float32 GPU router may legitimately pick either expert there.
 NEAR_TIE = 1e-6
 
-Route = namedtuple("Route", "idx w scores near_tie order_tie gap")
+Route = namedtuple("Route", "idx w scores near_tie order_tie gap choice")
 
 
 def _sigmoid64(z):
@@ -36,26 +37,34 @@ def _sigmoid64(z):
         return 1.0 / (1.0 + np.exp(-z))
 
 
-def route(x_bits, W_gate, k, scale, logit_bias=None, block=4096):
+def route(x_bits, W_gate, k, scale, logit_bias=None, block=4096, score_bias=None):
     """Sigmoid top-k router ("Tencent Hy3-295B architecture teardown", section
-    4.1, router flow steps 1, 3, 4 and 5; "Tencent Hy3-Flash Q&A", Q4.2).
+    4.1, router flow steps 1-5; "Tencent Hy3-Flash Q&A", Q4.2 and Q4.3).
 
     x_bits      uint16 [T, d]  bf16 hidden states
     W_gate      float32 [E, d] router weight
     k, scale    experts per token, router_scaling_factor (use float32(2.826))
     logit_bias  float32 [E] or None: added to each logit before the sigmoid
                 (the gate linear map's per-expert bias term)
+    score_bias  float32 [E] or None: e_score_correction_bias, added to the
+                scores for the top-k choice only (step 2 of the router flow;
+                Q4.3: it takes no part in the weights)
 
     Returns Route(idx int64 [T,k], w float64 [T,k], scores float32 [T,E],
-    near_tie bool [T], order_tie bool [T], gap float64 [T]).
+    near_tie bool [T], order_tie bool [T], gap float64 [T], choice float32
+    [T,E]).
 
     * scores = float32(sigmoid(x . W_gate^T + b)), logits summed in float64;
-    * idx[t] = the first k experts when all E are ordered by score descending,
-      equal scores by ascending expert index (slot j holds the j-th);
-    * w[t, j] = scale * s[idx_j] / sum_j s[idx_j]  (float64);
-    * near_tie: k < E and s_(k) - s_(k+1) < NEAR_TIE (the chosen set may differ
-      on a float32 GPU router); order_tie: some adjacent pair among the first
-      k+1 ranked scores is that close (the slot order may differ).
+    * choice = scores + score_bias as a float32 addition (= scores without a
+      score bias);
+    * idx[t] = the first k experts when all E are ordered by choice
+      descending, equal values by ascending expert index (slot j holds the
+      j-th);
+    * w[t, j] = scale * s[idx_j] / sum_j s[idx_j]  (float64, scores s);
+    * near_tie: k < E and c_(k) - c_(k+1) < NEAR_TIE on the ranked choice
+      values (the chosen set may differ on a float32 GPU router); order_tie:
+      some adjacent pair among the first k+1 ranked values is that close (the
+      slot order may differ).
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     W = np.asarray(W_gate, dtype=np.float32).astype(np.float64)
@@ -71,11 +80,15 @@ def route(x_bits, W_gate, k, scale, logit_bias=None, block=4096):
         if b is not None:
             logits = logits + b
         scores[t0:t0 + block] = _sigmoid64(logits).astype(np.float32)
-    # stable sort on the negated score: equal scores keep ascending expert order
-    order = np.argsort(-scores, axis=1, kind="stable")
+    if score_bias is None:
+        choice = scores
+    else:
+        choice = scores + np.asarray(score_bias, dtype=np.float32)[None, :]   # float32 addition
+    # stable sort on the negated value: equal values keep ascending expert order
+    order = np.argsort(-choice.astype(np.float64), axis=1, kind="stable")
     idx = order[:, :k].astype(np.int64)
-    ranked = np.take_along_axis(scores, order[:, :min(k + 1, E)], axis=1).astype(np.float64)
-    sel = ranked[:, :k]
+    ranked = np.take_along_axis(choice, order[:, :min(k + 1, E)], axis=1).astype(np.float64)
+    sel = np.take_along_axis(scores, idx, axis=1).astype(np.float64)
     w = np.float64(np.float32(scale)) * sel / sel.sum(axis=1, keepdims=True) if T else sel.copy()
     if k < E:
         gap = ranked[:, k - 1] - ranked[:, k]
@@ -84,7 +97,7 @@ def route(x_bits, W_gate, k, scale, logit_bias=None, block=4096):
     near_tie = gap < NEAR_TIE
     adj = ranked[:, :-1] - ranked[:, 1:] if ranked.shape[1] > 1 else np.zeros((T, 0))
     order_tie = near_tie | (np.any(adj < NEAR_TIE, axis=1) if adj.shape[1] else np.zeros(T, bool))
-    return Route(idx, w, scores, near_tie, order_tie, gap)
+    return Route(idx, w, scores, near_tie, order_tie, gap, choice)
 
 
 def expert_swiglu(x, W_gu, W_dn, bf16_activations=True):
@@ -138,6 +151,67 @@ def forward_tokens(tokens, x_bits, W_gate, W_gu_bits, W_dn_bits, k, scale, logit
     tokens = np.asarray(tokens, dtype=np.int64)
     return forward(np.asarray(x_bits)[tokens], W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias,
                    bf16_activations)
+
+
+# ----------------------------------------------------------------------------- full block
+
+def rms_norm_bf16(x_bits, w_bits, eps):
+    """route_norm: RMSNorm of bf16 rows with a bf16 weight, giving bf16 rows
+    ("Tencent Hy3-Flash Q&A", Q4.9: the router scores an RMS-normalised copy
+    of the hidden state).  The pages fix neither the precision nor eps; the
+    reading (the usual bf16-model one) is:
+
+    r = float32(1 / sqrt(sum(x^2) / d + eps))   (sum, division, sqrt in float64)
+    a = bf16(float32(x * r))                     (normalised row, cast to bf16)
+    y = bf16(a * w)                              (weight applied in bf16)
+
+    x_bits uint16 [T, d]; w_bits uint16 [d]; returns uint16 [T, d]."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, d = x_bits.shape
+    if T == 0:
+        return x_bits.copy()
+    x = bf16_bits_to_f64(x_bits)
+    v = np.sum(x * x, axis=1) / d + np.float64(eps)
+    r = (1.0 / np.sqrt(v)).astype(np.float32)
+    a = x.astype(np.float32) * r[:, None]                  # float32 products, rounded once
+    a16 = f32_to_bf16_bits(a)
+    prod = bf16_bits_to_f64(a16) * bf16_bits_to_f64(np.asarray(w_bits, dtype=np.uint16))[None, :]
+    return f32_to_bf16_bits(prod.astype(np.float32))       # exact in float32, then one bf16 rounding
+
+
+def forward_block(x_bits, W_gate, W_gu_bits, W_dn_bits, Ws_gu_bits, Ws_dn_bits, k, scale,
+                  norm_w_bits=None, eps=1e-6, score_bias=None, logit_bias=None):
+    """The Hy3 MoE block: shared expert plus routed experts.
+
+    out = SharedExpert(x) + sum_j w[t, j] * Expert_idx[t, j](x)   ("Tencent
+    Hy3-Flash Q&A", Q4.7), where the router scores route_norm(x) when
+    norm_w_bits is given (Q4.9) and selects with score_bias when given (Q4.3).
+    The experts, shared and routed, see x itself.  Ws_gu_bits [2F, d] and
+    Ws_dn_bits [d, F] are the shared expert's SwiGLU weights; its activation
+    and output are rounded to bf16 like a routed expert's.
+
+    Returns (out float64 [T, d], Route)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, d = x_bits.shape
+    xr = x_bits if norm_w_bits is None else rms_norm_bf16(x_bits, norm_w_bits, eps)
+    r = route(xr, W_gate, k, scale, logit_bias, score_bias=score_bias)
+    out = np.zeros((T, d), dtype=np.float64)
+    if T == 0:
+        return out, r
+    x = bf16_bits_to_f64(x_bits)
+    for e in np.unique(r.idx):
+        t, j = np.nonzero(r.idx == e)
+        y = expert_swiglu(x[t], bf16_bits_to_f64(W_gu_bits[e]), bf16_bits_to_f64(W_dn_bits[e]))
+        out[t] += r.w[t, j][:, None] * y
+    out += expert_swiglu(x, bf16_bits_to_f64(Ws_gu_bits), bf16_bits_to_f64(Ws_dn_bits))
+    return out, r
+
+
+def forward_block_tokens(tokens, x_bits, *args, **kwargs):
+    """Output rows of ``forward_block`` for the listed tokens only (tokens are
+    independent through the whole block)."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    return forward_block(np.asarray(x_bits)[tokens], *args, **kwargs)
 
 
 # ----------------------------------------------------------------------------- FP8
