@@ -1,7 +1,9 @@
 /*
  * hy3moe.h -- C ABI of the Hy3 MoE layer forward pass on MI355X (gfx950).
  *
- * The layer (one MoE FFN block of Hy3, routed experts only):
+ * The layer (one MoE FFN block of Hy3, routed experts; the full block with
+ * the shared expert, route_norm and the selection-only score bias is the
+ * hy3moe_block_* group further down):
  *   router   logits = x . W_gate^T (+ per-expert logit bias), computed in fp32;
  *            s = sigmoid(logits); the k experts with the largest s are chosen
  *            (equal scores: lower expert index first; slot j = j-th largest);
@@ -18,7 +20,8 @@
  *
  * Conventions for every call:
  *   - Every pointer argument is DEVICE memory owned by the caller, except the
- *     size_t* out-parameter of hy3moe_workspace_size (host).  The library never
+ *     size_t* out-parameters of the *_workspace_size calls and the
+ *     stage_events arrays of the *_timed calls (host).  The library never
  *     allocates, frees or synchronises; it keeps no state between calls apart
  *     from a thread-local copy of the last HIP error.
  *   - Layouts are dense and row-major.  bf16 = uint16_t bit patterns;
@@ -58,8 +61,9 @@ typedef enum {
 enum { HY3MOE_WEIGHTS_BF16 = 0, HY3MOE_WEIGHTS_FP8_E4M3 = 1 };
 
 /* Bytes of workspace hy3moe_forward (weight_dtype BF16) or hy3moe_forward_fp8
- * (FP8_E4M3) needs for these sizes; it also covers hy3moe_route and
- * hy3moe_permute.  Writes *bytes (host pointer).  Grows monotonically with T. */
+ * (FP8_E4M3) needs for these sizes; it also covers hy3moe_route,
+ * hy3moe_route_ex without norm_weight, and hy3moe_permute.  Writes *bytes
+ * (host pointer).  Grows monotonically with T. */
 int hy3moe_workspace_size(int T, int d, int E, int k, int d_ff, int weight_dtype, size_t* bytes);
 
 /* Router alone ("Tencent Hy3-295B architecture teardown", section 4.1).
@@ -146,6 +150,67 @@ int hy3moe_forward_fp8_timed(const uint16_t* x, const float* W_gate,
                              int T, int d, int E, int k, int d_ff, float scale, void* stream,
                              const float* logit_bias, int32_t* topk_idx, float* topk_w,
                              void* workspace, size_t workspace_bytes, void* const* stage_events);
+
+/* ---- the full Hy3 MoE block ("Tencent Hy3-Flash Q&A", Q4.3, Q4.7, Q4.9) ----
+ *
+ *   block out[t] = Shared(x_t) + sum_j w_j * Expert_idx[t,j](x_t)
+ *
+ * where Shared is a SwiGLU expert that every token passes through (Q4.7),
+ * the router scores route_norm(x) instead of x (Q4.9), and it chooses the k
+ * experts with the largest s + score_bias while the weights still use s
+ * (e_score_correction_bias, Q4.3; "Tencent Hy3-295B architecture teardown",
+ * section 4.1, router flow step 2).  The experts, shared and routed, see x.
+ *
+ * route_norm: r = fp32(1 / sqrt(sum_i x_i^2 / d + eps)) (sum, division and
+ * square root in fp64; the pages fix neither precision nor eps), the row
+ * x * r is rounded to bf16 and multiplied by the bf16 weight with one more
+ * bf16 rounding.  score_bias: choice value = fp32(s + b) (may be negative);
+ * equal values go to the lower expert index. */
+
+/* Bytes of workspace for hy3moe_block_forward at these sizes (with both
+ * route_norm and the shared expert); it also covers hy3moe_route_ex.  E <= 1023. */
+int hy3moe_block_workspace_size(int T, int d, int E, int k, int d_ff, size_t* bytes);
+
+/* Router of the full block.
+ *   norm_weight  bf16 [d] route_norm weight, or NULL for no route_norm
+ *   norm_eps     route_norm epsilon (fp32, >= 0; else HY3MOE_ERR_SHAPE)
+ *   logit_bias   fp32 [E] added to the logits before the sigmoid, or NULL
+ *   score_bias   fp32 [E] selection-only bias (e_score_correction_bias), or NULL
+ * Other arguments and outputs as for hy3moe_route; the workspace must hold
+ * what hy3moe_block_workspace_size (or, without norm_weight,
+ * hy3moe_workspace_size) reports for these sizes. */
+int hy3moe_route_ex(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,
+                    const float* W_gate, const float* logit_bias, const float* score_bias,
+                    int T, int d, int E, int k, float scale,
+                    int32_t* topk_idx, float* topk_w,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* The full block with bf16 experts.
+ *   norm_weight, norm_eps, score_bias   as for hy3moe_route_ex (each optional)
+ *   Ws_gate_up bf16 [2*d_ff, d], Ws_down bf16 [d, d_ff]: the shared expert,
+ *              with the routed experts' d_ff; both or neither (NULL)
+ *   out        fp32 [T, d] out, overwritten: shared + routed sum, no residual
+ * The shared expert runs as expert E of the grouped expert kernels, on every
+ * token; its activation and output are bf16 like a routed expert's, and its
+ * output row is added to the fp32 combine after the k routed terms with
+ * weight 1.  E <= 1023.  Other arguments as for hy3moe_forward. */
+int hy3moe_block_forward(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,
+                         const float* W_gate, const float* score_bias,
+                         const uint16_t* W_gate_up, const uint16_t* W_down,
+                         const uint16_t* Ws_gate_up, const uint16_t* Ws_down, float* out,
+                         int T, int d, int E, int k, int d_ff, float scale, void* stream,
+                         int32_t* topk_idx, float* topk_w,
+                         void* workspace, size_t workspace_bytes);
+
+/* hy3moe_block_forward with the six stage events of hy3moe_forward_timed
+ * (route_norm falls in the router stage). */
+int hy3moe_block_forward_timed(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,
+                               const float* W_gate, const float* score_bias,
+                               const uint16_t* W_gate_up, const uint16_t* W_down,
+                               const uint16_t* Ws_gate_up, const uint16_t* Ws_down, float* out,
+                               int T, int d, int E, int k, int d_ff, float scale, void* stream,
+                               int32_t* topk_idx, float* topk_w,
+                               void* workspace, size_t workspace_bytes, void* const* stage_events);
 
 /* Per-row e4m3 quantisation used by hy3moe_forward_fp8 for x:
  *   amax = max |x[r, :]|;  amax == 0 -> q = 0, s = 1;  otherwise

@@ -18,13 +18,18 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Regions used by hy3moe_route and hy3moe_permute come first, so their needs
-// are prefixes of the forward layout and do not depend on d or d_ff.
-Layout make_layout(int T, int d, int E, int k, int F, int dtype) {
+// Regions used by the routing and permute entries come first, so their needs
+// are prefixes of the forward layout and do not depend on d_ff.  shared: the
+// block's shared expert adds T expert rows (and one expert to the offsets);
+// norm: route_norm's bf16 copy of x.
+Layout make_layout(int T, int d, int E, int k, int F, int dtype, bool shared = false,
+                   bool norm = false) {
     Layout L{};
     const size_t Tk = static_cast<size_t>(T) * k;
+    const size_t R = Tk + (shared ? static_cast<size_t>(T) : 0);   // expert rows
+    L.rows = static_cast<int>(R);
     L.nb = (T + hy3::kRouteBlock - 1) / hy3::kRouteBlock;
-    L.max_mtiles = static_cast<int>(Tk / hy3::prefill_bm()) + E;
+    L.max_mtiles = static_cast<int>(R / hy3::prefill_bm()) + E + (shared ? 1 : 0);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -35,15 +40,16 @@ Layout make_layout(int T, int d, int E, int k, int F, int dtype) {
     L.planes = take(hy3::router_plane_elems(d, E) * sizeof(uint16_t));
     L.partial = take(L.nsplit > 1 ? static_cast<size_t>(L.nsplit) * T * E * sizeof(float) : 0);
     L.scores = take(static_cast<size_t>(T) * E * sizeof(float));
+    L.xn = take(norm ? static_cast<size_t>(T) * d * sizeof(uint16_t) : 0);
     L.blk_counts = take(static_cast<size_t>(E) * L.nb * sizeof(int32_t));
     L.blk_base = take(static_cast<size_t>(E) * L.nb * sizeof(int32_t));
     L.counts = take(static_cast<size_t>(E) * sizeof(int32_t));
-    L.offsets = take(static_cast<size_t>(E + 1) * sizeof(int32_t));
-    L.tile_off = take(static_cast<size_t>(E + 1) * sizeof(int32_t));
+    L.offsets = take(static_cast<size_t>(E + 2) * sizeof(int32_t));
+    L.tile_off = take(static_cast<size_t>(E + 2) * sizeof(int32_t));
     L.idx = take(Tk * sizeof(int32_t));
     L.w = take(Tk * sizeof(float));
     L.row_of = take(Tk * sizeof(int32_t));
-    L.tok_of = take(Tk * sizeof(int32_t));
+    L.tok_of = take(R * sizeof(int32_t));
     if (dtype == HY3MOE_WEIGHTS_FP8_E4M3) {
         L.h = take(Tk * F * sizeof(float));            // fp32 SwiGLU activations
         L.hq = take(Tk * F);                           // their e4m3 codes
@@ -52,10 +58,10 @@ Layout make_layout(int T, int d, int E, int k, int F, int dtype) {
         L.xq = take(static_cast<size_t>(T) * d);
         L.xs = take(static_cast<size_t>(T) * sizeof(float));
     } else {
-        L.h = take(Tk * F * sizeof(uint16_t));
+        L.h = take(R * F * sizeof(uint16_t));
         L.hq = L.hs = L.xq = L.xs = L.amax = 0;
     }
-    L.y = take(Tk * d * sizeof(uint16_t));
+    L.y = take(R * d * sizeof(uint16_t));
     L.total = off;
     return L;
 }
@@ -115,9 +121,37 @@ int hy3moe_route(const uint16_t* x, const float* W_gate, const float* logit_bias
     const Layout L = make_layout(T, d, E, k, 64, HY3MOE_WEIGHTS_BF16);
     if (workspace_bytes < route_bytes(L)) return HY3MOE_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
-    return hip_status(hy3::launch_router(x, W_gate, logit_bias, T, d, E, k, scale,
+    return hip_status(hy3::launch_router(x, W_gate, logit_bias, nullptr, T, d, E, k, scale,
                                          router_work(ws, L), topk_idx, topk_w, nullptr, L.nb,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int hy3moe_route_ex(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,
+                    const float* W_gate, const float* logit_bias, const float* score_bias, int T,
+                    int d, int E, int k, float scale, int32_t* topk_idx, float* topk_w,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_shape(T, d, E, k, 64);
+    if (st != HY3MOE_OK) return st;
+    if (!(norm_eps >= 0.f)) return HY3MOE_ERR_SHAPE;
+    if (T == 0) return HY3MOE_OK;
+    if (!x || !W_gate || !topk_idx || !topk_w || !workspace) return HY3MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(W_gate) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+        !aligned16(workspace) || (logit_bias && !aligned16(logit_bias)) ||
+        (score_bias && !aligned16(score_bias)) || (norm_weight && !aligned16(norm_weight)))
+        return HY3MOE_ERR_ALIGN;
+    const Layout L = make_layout(T, d, E, k, 64, HY3MOE_WEIGHTS_BF16, false, norm_weight != nullptr);
+    if (workspace_bytes < route_bytes(L)) return HY3MOE_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* xr = x;
+    if (norm_weight) {
+        uint16_t* xn = reinterpret_cast<uint16_t*>(ws + L.xn);
+        const hipError_t e = hy3::launch_rms_norm(x, norm_weight, T, d, norm_eps, xn, s);
+        if (e != hipSuccess) return hip_status(e);
+        xr = xn;
+    }
+    return hip_status(hy3::launch_router(xr, W_gate, logit_bias, score_bias, T, d, E, k, scale,
+                                         router_work(ws, L), topk_idx, topk_w, nullptr, L.nb, s));
 }
 
 int hy3moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts,
@@ -141,7 +175,7 @@ int hy3moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts
     e = hy3::launch_dispatch(topk_idx, T, E, k, L.nb, blk_counts,
                              reinterpret_cast<int32_t*>(ws + L.blk_base), counts, offsets,
                              reinterpret_cast<int32_t*>(ws + L.tile_off), hy3::prefill_bm(), row_of,
-                             token_of, s);
+                             token_of, 0, s);
     return hip_status(e);
 }
 
@@ -149,20 +183,30 @@ int hy3moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts
 
 namespace {
 
-static int forward_bf16(const uint16_t* x, const float* W_gate, const uint16_t* W_gate_up,
-                        const uint16_t* W_down, float* out, int T, int d, int E, int k, int d_ff,
-                        float scale, void* stream, const float* logit_bias, int32_t* topk_idx,
-                        float* topk_w, void* workspace, size_t workspace_bytes,
-                        void* const* ev) {
+// The bf16 layer, and the full block when any of its extras is given:
+// norm_w (route_norm), score_bias (selection-only bias), Ws_gu/Ws_dn (the
+// shared expert, both or neither).
+static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_eps,
+                        const float* W_gate, const float* logit_bias, const float* score_bias,
+                        const uint16_t* W_gate_up, const uint16_t* W_down, const uint16_t* Ws_gu,
+                        const uint16_t* Ws_dn, float* out, int T, int d, int E, int k, int d_ff,
+                        float scale, void* stream, int32_t* topk_idx, float* topk_w,
+                        void* workspace, size_t workspace_bytes, void* const* ev) {
+    const bool shared = Ws_gu != nullptr;
     int st = check_shape(T, d, E, k, d_ff);
     if (st != HY3MOE_OK) return st;
+    if (shared && E > 1023) return HY3MOE_ERR_UNSUPPORTED;
+    if (!(norm_eps >= 0.f)) return HY3MOE_ERR_SHAPE;
     if (T == 0) return HY3MOE_OK;
     if (!x || !W_gate || !W_gate_up || !W_down || !out || !workspace) return HY3MOE_ERR_NULL;
+    if ((Ws_gu == nullptr) != (Ws_dn == nullptr)) return HY3MOE_ERR_NULL;
     if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_gate_up) || !aligned16(W_down) ||
         !aligned16(out) || !aligned16(workspace) || (logit_bias && !aligned16(logit_bias)) ||
+        (score_bias && !aligned16(score_bias)) || (norm_w && !aligned16(norm_w)) ||
+        (Ws_gu && !aligned16(Ws_gu)) || (Ws_dn && !aligned16(Ws_dn)) ||
         (topk_idx && !aligned16(topk_idx)) || (topk_w && !aligned16(topk_w)))
         return HY3MOE_ERR_ALIGN;
-    const Layout L = make_layout(T, d, E, k, d_ff, HY3MOE_WEIGHTS_BF16);
+    const Layout L = make_layout(T, d, E, k, d_ff, HY3MOE_WEIGHTS_BF16, shared, norm_w != nullptr);
     if (workspace_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -175,34 +219,43 @@ static int forward_bf16(const uint16_t* x, const float* W_gate, const uint16_t* 
     int32_t* tok_of = reinterpret_cast<int32_t*>(ws + L.tok_of);
     uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
     uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
+    const int Eg = E + (shared ? 1 : 0);           // experts the GEMMs see
 
     hipError_t e = mark(ev, 0, s);
-    if (e != hipSuccess) return hip_status(e);
-    e = hy3::launch_router(x, W_gate, logit_bias, T, d, E, k, scale, router_work(ws, L), idx, w,
-                           blk_counts, L.nb, s);
+    const uint16_t* xr = x;                        // the router's input
+    if (e == hipSuccess && norm_w) {
+        uint16_t* xn = reinterpret_cast<uint16_t*>(ws + L.xn);
+        e = hy3::launch_rms_norm(x, norm_w, T, d, norm_eps, xn, s);
+        xr = xn;
+    }
+    if (e == hipSuccess)
+        e = hy3::launch_router(xr, W_gate, logit_bias, score_bias, T, d, E, k, scale,
+                               router_work(ws, L), idx, w, blk_counts, L.nb, s);
     if (e == hipSuccess) e = mark(ev, 1, s);
-    if (e != hipSuccess) return hip_status(e);
-    e = hy3::launch_dispatch(idx, T, E, k, L.nb, blk_counts,
-                             reinterpret_cast<int32_t*>(ws + L.blk_base),
-                             reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
-                             hy3::prefill_bm(), row_of, tok_of, s);
+    if (e == hipSuccess)
+        e = hy3::launch_dispatch(idx, T, E, k, L.nb, blk_counts,
+                                 reinterpret_cast<int32_t*>(ws + L.blk_base),
+                                 reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
+                                 hy3::prefill_bm(), row_of, tok_of, shared ? 1 : 0, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
-    if (e != hipSuccess) return hip_status(e);
     const bool decode = hy3::use_decode_path(T, d, d_ff, E, k);
-    if (decode)
-        e = hy3::launch_gate_up_decode(x, tok_of, W_gate_up, offsets, h, E, d, d_ff, s);
-    else
-        e = hy3::launch_gate_up_grouped(x, tok_of, W_gate_up, offsets, tile_off, L.max_mtiles, h, E,
-                                        d, d_ff, s);
+    if (e == hipSuccess) {
+        if (decode)
+            e = hy3::launch_gate_up_decode(x, tok_of, W_gate_up, Ws_gu, offsets, h, Eg, d, d_ff, s);
+        else
+            e = hy3::launch_gate_up_grouped(x, tok_of, W_gate_up, Ws_gu, offsets, tile_off,
+                                            L.max_mtiles, h, Eg, d, d_ff, s);
+    }
     if (e == hipSuccess) e = mark(ev, 3, s);
-    if (e != hipSuccess) return hip_status(e);
-    if (decode)
-        e = hy3::launch_down_decode(h, W_down, offsets, y, E, d, d_ff, s);
-    else
-        e = hy3::launch_down_grouped(h, W_down, offsets, tile_off, L.max_mtiles, y, E, d, d_ff, s);
+    if (e == hipSuccess) {
+        if (decode)
+            e = hy3::launch_down_decode(h, W_down, Ws_dn, offsets, y, Eg, d, d_ff, s);
+        else
+            e = hy3::launch_down_grouped(h, W_down, Ws_dn, offsets, tile_off, L.max_mtiles, y, Eg, d,
+                                         d_ff, s);
+    }
     if (e == hipSuccess) e = mark(ev, 4, s);
-    if (e != hipSuccess) return hip_status(e);
-    e = hy3::launch_combine(y, row_of, w, out, T, d, k, s);
+    if (e == hipSuccess) e = hy3::launch_combine(y, row_of, w, out, T, d, k, shared ? T * k : -1, s);
     if (e == hipSuccess) e = mark(ev, 5, s);
     return hip_status(e);
 }
@@ -230,14 +283,14 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
 
     hipError_t e = mark(ev, 0, s);
     if (e == hipSuccess)
-        e = hy3::launch_router(x, W_gate, logit_bias, T, d, E, k, scale, router_work(ws, L), idx, w,
-                               reinterpret_cast<int32_t*>(ws + L.blk_counts), L.nb, s);
+        e = hy3::launch_router(x, W_gate, logit_bias, nullptr, T, d, E, k, scale, router_work(ws, L),
+                               idx, w, reinterpret_cast<int32_t*>(ws + L.blk_counts), L.nb, s);
     if (e == hipSuccess) e = mark(ev, 1, s);
     if (e == hipSuccess)
         e = hy3::launch_dispatch(idx, T, E, k, L.nb, reinterpret_cast<int32_t*>(ws + L.blk_counts),
                                  reinterpret_cast<int32_t*>(ws + L.blk_base),
                                  reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
-                                 hy3::prefill_bm(), row_of, tok_of, s);
+                                 hy3::prefill_bm(), row_of, tok_of, 0, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
     if (e == hipSuccess) e = hy3::launch_quant_rows(x, T, d, xq, xs, s);
     if (e == hipSuccess) e = hy3::launch_fill_u32(amax, Tk, 0u, s);
@@ -250,7 +303,7 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
         e = hy3::launch_down_fp8(hq, hs, Wq_dn, s_dn, offsets, tile_off, L.max_mtiles, y, E, d, d_ff,
                                  s);
     if (e == hipSuccess) e = mark(ev, 4, s);
-    if (e == hipSuccess) e = hy3::launch_combine(y, row_of, w, out, T, d, k, s);
+    if (e == hipSuccess) e = hy3::launch_combine(y, row_of, w, out, T, d, k, -1, s);
     if (e == hipSuccess) e = mark(ev, 5, s);
     return hip_status(e);
 }
@@ -263,8 +316,9 @@ int hy3moe_forward(const uint16_t* x, const float* W_gate, const uint16_t* W_gat
                    const uint16_t* W_down, float* out, int T, int d, int E, int k, int d_ff,
                    float scale, void* stream, const float* logit_bias, int32_t* topk_idx,
                    float* topk_w, void* workspace, size_t workspace_bytes) {
-    return forward_bf16(x, W_gate, W_gate_up, W_down, out, T, d, E, k, d_ff, scale, stream,
-                        logit_bias, topk_idx, topk_w, workspace, workspace_bytes, nullptr);
+    return forward_bf16(x, nullptr, 0.f, W_gate, logit_bias, nullptr, W_gate_up, W_down, nullptr,
+                        nullptr, out, T, d, E, k, d_ff, scale, stream, topk_idx, topk_w, workspace,
+                        workspace_bytes, nullptr);
 }
 
 int hy3moe_forward_timed(const uint16_t* x, const float* W_gate, const uint16_t* W_gate_up,
@@ -272,8 +326,40 @@ int hy3moe_forward_timed(const uint16_t* x, const float* W_gate, const uint16_t*
                          float scale, void* stream, const float* logit_bias, int32_t* topk_idx,
                          float* topk_w, void* workspace, size_t workspace_bytes,
                          void* const* stage_events) {
-    return forward_bf16(x, W_gate, W_gate_up, W_down, out, T, d, E, k, d_ff, scale, stream,
-                        logit_bias, topk_idx, topk_w, workspace, workspace_bytes, stage_events);
+    return forward_bf16(x, nullptr, 0.f, W_gate, logit_bias, nullptr, W_gate_up, W_down, nullptr,
+                        nullptr, out, T, d, E, k, d_ff, scale, stream, topk_idx, topk_w, workspace,
+                        workspace_bytes, stage_events);
+}
+
+int hy3moe_block_workspace_size(int T, int d, int E, int k, int d_ff, size_t* bytes) {
+    if (!bytes) return HY3MOE_ERR_NULL;
+    const int st = check_shape(T, d, E, k, d_ff);
+    if (st != HY3MOE_OK) return st;
+    if (E > 1023) return HY3MOE_ERR_UNSUPPORTED;
+    *bytes = make_layout(T, d, E, k, d_ff, HY3MOE_WEIGHTS_BF16, true, true).total;
+    return HY3MOE_OK;
+}
+
+int hy3moe_block_forward(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,
+                         const float* W_gate, const float* score_bias, const uint16_t* W_gate_up,
+                         const uint16_t* W_down, const uint16_t* Ws_gate_up, const uint16_t* Ws_down,
+                         float* out, int T, int d, int E, int k, int d_ff, float scale, void* stream,
+                         int32_t* topk_idx, float* topk_w, void* workspace, size_t workspace_bytes) {
+    return forward_bf16(x, norm_weight, norm_eps, W_gate, nullptr, score_bias, W_gate_up, W_down,
+                        Ws_gate_up, Ws_down, out, T, d, E, k, d_ff, scale, stream, topk_idx, topk_w,
+                        workspace, workspace_bytes, nullptr);
+}
+
+int hy3moe_block_forward_timed(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,
+                               const float* W_gate, const float* score_bias,
+                               const uint16_t* W_gate_up, const uint16_t* W_down,
+                               const uint16_t* Ws_gate_up, const uint16_t* Ws_down, float* out, int T,
+                               int d, int E, int k, int d_ff, float scale, void* stream,
+                               int32_t* topk_idx, float* topk_w, void* workspace,
+                               size_t workspace_bytes, void* const* stage_events) {
+    return forward_bf16(x, norm_weight, norm_eps, W_gate, nullptr, score_bias, W_gate_up, W_down,
+                        Ws_gate_up, Ws_down, out, T, d, E, k, d_ff, scale, stream, topk_idx, topk_w,
+                        workspace, workspace_bytes, stage_events);
 }
 
 

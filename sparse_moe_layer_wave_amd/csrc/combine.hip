@@ -2,8 +2,10 @@
 // the k terms added in slot order with fp32 fused multiply-adds (bf16 expert
 // outputs are widened to fp32 before the sum, as the fp32-combine option of
 // the wmrh.cn Hy3 assembly blog, section 2.3, describes; the weighted sum of
-// "DeepSeek V4-Flash architecture Q&A", Q8.4).  Memory-bound: k bf16 rows in,
-// one fp32 row out per token.
+// "DeepSeek V4-Flash architecture Q&A", Q8.4).  With the full block's shared
+// expert ("Tencent Hy3-Flash Q&A", Q4.7) its output row for the token is
+// added last, with weight 1.  Memory-bound: k (+1) bf16 rows in, one fp32 row
+// out per token.
 
 #include "internal.h"
 
@@ -15,7 +17,8 @@ constexpr int kThreads = 256;
 __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict__ y,
                                                      const int32_t* __restrict__ row_of,
                                                      const float* __restrict__ w,
-                                                     float* __restrict__ out, int d, int k) {
+                                                     float* __restrict__ out, int d, int k,
+                                                     int shared_row0) {
     const int t = blockIdx.x;
     __shared__ int s_row[16];
     __shared__ float s_w[16];
@@ -36,6 +39,15 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
                 acc[2 * i + 1] = fmaf(wj, __uint_as_float(p[i] & 0xffff0000u), acc[2 * i + 1]);
             }
         }
+        if (shared_row0 >= 0) {
+            const uint4 v = *reinterpret_cast<const uint4*>(y + (static_cast<size_t>(shared_row0) + t) * d + c);
+            const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += __uint_as_float(p[i] << 16);
+                acc[2 * i + 1] += __uint_as_float(p[i] & 0xffff0000u);
+            }
+        }
         float4* o = reinterpret_cast<float4*>(out + static_cast<size_t>(t) * d + c);
         o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
         o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
@@ -45,8 +57,9 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of, const float* w, float* out,
-                          int T, int d, int k, hipStream_t s) {
-    hipLaunchKernelGGL(k_combine, dim3(T), dim3(kThreads), 0, s, y, row_of, w, out, d, k);
+                          int T, int d, int k, int shared_row0, hipStream_t s) {
+    hipLaunchKernelGGL(k_combine, dim3(T), dim3(kThreads), 0, s, y, row_of, w, out, d, k,
+                       shared_row0);
     return hipGetLastError();
 }
 

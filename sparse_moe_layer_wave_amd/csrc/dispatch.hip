@@ -15,7 +15,9 @@
 //                  offsets[e] + base[e, block] + #(tokens of the block before t
 //                  that chose e).
 // All of it is integer work with no atomics whose order matters, so the
-// result is the same on every run.
+// result is the same on every run.  With the shared expert of the full block
+// ("Tencent Hy3-Flash Q&A", Q4.7), it becomes expert E, whose rows are
+// T*k + t, one per token: the GEMMs then treat it like any routed expert.
 
 #include "internal.h"
 
@@ -71,16 +73,18 @@ __global__ __launch_bounds__(256) void k_block_scan(const int32_t* __restrict__ 
     if (threadIdx.x == 0) counts[e] = running;
 }
 
-// One workgroup of 1024 threads; E <= 1024.  offsets = exclusive scan of the
-// counts; tile_off = exclusive scan of ceil(count / bm), the M-tiles of the
-// grouped GEMMs.
+// One workgroup of 1024 threads over n = E (+1 with a shared expert, whose
+// count is `extra`) <= 1024 experts.  offsets = exclusive scan of the counts;
+// tile_off = exclusive scan of ceil(count / bm), the row blocks of the grouped
+// GEMMs.
 __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ counts, int E,
-                                                  int32_t* __restrict__ offsets,
+                                                  int extra, int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ tile_off, int bm) {
     __shared__ int s_cnt[1024];
     __shared__ int s_til[1024];
     const int tid = threadIdx.x;
-    const int c = tid < E ? counts[tid] : 0;
+    const int n = E + (extra > 0 ? 1 : 0);
+    const int c = tid < E ? counts[tid] : (tid < n ? extra : 0);
     const int nt = (c + bm - 1) / bm;
     s_cnt[tid] = c;
     s_til[tid] = nt;
@@ -93,22 +97,24 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
         s_til[tid] += a1;
         __syncthreads();
     }
-    if (tid < E) {
+    if (tid < n) {
         offsets[tid] = s_cnt[tid] - c;
         tile_off[tid] = s_til[tid] - nt;
     }
     if (tid == 0) {
-        offsets[E] = s_cnt[1023];
-        tile_off[E] = s_til[1023];
+        offsets[n] = s_cnt[1023];
+        tile_off[n] = s_til[1023];
     }
 }
 
+// shared_row0 >= 0: the shared expert's rows start there, one per token in
+// token order.
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, int T, int E,
                                                 int k, int nb,
                                                 const int32_t* __restrict__ blk_base,
                                                 const int32_t* __restrict__ offsets,
                                                 int32_t* __restrict__ row_of,
-                                                int32_t* __restrict__ tok_of) {
+                                                int32_t* __restrict__ tok_of, int shared_row0) {
     __shared__ unsigned long long mask[1024];
     for (int e = threadIdx.x; e < E; e += 256) mask[e] = 0ull;
     __syncthreads();
@@ -130,6 +136,12 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
             const int row = offsets[e] + blk_base[static_cast<size_t>(e) * nb + b] + rank;
             row_of[pair] = row;
             tok_of[row] = t;
+        }
+    }
+    if (shared_row0 >= 0) {
+        for (int tl = threadIdx.x; tl < kRouteBlock; tl += 256) {
+            const int t = b * kRouteBlock + tl;
+            if (t < T) tok_of[shared_row0 + t] = t;
         }
     }
 }
@@ -162,11 +174,12 @@ hipError_t launch_block_counts(const int32_t* idx, int T, int E, int k, int nb,
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
                            const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,
                            int32_t* offsets, int32_t* tile_off, int bm, int32_t* row_of,
-                           int32_t* tok_of, hipStream_t s) {
+                           int32_t* tok_of, int shared, hipStream_t s) {
     hipLaunchKernelGGL(k_block_scan, dim3(E), dim3(256), 0, s, blk_counts, blk_base, counts, nb);
-    hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, s, counts, E, offsets, tile_off, bm);
+    hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, s, counts, E, shared ? T : 0, offsets,
+                       tile_off, bm);
     hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(256), 0, s, idx, T, E, k, nb, blk_base, offsets,
-                       row_of, tok_of);
+                       row_of, tok_of, shared ? T * k : -1);
     return hipGetLastError();
 }
 

@@ -20,7 +20,10 @@
 //          ("DeepSeek V4-Flash architecture Q&A", Q4.5).
 // down:    wave w of block (e, n0) owns W_down rows n0+32w..+32 and writes
 //          y[r, n] = bf16(h[r] . W_down[e][n]).
-// An expert with more than 16 rows is handled in passes of 16 rows.
+// An expert with more than 16 rows is handled in passes of 16 rows.  The
+// shared expert of the full block, when present, is the last expert (all T
+// tokens, weights W_last); its workgroups are the longest, so they are
+// scheduled first.
 
 #include "internal.h"
 
@@ -44,11 +47,13 @@ __global__ __launch_bounds__(256) void k_decode_gemm(
     const uint16_t* __restrict__ A,        // gate_up: x [T, K]; down: h [rows, K]
     const int32_t* __restrict__ tok_of,    // gate_up only
     const uint16_t* __restrict__ W,        // gate_up: [E, 2N, K]; down: [E, N, K]
+    const uint16_t* __restrict__ W_last,   // non-NULL: weights of expert E - 1 (shared)
     const int32_t* __restrict__ offsets,
     uint16_t* __restrict__ C,              // gate_up: h [rows, N]; down: y [rows, N]
     int K, int N) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kSlab];
-    const int e = blockIdx.x;
+    const int E = gridDim.x;
+    const int e = W_last ? (blockIdx.x == 0 ? E - 1 : blockIdx.x - 1) : blockIdx.x;
     const int rbeg = offsets[e];
     const int rend = offsets[e + 1];
     if (rbeg == rend) return;
@@ -60,19 +65,17 @@ __global__ __launch_bounds__(256) void k_decode_gemm(
 
     // weight row of slab row sr (0..31): n-tile sr/16, row sr%16 of it
     int col0;
-    size_t wrow_base;   // element offset of slab row 0's weight row; others via wrow_of
-    const size_t wbase = static_cast<size_t>(e) * (GATE_UP ? 2 * N : N) * K;
+    const uint16_t* We = (W_last && e == E - 1) ? W_last : W + static_cast<size_t>(e) * (GATE_UP ? 2 * N : N) * K;
     auto wrow_of = [&](int sr) -> int {
         if (GATE_UP) return (sr < 16 ? 0 : N) + blockIdx.y * 64 + wave * 16 + (sr & 15);
         return blockIdx.y * 128 + wave * 32 + sr;
     };
-    (void)wrow_base;
     col0 = GATE_UP ? blockIdx.y * 64 + wave * 16 : blockIdx.y * 128 + wave * 32;
     // load instruction i (0..7) of a batch: slab rows 4i + lane/16, bytes (lane%16)*16
     const uint16_t* wsrc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        wsrc[i] = W + wbase + static_cast<size_t>(wrow_of(4 * i + (lane >> 4))) * K + (lane & 15) * 8;
+        wsrc[i] = We + static_cast<size_t>(wrow_of(4 * i + (lane >> 4))) * K + (lane & 15) * 8;
     int wdst[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) wdst[i] = slab_off(4 * i + (lane >> 4), lane & 15);
@@ -140,17 +143,18 @@ bool use_decode_path(int T, int d, int F, int E, int k) {
 }
 
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
-                                 const int32_t* offsets, uint16_t* h, int E, int d, int F,
-                                 hipStream_t s) {
+                                 const uint16_t* W_last, const int32_t* offsets, uint16_t* h,
+                                 int E, int d, int F, hipStream_t s) {
     hipLaunchKernelGGL(k_decode_gemm<true>, dim3(E, F / 64), dim3(256), 0, s, x, tok_of, W_gu,
-                       offsets, h, d, F);
+                       W_last, offsets, h, d, F);
     return hipGetLastError();
 }
 
-hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const int32_t* offsets,
-                              uint16_t* y, int E, int d, int F, hipStream_t s) {
+hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uint16_t* W_last,
+                              const int32_t* offsets, uint16_t* y, int E, int d, int F,
+                              hipStream_t s) {
     hipLaunchKernelGGL(k_decode_gemm<false>, dim3(E, d / 128), dim3(256), 0, s, h, nullptr, W_dn,
-                       offsets, y, F, d);
+                       W_last, offsets, y, F, d);
     return hipGetLastError();
 }
 

@@ -100,6 +100,7 @@ struct Args {
     const uint8_t* A;                              // gate_up: x [T, K]; down: h [rows, K]
     const int32_t* tok_of;                         // gate_up: token of each row
     const uint8_t* W;                              // gate_up: [E, 2N, K]; down: [E, N, K]
+    const uint8_t* W_last;                         // non-NULL: weights of expert E - 1 (shared)
     const int32_t* offsets;                        // [E+1] row offsets
     const int32_t* tile_off;                       // [E+1] offsets in 128-row blocks
     uint16_t* C;                                   // bf16 out: gate_up h (bf16 mode) or y [rows, N]
@@ -151,7 +152,10 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u)
                 wr = u.n * NCOLS + p;
                 wr = wr < N ? wr : 0;
             }
-            src[j] = g.W + (static_cast<size_t>(u.e) * (GATE_UP ? 2 * N : N) + wr) * rowbytes + lc * 16;
+            const uint8_t* We = (g.W_last && u.e == g.E - 1)
+                                    ? g.W_last
+                                    : g.W + static_cast<size_t>(u.e) * (GATE_UP ? 2 * N : N) * rowbytes;
+            src[j] = We + static_cast<size_t>(wr) * rowbytes + lc * 16;
         }
     }
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
@@ -403,18 +407,21 @@ hipError_t launch(Args g, int max_blocks, hipStream_t s) {
 int prefill_bm() { return 128; }
 
 hipError_t launch_gate_up_grouped(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
-                                  const int32_t* offsets, const int32_t* tile_off, int max_blocks,
-                                  uint16_t* h, int E, int d, int F, hipStream_t s) {
-    Args g{reinterpret_cast<const uint8_t*>(x), tok_of, reinterpret_cast<const uint8_t*>(W_gu), offsets,
-           tile_off, h, nullptr, nullptr, nullptr, nullptr, d, F, E, 0};
+                                  const uint16_t* W_last, const int32_t* offsets,
+                                  const int32_t* tile_off, int max_blocks, uint16_t* h, int E, int d,
+                                  int F, hipStream_t s) {
+    Args g{reinterpret_cast<const uint8_t*>(x), tok_of, reinterpret_cast<const uint8_t*>(W_gu),
+           reinterpret_cast<const uint8_t*>(W_last), offsets, tile_off, h, nullptr, nullptr, nullptr,
+           nullptr, d, F, E, 0};
     return launch<GU_BF16>(g, max_blocks, s);
 }
 
-hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const int32_t* offsets,
-                               const int32_t* tile_off, int max_blocks, uint16_t* y, int E, int d,
-                               int F, hipStream_t s) {
-    Args g{reinterpret_cast<const uint8_t*>(h), nullptr, reinterpret_cast<const uint8_t*>(W_dn), offsets,
-           tile_off, y, nullptr, nullptr, nullptr, nullptr, F, d, E, 0};
+hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const uint16_t* W_last,
+                               const int32_t* offsets, const int32_t* tile_off, int max_blocks,
+                               uint16_t* y, int E, int d, int F, hipStream_t s) {
+    Args g{reinterpret_cast<const uint8_t*>(h), nullptr, reinterpret_cast<const uint8_t*>(W_dn),
+           reinterpret_cast<const uint8_t*>(W_last), offsets, tile_off, y, nullptr, nullptr, nullptr,
+           nullptr, F, d, E, 0};
     return launch<DN_BF16>(g, max_blocks, s);
 }
 
@@ -422,14 +429,14 @@ hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const int32_t*
                               const uint8_t* Wq, const float* ws, const int32_t* offsets,
                               const int32_t* tile_off, int max_blocks, float* h32, uint32_t* amax,
                               int E, int d, int F, hipStream_t s) {
-    Args g{xq, tok_of, Wq, offsets, tile_off, nullptr, xs, ws, h32, amax, d, F, E, 0};
+    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, xs, ws, h32, amax, d, F, E, 0};
     return launch<GU_FP8>(g, max_blocks, s);
 }
 
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq, const float* ws,
                            const int32_t* offsets, const int32_t* tile_off, int max_blocks,
                            uint16_t* y, int E, int d, int F, hipStream_t s) {
-    Args g{hq, nullptr, Wq, offsets, tile_off, y, hs, ws, nullptr, nullptr, F, d, E, 0};
+    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, ws, nullptr, nullptr, F, d, E, 0};
     return launch<DN_FP8>(g, max_blocks, s);
 }
 

@@ -35,11 +35,12 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 
 // Workspace carving, computed identically on the host for every entry point.
 struct Layout {
-    size_t planes, partial, scores, blk_counts, blk_base, counts, offsets, tile_off, idx, w, row_of, tok_of, h, y,
-        xq, xs, hq, hs, amax, total;
+    size_t planes, partial, scores, blk_counts, blk_base, counts, offsets, tile_off, idx, w,
+        row_of, tok_of, h, y, xq, xs, hq, hs, amax, xn, total;
     int nb;              // routing blocks
     int nsplit;          // router d-chunks
-    int max_mtiles;      // upper bound on M-tiles of the grouped GEMMs
+    int max_mtiles;      // upper bound on row blocks of the grouped GEMMs
+    int rows;            // expert rows: T * k, plus T with a shared expert
 };
 
 // ---- launchers (each returns hipGetLastError() after enqueueing) ----
@@ -53,35 +54,49 @@ struct RouterWork {
 };
 int router_nsplit(int T, int d, int E);
 size_t router_plane_elems(int d, int E);
-hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bias, int T, int d,
-                         int E, int k, float scale, const RouterWork& rw, int32_t* idx, float* w,
-                         int32_t* blk_counts, int nb, hipStream_t s);
+// score_bias: selection-only bias added to the scores (NULL: none)
+hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bias,
+                         const float* score_bias, int T, int d, int E, int k, float scale,
+                         const RouterWork& rw, int32_t* idx, float* w, int32_t* blk_counts, int nb,
+                         hipStream_t s);
+// route_norm: xn = RMSNorm(x) * w as bf16 rows
+hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* w, int T, int d, float eps,
+                           uint16_t* xn, hipStream_t s);
 
+// shared = 1 appends expert E with every token as its rows (rows T*k + t),
+// so offsets and tile_off then hold E + 2 entries
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
                            const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,
                            int32_t* offsets, int32_t* tile_off, int bm, int32_t* row_of,
-                           int32_t* tok_of, hipStream_t s);
+                           int32_t* tok_of, int shared, hipStream_t s);
 
 // prefill-sized batches: MFMA grouped GEMMs over row blocks of prefill_bm() rows
-// (max_blocks bounds the number of row blocks, tile_off[E])
+// (max_blocks bounds the number of row blocks, tile_off[E]).  E counts the
+// experts of offsets/tile_off; with W_last non-NULL the last of them is the
+// shared expert, whose weights are W_last instead of W[E - 1].
 int prefill_bm();
 hipError_t launch_gate_up_grouped(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
-                                  const int32_t* offsets, const int32_t* tile_off, int max_blocks,
-                                  uint16_t* h, int E, int d, int F, hipStream_t s);
-hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const int32_t* offsets,
-                               const int32_t* tile_off, int max_blocks, uint16_t* y, int E, int d,
-                               int F, hipStream_t s);
+                                  const uint16_t* W_last, const int32_t* offsets,
+                                  const int32_t* tile_off, int max_blocks, uint16_t* h, int E, int d,
+                                  int F, hipStream_t s);
+hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const uint16_t* W_last,
+                               const int32_t* offsets, const int32_t* tile_off, int max_blocks,
+                               uint16_t* y, int E, int d, int F, hipStream_t s);
 
-// decode-sized batches: weight streaming, one workgroup per (expert, weight slice)
+// decode-sized batches: weight streaming, one workgroup per (expert, weight
+// slice); E and W_last as for the grouped GEMMs
 bool use_decode_path(int T, int d, int F, int E, int k);
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
-                                 const int32_t* offsets, uint16_t* h, int E, int d, int F,
-                                 hipStream_t s);
-hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const int32_t* offsets,
-                              uint16_t* y, int E, int d, int F, hipStream_t s);
+                                 const uint16_t* W_last, const int32_t* offsets, uint16_t* h,
+                                 int E, int d, int F, hipStream_t s);
+hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uint16_t* W_last,
+                              const int32_t* offsets, uint16_t* y, int E, int d, int F,
+                              hipStream_t s);
 
+// shared_row0 >= 0: row shared_row0 + t of y (the shared expert's output for
+// token t) is added with weight 1 after the k routed terms
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of, const float* w, float* out,
-                          int T, int d, int k, hipStream_t s);
+                          int T, int d, int k, int shared_row0, hipStream_t s);
 
 // fp8 path
 __device__ __forceinline__ uint8_t f32_to_e4m3(float v) {

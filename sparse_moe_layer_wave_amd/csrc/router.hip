@@ -1,6 +1,7 @@
 // Router of the Hy3 MoE layer: fp32 logits, sigmoid scores, top-k selection
 // and the renormalised, scaled weights ("Tencent Hy3-295B architecture
-// teardown", section 4.1, router flow steps 1, 3, 4 and 5).
+// teardown", section 4.1, router flow steps 1-5), and route_norm, the RMSNorm
+// of the router's input ("Tencent Hy3-Flash Q&A", Q4.9).
 //
 // Logits.  The gate weight is fp32 and the hidden states are bf16; the pages'
 // router casts both to float before the linear map.  k_router_prep splits each
@@ -8,15 +9,19 @@
 // exactly (8 significant bits each), so x.w = x.hi + x.mid + x.lo with every
 // product exact in fp32: an fp32-accurate GEMM on bf16 MFMA (fp32
 // accumulate) for three times the bf16 work.  Small batches split the d-sum
-// over nsplit workgroups; the last of them to finish (an atomic ticket per
-// output block) adds the partial sums in the fixed order s = 0..nsplit-1, so
-// the result does not depend on scheduling.
+// over nsplit workgroups, and a second kernel adds the partial sums in the
+// fixed order s = 0..nsplit-1, so the result does not depend on scheduling.
 //
-// Selection.  Scores lie in [0, 1], so their fp32 bit patterns order like the
-// values; key = (score bits << 32) | ~expert makes "largest score, then lowest
-// expert index" a plain 64-bit maximum.  Sixteen lanes (one DPP row) serve
-// one token: each scans every 16th expert for its best untaken key, the row
-// takes the maximum with row_ror DPP moves, k times.
+// Selection.  The choice value is the score, or the score plus the
+// selection-only e_score_correction_bias (a float32 addition; "Tencent
+// Hy3-Flash Q&A", Q4.3; router flow step 2), which may be negative.  Its bit
+// pattern is mapped to an unsigned key that orders like the value (sign bit
+// set: all bits flipped, else the sign bit set), and key = (value key << 32) |
+// ~expert makes "largest value, then lowest expert index" a plain 64-bit
+// maximum.  Sixteen lanes (one DPP row) serve one token: each scans every 16th
+// expert for its best untaken key, the row takes the maximum with row_ror DPP
+// moves, k times.  The weights use the chosen experts' scores, summed in slot
+// order.
 
 #include "internal.h"
 
@@ -184,10 +189,15 @@ constexpr int kSelThreads = 1024;   // 16 waves x 4 tokens = 64 tokens (one rout
 // (tb = 64 when E is small; larger E takes the block in sub-batches), then
 // selects k experts per token, 16 lanes each.  Writes idx/w and, when
 // blk_counts is given, the block's per-expert pair count.
+__device__ __forceinline__ uint32_t order_key(float v) {
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
 __global__ __launch_bounds__(kSelThreads) void k_router_select(
-    const float* __restrict__ scores, int T, int E, int k, float scale, int tb,
-    int32_t* __restrict__ idx, float* __restrict__ wout, int32_t* __restrict__ blk_counts,
-    int nb) {
+    const float* __restrict__ scores, const float* __restrict__ score_bias, int T, int E, int k,
+    float scale, int tb, int32_t* __restrict__ idx, float* __restrict__ wout,
+    int32_t* __restrict__ blk_counts, int nb) {
     extern __shared__ uint32_t s_score[];              // [tb][E + 1]
     __shared__ unsigned long long mask[1024];
     const int tid = threadIdx.x;
@@ -205,7 +215,8 @@ __global__ __launch_bounds__(kSelThreads) void k_router_select(
         const float* src = scores + static_cast<size_t>(t_first) * E;
         for (int p = tid; p < ntok * E; p += kSelThreads) {
             const int tl = p / E;
-            s_score[tl * ld + (p - tl * E)] = __float_as_uint(src[p]);
+            const int e = p - tl * E;
+            s_score[tl * ld + e] = order_key(score_bias ? src[p] + score_bias[e] : src[p]);
         }
         __syncthreads();
 
@@ -213,7 +224,6 @@ __global__ __launch_bounds__(kSelThreads) void k_router_select(
         const uint32_t* srow = s_score + (active ? ts : 0) * ld;
         unsigned long long taken = 0ull;                   // bit q: expert j + 16q chosen
         int my_e = 0;
-        float my_s = 0.f, sum = 0.f;
         for (int r = 0; r < k; ++r) {
             unsigned long long best = 0ull;
             if (active) {
@@ -228,14 +238,13 @@ __global__ __launch_bounds__(kSelThreads) void k_router_select(
             }
             best = row16_max(best);
             const int e_win = static_cast<int>(~static_cast<uint32_t>(best & 0xffffffffull));
-            const float s_win = __uint_as_float(static_cast<uint32_t>(best >> 32));
             if ((e_win & 15) == j) taken |= 1ull << (e_win >> 4);
-            if (r == j) {
-                my_e = e_win;
-                my_s = s_win;
-            }
-            sum += s_win;                                  // slot order, same in every lane
+            if (r == j) my_e = e_win;
         }
+        // lane j < k holds slot j; the weights use the scores themselves
+        const float my_s = (active && j < k) ? src[static_cast<size_t>(ts) * E + my_e] : 0.f;
+        float sum = 0.f;
+        for (int r = 0; r < k; ++r) sum += __shfl(my_s, (lane & ~15) | r, 64);   // slot order
         if (active && j < k) {
             const size_t pair = static_cast<size_t>(t_first + ts) * k + j;
             idx[pair] = my_e;
@@ -269,9 +278,10 @@ int router_nsplit(int T, int d, int E) {
 
 size_t router_plane_elems(int d, int E) { return static_cast<size_t>(3) * E * d; }
 
-hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bias, int T, int d,
-                         int E, int k, float scale, const RouterWork& rw, int32_t* idx, float* w,
-                         int32_t* blk_counts, int nb, hipStream_t s) {
+hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bias,
+                         const float* score_bias, int T, int d, int E, int k, float scale,
+                         const RouterWork& rw, int32_t* idx, float* w, int32_t* blk_counts, int nb,
+                         hipStream_t s) {
     const size_t n = static_cast<size_t>(E) * d;
     hipLaunchKernelGGL(k_router_prep, dim3(static_cast<unsigned>((n / 4 + 255) / 256)), dim3(256), 0,
                        s, W_gate, rw.planes, n);
@@ -286,8 +296,66 @@ hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bi
     }
     const int tb = select_tokens_per_pass(E);
     hipLaunchKernelGGL(k_router_select, dim3(nb), dim3(kSelThreads),
-                       static_cast<size_t>(tb) * (E + 1) * sizeof(uint32_t), s, rw.scores, T, E,
-                       k, scale, tb, idx, w, blk_counts, nb);
+                       static_cast<size_t>(tb) * (E + 1) * sizeof(uint32_t), s, rw.scores,
+                       score_bias, T, E, k, scale, tb, idx, w, blk_counts, nb);
+    return hipGetLastError();
+}
+
+namespace {
+
+constexpr int kNormThreads = 256;
+
+// route_norm: one workgroup per row.  The pages fix neither the precision nor
+// eps; this is the usual bf16-model reading: the sum of squares (exact
+// products of bf16 values) is accumulated in fp64, r = float(1 / sqrt(sum / d
+// + eps)) with the division and square root in fp64, the normalised row is
+// cast to bf16 and the bf16 weight is applied with one more bf16 rounding
+// (the product of two bf16 values is exact in fp32).
+__global__ __launch_bounds__(kNormThreads) void k_rms_norm_bf16(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ wgt,
+                                                               int d, float eps,
+                                                               uint16_t* __restrict__ xn) {
+    __shared__ double red[kNormThreads / 64];
+    const size_t row = blockIdx.x;
+    const uint16_t* xr = x + row * d;
+    double ss = 0.0;
+    for (int c = threadIdx.x * 8; c < d; c += kNormThreads * 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
+        const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double a = __uint_as_float(p[i] << 16), b = __uint_as_float(p[i] & 0xffff0000u);
+            ss += a * a + b * b;                          // exact products (bf16 squares fit fp64)
+        }
+    }
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    double tot = 0.0;
+    for (int i = 0; i < kNormThreads / 64; ++i) tot += red[i];
+    const float r = static_cast<float>(1.0 / sqrt(tot / d + static_cast<double>(eps)));
+    for (int c = threadIdx.x * 8; c < d; c += kNormThreads * 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
+        const uint4 g = *reinterpret_cast<const uint4*>(wgt + c);
+        const uint32_t p[4] = {v.x, v.y, v.z, v.w}, q[4] = {g.x, g.y, g.z, g.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a0 = bf16_to_f32(f32_to_bf16(__uint_as_float(p[i] << 16) * r));
+            const float a1 = bf16_to_f32(f32_to_bf16(__uint_as_float(p[i] & 0xffff0000u) * r));
+            const uint32_t y0 = f32_to_bf16(a0 * __uint_as_float(q[i] << 16));
+            const uint32_t y1 = f32_to_bf16(a1 * __uint_as_float(q[i] & 0xffff0000u));
+            o[i] = y0 | (y1 << 16);
+        }
+        *reinterpret_cast<uint4*>(xn + row * d + c) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* w, int T, int d, float eps,
+                           uint16_t* xn, hipStream_t s) {
+    hipLaunchKernelGGL(k_rms_norm_bf16, dim3(T), dim3(kNormThreads), 0, s, x, w, d, eps, xn);
     return hipGetLastError();
 }
 

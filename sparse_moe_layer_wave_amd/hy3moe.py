@@ -21,7 +21,8 @@ WEIGHTS_BF16, WEIGHTS_FP8_E4M3 = 0, 1
 EXPORTS = (
     "hy3moe_workspace_size", "hy3moe_route", "hy3moe_permute", "hy3moe_forward",
     "hy3moe_forward_timed", "hy3moe_forward_fp8", "hy3moe_forward_fp8_timed",
-    "hy3moe_quantize_rows_e4m3", "hy3moe_status_string",
+    "hy3moe_block_workspace_size", "hy3moe_route_ex", "hy3moe_block_forward",
+    "hy3moe_block_forward_timed", "hy3moe_quantize_rows_e4m3", "hy3moe_status_string",
     "hy3moe_last_hip_error",
 )
 
@@ -54,6 +55,11 @@ def lib():
     L.hy3moe_forward_timed.argtypes = [P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z, P]
     L.hy3moe_forward_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z]
     L.hy3moe_forward_fp8_timed.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z, P]
+    L.hy3moe_block_workspace_size.argtypes = [I, I, I, I, I, ctypes.POINTER(Z)]
+    L.hy3moe_route_ex.argtypes = [P, P, F, P, P, P, I, I, I, I, F, P, P, P, Z, S]
+    L.hy3moe_block_forward.argtypes = [P, P, F, P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, Z]
+    L.hy3moe_block_forward_timed.argtypes = [P, P, F, P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P,
+                                             P, Z, P]
     L.hy3moe_quantize_rows_e4m3.argtypes = [P, I, I, P, P, S]
     L.hy3moe_status_string.argtypes = [I]
     L.hy3moe_status_string.restype = ctypes.c_char_p
@@ -215,6 +221,83 @@ def forward_fp8(x, W_gate, Wq_gate_up, s_gate_up, Wq_down, s_down, k, scale, bia
     else:
         _check(lib().hy3moe_forward_fp8_timed(*args, _event_array(stage_events)),
                "hy3moe_forward_fp8_timed")
+    return (out, idx, w) if return_routing else out
+
+
+def block_workspace_size(T, d, E, k, d_ff):
+    n = ctypes.c_size_t(0)
+    _check(lib().hy3moe_block_workspace_size(T, d, E, k, d_ff, ctypes.byref(n)),
+           "hy3moe_block_workspace_size")
+    return n.value
+
+
+def route_ex(x, W_gate, k, scale, norm_weight=None, norm_eps=1e-6, bias=None, score_bias=None,
+             workspace=None):
+    """hy3moe_route_ex: the full block's router (optional route_norm weight,
+    pre-sigmoid logit bias and selection-only score bias).  Returns
+    (topk_idx int32 [T,k], topk_w fp32 [T,k])."""
+    T, d = x.shape
+    E = W_gate.shape[0]
+    _need(x, torch.bfloat16, (T, d), "x")
+    _need(W_gate, torch.float32, (E, d), "W_gate")
+    if norm_weight is not None:
+        _need(norm_weight, torch.bfloat16, (d,), "norm_weight")
+    if bias is not None:
+        _need(bias, torch.float32, (E,), "bias")
+    if score_bias is not None:
+        _need(score_bias, torch.float32, (E,), "score_bias")
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if workspace is None and T:
+        n = block_workspace_size(T, d, E, k, 64) if norm_weight is not None else workspace_size(T, d, E, k, 64)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().hy3moe_route_ex(_ptr(x), _ptr(norm_weight), float(norm_eps), _ptr(W_gate),
+                                 _ptr(bias), _ptr(score_bias), T, d, E, k, float(scale), _ptr(idx),
+                                 _ptr(w), _ptr(workspace),
+                                 0 if workspace is None else workspace.numel(), _stream()),
+           "hy3moe_route_ex")
+    return idx, w
+
+
+def block_forward(x, W_gate, W_gate_up, W_down, Ws_gate_up, Ws_down, k, scale, norm_weight=None,
+                  norm_eps=1e-6, score_bias=None, out=None, workspace=None, return_routing=False,
+                  stage_events=None):
+    """hy3moe_block_forward: shared expert + routed experts, with optional
+    route_norm and selection-only score bias.  Returns out fp32 [T,d] (and
+    (idx, w) if return_routing)."""
+    T, d = x.shape
+    E = W_gate.shape[0]
+    F = W_down.shape[2]
+    _need(x, torch.bfloat16, (T, d), "x")
+    _need(W_gate, torch.float32, (E, d), "W_gate")
+    _need(W_gate_up, torch.bfloat16, (E, 2 * F, d), "W_gate_up")
+    _need(W_down, torch.bfloat16, (E, d, F), "W_down")
+    if Ws_gate_up is not None or Ws_down is not None:
+        _need(Ws_gate_up, torch.bfloat16, (2 * F, d), "Ws_gate_up")
+        _need(Ws_down, torch.bfloat16, (d, F), "Ws_down")
+    if norm_weight is not None:
+        _need(norm_weight, torch.bfloat16, (d,), "norm_weight")
+    if score_bias is not None:
+        _need(score_bias, torch.float32, (E,), "score_bias")
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, (T, d), "out")
+    idx = w = None
+    if return_routing:
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if workspace is None and T:
+        workspace = torch.empty(max(block_workspace_size(T, d, E, k, F), 1), dtype=torch.uint8,
+                                device=x.device)
+    args = (_ptr(x), _ptr(norm_weight), float(norm_eps), _ptr(W_gate), _ptr(score_bias),
+            _ptr(W_gate_up), _ptr(W_down), _ptr(Ws_gate_up), _ptr(Ws_down), _ptr(out), T, d, E, k, F,
+            float(scale), _stream(), _ptr(idx), _ptr(w), _ptr(workspace),
+            0 if workspace is None else workspace.numel())
+    if stage_events is None:
+        _check(lib().hy3moe_block_forward(*args), "hy3moe_block_forward")
+    else:
+        _check(lib().hy3moe_block_forward_timed(*args, _event_array(stage_events)),
+               "hy3moe_block_forward_timed")
     return (out, idx, w) if return_routing else out
 
 

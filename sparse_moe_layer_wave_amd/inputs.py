@@ -14,6 +14,12 @@ Distributions (the second parameter of N(.,.) is a standard deviation):
 FP8 workload: W_gu / W_dn drawn as above in fp32, then per output row
 (= per output channel) scale s = amax/448 and codes e4m3(w / s) via torch's
 cast; the codes and the fp32 scales are the layer's inputs.
+Full-block workloads add:
+  norm_w      bf16  [d]       1 + N(0, 0.1)    route_norm weight
+  score_bias  fp32  [E]       N(0, 0.05)       selection-only score bias (moves
+                              a scale of score gaps, so it changes choices)
+  Ws_gu       bf16  [2F, d]   N(0, 0.02)       shared expert
+  Ws_dn       bf16  [d, F]    N(0, 0.02)
 
 Values depend on the device the generator runs on (torch's CPU and GPU
 generators differ): tests draw small cases on the CPU and copy them over, and
@@ -44,9 +50,15 @@ CONFIGS = {
             weights="bf16", skew=True),
     4: dict(name="hy3_fp8_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=4,
             weights="fp8", skew=False),
+    # the full block (shared expert, route_norm, selection-only score bias)
+    5: dict(name="hy3_block_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=5,
+            weights="bf16", skew=False, block=True),
+    6: dict(name="hy3_block_prefill_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=6,
+            weights="bf16", skew=False, block=True),
 }
 
-_STREAM_X, _STREAM_WG, _STREAM_BIAS, _STREAM_WGU, _STREAM_WDN = range(5)
+(_STREAM_X, _STREAM_WG, _STREAM_BIAS, _STREAM_WGU, _STREAM_WDN, _STREAM_NORM, _STREAM_SBIAS,
+ _STREAM_SGU, _STREAM_SDN) = range(9)
 
 
 def _gen(device, seed, stream):
@@ -106,6 +118,20 @@ def make_experts_fp8(E, d, F, seed, device="cpu"):
     return qgu, sgu, qdn, sdn
 
 
+def make_block_extras(d, E, F, seed, device="cpu"):
+    """route_norm weight, selection-only score bias and shared expert weights."""
+    gn = _gen(device, seed, _STREAM_NORM)
+    norm_w = (1.0 + 0.1 * torch.randn(d, generator=gn, device=device)).to(torch.bfloat16)
+    gs = _gen(device, seed, _STREAM_SBIAS)
+    score_bias = (0.05 * torch.randn(E, generator=gs, device=device)).to(torch.float32)
+    g1 = _gen(device, seed, _STREAM_SGU)
+    g2 = _gen(device, seed, _STREAM_SDN)
+    Ws_gu = _expert_fp32(2 * F, d, g1, device).to(torch.bfloat16)
+    Ws_dn = _expert_fp32(d, F, g2, device).to(torch.bfloat16)
+    return dict(norm_w=norm_w.contiguous(), score_bias=score_bias.contiguous(),
+                Ws_gu=Ws_gu.contiguous(), Ws_dn=Ws_dn.contiguous())
+
+
 def make_inputs(cfg, device="cpu", T=None, with_experts=True):
     """All inputs of one workload as torch tensors on ``device``.
 
@@ -124,6 +150,8 @@ def make_inputs(cfg, device="cpu", T=None, with_experts=True):
                 c["E"], c["d"], c["F"], c["seed"], device)
         else:
             out["W_gu"], out["W_dn"] = make_experts_bf16(c["E"], c["d"], c["F"], c["seed"], device)
+    if c.get("block", False):
+        out.update(make_block_extras(c["d"], c["E"], c["F"], c["seed"], device))
     return out
 
 

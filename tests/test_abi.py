@@ -124,3 +124,58 @@ def test_quantize_rows_argument_checks(L):
     assert q(NUL, 4, 64, A, A, NUL) == hy3moe.ERR_NULL
     assert q(A, 4, 64, MIS, A, NUL) == hy3moe.ERR_ALIGN
     assert q(NUL, 0, 64, NUL, NUL, NUL) == hy3moe.OK
+
+
+def _bws(L, T, d=4096, E=192, k=8, F=1536):
+    n = ctypes.c_size_t(0)
+    st = L.hy3moe_block_workspace_size(T, d, E, k, F, ctypes.byref(n))
+    return st, n.value
+
+
+def test_block_workspace_size(L):
+    prev = -1
+    for T in (1, 64, 8192, 65536):
+        st, n = _bws(L, T)
+        assert st == 0 and n > prev
+        prev = n
+        # the shared expert's T rows of y and the route_norm copy of x on top
+        assert n >= _ws(L, T)[1] + T * 4096 * 2 + T * 4096 * 2
+    assert _bws(L, 8, E=1024)[0] == hy3moe.ERR_UNSUPPORTED     # E + 1 experts in the dispatch
+    assert _bws(L, 8, E=1023)[0] == hy3moe.OK
+    assert L.hy3moe_block_workspace_size(8, 4096, 192, 8, 1536, None) == hy3moe.ERR_NULL
+
+
+def _blk(L, T=16, d=512, E=32, k=8, F=128, x=A, nw=A, eps=1e-6, wg=A, sb=NUL, gu=A, dn=A, sgu=A,
+         sdn=A, out=A, ws=A, nws=1 << 40):
+    return L.hy3moe_block_forward(x, nw, eps, wg, sb, gu, dn, sgu, sdn, out, T, d, E, k, F, 2.826,
+                                  NUL, NUL, NUL, ws, nws)
+
+
+def test_block_forward_argument_checks(L):
+    assert _blk(L, T=-1) == hy3moe.ERR_SHAPE
+    assert _blk(L, eps=-1.0) == hy3moe.ERR_SHAPE
+    assert _blk(L, eps=float("nan")) == hy3moe.ERR_SHAPE
+    assert _blk(L, E=1024, k=8) == hy3moe.ERR_UNSUPPORTED
+    assert _blk(L, x=NUL) == hy3moe.ERR_NULL
+    assert _blk(L, sgu=NUL) == hy3moe.ERR_NULL                  # shared expert: both or neither
+    assert _blk(L, sdn=NUL) == hy3moe.ERR_NULL
+    assert _blk(L, sb=MIS) == hy3moe.ERR_ALIGN
+    assert _blk(L, nw=MIS) == hy3moe.ERR_ALIGN
+    assert _blk(L, sgu=MIS) == hy3moe.ERR_ALIGN
+    st, need = _bws(L, 16, 512, 32, 8, 128)
+    assert _blk(L, nws=need - 1) == hy3moe.ERR_WORKSPACE
+    assert _blk(L, T=0, x=NUL, nw=NUL, wg=NUL, gu=NUL, dn=NUL, sgu=NUL, sdn=NUL, out=NUL, ws=NUL,
+                nws=0) == hy3moe.OK
+
+
+def test_route_ex_argument_checks(L):
+    def r(T=16, d=512, E=32, k=8, x=A, nw=NUL, eps=1e-6, sb=NUL, ws=A, nws=1 << 40):
+        return L.hy3moe_route_ex(x, nw, eps, A, NUL, sb, T, d, E, k, 2.826, A, A, ws, nws, NUL)
+    assert r(k=40) == hy3moe.ERR_SHAPE
+    assert r(eps=-0.5) == hy3moe.ERR_SHAPE
+    assert r(x=NUL) == hy3moe.ERR_NULL
+    assert r(sb=MIS) == hy3moe.ERR_ALIGN
+    assert r(nw=MIS) == hy3moe.ERR_ALIGN
+    assert r(nws=64) == hy3moe.ERR_WORKSPACE
+    assert r(nw=A, nws=64) == hy3moe.ERR_WORKSPACE
+    assert r(T=0, x=NUL, ws=NUL, nws=0) == hy3moe.OK
