@@ -6,8 +6,10 @@ One step = one hy3moe_forward call (router, dispatch order, gate_up, down,
 fp32 combine) over one batch of synthetic Hy3-shaped input already resident
 in HBM.  The main line is the decode batch (T=64 tokens, d=4096, 192 experts,
 top-8, d_ff=1536, bf16 experts); the prefill batch (T=8192) is reported in the
-same JSON line under "prefill".  Per-kernel durations come from HIP events
-recorded on the launch stream between the stages (hy3moe_forward_timed).
+same JSON line under "prefill", and the skewed, FP8 and full-block (shared
+expert, route_norm, score bias; hy3moe_block_forward) workloads under their
+own keys.  Per-kernel durations come from HIP events recorded on the launch
+stream between the stages (the *_timed entry points).
 
 Prints one JSON line.  Only one GPU is used; --gpus N > 1 exits with a message.
 """
@@ -43,7 +45,9 @@ def algorithmic(c, n_touched):
     """Bytes and FLOPs a kernel must move/compute, counting only touched
     experts' weights, each tensor once, and no padding."""
     T, d, E, k, F = c["T"], c["d"], c["E"], c["k"], c["F"]
-    rows = T * k
+    block = c.get("block", False)
+    rows = T * k + (T if block else 0)              # the shared expert sees every token
+    n_touched = n_touched + (1 if block else 0)
     wb = 1 if c.get("weights") == "fp8" else 2
     return {
         "gate_up": dict(bytes=n_touched * 2 * F * d * wb + T * d * 2 + rows * F * 2,
@@ -51,8 +55,8 @@ def algorithmic(c, n_touched):
         "down": dict(bytes=n_touched * d * F * wb + rows * F * 2 + rows * d * 2,
                      flops=2 * rows * F * d),
         "router": dict(bytes=E * d * 4 + T * d * 2 + rows * 8, flops=2 * T * d * E),
-        "combine": dict(bytes=rows * d * 2 + rows * 8 + T * d * 4, flops=2 * rows * d),
-        "layer_flops": T * (k * 6 * d * F + 2 * d * E),
+        "combine": dict(bytes=rows * d * 2 + T * k * 8 + T * d * 4, flops=2 * rows * d),
+        "layer_flops": T * ((k + (1 if block else 0)) * 6 * d * F + 2 * d * E),
     }
 
 
@@ -61,11 +65,21 @@ def run_workload(cfg, steps, warmup):
     c = inp["cfg"]
     T, d, E, k, F = c["T"], c["d"], c["E"], c["k"], c["F"]
     fp8 = c.get("weights") == "fp8"
-    ws = hy3moe.alloc_workspace(T, d, E, k, F, hy3moe.WEIGHTS_FP8_E4M3 if fp8 else hy3moe.WEIGHTS_BF16)
+    block = c.get("block", False)
+    if block:
+        ws = torch.empty(hy3moe.block_workspace_size(T, d, E, k, F), dtype=torch.uint8, device="cuda")
+    else:
+        ws = hy3moe.alloc_workspace(T, d, E, k, F,
+                                    hy3moe.WEIGHTS_FP8_E4M3 if fp8 else hy3moe.WEIGHTS_BF16)
     out = torch.empty((T, d), dtype=torch.float32, device="cuda")
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
 
     def step(evs=None, return_routing=False):
+        if block:
+            return hy3moe.block_forward(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], inp["Ws_gu"],
+                                        inp["Ws_dn"], k, inp["scale"], norm_weight=inp["norm_w"],
+                                        norm_eps=1e-6, score_bias=inp["score_bias"], out=out,
+                                        workspace=ws, stage_events=evs, return_routing=return_routing)
         if fp8:
             return hy3moe.forward_fp8(inp["x"], inp["W_gate"], inp["Wq_gu"], inp["s_gu"], inp["Wq_dn"],
                                       inp["s_dn"], k, inp["scale"], bias=inp["bias"], out=out,
@@ -167,7 +181,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 prefill line")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the skewed T=65536 and FP8 T=8192 lines")
+                    help="skip the skewed T=65536, FP8 T=8192 and full-block lines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 1 GiB device-to-device copy (outside every timed region), "
                          "a known byte count for scaling HBM traffic counters")
@@ -217,15 +231,17 @@ def main():
             "kernel_ms": {k: round(v, 5) for k, v in pre["stage_ms"].items()},
         }
     if not args.no_extra:
-        for key, cfg in (("skewed", 3), ("fp8", 4)):
-            res, _ = run_workload(cfg, max(3, args.steps // 10), min(args.warmup, 2))
+        for key, cfg, bound in (("skewed", 3, "mfma"), ("fp8", 4, "mfma"), ("block_decode", 5, "hbm"),
+                                ("block_prefill", 6, "mfma")):
+            n = args.steps if bound == "hbm" else max(3, args.steps // 10)
+            res, _ = run_workload(cfg, n, min(args.warmup, 2))
             line[key] = {
                 "workload": res["cfg"]["name"], "tokens_per_s": round(res["tokens_per_s"], 1),
                 "ms_per_step": round(res["ms_per_step"], 4),
                 "layer_tflops": round(res["layer_tflops"], 2),
                 "hottest_over_mean": round(res["hottest_over_mean"], 2),
-                "roofline": roofline(res, "gate_up", "mfma"),
-                "roofline_down": roofline(res, "down", "mfma"),
+                "roofline": roofline(res, "gate_up", bound),
+                "roofline_down": roofline(res, "down", bound),
                 "kernel_ms": {k: round(v, 5) for k, v in res["stage_ms"].items()},
             }
     if not args.no_cpu_baseline:
