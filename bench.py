@@ -6,9 +6,9 @@ One step = one hy3moe_forward call (router, dispatch order, gate_up, down,
 fp32 combine) over one batch of synthetic Hy3-shaped input already resident
 in HBM.  The main line is the decode batch (T=64 tokens, d=4096, 192 experts,
 top-8, d_ff=1536, bf16 experts); the prefill batch (T=8192) is reported in the
-same JSON line under "prefill", and the skewed, FP8 and full-block (shared
-expert, route_norm, score bias; hy3moe_block_forward) workloads under their
-own keys.  Per-kernel durations come from HIP events recorded on the launch
+same JSON line under "prefill", and the skewed, FP8 (T=8192 and T=64) and
+full-block (shared expert, route_norm, score bias; hy3moe_block_forward)
+workloads under their own keys.  Per-kernel durations come from HIP events recorded on the launch
 stream between the stages (the *_timed entry points).
 
 Prints one JSON line.  Only one GPU is used; --gpus N > 1 exits with a message.
@@ -181,7 +181,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 prefill line")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the skewed T=65536, FP8 T=8192 and full-block lines")
+                    help="skip the skewed T=65536, FP8 and full-block lines")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 1 GiB device-to-device copy (outside every timed region), "
                          "a known byte count for scaling HBM traffic counters")
@@ -231,8 +231,8 @@ def main():
             "kernel_ms": {k: round(v, 5) for k, v in pre["stage_ms"].items()},
         }
     if not args.no_extra:
-        for key, cfg, bound in (("skewed", 3, "mfma"), ("fp8", 4, "mfma"), ("block_decode", 5, "hbm"),
-                                ("block_prefill", 6, "mfma")):
+        for key, cfg, bound in (("skewed", 3, "mfma"), ("fp8", 4, "mfma"), ("fp8_decode", 7, "hbm"),
+                                ("block_decode", 5, "hbm"), ("block_prefill", 6, "mfma")):
             n = args.steps if bound == "hbm" else max(3, args.steps // 10)
             res, _ = run_workload(cfg, n, min(args.warmup, 2))
             line[key] = {

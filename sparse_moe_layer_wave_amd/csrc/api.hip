@@ -238,7 +238,7 @@ static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_ep
                                  reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
                                  hy3::prefill_bm(), row_of, tok_of, shared ? 1 : 0, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
-    const bool decode = hy3::use_decode_path(T, d, d_ff, E, k);
+    const bool decode = hy3::use_decode_path(T, d, d_ff, E, k, 2);
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_gate_up_decode(x, tok_of, W_gate_up, Ws_gu, offsets, h, Eg, d, d_ff, s);
@@ -292,16 +292,26 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
                                  reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
                                  hy3::prefill_bm(), row_of, tok_of, 0, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
+    const bool decode = hy3::use_decode_path(T, d, d_ff, E, k, 1);
     if (e == hipSuccess) e = hy3::launch_quant_rows(x, T, d, xq, xs, s);
     if (e == hipSuccess) e = hy3::launch_fill_u32(amax, Tk, 0u, s);
-    if (e == hipSuccess)
-        e = hy3::launch_gate_up_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, L.max_mtiles,
-                                    h32, amax, E, d, d_ff, s);
+    if (e == hipSuccess) {
+        if (decode)
+            e = hy3::launch_gate_up_decode_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, h32, amax, E, d,
+                                               d_ff, s);
+        else
+            e = hy3::launch_gate_up_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, L.max_mtiles,
+                                        h32, amax, E, d, d_ff, s);
+    }
     if (e == hipSuccess) e = hy3::launch_quant_rows_f32(h32, amax, static_cast<int>(Tk), d_ff, hq, hs, s);
     if (e == hipSuccess) e = mark(ev, 3, s);
-    if (e == hipSuccess)
-        e = hy3::launch_down_fp8(hq, hs, Wq_dn, s_dn, offsets, tile_off, L.max_mtiles, y, E, d, d_ff,
-                                 s);
+    if (e == hipSuccess) {
+        if (decode)
+            e = hy3::launch_down_decode_fp8(hq, hs, Wq_dn, s_dn, offsets, y, E, d, d_ff, s);
+        else
+            e = hy3::launch_down_fp8(hq, hs, Wq_dn, s_dn, offsets, tile_off, L.max_mtiles, y, E, d,
+                                     d_ff, s);
+    }
     if (e == hipSuccess) e = mark(ev, 4, s);
     if (e == hipSuccess) e = hy3::launch_combine(y, row_of, w, out, T, d, k, -1, s);
     if (e == hipSuccess) e = mark(ev, 5, s);

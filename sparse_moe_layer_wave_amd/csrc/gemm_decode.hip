@@ -2,24 +2,32 @@
 // so the work is streaming the touched experts' weights from HBM once.
 //
 // One workgroup = one expert x one slice of weight rows; 4 waves, each owning
-// 32 weight rows over the full K and the expert's rows 16 at a time
-// (v_mfma_f32_16x16x32_bf16: A = 16 token rows x 32 k, B = 32 k x 16 weight
-// rows; lane l holds row l%16 and k 8*(l/16)..+8 of both; C lane l holds
-// column l%16, rows 4*(l/16)..+4).
+// 32 weight rows over the full K and the expert's rows 16 at a time.  MFMA:
+//   bf16  v_mfma_f32_16x16x32_bf16: A = 16 token rows x 32 k, B = 32 k x 16
+//         weight rows; lane l holds row l%16 and k 8*(l/16)..+8 of both;
+//   e4m3  v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales): 128 k per step,
+//         lane l holds row l%16 and k 32*(l/16)..+32 of both;
+// C lane l holds column l%16, rows 4*(l/16)..+4.
 //
 // Weights are read in the order HBM streams best: each load instruction
-// covers 4 weight rows x 256 contiguous bytes (a whole-row run of 128 k),
-// the next batch already in flight in registers while the current one is
+// covers 4 weight rows x 256 contiguous bytes (128 bf16 or 256 e4m3 values of
+// k), the next batch already in flight in registers while the current one is
 // used.  The MFMA wants each lane on a single row, so every batch goes through
-// a wave-private 8 KB LDS slab [32 rows][128 k] whose 16-byte chunks are XOR-
-// swizzled by (row & 15): the 16-row fragment reads then hit 16 different
+// a wave-private 8 KB LDS slab [32 rows][256 bytes] whose 16-byte chunks are
+// XOR-swizzled by (row & 15): the 16-row fragment reads then hit 16 different
 // bank groups.  Only the owning wave touches its slab, so no barrier is needed.
 //
 // gate_up: wave w of block (e, c0) owns gate rows c0+16w..+16 and the matching
-//          up rows F+c0+16w..+16, and writes h[r, c] = bf16(SiLU(g) * u)
-//          ("DeepSeek V4-Flash architecture Q&A", Q4.5).
+//          up rows F+c0+16w..+16 ("DeepSeek V4-Flash architecture Q&A", Q4.5:
+//          SiLU on the gate branch).  bf16: h[r, c] = bf16(SiLU(g) * u).
+//          e4m3: g and u are rescaled by the token's activation scale and the
+//          channel's weight scale (Q7.4: one scale per output channel), h is
+//          stored as fp32 and the row's max |h| folded into amax[r] (integer
+//          atomic max on the bit pattern of |h|) for the row quantiser that
+//          follows.
 // down:    wave w of block (e, n0) owns W_down rows n0+32w..+32 and writes
-//          y[r, n] = bf16(h[r] . W_down[e][n]).
+//          y[r, n] = bf16(h[r] . W_down[e][n]) (e4m3: rescaled by the row's
+//          and the channel's scales first).
 // An expert with more than 16 rows is handled in passes of 16 rows.  The
 // shared expert of the full block, when present, is the last expert (all T
 // tokens, weights W_last); its workgroups are the longest, so they are
@@ -30,63 +38,81 @@
 namespace hy3 {
 namespace {
 
-constexpr int kBatchK = 128;            // k per batch (4 MFMA k-steps of 32)
-constexpr int kSlab = 32 * kBatchK;     // bf16 elements of one wave's LDS slab (8 KB)
+enum Mode { GU_BF16 = 0, DN_BF16 = 1, GU_FP8 = 2, DN_FP8 = 3 };
 
-union Frag {
-    bf16x8_t v;
-    i32x4_t q;
-};
+constexpr int kBatchB = 256;            // bytes of k per row and batch
+constexpr int kSlabB = 32 * kBatchB;    // bytes of one wave's LDS slab (8 KB)
 
-__device__ __forceinline__ int slab_off(int row, int chunk) {   // element offset, 16 chunks per row
-    return row * kBatchK + ((chunk ^ (row & 15)) << 3);
+__device__ __forceinline__ int slab_off(int row, int chunk) {   // byte offset, 16 chunks per row
+    return row * kBatchB + ((chunk ^ (row & 15)) << 4);
 }
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(256) void k_decode_gemm(
-    const uint16_t* __restrict__ A,        // gate_up: x [T, K]; down: h [rows, K]
-    const int32_t* __restrict__ tok_of,    // gate_up only
-    const uint16_t* __restrict__ W,        // gate_up: [E, 2N, K]; down: [E, N, K]
-    const uint16_t* __restrict__ W_last,   // non-NULL: weights of expert E - 1 (shared)
-    const int32_t* __restrict__ offsets,
-    uint16_t* __restrict__ C,              // gate_up: h [rows, N]; down: y [rows, N]
-    int K, int N) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kSlab];
+struct DecodeArgs {
+    const uint8_t* A;                   // gate_up: x (or its e4m3 codes) [T, K]; down: h [rows, K]
+    const int32_t* tok_of;              // gate_up only
+    const uint8_t* W;                   // gate_up: [E, 2N, K]; down: [E, N, K]
+    const uint8_t* W_last;              // non-NULL: weights of expert E - 1 (shared)
+    const int32_t* offsets;
+    uint16_t* C;                        // bf16 out: gate_up h (bf16 mode) or y [rows, N]
+    const float* a_scale;               // e4m3: per token (gate_up) or per row (down)
+    const float* w_scale;               // e4m3: [E, 2N] (gate_up) or [E, N] (down)
+    float* h32;                         // e4m3 gate_up: h [rows, N] fp32
+    uint32_t* amax;                     // e4m3 gate_up: [rows] bits of max |h|
+    int K, N;                           // K in elements
+};
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
+    constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8;
+    constexpr bool FP8 = MODE == GU_FP8 || MODE == DN_FP8;
+    constexpr int ESZ = FP8 ? 1 : 2;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kSlabB];
     const int E = gridDim.x;
-    const int e = W_last ? (blockIdx.x == 0 ? E - 1 : blockIdx.x - 1) : blockIdx.x;
-    const int rbeg = offsets[e];
-    const int rend = offsets[e + 1];
+    const int e = g.W_last ? (blockIdx.x == 0 ? E - 1 : blockIdx.x - 1) : blockIdx.x;
+    const int rbeg = g.offsets[e];
+    const int rend = g.offsets[e + 1];
     if (rbeg == rend) return;
+    const int K = g.K, N = g.N;
+    const size_t rowbytes = static_cast<size_t>(K) * ESZ;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int r16 = lane & 15;
-    const int kq = (lane >> 4) * 8;
-    uint16_t* slab = lds + wave * kSlab;
+    const int kq = lane >> 4;                          // quarter of the lane group
+    uint8_t* slab = lds + wave * kSlabB;
 
     // weight row of slab row sr (0..31): n-tile sr/16, row sr%16 of it
-    int col0;
-    const uint16_t* We = (W_last && e == E - 1) ? W_last : W + static_cast<size_t>(e) * (GATE_UP ? 2 * N : N) * K;
+    const uint8_t* We = (g.W_last && e == E - 1)
+                            ? g.W_last
+                            : g.W + static_cast<size_t>(e) * (GATE_UP ? 2 * N : N) * rowbytes;
     auto wrow_of = [&](int sr) -> int {
         if (GATE_UP) return (sr < 16 ? 0 : N) + blockIdx.y * 64 + wave * 16 + (sr & 15);
         return blockIdx.y * 128 + wave * 32 + sr;
     };
-    col0 = GATE_UP ? blockIdx.y * 64 + wave * 16 : blockIdx.y * 128 + wave * 32;
+    const int col0 = GATE_UP ? blockIdx.y * 64 + wave * 16 : blockIdx.y * 128 + wave * 32;
     // load instruction i (0..7) of a batch: slab rows 4i + lane/16, bytes (lane%16)*16
-    const uint16_t* wsrc[8];
+    const uint8_t* wsrc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        wsrc[i] = We + static_cast<size_t>(wrow_of(4 * i + (lane >> 4))) * K + (lane & 15) * 8;
+    for (int i = 0; i < 8; ++i) wsrc[i] = We + static_cast<size_t>(wrow_of(4 * i + kq)) * rowbytes + r16 * 16;
     int wdst[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wdst[i] = slab_off(4 * i + (lane >> 4), lane & 15);
+    for (int i = 0; i < 8; ++i) wdst[i] = slab_off(4 * i + kq, r16);
 
-    const int nb = K / kBatchK;
+    // e4m3: this lane's column scales (column col0 + r16, and + 16 for down)
+    float ws0 = 0.f, ws1 = 0.f;
+    if constexpr (FP8) {
+        const float* ws_e = g.w_scale + static_cast<size_t>(e) * (GATE_UP ? 2 * N : N);
+        ws0 = ws_e[col0 + r16];
+        ws1 = GATE_UP ? ws_e[N + col0 + r16] : ws_e[col0 + 16 + r16];
+    }
+
+    const int nb = static_cast<int>(rowbytes / kBatchB);
     for (int p0 = rbeg; p0 < rend; p0 += 16) {
         const int prow = p0 + r16;                    // A row this lane loads
         const bool va = prow < rend;
-        const uint16_t* a;
-        if (GATE_UP) a = A + static_cast<size_t>(va ? tok_of[prow] : 0) * K + kq;
-        else a = A + static_cast<size_t>(va ? prow : 0) * K + kq;
+        const size_t arow = GATE_UP ? static_cast<size_t>(va ? g.tok_of[prow] : 0)
+                                    : static_cast<size_t>(va ? prow : 0);
+        // this lane's A bytes within a batch start at kq * (FP8 ? 32 : 16)
+        const uint8_t* a = g.A + arow * rowbytes + kq * (FP8 ? 32 : 16);
 
         f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
         f32x4_t acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -94,26 +120,50 @@ __global__ __launch_bounds__(256) void k_decode_gemm(
 #pragma unroll
         for (int i = 0; i < 8; ++i) cur[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(wsrc[i]));
         for (int b = 0; b < nb; ++b) {
-            const int kb = b * kBatchK;
-            const int kn = (b + 1 < nb ? b + 1 : b) * kBatchK;   // last batch re-reads itself
+            const int kb = b * kBatchB;
+            const int kn = (b + 1 < nb ? b + 1 : b) * kBatchB;   // last batch re-reads itself
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 nxt[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(wsrc[i] + kn));
-            i32x4_t av[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                av[s] = va ? *reinterpret_cast<const i32x4_t*>(a + kb + 32 * s) : i32x4_t{0, 0, 0, 0};
 #pragma unroll
             for (int i = 0; i < 8; ++i) *reinterpret_cast<i32x4_t*>(slab + wdst[i]) = cur[i];
+            if constexpr (FP8) {
+                // 2 k-steps of 128: lane's 32 bytes = chunks 8 s + 2 kq, +1
+                i32x4_t av[2][2];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                // lane l: slab row (nt*16 + l%16), logical chunk 4 s + l/16
-                Frag fa, f0, f1;
-                fa.q = av[s];
-                f0.q = *reinterpret_cast<const i32x4_t*>(slab + slab_off(r16, 4 * s + (lane >> 4)));
-                f1.q = *reinterpret_cast<const i32x4_t*>(slab + slab_off(16 + r16, 4 * s + (lane >> 4)));
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.v, f0.v, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.v, f1.v, acc1, 0, 0, 0);
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        av[s][q] = va ? *reinterpret_cast<const i32x4_t*>(a + kb + 128 * s + 16 * q)
+                                      : i32x4_t{0, 0, 0, 0};
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int ch = 8 * s + 2 * kq;
+                    const i32x8_t fa = __builtin_shufflevector(av[s][0], av[s][1], 0, 1, 2, 3, 4, 5, 6, 7);
+                    const i32x4_t b00 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(r16, ch));
+                    const i32x4_t b01 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(r16, ch + 1));
+                    const i32x4_t b10 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(16 + r16, ch));
+                    const i32x4_t b11 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(16 + r16, ch + 1));
+                    const i32x8_t f0 = __builtin_shufflevector(b00, b01, 0, 1, 2, 3, 4, 5, 6, 7);
+                    const i32x8_t f1 = __builtin_shufflevector(b10, b11, 0, 1, 2, 3, 4, 5, 6, 7);
+                    acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, f0, acc0, 0, 0, 0, 127, 0, 127);
+                    acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, f1, acc1, 0, 0, 0, 127, 0, 127);
+                }
+            } else {
+                // 4 k-steps of 32: lane's 16 bytes = chunk 4 s + kq
+                i32x4_t av[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    av[s] = va ? *reinterpret_cast<const i32x4_t*>(a + kb + 64 * s) : i32x4_t{0, 0, 0, 0};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const i32x4_t f0 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(r16, 4 * s + kq));
+                    const i32x4_t f1 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(16 + r16, 4 * s + kq));
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[s]),
+                                                                    __builtin_bit_cast(bf16x8_t, f0), acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[s]),
+                                                                    __builtin_bit_cast(bf16x8_t, f1), acc1, 0, 0, 0);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
@@ -121,13 +171,30 @@ __global__ __launch_bounds__(256) void k_decode_gemm(
         // C lane l: column l%16, rows 4*(l/16)+i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = p0 + (lane >> 4) * 4 + i;
-            if (row < rend) {
-                if (GATE_UP) {
-                    C[static_cast<size_t>(row) * N + col0 + r16] = f32_to_bf16(silu_mul(acc0[i], acc1[i]));
-                } else {
-                    C[static_cast<size_t>(row) * N + col0 + r16] = f32_to_bf16(acc0[i]);
-                    C[static_cast<size_t>(row) * N + col0 + 16 + r16] = f32_to_bf16(acc1[i]);
+            const int row = p0 + kq * 4 + i;
+            const bool vr = row < rend;
+            const size_t crow = static_cast<size_t>(vr ? row : rbeg);
+            if constexpr (MODE == GU_BF16) {
+                if (vr) g.C[crow * N + col0 + r16] = f32_to_bf16(silu_mul(acc0[i], acc1[i]));
+            } else if constexpr (MODE == DN_BF16) {
+                if (vr) {
+                    g.C[crow * N + col0 + r16] = f32_to_bf16(acc0[i]);
+                    g.C[crow * N + col0 + 16 + r16] = f32_to_bf16(acc1[i]);
+                }
+            } else if constexpr (MODE == GU_FP8) {
+                const float sx = g.a_scale[g.tok_of[crow]];
+                const float hv = silu_mul(acc0[i] * sx * ws0, acc1[i] * sx * ws1);
+                if (vr) g.h32[crow * N + col0 + r16] = hv;
+                // row max over the 16 lanes that share this row
+                float m = fabsf(hv);
+#pragma unroll
+                for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+                if (vr && r16 == 0) atomicMax(&g.amax[crow], __float_as_uint(m));
+            } else {
+                const float sh = g.a_scale[crow];
+                if (vr) {
+                    g.C[crow * N + col0 + r16] = f32_to_bf16(acc0[i] * sh * ws0);
+                    g.C[crow * N + col0 + 16 + r16] = f32_to_bf16(acc1[i] * sh * ws1);
                 }
             }
         }
@@ -137,24 +204,46 @@ __global__ __launch_bounds__(256) void k_decode_gemm(
 }  // namespace
 
 // Decode path while the average expert gets at most 4 rows (so nearly every
-// expert fits one 16-row pass); needs d and d_ff to be multiples of 128.
-bool use_decode_path(int T, int d, int F, int E, int k) {
-    return static_cast<long long>(T) * k <= 4LL * E && (d % 128) == 0 && (F % 128) == 0;
+// expert fits one 16-row pass); rows of d and d_ff elements of esz bytes must
+// be whole 256-byte batches.
+bool use_decode_path(int T, int d, int F, int E, int k, int esz) {
+    return static_cast<long long>(T) * k <= 4LL * E && (d * esz) % kBatchB == 0 &&
+           (F * esz) % kBatchB == 0;
 }
 
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
                                  const uint16_t* W_last, const int32_t* offsets, uint16_t* h,
                                  int E, int d, int F, hipStream_t s) {
-    hipLaunchKernelGGL(k_decode_gemm<true>, dim3(E, F / 64), dim3(256), 0, s, x, tok_of, W_gu,
-                       W_last, offsets, h, d, F);
+    DecodeArgs g{reinterpret_cast<const uint8_t*>(x), tok_of, reinterpret_cast<const uint8_t*>(W_gu),
+                 reinterpret_cast<const uint8_t*>(W_last), offsets, h, nullptr, nullptr, nullptr,
+                 nullptr, d, F};
+    hipLaunchKernelGGL(k_decode_gemm<GU_BF16>, dim3(E, F / 64), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
 hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uint16_t* W_last,
                               const int32_t* offsets, uint16_t* y, int E, int d, int F,
                               hipStream_t s) {
-    hipLaunchKernelGGL(k_decode_gemm<false>, dim3(E, d / 128), dim3(256), 0, s, h, nullptr, W_dn,
-                       W_last, offsets, y, F, d);
+    DecodeArgs g{reinterpret_cast<const uint8_t*>(h), nullptr, reinterpret_cast<const uint8_t*>(W_dn),
+                 reinterpret_cast<const uint8_t*>(W_last), offsets, y, nullptr, nullptr, nullptr,
+                 nullptr, F, d};
+    hipLaunchKernelGGL(k_decode_gemm<DN_BF16>, dim3(E, d / 128), dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_up_decode_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
+                                     const uint8_t* Wq, const float* ws, const int32_t* offsets,
+                                     float* h32, uint32_t* amax, int E, int d, int F, hipStream_t s) {
+    DecodeArgs g{xq, tok_of, Wq, nullptr, offsets, nullptr, xs, ws, h32, amax, d, F};
+    hipLaunchKernelGGL(k_decode_gemm<GU_FP8>, dim3(E, F / 64), dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq,
+                                  const float* ws, const int32_t* offsets, uint16_t* y, int E,
+                                  int d, int F, hipStream_t s) {
+    DecodeArgs g{hq, nullptr, Wq, nullptr, offsets, y, hs, ws, nullptr, nullptr, F, d};
+    hipLaunchKernelGGL(k_decode_gemm<DN_FP8>, dim3(E, d / 128), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 

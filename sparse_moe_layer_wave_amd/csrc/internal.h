@@ -85,7 +85,7 @@ hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const ui
 
 // decode-sized batches: weight streaming, one workgroup per (expert, weight
 // slice); E and W_last as for the grouped GEMMs
-bool use_decode_path(int T, int d, int F, int E, int k);
+bool use_decode_path(int T, int d, int F, int E, int k, int esz);   // esz: bytes per weight
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
                                  const uint16_t* W_last, const int32_t* offsets, uint16_t* h,
                                  int E, int d, int F, hipStream_t s);
@@ -132,5 +132,12 @@ hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const int32_t*
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq, const float* ws,
                            const int32_t* offsets, const int32_t* tile_off, int max_mtiles,
                            uint16_t* y, int E, int d, int F, hipStream_t s);
+// decode-sized batches with e4m3 experts (weight streaming, as the bf16 ones)
+hipError_t launch_gate_up_decode_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
+                                     const uint8_t* Wq, const float* ws, const int32_t* offsets,
+                                     float* h32, uint32_t* amax, int E, int d, int F, hipStream_t s);
+hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq,
+                                  const float* ws, const int32_t* offsets, uint16_t* y, int E,
+                                  int d, int F, hipStream_t s);
 
 }  // namespace hy3

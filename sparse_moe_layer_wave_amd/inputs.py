@@ -55,6 +55,9 @@ CONFIGS = {
             weights="bf16", skew=False, block=True),
     6: dict(name="hy3_block_prefill_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=6,
             weights="bf16", skew=False, block=True),
+    # e4m3 experts at the decode batch
+    7: dict(name="hy3_fp8_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=7,
+            weights="fp8", skew=False),
 }
 
 (_STREAM_X, _STREAM_WG, _STREAM_BIAS, _STREAM_WGU, _STREAM_WDN, _STREAM_NORM, _STREAM_SBIAS,

@@ -1,6 +1,7 @@
 """GPU parity of the e4m3 expert path (through the C ABI) against the oracle's
 FP8 definition: the x row quantiser bit-exactly, the whole layer within
-3e-2 * rms(ref) on small cases and on sampled tokens of the Hy3 FP8 workload."""
+3e-2 * rms(ref) on small cases and on sampled tokens of the Hy3 FP8 workloads
+(prefill-sized grouped kernels and the decode-sized weight-streaming ones)."""
 
 import numpy as np
 import pytest
@@ -58,6 +59,24 @@ def test_fp8_small_full_parity(gpu_lib, T, E, k, F):
     print(T, E, k, F, stats)
 
 
+@pytest.mark.parametrize("T,E,k,F,d", [(16, 64, 8, 256, 512), (64, 192, 8, 256, 256),
+                                       (5, 24, 4, 512, 1024), (1, 8, 2, 256, 256),
+                                       (12, 32, 8, 384, 512)])
+def test_fp8_decode_path_full_parity(gpu_lib, T, E, k, F, d):
+    """T * k <= 4 E with d, d_ff multiples of 256: the e4m3 weight-streaming
+    kernels (the last case, d_ff = 384, takes the grouped kernels instead)."""
+    inp = _cpu_fp8_case(T, E, k, F, d=d, seed=42 + T)
+    c = inp["cfg"]
+    out, idx, w = _run_fp8(inp)
+    ref, r = oracle.forward_fp8(inputs.bits(inp["x"]), inp["W_gate"].numpy(), inputs.bits(inp["Wq_gu"]),
+                                inp["s_gu"].numpy(), inputs.bits(inp["Wq_dn"]), inp["s_dn"].numpy(),
+                                c["k"], inp["scale"])
+    stats = check_routing(idx.cpu().numpy(), w.cpu().numpy(), r, inp["scale"])
+    set_eq = np.array([set(a) == set(b) for a, b in zip(idx.cpu().numpy().tolist(), r.idx.tolist())])
+    stats.update(check_output_fp8_small(out.cpu().numpy(), ref, set_eq, TOL_FP8))
+    print(T, E, k, F, d, stats)
+
+
 def test_fp8_deterministic(gpu_lib):
     inp = _cpu_fp8_case(500, 32, 8, 128, seed=41)
     a = _run_fp8(inp)
@@ -66,9 +85,10 @@ def test_fp8_deterministic(gpu_lib):
         assert torch.equal(u, v)
 
 
-def test_hy3_fp8_T8192(gpu_lib):
+@pytest.mark.parametrize("cfg,n_sample", [(4, 10), (7, 16)])
+def test_hy3_fp8(gpu_lib, cfg, n_sample):
     from sparse_moe_layer_wave_amd import hy3moe as hy
-    inp = inputs.make_inputs(4, device="cuda")
+    inp = inputs.make_inputs(cfg, device="cuda")
     c = inp["cfg"]
     T = c["T"]
     out, idx, w = hy.forward_fp8(inp["x"], inp["W_gate"], inp["Wq_gu"], inp["s_gu"], inp["Wq_dn"],
@@ -80,10 +100,10 @@ def test_hy3_fp8_T8192(gpu_lib):
     idx_np = idx.cpu().numpy()
     stats = check_routing(idx_np, w.cpu().numpy(), r, inp["scale"])
     rng = np.random.default_rng(4)
-    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 10, replace=False)]))
+    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_sample, replace=False)]))
     ref, rs = oracle.forward_fp8_tokens(sample, x_bits, W, LazyExperts(inp["Wq_gu"]),
                                         LazyExperts(inp["s_gu"]), LazyExperts(inp["Wq_dn"]),
                                         LazyExperts(inp["s_dn"]), c["k"], inp["scale"])
     set_eq = np.array([set(a) == set(b) for a, b in zip(idx_np[sample].tolist(), rs.idx.tolist())])
     stats.update(check_output(out.cpu().numpy()[sample], ref, TOL_FP8, set_eq))
-    print("fp8", stats)
+    print("fp8", inp["cfg"]["name"], stats)
