@@ -132,6 +132,12 @@ def test_block_decode_path_shapes(gpu_lib, T):
     print(T, _compare_full(_case(T, 1024, 192, 8, 256, seed=80 + T)))
 
 
+def test_block_maximum_experts(gpu_lib):
+    """E = 1023 routed experts plus the shared one: 1024 experts in the
+    dispatch order, the most it takes."""
+    print(_compare_full(_case(200, 256, 1023, 16, 64, seed=76)))
+
+
 def test_block_zero_routed_experts_is_the_shared_expert(gpu_lib):
     inp_cpu = _case(200, 512, 32, 8, 128, seed=74)
     inp_cpu["W_gu"] = torch.zeros_like(inp_cpu["W_gu"])
