@@ -21,16 +21,20 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+// fp32 -> bf16 bits, round to nearest even (gfx950's v_cvt_pk_bf16_f32; NaN
+// stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// SiLU(g) * u = g * u / (1 + e^-g), with the hardware exp2 and reciprocal
+// (v_exp_f32, v_rcp_f32: about 1 ulp of fp32 each).  The result is stored as
+// bf16 (or quantised to e4m3), 2^-9 relative or coarser, so the fp32 error is
+// far below what the stored value keeps.  Limits: g -> -inf gives 0,
+// g -> +inf gives g * u.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-    return g / (1.0f + expf(-g)) * u;
+    const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);   // e^-g
+    return g * u * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // Workspace carving, computed identically on the host for every entry point.
