@@ -29,7 +29,7 @@
 // v_mfma_f32_32x32x16_bf16, or 64 e4m3 = one step of
 // v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales).  A slice of a tile is
 // 32 or 40 one-kilobyte copies (16 rows each), issued as
-// global_load_lds_dwordx4 straight into a 4-slot LDS ring, three slices
+// global_load_lds_dwordx4 straight into a 4-slot LDS ring, two slices
 // ahead of use; every wave issues its own share.  The copies are written in
 // inline assembly: the compiler does not see them as LDS stores and so does
 // not wait for all of them before each LDS read; the loop instead waits
@@ -51,6 +51,8 @@
 // weight panel are adjacent, so the panel streams into L2 once for all of
 // them; workgroups are dealt round-robin over the 8 XCDs, so the block index is
 // remapped to give each XCD a contiguous run of units.
+
+#include <algorithm>
 
 #include "internal.h"
 
@@ -96,6 +98,14 @@ struct Unit {
     int e, row0, rows, n;                          // n: column tile index of this shape
 };
 
+__device__ __forceinline__ int lane_id() {
+    // opaque (asm volatile): recomputed where used rather than hoisted out of
+    // the persistent unit loop and kept live across the MFMA loop
+    int lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    return lane;
+}
+
 struct Args {
     const uint8_t* A;                              // gate_up: x [T, K]; down: h [rows, K]
     const int32_t* tok_of;                         // gate_up: token of each row
@@ -113,7 +123,7 @@ struct Args {
 
 // One tile.  SQUARE: 256 rows x 256 weight rows; else 128 x 512.
 template <int MODE, bool SQUARE>
-__device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u) {
+__device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u, int wave) {
     constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8;
     constexpr bool FP8 = MODE == GU_FP8 || MODE == DN_FP8;
     constexpr int RA = SQUARE ? 256 : 128;         // A rows per slice
@@ -124,8 +134,8 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u)
     static_assert(kSlots * kSlotBytes <= kLdsBytes, "LDS");
     constexpr int NMFMA = FP8 ? 16 : 32;           // MFMAs per slice and wave
     const int N = g.N;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = lane_id();
+    const int tid = wave * 64 + lane;
     const int wm = SQUARE ? (wave & 1) : 0;
     const int wn = SQUARE ? (wave >> 1) : wave;
     const size_t rowbytes = static_cast<size_t>(g.K) * (FP8 ? 1 : 2);
@@ -202,30 +212,39 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u)
         }
     };
 
-    // ---- prologue: slices 0 .. kSlots-1 in flight (clamped: a short K
+    // ---- prologue: slices 0 .. kSlots-2 in flight (clamped: a short K
     // re-reads its last slice), slice 0 read
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
+    for (int s = 0; s < kSlots - 1; ++s) {
         const int kt = min(s, nk - 1);
 #pragma unroll
         for (int j = 0; j < NPW; ++j) copy_to_lds(src[j] + kt * kRowB, my_copies + s * kSlotBytes + j * 1024);
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kSlots - 1) * NPW));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kSlots - 2) * NPW));
     lds_barrier();
 #pragma unroll
     for (int r = 0; r < 16; ++r) read_frag(0, lds, r);
 
-    // ---- main loop, two slices per trip (fragment sets 0 and 1).  Every
-    // slice issues exactly NPW copies (slices past the end re-read the last
-    // one into a slot nobody reads again), so the waits are exact: at the top
-    // of slice kt, slices up to kt + kSlots - 1 are issued and kt + 1 must
-    // have landed.  Copy j of slice kt + kSlots follows MFMA j * NMFMA / NPW and
-    // the 16 fragment reads of slice kt + 1 are spread evenly over the MFMAs.
+    // ---- main loop, two slices per trip (fragment sets 0 and 1).  Slice kt
+    // runs its MFMAs on fragments read during slice kt - 1, reads slice kt + 1
+    // and refills the slot of slice kt - 1 with slice kt + kSlots - 1.  That
+    // slot's reads were consumed by the MFMAs of slice kt - 1, which every
+    // wave has issued before the barrier at the top of slice kt, so the
+    // barrier needs no wait for LDS reads: the reads of slice kt, still in
+    // flight, are waited for by the MFMAs that use them (the compiler's
+    // per-register waits), not at the barrier.  Every slice issues exactly
+    // NPW copies (slices past the end re-read the last one into a slot nobody
+    // reads again), so the waits are exact: at the top of slice kt, slices up
+    // to kt + kSlots - 2 are issued and kt + 1 must have landed.  Copy j
+    // follows MFMA j * NMFMA / NPW and the 16 fragment reads of slice kt + 1
+    // are spread evenly over the MFMAs.
     auto step = [&](int kt, int set) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kSlots - 2) * NPW));
-        lds_barrier();                                 // everyone: slice kt in registers, kt+1 landed
-        const int kin = min(kt + kSlots, nk - 1);
-        const uint32_t islot = my_copies + (kt & (kSlots - 1)) * kSlotBytes;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kSlots - 3) * NPW));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();                  // everyone: slice kt - 1 consumed, kt + 1 landed
+        asm volatile("" ::: "memory");
+        const int kin = min(kt + kSlots - 1, nk - 1);
+        const uint32_t islot = my_copies + ((kt + kSlots - 1) & (kSlots - 1)) * kSlotBytes;
         const uint8_t* rbase = lds + ((kt + 1) & (kSlots - 1)) * kSlotBytes;
 #pragma unroll
         for (int i = 0; i < NMFMA; ++i) {
@@ -264,7 +283,7 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u)
     float* srow = reinterpret_cast<float*>(lds + 4 * 128 * OPITCH);
     lds_barrier();                                     // every wave is done with the ring
     if constexpr (FP8) {
-        const int t = threadIdx.x;
+        const int t = tid;
         if (t < RA) {
             const int r = min(t, u.rows - 1);
             srow[t] = GATE_UP ? g.a_scale[g.tok_of[u.row0 + r]] : g.a_scale[u.row0 + r];
@@ -339,25 +358,24 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u)
     }
 }
 
+// Unit L -> tile.  Returns false for the second column tile of a partial
+// last panel (nothing to compute).
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void k_grouped(Args g) {
+__device__ __forceinline__ bool unit_of(const Args& g, int L, Unit& u, bool& square) {
     constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
-
     const int E = g.E, npanel = g.npanel;
-    const int G = gridDim.x;                       // a multiple of kXcds
-    const int L = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
-    if (L >= g.tile_off[E] * npanel) return;
     int lo = 0, hi = E - 1;                        // expert: last e with tile_off[e] * npanel <= L
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (g.tile_off[mid] * npanel <= L) lo = mid;
         else hi = mid - 1;
     }
-    Unit u;
     u.e = lo;
-    const int nb_e = g.tile_off[lo + 1] - g.tile_off[lo];
-    int v = L - g.tile_off[lo] * npanel;
+    // the table values are uniform: kept in scalar registers, so the unit
+    // arithmetic below runs on the scalar unit
+    const int t0 = __builtin_amdgcn_readfirstlane(g.tile_off[lo]);
+    const int nb_e = __builtin_amdgcn_readfirstlane(g.tile_off[lo + 1]) - t0;
+    int v = L - t0 * npanel;
     // chunks of kChunkBlocks row blocks; a chunk of m blocks has m * npanel
     // units: for each weight panel, its square tiles (two column tiles per
     // panel, pairs of blocks) and then its wide tile (odd last block)
@@ -375,7 +393,7 @@ __global__ __launch_bounds__(256, 1) void k_grouped(Args g) {
     const int panel = v / m;
     const int w = v - panel * m;
     int blk;
-    const bool square = w < 2 * pairs;
+    square = w < 2 * pairs;
     if (square) {
         u.n = 2 * panel + w / pairs;
         blk = c * kChunkBlocks + 2 * (w % pairs);
@@ -383,13 +401,36 @@ __global__ __launch_bounds__(256, 1) void k_grouped(Args g) {
         u.n = panel;
         blk = c * kChunkBlocks + 2 * pairs;
     }
-    u.row0 = g.offsets[lo] + blk * 128;
-    u.rows = min(square ? 256 : 128, g.offsets[lo + 1] - u.row0);
+    u.row0 = __builtin_amdgcn_readfirstlane(g.offsets[lo]) + blk * 128;
+    u.rows = min(square ? 256 : 128, __builtin_amdgcn_readfirstlane(g.offsets[lo + 1]) - u.row0);
     const int cols_sq = GATE_UP ? 128 : 256;       // output columns of a square tile
-    if (square && u.n * cols_sq >= g.N) return;    // second column tile of a partial last panel
+    return !(square && u.n * cols_sq >= g.N);
+}
 
-    if (square) tile<MODE, true>(g, lds, u);
-    else tile<MODE, false>(g, lds, u);
+// Persistent: one workgroup per CU, workgroup b on XCD b % 8 (the dispatcher
+// deals workgroups round-robin over the XCDs).  The units are split into 8
+// contiguous ranges, one per XCD, and the XCD's workgroups take its range
+// round-robin, so at any time an XCD works on consecutive units (one
+// expert's tiles, reading the same weight panels and token rows through its
+// L2).
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void k_grouped(Args g) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+    const int U = g.tile_off[g.E] * g.npanel;
+    const int per_wg = gridDim.x / kXcds;          // workgroups per XCD (grid: a multiple of kXcds)
+    const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+    const int per_xcd = (U + kXcds - 1) / kXcds;
+    int wave;                                      // opaque: not recomputed from the thread index later
+    asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(wave) : "v"(static_cast<int>(threadIdx.x) >> 6));
+    const int end = min((x + 1) * per_xcd, U);
+    for (int L = x * per_xcd + j; L < end; L += per_wg) {
+        Unit u;
+        bool square;
+        if (!unit_of<MODE>(g, L, u, square)) continue;
+        if (square) tile<MODE, true>(g, lds, u, wave);
+        else tile<MODE, false>(g, lds, u, wave);
+        lds_barrier();                             // every wave has read its staged output back
+    }
 }
 
 template <int MODE>
@@ -397,7 +438,13 @@ hipError_t launch(Args g, int max_blocks, hipStream_t s) {
     constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8;
     g.npanel = GATE_UP ? (g.N + 255) / 256 : (g.N + 511) / 512;   // 512 weight rows per panel
     const long long units = static_cast<long long>(max_blocks) * g.npanel;
-    const int grid = static_cast<int>((units + kXcds - 1) / kXcds * kXcds);
+    if (units == 0) return hipSuccess;
+    int dev = 0, cus = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    const long long cap = std::max(kXcds, cus / kXcds * kXcds);    // one workgroup per CU
+    const int grid = static_cast<int>(std::min(cap, (units + kXcds - 1) / kXcds * kXcds));
     hipLaunchKernelGGL(k_grouped<MODE>, dim3(grid), dim3(256), 0, s, g);
     return hipGetLastError();
 }
