@@ -182,6 +182,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 prefill line")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the skewed T=65536, FP8 and full-block lines")
+    ap.add_argument("--profile-workload", metavar="NAME",
+                    help="run only the named workload (a profiler pass: one workload per run), "
+                         "print its stage times and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 1 GiB device-to-device copy (outside every timed region), "
                          "a known byte count for scaling HBM traffic counters")
@@ -198,6 +201,16 @@ def main():
         torch.cuda.synchronize()
         del a, b
         torch.cuda.empty_cache()
+
+    if args.profile_workload:
+        names = {c["name"]: i for i, c in inputs.CONFIGS.items()}
+        if args.profile_workload not in names:
+            print(f"unknown workload {args.profile_workload!r}; one of {sorted(names)}", file=sys.stderr)
+            sys.exit(2)
+        res, _ = run_workload(names[args.profile_workload], args.steps, args.warmup)
+        print(json.dumps({"workload": args.profile_workload, "ms_per_step": round(res["ms_per_step"], 4),
+                          "kernel_ms": {k: round(v, 5) for k, v in res["stage_ms"].items()}}), flush=True)
+        return
 
     dec, _ = run_workload(1, args.steps, args.warmup)
     line = {

@@ -2,15 +2,15 @@
 
     python -m sparse_moe_layer_wave_amd.profile_summary --trace T.csv \
         [--fetch F.csv --write W.csv] --command "..." --out profiles/NAME.md \
-        [--traffic-json profiles/counters_gate_up_hy3_decode_T64.json --kernel k_decode_gemm \
-         --grid-x 49152 --grid-y 24 --source gemm_decode.hip]
+        [--traffic-json profiles/counters_gate_up_hy3_decode_T64.json --kernel "k_decode_gemm<0>" \
+         [--grid-x 49152 --grid-y 24] --source gemm_decode.hip]
 
 --trace is rocprofv3's kernel_trace.csv (--kernel-trace --output-format csv);
 --fetch / --write are counter_collection.csv files of two --pmc runs
 (FETCH_SIZE, WRITE_SIZE: KiB per dispatch).  The counters are scaled by what
-they read for the largest device copy in the same run (bench.py
---copy-calibration copies 1 GiB), so "bytes" means bytes as a plain copy of
-known size counts them.  The traffic JSON is what bench.py reports as
+they read for the run's first device copy (bench.py --copy-calibration copies
+1 GiB before anything else), so "bytes" means bytes as a plain copy of known
+size counts them.  The traffic JSON is what bench.py reports as
 roofline.traffic while the kernel's source file is unchanged (sha256 prefix).
 """
 
@@ -49,10 +49,13 @@ def _counters(path, counter):
         v = float(r["Counter_Value"])
         per[(name, int(r["Grid_Size"]))].append(v)
         if "copy" in name.lower():
-            copies.append((int(r["Grid_Size"]), v))
+            copies.append((int(r["Dispatch_Id"]), v))
+    # the calibration copy (bench.py --copy-calibration) is the run's first
+    # copy dispatch; later copies (dtype conversions of the inputs) are not
+    # of a known size
     scale = None
     if copies:
-        grid, v = max(copies)
+        _, v = min(copies)
         scale = COPY_BYTES / (v * 1024.0) if v > 0 else None
     return per, scale
 
@@ -66,8 +69,8 @@ def main():
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic-json")
     ap.add_argument("--kernel", help="kernel name (substring) for the traffic JSON")
-    ap.add_argument("--grid-x", type=int)
-    ap.add_argument("--grid-y", type=int, default=1)
+    ap.add_argument("--grid-x", type=int, help="grid of that kernel's launch (default: any)")
+    ap.add_argument("--grid-y", type=int)
     ap.add_argument("--source", help="source file (under csrc/) of that kernel")
     ap.add_argument("--workload", default="hy3_decode_T64")
     args = ap.parse_args()
@@ -100,7 +103,8 @@ def main():
                 fmb = f"{sum(fv) / len(fv) * 1024 * fscale / 1e6:.1f}"
             if wv and wscale:
                 wmb = f"{sum(wv) / len(wv) * 1024 * wscale / 1e6:.1f}"
-            if (args.kernel and args.kernel in name and gx == args.grid_x and gy == args.grid_y
+            if (args.kernel and args.kernel == name
+                    and args.grid_x in (None, gx) and args.grid_y in (None, gy)
                     and fv and wv and fscale and wscale):
                 traffic = (sum(fv) / len(fv) * 1024 * fscale + sum(wv) / len(wv) * 1024 * wscale)
         lines.append(f"| {name} | ({gx},{gy},{gz}) | {bx} | {len(durs)} | "
