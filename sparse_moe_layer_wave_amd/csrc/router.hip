@@ -18,9 +18,9 @@
 // pattern is mapped to an unsigned key that orders like the value (sign bit
 // set: all bits flipped, else the sign bit set), and key = (value key << 32) |
 // ~expert makes "largest value, then lowest expert index" a plain 64-bit
-// maximum.  Sixteen lanes (one DPP row) serve one token: each scans every 16th
-// expert for its best untaken key, the row takes the maximum with row_ror DPP
-// moves, k times.  The weights use the chosen experts' scores, summed in slot
+// maximum.  Sixteen lanes (one DPP row) serve one token: each keeps the keys
+// of every 16th expert in registers and offers its best untaken one, the row
+// takes the maximum with row_ror DPP moves, k times.  The weights use the chosen experts' scores, summed in slot
 // order.
 
 #include "internal.h"
@@ -185,84 +185,80 @@ __device__ __forceinline__ unsigned long long row16_max(unsigned long long v) {
 
 constexpr int kSelThreads = 1024;   // 16 waves x 4 tokens = 64 tokens (one routing block)
 
-// Copies the scores of a 64-token routing block into an LDS tile [tb][E + 1]
-// (tb = 64 when E is small; larger E takes the block in sub-batches), then
-// selects k experts per token, 16 lanes each.  Writes idx/w and, when
-// blk_counts is given, the block's per-expert pair count.
 __device__ __forceinline__ uint32_t order_key(float v) {
     const uint32_t b = __float_as_uint(v);
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// One 64-token routing block per workgroup, 16 lanes (one DPP row) per
+// token.  Lane j keeps the order keys of experts j, j + 16, ... (NQ of them)
+// in registers, clamped to at least 1 so that 0 can mark "taken or absent".
+// A round takes each lane's largest key (the lowest index among equals), the
+// row's maximum of (key << 32 | ~expert) by DPP, and clears the winner's key.
+// Writes idx/w and, when blk_counts is given, the block's per-expert pair
+// count.
+template <int NQ>
 __global__ __launch_bounds__(kSelThreads) void k_router_select(
     const float* __restrict__ scores, const float* __restrict__ score_bias, int T, int E, int k,
-    float scale, int tb, int32_t* __restrict__ idx, float* __restrict__ wout,
+    float scale, int32_t* __restrict__ idx, float* __restrict__ wout,
     int32_t* __restrict__ blk_counts, int nb) {
-    extern __shared__ uint32_t s_score[];              // [tb][E + 1]
     __shared__ unsigned long long mask[1024];
     const int tid = threadIdx.x;
-    const int ld = E + 1;
     for (int e = tid; e < E; e += kSelThreads) mask[e] = 0ull;
     const int lane = tid & 63;
     const int j = lane & 15;                              // lane within the token's row
-    const int ts = (tid >> 6) * 4 + (lane >> 4);          // token slot within a sub-batch
+    const int ts = (tid >> 6) * 4 + (lane >> 4);          // token slot within the block
+    const int t = blockIdx.x * kRouteBlock + ts;
+    const bool active = t < T;
+    const float* srow = scores + static_cast<size_t>(active ? t : 0) * E;
 
-    for (int sb = 0; sb < kRouteBlock; sb += tb) {
-        const int t_first = blockIdx.x * kRouteBlock + sb;
-        const int ntok = min(tb, T - t_first);
-        if (ntok <= 0) break;
-        __syncthreads();
-        const float* src = scores + static_cast<size_t>(t_first) * E;
-        for (int p = tid; p < ntok * E; p += kSelThreads) {
-            const int tl = p / E;
-            const int e = p - tl * E;
-            s_score[tl * ld + e] = order_key(score_bias ? src[p] + score_bias[e] : src[p]);
+    uint32_t key[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int e = j + 16 * q;
+        key[q] = 0u;
+        if (active && e < E) {
+            const float v = score_bias ? srow[e] + score_bias[e] : srow[e];
+            key[q] = max(order_key(v), 1u);
         }
-        __syncthreads();
-
-        const bool active = ts < ntok;
-        const uint32_t* srow = s_score + (active ? ts : 0) * ld;
-        unsigned long long taken = 0ull;                   // bit q: expert j + 16q chosen
-        int my_e = 0;
-        for (int r = 0; r < k; ++r) {
-            unsigned long long best = 0ull;
-            if (active) {
-                for (int q = 0, e = j; e < E; ++q, e += 16) {
-                    if (!((taken >> q) & 1ull)) {
-                        const unsigned long long key =
-                            (static_cast<unsigned long long>(srow[e]) << 32) |
-                            static_cast<uint32_t>(~static_cast<uint32_t>(e));
-                        best = key > best ? key : best;
-                    }
-                }
-            }
-            best = row16_max(best);
-            const int e_win = static_cast<int>(~static_cast<uint32_t>(best & 0xffffffffull));
-            if ((e_win & 15) == j) taken |= 1ull << (e_win >> 4);
-            if (r == j) my_e = e_win;
+    }
+    int my_e = 0;
+    for (int r = 0; r < k; ++r) {
+        uint32_t bk = 0u;
+        int bq = 0;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const bool better = key[q] > bk;
+            bk = better ? key[q] : bk;
+            bq = better ? q : bq;
         }
-        // lane j < k holds slot j; the weights use the scores themselves
-        const float my_s = (active && j < k) ? src[static_cast<size_t>(ts) * E + my_e] : 0.f;
-        float sum = 0.f;
-        for (int r = 0; r < k; ++r) sum += __shfl(my_s, (lane & ~15) | r, 64);   // slot order
-        if (active && j < k) {
-            const size_t pair = static_cast<size_t>(t_first + ts) * k + j;
-            idx[pair] = my_e;
-            wout[pair] = scale * (my_s / sum);
-            atomicOr(&mask[my_e], 1ull << (sb + ts));
-        }
+        unsigned long long best =
+            bk ? (static_cast<unsigned long long>(bk) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(j + 16 * bq))
+               : 0ull;
+        best = row16_max(best);
+        const int e_win = static_cast<int>(~static_cast<uint32_t>(best & 0xffffffffull));
+        const bool mine = (e_win & 15) == j;
+        const int qw = e_win >> 4;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) key[q] = (mine && q == qw) ? 0u : key[q];
+        if (r == j) my_e = e_win;
+    }
+    __syncthreads();                                      // mask cleared
+    // lane j < k holds slot j; the weights use the scores themselves
+    const float my_s = (active && j < k) ? srow[my_e] : 0.f;
+    float sum = 0.f;
+    for (int r = 0; r < k; ++r) sum += __shfl(my_s, (lane & ~15) | r, 64);   // slot order
+    if (active && j < k) {
+        const size_t pair = static_cast<size_t>(t) * k + j;
+        idx[pair] = my_e;
+        wout[pair] = scale * (my_s / sum);
+        atomicOr(&mask[my_e], 1ull << ts);
     }
     if (blk_counts) {
         __syncthreads();
         for (int e = tid; e < E; e += kSelThreads)
             blk_counts[static_cast<size_t>(e) * nb + blockIdx.x] = __popcll(mask[e]);
     }
-}
-
-int select_tokens_per_pass(int E) {
-    int tb = kRouteBlock;
-    while (tb > 8 && static_cast<size_t>(tb) * (E + 1) * sizeof(uint32_t) > 65536) tb >>= 1;
-    return tb;
 }
 
 }  // namespace
@@ -294,10 +290,19 @@ hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bi
         hipLaunchKernelGGL(k_router_reduce, dim3(static_cast<unsigned>((te + 255) / 256)), dim3(256),
                            0, s, rw.partial, bias, rw.scores, T, E, rw.nsplit);
     }
-    const int tb = select_tokens_per_pass(E);
-    hipLaunchKernelGGL(k_router_select, dim3(nb), dim3(kSelThreads),
-                       static_cast<size_t>(tb) * (E + 1) * sizeof(uint32_t), s, rw.scores,
-                       score_bias, T, E, k, scale, tb, idx, w, blk_counts, nb);
+    // keys per lane: E / 16 rounded up to a power of two (E <= 1024)
+    const int nq = (E + 15) / 16;
+#define HY3_SELECT(NQ)                                                                             \
+    hipLaunchKernelGGL(k_router_select<NQ>, dim3(nb), dim3(kSelThreads), 0, s, rw.scores, score_bias, \
+                       T, E, k, scale, idx, w, blk_counts, nb)
+    if (nq <= 1) HY3_SELECT(1);
+    else if (nq <= 2) HY3_SELECT(2);
+    else if (nq <= 4) HY3_SELECT(4);
+    else if (nq <= 8) HY3_SELECT(8);
+    else if (nq <= 16) HY3_SELECT(16);
+    else if (nq <= 32) HY3_SELECT(32);
+    else HY3_SELECT(64);
+#undef HY3_SELECT
     return hipGetLastError();
 }
 
