@@ -67,33 +67,6 @@ constexpr int kSlots = 4;                      // LDS ring depth
 constexpr int kXcds = 8;
 constexpr int kChunkBlocks = 8;                // row blocks of 128 per chunk (see work order)
 
-__device__ __forceinline__ int pchunk(int row, int c) { return c ^ ((row >> 2) & 3); }
-
-constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-// 16 bytes per lane from global memory into LDS: lane i's bytes land at
-// lds_base + 16 i (lds_base is wave-uniform, passed in M0; one wait state
-// between the M0 write and the copy).  M0 is listed as clobbered although
-// the compiler reserves it: nothing else in this file's device code uses M0
-// (the compiler sets it only for its own LDS-DMA builtins and for indirect
-// register indexing, neither of which appears here).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy_to_lds(const uint8_t* g, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds_base) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Barrier after this wave's LDS reads have completed; copies in flight are
-// not waited for.  Compiler fences keep memory operations on their side.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 struct Unit {
     int e, row0, rows, n;                          // n: column tile index of this shape
 };

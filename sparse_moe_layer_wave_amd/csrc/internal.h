@@ -37,6 +37,43 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g * u * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// ---- LDS staging used by the MFMA kernels (grouped GEMMs, router logits) ----
+
+// LDS rows of 64 bytes keep logical 16-byte chunk c at physical chunk
+// c ^ ((row >> 2) & 3): the 16 lanes of one phase of a fragment read (16 rows,
+// one logical chunk) then hit 16 distinct 4-bank groups, all 64 banks once.
+__device__ __forceinline__ int pchunk(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+// s_waitcnt immediate that waits until at most n vector memory operations of
+// the wave are outstanding (lgkmcnt and expcnt not waited for).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// 16 bytes per lane from global memory into LDS: lane i's bytes land at
+// lds_base + 16 i (lds_base is wave-uniform, passed in M0; one wait state
+// between the M0 write and the copy).  Written in assembly so that the
+// compiler does not treat the copy as an LDS store and wait for it before
+// every LDS read; the kernels wait for their copies with explicit vmcnt
+// counts.  M0 is listed as clobbered although the compiler reserves it: no
+// device code of the kernels that use this touches M0 otherwise (the
+// compiler sets it only for its own LDS-DMA builtins and for indirect
+// register indexing, neither of which they contain).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy_to_lds(const uint8_t* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Barrier after this wave's LDS reads have completed; copies in flight are
+// not waited for.  Compiler fences keep memory operations on their side.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Workspace carving, computed identically on the host for every entry point.
 struct Layout {
     size_t planes, partial, scores, blk_counts, blk_base, counts, offsets, tile_off, idx, w,

@@ -118,6 +118,21 @@ def test_route_entry_matches_forward_routing(gpu_lib):
     assert torch.equal(idx_r, idx_f) and torch.equal(w_r, w_f)
 
 
+@pytest.mark.parametrize("T,E,k,d", [(5000, 200, 8, 320), (4096, 1024, 16, 128), (4100, 7, 3, 64)])
+def test_router_large_batch_shapes(gpu_lib, T, E, k, d):
+    """Batches of 4096 tokens or more take the LDS-staged logits kernel:
+    token tiles of 256 with a ragged last one, expert groups of 192 with a
+    partial last one (E = 200, 1024) or a single short one (E = 7)."""
+    from sparse_moe_layer_wave_amd import hy3moe as hy
+    c = dict(inputs.CONFIGS[0], T=T, E=E, k=k, d=d, F=64, seed=300 + E)
+    inp_cpu = _cpu_case(c)
+    inp = _to("cuda", inp_cpu)
+    idx, w = hy.route(inp["x"], inp["W_gate"], k, inp["scale"])
+    torch.cuda.synchronize()
+    r = oracle.route(inputs.bits(inp_cpu["x"]), inp_cpu["W_gate"].numpy(), k, inp_cpu["scale"], None)
+    print(T, E, k, d, check_routing(idx.cpu().numpy(), w.cpu().numpy(), r, inp_cpu["scale"]))
+
+
 def test_zero_tokens_tie_to_lowest_experts(gpu_lib):
     inp = _cpu_case(0, T=64, seed=8)
     inp["x"][5] = 0
