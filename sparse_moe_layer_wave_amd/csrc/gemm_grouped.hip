@@ -25,20 +25,22 @@
 // square tiles and an odd last block as a wide tile, so no tile carries more
 // than 127 padding rows and both shapes do the same MFMA work.
 //
-// K advances in slices of 64 bytes per row (32 bf16 = two steps of
-// v_mfma_f32_32x32x16_bf16, or 64 e4m3 = one step of
-// v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales).  A slice of a tile is
-// 32 or 40 one-kilobyte copies (16 rows each), issued as
-// global_load_lds_dwordx4 straight into a 4-slot LDS ring, two slices
-// ahead of use; every wave issues its own share.  The copies are written in
-// inline assembly: the compiler does not see them as LDS stores and so does
-// not wait for all of them before each LDS read; the loop instead waits
-// (s_waitcnt vmcnt) for exactly the slice it needs and then meets the other
-// waves at a barrier.  Fragments of slice k+1 are read from LDS while the
-// MFMAs of slice k run, and the copies and reads are spread between the
-// MFMAs so that neither memory queue stalls the wave.
+// K advances in slices of 128 bytes per row (64 bf16 = four steps of
+// v_mfma_f32_32x32x16_bf16, or 128 e4m3 = two steps of
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales): whole cache lines, so
+// no line is requested twice.  A slice of a tile is 64 or 80 one-kilobyte
+// copies (8 rows each), issued as global_load_lds_dwordx4 straight into a
+// 2-slot LDS ring (64 or 80 KB per slot); every wave issues its own share.
+// The copies are written in inline assembly: the compiler does not see them
+// as LDS stores and so does not wait for all of them before each LDS read;
+// the loop instead waits (s_waitcnt vmcnt) for the slice it needs and then
+// meets the other waves at a barrier.  A slice is consumed in two halves of
+// 64 bytes: the fragments of the next half are read from LDS while the
+// MFMAs of the current half run, and the copies refilling the ring are
+// spread between the MFMAs of the second half, so that neither memory
+// queue stalls the wave.
 //
-// LDS row r keeps logical 16-byte chunk c at physical chunk c ^ ((r >> 2) & 3):
+// LDS row r keeps logical 16-byte chunk c at physical chunk c ^ ((r >> 1) & 7):
 // the 16 lanes of one phase of a fragment read (16 rows at one logical chunk)
 // then hit 16 distinct 4-bank groups, all 64 banks once.
 // MFMA lane layout: A lane l holds row l%32 and 16 bytes (bf16: k 8*(l/32)..+8
@@ -61,9 +63,9 @@ namespace {
 
 enum Mode { GU_BF16 = 0, DN_BF16 = 1, GU_FP8 = 2, DN_FP8 = 3 };
 
-constexpr int kRowB = 64;                      // bytes per LDS row (one K slice)
+constexpr int kRowB = 128;                     // bytes per LDS row (one K slice)
 constexpr int kLdsBytes = 160 * 1024;          // the whole LDS of a CU
-constexpr int kSlots = 4;                      // LDS ring depth
+constexpr int kSlots = 2;                      // LDS ring depth
 constexpr int kXcds = 8;
 constexpr int kChunkBlocks = 8;                // row blocks of 128 per chunk (see work order)
 
@@ -94,18 +96,24 @@ struct Args {
     int K, N, E, npanel;                           // K in elements; npanel: 512-row panels per expert
 };
 
+// LDS rows of one slice are 128 bytes: logical 16-byte chunk c of row r sits
+// at physical chunk c ^ ((r >> 1) & 7).  A fragment read phase (16 rows at
+// one logical chunk) then touches 16 distinct 4-bank groups.
+__device__ __forceinline__ int pchunk8(int row, int c) { return c ^ ((row >> 1) & 7); }
+
 // One tile.  SQUARE: 256 rows x 256 weight rows; else 128 x 512.
 template <int MODE, bool SQUARE>
 __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u, int wave) {
     constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8;
     constexpr bool FP8 = MODE == GU_FP8 || MODE == DN_FP8;
     constexpr int RA = SQUARE ? 256 : 128;         // A rows per slice
-    constexpr int NPW = SQUARE ? 8 : 10;           // 1 KB copies per wave per slice
     constexpr int WCOLS = SQUARE ? 128 : 256;      // gate_up: h columns of the tile
     constexpr int NCOLS = SQUARE ? 256 : 512;      // down: output columns of the tile
-    constexpr int kSlotBytes = (RA + NCOLS) * kRowB;   // one slice: 32 or 40 KB
+    constexpr int ROWS = RA + NCOLS;               // LDS rows of a slice
+    constexpr int NPW = ROWS / 8 / 4;              // 1 KB copies (8 rows) per wave per slice: 16 or 20
+    constexpr int kSlotBytes = ROWS * kRowB;       // one slice: 64 or 80 KB
     static_assert(kSlots * kSlotBytes <= kLdsBytes, "LDS");
-    constexpr int NMFMA = FP8 ? 16 : 32;           // MFMAs per slice and wave
+    constexpr int NMFMA = FP8 ? 16 : 32;           // MFMAs per half slice and wave
     const int N = g.N;
     const int lane = lane_id();
     const int tid = wave * 64 + lane;
@@ -114,17 +122,22 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
     const size_t rowbytes = static_cast<size_t>(g.K) * (FP8 ? 1 : 2);
     const int nk = static_cast<int>(rowbytes / kRowB);
 
-    // ---- copy sources: copy j of this wave fills LDS rows 16 i .. 16 i + 15,
-    // i = wave * NPW + j; lane -> row 16 i + lane / 4, physical chunk lane % 4
-    const uint8_t* src[NPW];
+    // ---- copy sources: copy j of this wave fills LDS rows 8 i .. 8 i + 7,
+    // i = wave * NPW + j; lane -> row 8 i + lane / 8, physical chunk lane % 8,
+    // so each row's 128 bytes (a whole cache line) come from one copy.  Per
+    // copy the lane keeps the 32-bit index of its source row (token row or
+    // weight row); the address is formed when the copy is issued.  Whether a
+    // copy reads token rows or weight rows depends on (wave, j) only.
+    const uint8_t* We = (g.W_last && u.e == g.E - 1)
+                            ? g.W_last
+                            : g.W + static_cast<size_t>(u.e) * (GATE_UP ? 2 * N : N) * rowbytes;
+    int srow_of[NPW];
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
-        const int row = 16 * (wave * NPW + j) + (lane >> 2);
-        const int lc = pchunk(row, lane & 3);
-        if (row < RA) {
+        const int row = 8 * (wave * NPW + j) + (lane >> 3);
+        if (8 * (wave * NPW + j) < RA) {
             const int r = min(row, u.rows - 1);                // padding rows repeat a valid row
-            const size_t ar = GATE_UP ? static_cast<size_t>(g.tok_of[u.row0 + r]) : static_cast<size_t>(u.row0 + r);
-            src[j] = g.A + ar * rowbytes + lc * 16;
+            srow_of[j] = GATE_UP ? g.tok_of[u.row0 + r] : u.row0 + r;
         } else {
             const int p = row - RA;                            // weight panel row
             int wr;
@@ -135,27 +148,38 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
                 wr = u.n * NCOLS + p;
                 wr = wr < N ? wr : 0;
             }
-            const uint8_t* We = (g.W_last && u.e == g.E - 1)
-                                    ? g.W_last
-                                    : g.W + static_cast<size_t>(u.e) * (GATE_UP ? 2 * N : N) * rowbytes;
-            src[j] = We + static_cast<size_t>(wr) * rowbytes + lc * 16;
+            srow_of[j] = wr;
         }
     }
+    // logical chunk of the lane: (row >> 1) & 7 = 4 (i & 1) + lane / 16
+    int lco[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) lco[q] = ((lane & 7) ^ (4 * q + (lane >> 4))) * 16;
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
     const uint32_t my_copies = lds0 + static_cast<uint32_t>(wave * NPW) * 1024u;
+    auto issue_copy = [&](int j, int kt, uint32_t slot) {
+        const uint8_t* base = (8 * (wave * NPW + j) < RA) ? g.A : We;
+        const uint8_t* src = base + static_cast<size_t>(static_cast<uint32_t>(srow_of[j])) * rowbytes +
+                             static_cast<size_t>(kt) * kRowB + lco[(wave * NPW + j) & 1];
+        copy_to_lds(src, slot + j * 1024);
+    };
 
     // ---- fragment addresses: rows a0 + 32 mb + l32 and b0 + 32 nb + l32; the
     // physical chunk only depends on l32 (block offsets are multiples of 32).
-    // Half-fragment h of a block is one 16-byte read: bf16: the lane's 8
-    // values of k step h (chunk 2 h + khalf); e4m3: bytes 16 h.. of the lane's
-    // 32 (chunk 2 khalf + h).
+    // A slice is two halves of 64 bytes; half-fragment h of a block in half
+    // hs is one 16-byte read: bf16: the lane's 8 values of k step 2 hs + h
+    // (chunk 4 hs + 2 h + khalf); e4m3: bytes 16 h.. of the lane's 32 of the
+    // k step hs (chunk 4 hs + 2 khalf + h).
     const int l32 = lane & 31;
     const int khalf = lane >> 5;
     const int a0 = wm * 128;
     const int b0 = RA + wn * 128;
-    int off[2];
+    int off[2][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) off[h] = l32 * kRowB + pchunk(l32, FP8 ? 2 * khalf + h : 2 * h + khalf) * 16;
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            off[hs][h] = l32 * kRowB + pchunk8(l32, FP8 ? 4 * hs + 2 * khalf + h : 4 * hs + 2 * h + khalf) * 16;
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -163,13 +187,13 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16_t{};
 
-    // read r of a slice (16 per slice): half h = r / 8; r % 8 < 4: A block r % 4,
-    // else B block r % 4
-    i32x4_t fa[2][2][4], fb[2][2][4];                  // [set][half][block]
-    auto read_frag = [&](int set, const uint8_t* base, int r) {
+    // read r of a half slice (16 per half): h = r / 8; r % 8 < 4: A block
+    // r % 4, else B block r % 4
+    i32x4_t fa[2][2][4], fb[2][2][4];                  // [set][h][block]
+    auto read_frag = [&](int set, const uint8_t* base, int hs, int r) {
         const int h = r >> 3, b = r & 3;
-        if ((r & 4) == 0) fa[set][h][b] = *reinterpret_cast<const i32x4_t*>(base + (a0 + 32 * b) * kRowB + off[h]);
-        else fb[set][h][b] = *reinterpret_cast<const i32x4_t*>(base + (b0 + 32 * b) * kRowB + off[h]);
+        if ((r & 4) == 0) fa[set][h][b] = *reinterpret_cast<const i32x4_t*>(base + (a0 + 32 * b) * kRowB + off[hs][h]);
+        else fb[set][h][b] = *reinterpret_cast<const i32x4_t*>(base + (b0 + 32 * b) * kRowB + off[hs][h]);
     };
     auto mfma = [&](int set, int i) {
         if constexpr (FP8) {
@@ -185,60 +209,59 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
         }
     };
 
-    // ---- prologue: slices 0 .. kSlots-2 in flight (clamped: a short K
-    // re-reads its last slice), slice 0 read
+    // ---- prologue: slices 0 and 1 in flight (clamped: a one-slice K
+    // re-reads slice 0), the first half of slice 0 read
 #pragma unroll
-    for (int s = 0; s < kSlots - 1; ++s) {
+    for (int s = 0; s < kSlots; ++s) {
         const int kt = min(s, nk - 1);
 #pragma unroll
-        for (int j = 0; j < NPW; ++j) copy_to_lds(src[j] + kt * kRowB, my_copies + s * kSlotBytes + j * 1024);
+        for (int j = 0; j < NPW; ++j) issue_copy(j, kt, my_copies + s * kSlotBytes);
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kSlots - 2) * NPW));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NPW));
     lds_barrier();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) read_frag(0, lds, r);
+    for (int r = 0; r < 16; ++r) read_frag(0, lds, 0, r);
 
-    // ---- main loop, two slices per trip (fragment sets 0 and 1).  Slice kt
-    // runs its MFMAs on fragments read during slice kt - 1, reads slice kt + 1
-    // and refills the slot of slice kt - 1 with slice kt + kSlots - 1.  That
-    // slot's reads were consumed by the MFMAs of slice kt - 1, which every
-    // wave has issued before the barrier at the top of slice kt, so the
-    // barrier needs no wait for LDS reads: the reads of slice kt, still in
-    // flight, are waited for by the MFMAs that use them (the compiler's
-    // per-register waits), not at the barrier.  Every slice issues exactly
-    // NPW copies (slices past the end re-read the last one into a slot nobody
-    // reads again), so the waits are exact: at the top of slice kt, slices up
-    // to kt + kSlots - 2 are issued and kt + 1 must have landed.  Copy j
-    // follows MFMA j * NMFMA / NPW and the 16 fragment reads of slice kt + 1
-    // are spread evenly over the MFMAs.
-    auto step = [&](int kt, int set) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kSlots - 3) * NPW));
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();                  // everyone: slice kt - 1 consumed, kt + 1 landed
-        asm volatile("" ::: "memory");
-        const int kin = min(kt + kSlots - 1, nk - 1);
-        const uint32_t islot = my_copies + ((kt + kSlots - 1) & (kSlots - 1)) * kSlotBytes;
-        const uint8_t* rbase = lds + ((kt + 1) & (kSlots - 1)) * kSlotBytes;
+    // ---- main loop over slices, each in two halves.  First half: MFMAs on
+    // the first half of slice kt (read during slice kt - 1), reading its
+    // second half.  Then wait until slice kt + 1 has landed and meet the
+    // other waves: every read of slice kt is then done (lds_barrier waits
+    // for this wave's reads), so its slot is free.  Second half: MFMAs on the
+    // second half, reading the first half of slice kt + 1 and refilling the
+    // slot with slice kt + 2 (slices past the end re-read the last one into
+    // a slot nobody reads again).  Copy j follows MFMA j * NMFMA / NPW; the
+    // 16 fragment reads are spread evenly over the MFMAs.
+    for (int kt = 0; kt < nk; ++kt) {
+        const uint8_t* cur = lds + (kt & 1) * kSlotBytes;
+        const uint8_t* nxt = lds + ((kt + 1) & 1) * kSlotBytes;
 #pragma unroll
         for (int i = 0; i < NMFMA; ++i) {
-            mfma(set, i);
-#pragma unroll
-            for (int j = 0; j < NPW; ++j)
-                if (i == j * NMFMA / NPW) copy_to_lds(src[j] + kin * kRowB, islot + j * 1024);
+            mfma(0, i);
             if constexpr (FP8) {
-                read_frag(set ^ 1, rbase, i);
+                read_frag(1, cur, 1, i);
             } else {
-                if (i & 1) read_frag(set ^ 1, rbase, i >> 1);
+                if (i & 1) read_frag(1, cur, 1, i >> 1);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        step(kt, 0);
-        step(kt + 1, 1);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        lds_barrier();                                 // slice kt + 1 landed, slice kt read by all
+        const int kin = min(kt + 2, nk - 1);
+        const uint32_t islot = my_copies + (kt & 1) * kSlotBytes;
+#pragma unroll
+        for (int i = 0; i < NMFMA; ++i) {
+            mfma(1, i);
+#pragma unroll
+            for (int j = 0; j < NPW; ++j)
+                if (i == j * NMFMA / NPW) issue_copy(j, kin, islot);
+            if constexpr (FP8) {
+                read_frag(0, nxt, 0, i);
+            } else {
+                if (i & 1) read_frag(0, nxt, 0, i >> 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    if (kt < nk) step(kt, 0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));          // no copy may land after the tile ends
 
     // ---- epilogue.  Each wave stages its output block in LDS (row-major,
