@@ -29,8 +29,11 @@
 // v_mfma_f32_32x32x16_bf16, or 128 e4m3 = two steps of
 // v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales): whole cache lines, so
 // no line is requested twice.  A slice of a tile is 64 or 80 one-kilobyte
-// copies (8 rows each), issued as global_load_lds_dwordx4 straight into a
-// 2-slot LDS ring (64 or 80 KB per slot); every wave issues its own share.
+// copies (8 rows each), issued as global_load_lds_dwordx4 straight into LDS
+// rings; every wave issues its own share.  Square tiles keep token rows and
+// weight rows in rings of their own (2 and 3 slots of 32 KB), so the weight
+// copies of a slice start a half slice earlier and a barrier never waits for
+// the whole queue; wide tiles use one ring of 2 slots of 80 KB.
 // The copies are written in inline assembly: the compiler does not see them
 // as LDS stores and so does not wait for all of them before each LDS read;
 // the loop instead waits (s_waitcnt vmcnt) for the slice it needs and then
@@ -110,9 +113,6 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
     constexpr int WCOLS = SQUARE ? 128 : 256;      // gate_up: h columns of the tile
     constexpr int NCOLS = SQUARE ? 256 : 512;      // down: output columns of the tile
     constexpr int ROWS = RA + NCOLS;               // LDS rows of a slice
-    constexpr int NPW = ROWS / 8 / 4;              // 1 KB copies (8 rows) per wave per slice: 16 or 20
-    constexpr int kSlotBytes = ROWS * kRowB;       // one slice: 64 or 80 KB
-    static_assert(kSlots * kSlotBytes <= kLdsBytes, "LDS");
     constexpr int NMFMA = FP8 ? 16 : 32;           // MFMAs per half slice and wave
     const int N = g.N;
     const int lane = lane_id();
@@ -122,24 +122,36 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
     const size_t rowbytes = static_cast<size_t>(g.K) * (FP8 ? 1 : 2);
     const int nk = static_cast<int>(rowbytes / kRowB);
 
-    // ---- copy sources: copy j of this wave fills LDS rows 8 i .. 8 i + 7,
-    // i = wave * NPW + j; lane -> row 8 i + lane / 8, physical chunk lane % 8,
-    // so each row's 128 bytes (a whole cache line) come from one copy.  Per
-    // copy the lane keeps the 32-bit index of its source row (token row or
-    // weight row); the address is formed when the copy is issued.  Whether a
-    // copy reads token rows or weight rows depends on (wave, j) only.
+    // ---- copy sources.  A copy fills 8 LDS rows of 128 bytes (lane -> row
+    // + lane / 8, physical chunk lane % 8), so each row's whole cache line
+    // comes from one copy.  Per copy the lane keeps the 32-bit index of its
+    // source row (token row or weight row); the address is formed when the
+    // copy is issued.
+    //   square: token rows and weight rows have rings of their own, 2 and 3
+    //     slots of 32 KB; copy j < 8 of a wave fills token row group
+    //     8 wave + j, copy 8 + j weight row group 8 wave + j;
+    //   wide: one ring of 2 slots of 80 KB (128 token rows, then 512 weight
+    //     rows); copy j fills row group 20 wave + j.
+    // Whether a copy reads token rows or weight rows depends on (wave, j) only.
+    constexpr int NPW = SQUARE ? 16 : 20;          // 1 KB copies per wave per slice
+    constexpr int kASlot = RA * kRowB;             // square: token ring slot (32 KB)
+    constexpr int kBSlot = NCOLS * kRowB;          // square: weight ring slot (32 KB)
+    constexpr int kSlotBytes = ROWS * kRowB;       // wide: ring slot (80 KB)
+    static_assert(SQUARE ? 2 * kASlot + 3 * kBSlot <= kLdsBytes : kSlots * kSlotBytes <= kLdsBytes, "LDS");
+    auto is_a = [&](int j) { return SQUARE ? j < 8 : 8 * (wave * NPW + j) < RA; };
+    auto group = [&](int j) { return SQUARE ? 8 * wave + (j & 7) : wave * NPW + j; };   // within its ring slot
     const uint8_t* We = (g.W_last && u.e == g.E - 1)
                             ? g.W_last
                             : g.W + static_cast<size_t>(u.e) * (GATE_UP ? 2 * N : N) * rowbytes;
     int srow_of[NPW];
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
-        const int row = 8 * (wave * NPW + j) + (lane >> 3);
-        if (8 * (wave * NPW + j) < RA) {
+        const int row = 8 * group(j) + (lane >> 3);
+        if (is_a(j)) {
             const int r = min(row, u.rows - 1);                // padding rows repeat a valid row
             srow_of[j] = GATE_UP ? g.tok_of[u.row0 + r] : u.row0 + r;
         } else {
-            const int p = row - RA;                            // weight panel row
+            const int p = SQUARE ? row : row - RA;             // weight panel row
             int wr;
             if (GATE_UP) {
                 const int col = u.n * WCOLS + (p >> 7) * 64 + (p & 63);
@@ -151,29 +163,30 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
             srow_of[j] = wr;
         }
     }
-    // logical chunk of the lane: (row >> 1) & 7 = 4 (i & 1) + lane / 16
+    // logical chunk of the lane: (row >> 1) & 7 = 4 (group & 1) + lane / 16
     int lco[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) lco[q] = ((lane & 7) ^ (4 * q + (lane >> 4))) * 16;
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-    const uint32_t my_copies = lds0 + static_cast<uint32_t>(wave * NPW) * 1024u;
+    // slot: LDS address of the ring slot the copy fills
     auto issue_copy = [&](int j, int kt, uint32_t slot) {
-        const uint8_t* base = (8 * (wave * NPW + j) < RA) ? g.A : We;
+        const uint8_t* base = is_a(j) ? g.A : We;
         const uint8_t* src = base + static_cast<size_t>(static_cast<uint32_t>(srow_of[j])) * rowbytes +
-                             static_cast<size_t>(kt) * kRowB + lco[(wave * NPW + j) & 1];
-        copy_to_lds(src, slot + j * 1024);
+                             static_cast<size_t>(kt) * kRowB + lco[group(j) & 1];
+        copy_to_lds(src, slot + group(j) * 1024);
     };
 
-    // ---- fragment addresses: rows a0 + 32 mb + l32 and b0 + 32 nb + l32; the
-    // physical chunk only depends on l32 (block offsets are multiples of 32).
-    // A slice is two halves of 64 bytes; half-fragment h of a block in half
-    // hs is one 16-byte read: bf16: the lane's 8 values of k step 2 hs + h
-    // (chunk 4 hs + 2 h + khalf); e4m3: bytes 16 h.. of the lane's 32 of the
-    // k step hs (chunk 4 hs + 2 khalf + h).
+    // ---- fragment addresses: token rows a0 + 32 mb + l32 and weight rows
+    // b0 + 32 nb + l32 of their slots; the physical chunk only depends on l32
+    // (block offsets are multiples of 32).  A slice is two halves of 64
+    // bytes; half-fragment h of a block in half hs is one 16-byte read:
+    // bf16: the lane's 8 values of k step 2 hs + h (chunk 4 hs + 2 h + khalf);
+    // e4m3: bytes 16 h.. of the lane's 32 of the k step hs (chunk
+    // 4 hs + 2 khalf + h).
     const int l32 = lane & 31;
     const int khalf = lane >> 5;
     const int a0 = wm * 128;
-    const int b0 = RA + wn * 128;
+    const int b0 = (SQUARE ? 0 : RA) + wn * 128;
     int off[2][2];
 #pragma unroll
     for (int hs = 0; hs < 2; ++hs)
@@ -188,12 +201,12 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16_t{};
 
     // read r of a half slice (16 per half): h = r / 8; r % 8 < 4: A block
-    // r % 4, else B block r % 4
+    // r % 4 (from abase), else B block r % 4 (from bbase)
     i32x4_t fa[2][2][4], fb[2][2][4];                  // [set][h][block]
-    auto read_frag = [&](int set, const uint8_t* base, int hs, int r) {
+    auto read_frag = [&](int set, const uint8_t* abase, const uint8_t* bbase, int hs, int r) {
         const int h = r >> 3, b = r & 3;
-        if ((r & 4) == 0) fa[set][h][b] = *reinterpret_cast<const i32x4_t*>(base + (a0 + 32 * b) * kRowB + off[hs][h]);
-        else fb[set][h][b] = *reinterpret_cast<const i32x4_t*>(base + (b0 + 32 * b) * kRowB + off[hs][h]);
+        if ((r & 4) == 0) fa[set][h][b] = *reinterpret_cast<const i32x4_t*>(abase + (a0 + 32 * b) * kRowB + off[hs][h]);
+        else fb[set][h][b] = *reinterpret_cast<const i32x4_t*>(bbase + (b0 + 32 * b) * kRowB + off[hs][h]);
     };
     auto mfma = [&](int set, int i) {
         if constexpr (FP8) {
@@ -208,58 +221,112 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
                 acc[mb][nb], 0, 0, 0);
         }
     };
-
-    // ---- prologue: slices 0 and 1 in flight (clamped: a one-slice K
-    // re-reads slice 0), the first half of slice 0 read
-#pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-        const int kt = min(s, nk - 1);
-#pragma unroll
-        for (int j = 0; j < NPW; ++j) issue_copy(j, kt, my_copies + s * kSlotBytes);
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NPW));
-    lds_barrier();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) read_frag(0, lds, 0, r);
-
-    // ---- main loop over slices, each in two halves.  First half: MFMAs on
-    // the first half of slice kt (read during slice kt - 1), reading its
-    // second half.  Then wait until slice kt + 1 has landed and meet the
-    // other waves: every read of slice kt is then done (lds_barrier waits
-    // for this wave's reads), so its slot is free.  Second half: MFMAs on the
-    // second half, reading the first half of slice kt + 1 and refilling the
-    // slot with slice kt + 2 (slices past the end re-read the last one into
-    // a slot nobody reads again).  Copy j follows MFMA j * NMFMA / NPW; the
-    // 16 fragment reads are spread evenly over the MFMAs.
-    for (int kt = 0; kt < nk; ++kt) {
-        const uint8_t* cur = lds + (kt & 1) * kSlotBytes;
-        const uint8_t* nxt = lds + ((kt + 1) & 1) * kSlotBytes;
-#pragma unroll
-        for (int i = 0; i < NMFMA; ++i) {
-            mfma(0, i);
-            if constexpr (FP8) {
-                read_frag(1, cur, 1, i);
-            } else {
-                if (i & 1) read_frag(1, cur, 1, i >> 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+    // the 16 reads of a half are spread evenly over its MFMAs
+    auto read_at = [&](int set, const uint8_t* abase, const uint8_t* bbase, int hs, int i) {
+        if constexpr (FP8) {
+            read_frag(set, abase, bbase, hs, i);
+        } else {
+            if (i & 1) read_frag(set, abase, bbase, hs, i >> 1);
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        lds_barrier();                                 // slice kt + 1 landed, slice kt read by all
-        const int kin = min(kt + 2, nk - 1);
-        const uint32_t islot = my_copies + (kt & 1) * kSlotBytes;
+    };
+
+    if constexpr (SQUARE) {
+        // ---- square: token ring (2 slots) at 0, weight ring (3 slots) after.
+        // Slice kt: first half: MFMAs on its first half (read during slice
+        // kt - 1), reading its second half, and the weight copies of slice
+        // kt + 2 into the weight slot of slice kt - 1 (read by every wave
+        // before the barrier of slice kt - 1).  Barrier: slice kt + 1 landed
+        // (only the weight copies of kt + 2 may be in flight) and every read
+        // of slice kt done.  Second half: MFMAs on its second half, reading
+        // the first half of slice kt + 1, and the token copies of slice kt + 2
+        // into the token slot of slice kt.  Slices past the end re-read the
+        // last one into slots nobody reads again.  Issue order per wave:
+        // B(kt+1), A(kt+1), B(kt+2), so the waits are exact.
+        const uint32_t abase0 = lds0, bbase0 = lds0 + 2 * kASlot;
+        auto aslot = [&](int kt) { return kt & 1; };
+        auto bslot = [&](int kt) { return kt % 3; };
 #pragma unroll
-        for (int i = 0; i < NMFMA; ++i) {
-            mfma(1, i);
+        for (int s = 0; s < 2; ++s) {
+            const int kt = min(s, nk - 1);
 #pragma unroll
-            for (int j = 0; j < NPW; ++j)
-                if (i == j * NMFMA / NPW) issue_copy(j, kin, islot);
-            if constexpr (FP8) {
-                read_frag(0, nxt, 0, i);
-            } else {
-                if (i & 1) read_frag(0, nxt, 0, i >> 1);
+            for (int j = 8; j < 16; ++j) issue_copy(j, kt, bbase0 + s * kBSlot);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) issue_copy(j, kt, abase0 + s * kASlot);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));     // slice 0 landed
+        lds_barrier();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) read_frag(0, lds, lds + 2 * kASlot, 0, r);
+
+        for (int kt = 0; kt < nk; ++kt) {
+            const uint8_t* ca = lds + aslot(kt) * kASlot;
+            const uint8_t* cb = lds + 2 * kASlot + bslot(kt) * kBSlot;
+            const uint8_t* na = lds + aslot(kt + 1) * kASlot;
+            const uint8_t* nb_ = lds + 2 * kASlot + bslot(kt + 1) * kBSlot;
+            const int kin = min(kt + 2, nk - 1);
+            const uint32_t bfill = bbase0 + bslot(kt + 2) * kBSlot;
+#pragma unroll
+            for (int i = 0; i < NMFMA; ++i) {
+                mfma(0, i);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (i == j * NMFMA / 8) issue_copy(8 + j, kin, bfill);
+                read_at(1, ca, cb, 1, i);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+            lds_barrier();                             // slice kt + 1 landed, slice kt read by all
+            const uint32_t afill = abase0 + aslot(kt) * kASlot;
+#pragma unroll
+            for (int i = 0; i < NMFMA; ++i) {
+                mfma(1, i);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (i == j * NMFMA / 8) issue_copy(j, kin, afill);
+                read_at(0, na, nb_, 0, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else {
+        // ---- wide: one ring of 2 slots.  First half of slice kt: MFMAs on its
+        // first half, reading its second half.  Barrier: slice kt + 1 landed,
+        // every read of slice kt done.  Second half: MFMAs on its second half,
+        // reading the first half of slice kt + 1 and refilling the slot with
+        // slice kt + 2.
+        const uint32_t my_base = lds0;
+#pragma unroll
+        for (int s = 0; s < kSlots; ++s) {
+            const int kt = min(s, nk - 1);
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) issue_copy(j, kt, my_base + s * kSlotBytes);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NPW));
+        lds_barrier();
+#pragma unroll
+        for (int r = 0; r < 16; ++r) read_frag(0, lds, lds, 0, r);
+
+        for (int kt = 0; kt < nk; ++kt) {
+            const uint8_t* cur = lds + (kt & 1) * kSlotBytes;
+            const uint8_t* nxt = lds + ((kt + 1) & 1) * kSlotBytes;
+#pragma unroll
+            for (int i = 0; i < NMFMA; ++i) {
+                mfma(0, i);
+                read_at(1, cur, cur, 1, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            lds_barrier();                             // slice kt + 1 landed, slice kt read by all
+            const int kin = min(kt + 2, nk - 1);
+            const uint32_t islot = my_base + (kt & 1) * kSlotBytes;
+#pragma unroll
+            for (int i = 0; i < NMFMA; ++i) {
+                mfma(1, i);
+#pragma unroll
+                for (int j = 0; j < NPW; ++j)
+                    if (i == j * NMFMA / NPW) issue_copy(j, kin, islot);
+                read_at(0, nxt, nxt, 0, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));          // no copy may land after the tile ends
