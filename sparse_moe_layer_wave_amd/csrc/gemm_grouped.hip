@@ -51,11 +51,12 @@
 // the same for a weight row; C lane l holds column l%32 and rows
 // 8*(j/4) + 4*(l/32) + j%4, j = 0..15.
 //
-// Work order: a 1-D grid over units (expert, chunk of up to 8 row blocks,
-// 512-row weight panel, tile).  The tiles of one chunk that read the same
+// Work order: units (expert, chunk of up to 8 row blocks, 512-row weight
+// panel, tile) in one sequence; the tiles of one chunk that read the same
 // weight panel are adjacent, so the panel streams into L2 once for all of
-// them; workgroups are dealt round-robin over the 8 XCDs, so the block index is
-// remapped to give each XCD a contiguous run of units.
+// them.  The grid is persistent (one workgroup per CU): the sequence is cut
+// into 8 contiguous ranges, one per XCD, which that XCD's workgroups take
+// round-robin.
 
 #include <algorithm>
 

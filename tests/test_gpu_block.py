@@ -98,6 +98,20 @@ def test_route_ex_parity(gpu_lib, norm, sbias):
         assert np.mean(np.any(r0.idx != r.idx, axis=1)) > 0.2
 
 
+def test_route_ex_large_batch(gpu_lib):
+    """4096 tokens or more: the LDS-staged logits kernel, here with route_norm
+    and the score bias, a ragged last token tile and a partial expert group."""
+    from sparse_moe_layer_wave_amd import hy3moe as hy
+    inp_cpu = _case(4500, 256, 200, 8, 64, seed=77)
+    inp = _gpu(inp_cpu)
+    c = inp["cfg"]
+    idx, w = hy.route_ex(inp["x"], inp["W_gate"], c["k"], inp["scale"], norm_weight=inp["norm_w"],
+                         norm_eps=EPS, score_bias=inp["score_bias"])
+    torch.cuda.synchronize()
+    r = _oracle_route(inp_cpu, True, True)
+    print(check_routing(idx.cpu().numpy(), w.cpu().numpy(), r, inp_cpu["scale"]))
+
+
 def test_route_ex_negative_choice_values(gpu_lib):
     """A bias that makes most choice values negative still orders by value."""
     from sparse_moe_layer_wave_amd import hy3moe as hy
