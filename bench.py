@@ -103,8 +103,11 @@ def run_workload(cfg, steps, warmup):
     elapsed = time.perf_counter() - t0
     stage_ms = {name: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)]))
                 for i, name in enumerate(hy3moe.STAGES)}
+    # GPU time of each whole step (first to last stage event): median and spread
+    step_gpu = np.array([evs[s][0].elapsed_time(evs[s][len(hy3moe.STAGES)]) for s in range(steps)])
+    step_gpu_ms = {q: round(float(np.percentile(step_gpu, p)), 5) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
     alg = algorithmic(c, n_touched)
-    res = dict(cfg=c, ms_per_step=elapsed / steps * 1e3, tokens_per_s=T * steps / elapsed,
+    res = dict(cfg=c, ms_per_step=elapsed / steps * 1e3, tokens_per_s=T * steps / elapsed, step_gpu_ms=step_gpu_ms,
                stage_ms=stage_ms, n_touched=n_touched, alg=alg,
                layer_tflops=alg["layer_flops"] * steps / elapsed / 1e12,
                hottest_over_mean=float(load.max() / load.mean()))
@@ -209,7 +212,8 @@ def main():
             sys.exit(2)
         res, _ = run_workload(names[args.profile_workload], args.steps, args.warmup)
         print(json.dumps({"workload": args.profile_workload, "ms_per_step": round(res["ms_per_step"], 4),
-                          "kernel_ms": {k: round(v, 5) for k, v in res["stage_ms"].items()}}), flush=True)
+                          "kernel_ms": {k: round(v, 5) for k, v in res["stage_ms"].items()},
+                          "step_gpu_ms": res["step_gpu_ms"]}), flush=True)
         return
 
     dec, _ = run_workload(1, args.steps, args.warmup)
@@ -230,6 +234,7 @@ def main():
                    "d_ff": 1536, "experts_touched": dec["n_touched"]},
         "roofline": roofline(dec, "gate_up", "hbm"),
         "kernel_ms": {k: round(v, 5) for k, v in dec["stage_ms"].items()},
+        "step_gpu_ms": dec["step_gpu_ms"],
         "layer_tflops": round(dec["layer_tflops"], 3),
     }
     if not args.no_prefill:
@@ -242,6 +247,7 @@ def main():
             "roofline": roofline(pre, "gate_up", "mfma"),
             "roofline_down": roofline(pre, "down", "mfma"),
             "kernel_ms": {k: round(v, 5) for k, v in pre["stage_ms"].items()},
+            "step_gpu_ms": pre["step_gpu_ms"],
         }
     if not args.no_extra:
         for key, cfg, bound in (("skewed", 3, "mfma"), ("fp8", 4, "mfma"), ("fp8_decode", 7, "hbm"),
@@ -256,6 +262,7 @@ def main():
                 "roofline": roofline(res, "gate_up", bound),
                 "roofline_down": roofline(res, "down", bound),
                 "kernel_ms": {k: round(v, 5) for k, v in res["stage_ms"].items()},
+                "step_gpu_ms": res["step_gpu_ms"],
             }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(1)
