@@ -14,8 +14,9 @@
 //                  and gives pair (t, j) of expert e the row
 //                  offsets[e] + base[e, block] + #(tokens of the block before t
 //                  that chose e).
-// All of it is integer work with no atomics whose order matters, so the
-// result is the same on every run.  With the shared expert of the full block
+// A batch of one routing block (T <= 64) does all three in one workgroup
+// (k_dispatch_one).  All of it is integer work with no atomics whose order
+// matters, so the result is the same on every run.  With the shared expert of the full block
 // ("Tencent Hy3-Flash Q&A", Q4.7), it becomes expert E, whose rows are
 // T*k + t, one per token: the GEMMs then treat it like any routed expert.
 
@@ -146,6 +147,65 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
     }
 }
 
+// A single routing block (T <= 64): counts, offsets, tile offsets and the
+// dispatch order in one workgroup of 1024 threads, the same results as
+// k_block_scan + k_offsets + k_scatter with nb = 1 (every block base is 0).
+__global__ __launch_bounds__(1024) void k_dispatch_one(const int32_t* __restrict__ idx, int T, int E,
+                                                      int k, int extra, int bm,
+                                                      int32_t* __restrict__ blk_base,
+                                                      int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ tile_off,
+                                                      int32_t* __restrict__ row_of,
+                                                      int32_t* __restrict__ tok_of, int shared_row0) {
+    __shared__ unsigned long long mask[1024];
+    __shared__ int s_cnt[1024];
+    __shared__ int s_til[1024];
+    __shared__ int s_off[1024];
+    const int tid = threadIdx.x;
+    mask[tid] = 0ull;
+    __syncthreads();
+    const int npairs = T * k;
+    for (int p = tid; p < npairs; p += 1024) atomicOr(&mask[idx[p]], 1ull << (p / k));
+    __syncthreads();
+    const int n = E + (extra > 0 ? 1 : 0);
+    const int c = tid < E ? __popcll(mask[tid]) : (tid < n ? extra : 0);
+    const int nt = (c + bm - 1) / bm;
+    s_cnt[tid] = c;
+    s_til[tid] = nt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int a0 = tid >= off ? s_cnt[tid - off] : 0;
+        const int a1 = tid >= off ? s_til[tid - off] : 0;
+        __syncthreads();
+        s_cnt[tid] += a0;
+        s_til[tid] += a1;
+        __syncthreads();
+    }
+    s_off[tid] = s_cnt[tid] - c;
+    if (tid < E) {
+        counts[tid] = c;
+        blk_base[tid] = 0;
+    }
+    if (tid < n) {
+        offsets[tid] = s_cnt[tid] - c;
+        tile_off[tid] = s_til[tid] - nt;
+    }
+    if (tid == 0) {
+        offsets[n] = s_cnt[1023];
+        tile_off[n] = s_til[1023];
+    }
+    __syncthreads();
+    for (int p = tid; p < npairs; p += 1024) {
+        const int t = p / k;
+        const int e = idx[p];
+        const int row = s_off[e] + __popcll(mask[e] & ((1ull << t) - 1ull));
+        row_of[p] = row;
+        tok_of[row] = t;
+    }
+    if (shared_row0 >= 0 && tid < T) tok_of[shared_row0 + tid] = tid;
+}
+
 // Per-block counts when the routing comes from the caller (hy3moe_permute).
 __global__ __launch_bounds__(256) void k_block_counts(const int32_t* __restrict__ idx, int T,
                                                      int E, int k, int nb,
@@ -175,6 +235,11 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
                            const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,
                            int32_t* offsets, int32_t* tile_off, int bm, int32_t* row_of,
                            int32_t* tok_of, int shared, hipStream_t s) {
+    if (nb == 1) {
+        hipLaunchKernelGGL(k_dispatch_one, dim3(1), dim3(1024), 0, s, idx, T, E, k, shared ? T : 0, bm,
+                           blk_base, counts, offsets, tile_off, row_of, tok_of, shared ? T * k : -1);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_block_scan, dim3(E), dim3(256), 0, s, blk_counts, blk_base, counts, nb);
     hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, s, counts, E, shared ? T : 0, offsets,
                        tile_off, bm);
