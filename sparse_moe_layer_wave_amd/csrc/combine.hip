@@ -22,7 +22,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
     const int t = blockIdx.x;
     __shared__ int s_row[16];
     __shared__ float s_w[16];
-    if (threadIdx.x < k) {
+    if (static_cast<int>(threadIdx.x) < k) {
         s_row[threadIdx.x] = row_of[static_cast<size_t>(t) * k + threadIdx.x];
         s_w[threadIdx.x] = w[static_cast<size_t>(t) * k + threadIdx.x];
     }
