@@ -183,6 +183,29 @@ def test_empty_batch(gpu_lib):
     assert out.shape == (0, 512)
 
 
+def test_empty_batch_every_entry(gpu_lib):
+    """T = 0 is a successful no-op on every entry point: empty outputs, no launch."""
+    from sparse_moe_layer_wave_amd import hy3moe as hy
+    c = dict(inputs.CONFIGS[0], T=0)
+    inp = _to("cuda", _cpu_case(c))
+    idx, w = hy.route(inp["x"], inp["W_gate"], 8, inp["scale"])
+    assert idx.shape == (0, 8) and w.shape == (0, 8)
+    counts, offsets, row_of, token_of = hy.permute(idx, c["E"])
+    assert int(counts.sum()) == 0 and row_of.numel() == 0 and token_of.numel() == 0
+    assert torch.all(offsets == 0)
+    blk = inputs.make_inputs(dict(inputs.CONFIGS[5], T=0, d=512, E=32, F=128), device="cuda")
+    idx, w = hy.route_ex(blk["x"], blk["W_gate"], 8, blk["scale"], norm_weight=blk["norm_w"],
+                         score_bias=blk["score_bias"])
+    assert idx.shape == (0, 8)
+    out = hy.block_forward(blk["x"], blk["W_gate"], blk["W_gu"], blk["W_dn"], blk["Ws_gu"], blk["Ws_dn"], 8,
+                           blk["scale"], norm_weight=blk["norm_w"], score_bias=blk["score_bias"])
+    assert out.shape == (0, 512)
+    f8 = inputs.make_inputs(dict(inputs.CONFIGS[4], T=0, d=512, E=32, F=256), device="cuda")
+    out = hy.forward_fp8(f8["x"], f8["W_gate"], f8["Wq_gu"], f8["s_gu"], f8["Wq_dn"], f8["s_dn"], 8, f8["scale"])
+    assert out.shape == (0, 512)
+    torch.cuda.synchronize()
+
+
 def test_deterministic(gpu_lib):
     from sparse_moe_layer_wave_amd import hy3moe as hy
     inp = _to("cuda", _cpu_case(0, T=777, seed=11))
