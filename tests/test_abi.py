@@ -179,3 +179,40 @@ def test_route_ex_argument_checks(L):
     assert r(nws=64) == hy3moe.ERR_WORKSPACE
     assert r(nw=A, nws=64) == hy3moe.ERR_WORKSPACE
     assert r(T=0, x=NUL, ws=NUL, nws=0) == hy3moe.OK
+
+
+def test_header_compiles_as_c_and_links(tmp_path, L):
+    """A plain C99 caller: include/hy3moe.h compiles as C with warnings as
+    errors, every declared function links against libhy3moe.so, and host-only
+    calls (sizes, argument rejection) work without a GPU."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    names = sorted(hy3moe.EXPORTS)
+    table = ",\n    ".join(f"(fn){n}" for n in names)
+    src = tmp_path / "use_abi.c"
+    src.write_text(f"""#include <stdio.h>
+#include "hy3moe.h"
+typedef void (*fn)(void);
+static fn every_entry[] = {{
+    {table}
+}};
+int main(void) {{
+    size_t bytes = 0;
+    int ok = hy3moe_workspace_size(64, 4096, 192, 8, 1536, HY3MOE_WEIGHTS_BF16, &bytes);
+    int bad = hy3moe_workspace_size(-1, 4096, 192, 8, 1536, HY3MOE_WEIGHTS_BF16, &bytes);
+    printf("%d %d %d %s\\n", (int)(sizeof every_entry / sizeof every_entry[0]), ok, bad,
+           hy3moe_status_string(bad));
+    return (ok == HY3MOE_OK && bad != HY3MOE_OK) ? 0 : 1;
+}}
+""")
+    exe = tmp_path / "use_abi"
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), hy3moe.LIB_PATH, f"-Wl,-rpath,{os.path.dirname(hy3moe.LIB_PATH)}",
+                    "-o", str(exe)], check=True, capture_output=True, text=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0, res.stdout + res.stderr
+    n, ok, bad, msg = res.stdout.split(maxsplit=3)
+    assert int(n) == len(names) and int(ok) == 0 and int(bad) < 0 and msg.strip()
