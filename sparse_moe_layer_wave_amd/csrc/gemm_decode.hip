@@ -203,11 +203,14 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
 
 }  // namespace
 
-// Decode path while the average expert gets at most 4 rows (so nearly every
-// expert fits one 16-row pass); rows of d and d_ff elements of esz bytes must
-// be whole 256-byte batches.
+// Decode path while the average expert gets at most 8 rows (most experts fit
+// one 16-row pass); rows of d and d_ff elements of esz bytes must be whole
+// 256-byte batches.  Measured at d = 4096, E = 192, k = 8, d_ff = 1536: the
+// weight-streaming kernels beat the grouped GEMMs up to T = 192 (T = 128:
+// 1.18 vs 1.34 ms; T = 192: 1.32 vs 1.35 ms) and lose from T = 256 (1.48 vs
+// 1.36 ms).
 bool use_decode_path(int T, int d, int F, int E, int k, int esz) {
-    return static_cast<long long>(T) * k <= 4LL * E && (d * esz) % kBatchB == 0 &&
+    return static_cast<long long>(T) * k <= 8LL * E && (d * esz) % kBatchB == 0 &&
            (F * esz) % kBatchB == 0;
 }
 
