@@ -238,10 +238,11 @@ static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_ep
                                  reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
                                  hy3::prefill_bm(), row_of, tok_of, shared ? 1 : 0, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
-    const bool decode = hy3::use_decode_path(T, d, d_ff, E, k, 2);
+    const bool decode = hy3::use_decode_path(T, d, d_ff, E, k, 2, shared);
     if (e == hipSuccess) {
         if (decode)
-            e = hy3::launch_gate_up_decode(x, tok_of, W_gate_up, Ws_gu, offsets, h, Eg, d, d_ff, s);
+            e = hy3::launch_gate_up_decode(x, tok_of, W_gate_up, Ws_gu, offsets, h, Eg, d, d_ff,
+                                           shared ? T : 0, s);
         else
             e = hy3::launch_gate_up_grouped(x, tok_of, W_gate_up, Ws_gu, offsets, tile_off,
                                             L.max_mtiles, h, Eg, d, d_ff, s);
@@ -249,7 +250,7 @@ static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_ep
     if (e == hipSuccess) e = mark(ev, 3, s);
     if (e == hipSuccess) {
         if (decode)
-            e = hy3::launch_down_decode(h, W_down, Ws_dn, offsets, y, Eg, d, d_ff, s);
+            e = hy3::launch_down_decode(h, W_down, Ws_dn, offsets, y, Eg, d, d_ff, shared ? T : 0, s);
         else
             e = hy3::launch_down_grouped(h, W_down, Ws_dn, offsets, tile_off, L.max_mtiles, y, Eg, d,
                                          d_ff, s);
@@ -292,7 +293,7 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
                                  reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
                                  hy3::prefill_bm(), row_of, tok_of, 0, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
-    const bool decode = hy3::use_decode_path(T, d, d_ff, E, k, 1);
+    const bool decode = hy3::use_decode_path(T, d, d_ff, E, k, 1, false);
     if (e == hipSuccess) e = hy3::launch_quant_rows(x, T, d, xq, xs, s);
     if (e == hipSuccess) e = hy3::launch_fill_u32(amax, Tk, 0u, s);
     if (e == hipSuccess) {

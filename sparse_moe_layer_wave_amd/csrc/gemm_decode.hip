@@ -30,8 +30,8 @@
 //          and the channel's scales first).
 // An expert with more than 16 rows is handled in passes of 16 rows.  The
 // shared expert of the full block, when present, is the last expert (all T
-// tokens, weights W_last); its workgroups are the longest, so they are
-// scheduled first.
+// tokens, weights W_last), cut into 16-row slices that get a column of
+// workgroups each, scheduled first.
 
 #include "internal.h"
 
@@ -59,6 +59,8 @@ struct DecodeArgs {
     float* h32;                         // e4m3 gate_up: h [rows, N] fp32
     uint32_t* amax;                     // e4m3 gate_up: [rows] bits of max |h|
     int K, N;                           // K in elements
+    int E;                              // experts, the shared one included
+    int nsh;                            // workgroup columns of the shared expert (16 rows each)
 };
 
 template <int MODE>
@@ -67,11 +69,21 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
     constexpr bool FP8 = MODE == GU_FP8 || MODE == DN_FP8;
     constexpr int ESZ = FP8 ? 1 : 2;
     __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kSlabB];
-    const int E = gridDim.x;
-    const int e = g.W_last ? (blockIdx.x == 0 ? E - 1 : blockIdx.x - 1) : blockIdx.x;
-    const int rbeg = g.offsets[e];
-    const int rend = g.offsets[e + 1];
-    if (rbeg == rend) return;
+    const int E = g.E;
+    // The shared expert (all T tokens) is cut into 16-row slices, one column of
+    // workgroups each, so its weights stream in parallel rather than in T / 16
+    // serial passes; its columns come first.
+    int e, rbeg, rend;
+    if (g.W_last && static_cast<int>(blockIdx.x) < g.nsh) {
+        e = E - 1;
+        rbeg = g.offsets[E - 1] + 16 * static_cast<int>(blockIdx.x);
+        rend = min(rbeg + 16, g.offsets[E]);
+    } else {
+        e = static_cast<int>(blockIdx.x) - (g.W_last ? g.nsh : 0);
+        rbeg = g.offsets[e];
+        rend = g.offsets[e + 1];
+    }
+    if (rbeg >= rend) return;
     const int K = g.K, N = g.N;
     const size_t rowbytes = static_cast<size_t>(K) * ESZ;
     const int lane = threadIdx.x & 63;
@@ -208,36 +220,51 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
 // 256-byte batches.  Measured at d = 4096, E = 192, k = 8, d_ff = 1536: the
 // weight-streaming kernels beat the grouped GEMMs up to T = 192 (T = 128:
 // 1.18 vs 1.34 ms; T = 192: 1.32 vs 1.35 ms) and lose from T = 256 (1.48 vs
-// 1.36 ms).
-bool use_decode_path(int T, int d, int F, int E, int k, int esz) {
-    return static_cast<long long>(T) * k <= 8LL * E && (d * esz) % kBatchB == 0 &&
+// 1.36 ms).  The full block's shared expert adds its T rows: the block takes
+// the decode path to T = 160 (1.32 vs 1.33 ms) and not at T = 192 (1.41 vs
+// 1.33 ms).
+bool use_decode_path(int T, int d, int F, int E, int k, int esz, bool shared) {
+    const long long rows = static_cast<long long>(T) * k + (shared ? T : 0);
+    return rows <= 8LL * E && (d * esz) % kBatchB == 0 &&
            (F * esz) % kBatchB == 0;
 }
 
+namespace {
+// grid columns: the routed experts plus the shared expert's 16-row slices
+int shared_slices(const void* W_last, int shared_rows) { return W_last ? (shared_rows + 15) / 16 : 0; }
+int grid_columns(const void* W_last, int E, int nsh) { return W_last ? E - 1 + nsh : E; }
+}  // namespace
+
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
                                  const uint16_t* W_last, const int32_t* offsets, uint16_t* h,
-                                 int E, int d, int F, hipStream_t s) {
+                                 int E, int d, int F, int shared_rows, hipStream_t s) {
+    const int nsh = shared_slices(W_last, shared_rows);
     DecodeArgs g{reinterpret_cast<const uint8_t*>(x), tok_of, reinterpret_cast<const uint8_t*>(W_gu),
                  reinterpret_cast<const uint8_t*>(W_last), offsets, h, nullptr, nullptr, nullptr,
-                 nullptr, d, F};
-    hipLaunchKernelGGL(k_decode_gemm<GU_BF16>, dim3(E, F / 64), dim3(256), 0, s, g);
+                 nullptr, d, F, E, nsh};
+    const int cols = grid_columns(W_last, E, nsh);
+    if (cols == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_decode_gemm<GU_BF16>, dim3(cols, F / 64), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
 hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uint16_t* W_last,
                               const int32_t* offsets, uint16_t* y, int E, int d, int F,
-                              hipStream_t s) {
+                              int shared_rows, hipStream_t s) {
+    const int nsh = shared_slices(W_last, shared_rows);
     DecodeArgs g{reinterpret_cast<const uint8_t*>(h), nullptr, reinterpret_cast<const uint8_t*>(W_dn),
                  reinterpret_cast<const uint8_t*>(W_last), offsets, y, nullptr, nullptr, nullptr,
-                 nullptr, F, d};
-    hipLaunchKernelGGL(k_decode_gemm<DN_BF16>, dim3(E, d / 128), dim3(256), 0, s, g);
+                 nullptr, F, d, E, nsh};
+    const int cols = grid_columns(W_last, E, nsh);
+    if (cols == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_decode_gemm<DN_BF16>, dim3(cols, d / 128), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
 hipError_t launch_gate_up_decode_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                                      const uint8_t* Wq, const float* ws, const int32_t* offsets,
                                      float* h32, uint32_t* amax, int E, int d, int F, hipStream_t s) {
-    DecodeArgs g{xq, tok_of, Wq, nullptr, offsets, nullptr, xs, ws, h32, amax, d, F};
+    DecodeArgs g{xq, tok_of, Wq, nullptr, offsets, nullptr, xs, ws, h32, amax, d, F, E, 0};
     hipLaunchKernelGGL(k_decode_gemm<GU_FP8>, dim3(E, F / 64), dim3(256), 0, s, g);
     return hipGetLastError();
 }
@@ -245,7 +272,7 @@ hipError_t launch_gate_up_decode_fp8(const uint8_t* xq, const float* xs, const i
 hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq,
                                   const float* ws, const int32_t* offsets, uint16_t* y, int E,
                                   int d, int F, hipStream_t s) {
-    DecodeArgs g{hq, nullptr, Wq, nullptr, offsets, y, hs, ws, nullptr, nullptr, F, d};
+    DecodeArgs g{hq, nullptr, Wq, nullptr, offsets, y, hs, ws, nullptr, nullptr, F, d, E, 0};
     hipLaunchKernelGGL(k_decode_gemm<DN_FP8>, dim3(E, d / 128), dim3(256), 0, s, g);
     return hipGetLastError();
 }

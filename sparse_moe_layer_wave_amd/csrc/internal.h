@@ -126,13 +126,15 @@ hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const ui
 
 // decode-sized batches: weight streaming, one workgroup per (expert, weight
 // slice); E and W_last as for the grouped GEMMs
-bool use_decode_path(int T, int d, int F, int E, int k, int esz);   // esz: bytes per weight
+bool use_decode_path(int T, int d, int F, int E, int k, int esz, bool shared);   // esz: bytes per weight
+// shared_rows: rows of the shared expert (expert E - 1, weights W_last;
+// ignored without W_last)
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
                                  const uint16_t* W_last, const int32_t* offsets, uint16_t* h,
-                                 int E, int d, int F, hipStream_t s);
+                                 int E, int d, int F, int shared_rows, hipStream_t s);
 hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uint16_t* W_last,
                               const int32_t* offsets, uint16_t* y, int E, int d, int F,
-                              hipStream_t s);
+                              int shared_rows, hipStream_t s);
 
 // shared_row0 >= 0: row shared_row0 + t of y (the shared expert's output for
 // token t) is added with weight 1 after the k routed terms
