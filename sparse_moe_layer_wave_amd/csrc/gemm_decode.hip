@@ -28,10 +28,11 @@
 // down:    wave w of block (e, n0) owns W_down rows n0+32w..+32 and writes
 //          y[r, n] = bf16(h[r] . W_down[e][n]) (e4m3: rescaled by the row's
 //          and the channel's scales first).
-// An expert with more than 16 rows is handled in passes of 16 rows.  The
-// shared expert of the full block, when present, is the last expert (all T
-// tokens, weights W_last), cut into 16-row slices that get a column of
-// workgroups each, scheduled first.
+// Every expert's rows are cut into 16-row slices (their offsets come from the
+// dispatch run with a 16-row block), one column of workgroups per slice, so
+// an expert with many rows streams its weights in parallel columns rather
+// than in serial passes.  The shared expert of the full block, when present,
+// is the last expert (all T tokens, weights W_last).
 
 #include "internal.h"
 
@@ -53,6 +54,7 @@ struct DecodeArgs {
     const uint8_t* W;                   // gate_up: [E, 2N, K]; down: [E, N, K]
     const uint8_t* W_last;              // non-NULL: weights of expert E - 1 (shared)
     const int32_t* offsets;
+    const int32_t* slice_off;           // [E+1] offsets in 16-row slices (one workgroup column each)
     uint16_t* C;                        // bf16 out: gate_up h (bf16 mode) or y [rows, N]
     const float* a_scale;               // e4m3: per token (gate_up) or per row (down)
     const float* w_scale;               // e4m3: [E, 2N] (gate_up) or [E, N] (down)
@@ -60,7 +62,6 @@ struct DecodeArgs {
     uint32_t* amax;                     // e4m3 gate_up: [rows] bits of max |h|
     int K, N;                           // K in elements
     int E;                              // experts, the shared one included
-    int nsh;                            // workgroup columns of the shared expert (16 rows each)
 };
 
 template <int MODE>
@@ -70,19 +71,22 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
     constexpr int ESZ = FP8 ? 1 : 2;
     __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kSlabB];
     const int E = g.E;
-    // The shared expert (all T tokens) is cut into 16-row slices, one column of
-    // workgroups each, so its weights stream in parallel rather than in T / 16
-    // serial passes; its columns come first.
-    int e, rbeg, rend;
-    if (g.W_last && static_cast<int>(blockIdx.x) < g.nsh) {
-        e = E - 1;
-        rbeg = g.offsets[E - 1] + 16 * static_cast<int>(blockIdx.x);
-        rend = min(rbeg + 16, g.offsets[E]);
-    } else {
-        e = static_cast<int>(blockIdx.x) - (g.W_last ? g.nsh : 0);
-        rbeg = g.offsets[e];
-        rend = g.offsets[e + 1];
+    // Every expert's rows are cut into 16-row slices, one column of workgroups
+    // each, so an expert with many rows (a hot expert, or the shared one with
+    // all T tokens) streams its weights in parallel columns rather than in
+    // serial passes.  Column L: the last expert e with slice_off[e] <= L.
+    const int L = static_cast<int>(blockIdx.x);
+    if (L >= __builtin_amdgcn_readfirstlane(g.slice_off[E])) return;
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (__builtin_amdgcn_readfirstlane(g.slice_off[mid]) <= L) lo = mid;
+        else hi = mid - 1;
     }
+    const int e = lo;
+    const int rbeg = __builtin_amdgcn_readfirstlane(g.offsets[e]) +
+                     16 * (L - __builtin_amdgcn_readfirstlane(g.slice_off[e]));
+    const int rend = min(rbeg + 16, __builtin_amdgcn_readfirstlane(g.offsets[e + 1]));
     if (rbeg >= rend) return;
     const int K = g.K, N = g.N;
     const size_t rowbytes = static_cast<size_t>(K) * ESZ;
@@ -215,65 +219,59 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
 
 }  // namespace
 
-// Decode path while the average expert gets at most 8 rows (most experts fit
-// one 16-row pass); rows of d and d_ff elements of esz bytes must be whole
-// 256-byte batches.  Measured at d = 4096, E = 192, k = 8, d_ff = 1536: the
-// weight-streaming kernels beat the grouped GEMMs up to T = 192 (T = 128:
-// 1.18 vs 1.34 ms; T = 192: 1.32 vs 1.35 ms) and lose from T = 256 (1.48 vs
-// 1.36 ms).  The full block's shared expert adds its T rows: the block takes
-// the decode path to T = 160 (1.32 vs 1.33 ms) and not at T = 192 (1.41 vs
-// 1.33 ms).
+// Decode path up to about 11 rows per expert on average; rows of d and d_ff
+// elements of esz bytes must be whole 256-byte batches.  Measured on the whole
+// layer at d = 4096, E = 192, k = 8, d_ff = 1536 (decode vs grouped GEMMs):
+// T = 192 1.26 vs 1.35 ms, T = 256 1.33 vs 1.36 ms, T = 320 1.56 vs 1.36 ms.
+// The full block's shared expert adds T rows, counted twice: each of its
+// 16-row slices streams a whole expert's weights.
 bool use_decode_path(int T, int d, int F, int E, int k, int esz, bool shared) {
-    const long long rows = static_cast<long long>(T) * k + (shared ? T : 0);
-    return rows <= 8LL * E && (d * esz) % kBatchB == 0 &&
+    const long long rows = static_cast<long long>(T) * k + (shared ? 2LL * T : 0);
+    return rows <= 11LL * E && (d * esz) % kBatchB == 0 &&
            (F * esz) % kBatchB == 0;
 }
 
-namespace {
-// grid columns: the routed experts plus the shared expert's 16-row slices
-int shared_slices(const void* W_last, int shared_rows) { return W_last ? (shared_rows + 15) / 16 : 0; }
-int grid_columns(const void* W_last, int E, int nsh) { return W_last ? E - 1 + nsh : E; }
-}  // namespace
+int decode_bm() { return 16; }
 
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
-                                 const uint16_t* W_last, const int32_t* offsets, uint16_t* h,
-                                 int E, int d, int F, int shared_rows, hipStream_t s) {
-    const int nsh = shared_slices(W_last, shared_rows);
+                                 const uint16_t* W_last, const int32_t* offsets,
+                                 const int32_t* slice_off, int max_slices, uint16_t* h, int E, int d,
+                                 int F, hipStream_t s) {
     DecodeArgs g{reinterpret_cast<const uint8_t*>(x), tok_of, reinterpret_cast<const uint8_t*>(W_gu),
-                 reinterpret_cast<const uint8_t*>(W_last), offsets, h, nullptr, nullptr, nullptr,
-                 nullptr, d, F, E, nsh};
-    const int cols = grid_columns(W_last, E, nsh);
-    if (cols == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_decode_gemm<GU_BF16>, dim3(cols, F / 64), dim3(256), 0, s, g);
+                 reinterpret_cast<const uint8_t*>(W_last), offsets, slice_off, h, nullptr, nullptr,
+                 nullptr, nullptr, d, F, E};
+    if (max_slices == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_decode_gemm<GU_BF16>, dim3(max_slices, F / 64), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
 hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uint16_t* W_last,
-                              const int32_t* offsets, uint16_t* y, int E, int d, int F,
-                              int shared_rows, hipStream_t s) {
-    const int nsh = shared_slices(W_last, shared_rows);
+                              const int32_t* offsets, const int32_t* slice_off, int max_slices,
+                              uint16_t* y, int E, int d, int F, hipStream_t s) {
     DecodeArgs g{reinterpret_cast<const uint8_t*>(h), nullptr, reinterpret_cast<const uint8_t*>(W_dn),
-                 reinterpret_cast<const uint8_t*>(W_last), offsets, y, nullptr, nullptr, nullptr,
-                 nullptr, F, d, E, nsh};
-    const int cols = grid_columns(W_last, E, nsh);
-    if (cols == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_decode_gemm<DN_BF16>, dim3(cols, d / 128), dim3(256), 0, s, g);
+                 reinterpret_cast<const uint8_t*>(W_last), offsets, slice_off, y, nullptr, nullptr,
+                 nullptr, nullptr, F, d, E};
+    if (max_slices == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_decode_gemm<DN_BF16>, dim3(max_slices, d / 128), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
 hipError_t launch_gate_up_decode_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                                      const uint8_t* Wq, const float* ws, const int32_t* offsets,
-                                     float* h32, uint32_t* amax, int E, int d, int F, hipStream_t s) {
-    DecodeArgs g{xq, tok_of, Wq, nullptr, offsets, nullptr, xs, ws, h32, amax, d, F, E, 0};
-    hipLaunchKernelGGL(k_decode_gemm<GU_FP8>, dim3(E, F / 64), dim3(256), 0, s, g);
+                                     const int32_t* slice_off, int max_slices, float* h32,
+                                     uint32_t* amax, int E, int d, int F, hipStream_t s) {
+    DecodeArgs g{xq, tok_of, Wq, nullptr, offsets, slice_off, nullptr, xs, ws, h32, amax, d, F, E};
+    if (max_slices == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_decode_gemm<GU_FP8>, dim3(max_slices, F / 64), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
 hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq,
-                                  const float* ws, const int32_t* offsets, uint16_t* y, int E,
-                                  int d, int F, hipStream_t s) {
-    DecodeArgs g{hq, nullptr, Wq, nullptr, offsets, y, hs, ws, nullptr, nullptr, F, d, E, 0};
-    hipLaunchKernelGGL(k_decode_gemm<DN_FP8>, dim3(E, d / 128), dim3(256), 0, s, g);
+                                  const float* ws, const int32_t* offsets, const int32_t* slice_off,
+                                  int max_slices, uint16_t* y, int E, int d, int F, hipStream_t s) {
+    DecodeArgs g{hq, nullptr, Wq, nullptr, offsets, slice_off, y, hs, ws, nullptr, nullptr, F, d, E};
+    if (max_slices == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_decode_gemm<DN_FP8>, dim3(max_slices, d / 128), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 

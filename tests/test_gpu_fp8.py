@@ -63,7 +63,7 @@ def test_fp8_small_full_parity(gpu_lib, T, E, k, F):
                                        (5, 24, 4, 512, 1024), (1, 8, 2, 256, 256),
                                        (12, 32, 8, 384, 512)])
 def test_fp8_decode_path_full_parity(gpu_lib, T, E, k, F, d):
-    """T * k <= 8 E with d, d_ff multiples of 256: the e4m3 weight-streaming
+    """T * k <= 11 E with d, d_ff multiples of 256: the e4m3 weight-streaming
     kernels (the last case, d_ff = 384, takes the grouped kernels instead)."""
     inp = _cpu_fp8_case(T, E, k, F, d=d, seed=42 + T)
     c = inp["cfg"]

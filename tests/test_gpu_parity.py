@@ -164,8 +164,8 @@ def test_all_tokens_one_expert(gpu_lib):
 @pytest.mark.parametrize("T,E,k,hot", [(64, 192, 8, True), (96, 192, 8, False), (16, 32, 8, True),
                                        (3, 40, 5, False)])
 def test_decode_path_shapes(gpu_lib, T, E, k, hot):
-    """Small batches (T*k <= 8E) take the weight-streaming kernels; a hot
-    expert with more than 16 rows exercises their multi-pass loop."""
+    """Small batches (T*k <= 11E) take the weight-streaming kernels; a hot
+    expert with more than 16 rows is cut into several 16-row slices."""
     c = dict(inputs.CONFIGS[0], T=T, E=E, k=k, F=128, seed=200 + T)
     inp = _cpu_case(c)
     if hot:
