@@ -251,7 +251,8 @@ def main():
         }
     if not args.no_extra:
         for key, cfg, bound in (("skewed", 3, "mfma"), ("fp8", 4, "mfma"), ("fp8_decode", 7, "hbm"),
-                                ("block_decode", 5, "hbm"), ("block_prefill", 6, "mfma")):
+                                ("block_decode", 5, "hbm"), ("block_prefill", 6, "mfma"),
+                                ("skewed_decode", 8, "hbm")):
             n = args.steps if bound == "hbm" else max(3, args.steps // 10)
             res, _ = run_workload(cfg, n, min(args.warmup, 2))
             line[key] = {

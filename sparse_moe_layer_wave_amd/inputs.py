@@ -58,6 +58,10 @@ CONFIGS = {
     # e4m3 experts at the decode batch
     7: dict(name="hy3_fp8_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=7,
             weights="fp8", skew=False),
+    # the skewed routing of workload 3 at the decode batch (hot experts get
+    # tens of rows)
+    8: dict(name="hy3_skewed_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=8,
+            weights="bf16", skew=True),
 }
 
 (_STREAM_X, _STREAM_WG, _STREAM_BIAS, _STREAM_WGU, _STREAM_WDN, _STREAM_NORM, _STREAM_SBIAS,

@@ -259,6 +259,14 @@ def test_hy3_decode_T64(gpu_lib):
     print("decode", _hy3_case(1, 20))
 
 
+def test_hy3_skewed_decode_T64(gpu_lib):
+    """Decode batch with the skewed routing: hot experts get tens of rows,
+    each cut into several 16-row slices of the weight-streaming kernels."""
+    stats = _hy3_case(8, 20)
+    print("skewed decode", stats)
+    assert stats["hottest_over_mean"] > 8
+
+
 def test_hy3_prefill_T8192(gpu_lib):
     print("prefill", _hy3_case(2, 12))
 
