@@ -4,11 +4,12 @@
 // of the router's input ("Tencent Hy3-Flash Q&A", Q4.9).
 //
 // Logits.  The gate weight is fp32 and the hidden states are bf16; the pages'
-// router casts both to float before the linear map.  k_router_prep splits each
-// fp32 weight w into three bf16 planes by truncation, w = hi + mid + lo
-// exactly (8 significant bits each), so x.w = x.hi + x.mid + x.lo with every
-// product exact in fp32: an fp32-accurate GEMM on bf16 MFMA (fp32
-// accumulate) for three times the bf16 work.  Small batches split the d-sum
+// router casts both to float before the linear map.  Each fp32 weight w is
+// split into three bf16 planes by truncation, w = hi + mid + lo exactly (8
+// significant bits each), so x.w = x.hi + x.mid + x.lo with every product
+// exact in fp32: an fp32-accurate GEMM on bf16 MFMA (fp32 accumulate) for
+// three times the bf16 work.  Small batches split in registers as they load
+// W; large ones read planes that k_router_prep writes once per call.  Small batches split the d-sum
 // over nsplit workgroups, and a second kernel adds the partial sums in the
 // fixed order s = 0..nsplit-1, so the result does not depend on scheduling.
 // Batches of 4096 tokens or more take k_router_logits_tiled (LDS-staged
@@ -71,13 +72,39 @@ __device__ __forceinline__ float sigmoid_bias(float z, const float* bias, int e)
     return 1.0f / (1.0f + expf(-z));
 }
 
+// Eight fp32 weights -> their hi, mid and lo bf16 planes, two values per
+// 32-bit word (element 2 i in the low half), as k_router_prep writes them.
+__device__ __forceinline__ void split_planes(float4 a, float4 b, i32x4_t* out) {
+    const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t hi[8], mid[8], lo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t uh = __float_as_uint(w[j]) & 0xffff0000u;
+        const float r1 = w[j] - __uint_as_float(uh);         // exact: <= 16 significant bits
+        const uint32_t um = __float_as_uint(r1) & 0xffff0000u;
+        const float r2 = r1 - __uint_as_float(um);           // exact: <= 8 significant bits
+        hi[j] = uh >> 16;
+        mid[j] = um >> 16;
+        lo[j] = __float_as_uint(r2) >> 16;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        out[0][q] = static_cast<int>(hi[2 * q] | (hi[2 * q + 1] << 16));
+        out[1][q] = static_cast<int>(mid[2 * q] | (mid[2 * q + 1] << 16));
+        out[2][q] = static_cast<int>(lo[2 * q] | (lo[2 * q + 1] << 16));
+    }
+}
+
 // Workgroup (tb, eb, s): tokens 256 tb.., experts 32 eb.., d-chunk s; wave w
 // owns tokens 64 w..64 w+63 as two 32-row MFMA blocks.
 // MFMA 32x32x16: A lane l = token l%32, k 8*(l/32)..+8; B lane l = expert
 // l%32, same k; C lane l = expert l%32, tokens 8*(j/4) + 4*(l/32) + j%4.
 // nsplit == 1 writes sigmoid scores; otherwise raw partial logits per chunk.
+// The weight is read as fp32 and split into its three bf16 planes in
+// registers (split_planes, the same arithmetic as k_router_prep), so small
+// batches need no separate plane pass.
 __global__ __launch_bounds__(256) void k_router_logits(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
+    const uint16_t* __restrict__ x, const float* __restrict__ W,
     const float* __restrict__ bias, float* __restrict__ partial, float* __restrict__ scores,
     int T, int d, int E, int kchunk, int nsplit) {
     const int lane = threadIdx.x & 63;
@@ -88,7 +115,6 @@ __global__ __launch_bounds__(256) void k_router_logits(
     const int k0 = blockIdx.z * kchunk;
     const int l32 = lane & 31;
     const int kh = (lane >> 5) * 8;
-    const size_t plane = static_cast<size_t>(E) * d;
 
     const uint16_t* xa[2];
 #pragma unroll
@@ -97,7 +123,7 @@ __global__ __launch_bounds__(256) void k_router_logits(
         xa[mb] = x + static_cast<size_t>(ta) * d + k0 + kh;
     }
     const int eb = min(e0 + l32, E - 1);
-    const uint16_t* wb = planes + static_cast<size_t>(eb) * d + k0 + kh;
+    const float* wb = W + static_cast<size_t>(eb) * d + k0 + kh;
 
     f32x16_t acc[2] = {{}, {}};
     for (int kb = 0; kb < kchunk; kb += 16 * kUnroll) {
@@ -107,9 +133,8 @@ __global__ __launch_bounds__(256) void k_router_logits(
             const int kk = min(kb + 16 * u, kchunk - 16);  // kchunk is a multiple of 32
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) av[u][mb] = *reinterpret_cast<const i32x4_t*>(xa[mb] + kk);
-#pragma unroll
-            for (int p = 0; p < 3; ++p)
-                bv[u][p] = *reinterpret_cast<const i32x4_t*>(wb + p * plane + kk);
+            split_planes(*reinterpret_cast<const float4*>(wb + kk), *reinterpret_cast<const float4*>(wb + kk + 4),
+                         bv[u]);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -434,17 +459,17 @@ hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bi
                          const float* score_bias, int T, int d, int E, int k, float scale,
                          const RouterWork& rw, int32_t* idx, float* w, int32_t* blk_counts, int nb,
                          hipStream_t s) {
-    const size_t n = static_cast<size_t>(E) * d;
-    hipLaunchKernelGGL(k_router_prep, dim3(static_cast<unsigned>((n / 4 + 255) / 256)), dim3(256), 0,
-                       s, W_gate, rw.planes, n);
     if (T >= kTiledMinT) {
+        const size_t n = static_cast<size_t>(E) * d;
+        hipLaunchKernelGGL(k_router_prep, dim3(static_cast<unsigned>((n / 4 + 255) / 256)), dim3(256), 0,
+                           s, W_gate, rw.planes, n);
         dim3 g1((T + kTiledTokens - 1) / kTiledTokens, (E + kTiledExperts - 1) / kTiledExperts, rw.nsplit);
         hipLaunchKernelGGL(k_router_logits_tiled, g1, dim3(256), 0, s, x, rw.planes, bias, rw.partial,
                            rw.scores, T, d, E, d / rw.nsplit, rw.nsplit);
     } else {
         dim3 g1((T + kLogitTokens - 1) / kLogitTokens, (E + kLogitExperts - 1) / kLogitExperts,
                 rw.nsplit);
-        hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, s, x, rw.planes, bias, rw.partial,
+        hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, s, x, W_gate, bias, rw.partial,
                            rw.scores, T, d, E, d / rw.nsplit, rw.nsplit);
     }
     if (rw.nsplit > 1) {
