@@ -11,6 +11,12 @@ full-block (shared expert, route_norm, score bias; hy3moe_block_forward)
 workloads under their own keys.  Per-kernel durations come from HIP events recorded on the launch
 stream between the stages (the *_timed entry points).
 
+Under "prefill" / "at_measured_clock" the MFMA fractions are given once more
+against the dense bf16 peak at the graphics clock amd-smi reports while the
+prefill layer runs back to back (after the timed steps): MI355X lowers its
+clock well below the 2.4 GHz of the published peak under sustained MFMA load.
+"roofline" itself is always against the published peak.
+
 Prints one JSON line.  Only one GPU is used; --gpus N > 1 exits with a message.
 """
 
@@ -18,7 +24,11 @@ import argparse
 import hashlib
 import json
 import os
+import re
+import shutil
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +42,7 @@ from sparse_moe_layer_wave_amd import hy3moe, inputs  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+NOMINAL_SCLK_GHZ = 2.4         # graphics clock the dense peaks are quoted at
 
 
 def _events(n):
@@ -60,7 +71,45 @@ def algorithmic(c, n_touched):
     }
 
 
-def run_workload(cfg, steps, warmup):
+def _smi_gfx_clock_mhz():
+    """Mean of the per-XCD graphics clocks amd-smi reports right now (MHz), or
+    None when amd-smi is missing or prints no clock."""
+    exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if exe is None:
+        return None
+    try:
+        txt = subprocess.run([exe, "metric", "-c"], capture_output=True, text=True, timeout=15).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    mhz = [int(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", txt)]
+    return sum(mhz) / len(mhz) if mhz else None
+
+
+def clock_probe(step, seconds):
+    """Graphics clock (GHz) while `step` runs back to back for about `seconds`
+    (outside every timed region): amd-smi is sampled twice from a helper
+    thread, after a third and two thirds of the time.  None if unavailable."""
+    samples = []
+
+    def sampler():
+        for frac in (1 / 3, 2 / 3):
+            time.sleep(seconds / 3)
+            v = _smi_gfx_clock_mhz()
+            if v is not None:
+                samples.append(v)
+
+    th = threading.Thread(target=sampler)
+    t0 = time.perf_counter()
+    th.start()
+    while th.is_alive() or time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    th.join()
+    return round(sum(samples) / len(samples) / 1e3, 3) if samples else None
+
+
+def run_workload(cfg, steps, warmup, clock_probe_s=0.0):
     inp = inputs.make_inputs(cfg, device="cuda")
     c = inp["cfg"]
     T, d, E, k, F = c["T"], c["d"], c["E"], c["k"], c["F"]
@@ -110,7 +159,8 @@ def run_workload(cfg, steps, warmup):
     res = dict(cfg=c, ms_per_step=elapsed / steps * 1e3, tokens_per_s=T * steps / elapsed, step_gpu_ms=step_gpu_ms,
                stage_ms=stage_ms, n_touched=n_touched, alg=alg,
                layer_tflops=alg["layer_flops"] * steps / elapsed / 1e12,
-               hottest_over_mean=float(load.max() / load.mean()))
+               hottest_over_mean=float(load.max() / load.mean()),
+               sclk_ghz=clock_probe(step, clock_probe_s) if clock_probe_s > 0 else None)
     del inp, ws, out
     torch.cuda.empty_cache()
     return res, idx
@@ -188,6 +238,9 @@ def main():
     ap.add_argument("--profile-workload", metavar="NAME",
                     help="run only the named workload (a profiler pass: one workload per run), "
                          "print its stage times and exit")
+    ap.add_argument("--clock-probe", type=float, default=2.5, metavar="SECONDS",
+                    help="after the timed prefill steps, run them back to back this long while amd-smi "
+                         "samples the graphics clock (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 1 GiB device-to-device copy (outside every timed region), "
                          "a known byte count for scaling HBM traffic counters")
@@ -238,7 +291,7 @@ def main():
         "layer_tflops": round(dec["layer_tflops"], 3),
     }
     if not args.no_prefill:
-        pre, _ = run_workload(2, max(5, args.steps // 5), args.warmup)
+        pre, _ = run_workload(2, max(5, args.steps // 5), args.warmup, clock_probe_s=args.clock_probe)
         line["prefill"] = {
             "workload": pre["cfg"]["name"], "tokens_per_s": round(pre["tokens_per_s"], 1),
             "ms_per_step": round(pre["ms_per_step"], 4),
@@ -249,6 +302,18 @@ def main():
             "kernel_ms": {k: round(v, 5) for k, v in pre["stage_ms"].items()},
             "step_gpu_ms": pre["step_gpu_ms"],
         }
+        # the same fractions against the dense bf16 peak at the graphics clock
+        # the GPU held while running this layer back to back (amd-smi)
+        if pre["sclk_ghz"]:
+            peak = BF16_PEAK_TFLOPS * pre["sclk_ghz"] / NOMINAL_SCLK_GHZ
+            gu = line["prefill"]["roofline"]["achieved"]
+            line["prefill"]["at_measured_clock"] = {
+                "sclk_ghz": pre["sclk_ghz"], "bf16_peak_tflops": round(peak, 1),
+                "gate_up_frac": round(gu / peak, 4),
+                "down_frac": round(line["prefill"]["roofline_down"]["achieved"] / peak, 4),
+                "layer_frac": round(pre["layer_tflops"] / peak, 4)}
+        else:
+            line["prefill"]["at_measured_clock"] = None
     if not args.no_extra:
         for key, cfg, bound in (("skewed", 3, "mfma"), ("fp8", 4, "mfma"), ("fp8_decode", 7, "hbm"),
                                 ("block_decode", 5, "hbm"), ("block_prefill", 6, "mfma"),
