@@ -30,7 +30,10 @@
  *     Calls only enqueue work on it; results are ready once the stream has
  *     reached that point.  Device faults surface at the caller's next sync.
  *   - Arguments are checked on the host before anything is enqueued; a
- *     negative status means nothing was enqueued.  T == 0 is a successful
+ *     negative status other than HY3MOE_ERR_HIP means nothing was enqueued.
+ *     HY3MOE_ERR_HIP means a kernel launch (or a stage event record) failed:
+ *     the launches before it may have been enqueued, and the outputs are
+ *     undefined.  T == 0 is a successful
  *     no-op.  Supported shapes: 1 <= k <= min(E, 16), 1 <= E <= 1024,
  *     d and d_ff multiples of 64, T <= 2^24.
  *     Every pointer must be 16-byte aligned.
