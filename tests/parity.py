@@ -86,23 +86,30 @@ class LazyExperts:
         return self._bits(self._t[int(e)])
 
 
-def check_output_fp8_small(out_gpu, out_ref, valid=None, tol_max=3e-2):
-    """Small-d_ff e4m3 cases.  One SwiGLU activation whose fp32 value falls on
-    the other side of an e4m3 rounding boundary than the oracle's (the two
-    differ in their last bits) moves by one e4m3 step, 1/8 of its size; with
-    only d_ff terms per output, that one step can move an output by several
-    percent of rms.  So here: rms error <= 1e-2 * rms(ref), at most 1e-4 of the
-    elements beyond tol_max * rms(ref), none beyond 5 * tol_max * rms(ref)."""
+def check_output_fp8_small(out_gpu, out_ref, valid, tol_max, n_act):
+    """Small-d_ff e4m3 cases.  Both sides quantise each (token, slot) SwiGLU
+    activation row to e4m3 from float32 values, but the GPU's float32
+    activation comes from another accumulation order and can sit a few float32
+    ulps away from the oracle's.  Where that straddles an e4m3 rounding
+    boundary, one activation takes the neighbouring code (one e4m3 step, 1/8 of
+    its size), and with only d_ff terms per output this moves that token's
+    outputs by up to several percent of rms.  The chance per activation is a
+    few ulps of 2^-23 against e4m3's 2^-3 spacing: below 1e-5.  So, with n_act
+    quantised activations (rows x d_ff): rms error <= 1e-2 * rms(ref); no
+    element beyond 5 * tol_max * rms(ref); and the elements beyond
+    tol_max * rms(ref) confined to at most max(2, 3e-5 * n_act) tokens."""
     out_gpu = np.asarray(out_gpu, dtype=np.float64)
     if valid is None:
         valid = np.ones(out_ref.shape[0], dtype=bool)
     d = np.abs(out_gpu[valid] - out_ref[valid])
     rms = float(np.sqrt(np.mean(out_ref ** 2)))
     rms_err = float(np.sqrt(np.mean(d ** 2)))
-    frac = float(np.mean(d > tol_max * rms))
+    beyond = d > tol_max * rms
+    n_tok = int(np.count_nonzero(beyond.any(axis=1)))
+    allowed = max(2, int(3e-5 * n_act))
     assert np.all(np.isfinite(out_gpu))
     assert rms_err <= 1e-2 * rms, f"rms error {rms_err:.3e} > 1e-2 * rms {rms:.3e}"
-    assert frac <= 1e-4, f"{frac:.2e} of elements beyond {tol_max} * rms"
+    assert n_tok <= allowed, f"{n_tok} tokens with elements beyond {tol_max} * rms (allowed {allowed})"
     assert d.max() <= 5 * tol_max * rms, f"max|d| {d.max():.3e} > {5 * tol_max} * rms"
     return dict(max_abs=float(d.max()), rms_ref=rms, ratio=float(d.max()) / rms,
-                rms_err_ratio=rms_err / rms, frac_beyond=frac)
+                rms_err_ratio=rms_err / rms, tokens_beyond=n_tok, frac_beyond=float(np.mean(beyond)))
