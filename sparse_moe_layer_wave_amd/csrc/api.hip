@@ -235,18 +235,19 @@ static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_ep
     // decode-sized batches: tile_off holds 16-row slice offsets for the
     // weight-streaming kernels, else 128-row block offsets for the grouped GEMMs
     const bool decode = hy3::use_decode_path(T, d, d_ff, E, k, 2, shared);
-    const int max_slices = (L.rows + hy3::decode_bm() - 1) / hy3::decode_bm() + Eg;
+    const int rg = hy3::decode_row_groups(T, k, E, shared);
+    const int max_slices = (L.rows + hy3::decode_bm(rg) - 1) / hy3::decode_bm(rg) + Eg;
     if (e == hipSuccess)
         e = hy3::launch_dispatch(idx, T, E, k, L.nb, blk_counts,
                                  reinterpret_cast<int32_t*>(ws + L.blk_base),
                                  reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
-                                 decode ? hy3::decode_bm() : hy3::prefill_bm(), row_of, tok_of,
+                                 decode ? hy3::decode_bm(rg) : hy3::prefill_bm(), row_of, tok_of,
                                  shared ? 1 : 0, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_gate_up_decode(x, tok_of, W_gate_up, Ws_gu, offsets, tile_off, max_slices,
-                                           h, Eg, d, d_ff, s);
+                                           h, Eg, d, d_ff, rg, s);
         else
             e = hy3::launch_gate_up_grouped(x, tok_of, W_gate_up, Ws_gu, offsets, tile_off,
                                             L.max_mtiles, h, Eg, d, d_ff, s);
@@ -255,7 +256,7 @@ static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_ep
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_down_decode(h, W_down, Ws_dn, offsets, tile_off, max_slices, y, Eg, d,
-                                        d_ff, s);
+                                        d_ff, rg, s);
         else
             e = hy3::launch_down_grouped(h, W_down, Ws_dn, offsets, tile_off, L.max_mtiles, y, Eg, d,
                                          d_ff, s);
@@ -293,19 +294,20 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
                                idx, w, reinterpret_cast<int32_t*>(ws + L.blk_counts), L.nb, s);
     if (e == hipSuccess) e = mark(ev, 1, s);
     const bool decode = hy3::use_decode_path(T, d, d_ff, E, k, 1, false);
-    const int max_slices = (L.rows + hy3::decode_bm() - 1) / hy3::decode_bm() + E;
+    const int rg = hy3::decode_row_groups(T, k, E, false);
+    const int max_slices = (L.rows + hy3::decode_bm(rg) - 1) / hy3::decode_bm(rg) + E;
     if (e == hipSuccess)
         e = hy3::launch_dispatch(idx, T, E, k, L.nb, reinterpret_cast<int32_t*>(ws + L.blk_counts),
                                  reinterpret_cast<int32_t*>(ws + L.blk_base),
                                  reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
-                                 decode ? hy3::decode_bm() : hy3::prefill_bm(), row_of, tok_of, 0, s);
+                                 decode ? hy3::decode_bm(rg) : hy3::prefill_bm(), row_of, tok_of, 0, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
     if (e == hipSuccess) e = hy3::launch_quant_rows(x, T, d, xq, xs, s);
     if (e == hipSuccess) e = hy3::launch_fill_u32(amax, Tk, 0u, s);
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_gate_up_decode_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, max_slices,
-                                               h32, amax, E, d, d_ff, s);
+                                               h32, amax, E, d, d_ff, rg, s);
         else
             e = hy3::launch_gate_up_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, L.max_mtiles,
                                         h32, amax, E, d, d_ff, s);
@@ -315,7 +317,7 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_down_decode_fp8(hq, hs, Wq_dn, s_dn, offsets, tile_off, max_slices, y, E, d,
-                                            d_ff, s);
+                                            d_ff, rg, s);
         else
             e = hy3::launch_down_fp8(hq, hs, Wq_dn, s_dn, offsets, tile_off, L.max_mtiles, y, E, d,
                                      d_ff, s);

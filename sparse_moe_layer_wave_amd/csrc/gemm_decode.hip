@@ -75,7 +75,7 @@ struct DecodeArgs {
     int E;                              // experts, the shared one included
 };
 
-template <int MODE, int SUBS>
+template <int MODE, int SUBS, int RG>
 __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
     constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8;
     constexpr bool FP8 = MODE == GU_FP8 || MODE == DN_FP8;
@@ -96,8 +96,8 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
     }
     const int e = lo;
     const int rbeg = __builtin_amdgcn_readfirstlane(g.offsets[e]) +
-                     16 * (L - __builtin_amdgcn_readfirstlane(g.slice_off[e]));
-    const int rend = min(rbeg + 16, __builtin_amdgcn_readfirstlane(g.offsets[e + 1]));
+                     16 * RG * (L - __builtin_amdgcn_readfirstlane(g.slice_off[e]));
+    const int rend = min(rbeg + 16 * RG, __builtin_amdgcn_readfirstlane(g.offsets[e + 1]));
     if (rbeg >= rend) return;
     const int K = g.K, N = g.N;
     const size_t rowbytes = static_cast<size_t>(K) * ESZ;
@@ -141,16 +141,26 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
     }
 
     const int nb = static_cast<int>(rowbytes / kBatchB);
-    for (int p0 = rbeg; p0 < rend; p0 += 16) {
-        const int prow = p0 + r16;                    // A row this lane loads
-        const bool va = prow < rend;
-        const size_t arow = GATE_UP ? static_cast<size_t>(va ? g.tok_of[prow] : 0)
-                                    : static_cast<size_t>(va ? prow : 0);
-        // this lane's A bytes within a batch start at kq * (FP8 ? 32 : 16)
-        const uint8_t* a = g.A + arow * rowbytes + kq * (FP8 ? 32 : 16);
+    for (int p0 = rbeg; p0 < rend; p0 += 16 * RG) {
+        // row group q of the pass: rows p0 + 16 q .. + 16; this lane loads A row p0 + 16 q + r16
+        bool va[RG];
+        const uint8_t* a[RG];
+#pragma unroll
+        for (int q = 0; q < RG; ++q) {
+            const int prow = p0 + 16 * q + r16;
+            va[q] = prow < rend;
+            const size_t arow = GATE_UP ? static_cast<size_t>(va[q] ? g.tok_of[prow] : 0)
+                                        : static_cast<size_t>(va[q] ? prow : 0);
+            // this lane's A bytes within a batch start at kq * (FP8 ? 32 : 16)
+            a[q] = g.A + arow * rowbytes + kq * (FP8 ? 32 : 16);
+        }
 
-        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
-        f32x4_t acc1 = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t acc0[RG], acc1[RG];
+#pragma unroll
+        for (int q = 0; q < RG; ++q) {
+            acc0[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            acc1[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
         i32x4_t cur[8], nxt[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) cur[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(wsrc[i]));
@@ -168,140 +178,177 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
             for (int i = 0; i < 8; ++i) *reinterpret_cast<i32x4_t*>(slab + wdst[i]) = cur[i];
             if constexpr (FP8) {
                 // 2 k-steps of 128: lane's 32 bytes = chunks 8 s + 2 kq, +1
-                i32x4_t av[2][2];
+                i32x4_t av[RG][2][2];
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
+                for (int q = 0; q < RG; ++q)
 #pragma unroll
-                    for (int q = 0; q < 2; ++q)
-                        av[s][q] = va ? *reinterpret_cast<const i32x4_t*>(a + kb + 128 * s + 16 * q)
-                                      : i32x4_t{0, 0, 0, 0};
+                    for (int s = 0; s < 2; ++s)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            av[q][s][h] = va[q] ? *reinterpret_cast<const i32x4_t*>(a[q] + kb + 128 * s + 16 * h)
+                                                : i32x4_t{0, 0, 0, 0};
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const int ch = 8 * s + 2 * kq;
-                    const i32x8_t fa = __builtin_shufflevector(av[s][0], av[s][1], 0, 1, 2, 3, 4, 5, 6, 7);
                     const i32x4_t b00 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(r16, ch));
                     const i32x4_t b01 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(r16, ch + 1));
                     const i32x4_t b10 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(16 + r16, ch));
                     const i32x4_t b11 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(16 + r16, ch + 1));
                     const i32x8_t f0 = __builtin_shufflevector(b00, b01, 0, 1, 2, 3, 4, 5, 6, 7);
                     const i32x8_t f1 = __builtin_shufflevector(b10, b11, 0, 1, 2, 3, 4, 5, 6, 7);
-                    acc0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, f0, acc0, 0, 0, 0, 127, 0, 127);
-                    acc1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, f1, acc1, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                    for (int q = 0; q < RG; ++q) {
+                        const i32x8_t fa = __builtin_shufflevector(av[q][s][0], av[q][s][1], 0, 1, 2, 3, 4, 5, 6, 7);
+                        acc0[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, f0, acc0[q], 0, 0, 0, 127, 0, 127);
+                        acc1[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, f1, acc1[q], 0, 0, 0, 127, 0, 127);
+                    }
                 }
             } else {
                 // 4 k-steps of 32: lane's 16 bytes = chunk 4 s + kq
-                i32x4_t av[4];
+                i32x4_t av[RG][4];
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    av[s] = va ? *reinterpret_cast<const i32x4_t*>(a + kb + 64 * s) : i32x4_t{0, 0, 0, 0};
+                for (int q = 0; q < RG; ++q)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        av[q][s] = va[q] ? *reinterpret_cast<const i32x4_t*>(a[q] + kb + 64 * s) : i32x4_t{0, 0, 0, 0};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const i32x4_t f0 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(r16, 4 * s + kq));
                     const i32x4_t f1 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(16 + r16, 4 * s + kq));
-                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[s]),
-                                                                    __builtin_bit_cast(bf16x8_t, f0), acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[s]),
-                                                                    __builtin_bit_cast(bf16x8_t, f1), acc1, 0, 0, 0);
+#pragma unroll
+                    for (int q = 0; q < RG; ++q) {
+                        acc0[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[q][s]),
+                                                                          __builtin_bit_cast(bf16x8_t, f0), acc0[q], 0, 0, 0);
+                        acc1[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[q][s]),
+                                                                          __builtin_bit_cast(bf16x8_t, f1), acc1[q], 0, 0, 0);
+                    }
                 }
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
             if (b != nb - 1) continue;
-            // end of block sb: C lane l: column l%16, rows 4*(l/16)+i
+            // end of block sb: C lane l: column l%16, rows 4*(l/16)+i of each row group
             const int col0 = colb + sb * SUBROWS;
             float w0 = ws0[0], w1 = ws1[0];
 #pragma unroll
             for (int q = 1; q < SUBS; ++q) if (sb == q) { w0 = ws0[q]; w1 = ws1[q]; }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = p0 + kq * 4 + i;
-                const bool vr = row < rend;
-                const size_t crow = static_cast<size_t>(vr ? row : rbeg);
-                if constexpr (MODE == GU_BF16) {
-                    if (vr) g.C[crow * N + col0 + r16] = f32_to_bf16(silu_mul(acc0[i], acc1[i]));
-                } else if constexpr (MODE == DN_BF16) {
-                    if (vr) {
-                        g.C[crow * N + col0 + r16] = f32_to_bf16(acc0[i]);
-                        g.C[crow * N + col0 + 16 + r16] = f32_to_bf16(acc1[i]);
-                    }
-                } else if constexpr (MODE == GU_FP8) {
-                    const float sx = g.a_scale[g.tok_of[crow]];
-                    const float hv = silu_mul(acc0[i] * sx * w0, acc1[i] * sx * w1);
-                    if (vr) g.h32[crow * N + col0 + r16] = hv;
-                    // row max over the 16 lanes that share this row
-                    float m = fabsf(hv);
+            for (int q = 0; q < RG; ++q) {
 #pragma unroll
-                    for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
-                    if (vr && r16 == 0) atomicMax(&g.amax[crow], __float_as_uint(m));
-                } else {
-                    const float sh = g.a_scale[crow];
-                    if (vr) {
-                        g.C[crow * N + col0 + r16] = f32_to_bf16(acc0[i] * sh * w0);
-                        g.C[crow * N + col0 + 16 + r16] = f32_to_bf16(acc1[i] * sh * w1);
+                for (int i = 0; i < 4; ++i) {
+                    const int row = p0 + 16 * q + kq * 4 + i;
+                    const bool vr = row < rend;
+                    const size_t crow = static_cast<size_t>(vr ? row : rbeg);
+                    if constexpr (MODE == GU_BF16) {
+                        if (vr) g.C[crow * N + col0 + r16] = f32_to_bf16(silu_mul(acc0[q][i], acc1[q][i]));
+                    } else if constexpr (MODE == DN_BF16) {
+                        if (vr) {
+                            g.C[crow * N + col0 + r16] = f32_to_bf16(acc0[q][i]);
+                            g.C[crow * N + col0 + 16 + r16] = f32_to_bf16(acc1[q][i]);
+                        }
+                    } else if constexpr (MODE == GU_FP8) {
+                        const float sx = g.a_scale[g.tok_of[crow]];
+                        const float hv = silu_mul(acc0[q][i] * sx * w0, acc1[q][i] * sx * w1);
+                        if (vr) g.h32[crow * N + col0 + r16] = hv;
+                        // row max over the 16 lanes that share this row
+                        float m = fabsf(hv);
+#pragma unroll
+                        for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+                        if (vr && r16 == 0) atomicMax(&g.amax[crow], __float_as_uint(m));
+                    } else {
+                        const float sh = g.a_scale[crow];
+                        if (vr) {
+                            g.C[crow * N + col0 + r16] = f32_to_bf16(acc0[q][i] * sh * w0);
+                            g.C[crow * N + col0 + 16 + r16] = f32_to_bf16(acc1[q][i] * sh * w1);
+                        }
                     }
                 }
             }
-            acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < RG; ++q) {
+                acc0[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                acc1[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
         }
     }
 }
 
 }  // namespace
 
-// Decode path up to about 11 rows per expert on average; rows of d and d_ff
-// elements of esz bytes must be whole 256-byte batches.  Measured on the whole
-// layer at d = 4096, E = 192, k = 8, d_ff = 1536 (decode vs grouped GEMMs):
-// T = 192 1.26 vs 1.35 ms, T = 256 1.33 vs 1.36 ms, T = 320 1.56 vs 1.36 ms.
-// The full block's shared expert adds T rows, counted twice: each of its
-// 16-row slices streams a whole expert's weights.
-bool use_decode_path(int T, int d, int F, int E, int k, int esz, bool shared) {
-    const long long rows = static_cast<long long>(T) * k + (shared ? 2LL * T : 0);
-    return rows <= 11LL * E && (d * esz) % kBatchB == 0 &&
-           (F * esz) % kBatchB == 0;
+// Rows per pass: a workgroup takes up to 16 rows (one MFMA row group) or 32
+// (two groups sharing every weight batch).  Two groups stream an expert with
+// 17-32 rows once instead of twice, but hold 26 more registers (3 waves per
+// SIMD instead of 4), so they are used where experts get 8 or more rows on
+// average.  At fewer (T = 64, 192 experts: 2.7 rows each) one group is 1%
+// faster; the full block's shared expert (all T rows) gained nothing from two.
+int decode_row_groups(int T, int k, int E, bool shared) {
+    (void)shared;
+    return static_cast<long long>(T) * k >= 8LL * E ? 2 : 1;
 }
 
-int decode_bm() { return 16; }
+// Decode path up to about 11 rows per expert on average with one row group
+// and 20 with two; rows of d and d_ff elements of esz bytes must be whole
+// 256-byte batches.  Measured on the whole layer at d = 4096, E = 192, k = 8,
+// d_ff = 1536 (grouped GEMMs vs this path): T = 128 1.17 vs 1.17 ms (one
+// group); with two groups T = 192 1.26 vs 1.19, T = 256 1.32 vs 1.24,
+// T = 320 1.38 vs 1.26, T = 384 1.37 vs 1.31, T = 448 1.38 vs 1.34,
+// T = 512 1.39 vs 1.51 ms.  The full block's shared expert adds T rows,
+// counted twice: each of its slices streams a whole expert's weights.
+bool use_decode_path(int T, int d, int F, int E, int k, int esz, bool shared) {
+    const long long rows = static_cast<long long>(T) * k + (shared ? 2LL * T : 0);
+    const int rg = decode_row_groups(T, k, E, shared);
+    return rows <= (rg == 2 ? 20LL : 11LL) * E && (d * esz) % kBatchB == 0 && (F * esz) % kBatchB == 0;
+}
+
+int decode_bm(int rg) { return 16 * rg; }
 
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
                                  const uint16_t* W_last, const int32_t* offsets,
                                  const int32_t* slice_off, int max_slices, uint16_t* h, int E, int d,
-                                 int F, hipStream_t s) {
+                                 int F, int rg, hipStream_t s) {
     DecodeArgs g{reinterpret_cast<const uint8_t*>(x), tok_of, reinterpret_cast<const uint8_t*>(W_gu),
                  reinterpret_cast<const uint8_t*>(W_last), offsets, slice_off, h, nullptr, nullptr,
                  nullptr, nullptr, d, F, E};
     if (max_slices == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_decode_gemm<GU_BF16, kSubsBf16>), dim3(max_slices, F / (64 * kSubsBf16)), dim3(256), 0, s, g);
+    const dim3 grid(max_slices, F / (64 * kSubsBf16));
+    if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<GU_BF16, kSubsBf16, 2>), grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((k_decode_gemm<GU_BF16, kSubsBf16, 1>), grid, dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
 hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uint16_t* W_last,
                               const int32_t* offsets, const int32_t* slice_off, int max_slices,
-                              uint16_t* y, int E, int d, int F, hipStream_t s) {
+                              uint16_t* y, int E, int d, int F, int rg, hipStream_t s) {
     DecodeArgs g{reinterpret_cast<const uint8_t*>(h), nullptr, reinterpret_cast<const uint8_t*>(W_dn),
                  reinterpret_cast<const uint8_t*>(W_last), offsets, slice_off, y, nullptr, nullptr,
                  nullptr, nullptr, F, d, E};
     if (max_slices == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_decode_gemm<DN_BF16, kSubsBf16>), dim3(max_slices, d / (128 * kSubsBf16)), dim3(256), 0, s, g);
+    const dim3 grid(max_slices, d / (128 * kSubsBf16));
+    if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<DN_BF16, kSubsBf16, 2>), grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((k_decode_gemm<DN_BF16, kSubsBf16, 1>), grid, dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
 hipError_t launch_gate_up_decode_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                                      const uint8_t* Wq, const float* ws, const int32_t* offsets,
                                      const int32_t* slice_off, int max_slices, float* h32,
-                                     uint32_t* amax, int E, int d, int F, hipStream_t s) {
+                                     uint32_t* amax, int E, int d, int F, int rg, hipStream_t s) {
     DecodeArgs g{xq, tok_of, Wq, nullptr, offsets, slice_off, nullptr, xs, ws, h32, amax, d, F, E};
     if (max_slices == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_decode_gemm<GU_FP8, kSubsFp8>), dim3(max_slices, F / (64 * kSubsFp8)), dim3(256), 0, s, g);
+    const dim3 grid(max_slices, F / (64 * kSubsFp8));
+    if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<GU_FP8, kSubsFp8, 2>), grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((k_decode_gemm<GU_FP8, kSubsFp8, 1>), grid, dim3(256), 0, s, g);
     return hipGetLastError();
 }
 
 hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq,
                                   const float* ws, const int32_t* offsets, const int32_t* slice_off,
-                                  int max_slices, uint16_t* y, int E, int d, int F, hipStream_t s) {
+                                  int max_slices, uint16_t* y, int E, int d, int F, int rg, hipStream_t s) {
     DecodeArgs g{hq, nullptr, Wq, nullptr, offsets, slice_off, y, hs, ws, nullptr, nullptr, F, d, E};
     if (max_slices == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_decode_gemm<DN_FP8, kSubsFp8>), dim3(max_slices, d / (128 * kSubsFp8)), dim3(256), 0, s, g);
+    const dim3 grid(max_slices, d / (128 * kSubsFp8));
+    if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<DN_FP8, kSubsFp8, 2>), grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((k_decode_gemm<DN_FP8, kSubsFp8, 1>), grid, dim3(256), 0, s, g);
     return hipGetLastError();
 }
 

@@ -127,17 +127,19 @@ hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const ui
 // decode-sized batches: weight streaming, one workgroup per (expert, weight
 // slice); E and W_last as for the grouped GEMMs
 bool use_decode_path(int T, int d, int F, int E, int k, int esz, bool shared);   // esz: bytes per weight
-// Decode-sized batches.  slice_off: [E+1] offsets of the experts' 16-row
-// slices (the dispatch's block offsets with decode_bm() rows per block);
+// Decode-sized batches.  rg: 16-row groups a workgroup takes per pass (1 or
+// 2, from decode_row_groups); slice_off: [E+1] offsets of the experts' slices
+// of decode_bm(rg) rows (the dispatch's block offsets with that block size);
 // max_slices: an upper bound on slice_off[E], the grid's column count.
-int decode_bm();
+int decode_row_groups(int T, int k, int E, bool shared);
+int decode_bm(int rg);
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
                                  const uint16_t* W_last, const int32_t* offsets,
                                  const int32_t* slice_off, int max_slices, uint16_t* h, int E, int d,
-                                 int F, hipStream_t s);
+                                 int F, int rg, hipStream_t s);
 hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uint16_t* W_last,
                               const int32_t* offsets, const int32_t* slice_off, int max_slices,
-                              uint16_t* y, int E, int d, int F, hipStream_t s);
+                              uint16_t* y, int E, int d, int F, int rg, hipStream_t s);
 
 // shared_row0 >= 0: row shared_row0 + t of y (the shared expert's output for
 // token t) is added with weight 1 after the k routed terms
@@ -182,9 +184,9 @@ hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq
 hipError_t launch_gate_up_decode_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                                      const uint8_t* Wq, const float* ws, const int32_t* offsets,
                                      const int32_t* slice_off, int max_slices, float* h32,
-                                     uint32_t* amax, int E, int d, int F, hipStream_t s);
+                                     uint32_t* amax, int E, int d, int F, int rg, hipStream_t s);
 hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq,
                                   const float* ws, const int32_t* offsets, const int32_t* slice_off,
-                                  int max_slices, uint16_t* y, int E, int d, int F, hipStream_t s);
+                                  int max_slices, uint16_t* y, int E, int d, int F, int rg, hipStream_t s);
 
 }  // namespace hy3

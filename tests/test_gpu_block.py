@@ -141,8 +141,9 @@ def test_block_ragged_and_small_shapes(gpu_lib, T, k, E, F, norm, sbias):
 
 @pytest.mark.parametrize("T", [16, 64])
 def test_block_decode_path_shapes(gpu_lib, T):
-    """T * k + 2 T <= 11 E with d, d_ff multiples of 128: the weight-streaming kernels,
-    the shared expert as their last expert with all T rows."""
+    """T * k + 2 T <= 11 E (20 E with two row groups) with d, d_ff multiples
+    of 128: the weight-streaming kernels, the shared expert as their last
+    expert with all T rows."""
     print(T, _compare_full(_case(T, 1024, 192, 8, 256, seed=80 + T)))
 
 

@@ -61,10 +61,11 @@ def test_fp8_small_full_parity(gpu_lib, T, E, k, F):
 
 @pytest.mark.parametrize("T,E,k,F,d", [(16, 64, 8, 256, 512), (64, 192, 8, 256, 256),
                                        (5, 24, 4, 512, 1024), (1, 8, 2, 256, 256),
-                                       (12, 32, 8, 384, 512)])
+                                       (12, 32, 8, 384, 512), (56, 24, 8, 256, 512)])
 def test_fp8_decode_path_full_parity(gpu_lib, T, E, k, F, d):
-    """T * k <= 11 E with d, d_ff multiples of 256: the e4m3 weight-streaming
-    kernels (the last case, d_ff = 384, takes the grouped kernels instead)."""
+    """T * k <= 11 E (20 E with two row groups) with d, d_ff multiples of 256: the e4m3 weight-streaming
+    kernels (the fifth case, d_ff = 384, takes the grouped kernels instead;
+    the last, 19 rows per expert, two 16-row groups per pass)."""
     inp = _cpu_fp8_case(T, E, k, F, d=d, seed=42 + T)
     c = inp["cfg"]
     out, idx, w = _run_fp8(inp)

@@ -162,10 +162,14 @@ def test_all_tokens_one_expert(gpu_lib):
 
 
 @pytest.mark.parametrize("T,E,k,hot", [(64, 192, 8, True), (96, 192, 8, False), (16, 32, 8, True),
-                                       (3, 40, 5, False)])
+                                       (3, 40, 5, False), (56, 24, 8, False), (56, 24, 8, True),
+                                       (40, 16, 4, False)])
 def test_decode_path_shapes(gpu_lib, T, E, k, hot):
-    """Small batches (T*k <= 11E) take the weight-streaming kernels; a hot
-    expert with more than 16 rows is cut into several 16-row slices."""
+    """Small batches take the weight-streaming kernels: T*k <= 11E with one
+    16-row group per pass, and, where experts average 8 or more rows
+    (T*k >= 8E), T*k <= 20E with two groups (32-row slices; the last three
+    cases, the second with a 56-row hot expert cut into two slices).  A hot
+    expert with more rows than a slice is cut into several slices."""
     c = dict(inputs.CONFIGS[0], T=T, E=E, k=k, F=128, seed=200 + T)
     inp = _cpu_case(c)
     if hot:

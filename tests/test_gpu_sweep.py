@@ -3,9 +3,10 @@ e4m3 layer and the full block, every token compared with the oracle.
 
 The shapes are drawn once from a fixed generator, so every run tests the same
 cases.  About half of each kind is drawn to take the weight-streaming decode
-kernels (T * k <= 11 E, d and d_ff whole 256-byte batches) and the rest the
-grouped GEMMs, with expert counts, k, d and d_ff in the ranges the library
-takes (d and d_ff multiples of 64, of 128 with e4m3 experts; k <= min(E, 16)).
+kernels (T * k <= 11 E, or 20 E where T * k >= 8 E, d and d_ff whole 256-byte
+batches) and the rest the grouped GEMMs, with expert counts, k, d and d_ff in
+the ranges the library takes (d and d_ff multiples of 64, of 128 with e4m3
+experts; k <= min(E, 16)).
 Criteria as in the other parity tests: routing bit-exact except flagged
 near-ties; outputs within
 1e-2 * rms(ref) with bf16 experts, and the small-d_ff e4m3 criterion with e4m3
