@@ -2,7 +2,7 @@
 
     python -m sparse_moe_layer_wave_amd.profile_summary --trace T.csv \
         [--fetch F.csv --write W.csv] --command "..." --out profiles/NAME.md \
-        [--traffic-json profiles/counters_gate_up_hy3_decode_T64.json --kernel "k_decode_gemm<0, 1>" \
+        [--traffic-json profiles/counters_gate_up_hy3_decode_T64.json --kernel "k_decode_gemm<0, 1, 1>" \
          [--grid-x 49152 --grid-y 24] --source gemm_decode.hip]
 
 --trace is rocprofv3's kernel_trace.csv (--kernel-trace --output-format csv);
