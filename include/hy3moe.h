@@ -33,10 +33,9 @@
  *     negative status other than HY3MOE_ERR_HIP means nothing was enqueued.
  *     HY3MOE_ERR_HIP means a kernel launch (or a stage event record) failed:
  *     the launches before it may have been enqueued, and the outputs are
- *     undefined.  T == 0 is a successful
- *     no-op.  Supported shapes: 1 <= k <= min(E, 16), 1 <= E <= 1024,
- *     d and d_ff multiples of 64, T <= 2^24.
- *     Every pointer must be 16-byte aligned.
+ *     undefined.  T == 0 is a successful no-op.  Supported shapes:
+ *     1 <= k <= min(E, 16), 1 <= E <= 1024, d and d_ff multiples of 64,
+ *     T <= 2^24.  Every pointer must be 16-byte aligned.
  *   - The workspace is scratch device memory of at least the size that
  *     hy3moe_workspace_size reports; its contents on entry do not matter and
  *     are undefined on return.  Calls that share a workspace must not overlap.
