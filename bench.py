@@ -226,6 +226,28 @@ def cpu_baseline(cfg, max_seconds=25.0):
                       f"{chunk} (NumPy float64, OpenBLAS), {el:.1f} s"}
 
 
+def shares(steps, warmup):
+    """The expert GEMMs at one GPU's share of a sharded layer (Hy3 dims, bf16).
+    8-way expert parallelism gives each GPU 24 experts and, after the
+    dispatch exchange, T*k/8 of the (token, slot) rows of a T-token batch: a
+    24-expert layer with k = 8 over T/8 tokens has the same expert GEMMs
+    (its router and combine are not the sharded ones).  d_ff parallelism gives
+    each GPU all experts with d_ff/8 (192) or d_ff/4 (384) columns."""
+    base = dict(inputs.CONFIGS[1])
+    cases = [("ep8_prefill_T8192", dict(base, T=1024, E=24, seed=11), "mfma"),
+             ("ep8_decode_T64x8", dict(base, T=64, E=24, seed=12), "hbm"),
+             ("tp8_decode_T64", dict(base, T=64, F=192, seed=13), "hbm"),
+             ("tp4_decode_T64", dict(base, T=64, F=384, seed=14), "hbm")]
+    out = {"shares": "expert GEMMs at one GPU's share (8 GPUs expert-parallel, or d_ff split 8 / 4 ways)"}
+    for name, c, bound in cases:
+        c["name"] = name
+        res, _ = run_workload(c, steps, warmup)
+        out[name] = {"T": c["T"], "E": c["E"], "d_ff": c["F"], "experts_touched": res["n_touched"],
+                     "gemm_ms": round(res["stage_ms"]["gate_up"] + res["stage_ms"]["down"], 4),
+                     "roofline": roofline(res, "gate_up", bound), "roofline_down": roofline(res, "down", bound)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +263,9 @@ def main():
     ap.add_argument("--clock-probe", type=float, default=2.5, metavar="SECONDS",
                     help="after the timed prefill steps, run them back to back this long while amd-smi "
                          "samples the graphics clock (0: skip)")
+    ap.add_argument("--shares", action="store_true",
+                    help="print one JSON line with the expert GEMMs at one GPU's share of an 8-way expert-parallel "
+                         "or 8- / 4-way d_ff-parallel layer, and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 1 GiB device-to-device copy (outside every timed region), "
                          "a known byte count for scaling HBM traffic counters")
@@ -257,6 +282,10 @@ def main():
         torch.cuda.synchronize()
         del a, b
         torch.cuda.empty_cache()
+
+    if args.shares:
+        print(json.dumps(shares(args.steps, args.warmup)), flush=True)
+        return
 
     if args.profile_workload:
         names = {c["name"]: i for i, c in inputs.CONFIGS.items()}
