@@ -204,6 +204,27 @@ int hy3moe_block_forward(const uint16_t* x, const uint16_t* norm_weight, float n
                          int32_t* topk_idx, float* topk_w,
                          void* workspace, size_t workspace_bytes);
 
+/* The decoder layer's residual branch ended in the block: hy3moe_block_forward
+ * with a bf16 output and the residual added in the fp32 combine (the wmrh.cn
+ * Hy3 assembly blog: the residual add of section 3.2, in fp32 as section 2.3
+ * describes, rounded back to bf16):
+ *   out[t] = bf16( (sum_j w_j * y_j + shared_t) + residual[t] )
+ * with the sum in fp32 as for hy3moe_block_forward, the residual widened to
+ * fp32 and added last, and one round to nearest even.
+ *   residual  bf16 [T, d] in, or NULL for no residual (out is then the block
+ *             output rounded to bf16)
+ *   out       bf16 [T, d] out, overwritten; it may be the residual buffer
+ *             itself (in-place update) and must not overlap any other argument
+ * Other arguments, errors and workspace as for hy3moe_block_forward. */
+int hy3moe_block_forward_bf16(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,
+                              const float* W_gate, const float* score_bias,
+                              const uint16_t* W_gate_up, const uint16_t* W_down,
+                              const uint16_t* Ws_gate_up, const uint16_t* Ws_down,
+                              const uint16_t* residual, uint16_t* out,
+                              int T, int d, int E, int k, int d_ff, float scale, void* stream,
+                              int32_t* topk_idx, float* topk_w,
+                              void* workspace, size_t workspace_bytes);
+
 /* hy3moe_block_forward with the six stage events of hy3moe_forward_timed
  * (route_norm falls in the router stage). */
 int hy3moe_block_forward_timed(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,

@@ -22,6 +22,9 @@ quantises to OCP e4m3):
   copy of x (route_norm, Q4.9) and choosing with the selection-only
   e_score_correction_bias (Q4.3; "Tencent Hy3-295B architecture teardown",
   section 4.1, router flow step 2);
+* residual branch (``forward_block_residual``): the bf16 residual row added to
+  the block output in a wider type -- wmrh.cn Hy3 assembly blog, sections 3.2
+  (residual add) and 2.3 (fp32 combine);
 * combine: per-expert loop adding weight * expert output into the token's row
   -- "DeepSeek V4-Flash architecture Q&A", Q8.4 (the MoE forward sketch and
   the index_add_ note), done in float64 so the fp32-combine requirement
@@ -43,13 +46,14 @@ from .codecs import (bf16_bits_to_f64, f32_to_bf16_bits, round_to_bf16, e4m3_bit
                      f32_to_e4m3_bits, E4M3_MAX)
 from .moe import (route, expert_swiglu, forward, forward_tokens, quant_row_e4m3,
                   quant_rows_e4m3, forward_fp8, forward_fp8_tokens, rms_norm_bf16,
-                  forward_block, forward_block_tokens, expert_param_count, flops_per_token,
+                  forward_block, forward_block_tokens, forward_block_residual,
+                  expert_param_count, flops_per_token,
                   NEAR_TIE)
 
 __all__ = [
     "bf16_bits_to_f64", "f32_to_bf16_bits", "round_to_bf16", "e4m3_bits_to_f64", "f32_to_e4m3_bits",
     "E4M3_MAX", "route", "expert_swiglu", "forward", "forward_tokens",
     "quant_row_e4m3", "quant_rows_e4m3", "forward_fp8", "forward_fp8_tokens",
-    "rms_norm_bf16", "forward_block", "forward_block_tokens",
+    "rms_norm_bf16", "forward_block", "forward_block_tokens", "forward_block_residual",
     "expert_param_count", "flops_per_token", "NEAR_TIE",
 ]

@@ -214,6 +214,21 @@ def forward_block_tokens(tokens, x_bits, *args, **kwargs):
     return forward_block(np.asarray(x_bits)[tokens], *args, **kwargs)
 
 
+def forward_block_residual(x_bits, *args, residual_bits=None, **kwargs):
+    """The decoder layer's residual branch ended in the block: the block output
+    of ``forward_block`` plus the bf16 residual row (wmrh.cn Hy3 assembly blog,
+    section 3.2, the residual add; section 2.3, the branches added in a wider
+    type than bf16), in float64 and not rounded.  The library rounds this sum
+    once to bf16; the tolerance of the comparison covers that rounding.
+
+    residual_bits uint16 [T, d] or None (then the block output alone).
+    Returns (out float64 [T, d], Route)."""
+    out, r = forward_block(x_bits, *args, **kwargs)
+    if residual_bits is not None:
+        out = out + bf16_bits_to_f64(np.asarray(residual_bits, dtype=np.uint16))
+    return out, r
+
+
 # ----------------------------------------------------------------------------- FP8
 
 def quant_row_e4m3(v):

@@ -185,23 +185,27 @@ namespace {
 
 // The bf16 layer, and the full block when any of its extras is given:
 // norm_w (route_norm), score_bias (selection-only bias), Ws_gu/Ws_dn (the
-// shared expert, both or neither).
+// shared expert, both or neither).  With out_bf16 instead of out, the
+// output is bf16 with the residual (if any) added in the combine.
 static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_eps,
                         const float* W_gate, const float* logit_bias, const float* score_bias,
                         const uint16_t* W_gate_up, const uint16_t* W_down, const uint16_t* Ws_gu,
                         const uint16_t* Ws_dn, float* out, int T, int d, int E, int k, int d_ff,
                         float scale, void* stream, int32_t* topk_idx, float* topk_w,
-                        void* workspace, size_t workspace_bytes, void* const* ev) {
+                        void* workspace, size_t workspace_bytes, void* const* ev,
+                        const uint16_t* resid = nullptr, uint16_t* out_bf16 = nullptr) {
     const bool shared = Ws_gu != nullptr;
     int st = check_shape(T, d, E, k, d_ff);
     if (st != HY3MOE_OK) return st;
     if (shared && E > 1023) return HY3MOE_ERR_UNSUPPORTED;
     if (!(norm_eps >= 0.f)) return HY3MOE_ERR_SHAPE;
     if (T == 0) return HY3MOE_OK;
-    if (!x || !W_gate || !W_gate_up || !W_down || !out || !workspace) return HY3MOE_ERR_NULL;
+    if (!x || !W_gate || !W_gate_up || !W_down || !(out || out_bf16) || !workspace)
+        return HY3MOE_ERR_NULL;
     if ((Ws_gu == nullptr) != (Ws_dn == nullptr)) return HY3MOE_ERR_NULL;
     if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_gate_up) || !aligned16(W_down) ||
-        !aligned16(out) || !aligned16(workspace) || (logit_bias && !aligned16(logit_bias)) ||
+        !aligned16(out ? static_cast<const void*>(out) : out_bf16) || !aligned16(workspace) ||
+        (resid && !aligned16(resid)) || (logit_bias && !aligned16(logit_bias)) ||
         (score_bias && !aligned16(score_bias)) || (norm_w && !aligned16(norm_w)) ||
         (Ws_gu && !aligned16(Ws_gu)) || (Ws_dn && !aligned16(Ws_dn)) ||
         (topk_idx && !aligned16(topk_idx)) || (topk_w && !aligned16(topk_w)))
@@ -262,7 +266,12 @@ static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_ep
                                          d_ff, s);
     }
     if (e == hipSuccess) e = mark(ev, 4, s);
-    if (e == hipSuccess) e = hy3::launch_combine(y, row_of, w, out, T, d, k, shared ? T * k : -1, s);
+    if (e == hipSuccess) {
+        if (out_bf16)
+            e = hy3::launch_combine_bf16(y, row_of, w, resid, out_bf16, T, d, k, shared ? T * k : -1, s);
+        else
+            e = hy3::launch_combine(y, row_of, w, out, T, d, k, shared ? T * k : -1, s);
+    }
     if (e == hipSuccess) e = mark(ev, 5, s);
     return hip_status(e);
 }
@@ -368,6 +377,18 @@ int hy3moe_block_forward(const uint16_t* x, const uint16_t* norm_weight, float n
     return forward_bf16(x, norm_weight, norm_eps, W_gate, nullptr, score_bias, W_gate_up, W_down,
                         Ws_gate_up, Ws_down, out, T, d, E, k, d_ff, scale, stream, topk_idx, topk_w,
                         workspace, workspace_bytes, nullptr);
+}
+
+int hy3moe_block_forward_bf16(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,
+                              const float* W_gate, const float* score_bias,
+                              const uint16_t* W_gate_up, const uint16_t* W_down,
+                              const uint16_t* Ws_gate_up, const uint16_t* Ws_down,
+                              const uint16_t* residual, uint16_t* out, int T, int d, int E, int k,
+                              int d_ff, float scale, void* stream, int32_t* topk_idx, float* topk_w,
+                              void* workspace, size_t workspace_bytes) {
+    return forward_bf16(x, norm_weight, norm_eps, W_gate, nullptr, score_bias, W_gate_up, W_down,
+                        Ws_gate_up, Ws_down, nullptr, T, d, E, k, d_ff, scale, stream, topk_idx,
+                        topk_w, workspace, workspace_bytes, nullptr, residual, out);
 }
 
 int hy3moe_block_forward_timed(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,

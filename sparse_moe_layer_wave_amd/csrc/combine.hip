@@ -6,6 +6,12 @@
 // expert ("Tencent Hy3-Flash Q&A", Q4.7) its output row for the token is
 // added last, with weight 1.  Memory-bound: k (+1) bf16 rows in, one fp32 row
 // out per token.
+//
+// The bf16-output form also ends the decoder layer's residual branch (the
+// same blog: the residual add of section 3.2, done as section 2.3 describes
+// the fp32 combine): the sum above, then the bf16 residual row widened to
+// fp32 and added, and one rounding (nearest even) back to bf16.  The residual is read and the output written by the
+// same thread, element for element, so the output may overwrite the residual.
 
 #include "internal.h"
 
@@ -14,10 +20,11 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <bool BF16_OUT>
 __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict__ y,
                                                      const int32_t* __restrict__ row_of,
                                                      const float* __restrict__ w,
-                                                     float* __restrict__ out, int d, int k,
+                                                     const uint16_t* resid, void* out, int d, int k,
                                                      int shared_row0) {
     const int t = blockIdx.x;
     __shared__ int s_row[16];
@@ -48,9 +55,28 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
                 acc[2 * i + 1] += __uint_as_float(p[i] & 0xffff0000u);
             }
         }
-        float4* o = reinterpret_cast<float4*>(out + static_cast<size_t>(t) * d + c);
-        o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        if constexpr (BF16_OUT) {
+            const size_t at = static_cast<size_t>(t) * d + c;
+            if (resid) {
+                const uint4 v = *reinterpret_cast<const uint4*>(resid + at);
+                const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] += __uint_as_float(p[i] << 16);
+                    acc[2 * i + 1] += __uint_as_float(p[i] & 0xffff0000u);
+                }
+            }
+            uint32_t q[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                q[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) |
+                       (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + at) = make_uint4(q[0], q[1], q[2], q[3]);
+        } else {
+            float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + static_cast<size_t>(t) * d + c);
+            o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        }
     }
 }
 
@@ -58,8 +84,16 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of, const float* w, float* out,
                           int T, int d, int k, int shared_row0, hipStream_t s) {
-    hipLaunchKernelGGL(k_combine, dim3(T), dim3(kThreads), 0, s, y, row_of, w, out, d, k,
-                       shared_row0);
+    hipLaunchKernelGGL(k_combine<false>, dim3(T), dim3(kThreads), 0, s, y, row_of, w, nullptr,
+                       static_cast<void*>(out), d, k, shared_row0);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_bf16(const uint16_t* y, const int32_t* row_of, const float* w,
+                               const uint16_t* resid, uint16_t* out, int T, int d, int k,
+                               int shared_row0, hipStream_t s) {
+    hipLaunchKernelGGL(k_combine<true>, dim3(T), dim3(kThreads), 0, s, y, row_of, w, resid,
+                       static_cast<void*>(out), d, k, shared_row0);
     return hipGetLastError();
 }
 

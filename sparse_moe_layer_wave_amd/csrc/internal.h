@@ -145,6 +145,11 @@ hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uin
 // token t) is added with weight 1 after the k routed terms
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of, const float* w, float* out,
                           int T, int d, int k, int shared_row0, hipStream_t s);
+// the same sum plus the bf16 residual row (if resid is not null), rounded to
+// bf16 into out (which may be resid itself)
+hipError_t launch_combine_bf16(const uint16_t* y, const int32_t* row_of, const float* w,
+                               const uint16_t* resid, uint16_t* out, int T, int d, int k,
+                               int shared_row0, hipStream_t s);
 
 // fp8 path
 __device__ __forceinline__ uint8_t f32_to_e4m3(float v) {

@@ -22,7 +22,7 @@ EXPORTS = (
     "hy3moe_workspace_size", "hy3moe_route", "hy3moe_permute", "hy3moe_forward",
     "hy3moe_forward_timed", "hy3moe_forward_fp8", "hy3moe_forward_fp8_timed",
     "hy3moe_block_workspace_size", "hy3moe_route_ex", "hy3moe_block_forward",
-    "hy3moe_block_forward_timed", "hy3moe_quantize_rows_e4m3", "hy3moe_status_string",
+    "hy3moe_block_forward_timed", "hy3moe_block_forward_bf16", "hy3moe_quantize_rows_e4m3", "hy3moe_status_string",
     "hy3moe_last_hip_error",
 )
 
@@ -60,6 +60,8 @@ def lib():
     L.hy3moe_block_forward.argtypes = [P, P, F, P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, Z]
     L.hy3moe_block_forward_timed.argtypes = [P, P, F, P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P,
                                              P, Z, P]
+    L.hy3moe_block_forward_bf16.argtypes = [P, P, F, P, P, P, P, P, P, P, P, I, I, I, I, I, F, S, P,
+                                            P, P, Z]
     L.hy3moe_quantize_rows_e4m3.argtypes = [P, I, I, P, P, S]
     L.hy3moe_status_string.argtypes = [I]
     L.hy3moe_status_string.restype = ctypes.c_char_p
@@ -298,6 +300,46 @@ def block_forward(x, W_gate, W_gate_up, W_down, Ws_gate_up, Ws_down, k, scale, n
     else:
         _check(lib().hy3moe_block_forward_timed(*args, _event_array(stage_events)),
                "hy3moe_block_forward_timed")
+    return (out, idx, w) if return_routing else out
+
+
+def block_forward_bf16(x, W_gate, W_gate_up, W_down, Ws_gate_up, Ws_down, k, scale, residual=None,
+                       norm_weight=None, norm_eps=1e-6, score_bias=None, out=None, workspace=None,
+                       return_routing=False):
+    """hy3moe_block_forward_bf16: the block's output plus the bf16 residual
+    (if given), summed in fp32 and rounded once to bf16.  Returns out bf16
+    [T,d] (and (idx, w) if return_routing); out may be the residual tensor."""
+    T, d = x.shape
+    E = W_gate.shape[0]
+    F = W_down.shape[2]
+    _need(x, torch.bfloat16, (T, d), "x")
+    _need(W_gate, torch.float32, (E, d), "W_gate")
+    _need(W_gate_up, torch.bfloat16, (E, 2 * F, d), "W_gate_up")
+    _need(W_down, torch.bfloat16, (E, d, F), "W_down")
+    if Ws_gate_up is not None or Ws_down is not None:
+        _need(Ws_gate_up, torch.bfloat16, (2 * F, d), "Ws_gate_up")
+        _need(Ws_down, torch.bfloat16, (d, F), "Ws_down")
+    if norm_weight is not None:
+        _need(norm_weight, torch.bfloat16, (d,), "norm_weight")
+    if score_bias is not None:
+        _need(score_bias, torch.float32, (E,), "score_bias")
+    if residual is not None:
+        _need(residual, torch.bfloat16, (T, d), "residual")
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, (T, d), "out")
+    idx = w = None
+    if return_routing:
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if workspace is None and T:
+        workspace = torch.empty(max(block_workspace_size(T, d, E, k, F), 1), dtype=torch.uint8,
+                                device=x.device)
+    _check(lib().hy3moe_block_forward_bf16(
+        _ptr(x), _ptr(norm_weight), float(norm_eps), _ptr(W_gate), _ptr(score_bias), _ptr(W_gate_up),
+        _ptr(W_down), _ptr(Ws_gate_up), _ptr(Ws_down), _ptr(residual), _ptr(out), T, d, E, k, F,
+        float(scale), _stream(), _ptr(idx), _ptr(w), _ptr(workspace),
+        0 if workspace is None else workspace.numel()), "hy3moe_block_forward_bf16")
     return (out, idx, w) if return_routing else out
 
 

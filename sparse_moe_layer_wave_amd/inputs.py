@@ -20,6 +20,8 @@ Full-block workloads add:
                               a scale of score gaps, so it changes choices)
   Ws_gu       bf16  [2F, d]   N(0, 0.02)       shared expert
   Ws_dn       bf16  [d, F]    N(0, 0.02)
+  residual    bf16  [T, d]    N(0, 1)          residual stream of the bf16-output
+                              block (make_residual; drawn only when asked for)
 
 Values depend on the device the generator runs on (torch's CPU and GPU
 generators differ): tests draw small cases on the CPU and copy them over, and
@@ -65,7 +67,7 @@ CONFIGS = {
 }
 
 (_STREAM_X, _STREAM_WG, _STREAM_BIAS, _STREAM_WGU, _STREAM_WDN, _STREAM_NORM, _STREAM_SBIAS,
- _STREAM_SGU, _STREAM_SDN) = range(9)
+ _STREAM_SGU, _STREAM_SDN, _STREAM_RESID) = range(10)
 
 
 def _gen(device, seed, stream):
@@ -76,6 +78,12 @@ def _gen(device, seed, stream):
 
 def make_x(T, d, seed, device="cpu"):
     g = _gen(device, seed, _STREAM_X)
+    return torch.randn((T, d), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+def make_residual(T, d, seed, device="cpu"):
+    """The decoder layer's residual stream for the bf16-output block."""
+    g = _gen(device, seed, _STREAM_RESID)
     return torch.randn((T, d), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
 
 

@@ -168,6 +168,21 @@ def test_block_forward_argument_checks(L):
                 nws=0) == hy3moe.OK
 
 
+def test_block_forward_bf16_argument_checks(L):
+    def b(T=16, d=512, E=32, k=8, F=128, res=A, out=A, x=A, sgu=A, ws=A, nws=1 << 40):
+        return L.hy3moe_block_forward_bf16(x, A, 1e-6, A, NUL, A, A, sgu, A, res, out, T, d, E, k, F,
+                                           2.826, NUL, NUL, NUL, ws, nws)
+    assert b(T=-1) == hy3moe.ERR_SHAPE
+    assert b(out=NUL) == hy3moe.ERR_NULL
+    assert b(x=NUL) == hy3moe.ERR_NULL
+    assert b(sgu=NUL) == hy3moe.ERR_NULL
+    assert b(out=MIS) == hy3moe.ERR_ALIGN
+    assert b(res=MIS) == hy3moe.ERR_ALIGN
+    st, need = _bws(L, 16, 512, 32, 8, 128)
+    assert b(nws=need - 1) == hy3moe.ERR_WORKSPACE
+    assert b(T=0, res=NUL, out=NUL, x=NUL, sgu=NUL, ws=NUL, nws=0) == hy3moe.OK
+
+
 def test_route_ex_argument_checks(L):
     def r(T=16, d=512, E=32, k=8, x=A, nw=NUL, eps=1e-6, sb=NUL, ws=A, nws=1 << 40):
         return L.hy3moe_route_ex(x, nw, eps, A, NUL, sb, T, d, E, k, 2.826, A, A, ws, nws, NUL)

@@ -196,3 +196,52 @@ def test_hy3_block_decode_T64(gpu_lib):
 
 def test_hy3_block_prefill_T8192(gpu_lib):
     print("block prefill", _hy3_block_case(6, 10))
+
+
+# ----------------------------------------------------------------------------- bf16 output + residual
+
+@pytest.mark.parametrize("T,d,E,k,F", [(64, 512, 32, 8, 256), (300, 512, 32, 8, 128)],
+                         ids=["decode-path", "grouped-path"])
+def test_block_bf16_output_with_residual(gpu_lib, T, d, E, k, F):
+    """hy3moe_block_forward_bf16 against the oracle's residual branch, and bit
+    for bit against the fp32 block output plus the residual rounded once to
+    bf16 (the fused combine does the same fp32 additions), also in place
+    (out = residual) and with no residual."""
+    from sparse_moe_layer_wave_amd import hy3moe as hy
+    inp = _case(T, d, E, k, F, seed=900 + T)
+    res_cpu = inputs.make_residual(T, d, 900 + T)
+    g = _gpu(inp)
+    res = res_cpu.cuda()
+    kw = dict(norm_weight=g["norm_w"], norm_eps=EPS, score_bias=g["score_bias"])
+    args = (g["x"], g["W_gate"], g["W_gu"], g["W_dn"], g["Ws_gu"], g["Ws_dn"], k, inp["scale"])
+    out, idx, w = hy.block_forward_bf16(*args, residual=res, return_routing=True, **kw)
+    out32 = hy.block_forward(*args, **kw)
+    plain = hy.block_forward_bf16(*args, **kw)
+    inplace = res.clone()
+    hy.block_forward_bf16(*args, residual=inplace, out=inplace, **kw)
+    torch.cuda.synchronize()
+    expect = (out32.cpu() + res_cpu.float()).to(torch.bfloat16)
+    assert torch.equal(out.cpu().view(torch.int16), expect.view(torch.int16))
+    assert torch.equal(inplace.cpu().view(torch.int16), expect.view(torch.int16))
+    assert torch.equal(plain.cpu().view(torch.int16), out32.cpu().to(torch.bfloat16).view(torch.int16))
+
+    x_bits = inputs.bits(inp["x"])
+    ref, r = oracle.forward_block_residual(
+        x_bits, inputs.bits(inp["W_gate"]), inputs.bits(inp["W_gu"]), inputs.bits(inp["W_dn"]),
+        inputs.bits(inp["Ws_gu"]), inputs.bits(inp["Ws_dn"]), k, inp["scale"],
+        norm_w_bits=inputs.bits(inp["norm_w"]), eps=EPS, score_bias=inputs.bits(inp["score_bias"]),
+        residual_bits=inputs.bits(res_cpu))
+    idx_np = idx.cpu().numpy()
+    stats = check_routing(idx_np, w.cpu().numpy(), r, inp["scale"])
+    set_eq = np.array([set(a) == set(b) for a, b in zip(idx_np.tolist(), r.idx.tolist())], dtype=bool)
+    # the output is rounded once to bf16: at most half an ulp, which is at
+    # most 2^-8 of the rounded value; that much is allowed on top of the
+    # layer's 1e-2 * rms(ref)
+    gpu = out.cpu().float().numpy().astype(np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    excess = np.abs(gpu - ref) - 2.0 ** -8 * np.abs(gpu)
+    assert np.all(np.isfinite(gpu))
+    worst = float(np.max(excess[set_eq])) if set_eq.any() else 0.0
+    assert worst <= TOL_BF16 * rms, f"{worst:.3e} > {TOL_BF16} * rms {rms:.3e}"
+    stats.update(excess_over_rounding=worst, rms_ref=rms)
+    print(T, d, E, k, F, stats)

@@ -237,3 +237,29 @@ def test_block_tokens_are_independent():
     sub = [0, 7, 29]
     part, _ = oracle.forward_block_tokens(sub, x, Wg, Wgu, Wdn, Wsgu, Wsdn, 4, SCALE, **kw)
     assert np.array_equal(part, out[sub])
+
+
+# ----------------------------------------------------------------------------- residual branch
+
+def test_residual_branch_with_zero_experts_is_the_residual():
+    rng = np.random.default_rng(63)
+    x, Wg, Wgu, Wdn, Wsgu, Wsdn = _layer(rng, 20, 128, 16, 64)
+    res = _bits(rng.standard_normal((20, 128)))
+    out, _ = oracle.forward_block_residual(x, Wg, Wgu, np.zeros_like(Wdn), Wsgu, np.zeros_like(Wsdn), 4,
+                                           SCALE, residual_bits=res)
+    assert np.array_equal(out, codecs.bf16_bits_to_f64(res))
+
+
+def test_residual_branch_adds_the_residual_to_the_block():
+    rng = np.random.default_rng(64)
+    x, Wg, Wgu, Wdn, Wsgu, Wsdn = _layer(rng, 20, 128, 16, 64)
+    res = _bits(rng.standard_normal((20, 128)))
+    kw = dict(norm_w_bits=_bits(np.ones(128)), eps=1e-6)
+    blk, r0 = oracle.forward_block(x, Wg, Wgu, Wdn, Wsgu, Wsdn, 4, SCALE, **kw)
+    none, r1 = oracle.forward_block_residual(x, Wg, Wgu, Wdn, Wsgu, Wsdn, 4, SCALE, **kw)
+    out, r2 = oracle.forward_block_residual(x, Wg, Wgu, Wdn, Wsgu, Wsdn, 4, SCALE, residual_bits=res, **kw)
+    assert np.array_equal(none, blk) and np.array_equal(r2.idx, r0.idx)
+    # the residual is x itself here: out = x + block(x), element by element
+    same, _ = oracle.forward_block_residual(x, Wg, Wgu, Wdn, Wsgu, Wsdn, 4, SCALE, residual_bits=x, **kw)
+    assert np.array_equal(same, codecs.bf16_bits_to_f64(x) + blk)
+    assert np.allclose(out - blk, codecs.bf16_bits_to_f64(res), rtol=0, atol=1e-14)
