@@ -59,7 +59,7 @@ def algorithmic(c, n_touched):
     block = c.get("block", False)
     rows = T * k + (T if block else 0)              # the shared expert sees every token
     n_touched = n_touched + (1 if block else 0)
-    wb = 1 if c.get("weights") == "fp8" else 2
+    wb = 1 if c.get("weights") in ("fp8", "fp8_block128") else 2     # weight scales not counted
     return {
         "gate_up": dict(bytes=n_touched * 2 * F * d * wb + T * d * 2 + rows * F * 2,
                         flops=2 * rows * d * 2 * F),
@@ -113,7 +113,8 @@ def run_workload(cfg, steps, warmup, clock_probe_s=0.0):
     inp = inputs.make_inputs(cfg, device="cuda")
     c = inp["cfg"]
     T, d, E, k, F = c["T"], c["d"], c["E"], c["k"], c["F"]
-    fp8 = c.get("weights") == "fp8"
+    fp8 = c.get("weights") in ("fp8", "fp8_block128")
+    block128 = c.get("weights") == "fp8_block128"
     block = c.get("block", False)
     if block:
         ws = torch.empty(hy3moe.block_workspace_size(T, d, E, k, F), dtype=torch.uint8, device="cuda")
@@ -132,7 +133,8 @@ def run_workload(cfg, steps, warmup, clock_probe_s=0.0):
         if fp8:
             return hy3moe.forward_fp8(inp["x"], inp["W_gate"], inp["Wq_gu"], inp["s_gu"], inp["Wq_dn"],
                                       inp["s_dn"], k, inp["scale"], bias=inp["bias"], out=out,
-                                      workspace=ws, stage_events=evs, return_routing=return_routing)
+                                      workspace=ws, stage_events=evs, return_routing=return_routing,
+                                      block128=block128)
         return hy3moe.forward(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], k, inp["scale"],
                               bias=inp["bias"], out=out, workspace=ws, stage_events=evs,
                               return_routing=return_routing)
@@ -174,7 +176,7 @@ def roofline(res, kernel, bound):
         peak, unit = HBM_PEAK_GBS, "GB/s"
     else:
         achieved = a["flops"] / (ms * 1e-3) / 1e12
-        fp8 = res["cfg"].get("weights") == "fp8"
+        fp8 = res["cfg"].get("weights") in ("fp8", "fp8_block128")
         peak, unit = (FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS), "TFLOP/s"
     return {"bound": bound, "kernel": kernel, "achieved": round(achieved, 2), "peak": peak,
             "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic(kernel, res),
@@ -346,7 +348,8 @@ def main():
     if not args.no_extra:
         for key, cfg, bound in (("skewed", 3, "mfma"), ("fp8", 4, "mfma"), ("fp8_decode", 7, "hbm"),
                                 ("block_decode", 5, "hbm"), ("block_prefill", 6, "mfma"),
-                                ("skewed_decode", 8, "hbm")):
+                                ("skewed_decode", 8, "hbm"), ("fp8_block128_decode", 9, "hbm"),
+                                ("fp8_block128", 10, "mfma")):
             n = args.steps if bound == "hbm" else max(3, args.steps // 10)
             res, _ = run_workload(cfg, n, min(args.warmup, 2))
             line[key] = {

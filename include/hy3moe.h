@@ -153,6 +153,38 @@ int hy3moe_forward_fp8_timed(const uint16_t* x, const float* W_gate,
                              const float* logit_bias, int32_t* topk_idx, float* topk_w,
                              void* workspace, size_t workspace_bytes, void* const* stage_events);
 
+/* The whole layer with e4m3 experts quantised in 128 x 128 blocks, one fp32
+ * scale per block ("DeepSeek V4-Flash architecture Q&A", Q7.2: block-wise
+ * quantisation of the weight matrices):
+ *   Wq_gate_up e4m3 [E, 2*d_ff, d], sb_gate_up fp32 [E, 2*d_ff/128, d/128]
+ *   Wq_down    e4m3 [E, d, d_ff],   sb_down    fp32 [E, d/128, d_ff/128]
+ * weight [e, n, i] = e4m3 value * sb[e, n/128, i/128] (row-major scale grids).
+ * Activations are quantised per row as in hy3moe_forward_fp8.  Each 128-wide
+ * k-block's fp8 MFMA product is scaled by its block's scale and added to the
+ * fp32 accumulator, which is rescaled by the row scale at the end
+ * (decode-sized batches on the weight-streaming kernels, larger ones on
+ * grouped kernels with 128 x 128 tiles, one weight block per tile and
+ * k-block).  d and d_ff must be
+ * multiples of 256 and at most 16384 (HY3MOE_ERR_UNSUPPORTED otherwise); the
+ * workspace is hy3moe_workspace_size with HY3MOE_WEIGHTS_FP8_E4M3.  Other
+ * arguments as for hy3moe_forward_fp8. */
+int hy3moe_forward_fp8_block128(const uint16_t* x, const float* W_gate,
+                                const uint8_t* Wq_gate_up, const float* sb_gate_up,
+                                const uint8_t* Wq_down, const float* sb_down, float* out,
+                                int T, int d, int E, int k, int d_ff, float scale, void* stream,
+                                const float* logit_bias, int32_t* topk_idx, float* topk_w,
+                                void* workspace, size_t workspace_bytes);
+
+/* hy3moe_forward_fp8_block128 with the six stage events of
+ * hy3moe_forward_fp8_timed. */
+int hy3moe_forward_fp8_block128_timed(const uint16_t* x, const float* W_gate,
+                                      const uint8_t* Wq_gate_up, const float* sb_gate_up,
+                                      const uint8_t* Wq_down, const float* sb_down, float* out,
+                                      int T, int d, int E, int k, int d_ff, float scale,
+                                      void* stream, const float* logit_bias, int32_t* topk_idx,
+                                      float* topk_w, void* workspace, size_t workspace_bytes,
+                                      void* const* stage_events);
+
 /* ---- the full Hy3 MoE block ("Tencent Hy3-Flash Q&A", Q4.3, Q4.7, Q4.9) ----
  *
  *   block out[t] = Shared(x_t) + sum_j w_j * Expert_idx[t,j](x_t)

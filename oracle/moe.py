@@ -257,11 +257,27 @@ def quant_rows_e4m3(M):
     return q, s
 
 
+def dequant_e4m3(q, s):
+    """Dequantised float64 weight matrix from e4m3 codes q [R, C] and fp32
+    scales: s [R] gives one scale per row (output channel); s [R/128, C/128]
+    gives one per 128 x 128 block, element (n, i) taking s[n // 128, i // 128]
+    ("DeepSeek V4-Flash architecture Q&A", Q7.2: block-wise quantisation)."""
+    w = e4m3_bits_to_f64(np.asarray(q, dtype=np.uint8))
+    s = np.asarray(s, dtype=np.float64)
+    if s.ndim == 1:
+        return w * s[:, None]
+    R, C = w.shape
+    assert s.shape == (R // 128, C // 128) and R % 128 == 0 and C % 128 == 0
+    return w * np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
+
+
 def forward_fp8(x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale, logit_bias=None):
     """Routed MoE output with e4m3 experts.
 
     Wq_gu uint8 [E,2F,d] with float32 per-output-row scales s_gu [E,2F];
-    Wq_dn uint8 [E,d,F] with s_dn [E,d].  Routing is the float32 router of
+    Wq_dn uint8 [E,d,F] with s_dn [E,d].  Or block scales, one per 128 x 128
+    block: s_gu [E,2F/128,d/128] and s_dn [E,d/128,F/128] (``dequant_e4m3``).
+    Routing is the float32 router of
     ``route``.  Each token's bf16 row is quantised with quant_row_e4m3 before
     the gate_up product; each (token, slot) SwiGLU activation row, rounded to
     float32, is quantised the same way before the down product.  Products use
@@ -278,8 +294,8 @@ def forward_fp8(x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale, logit_bias=N
     F = Wq_dn.shape[2]
     for e in np.unique(r.idx):
         t, j = np.nonzero(r.idx == e)
-        Wgu = e4m3_bits_to_f64(Wq_gu[e]) * np.asarray(s_gu[e], np.float64)[:, None]
-        Wdn = e4m3_bits_to_f64(Wq_dn[e]) * np.asarray(s_dn[e], np.float64)[:, None]
+        Wgu = dequant_e4m3(Wq_gu[e], s_gu[e])
+        Wdn = dequant_e4m3(Wq_dn[e], s_dn[e])
         g = xd[t] @ Wgu[:F].T
         u = xd[t] @ Wgu[F:].T
         a = g * _sigmoid64(g) * u

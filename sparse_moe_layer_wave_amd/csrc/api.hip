@@ -279,7 +279,7 @@ static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_ep
 int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, const float* s_gu,
                 const uint8_t* Wq_dn, const float* s_dn, float* out, int T, int d, int E, int k,
                 int d_ff, float scale, void* stream, const float* logit_bias, int32_t* topk_idx,
-                float* topk_w, void* workspace, const Layout& L, void* const* ev) {
+                float* topk_w, void* workspace, const Layout& L, void* const* ev, bool block) {
     char* ws = static_cast<char*>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t Tk = static_cast<size_t>(T) * k;
@@ -316,7 +316,10 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_gate_up_decode_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, max_slices,
-                                               h32, amax, E, d, d_ff, rg, s);
+                                               h32, amax, E, d, d_ff, rg, block, s);
+        else if (block)
+            e = hy3::launch_gate_up_fp8_block(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off,
+                                              L.max_mtiles, h32, amax, E, d, d_ff, s);
         else
             e = hy3::launch_gate_up_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, L.max_mtiles,
                                         h32, amax, E, d, d_ff, s);
@@ -326,7 +329,10 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_down_decode_fp8(hq, hs, Wq_dn, s_dn, offsets, tile_off, max_slices, y, E, d,
-                                            d_ff, rg, s);
+                                            d_ff, rg, block, s);
+        else if (block)
+            e = hy3::launch_down_fp8_block(hq, hs, Wq_dn, s_dn, offsets, tile_off, L.max_mtiles, y, E,
+                                           d, d_ff, s);
         else
             e = hy3::launch_down_fp8(hq, hs, Wq_dn, s_dn, offsets, tile_off, L.max_mtiles, y, E, d,
                                      d_ff, s);
@@ -335,6 +341,32 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
     if (e == hipSuccess) e = hy3::launch_combine(y, row_of, w, out, T, d, k, -1, s);
     if (e == hipSuccess) e = mark(ev, 5, s);
     return hip_status(e);
+}
+
+// Argument checks shared by the e4m3 entry points.  Block-scaled weights
+// need d and d_ff in whole 256-element batches of the weight-streaming
+// kernels and at most 16384 (128 k-blocks per row).
+int fp8_entry(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, const float* s_gu,
+              const uint8_t* Wq_dn, const float* s_dn, float* out, int T, int d, int E, int k,
+              int d_ff, float scale, void* stream, const float* logit_bias, int32_t* topk_idx,
+              float* topk_w, void* workspace, size_t workspace_bytes, void* const* ev, bool block) {
+    int st = check_shape(T, d, E, k, d_ff);
+    if (st != HY3MOE_OK) return st;
+    if (T == 0) return HY3MOE_OK;
+    if (!x || !W_gate || !Wq_gu || !s_gu || !Wq_dn || !s_dn || !out || !workspace)
+        return HY3MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(W_gate) || !aligned16(Wq_gu) || !aligned16(s_gu) ||
+        !aligned16(Wq_dn) || !aligned16(s_dn) || !aligned16(out) || !aligned16(workspace) ||
+        (logit_bias && !aligned16(logit_bias)) || (topk_idx && !aligned16(topk_idx)) ||
+        (topk_w && !aligned16(topk_w)))
+        return HY3MOE_ERR_ALIGN;
+    if ((d % 128) != 0 || (d_ff % 128) != 0) return HY3MOE_ERR_UNSUPPORTED;
+    if (block && ((d % 256) != 0 || (d_ff % 256) != 0 || d > 16384 || d_ff > 16384))
+        return HY3MOE_ERR_UNSUPPORTED;
+    const Layout L = make_layout(T, d, E, k, d_ff, HY3MOE_WEIGHTS_FP8_E4M3);
+    if (workspace_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
+    return forward_fp8(x, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, out, T, d, E, k, d_ff, scale, stream,
+                       logit_bias, topk_idx, topk_w, workspace, L, ev, block);
 }
 
 }  // namespace
@@ -410,21 +442,8 @@ int hy3moe_forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq
                        float* out, int T, int d, int E, int k, int d_ff, float scale, void* stream,
                        const float* logit_bias, int32_t* topk_idx, float* topk_w, void* workspace,
                        size_t workspace_bytes) {
-    int st = check_shape(T, d, E, k, d_ff);
-    if (st != HY3MOE_OK) return st;
-    if (T == 0) return HY3MOE_OK;
-    if (!x || !W_gate || !Wq_gate_up || !s_gate_up || !Wq_down || !s_down || !out || !workspace)
-        return HY3MOE_ERR_NULL;
-    if (!aligned16(x) || !aligned16(W_gate) || !aligned16(Wq_gate_up) || !aligned16(s_gate_up) ||
-        !aligned16(Wq_down) || !aligned16(s_down) || !aligned16(out) || !aligned16(workspace) ||
-        (logit_bias && !aligned16(logit_bias)) || (topk_idx && !aligned16(topk_idx)) ||
-        (topk_w && !aligned16(topk_w)))
-        return HY3MOE_ERR_ALIGN;
-    if ((d % 128) != 0 || (d_ff % 128) != 0) return HY3MOE_ERR_UNSUPPORTED;
-    const Layout L = make_layout(T, d, E, k, d_ff, HY3MOE_WEIGHTS_FP8_E4M3);
-    if (workspace_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
-    return forward_fp8(x, W_gate, Wq_gate_up, s_gate_up, Wq_down, s_down, out, T, d, E, k, d_ff,
-                       scale, stream, logit_bias, topk_idx, topk_w, workspace, L, nullptr);
+    return fp8_entry(x, W_gate, Wq_gate_up, s_gate_up, Wq_down, s_down, out, T, d, E, k, d_ff, scale,
+                     stream, logit_bias, topk_idx, topk_w, workspace, workspace_bytes, nullptr, false);
 }
 
 int hy3moe_forward_fp8_timed(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gate_up,
@@ -433,21 +452,31 @@ int hy3moe_forward_fp8_timed(const uint16_t* x, const float* W_gate, const uint8
                              void* stream, const float* logit_bias, int32_t* topk_idx,
                              float* topk_w, void* workspace, size_t workspace_bytes,
                              void* const* stage_events) {
-    int st = check_shape(T, d, E, k, d_ff);
-    if (st != HY3MOE_OK) return st;
-    if (T == 0) return HY3MOE_OK;
-    if (!x || !W_gate || !Wq_gate_up || !s_gate_up || !Wq_down || !s_down || !out || !workspace)
-        return HY3MOE_ERR_NULL;
-    if (!aligned16(x) || !aligned16(W_gate) || !aligned16(Wq_gate_up) || !aligned16(s_gate_up) ||
-        !aligned16(Wq_down) || !aligned16(s_down) || !aligned16(out) || !aligned16(workspace) ||
-        (logit_bias && !aligned16(logit_bias)) || (topk_idx && !aligned16(topk_idx)) ||
-        (topk_w && !aligned16(topk_w)))
-        return HY3MOE_ERR_ALIGN;
-    if ((d % 128) != 0 || (d_ff % 128) != 0) return HY3MOE_ERR_UNSUPPORTED;
-    const Layout L = make_layout(T, d, E, k, d_ff, HY3MOE_WEIGHTS_FP8_E4M3);
-    if (workspace_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
-    return forward_fp8(x, W_gate, Wq_gate_up, s_gate_up, Wq_down, s_down, out, T, d, E, k, d_ff,
-                       scale, stream, logit_bias, topk_idx, topk_w, workspace, L, stage_events);
+    return fp8_entry(x, W_gate, Wq_gate_up, s_gate_up, Wq_down, s_down, out, T, d, E, k, d_ff, scale,
+                     stream, logit_bias, topk_idx, topk_w, workspace, workspace_bytes, stage_events,
+                     false);
+}
+
+int hy3moe_forward_fp8_block128(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gate_up,
+                                const float* sb_gate_up, const uint8_t* Wq_down, const float* sb_down,
+                                float* out, int T, int d, int E, int k, int d_ff, float scale,
+                                void* stream, const float* logit_bias, int32_t* topk_idx,
+                                float* topk_w, void* workspace, size_t workspace_bytes) {
+    return fp8_entry(x, W_gate, Wq_gate_up, sb_gate_up, Wq_down, sb_down, out, T, d, E, k, d_ff,
+                     scale, stream, logit_bias, topk_idx, topk_w, workspace, workspace_bytes, nullptr,
+                     true);
+}
+
+int hy3moe_forward_fp8_block128_timed(const uint16_t* x, const float* W_gate,
+                                      const uint8_t* Wq_gate_up, const float* sb_gate_up,
+                                      const uint8_t* Wq_down, const float* sb_down, float* out, int T,
+                                      int d, int E, int k, int d_ff, float scale, void* stream,
+                                      const float* logit_bias, int32_t* topk_idx, float* topk_w,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* const* stage_events) {
+    return fp8_entry(x, W_gate, Wq_gate_up, sb_gate_up, Wq_down, sb_down, out, T, d, E, k, d_ff,
+                     scale, stream, logit_bias, topk_idx, topk_w, workspace, workspace_bytes,
+                     stage_events, true);
 }
 
 int hy3moe_quantize_rows_e4m3(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,

@@ -40,7 +40,8 @@
 namespace hy3 {
 namespace {
 
-enum Mode { GU_BF16 = 0, DN_BF16 = 1, GU_FP8 = 2, DN_FP8 = 3 };
+// FP8B: e4m3 weights with one fp32 scale per 128 x 128 block (below).
+enum Mode { GU_BF16 = 0, DN_BF16 = 1, GU_FP8 = 2, DN_FP8 = 3, GU_FP8B = 4, DN_FP8B = 5 };
 
 // Column blocks per workgroup, taken one after the other with the weight
 // stream running on across the boundary.  An e4m3 block moves half the bytes
@@ -77,8 +78,9 @@ struct DecodeArgs {
 
 template <int MODE, int SUBS, int RG>
 __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
-    constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8;
-    constexpr bool FP8 = MODE == GU_FP8 || MODE == DN_FP8;
+    constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8 || MODE == GU_FP8B;
+    constexpr bool BLK = MODE == GU_FP8B || MODE == DN_FP8B;
+    constexpr bool FP8 = MODE >= GU_FP8;
     constexpr int ESZ = FP8 ? 1 : 2;
     __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kSlabB];
     const int E = g.E;
@@ -128,11 +130,26 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
 
     // e4m3: this lane's column scales per block (column col0 + r16, and + 16 for down)
     float ws0[SUBS], ws1[SUBS];
+    // block scales: the wave's acc0 / acc1 weight rows lie in one 128-row
+    // block each; lane i keeps that block row's scales of k-blocks i and 64 + i
+    int bsc0[SUBS][2], bsc1[SUBS][2];
 #pragma unroll
     for (int sb = 0; sb < SUBS; ++sb) {
-        ws0[sb] = 0.f;
-        ws1[sb] = 0.f;
-        if constexpr (FP8) {
+        ws0[sb] = BLK ? 1.f : 0.f;
+        ws1[sb] = BLK ? 1.f : 0.f;
+        bsc0[sb][0] = bsc0[sb][1] = bsc1[sb][0] = bsc1[sb][1] = 0;
+        if constexpr (BLK) {
+            const int KB = K >> 7;
+            const float* se = g.w_scale + static_cast<size_t>(e) * ((GATE_UP ? 2 * N : N) >> 7) * KB;
+            const int c0 = colb + sb * SUBROWS;
+            const int nb0 = c0 >> 7, nb1 = GATE_UP ? (N + c0) >> 7 : (c0 + 16) >> 7;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int kk = lane + 64 * h;
+                bsc0[sb][h] = kk < KB ? __float_as_int(se[static_cast<size_t>(nb0) * KB + kk]) : 0;
+                bsc1[sb][h] = kk < KB ? __float_as_int(se[static_cast<size_t>(nb1) * KB + kk]) : 0;
+            }
+        } else if constexpr (FP8) {
             const float* ws_e = g.w_scale + static_cast<size_t>(e) * (GATE_UP ? 2 * N : N);
             const int c0 = colb + sb * SUBROWS;
             ws0[sb] = ws_e[c0 + r16];
@@ -187,6 +204,24 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
                         for (int h = 0; h < 2; ++h)
                             av[q][s][h] = va[q] ? *reinterpret_cast<const i32x4_t*>(a[q] + kb + 128 * s + 16 * h)
                                                 : i32x4_t{0, 0, 0, 0};
+                // block scales of this batch's two k-blocks (2b, 2b + 1)
+                float sc0[2] = {1.f, 1.f}, sc1[2] = {1.f, 1.f};
+                if constexpr (BLK) {
+                    int v0[2] = {bsc0[0][0], bsc0[0][1]}, v1[2] = {bsc1[0][0], bsc1[0][1]};
+#pragma unroll
+                    for (int q = 1; q < SUBS; ++q)
+                        if (sb == q) {
+                            v0[0] = bsc0[q][0]; v0[1] = bsc0[q][1];
+                            v1[0] = bsc1[q][0]; v1[1] = bsc1[q][1];
+                        }
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const int kblk = 2 * b + s;
+                        const bool hi = kblk >= 64;
+                        sc0[s] = __int_as_float(__builtin_amdgcn_readlane(hi ? v0[1] : v0[0], kblk & 63));
+                        sc1[s] = __int_as_float(__builtin_amdgcn_readlane(hi ? v1[1] : v1[0], kblk & 63));
+                    }
+                }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const int ch = 8 * s + 2 * kq;
@@ -199,8 +234,21 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
 #pragma unroll
                     for (int q = 0; q < RG; ++q) {
                         const i32x8_t fa = __builtin_shufflevector(av[q][s][0], av[q][s][1], 0, 1, 2, 3, 4, 5, 6, 7);
-                        acc0[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, f0, acc0[q], 0, 0, 0, 127, 0, 127);
-                        acc1[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, f1, acc1[q], 0, 0, 0, 127, 0, 127);
+                        if constexpr (BLK) {
+                            // one k-step is one 128-wide k-block: its product
+                            // is scaled by the block's scale and added in fp32
+                            const f32x4_t z{0.f, 0.f, 0.f, 0.f};
+                            const f32x4_t t0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, f0, z, 0, 0, 0, 127, 0, 127);
+                            const f32x4_t t1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, f1, z, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                acc0[q][i] = fmaf(t0[i], sc0[s], acc0[q][i]);
+                                acc1[q][i] = fmaf(t1[i], sc1[s], acc1[q][i]);
+                            }
+                        } else {
+                            acc0[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, f0, acc0[q], 0, 0, 0, 127, 0, 127);
+                            acc1[q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, f1, acc1[q], 0, 0, 0, 127, 0, 127);
+                        }
                     }
                 }
             } else {
@@ -246,7 +294,7 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
                             g.C[crow * N + col0 + r16] = f32_to_bf16(acc0[q][i]);
                             g.C[crow * N + col0 + 16 + r16] = f32_to_bf16(acc1[q][i]);
                         }
-                    } else if constexpr (MODE == GU_FP8) {
+                    } else if constexpr (MODE == GU_FP8 || MODE == GU_FP8B) {
                         const float sx = g.a_scale[g.tok_of[crow]];
                         const float hv = silu_mul(acc0[q][i] * sx * w0, acc1[q][i] * sx * w1);
                         if (vr) g.h32[crow * N + col0 + r16] = hv;
@@ -332,23 +380,35 @@ hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uin
 hipError_t launch_gate_up_decode_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                                      const uint8_t* Wq, const float* ws, const int32_t* offsets,
                                      const int32_t* slice_off, int max_slices, float* h32,
-                                     uint32_t* amax, int E, int d, int F, int rg, hipStream_t s) {
+                                     uint32_t* amax, int E, int d, int F, int rg, bool block,
+                                     hipStream_t s) {
     DecodeArgs g{xq, tok_of, Wq, nullptr, offsets, slice_off, nullptr, xs, ws, h32, amax, d, F, E};
     if (max_slices == 0) return hipSuccess;
     const dim3 grid(max_slices, F / (64 * kSubsFp8));
-    if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<GU_FP8, kSubsFp8, 2>), grid, dim3(256), 0, s, g);
-    else hipLaunchKernelGGL((k_decode_gemm<GU_FP8, kSubsFp8, 1>), grid, dim3(256), 0, s, g);
+    if (block) {
+        if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<GU_FP8B, kSubsFp8, 2>), grid, dim3(256), 0, s, g);
+        else hipLaunchKernelGGL((k_decode_gemm<GU_FP8B, kSubsFp8, 1>), grid, dim3(256), 0, s, g);
+    } else {
+        if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<GU_FP8, kSubsFp8, 2>), grid, dim3(256), 0, s, g);
+        else hipLaunchKernelGGL((k_decode_gemm<GU_FP8, kSubsFp8, 1>), grid, dim3(256), 0, s, g);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq,
                                   const float* ws, const int32_t* offsets, const int32_t* slice_off,
-                                  int max_slices, uint16_t* y, int E, int d, int F, int rg, hipStream_t s) {
+                                  int max_slices, uint16_t* y, int E, int d, int F, int rg, bool block,
+                                  hipStream_t s) {
     DecodeArgs g{hq, nullptr, Wq, nullptr, offsets, slice_off, y, hs, ws, nullptr, nullptr, F, d, E};
     if (max_slices == 0) return hipSuccess;
     const dim3 grid(max_slices, d / (128 * kSubsFp8));
-    if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<DN_FP8, kSubsFp8, 2>), grid, dim3(256), 0, s, g);
-    else hipLaunchKernelGGL((k_decode_gemm<DN_FP8, kSubsFp8, 1>), grid, dim3(256), 0, s, g);
+    if (block) {
+        if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<DN_FP8B, kSubsFp8, 2>), grid, dim3(256), 0, s, g);
+        else hipLaunchKernelGGL((k_decode_gemm<DN_FP8B, kSubsFp8, 1>), grid, dim3(256), 0, s, g);
+    } else {
+        if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<DN_FP8, kSubsFp8, 2>), grid, dim3(256), 0, s, g);
+        else hipLaunchKernelGGL((k_decode_gemm<DN_FP8, kSubsFp8, 1>), grid, dim3(256), 0, s, g);
+    }
     return hipGetLastError();
 }
 

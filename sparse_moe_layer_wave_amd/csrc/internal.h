@@ -185,13 +185,28 @@ hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const int32_t*
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq, const float* ws,
                            const int32_t* offsets, const int32_t* tile_off, int max_mtiles,
                            uint16_t* y, int E, int d, int F, hipStream_t s);
-// decode-sized batches with e4m3 experts (weight streaming, as the bf16 ones)
+// decode-sized batches with e4m3 experts (weight streaming, as the bf16 ones).
+// block: ws holds one fp32 scale per 128 x 128 weight block, [E, rows/128,
+// K/128] (rows = 2F for gate_up, d for down; K = d, F), instead of one per
+// output channel; K <= 16384.
 hipError_t launch_gate_up_decode_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                                      const uint8_t* Wq, const float* ws, const int32_t* offsets,
                                      const int32_t* slice_off, int max_slices, float* h32,
-                                     uint32_t* amax, int E, int d, int F, int rg, hipStream_t s);
+                                     uint32_t* amax, int E, int d, int F, int rg, bool block,
+                                     hipStream_t s);
 hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq,
                                   const float* ws, const int32_t* offsets, const int32_t* slice_off,
-                                  int max_slices, uint16_t* y, int E, int d, int F, int rg, hipStream_t s);
+                                  int max_slices, uint16_t* y, int E, int d, int F, int rg, bool block,
+                                  hipStream_t s);
+
+// prefill-sized batches with e4m3 weights in 128 x 128 blocks (one fp32
+// scale each, sb [E, rows/128, K/128]); K <= 16384, tile_off in 128-row blocks
+hipError_t launch_gate_up_fp8_block(const uint8_t* xq, const float* xs, const int32_t* tok_of,
+                                    const uint8_t* Wq, const float* sb, const int32_t* offsets,
+                                    const int32_t* tile_off, int max_mtiles, float* h32,
+                                    uint32_t* amax, int E, int d, int F, hipStream_t s);
+hipError_t launch_down_fp8_block(const uint8_t* hq, const float* hs, const uint8_t* Wq,
+                                 const float* sb, const int32_t* offsets, const int32_t* tile_off,
+                                 int max_mtiles, uint16_t* y, int E, int d, int F, hipStream_t s);
 
 }  // namespace hy3

@@ -21,6 +21,7 @@ WEIGHTS_BF16, WEIGHTS_FP8_E4M3 = 0, 1
 EXPORTS = (
     "hy3moe_workspace_size", "hy3moe_route", "hy3moe_permute", "hy3moe_forward",
     "hy3moe_forward_timed", "hy3moe_forward_fp8", "hy3moe_forward_fp8_timed",
+    "hy3moe_forward_fp8_block128", "hy3moe_forward_fp8_block128_timed",
     "hy3moe_block_workspace_size", "hy3moe_route_ex", "hy3moe_block_forward",
     "hy3moe_block_forward_timed", "hy3moe_block_forward_bf16", "hy3moe_quantize_rows_e4m3", "hy3moe_status_string",
     "hy3moe_last_hip_error",
@@ -55,6 +56,8 @@ def lib():
     L.hy3moe_forward_timed.argtypes = [P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z, P]
     L.hy3moe_forward_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z]
     L.hy3moe_forward_fp8_timed.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z, P]
+    L.hy3moe_forward_fp8_block128.argtypes = L.hy3moe_forward_fp8.argtypes
+    L.hy3moe_forward_fp8_block128_timed.argtypes = L.hy3moe_forward_fp8_timed.argtypes
     L.hy3moe_block_workspace_size.argtypes = [I, I, I, I, I, ctypes.POINTER(Z)]
     L.hy3moe_route_ex.argtypes = [P, P, F, P, P, P, I, I, I, I, F, P, P, P, Z, S]
     L.hy3moe_block_forward.argtypes = [P, P, F, P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, Z]
@@ -193,17 +196,24 @@ def _event_array(stage_events):
 
 
 def forward_fp8(x, W_gate, Wq_gate_up, s_gate_up, Wq_down, s_down, k, scale, bias=None, out=None,
-                workspace=None, return_routing=False, stage_events=None):
-    """hy3moe_forward_fp8: e4m3 experts (uint8 codes) with fp32 per-channel scales."""
+                workspace=None, return_routing=False, stage_events=None, block128=False):
+    """hy3moe_forward_fp8: e4m3 experts (uint8 codes) with fp32 per-channel
+    scales; with block128=True, hy3moe_forward_fp8_block128: one fp32 scale
+    per 128 x 128 weight block, s_gate_up [E, 2F/128, d/128] and s_down
+    [E, d/128, F/128]."""
     T, d = x.shape
     E = W_gate.shape[0]
     F = Wq_down.shape[2]
     _need(x, torch.bfloat16, (T, d), "x")
     _need(W_gate, torch.float32, (E, d), "W_gate")
     _need(Wq_gate_up, torch.uint8, (E, 2 * F, d), "Wq_gate_up")
-    _need(s_gate_up, torch.float32, (E, 2 * F), "s_gate_up")
     _need(Wq_down, torch.uint8, (E, d, F), "Wq_down")
-    _need(s_down, torch.float32, (E, d), "s_down")
+    if block128:
+        _need(s_gate_up, torch.float32, (E, 2 * F // 128, d // 128), "s_gate_up")
+        _need(s_down, torch.float32, (E, d // 128, F // 128), "s_down")
+    else:
+        _need(s_gate_up, torch.float32, (E, 2 * F), "s_gate_up")
+        _need(s_down, torch.float32, (E, d), "s_down")
     if bias is not None:
         _need(bias, torch.float32, (E,), "bias")
     if out is None:
@@ -218,12 +228,17 @@ def forward_fp8(x, W_gate, Wq_gate_up, s_gate_up, Wq_down, s_down, k, scale, bia
     args = (_ptr(x), _ptr(W_gate), _ptr(Wq_gate_up), _ptr(s_gate_up), _ptr(Wq_down), _ptr(s_down),
             _ptr(out), T, d, E, k, F, float(scale), _stream(), _ptr(bias), _ptr(idx), _ptr(w),
             _ptr(workspace), 0 if workspace is None else workspace.numel())
+    name = "hy3moe_forward_fp8_block128" if block128 else "hy3moe_forward_fp8"
     if stage_events is None:
-        _check(lib().hy3moe_forward_fp8(*args), "hy3moe_forward_fp8")
+        _check(getattr(lib(), name)(*args), name)
     else:
-        _check(lib().hy3moe_forward_fp8_timed(*args, _event_array(stage_events)),
-               "hy3moe_forward_fp8_timed")
+        _check(getattr(lib(), name + "_timed")(*args, _event_array(stage_events)), name + "_timed")
     return (out, idx, w) if return_routing else out
+
+
+def forward_fp8_block128(x, W_gate, Wq_gate_up, sb_gate_up, Wq_down, sb_down, k, scale, **kw):
+    """hy3moe_forward_fp8_block128 (forward_fp8 with block128=True)."""
+    return forward_fp8(x, W_gate, Wq_gate_up, sb_gate_up, Wq_down, sb_down, k, scale, block128=True, **kw)
 
 
 def block_workspace_size(T, d, E, k, d_ff):

@@ -14,6 +14,8 @@ Distributions (the second parameter of N(.,.) is a standard deviation):
 FP8 workload: W_gu / W_dn drawn as above in fp32, then per output row
 (= per output channel) scale s = amax/448 and codes e4m3(w / s) via torch's
 cast; the codes and the fp32 scales are the layer's inputs.
+Block-128 FP8 workload: the same fp32 draws, one scale s = amax/448 per
+128 x 128 block of each weight matrix instead of per row.
 Full-block workloads add:
   norm_w      bf16  [d]       1 + N(0, 0.1)    route_norm weight
   score_bias  fp32  [E]       N(0, 0.05)       selection-only score bias (moves
@@ -64,6 +66,11 @@ CONFIGS = {
     # tens of rows)
     8: dict(name="hy3_skewed_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=8,
             weights="bf16", skew=True),
+    # e4m3 experts with one scale per 128 x 128 weight block
+    9: dict(name="hy3_fp8_block128_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=9,
+            weights="fp8_block128", skew=False),
+    10: dict(name="hy3_fp8_block128_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=10,
+             weights="fp8_block128", skew=False),
 }
 
 (_STREAM_X, _STREAM_WG, _STREAM_BIAS, _STREAM_WGU, _STREAM_WDN, _STREAM_NORM, _STREAM_SBIAS,
@@ -133,6 +140,33 @@ def make_experts_fp8(E, d, F, seed, device="cpu"):
     return qgu, sgu, qdn, sdn
 
 
+def _block128_e4m3(w):
+    """One fp32 scale per 128 x 128 block: s = amax / 448 (1 for an all-zero
+    block), codes e4m3(w / s) via torch's cast."""
+    R, C = w.shape
+    b = w.reshape(R // 128, 128, C // 128, 128)
+    amax = b.abs().amax(dim=(1, 3))
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (b / s[:, None, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.reshape(R, C).view(torch.uint8), s.to(torch.float32)
+
+
+def make_experts_fp8_block128(E, d, F, seed, device="cpu"):
+    """The fp8 workload's fp32 expert weights (same draws), quantised in
+    128 x 128 blocks: codes [E,2F,d] / [E,d,F], scales [E,2F/128,d/128] /
+    [E,d/128,F/128]."""
+    qgu = torch.empty((E, 2 * F, d), dtype=torch.uint8, device=device)
+    sgu = torch.empty((E, 2 * F // 128, d // 128), dtype=torch.float32, device=device)
+    qdn = torch.empty((E, d, F), dtype=torch.uint8, device=device)
+    sdn = torch.empty((E, d // 128, F // 128), dtype=torch.float32, device=device)
+    g1 = _gen(device, seed, _STREAM_WGU)
+    g2 = _gen(device, seed, _STREAM_WDN)
+    for e in range(E):
+        qgu[e], sgu[e] = _block128_e4m3(_expert_fp32(2 * F, d, g1, device))
+        qdn[e], sdn[e] = _block128_e4m3(_expert_fp32(d, F, g2, device))
+    return qgu, sgu, qdn, sdn
+
+
 def make_block_extras(d, E, F, seed, device="cpu"):
     """route_norm weight, selection-only score bias and shared expert weights."""
     gn = _gen(device, seed, _STREAM_NORM)
@@ -160,7 +194,10 @@ def make_inputs(cfg, device="cpu", T=None, with_experts=True):
     out["x"] = make_x(c["T"], c["d"], c["seed"], device)
     out["W_gate"], out["bias"] = make_router(c["E"], c["d"], c["seed"], device, c.get("skew", False))
     if with_experts:
-        if c.get("weights", "bf16") == "fp8":
+        if c.get("weights", "bf16") == "fp8_block128":
+            out["Wq_gu"], out["s_gu"], out["Wq_dn"], out["s_dn"] = make_experts_fp8_block128(
+                c["E"], c["d"], c["F"], c["seed"], device)
+        elif c.get("weights", "bf16") == "fp8":
             out["Wq_gu"], out["s_gu"], out["Wq_dn"], out["s_dn"] = make_experts_fp8(
                 c["E"], c["d"], c["F"], c["seed"], device)
         else:

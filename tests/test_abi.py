@@ -183,6 +183,20 @@ def test_block_forward_bf16_argument_checks(L):
     assert b(T=0, res=NUL, out=NUL, x=NUL, sgu=NUL, ws=NUL, nws=0) == hy3moe.OK
 
 
+def test_forward_fp8_block128_argument_checks(L):
+    def f(T=16, d=512, E=32, k=8, F=256, x=A, sg=A, out=A, ws=A, nws=64):
+        return L.hy3moe_forward_fp8_block128(x, A, A, sg, A, A, out, T, d, E, k, F, 2.826, NUL, NUL,
+                                             NUL, NUL, ws, nws)
+    assert f(T=-1) == hy3moe.ERR_SHAPE
+    assert f(F=384) == hy3moe.ERR_UNSUPPORTED            # whole 256-element batches only
+    assert f(d=640) == hy3moe.ERR_UNSUPPORTED
+    assert f(d=16640) == hy3moe.ERR_UNSUPPORTED          # more than 128 k-blocks per row
+    assert f(sg=NUL) == hy3moe.ERR_NULL
+    assert f(sg=MIS) == hy3moe.ERR_ALIGN
+    assert f(nws=64) == hy3moe.ERR_WORKSPACE
+    assert f(T=0, x=NUL, sg=NUL, out=NUL, ws=NUL, nws=0) == hy3moe.OK
+
+
 def test_route_ex_argument_checks(L):
     def r(T=16, d=512, E=32, k=8, x=A, nw=NUL, eps=1e-6, sb=NUL, ws=A, nws=1 << 40):
         return L.hy3moe_route_ex(x, nw, eps, A, NUL, sb, T, d, E, k, 2.826, A, A, ws, nws, NUL)

@@ -86,14 +86,16 @@ def test_fp8_deterministic(gpu_lib):
         assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("cfg,n_sample", [(4, 10), (7, 16)])
+@pytest.mark.parametrize("cfg,n_sample", [(4, 10), (7, 16), (9, 16), (10, 10)])
 def test_hy3_fp8(gpu_lib, cfg, n_sample):
+    """Per-channel scales (workloads 4, 7) and 128 x 128 block scales (9, 10)."""
     from sparse_moe_layer_wave_amd import hy3moe as hy
     inp = inputs.make_inputs(cfg, device="cuda")
     c = inp["cfg"]
     T = c["T"]
     out, idx, w = hy.forward_fp8(inp["x"], inp["W_gate"], inp["Wq_gu"], inp["s_gu"], inp["Wq_dn"],
-                                 inp["s_dn"], c["k"], inp["scale"], return_routing=True)
+                                 inp["s_dn"], c["k"], inp["scale"], return_routing=True,
+                                 block128=c["weights"] == "fp8_block128")
     torch.cuda.synchronize()
     x_bits = inputs.bits(inp["x"])
     W = inputs.bits(inp["W_gate"])
@@ -108,3 +110,54 @@ def test_hy3_fp8(gpu_lib, cfg, n_sample):
     set_eq = np.array([set(a) == set(b) for a, b in zip(idx_np[sample].tolist(), rs.idx.tolist())])
     stats.update(check_output(out.cpu().numpy()[sample], ref, TOL_FP8, set_eq))
     print("fp8", inp["cfg"]["name"], stats)
+
+
+# ----------------------------------------------------------------------------- 128 x 128 block scales
+
+def _cpu_fp8_block_case(T, E, k, F, d, seed):
+    c = dict(inputs.CONFIGS[9], T=T, d=d, E=E, k=k, F=F, seed=seed)
+    return inputs.make_inputs(c, device="cpu")
+
+
+@pytest.mark.parametrize("T,E,k,F,d", [(16, 64, 8, 256, 512), (1, 8, 2, 256, 256), (56, 24, 8, 256, 512),
+                                       (300, 32, 8, 256, 512), (700, 48, 4, 512, 768),
+                                       (129, 16, 16, 256, 1024)])
+def test_fp8_block128_full_parity(gpu_lib, T, E, k, F, d):
+    """hy3moe_forward_fp8_block128 on every token: decode-sized batches and
+    larger ones (all on the weight-streaming kernels), one and two row groups,
+    d up to 8 k-blocks and k = 16."""
+    from sparse_moe_layer_wave_amd import hy3moe as hy
+    inp = _cpu_fp8_block_case(T, E, k, F, d, seed=60 + T)
+    dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
+    out, idx, w = hy.forward_fp8_block128(dev["x"], dev["W_gate"], dev["Wq_gu"], dev["s_gu"], dev["Wq_dn"],
+                                          dev["s_dn"], k, inp["scale"], return_routing=True)
+    torch.cuda.synchronize()
+    ref, r = oracle.forward_fp8(inputs.bits(inp["x"]), inp["W_gate"].numpy(), inputs.bits(inp["Wq_gu"]),
+                                inp["s_gu"].numpy(), inputs.bits(inp["Wq_dn"]), inp["s_dn"].numpy(),
+                                k, inp["scale"])
+    stats = check_routing(idx.cpu().numpy(), w.cpu().numpy(), r, inp["scale"])
+    set_eq = np.array([set(a) == set(b) for a, b in zip(idx.cpu().numpy().tolist(), r.idx.tolist())])
+    stats.update(check_output_fp8_small(out.cpu().numpy(), ref, set_eq, TOL_FP8, T * k * F))
+    print(T, E, k, F, d, stats)
+
+
+def test_fp8_block128_uses_the_block_scales(gpu_lib):
+    """Scaling one 128 x 128 block of one expert's down matrix by 2 doubles
+    exactly that block's contribution: with a power-of-two factor every
+    product and partial sum scales exactly, so the output changes only in the
+    block's 128 output channels, for the tokens routed to that expert."""
+    from sparse_moe_layer_wave_amd import hy3moe as hy
+    inp = _cpu_fp8_block_case(40, 16, 4, 256, 512, seed=71)
+    dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
+    args = (dev["x"], dev["W_gate"], dev["Wq_gu"], dev["s_gu"], dev["Wq_dn"])
+    out, idx, _ = hy.forward_fp8_block128(*args, dev["s_dn"], 4, inp["scale"], return_routing=True)
+    s2 = dev["s_dn"].clone()
+    s2[3, 1, :] *= 2.0                                  # expert 3, output channels 128..255, all k
+    out2 = hy.forward_fp8_block128(*args, s2, 4, inp["scale"])
+    torch.cuda.synchronize()
+    a, b = out.cpu().numpy(), out2.cpu().numpy()
+    hit = (idx.cpu().numpy() == 3).any(axis=1)
+    assert hit.any() and not hit.all()
+    assert np.array_equal(a[~hit], b[~hit])
+    assert np.array_equal(a[:, :128], b[:, :128]) and np.array_equal(a[:, 256:], b[:, 256:])
+    assert np.any(a[hit, 128:256] != b[hit, 128:256])

@@ -83,3 +83,68 @@ def test_fp8_routing_equals_bf16_routing():
     _, r8 = oracle.forward_fp8(x, Wg, qgu, s1, qdn, s2, 4, SCALE)
     r = oracle.route(x, Wg, 4, SCALE)
     assert np.array_equal(r8.idx, r.idx) and np.array_equal(r8.w, r.w)
+
+
+def _fp8_layer(rng, T, d, E, F):
+    x = codecs.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    Wg = (rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)
+    qgu = codecs.f32_to_e4m3_bits((rng.standard_normal((E, 2 * F, d)) * 0.1).astype(np.float32))
+    qdn = codecs.f32_to_e4m3_bits((rng.standard_normal((E, d, F)) * 0.1).astype(np.float32))
+    return x, Wg, qgu, qdn
+
+
+def test_block_scales_constant_along_k_equal_row_scales():
+    """128 x 128 block scales that depend only on the row block give the same
+    layer as per-row scales repeated over each block's 128 rows."""
+    rng = np.random.default_rng(24)
+    T, d, E, F, k = 20, 256, 6, 128, 3
+    x, Wg, qgu, qdn = _fp8_layer(rng, T, d, E, F)
+    cgu = (2.0 ** rng.integers(-9, -3, (E, 2 * F // 128)) * (1 + rng.random((E, 2 * F // 128)))).astype(np.float32)
+    cdn = (2.0 ** rng.integers(-9, -3, (E, d // 128)) * (1 + rng.random((E, d // 128)))).astype(np.float32)
+    bgu = np.repeat(cgu[:, :, None], d // 128, axis=2)
+    bdn = np.repeat(cdn[:, :, None], F // 128, axis=2)
+    rgu = np.repeat(cgu, 128, axis=1)
+    rdn = np.repeat(cdn, 128, axis=1)
+    out_b, rb = oracle.forward_fp8(x, Wg, qgu, bgu, qdn, bdn, k, SCALE)
+    out_r, rr = oracle.forward_fp8(x, Wg, qgu, rgu, qdn, rdn, k, SCALE)
+    assert np.array_equal(rb.idx, rr.idx)
+    assert np.array_equal(out_b, out_r)
+
+
+def test_block_scale_acts_on_its_own_k_range_only():
+    """A zero scale on k-block j of every row block is the same layer as
+    zero codes in columns 128 j .. 128 j + 127 with unit scales; a zero scale
+    on row block m zeroes exactly that block's output channels of down."""
+    rng = np.random.default_rng(25)
+    T, d, E, F, k = 20, 384, 5, 256, 2
+    x, Wg, qgu, qdn = _fp8_layer(rng, T, d, E, F)
+    bgu = np.ones((E, 2 * F // 128, d // 128), np.float32)
+    bdn = np.ones((E, d // 128, F // 128), np.float32)
+    bgu[:, :, 1] = 0.0                                  # k columns 128..255 of gate_up
+    bdn[:, :, 0] = 0.0                                  # k columns 0..127 of down
+    zgu = qgu.copy()
+    zgu[:, :, 128:256] = 0
+    zdn = qdn.copy()
+    zdn[:, :, 0:128] = 0
+    out_b, _ = oracle.forward_fp8(x, Wg, qgu, bgu, qdn, bdn, k, SCALE)
+    out_z, _ = oracle.forward_fp8(x, Wg, zgu, np.ones((E, 2 * F), np.float32), zdn,
+                                  np.ones((E, d), np.float32), k, SCALE)
+    assert np.array_equal(out_b, out_z)
+    assert np.any(out_b != 0)
+    bdn2 = np.ones((E, d // 128, F // 128), np.float32)
+    bdn2[:, 2, :] = 0.0                                 # output channels 256..383
+    out_m, _ = oracle.forward_fp8(x, Wg, qgu, np.ones_like(bgu), qdn, bdn2, k, SCALE)
+    assert np.all(out_m[:, 256:384] == 0) and np.all(out_m[:, :256] != 0)
+
+
+def test_block_dequantisation_element_by_element():
+    """dequant_e4m3 with block scales against a per-element loop."""
+    rng = np.random.default_rng(26)
+    q = rng.integers(0, 256, (256, 384)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0                            # no NaN codes
+    s = rng.random((2, 3)).astype(np.float32)
+    w = oracle.dequant_e4m3(q, s)
+    lut = codecs.e4m3_bits_to_f64(np.arange(256, dtype=np.uint8))
+    for n in range(0, 256, 7):
+        for i in range(0, 384, 5):
+            assert w[n, i] == lut[q[n, i]] * float(s[n // 128, i // 128])
