@@ -63,3 +63,26 @@ def test_block_forward_graph(gpu_lib):
                                             inp["Ws_dn"], 8, inp["scale"], norm_weight=inp["norm_w"],
                                             norm_eps=1e-6, score_bias=inp["score_bias"], out=out,
                                             workspace=ws))
+
+
+@pytest.mark.parametrize("T", [40, 600], ids=["decode-kernels", "grouped-kernels"])
+def test_forward_fp8_block128_graph(gpu_lib, T):
+    c = dict(inputs.CONFIGS[9], T=T, d=512, E=32, F=256, seed=430 + T)
+    inp = inputs.make_inputs(c, device="cuda")
+    ws = hy.alloc_workspace(T, 512, 32, 8, 256, hy.WEIGHTS_FP8_E4M3)
+    out = torch.empty((T, 512), dtype=torch.float32, device="cuda")
+    _replays_match(lambda: hy.forward_fp8_block128(inp["x"], inp["W_gate"], inp["Wq_gu"], inp["s_gu"],
+                                                   inp["Wq_dn"], inp["s_dn"], 8, inp["scale"], out=out,
+                                                   workspace=ws))
+
+
+def test_block_forward_bf16_graph(gpu_lib):
+    c = dict(inputs.CONFIGS[5], T=64, d=512, E=32, F=128, seed=440)
+    inp = inputs.make_inputs(c, device="cuda")
+    res = inputs.make_residual(64, 512, 440, device="cuda")
+    ws = torch.empty(hy.block_workspace_size(64, 512, 32, 8, 128), dtype=torch.uint8, device="cuda")
+    out = torch.empty((64, 512), dtype=torch.bfloat16, device="cuda")
+    _replays_match(lambda: hy.block_forward_bf16(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], inp["Ws_gu"],
+                                                 inp["Ws_dn"], 8, inp["scale"], residual=res,
+                                                 norm_weight=inp["norm_w"], norm_eps=1e-6,
+                                                 score_bias=inp["score_bias"], out=out, workspace=ws))

@@ -1,5 +1,6 @@
 """GPU parity on a seeded sweep of small random shapes: the bf16 layer, the
-e4m3 layer and the full block, every token compared with the oracle.
+e4m3 layer (per-channel and 128 x 128 block scales) and the full block, every
+token compared with the oracle.
 
 The shapes are drawn once from a fixed generator, so every run tests the same
 cases.  About half of each kind is drawn to take the weight-streaming decode
@@ -50,6 +51,9 @@ def _draw(n, seed, esz, max_e=96):
 BF16_CASES = _draw(12, 2024, 2)
 FP8_CASES = _draw(6, 2025, 1)
 BLOCK_CASES = _draw(6, 2026, 2)
+# 128 x 128 block scales: d and d_ff in whole 256-element batches
+BLK128_CASES = [(T, 256 * ((d + 255) // 256), E, k, 256 * ((F + 255) // 256))
+                for T, d, E, k, F in _draw(6, 2027, 1)]
 
 
 def _ids(cases):
@@ -114,4 +118,22 @@ def test_sweep_block(gpu_lib, T, d, E, k, F):
     idx = idx.cpu().numpy()
     stats = check_routing(idx, w.cpu().numpy(), r, inp["scale"])
     stats.update(check_output(out.cpu().numpy(), ref, TOL_BF16, _set_eq(idx, r)))
+    print(T, d, E, k, F, stats)
+
+
+@pytest.mark.parametrize("T,d,E,k,F", BLK128_CASES, ids=_ids(BLK128_CASES))
+def test_sweep_fp8_block128(gpu_lib, T, d, E, k, F):
+    from sparse_moe_layer_wave_amd import hy3moe as hy
+    c = dict(inputs.CONFIGS[9], T=T, d=d, E=E, k=k, F=F, seed=800 + T)
+    inp = inputs.make_inputs(c, device="cpu")
+    dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
+    out, idx, w = hy.forward_fp8_block128(dev["x"], dev["W_gate"], dev["Wq_gu"], dev["s_gu"], dev["Wq_dn"],
+                                          dev["s_dn"], k, inp["scale"], return_routing=True)
+    torch.cuda.synchronize()
+    ref, r = oracle.forward_fp8(inputs.bits(inp["x"]), inp["W_gate"].numpy(), inputs.bits(inp["Wq_gu"]),
+                                inp["s_gu"].numpy(), inputs.bits(inp["Wq_dn"]), inp["s_dn"].numpy(),
+                                k, inp["scale"])
+    idx = idx.cpu().numpy()
+    stats = check_routing(idx, w.cpu().numpy(), r, inp["scale"])
+    stats.update(check_output_fp8_small(out.cpu().numpy(), ref, _set_eq(idx, r), TOL_FP8, T * k * F))
     print(T, d, E, k, F, stats)
