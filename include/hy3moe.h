@@ -161,13 +161,13 @@ int hy3moe_forward_fp8_timed(const uint16_t* x, const float* W_gate,
  * weight [e, n, i] = e4m3 value * sb[e, n/128, i/128] (row-major scale grids).
  * Activations are quantised per row as in hy3moe_forward_fp8.  Each 128-wide
  * k-block's fp8 MFMA product is scaled by its block's scale and added to the
- * fp32 accumulator, which is rescaled by the row scale at the end
- * (decode-sized batches on the weight-streaming kernels, larger ones on
- * grouped kernels with 128 x 128 tiles, one weight block per tile and
- * k-block).  d and d_ff must be
- * multiples of 256 and at most 16384 (HY3MOE_ERR_UNSUPPORTED otherwise); the
- * workspace is hy3moe_workspace_size with HY3MOE_WEIGHTS_FP8_E4M3.  Other
- * arguments as for hy3moe_forward_fp8. */
+ * fp32 accumulator, which is rescaled by the row scale at the end.
+ * Decode-sized batches run on the weight-streaming kernels; larger ones run on
+ * grouped kernels with 128 x 128 tiles, one weight block per tile and k-block.
+ * d and d_ff must be multiples of 256 and at most 16384
+ * (HY3MOE_ERR_UNSUPPORTED otherwise).  The workspace is
+ * hy3moe_workspace_size with HY3MOE_WEIGHTS_FP8_E4M3.  Other arguments as for
+ * hy3moe_forward_fp8. */
 int hy3moe_forward_fp8_block128(const uint16_t* x, const float* W_gate,
                                 const uint8_t* Wq_gate_up, const float* sb_gate_up,
                                 const uint8_t* Wq_down, const float* sb_down, float* out,
