@@ -66,6 +66,7 @@ def algorithmic(c, n_touched):
         "down": dict(bytes=n_touched * d * F * wb + rows * F * 2 + rows * d * 2,
                      flops=2 * rows * F * d),
         "router": dict(bytes=E * d * 4 + T * d * 2 + rows * 8, flops=2 * T * d * E),
+        # out: fp32, or bf16 out plus the bf16 residual read: 4 bytes per element either way
         "combine": dict(bytes=rows * d * 2 + T * k * 8 + T * d * 4, flops=2 * rows * d),
         "layer_flops": T * ((k + (1 if block else 0)) * 6 * d * F + 2 * d * E),
     }
@@ -121,10 +122,17 @@ def run_workload(cfg, steps, warmup, clock_probe_s=0.0):
     else:
         ws = hy3moe.alloc_workspace(T, d, E, k, F,
                                     hy3moe.WEIGHTS_FP8_E4M3 if fp8 else hy3moe.WEIGHTS_BF16)
-    out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    residual = c.get("residual", False)
+    out = torch.empty((T, d), dtype=torch.bfloat16 if residual else torch.float32, device="cuda")
     idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
 
     def step(evs=None, return_routing=False):
+        if residual:
+            return hy3moe.block_forward_bf16(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], inp["Ws_gu"],
+                                             inp["Ws_dn"], k, inp["scale"], residual=inp["residual"],
+                                             norm_weight=inp["norm_w"], norm_eps=1e-6,
+                                             score_bias=inp["score_bias"], out=out, workspace=ws,
+                                             stage_events=evs, return_routing=return_routing)
         if block:
             return hy3moe.block_forward(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], inp["Ws_gu"],
                                         inp["Ws_dn"], k, inp["scale"], norm_weight=inp["norm_w"],
@@ -349,7 +357,7 @@ def main():
         for key, cfg, bound in (("skewed", 3, "mfma"), ("fp8", 4, "mfma"), ("fp8_decode", 7, "hbm"),
                                 ("block_decode", 5, "hbm"), ("block_prefill", 6, "mfma"),
                                 ("skewed_decode", 8, "hbm"), ("fp8_block128_decode", 9, "hbm"),
-                                ("fp8_block128", 10, "mfma")):
+                                ("fp8_block128", 10, "mfma"), ("block_residual_prefill", 11, "mfma")):
             n = args.steps if bound == "hbm" else max(3, args.steps // 10)
             res, _ = run_workload(cfg, n, min(args.warmup, 2))
             line[key] = {

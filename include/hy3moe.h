@@ -257,6 +257,17 @@ int hy3moe_block_forward_bf16(const uint16_t* x, const uint16_t* norm_weight, fl
                               int32_t* topk_idx, float* topk_w,
                               void* workspace, size_t workspace_bytes);
 
+/* hy3moe_block_forward_bf16 with the six stage events of hy3moe_forward_timed. */
+int hy3moe_block_forward_bf16_timed(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,
+                                    const float* W_gate, const float* score_bias,
+                                    const uint16_t* W_gate_up, const uint16_t* W_down,
+                                    const uint16_t* Ws_gate_up, const uint16_t* Ws_down,
+                                    const uint16_t* residual, uint16_t* out,
+                                    int T, int d, int E, int k, int d_ff, float scale, void* stream,
+                                    int32_t* topk_idx, float* topk_w,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* const* stage_events);
+
 /* hy3moe_block_forward with the six stage events of hy3moe_forward_timed
  * (route_norm falls in the router stage). */
 int hy3moe_block_forward_timed(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,

@@ -423,6 +423,19 @@ int hy3moe_block_forward_bf16(const uint16_t* x, const uint16_t* norm_weight, fl
                         topk_w, workspace, workspace_bytes, nullptr, residual, out);
 }
 
+int hy3moe_block_forward_bf16_timed(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,
+                                    const float* W_gate, const float* score_bias,
+                                    const uint16_t* W_gate_up, const uint16_t* W_down,
+                                    const uint16_t* Ws_gate_up, const uint16_t* Ws_down,
+                                    const uint16_t* residual, uint16_t* out, int T, int d, int E,
+                                    int k, int d_ff, float scale, void* stream, int32_t* topk_idx,
+                                    float* topk_w, void* workspace, size_t workspace_bytes,
+                                    void* const* stage_events) {
+    return forward_bf16(x, norm_weight, norm_eps, W_gate, nullptr, score_bias, W_gate_up, W_down,
+                        Ws_gate_up, Ws_down, nullptr, T, d, E, k, d_ff, scale, stream, topk_idx,
+                        topk_w, workspace, workspace_bytes, stage_events, residual, out);
+}
+
 int hy3moe_block_forward_timed(const uint16_t* x, const uint16_t* norm_weight, float norm_eps,
                                const float* W_gate, const float* score_bias,
                                const uint16_t* W_gate_up, const uint16_t* W_down,

@@ -23,7 +23,8 @@ EXPORTS = (
     "hy3moe_forward_timed", "hy3moe_forward_fp8", "hy3moe_forward_fp8_timed",
     "hy3moe_forward_fp8_block128", "hy3moe_forward_fp8_block128_timed",
     "hy3moe_block_workspace_size", "hy3moe_route_ex", "hy3moe_block_forward",
-    "hy3moe_block_forward_timed", "hy3moe_block_forward_bf16", "hy3moe_quantize_rows_e4m3", "hy3moe_status_string",
+    "hy3moe_block_forward_timed", "hy3moe_block_forward_bf16", "hy3moe_block_forward_bf16_timed",
+    "hy3moe_quantize_rows_e4m3", "hy3moe_status_string",
     "hy3moe_last_hip_error",
 )
 
@@ -65,6 +66,7 @@ def lib():
                                              P, Z, P]
     L.hy3moe_block_forward_bf16.argtypes = [P, P, F, P, P, P, P, P, P, P, P, I, I, I, I, I, F, S, P,
                                             P, P, Z]
+    L.hy3moe_block_forward_bf16_timed.argtypes = L.hy3moe_block_forward_bf16.argtypes + [P]
     L.hy3moe_quantize_rows_e4m3.argtypes = [P, I, I, P, P, S]
     L.hy3moe_status_string.argtypes = [I]
     L.hy3moe_status_string.restype = ctypes.c_char_p
@@ -320,7 +322,7 @@ def block_forward(x, W_gate, W_gate_up, W_down, Ws_gate_up, Ws_down, k, scale, n
 
 def block_forward_bf16(x, W_gate, W_gate_up, W_down, Ws_gate_up, Ws_down, k, scale, residual=None,
                        norm_weight=None, norm_eps=1e-6, score_bias=None, out=None, workspace=None,
-                       return_routing=False):
+                       return_routing=False, stage_events=None):
     """hy3moe_block_forward_bf16: the block's output plus the bf16 residual
     (if given), summed in fp32 and rounded once to bf16.  Returns out bf16
     [T,d] (and (idx, w) if return_routing); out may be the residual tensor."""
@@ -350,11 +352,15 @@ def block_forward_bf16(x, W_gate, W_gate_up, W_down, Ws_gate_up, Ws_down, k, sca
     if workspace is None and T:
         workspace = torch.empty(max(block_workspace_size(T, d, E, k, F), 1), dtype=torch.uint8,
                                 device=x.device)
-    _check(lib().hy3moe_block_forward_bf16(
-        _ptr(x), _ptr(norm_weight), float(norm_eps), _ptr(W_gate), _ptr(score_bias), _ptr(W_gate_up),
-        _ptr(W_down), _ptr(Ws_gate_up), _ptr(Ws_down), _ptr(residual), _ptr(out), T, d, E, k, F,
-        float(scale), _stream(), _ptr(idx), _ptr(w), _ptr(workspace),
-        0 if workspace is None else workspace.numel()), "hy3moe_block_forward_bf16")
+    args = (_ptr(x), _ptr(norm_weight), float(norm_eps), _ptr(W_gate), _ptr(score_bias), _ptr(W_gate_up),
+            _ptr(W_down), _ptr(Ws_gate_up), _ptr(Ws_down), _ptr(residual), _ptr(out), T, d, E, k, F,
+            float(scale), _stream(), _ptr(idx), _ptr(w), _ptr(workspace),
+            0 if workspace is None else workspace.numel())
+    if stage_events is None:
+        _check(lib().hy3moe_block_forward_bf16(*args), "hy3moe_block_forward_bf16")
+    else:
+        _check(lib().hy3moe_block_forward_bf16_timed(*args, _event_array(stage_events)),
+               "hy3moe_block_forward_bf16_timed")
     return (out, idx, w) if return_routing else out
 
 

@@ -71,6 +71,9 @@ CONFIGS = {
             weights="fp8_block128", skew=False),
     10: dict(name="hy3_fp8_block128_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=10,
              weights="fp8_block128", skew=False),
+    # the full block ending the residual branch: bf16 output, residual added
+    11: dict(name="hy3_block_residual_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=11,
+             weights="bf16", skew=False, block=True, residual=True),
 }
 
 (_STREAM_X, _STREAM_WG, _STREAM_BIAS, _STREAM_WGU, _STREAM_WDN, _STREAM_NORM, _STREAM_SBIAS,
@@ -204,6 +207,8 @@ def make_inputs(cfg, device="cpu", T=None, with_experts=True):
             out["W_gu"], out["W_dn"] = make_experts_bf16(c["E"], c["d"], c["F"], c["seed"], device)
     if c.get("block", False):
         out.update(make_block_extras(c["d"], c["E"], c["F"], c["seed"], device))
+    if c.get("residual", False):
+        out["residual"] = make_residual(c["T"], c["d"], c["seed"], device)
     return out
 
 
