@@ -121,11 +121,13 @@ def _cpu_fp8_block_case(T, E, k, F, d, seed):
 
 @pytest.mark.parametrize("T,E,k,F,d", [(16, 64, 8, 256, 512), (1, 8, 2, 256, 256), (56, 24, 8, 256, 512),
                                        (300, 32, 8, 256, 512), (700, 48, 4, 512, 768),
-                                       (129, 16, 16, 256, 1024)])
+                                       (129, 16, 16, 256, 1024), (50, 1000, 4, 256, 256),
+                                       (3000, 1000, 2, 256, 256)])
 def test_fp8_block128_full_parity(gpu_lib, T, E, k, F, d):
-    """hy3moe_forward_fp8_block128 on every token: decode-sized batches and
-    larger ones (all on the weight-streaming kernels), one and two row groups,
-    d up to 8 k-blocks and k = 16."""
+    """hy3moe_forward_fp8_block128 on every token: decode-sized batches (the
+    weight-streaming kernels, one and two row groups) and larger ones (the
+    128 x 128 grouped kernels), d up to 8 k-blocks, k = 16, and 1000 experts
+    on both paths."""
     from sparse_moe_layer_wave_amd import hy3moe as hy
     inp = _cpu_fp8_block_case(T, E, k, F, d, seed=60 + T)
     dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
