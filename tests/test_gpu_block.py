@@ -245,3 +245,35 @@ def test_block_bf16_output_with_residual(gpu_lib, T, d, E, k, F):
     assert worst <= TOL_BF16 * rms, f"{worst:.3e} > {TOL_BF16} * rms {rms:.3e}"
     stats.update(excess_over_rounding=worst, rms_ref=rms)
     print(T, d, E, k, F, stats)
+
+
+def test_hy3_block_residual_T8192(gpu_lib):
+    """The bf16-output block with the residual at the Hy3 prefill size (the
+    grouped kernels): sampled tokens against the oracle's residual branch, and
+    every element bit for bit against the fp32 block output plus the residual
+    rounded once to bf16."""
+    from sparse_moe_layer_wave_amd import hy3moe as hy
+    inp = inputs.make_inputs(11, device="cuda")
+    c = inp["cfg"]
+    T, k = c["T"], c["k"]
+    kw = dict(norm_weight=inp["norm_w"], norm_eps=EPS, score_bias=inp["score_bias"])
+    args = (inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], inp["Ws_gu"], inp["Ws_dn"], k, inp["scale"])
+    out, idx, w = hy.block_forward_bf16(*args, residual=inp["residual"], return_routing=True, **kw)
+    out32 = hy.block_forward(*args, **kw)
+    expect = (out32 + inp["residual"].float()).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), expect.view(torch.int16))
+    r = _oracle_route(inp)
+    idx_np = idx.cpu().numpy()
+    stats = check_routing(idx_np, w.cpu().numpy(), r, inp["scale"])
+    sample = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(11).choice(T, 10, replace=False)]))
+    blk, rs = _oracle_block(inp, tokens=sample)
+    ref = blk + oracle.bf16_bits_to_f64(inputs.bits(inp["residual"])[sample])
+    set_eq = np.array([set(a) == set(b) for a, b in zip(idx_np[sample].tolist(), rs.idx.tolist())])
+    gpu = out.float().cpu().numpy().astype(np.float64)[sample]
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    excess = np.abs(gpu - ref) - 2.0 ** -8 * np.abs(gpu)      # allowance: the output's own bf16 rounding
+    worst = float(np.max(excess[set_eq])) if set_eq.any() else 0.0
+    assert worst <= TOL_BF16 * rms, f"{worst:.3e} > {TOL_BF16} * rms {rms:.3e}"
+    stats.update(excess_over_rounding=worst, rms_ref=rms)
+    print("block residual prefill", stats)
