@@ -44,16 +44,17 @@ itself, and anything that would need the real model's weights.
 
 from .codecs import (bf16_bits_to_f64, f32_to_bf16_bits, round_to_bf16, e4m3_bits_to_f64,
                      f32_to_e4m3_bits, E4M3_MAX)
-from .moe import (route, expert_swiglu, forward, forward_tokens, quant_row_e4m3,
-                  quant_rows_e4m3, dequant_e4m3, forward_fp8, forward_fp8_tokens, rms_norm_bf16,
-                  forward_block, forward_block_tokens, forward_block_residual,
-                  expert_param_count, flops_per_token,
-                  NEAR_TIE)
+from .moe import (route, expert_swiglu, expert_swiglu_parts, forward, forward_tokens,
+                  quant_row_e4m3, quant_row_e4m3_parts, quant_rows_e4m3, dequant_e4m3, forward_fp8,
+                  forward_fp8_tokens, rms_norm_bf16, forward_block, forward_block_tokens,
+                  forward_block_residual, forward_detail, forward_fp8_detail, Detail,
+                  expert_param_count, flops_per_token, NEAR_TIE)
 
 __all__ = [
     "bf16_bits_to_f64", "f32_to_bf16_bits", "round_to_bf16", "e4m3_bits_to_f64", "f32_to_e4m3_bits",
-    "E4M3_MAX", "route", "expert_swiglu", "forward", "forward_tokens",
-    "quant_row_e4m3", "quant_rows_e4m3", "dequant_e4m3", "forward_fp8", "forward_fp8_tokens",
-    "rms_norm_bf16", "forward_block", "forward_block_tokens", "forward_block_residual",
+    "E4M3_MAX", "route", "expert_swiglu", "expert_swiglu_parts", "forward", "forward_tokens",
+    "quant_row_e4m3", "quant_row_e4m3_parts", "quant_rows_e4m3", "dequant_e4m3", "forward_fp8",
+    "forward_fp8_tokens", "rms_norm_bf16", "forward_block", "forward_block_tokens",
+    "forward_block_residual", "forward_detail", "forward_fp8_detail", "Detail",
     "expert_param_count", "flops_per_token", "NEAR_TIE",
 ]

@@ -32,6 +32,14 @@ NEAR_TIE = 1e-6
 Route = namedtuple("Route", "idx w scores near_tie order_tie gap choice")
 
 
+def _weights_f64(w):
+    """An expert weight matrix as float64 values: bf16 bit patterns (uint16)
+    are decoded; an array that is already float64 (the same values, decoded
+    beforehand) is taken as it is."""
+    w = np.asarray(w)
+    return w if w.dtype == np.float64 else bf16_bits_to_f64(w)
+
+
 def _sigmoid64(z):
     with np.errstate(over="ignore"):
         return 1.0 / (1.0 + np.exp(-z))
@@ -100,6 +108,22 @@ def route(x_bits, W_gate, k, scale, logit_bias=None, block=4096, score_bias=None
     return Route(idx, w, scores, near_tie, order_tie, gap, choice)
 
 
+def _swiglu_act(x, W_gu, F):
+    """a = SiLU(x W_gate^T) * (x W_up^T) in float64, W_gu [2F, d] with the
+    gate rows first."""
+    g = x @ W_gu[:F].T
+    u = x @ W_gu[F:].T
+    return g * _sigmoid64(g) * u
+
+
+def expert_swiglu_parts(x, W_gu, W_dn):
+    """The two tensors a bf16 SwiGLU expert stores, each before its bf16
+    rounding (float64): h_pre = a [n, F] and y_pre = bf16(h_pre) W_dn^T
+    [n, d].  expert_swiglu's output is bf16(y_pre)."""
+    h_pre = _swiglu_act(x, W_gu, W_dn.shape[1])
+    return h_pre, round_to_bf16(h_pre) @ W_dn.T
+
+
 def expert_swiglu(x, W_gu, W_dn, bf16_activations=True):
     """One SwiGLU expert on rows x [n, d] (float64).
 
@@ -109,13 +133,9 @@ def expert_swiglu(x, W_gu, W_dn, bf16_activations=True):
     a = SiLU(x W_gate^T) * (x W_up^T), y = a W_dn^T ("DeepSeek V4-Flash
     architecture Q&A", Q4.5).  With bf16_activations, a and y are rounded to
     bf16 (the tensors a bf16 model stores); the products stay float64."""
-    F = W_dn.shape[1]
-    g = x @ W_gu[:F].T
-    u = x @ W_gu[F:].T
-    a = g * _sigmoid64(g) * u
     if bf16_activations:
-        return round_to_bf16(round_to_bf16(a) @ W_dn.T)
-    return a @ W_dn.T
+        return round_to_bf16(expert_swiglu_parts(x, W_gu, W_dn)[1])
+    return _swiglu_act(x, W_gu, W_dn.shape[1]) @ W_dn.T
 
 
 def forward(x_bits, W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias=None,
@@ -138,7 +158,7 @@ def forward(x_bits, W_gate, W_gu_bits, W_dn_bits, k, scale, logit_bias=None,
     x = bf16_bits_to_f64(x_bits)
     for e in np.unique(r.idx):
         t, j = np.nonzero(r.idx == e)          # a token picks an expert at most once
-        y = expert_swiglu(x[t], bf16_bits_to_f64(W_gu_bits[e]), bf16_bits_to_f64(W_dn_bits[e]),
+        y = expert_swiglu(x[t], _weights_f64(W_gu_bits[e]), _weights_f64(W_dn_bits[e]),
                           bf16_activations)
         out[t] += r.w[t, j][:, None] * y
     return out, r
@@ -201,9 +221,9 @@ def forward_block(x_bits, W_gate, W_gu_bits, W_dn_bits, Ws_gu_bits, Ws_dn_bits, 
     x = bf16_bits_to_f64(x_bits)
     for e in np.unique(r.idx):
         t, j = np.nonzero(r.idx == e)
-        y = expert_swiglu(x[t], bf16_bits_to_f64(W_gu_bits[e]), bf16_bits_to_f64(W_dn_bits[e]))
+        y = expert_swiglu(x[t], _weights_f64(W_gu_bits[e]), _weights_f64(W_dn_bits[e]))
         out[t] += r.w[t, j][:, None] * y
-    out += expert_swiglu(x, bf16_bits_to_f64(Ws_gu_bits), bf16_bits_to_f64(Ws_dn_bits))
+    out += expert_swiglu(x, _weights_f64(Ws_gu_bits), _weights_f64(Ws_dn_bits))
     return out, r
 
 
@@ -238,13 +258,21 @@ def quant_row_e4m3(v):
     r = float32(448 / amax), codes = e4m3(float32(v * r)) (nearest, ties to
     even, saturating) and scale s = float32(amax / 448); the dequantised row is
     codes * s.  Returns (uint8 codes, float32 scale)."""
+    q, s, _ = quant_row_e4m3_parts(v)
+    return q, s
+
+
+def quant_row_e4m3_parts(v):
+    """quant_row_e4m3 with the float32 values it rounds: returns (codes,
+    scale, scaled) where scaled = float32(v * r) (zeros for an all-zero
+    row), so codes = e4m3(scaled)."""
     v = np.asarray(v, dtype=np.float32)
     amax = np.max(np.abs(v)) if v.size else np.float32(0)
     if amax == 0:
-        return np.zeros(v.shape, dtype=np.uint8), np.float32(1.0)
+        return np.zeros(v.shape, dtype=np.uint8), np.float32(1.0), np.zeros(v.shape, np.float32)
     r = np.float32(E4M3_MAX) / np.float32(amax)
-    q = f32_to_e4m3_bits(v * r)
-    return q, np.float32(amax) / np.float32(E4M3_MAX)
+    scaled = v * r
+    return f32_to_e4m3_bits(scaled), np.float32(amax) / np.float32(E4M3_MAX), scaled
 
 
 def quant_rows_e4m3(M):
@@ -289,20 +317,40 @@ def forward_fp8(x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale, logit_bias=N
     out = np.zeros((T, d), dtype=np.float64)
     if T == 0:
         return out, r
-    qx, sx = quant_rows_e4m3(bf16_bits_to_f64(x_bits).astype(np.float32))
-    xd = e4m3_bits_to_f64(qx) * sx.astype(np.float64)[:, None]
-    F = Wq_dn.shape[2]
+    xd = _dequant_x_e4m3(x_bits)
     for e in np.unique(r.idx):
         t, j = np.nonzero(r.idx == e)
-        Wgu = dequant_e4m3(Wq_gu[e], s_gu[e])
-        Wdn = dequant_e4m3(Wq_dn[e], s_dn[e])
-        g = xd[t] @ Wgu[:F].T
-        u = xd[t] @ Wgu[F:].T
-        a = g * _sigmoid64(g) * u
-        qa, sa = quant_rows_e4m3(a.astype(np.float32))
-        ad = e4m3_bits_to_f64(qa) * sa.astype(np.float64)[:, None]
-        out[t] += r.w[t, j][:, None] * round_to_bf16(ad @ Wdn.T)
+        y_pre = _fp8_expert_parts(xd[t], Wq_gu[e], s_gu[e], Wq_dn[e], s_dn[e])[3]
+        out[t] += r.w[t, j][:, None] * round_to_bf16(y_pre)
     return out, r
+
+
+def _dequant_x_e4m3(x_bits):
+    """The bf16 rows quantised per row (quant_row_e4m3 of float32(x)) and
+    dequantised, float64."""
+    qx, sx = quant_rows_e4m3(bf16_bits_to_f64(x_bits).astype(np.float32))
+    return e4m3_bits_to_f64(qx) * sx.astype(np.float64)[:, None]
+
+
+def _fp8_expert_parts(xd, Wq_gu_e, s_gu_e, Wq_dn_e, s_dn_e):
+    """One e4m3 expert on dequantised x rows xd [n, d] (float64).
+
+    a = SiLU(xd Wg^T) * (xd Wu^T) with the dequantised weights; each row of
+    float32(a) is quantised with quant_row_e4m3 and dequantised; the expert
+    output before its bf16 rounding is y_pre = dequant(a) Wd^T.  Returns
+    (scaled float32 [n, F], the values quant_row_e4m3 rounds to e4m3;
+    s_a float32 [n], the rows' scales; a_deq float64 [n, F]; y_pre float64
+    [n, d])."""
+    Wdn = dequant_e4m3(Wq_dn_e, s_dn_e)
+    a = _swiglu_act(xd, dequant_e4m3(Wq_gu_e, s_gu_e), Wdn.shape[1])
+    n, F = a.shape
+    qa = np.empty((n, F), np.uint8)
+    sa = np.empty(n, np.float32)
+    scaled = np.empty((n, F), np.float32)
+    for i in range(n):
+        qa[i], sa[i], scaled[i] = quant_row_e4m3_parts(a[i].astype(np.float32))
+    ad = e4m3_bits_to_f64(qa) * sa.astype(np.float64)[:, None]
+    return scaled, sa, ad, ad @ Wdn.T
 
 
 def forward_fp8_tokens(tokens, x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale, logit_bias=None):
@@ -310,6 +358,71 @@ def forward_fp8_tokens(tokens, x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scal
     tokens = np.asarray(tokens, dtype=np.int64)
     return forward_fp8(np.asarray(x_bits)[tokens], W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale,
                        logit_bias)
+
+
+# ----------------------------------------------------------------------------- per-slot parts
+
+Detail = namedtuple("Detail", "tokens expert w h y scaled s_a a_deq")
+
+
+def forward_detail(tokens, x_bits, r, W_gu_bits, W_dn_bits, Ws_gu_bits=None, Ws_dn_bits=None):
+    """The per-slot terms of ``forward`` (of ``forward_block`` when the shared
+    expert's weights are given) for the listed tokens, each stored tensor
+    before its bf16 rounding.
+
+    r is ``route``'s result for the whole batch.  Slot j < k of token t is
+    expert r.idx[t, j] with weight r.w[t, j]; with a shared expert, slot k is
+    it, with weight 1 and expert id -1.  Returns Detail(tokens, expert int64
+    [n, S], w float64 [n, S], h float64 [n, S, F], y float64 [n, S, d], None,
+    None, None): h is the SwiGLU activation and y the expert output, both as
+    ``expert_swiglu_parts`` gives them.  The layer's row is sum_j w * bf16(y)."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    x = bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16)[tokens])
+    idx = r.idx[tokens]
+    n, k = idx.shape
+    shared = Ws_gu_bits is not None
+    S = k + (1 if shared else 0)
+    F = np.asarray(W_dn_bits[int(idx[0, 0])]).shape[-1] if n else 0
+    d = x.shape[1]
+    h = np.zeros((n, S, F))
+    y = np.zeros((n, S, d))
+    expert = np.full((n, S), -1, dtype=np.int64)
+    expert[:, :k] = idx
+    w = np.ones((n, S))
+    w[:, :k] = r.w[tokens]
+    for e in np.unique(idx):
+        ti, j = np.nonzero(idx == e)
+        h[ti, j], y[ti, j] = expert_swiglu_parts(x[ti], _weights_f64(W_gu_bits[e]),
+                                                 _weights_f64(W_dn_bits[e]))
+    if shared and n:
+        h[:, k], y[:, k] = expert_swiglu_parts(x, _weights_f64(Ws_gu_bits), _weights_f64(Ws_dn_bits))
+    return Detail(tokens, expert, w, h, y, None, None, None)
+
+
+def forward_fp8_detail(tokens, x_bits, r, Wq_gu, s_gu, Wq_dn, s_dn):
+    """The per-slot terms of ``forward_fp8`` for the listed tokens (r:
+    ``route``'s result for the whole batch; slot j is expert r.idx[t, j]).
+
+    Returns Detail(tokens, expert [n, k], w [n, k], None, y float64 [n, k, d],
+    scaled float32 [n, k, F], s_a float32 [n, k], a_deq float64 [n, k, F]):
+    scaled holds the values the activation quantiser rounds to e4m3, s_a the
+    activation rows' scales, a_deq the dequantised activations and y the
+    expert outputs before their bf16 rounding."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    xd = _dequant_x_e4m3(np.asarray(x_bits, dtype=np.uint16)[tokens])
+    idx = r.idx[tokens]
+    n, k = idx.shape
+    F = np.asarray(Wq_dn[int(idx[0, 0])]).shape[-1] if n else 0
+    d = xd.shape[1]
+    y = np.zeros((n, k, d))
+    scaled = np.zeros((n, k, F), np.float32)
+    s_a = np.zeros((n, k), np.float32)
+    a_deq = np.zeros((n, k, F))
+    for e in np.unique(idx):
+        ti, j = np.nonzero(idx == e)
+        scaled[ti, j], s_a[ti, j], a_deq[ti, j], y[ti, j] = _fp8_expert_parts(
+            xd[ti], Wq_gu[e], s_gu[e], Wq_dn[e], s_dn[e])
+    return Detail(tokens, idx.astype(np.int64), r.w[tokens].copy(), None, y, scaled, s_a, a_deq)
 
 
 # ----------------------------------------------------------------------------- accounting

@@ -148,3 +148,165 @@ def test_block_dequantisation_element_by_element():
     for n in range(0, 256, 7):
         for i in range(0, 384, 5):
             assert w[n, i] == lut[q[n, i]] * float(s[n // 128, i // 128])
+
+
+# ----------------------------------------------------------------------------- where the layer quantises
+#
+# One-hot expert weights make the FP8 layer a closed form.  Gate row f of
+# expert e picks one x column, ig[e, f], with one e4m3 code and a power-of-two
+# row scale, so g = dequant(x)[ig] * w_g exactly (likewise u); down row c
+# picks one activation column, fd[e, c], so y_c = dequant(a)[fd] * w_d
+# exactly.  The expected output is then written with torch's e4m3 cast and
+# scipy's sigmoid, independently of the oracle's codecs: x quantised per
+# token row, the float32 activation a quantised per (token, slot) row,
+# r = float32(448 / amax), codes = e4m3(float32(a * r)), scale
+# float32(amax / 448), dequantised as codes * scale ("DeepSeek V4-Flash
+# architecture Q&A", Q7.2 and Q7.4).  Mutant copies of the oracle that move
+# or drop either quantisation must fail the same check.
+
+def _torch_e4m3(v32):
+    """torch's float8_e4m3fn cast of float32 values clipped to +-448: (codes, values)."""
+    t = torch.from_numpy(np.clip(np.asarray(v32, np.float32), -448.0, 448.0)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy(), t.to(torch.float64).numpy()
+
+
+def _torch_e4m3_value(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _torch_quant_rows(M32):
+    """Dequantised per-row e4m3 quantisation of float32 rows (numpy float32
+    arithmetic for r, v * r and the scale; torch for the rounding)."""
+    M32 = np.asarray(M32, np.float32)
+    out = np.zeros(M32.shape)
+    for i, v in enumerate(M32):
+        amax = np.max(np.abs(v))
+        if amax == 0:
+            continue
+        r = np.float32(448.0) / amax
+        _, vals = _torch_e4m3(v * r)
+        out[i] = vals * np.float64(amax / np.float32(448.0))
+    return out
+
+
+def _bf16_nearest(v):
+    """Nearest bf16 value (8 significant bits, ties to even) via frexp."""
+    m, e = np.frexp(np.asarray(v, np.float64))
+    return np.ldexp(np.round(m * 256.0), e - 8)          # np.round: half to even; m * 256 exact
+
+
+def _one_hot_fp8_layer(seed, x_exact):
+    rng = np.random.default_rng(seed)
+    T, d, E, F = 12, 128, 3, 64
+    if x_exact:
+        # rows of e4m3 values times 2^m whose largest magnitude is 448 * 2^m:
+        # quantising them is exact, so the layer sees x itself
+        codes = rng.integers(0x20, 0x7E, (T, d)).astype(np.uint8) | (rng.integers(0, 2, (T, d)) << 7).astype(np.uint8)
+        codes[:, 5] = 0x7E
+        xv = _torch_e4m3_value(codes) * np.ldexp(1.0, rng.integers(-9, -5, T))[:, None]
+    else:
+        xv = rng.standard_normal((T, d))
+    x = codecs.f32_to_bf16_bits(xv.astype(np.float32))
+    assert not x_exact or np.array_equal(codecs.bf16_bits_to_f64(x), xv)
+    Wg = (rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32)
+    sel = lambda n, hi: rng.integers(0, hi, n)
+    wcode = lambda n: (rng.integers(0x30, 0x48, n) | (rng.integers(0, 2, n) << 7)).astype(np.uint8)
+    ig, iu, fd = sel((E, F), d), sel((E, F), d), sel((E, d), F)
+    cg, cu, cd = wcode((E, F)), wcode((E, F)), wcode((E, d))
+    pg, pu, pd = (rng.integers(-4, 0, s).astype(np.float64) for s in ((E, F), (E, F), (E, d)))
+    Wq_gu = np.zeros((E, 2 * F, d), np.uint8)
+    Wq_dn = np.zeros((E, d, F), np.uint8)
+    ee, ff = np.meshgrid(np.arange(E), np.arange(F), indexing="ij")
+    Wq_gu[ee, ff, ig] = cg
+    Wq_gu[ee, F + ff, iu] = cu
+    ec, cc = np.meshgrid(np.arange(E), np.arange(d), indexing="ij")
+    Wq_dn[ec, cc, fd] = cd
+    s_gu = np.concatenate([np.ldexp(1.0, pg.astype(int)), np.ldexp(1.0, pu.astype(int))], axis=1).astype(np.float32)
+    s_dn = np.ldexp(1.0, pd.astype(int)).astype(np.float32)
+    layer = dict(x=x, Wg=Wg, Wq_gu=Wq_gu, s_gu=s_gu, Wq_dn=Wq_dn, s_dn=s_dn, k=E)
+    # ---- the closed form
+    from scipy.special import expit
+    x64 = codecs.bf16_bits_to_f64(x)
+    xd = x64 if x_exact else _torch_quant_rows(x64.astype(np.float32))
+    wg = _torch_e4m3_value(cg) * s_gu[:, :F]
+    wu = _torch_e4m3_value(cu) * s_gu[:, F:]
+    wd = _torch_e4m3_value(cd) * s_dn
+    g = xd[:, ig] * wg[None]                                 # [T, E, F], exact
+    u = xd[:, iu] * wu[None]
+    a32 = (g * expit(g) * u).astype(np.float32)
+    ad = _torch_quant_rows(a32.reshape(T * E, F)).reshape(T, E, F)
+    y = np.take_along_axis(ad, np.broadcast_to(fd[None], (T, E, d)), axis=2) * wd[None]   # exact
+    s = expit(x64 @ Wg.astype(np.float64).T).astype(np.float32).astype(np.float64)
+    w = np.float64(np.float32(SCALE)) * s / s.sum(axis=1, keepdims=True)
+    expect = np.einsum("te,tec->tc", w, _bf16_nearest(y))
+    return layer, expect
+
+
+def _fp8_closed_form_holds(forward_fp8, seed, x_exact):
+    L, expect = _one_hot_fp8_layer(seed, x_exact)
+    out, _ = forward_fp8(L["x"], L["Wg"], L["Wq_gu"], L["s_gu"], L["Wq_dn"], L["s_dn"], L["k"], SCALE)
+    return bool(np.max(np.abs(out - expect)) <= 1e-12 * np.max(np.abs(expect)))
+
+
+def _mutant_fp8(kind):
+    """A scratch copy of the oracle's FP8 layer with one deliberate change:
+    no_h_quant (the down product takes float64 a), h_bf16_first (a rounded to
+    bf16 before its quantisation), h_per_token (one scale over a token's k
+    activation rows), no_x_quant (the gate_up product takes x itself).  The
+    scale's exact float32 value is pinned by the quantiser tests above: a
+    one-ulp change of it does not survive the bf16 rounding of y."""
+    def fwd(x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale):
+        r = oracle.route(x_bits, W_gate, k, scale)
+        x = codecs.bf16_bits_to_f64(x_bits)
+        T, F = x.shape[0], Wq_dn.shape[2]
+        if kind == "no_x_quant":
+            xd = x
+        else:
+            qx, sx = oracle.quant_rows_e4m3(x.astype(np.float32))
+            xd = codecs.e4m3_bits_to_f64(qx) * sx.astype(np.float64)[:, None]
+        a = np.zeros((T, k, F))
+        for e in np.unique(r.idx):
+            t, j = np.nonzero(r.idx == e)
+            Wgu = oracle.dequant_e4m3(Wq_gu[e], s_gu[e])
+            g, u = xd[t] @ Wgu[:F].T, xd[t] @ Wgu[F:].T
+            a[t, j] = g / (1.0 + np.exp(-g)) * u
+        if kind == "no_h_quant":
+            ad = a
+        elif kind == "h_per_token":
+            ad = np.stack([_oracle_deq_rows(a[t].reshape(1, -1)).reshape(k, F) for t in range(T)])
+        else:
+            src = codecs.round_to_bf16(a) if kind == "h_bf16_first" else a
+            ad = _oracle_deq_rows(src.reshape(T * k, F)).reshape(T, k, F)
+        out = np.zeros(x.shape)
+        for e in np.unique(r.idx):
+            t, j = np.nonzero(r.idx == e)
+            y = ad[t, j] @ oracle.dequant_e4m3(Wq_dn[e], s_dn[e]).T
+            out[t] += r.w[t, j][:, None] * codecs.round_to_bf16(y)
+        return out, r
+    return fwd
+
+
+def _oracle_deq_rows(M):
+    q, s = oracle.quant_rows_e4m3(np.asarray(M, np.float32))
+    return codecs.e4m3_bits_to_f64(q) * s.astype(np.float64)[:, None]
+
+
+def test_fp8_quantisation_placement_closed_form():
+    """The oracle's FP8 layer equals the one-hot closed form, with x exactly
+    e4m3-representable (pins the activation quantisation alone) and with
+    general bf16 x (pins both quantisations)."""
+    for seed in (90, 91):
+        assert _fp8_closed_form_holds(oracle.forward_fp8, seed, x_exact=True)
+        assert _fp8_closed_form_holds(oracle.forward_fp8, seed, x_exact=False)
+
+
+def test_fp8_closed_form_rejects_moved_quantisations():
+    """Each mutant fails the closed-form check: the check is sharp enough to
+    catch a dropped or moved quantisation of either operand."""
+    for kind in ("no_h_quant", "h_bf16_first", "h_per_token"):
+        assert not _fp8_closed_form_holds(_mutant_fp8(kind), 90, x_exact=True), kind
+    # x itself is exact in the first form, so dropping its quantisation needs the second
+    assert _fp8_closed_form_holds(_mutant_fp8("no_x_quant"), 90, x_exact=True)
+    assert not _fp8_closed_form_holds(_mutant_fp8("no_x_quant"), 90, x_exact=False)
+    # the scratch copy itself, unmutated in effect, agrees with the closed form
+    assert _fp8_closed_form_holds(_mutant_fp8("none"), 90, x_exact=False)
