@@ -23,7 +23,9 @@
  *     size_t* out-parameters of the *_workspace_size calls and the
  *     stage_events arrays of the *_timed calls (host).  The library never
  *     allocates, frees or synchronises; it keeps no state between calls apart
- *     from a thread-local copy of the last HIP error.
+ *     from a thread-local copy of the last HIP error and a per-device cache
+ *     of the compute-unit count (queried on a device's first launch; safe to
+ *     fill from several threads at once).
  *   - Layouts are dense and row-major.  bf16 = uint16_t bit patterns;
  *     e4m3 = uint8_t codes of the OCP E4M3FN format (bias 7, max 448, no inf).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
@@ -87,12 +89,17 @@ int hy3moe_route(const uint16_t* x, const float* W_gate, const float* logit_bias
  * expert, i.e. expert-contiguous rows, ascending token inside an expert (the
  * grouping the per-expert loop of "DeepSeek V4-Flash architecture Q&A", Q8.4,
  * performs, laid out for grouped GEMMs).
- *   topk_idx  int32 [T, k] in (every entry in [0, E); a token lists an expert at most once)
+ *   topk_idx  int32 [T, k] in: the experts of each token
  *   counts    int32 [E] out: pairs per expert
- *   offsets   int32 [E+1] out: exclusive prefix sum of counts (offsets[E] = T*k)
+ *   offsets   int32 [E+1] out: exclusive prefix sum of counts (offsets[E] =
+ *             the number of pairs given a row, T*k for a valid routing)
  *   row_of    int32 [T, k] out: row of pair (t, j) in expert-contiguous order
- *   token_of  int32 [T*k] out: token of each row
- * Entries outside [0, E) are not detected and give undefined results. */
+ *   token_of  int32 [T*k] out: token of each row; entries from offsets[E] on
+ *             are not written
+ * Entries are checked on the device: a pair whose expert is outside [0, E),
+ * or repeats an expert listed earlier in the same token's row, is dropped --
+ * it is counted for no expert and gets row_of = -1 -- and the other pairs
+ * keep the order above.  Nothing is read or written out of bounds. */
 int hy3moe_permute(const int32_t* topk_idx, int T, int E, int k,
                    int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* token_of,
                    void* workspace, size_t workspace_bytes, void* stream);
@@ -278,7 +285,10 @@ int hy3moe_block_forward_timed(const uint16_t* x, const uint16_t* norm_weight, f
                                int32_t* topk_idx, float* topk_w,
                                void* workspace, size_t workspace_bytes, void* const* stage_events);
 
-/* Per-row e4m3 quantisation used by hy3moe_forward_fp8 for x:
+/* Per-row e4m3 quantisation used by hy3moe_forward_fp8 for x ("DeepSeek
+ * V4-Flash architecture Q&A", Q7.2: the E4M3 format, range +-448, for forward
+ * activations; Q7.4: scaling factors per channel; here one fp32 scale per
+ * activation row):
  *   amax = max |x[r, :]|;  amax == 0 -> q = 0, s = 1;  otherwise
  *   r = fp32(448 / amax), q = e4m3(fp32(x * r)) rounded to nearest even and
  *   saturated to +-448, s = fp32(amax / 448); the row dequantises as q * s.

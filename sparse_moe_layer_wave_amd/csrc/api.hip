@@ -3,8 +3,33 @@
 // the host before anything is enqueued; the library never allocates, frees or
 // synchronises.
 
+#include <atomic>
+
 #include "../../include/hy3moe.h"
 #include "internal.h"
+
+namespace hy3 {
+
+hipError_t device_cu_count(int* cus) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];   // 0: not yet queried
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) {
+            *cus = v;
+            return hipSuccess;
+        }
+    }
+    err = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err == hipSuccess && dev >= 0 && dev < kMaxDevices && *cus > 0)
+        cache[dev].store(*cus, std::memory_order_relaxed);
+    return err;
+}
+
+}  // namespace hy3
 
 namespace {
 
@@ -175,7 +200,7 @@ int hy3moe_permute(const int32_t* topk_idx, int T, int E, int k, int32_t* counts
     e = hy3::launch_dispatch(topk_idx, T, E, k, L.nb, blk_counts,
                              reinterpret_cast<int32_t*>(ws + L.blk_base), counts, offsets,
                              reinterpret_cast<int32_t*>(ws + L.tile_off), hy3::prefill_bm(), row_of,
-                             token_of, 0, s);
+                             token_of, 0, s, true);
     return hip_status(e);
 }
 

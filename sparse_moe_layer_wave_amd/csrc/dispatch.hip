@@ -16,7 +16,12 @@
 //                  that chose e).
 // A batch of one routing block (T <= 64) does all three in one workgroup
 // (k_dispatch_one).  All of it is integer work with no atomics whose order
-// matters, so the result is the same on every run.  With the shared expert of the full block
+// matters, so the result is the same on every run.
+//
+// A routing the caller supplies (hy3moe_permute) is checked as it is read
+// (the CHECKED instances): a pair whose expert is outside [0, E), or repeats
+// an expert listed earlier for the same token, takes no row (row_of = -1) and
+// is counted for no expert.  The router's own routing needs no check.  With the shared expert of the full block
 // ("Tencent Hy3-Flash Q&A", Q4.7), it becomes expert E, whose rows are
 // T*k + t, one per token: the GEMMs then treat it like any routed expert.
 
@@ -24,6 +29,18 @@
 
 namespace hy3 {
 namespace {
+
+// Whether pair j of a token row is dispatched: always for the router's own
+// routing; for a caller's, only an expert in [0, E) not listed earlier in the
+// row.
+template <bool CHECKED>
+__device__ __forceinline__ bool pair_ok(const int32_t* __restrict__ row, int j, int e, int E) {
+    if constexpr (!CHECKED) return true;
+    if (e < 0 || e >= E) return false;
+    for (int i = 0; i < j; ++i)
+        if (row[i] == e) return false;
+    return true;
+}
 
 // Exclusive scan over one workgroup of 256 threads; returns the total.
 __device__ int block_exclusive_scan(int v, int* lds /* >= 256 + 1 ints */, int& excl) {
@@ -110,6 +127,7 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
 
 // shared_row0 >= 0: the shared expert's rows start there, one per token in
 // token order.
+template <bool CHECKED>
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx, int T, int E,
                                                 int k, int nb,
                                                 const int32_t* __restrict__ blk_base,
@@ -124,7 +142,11 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
     for (int p = threadIdx.x; p < npairs; p += 256) {
         const int tl = p / k;
         const int t = b * kRouteBlock + tl;
-        if (t < T) atomicOr(&mask[idx[static_cast<size_t>(t) * k + (p - tl * k)]], 1ull << tl);
+        if (t < T) {
+            const int32_t* row = idx + static_cast<size_t>(t) * k;
+            const int e = row[p - tl * k];
+            if (pair_ok<CHECKED>(row, p - tl * k, e, E)) atomicOr(&mask[e], 1ull << tl);
+        }
     }
     __syncthreads();
     for (int p = threadIdx.x; p < npairs; p += 256) {
@@ -133,6 +155,10 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
         if (t < T) {
             const size_t pair = static_cast<size_t>(t) * k + (p - tl * k);
             const int e = idx[pair];
+            if (!pair_ok<CHECKED>(idx + static_cast<size_t>(t) * k, p - tl * k, e, E)) {
+                row_of[pair] = -1;
+                continue;
+            }
             const int rank = __popcll(mask[e] & ((1ull << tl) - 1ull));
             const int row = offsets[e] + blk_base[static_cast<size_t>(e) * nb + b] + rank;
             row_of[pair] = row;
@@ -150,6 +176,7 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ idx
 // A single routing block (T <= 64): counts, offsets, tile offsets and the
 // dispatch order in one workgroup of 1024 threads, the same results as
 // k_block_scan + k_offsets + k_scatter with nb = 1 (every block base is 0).
+template <bool CHECKED>
 __global__ __launch_bounds__(1024) void k_dispatch_one(const int32_t* __restrict__ idx, int T, int E,
                                                       int k, int extra, int bm,
                                                       int32_t* __restrict__ blk_base,
@@ -166,7 +193,11 @@ __global__ __launch_bounds__(1024) void k_dispatch_one(const int32_t* __restrict
     mask[tid] = 0ull;
     __syncthreads();
     const int npairs = T * k;
-    for (int p = tid; p < npairs; p += 1024) atomicOr(&mask[idx[p]], 1ull << (p / k));
+    for (int p = tid; p < npairs; p += 1024) {
+        const int t = p / k;
+        const int e = idx[p];
+        if (pair_ok<CHECKED>(idx + static_cast<size_t>(t) * k, p - t * k, e, E)) atomicOr(&mask[e], 1ull << t);
+    }
     __syncthreads();
     const int n = E + (extra > 0 ? 1 : 0);
     const int c = tid < E ? __popcll(mask[tid]) : (tid < n ? extra : 0);
@@ -199,6 +230,10 @@ __global__ __launch_bounds__(1024) void k_dispatch_one(const int32_t* __restrict
     for (int p = tid; p < npairs; p += 1024) {
         const int t = p / k;
         const int e = idx[p];
+        if (!pair_ok<CHECKED>(idx + static_cast<size_t>(t) * k, p - t * k, e, E)) {
+            row_of[p] = -1;
+            continue;
+        }
         const int row = s_off[e] + __popcll(mask[e] & ((1ull << t) - 1ull));
         row_of[p] = row;
         tok_of[row] = t;
@@ -206,7 +241,8 @@ __global__ __launch_bounds__(1024) void k_dispatch_one(const int32_t* __restrict
     if (shared_row0 >= 0 && tid < T) tok_of[shared_row0 + tid] = tid;
 }
 
-// Per-block counts when the routing comes from the caller (hy3moe_permute).
+// Per-block counts when the routing comes from the caller (hy3moe_permute),
+// checked as k_scatter<true> checks it.
 __global__ __launch_bounds__(256) void k_block_counts(const int32_t* __restrict__ idx, int T,
                                                      int E, int k, int nb,
                                                      int32_t* __restrict__ blk_counts) {
@@ -216,7 +252,11 @@ __global__ __launch_bounds__(256) void k_block_counts(const int32_t* __restrict_
     const int b = blockIdx.x;
     for (int p = threadIdx.x; p < kRouteBlock * k; p += 256) {
         const int t = b * kRouteBlock + p / k;
-        if (t < T) atomicAdd(&cnt[idx[static_cast<size_t>(t) * k + (p % k)]], 1);
+        if (t < T) {
+            const int32_t* row = idx + static_cast<size_t>(t) * k;
+            const int e = row[p % k];
+            if (pair_ok<true>(row, p % k, e, E)) atomicAdd(&cnt[e], 1);
+        }
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 256)
@@ -234,16 +274,18 @@ hipError_t launch_block_counts(const int32_t* idx, int T, int E, int k, int nb,
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
                            const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,
                            int32_t* offsets, int32_t* tile_off, int bm, int32_t* row_of,
-                           int32_t* tok_of, int shared, hipStream_t s) {
+                           int32_t* tok_of, int shared, hipStream_t s, bool checked) {
     if (nb == 1) {
-        hipLaunchKernelGGL(k_dispatch_one, dim3(1), dim3(1024), 0, s, idx, T, E, k, shared ? T : 0, bm,
+        auto kern = checked ? k_dispatch_one<true> : k_dispatch_one<false>;
+        hipLaunchKernelGGL(kern, dim3(1), dim3(1024), 0, s, idx, T, E, k, shared ? T : 0, bm,
                            blk_base, counts, offsets, tile_off, row_of, tok_of, shared ? T * k : -1);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(k_block_scan, dim3(E), dim3(256), 0, s, blk_counts, blk_base, counts, nb);
     hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, s, counts, E, shared ? T : 0, offsets,
                        tile_off, bm);
-    hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(256), 0, s, idx, T, E, k, nb, blk_base, offsets,
+    auto scatter = checked ? k_scatter<true> : k_scatter<false>;
+    hipLaunchKernelGGL(scatter, dim3(nb), dim3(256), 0, s, idx, T, E, k, nb, blk_base, offsets,
                        row_of, tok_of, shared ? T * k : -1);
     return hipGetLastError();
 }

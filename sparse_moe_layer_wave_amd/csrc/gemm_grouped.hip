@@ -503,9 +503,8 @@ hipError_t launch(Args g, int max_blocks, hipStream_t s) {
     g.npanel = GATE_UP ? (g.N + 255) / 256 : (g.N + 511) / 512;   // 512 weight rows per panel
     const long long units = static_cast<long long>(max_blocks) * g.npanel;
     if (units == 0) return hipSuccess;
-    int dev = 0, cus = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0;
+    const hipError_t err = device_cu_count(&cus);
     if (err != hipSuccess) return err;
     const long long cap = std::max(kXcds, cus / kXcds * kXcds);    // one workgroup per CU
     const int grid = static_cast<int>(std::min(cap, (units + kXcds - 1) / kXcds * kXcds));

@@ -74,6 +74,11 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Compute units of the current device.  The count is queried once per device
+// and kept for the life of the process (a table of atomics: concurrent first
+// calls store the same value), so a launch costs one hipGetDevice.
+hipError_t device_cu_count(int* cus);
+
 // Workspace carving, computed identically on the host for every entry point.
 struct Layout {
     size_t planes, partial, scores, blk_counts, blk_base, counts, offsets, tile_off, idx, w,
@@ -105,11 +110,13 @@ hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* w, int T, int d, f
                            uint16_t* xn, hipStream_t s);
 
 // shared = 1 appends expert E with every token as its rows (rows T*k + t),
-// so offsets and tile_off then hold E + 2 entries
+// so offsets and tile_off then hold E + 2 entries.  checked: the routing is
+// the caller's; pairs with an expert outside [0, E) or repeated within the
+// token's row take no row (row_of = -1) and are counted for no expert.
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
                            const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,
                            int32_t* offsets, int32_t* tile_off, int bm, int32_t* row_of,
-                           int32_t* tok_of, int shared, hipStream_t s);
+                           int32_t* tok_of, int shared, hipStream_t s, bool checked = false);
 
 // prefill-sized batches: MFMA grouped GEMMs over row blocks of prefill_bm() rows
 // (max_blocks bounds the number of row blocks, tile_off[E]).  E counts the

@@ -8,9 +8,11 @@ outputs).  The tolerances and their reasons:
   d terms), which moves a score by at most a quarter of that.
 * routing weights: |dw| <= 1e-5 * scale (the same score error divided by a
   sum of k scores, plus fp32 rounding of the division and scaling).
-* outputs: max |out_gpu - out_ref| <= tol * rms(out_ref), tol = 1e-2 with bf16
-  experts and 3e-2 with e4m3 experts, over the tokens whose chosen expert set
-  equals the oracle's.
+* outputs: |out_gpu - out_ref| <= tol * rms(out_ref) element by element,
+  tol = 1e-2 with bf16 experts and 3e-2 with e4m3 experts, over the tokens
+  whose chosen expert set equals the oracle's -- except where a stored
+  activation sits so close to a rounding boundary that the GPU's float32 value
+  may round to the other neighbour (check_output_flips).
 """
 
 import numpy as np
@@ -40,15 +42,22 @@ def check_routing(idx_gpu, w_gpu, r, scale):
 
 def expected_permutation(idx, E):
     """Stable counting sort of the (token, slot) pairs by expert, via NumPy's
-    stable argsort: rows of one expert contiguous, ascending token inside."""
+    stable argsort: rows of one expert contiguous, ascending token inside.
+    Pairs whose expert is outside [0, E) or repeats an expert earlier in the
+    token's row are dropped (row -1, no token_of entry), as hy3moe_permute
+    specifies for a caller's routing."""
     idx = np.asarray(idx, dtype=np.int64)
     T, k = idx.shape
-    flat = idx.reshape(-1)
-    order = np.argsort(flat, kind="stable")
-    counts = np.bincount(flat, minlength=E)
+    ok = (idx >= 0) & (idx < E)
+    for j in range(1, k):
+        ok[:, j] &= ~np.any(idx[:, :j] == idx[:, j:j + 1], axis=1)
+    flat = np.where(ok, idx, E).reshape(-1)
+    n = int(ok.sum())
+    order = np.argsort(flat, kind="stable")[:n]
+    counts = np.bincount(flat[order], minlength=E)[:E]
     offsets = np.concatenate([[0], np.cumsum(counts)])
-    row_of = np.empty(T * k, dtype=np.int64)
-    row_of[order] = np.arange(T * k)
+    row_of = np.full(T * k, -1, dtype=np.int64)
+    row_of[order] = np.arange(n)
     token_of = order // k
     return counts, offsets, row_of.reshape(T, k), token_of
 
@@ -58,18 +67,7 @@ def check_permutation(idx, E, counts, offsets, row_of, token_of):
     assert np.array_equal(np.asarray(counts), c)
     assert np.array_equal(np.asarray(offsets), o)
     assert np.array_equal(np.asarray(row_of), r)
-    assert np.array_equal(np.asarray(token_of), t)
-
-
-def check_output(out_gpu, out_ref, tol, valid=None):
-    out_gpu = np.asarray(out_gpu, dtype=np.float64)
-    rms = float(np.sqrt(np.mean(out_ref ** 2))) if out_ref.size else 0.0
-    if valid is None:
-        valid = np.ones(out_ref.shape[0], dtype=bool)
-    err = float(np.max(np.abs(out_gpu[valid] - out_ref[valid]))) if valid.any() else 0.0
-    assert np.all(np.isfinite(out_gpu))
-    assert err <= tol * rms, f"max|d| {err:.3e} > {tol} * rms {rms:.3e}"
-    return dict(max_abs=err, rms_ref=rms, ratio=err / rms if rms else 0.0)
+    assert np.array_equal(np.asarray(token_of)[:len(t)], t)
 
 
 class LazyExperts:
@@ -86,30 +84,180 @@ class LazyExperts:
         return self._bits(self._t[int(e)])
 
 
-def check_output_fp8_small(out_gpu, out_ref, valid, tol_max, n_act):
-    """Small-d_ff e4m3 cases.  Both sides quantise each (token, slot) SwiGLU
-    activation row to e4m3 from float32 values, but the GPU's float32
-    activation comes from another accumulation order and can sit a few float32
-    ulps away from the oracle's.  Where that straddles an e4m3 rounding
-    boundary, one activation takes the neighbouring code (one e4m3 step, 1/8 of
-    its size), and with only d_ff terms per output this moves that token's
-    outputs by up to several percent of rms.  The chance per activation is a
-    few ulps of 2^-23 against e4m3's 2^-3 spacing: below 1e-5.  So, with n_act
-    quantised activations (rows x d_ff): rms error <= 1e-2 * rms(ref); no
-    element beyond 5 * tol_max * rms(ref); and the elements beyond
-    tol_max * rms(ref) confined to at most max(2, 3e-5 * n_act) tokens."""
+# ----------------------------------------------------------------------------- rounding-boundary flips
+#
+# The layer stores three activations in narrow types, and the oracle rounds
+# each where the layer does: h (bf16, or e4m3 with a row scale) and y (bf16).
+# The GPU rounds its own float32 value of each, which differs from the
+# oracle's float64 one in the last bits (other summation order, hardware
+# exp2 / reciprocal).  Where the two fall on the two sides of a rounding
+# boundary the stored values differ by one step, and with weights near 0.35
+# one step of a large |y| is above 1e-2 * rms.  So an element may exceed the
+# bound only by flips available to it, each predicted from the oracle's own
+# pre-rounding values:
+#
+#   h (bf16 experts):  flippable if within ETA_H steps of a bf16 boundary, or
+#       within ETA_HA * max|h of its row| (the float32 error of a small h
+#       made of cancelling terms).  A flip moves y_c by |Wd[c, f]| * step.
+#   h (e4m3):  the value quantised, v = a * r, flippable if within ETA_Q steps
+#       of an e4m3 boundary or within ETA_QA * 448 (the row's largest v).  A
+#       flip moves y_c by |Wd[c, f]| * step * s_a, and the element may take it.
+#   y:  the GPU's float32 y may be off the oracle's pre-rounding y by D_c =
+#       the h flips above + ETA_Y * sum_f |Wd[c, f] * h_f| (float32 sums of F
+#       products and the scale multiplications); y flips if it lies within D_c
+#       of a bf16 boundary, moving the element by w * step(y).
+#
+# The ETA values are chosen from the GPU's float32 error with margin: the
+# gate and up sums over d terms carry about 2^-18 relative error, so h and v
+# carry about 2^-17 relative, which is 2^-9 of a bf16 step (2^-8 relative)
+# and 2^-13 of an e4m3 step (2^-4 relative) -- ETA_H and ETA_Q allow 2x and
+# 8x that; the float32 sum of F exact products carries far less than
+# ETA_Y = 2^-20 of the sum of the magnitudes of its terms.
+ETA_H = 2.0 ** -8
+ETA_HA = 2.0 ** -18
+ETA_Q = 2.0 ** -10
+ETA_QA = 2.0 ** -16
+ETA_Y = 2.0 ** -20
+
+
+def bf16_boundary(v):
+    """For float64 values: (distance to the nearest bf16 rounding boundary,
+    the larger bf16 step on either side of that boundary)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    m, e = np.frexp(np.where(a > 0, a, 2.0 ** -126))
+    step = np.ldexp(1.0, e - 8)                       # spacing of the binade [2^(e-1), 2^e)
+    lo = np.floor(a / step) * step                    # the bf16 value at or below a
+    at_pow2 = lo == np.ldexp(1.0, e - 1)
+    below = np.where(at_pow2, step / 2, step)         # spacing just below lo
+    dist = np.minimum(np.abs(a - (lo + step / 2)), np.abs(a - (lo - below / 2)))
+    return dist, step
+
+
+_E4M3_POS = None
+
+
+def e4m3_boundary(v):
+    """For float32 / float64 values on the e4m3 scale: (distance to the
+    nearest e4m3 rounding boundary, the larger e4m3 step beside it).  Values
+    beyond 448 saturate and have no boundary above."""
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        from oracle import codecs
+        vals = codecs.e4m3_bits_to_f64(np.arange(0x7F, dtype=np.uint8))
+        _E4M3_POS = np.unique(vals[np.isfinite(vals)])          # 0, 2^-9, ..., 448
+    grid = _E4M3_POS
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    i = np.clip(np.searchsorted(grid, a, side="right") - 1, 0, len(grid) - 1)
+    lo = grid[i]
+    hi = grid[np.minimum(i + 1, len(grid) - 1)]
+    prev = grid[np.maximum(i - 1, 0)]
+    up = np.where(hi > lo, (lo + hi) / 2, np.inf)
+    down = np.where(lo > prev, (prev + lo) / 2, -np.inf)
+    dist = np.minimum(np.abs(a - up), np.abs(a - down))
+    return dist, np.maximum(hi - lo, lo - prev)
+
+
+def flip_allowance(det, W_dn_of, fp8):
+    """Per element of the detail's tokens [n, d]: how far the GPU's output may
+    move from the oracle's through predicted rounding-boundary flips.
+    W_dn_of(e) gives expert e's down matrix as float64 [d, F] (e = -1: the
+    shared expert)."""
+    n, S = det.expert.shape
+    d = det.y.shape[2]
+    A = np.zeros((n, d))
+    for e in np.unique(det.expert):
+        ti, j = np.nonzero(det.expert == e)
+        Wd = np.abs(W_dn_of(int(e)))                  # [d, F]
+        if fp8:
+            v = det.scaled[ti, j].astype(np.float64)
+            dist, step = e4m3_boundary(v)
+            flag = (dist <= ETA_Q * step) | (dist <= ETA_QA * 448.0)
+            C = (flag * step * det.s_a[ti, j].astype(np.float64)[:, None]) @ Wd.T
+            D = C + ETA_Y * (np.abs(det.a_deq[ti, j]) @ Wd.T)
+        else:
+            h = det.h[ti, j]
+            dist, step = bf16_boundary(h)
+            flag = (dist <= ETA_H * step) | (dist <= ETA_HA * np.max(np.abs(h), axis=1, keepdims=True))
+            C = np.zeros((len(ti), d))
+            from oracle import codecs
+            D = (flag * step) @ Wd.T + ETA_Y * (np.abs(codecs.round_to_bf16(h)) @ Wd.T)
+        ydist, ystep = bf16_boundary(det.y[ti, j])
+        np.add.at(A, ti, det.w[ti, j][:, None] * (C + ystep * (ydist <= D)))
+    return A
+
+
+def check_output_flips(out_gpu, out_ref, valid, tol, detail=None, W_dn_of=None, fp8=False,
+                       out_bf16=False):
+    """Every element of every valid token: |out_gpu - out_ref| <= tol * rms
+    + A, where A is the flip allowance of the element (zero unless one of its
+    stored activations lies at a rounding boundary) and, for a bf16 output
+    (out_bf16), half a bf16 step of the output's own rounding.
+
+    valid: tokens whose expert set equals the oracle's (None: all).
+    detail(tokens): the oracle's per-slot parts of those tokens
+    (oracle.forward_detail / forward_fp8_detail); only called for tokens with
+    an element beyond the bound.  W_dn_of: as for flip_allowance."""
     out_gpu = np.asarray(out_gpu, dtype=np.float64)
+    T = out_ref.shape[0]
     if valid is None:
-        valid = np.ones(out_ref.shape[0], dtype=bool)
-    d = np.abs(out_gpu[valid] - out_ref[valid])
-    rms = float(np.sqrt(np.mean(out_ref ** 2)))
-    rms_err = float(np.sqrt(np.mean(d ** 2)))
-    beyond = d > tol_max * rms
-    n_tok = int(np.count_nonzero(beyond.any(axis=1)))
-    allowed = max(2, int(3e-5 * n_act))
+        valid = np.ones(T, dtype=bool)
     assert np.all(np.isfinite(out_gpu))
-    assert rms_err <= 1e-2 * rms, f"rms error {rms_err:.3e} > 1e-2 * rms {rms:.3e}"
-    assert n_tok <= allowed, f"{n_tok} tokens with elements beyond {tol_max} * rms (allowed {allowed})"
-    assert d.max() <= 5 * tol_max * rms, f"max|d| {d.max():.3e} > {5 * tol_max} * rms"
-    return dict(max_abs=float(d.max()), rms_ref=rms, ratio=float(d.max()) / rms,
-                rms_err_ratio=rms_err / rms, tokens_beyond=n_tok, frac_beyond=float(np.mean(beyond)))
+    rms = float(np.sqrt(np.mean(out_ref ** 2))) if out_ref.size else 0.0
+    diff = np.abs(out_gpu - out_ref)
+    base = np.full(out_ref.shape, tol * rms)
+    if out_bf16:
+        base = base + 0.5 * bf16_boundary(np.maximum(np.abs(out_ref), np.abs(out_gpu)))[1]
+    over = (diff > base) & valid[:, None]
+    toks = np.nonzero(over.any(axis=1))[0]
+    stats = dict(rms_ref=rms, max_ratio=float(diff[valid].max() / rms) if valid.any() and rms else 0.0,
+                 elems_over_tol=int(over.sum()), tokens_over_tol=int(len(toks)), tokens=int(valid.sum()))
+    if len(toks):
+        assert detail is not None, f"{len(toks)} tokens beyond {tol} * rms and no flip model given"
+        A = flip_allowance(detail(toks), W_dn_of, fp8)
+        excess = diff[toks] - base[toks]
+        bad = over[toks] & (excess > A)
+        assert not bad.any(), (f"{int(bad.sum())} elements beyond {tol} * rms not explained by rounding "
+                               f"flips (worst excess {float(excess[bad].max()):.3e}, rms {rms:.3e})")
+        stats["max_excess_over_allowance"] = float(np.max(np.where(over[toks], excess / np.maximum(A, 1e-300), 0)))
+    return stats
+
+
+def bf16_flip_model(x_bits, r, W_gu, W_dn, Ws_gu=None, Ws_dn=None):
+    """check_output_flips keywords for bf16 experts: the oracle's per-slot
+    parts under its routing r (of the same token rows as x_bits), and the
+    experts' down matrices.  W_gu / W_dn index by expert to bf16 bit patterns
+    (arrays or LazyExperts); Ws_*: the shared expert, if any."""
+    import oracle
+
+    def W_dn_of(e):
+        return oracle.bf16_bits_to_f64(Ws_dn if e < 0 else W_dn[e])
+
+    return dict(detail=lambda toks: oracle.forward_detail(toks, x_bits, r, W_gu, W_dn, Ws_gu, Ws_dn),
+                W_dn_of=W_dn_of)
+
+
+def fp8_flip_model(x_bits, r, Wq_gu, s_gu, Wq_dn, s_dn):
+    """check_output_flips keywords for e4m3 experts (per-channel or 128 x 128
+    block scales)."""
+    import oracle
+    return dict(detail=lambda toks: oracle.forward_fp8_detail(toks, x_bits, r, Wq_gu, s_gu, Wq_dn, s_dn),
+                W_dn_of=lambda e: oracle.dequant_e4m3(Wq_dn[e], s_dn[e]), fp8=True)
+
+
+def set_equal(idx_gpu, r):
+    """Tokens whose GPU expert set equals the oracle's."""
+    return np.array([set(a) == set(b) for a, b in zip(np.asarray(idx_gpu).tolist(), r.idx.tolist())],
+                    dtype=bool)
+
+
+def stratified_tokens(idx, E, block=128):
+    """Tokens covering every (expert, 128-row block) of the expert-contiguous
+    row order the routing idx gives: the token of each block's first and last
+    row (the last block of an expert may be partial), plus the batch's first
+    and last token."""
+    _, offsets, _, token_of = expected_permutation(idx, E)
+    picks = [0, len(idx) - 1]
+    for e in range(E):
+        for b0 in range(offsets[e], offsets[e + 1], block):
+            picks += [token_of[b0], token_of[min(b0 + block, offsets[e + 1]) - 1]]
+    return np.unique(np.asarray(picks, dtype=np.int64))

@@ -1,14 +1,17 @@
 """GPU parity of the e4m3 expert path (through the C ABI) against the oracle's
 FP8 definition: the x row quantiser bit-exactly, the whole layer within
-3e-2 * rms(ref) on small cases and on sampled tokens of the Hy3 FP8 workloads
-(prefill-sized grouped kernels and the decode-sized weight-streaming ones)."""
+3e-2 * rms(ref) element by element on every token (check_output_flips: an
+element may exceed the bound only by the e4m3 and bf16 rounding-boundary
+flips the oracle's own values allow), on small cases and on the Hy3 FP8
+workloads (prefill-sized grouped kernels and the decode-sized
+weight-streaming ones)."""
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from parity import LazyExperts, check_output, check_output_fp8_small, check_routing
+from parity import LazyExperts, check_output_flips, check_routing, fp8_flip_model, set_equal
 from sparse_moe_layer_wave_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -33,6 +36,21 @@ def _cpu_fp8_case(T, E, k, F, d=512, seed=40):
     return inputs.make_inputs(c, device="cpu")
 
 
+def _compare_cpu_case(inp, out, idx, w):
+    """Routing and every output element of a CPU-drawn e4m3 case against the
+    oracle (per-channel or block scales: the oracle's dequantisation reads
+    the scale array's shape)."""
+    c = inp["cfg"]
+    args = (inputs.bits(inp["Wq_gu"]), inp["s_gu"].numpy(), inputs.bits(inp["Wq_dn"]), inp["s_dn"].numpy())
+    x_bits = inputs.bits(inp["x"])
+    ref, r = oracle.forward_fp8(x_bits, inp["W_gate"].numpy(), *args, c["k"], inp["scale"])
+    idx = idx.cpu().numpy()
+    stats = check_routing(idx, w.cpu().numpy(), r, inp["scale"])
+    stats.update(check_output_flips(out.cpu().numpy(), ref, set_equal(idx, r), TOL_FP8,
+                                    **fp8_flip_model(x_bits, r, *args)))
+    return stats
+
+
 def _run_fp8(inp):
     from sparse_moe_layer_wave_amd import hy3moe as hy
     c = inp["cfg"]
@@ -48,14 +66,8 @@ def _run_fp8(inp):
                                      (700, 48, 8, 128)])
 def test_fp8_small_full_parity(gpu_lib, T, E, k, F):
     inp = _cpu_fp8_case(T, E, k, F)
-    c = inp["cfg"]
     out, idx, w = _run_fp8(inp)
-    ref, r = oracle.forward_fp8(inputs.bits(inp["x"]), inp["W_gate"].numpy(), inputs.bits(inp["Wq_gu"]),
-                                inp["s_gu"].numpy(), inputs.bits(inp["Wq_dn"]), inp["s_dn"].numpy(),
-                                c["k"], inp["scale"])
-    stats = check_routing(idx.cpu().numpy(), w.cpu().numpy(), r, inp["scale"])
-    set_eq = np.array([set(a) == set(b) for a, b in zip(idx.cpu().numpy().tolist(), r.idx.tolist())])
-    stats.update(check_output_fp8_small(out.cpu().numpy(), ref, set_eq, TOL_FP8, T * k * F))
+    stats = _compare_cpu_case(inp, out, idx, w)
     print(T, E, k, F, stats)
 
 
@@ -67,14 +79,8 @@ def test_fp8_decode_path_full_parity(gpu_lib, T, E, k, F, d):
     kernels (the fifth case, d_ff = 384, takes the grouped kernels instead;
     the last, 19 rows per expert, two 16-row groups per pass)."""
     inp = _cpu_fp8_case(T, E, k, F, d=d, seed=42 + T)
-    c = inp["cfg"]
     out, idx, w = _run_fp8(inp)
-    ref, r = oracle.forward_fp8(inputs.bits(inp["x"]), inp["W_gate"].numpy(), inputs.bits(inp["Wq_gu"]),
-                                inp["s_gu"].numpy(), inputs.bits(inp["Wq_dn"]), inp["s_dn"].numpy(),
-                                c["k"], inp["scale"])
-    stats = check_routing(idx.cpu().numpy(), w.cpu().numpy(), r, inp["scale"])
-    set_eq = np.array([set(a) == set(b) for a, b in zip(idx.cpu().numpy().tolist(), r.idx.tolist())])
-    stats.update(check_output_fp8_small(out.cpu().numpy(), ref, set_eq, TOL_FP8, T * k * F))
+    stats = _compare_cpu_case(inp, out, idx, w)
     print(T, E, k, F, d, stats)
 
 
@@ -86,29 +92,25 @@ def test_fp8_deterministic(gpu_lib):
         assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("cfg,n_sample", [(4, 10), (7, 16), (9, 16), (10, 10)])
-def test_hy3_fp8(gpu_lib, cfg, n_sample):
-    """Per-channel scales (workloads 4, 7) and 128 x 128 block scales (9, 10)."""
+@pytest.mark.parametrize("cfg", [4, 7, 9, 10])
+def test_hy3_fp8(gpu_lib, cfg):
+    """Per-channel scales (workloads 4, 7) and 128 x 128 block scales (9, 10),
+    every token."""
     from sparse_moe_layer_wave_amd import hy3moe as hy
     inp = inputs.make_inputs(cfg, device="cuda")
     c = inp["cfg"]
-    T = c["T"]
     out, idx, w = hy.forward_fp8(inp["x"], inp["W_gate"], inp["Wq_gu"], inp["s_gu"], inp["Wq_dn"],
                                  inp["s_dn"], c["k"], inp["scale"], return_routing=True,
                                  block128=c["weights"] == "fp8_block128")
     torch.cuda.synchronize()
     x_bits = inputs.bits(inp["x"])
     W = inputs.bits(inp["W_gate"])
-    r = oracle.route(x_bits, W, c["k"], inp["scale"])
+    args = tuple(LazyExperts(inp[n]) for n in ("Wq_gu", "s_gu", "Wq_dn", "s_dn"))
+    ref, r = oracle.forward_fp8(x_bits, W, *args, c["k"], inp["scale"])
     idx_np = idx.cpu().numpy()
     stats = check_routing(idx_np, w.cpu().numpy(), r, inp["scale"])
-    rng = np.random.default_rng(4)
-    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_sample, replace=False)]))
-    ref, rs = oracle.forward_fp8_tokens(sample, x_bits, W, LazyExperts(inp["Wq_gu"]),
-                                        LazyExperts(inp["s_gu"]), LazyExperts(inp["Wq_dn"]),
-                                        LazyExperts(inp["s_dn"]), c["k"], inp["scale"])
-    set_eq = np.array([set(a) == set(b) for a, b in zip(idx_np[sample].tolist(), rs.idx.tolist())])
-    stats.update(check_output(out.cpu().numpy()[sample], ref, TOL_FP8, set_eq))
+    stats.update(check_output_flips(out.cpu().numpy(), ref, set_equal(idx_np, r), TOL_FP8,
+                                    **fp8_flip_model(x_bits, r, *args)))
     print("fp8", inp["cfg"]["name"], stats)
 
 
@@ -134,12 +136,7 @@ def test_fp8_block128_full_parity(gpu_lib, T, E, k, F, d):
     out, idx, w = hy.forward_fp8_block128(dev["x"], dev["W_gate"], dev["Wq_gu"], dev["s_gu"], dev["Wq_dn"],
                                           dev["s_dn"], k, inp["scale"], return_routing=True)
     torch.cuda.synchronize()
-    ref, r = oracle.forward_fp8(inputs.bits(inp["x"]), inp["W_gate"].numpy(), inputs.bits(inp["Wq_gu"]),
-                                inp["s_gu"].numpy(), inputs.bits(inp["Wq_dn"]), inp["s_dn"].numpy(),
-                                k, inp["scale"])
-    stats = check_routing(idx.cpu().numpy(), w.cpu().numpy(), r, inp["scale"])
-    set_eq = np.array([set(a) == set(b) for a, b in zip(idx.cpu().numpy().tolist(), r.idx.tolist())])
-    stats.update(check_output_fp8_small(out.cpu().numpy(), ref, set_eq, TOL_FP8, T * k * F))
+    stats = _compare_cpu_case(inp, out, idx, w)
     print(T, E, k, F, d, stats)
 
 

@@ -9,16 +9,16 @@ batches) and the rest the grouped GEMMs, with expert counts, k, d and d_ff in
 the ranges the library takes (d and d_ff multiples of 64, of 128 with e4m3
 experts; k <= min(E, 16)).
 Criteria as in the other parity tests: routing bit-exact except flagged
-near-ties; outputs within
-1e-2 * rms(ref) with bf16 experts, and the small-d_ff e4m3 criterion with e4m3
-experts."""
+near-ties; outputs within 1e-2 * rms(ref) with bf16 experts and 3e-2 * rms(ref)
+with e4m3 experts, element by element, an element exceeding it only by the
+rounding-boundary flips check_output_flips predicts from the oracle."""
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from parity import check_output, check_output_fp8_small, check_routing
+from parity import bf16_flip_model, check_output_flips, check_routing, fp8_flip_model
 from sparse_moe_layer_wave_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -79,7 +79,9 @@ def test_sweep_bf16(gpu_lib, T, d, E, k, F):
                             inputs.bits(inp["W_dn"]), k, inp["scale"], b)
     idx = idx.cpu().numpy()
     stats = check_routing(idx, w.cpu().numpy(), r, inp["scale"])
-    stats.update(check_output(out.cpu().numpy(), ref, TOL_BF16, _set_eq(idx, r)))
+    stats.update(check_output_flips(out.cpu().numpy(), ref, _set_eq(idx, r), TOL_BF16,
+                                    **bf16_flip_model(inputs.bits(inp["x"]), r, inputs.bits(inp["W_gu"]),
+                                                      inputs.bits(inp["W_dn"]))))
     print(T, d, E, k, F, "skew" if skew else "", stats)
 
 
@@ -97,7 +99,10 @@ def test_sweep_fp8(gpu_lib, T, d, E, k, F):
                                 k, inp["scale"])
     idx = idx.cpu().numpy()
     stats = check_routing(idx, w.cpu().numpy(), r, inp["scale"])
-    stats.update(check_output_fp8_small(out.cpu().numpy(), ref, _set_eq(idx, r), TOL_FP8, T * k * F))
+    stats.update(check_output_flips(out.cpu().numpy(), ref, _set_eq(idx, r), TOL_FP8,
+                                    **fp8_flip_model(inputs.bits(inp["x"]), r, inputs.bits(inp["Wq_gu"]),
+                                                     inp["s_gu"].numpy(), inputs.bits(inp["Wq_dn"]),
+                                                     inp["s_dn"].numpy())))
     print(T, d, E, k, F, stats)
 
 
@@ -117,7 +122,10 @@ def test_sweep_block(gpu_lib, T, d, E, k, F):
                                   score_bias=inputs.bits(inp["score_bias"]))
     idx = idx.cpu().numpy()
     stats = check_routing(idx, w.cpu().numpy(), r, inp["scale"])
-    stats.update(check_output(out.cpu().numpy(), ref, TOL_BF16, _set_eq(idx, r)))
+    stats.update(check_output_flips(out.cpu().numpy(), ref, _set_eq(idx, r), TOL_BF16,
+                                    **bf16_flip_model(inputs.bits(inp["x"]), r, inputs.bits(inp["W_gu"]),
+                                                      inputs.bits(inp["W_dn"]), inputs.bits(inp["Ws_gu"]),
+                                                      inputs.bits(inp["Ws_dn"]))))
     print(T, d, E, k, F, stats)
 
 
@@ -135,5 +143,8 @@ def test_sweep_fp8_block128(gpu_lib, T, d, E, k, F):
                                 k, inp["scale"])
     idx = idx.cpu().numpy()
     stats = check_routing(idx, w.cpu().numpy(), r, inp["scale"])
-    stats.update(check_output_fp8_small(out.cpu().numpy(), ref, _set_eq(idx, r), TOL_FP8, T * k * F))
+    stats.update(check_output_flips(out.cpu().numpy(), ref, _set_eq(idx, r), TOL_FP8,
+                                    **fp8_flip_model(inputs.bits(inp["x"]), r, inputs.bits(inp["Wq_gu"]),
+                                                     inp["s_gu"].numpy(), inputs.bits(inp["Wq_dn"]),
+                                                     inp["s_dn"].numpy())))
     print(T, d, E, k, F, stats)
