@@ -8,14 +8,17 @@ in HBM.  The main line is the decode batch (T=64 tokens, d=4096, 192 experts,
 top-8, d_ff=1536, bf16 experts); the prefill batch (T=8192) is reported in the
 same JSON line under "prefill", and the skewed, FP8 (T=8192 and T=64) and
 full-block (shared expert, route_norm, score bias; hy3moe_block_forward)
-workloads under their own keys.  Per-kernel durations come from HIP events recorded on the launch
-stream between the stages (the *_timed entry points).
+workloads under their own keys.  Per-kernel durations come from HIP events
+recorded on the launch stream between the stages (the *_timed entry points).
+Fractions of peak are against MI355X's published dense peaks (bf16 2.5
+PFLOP/s, fp8 5.0 PFLOP/s, HBM 8 TB/s).
 
-Under "prefill" / "at_measured_clock" the MFMA fractions are given once more
-against the dense bf16 peak at the graphics clock amd-smi reports while the
-prefill layer runs back to back (after the timed steps): MI355X lowers its
-clock well below the 2.4 GHz of the published peak under sustained MFMA load.
-"roofline" itself is always against the published peak.
+The cpu_baseline leg (skip with --no-cpu-baseline) runs the CPU oracle on the
+host after the GPU work: its throughput on the whole decode batch and on a
+1024-token sample of the prefill batch (expert weights copied to the host and
+decoded to float64 before the timed region), and, per workload, the GPU's
+routing against the oracle's on every token (near-tie tokens flagged, chosen
+sets and slot orders that differ) under "routing_vs_oracle".
 
 Prints one JSON line.  Only one GPU is used; --gpus N > 1 exits with a message.
 """
@@ -24,11 +27,7 @@ import argparse
 import hashlib
 import json
 import os
-import re
-import shutil
-import subprocess
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -42,7 +41,7 @@ from sparse_moe_layer_wave_amd import hy3moe, inputs  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
-NOMINAL_SCLK_GHZ = 2.4         # graphics clock the dense peaks are quoted at
+ROUTE_NORM_EPS = float(np.float32(1e-6))
 
 
 def _events(n):
@@ -53,18 +52,26 @@ def _events(n):
 
 
 def algorithmic(c, n_touched):
-    """Bytes and FLOPs a kernel must move/compute, counting only touched
-    experts' weights, each tensor once, and no padding."""
+    """Bytes and FLOPs a stage must move/compute, counting only touched
+    experts' weights, each tensor once, and no padding.  With e4m3 experts the
+    gate_up stage is the x quantiser (bf16 x in, e4m3 codes and row scales
+    out) plus the gate_up product, whose h is the e4m3 activation with its row
+    scale; weight scales are not counted."""
     T, d, E, k, F = c["T"], c["d"], c["E"], c["k"], c["F"]
     block = c.get("block", False)
     rows = T * k + (T if block else 0)              # the shared expert sees every token
     n_touched = n_touched + (1 if block else 0)
-    wb = 1 if c.get("weights") in ("fp8", "fp8_block128") else 2     # weight scales not counted
+    fp8 = c.get("weights") in ("fp8", "fp8_block128")
+    wb = 1 if fp8 else 2
+    if fp8:
+        gu_bytes = n_touched * 2 * F * d + T * d * 2 + rows * (F + 4)
+        dn_bytes = n_touched * d * F + rows * (F + 4) + rows * d * 2
+    else:
+        gu_bytes = n_touched * 2 * F * d * wb + T * d * 2 + rows * F * 2
+        dn_bytes = n_touched * d * F * wb + rows * F * 2 + rows * d * 2
     return {
-        "gate_up": dict(bytes=n_touched * 2 * F * d * wb + T * d * 2 + rows * F * 2,
-                        flops=2 * rows * d * 2 * F),
-        "down": dict(bytes=n_touched * d * F * wb + rows * F * 2 + rows * d * 2,
-                     flops=2 * rows * F * d),
+        "gate_up": dict(bytes=gu_bytes, flops=2 * rows * d * 2 * F),
+        "down": dict(bytes=dn_bytes, flops=2 * rows * F * d),
         "router": dict(bytes=E * d * 4 + T * d * 2 + rows * 8, flops=2 * T * d * E),
         # out: fp32, or bf16 out plus the bf16 residual read: 4 bytes per element either way
         "combine": dict(bytes=rows * d * 2 + T * k * 8 + T * d * 4, flops=2 * rows * d),
@@ -72,45 +79,7 @@ def algorithmic(c, n_touched):
     }
 
 
-def _smi_gfx_clock_mhz():
-    """Mean of the per-XCD graphics clocks amd-smi reports right now (MHz), or
-    None when amd-smi is missing or prints no clock."""
-    exe = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
-    if exe is None:
-        return None
-    try:
-        txt = subprocess.run([exe, "metric", "-c"], capture_output=True, text=True, timeout=15).stdout
-    except (OSError, subprocess.SubprocessError):
-        return None
-    mhz = [int(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", txt)]
-    return sum(mhz) / len(mhz) if mhz else None
-
-
-def clock_probe(step, seconds):
-    """Graphics clock (GHz) while `step` runs back to back for about `seconds`
-    (outside every timed region): amd-smi is sampled twice from a helper
-    thread, after a third and two thirds of the time.  None if unavailable."""
-    samples = []
-
-    def sampler():
-        for frac in (1 / 3, 2 / 3):
-            time.sleep(seconds / 3)
-            v = _smi_gfx_clock_mhz()
-            if v is not None:
-                samples.append(v)
-
-    th = threading.Thread(target=sampler)
-    t0 = time.perf_counter()
-    th.start()
-    while th.is_alive() or time.perf_counter() - t0 < seconds:
-        for _ in range(20):
-            step()
-        torch.cuda.synchronize()
-    th.join()
-    return round(sum(samples) / len(samples) / 1e3, 3) if samples else None
-
-
-def run_workload(cfg, steps, warmup, clock_probe_s=0.0):
+def run_workload(cfg, steps, warmup):
     inp = inputs.make_inputs(cfg, device="cuda")
     c = inp["cfg"]
     T, d, E, k, F = c["T"], c["d"], c["E"], c["k"], c["F"]
@@ -130,13 +99,13 @@ def run_workload(cfg, steps, warmup, clock_probe_s=0.0):
         if residual:
             return hy3moe.block_forward_bf16(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], inp["Ws_gu"],
                                              inp["Ws_dn"], k, inp["scale"], residual=inp["residual"],
-                                             norm_weight=inp["norm_w"], norm_eps=1e-6,
+                                             norm_weight=inp["norm_w"], norm_eps=ROUTE_NORM_EPS,
                                              score_bias=inp["score_bias"], out=out, workspace=ws,
                                              stage_events=evs, return_routing=return_routing)
         if block:
             return hy3moe.block_forward(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], inp["Ws_gu"],
                                         inp["Ws_dn"], k, inp["scale"], norm_weight=inp["norm_w"],
-                                        norm_eps=1e-6, score_bias=inp["score_bias"], out=out,
+                                        norm_eps=ROUTE_NORM_EPS, score_bias=inp["score_bias"], out=out,
                                         workspace=ws, stage_events=evs, return_routing=return_routing)
         if fp8:
             return hy3moe.forward_fp8(inp["x"], inp["W_gate"], inp["Wq_gu"], inp["s_gu"], inp["Wq_dn"],
@@ -166,11 +135,17 @@ def run_workload(cfg, steps, warmup, clock_probe_s=0.0):
     step_gpu = np.array([evs[s][0].elapsed_time(evs[s][len(hy3moe.STAGES)]) for s in range(steps)])
     step_gpu_ms = {q: round(float(np.percentile(step_gpu, p)), 5) for q, p in (("p10", 10), ("p50", 50), ("p90", 90))}
     alg = algorithmic(c, n_touched)
+    # what the routing check of the cpu_baseline leg needs: the GPU's routing
+    # and the router's inputs, on the host
+    routing = dict(name=c["name"], idx=idx_r.cpu().numpy(), x=inputs.bits(inp["x"]),
+                   W_gate=inputs.bits(inp["W_gate"]), k=k, scale=inp["scale"],
+                   bias=None if inp["bias"] is None else inputs.bits(inp["bias"]),
+                   norm_w=inputs.bits(inp["norm_w"]) if block else None,
+                   score_bias=inputs.bits(inp["score_bias"]) if block else None)
     res = dict(cfg=c, ms_per_step=elapsed / steps * 1e3, tokens_per_s=T * steps / elapsed, step_gpu_ms=step_gpu_ms,
                stage_ms=stage_ms, n_touched=n_touched, alg=alg,
                layer_tflops=alg["layer_flops"] * steps / elapsed / 1e12,
-               hottest_over_mean=float(load.max() / load.mean()),
-               sclk_ghz=clock_probe(step, clock_probe_s) if clock_probe_s > 0 else None)
+               hottest_over_mean=float(load.max() / load.mean()), routing=routing)
     del inp, ws, out
     torch.cuda.empty_cache()
     return res, idx
@@ -186,7 +161,11 @@ def roofline(res, kernel, bound):
         achieved = a["flops"] / (ms * 1e-3) / 1e12
         fp8 = res["cfg"].get("weights") in ("fp8", "fp8_block128")
         peak, unit = (FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS), "TFLOP/s"
-    return {"bound": bound, "kernel": kernel, "achieved": round(achieved, 2), "peak": peak,
+    fp8 = res["cfg"].get("weights") in ("fp8", "fp8_block128")
+    label = kernel
+    if fp8 and kernel == "gate_up":
+        label = "gate_up stage (x quantiser, gate_up GEMM, h quantiser)"
+    return {"bound": bound, "kernel": label, "achieved": round(achieved, 2), "peak": peak,
             "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic(kernel, res),
             "avg_kernel_ms": round(ms, 5)}
 
@@ -205,35 +184,70 @@ def traffic(kernel, res):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, max_seconds=25.0):
-    """The oracle, as it stands, on the first tokens of the same workload."""
+def _host_experts(t, experts):
+    """Host float64 copies of the listed experts of a device weight tensor,
+    keyed by expert (the oracle indexes them like the bit-pattern array)."""
     import oracle
-    from threadpoolctl import threadpool_info
+    return {int(e): oracle.bf16_bits_to_f64(inputs.bits(t[int(e)])) for e in experts}
 
-    class Lazy:                         # expert weights stay in HBM until the oracle needs one
-        def __init__(self, t):
-            self.t = t
 
-        def __getitem__(self, e):
-            return inputs.bits(self.t[int(e)])
-
+def _time_oracle(cfg, n_tokens):
+    """oracle.forward on the first n_tokens of a bf16 workload: the expert
+    weights the sample touches are copied to the host and decoded to float64
+    first, outside the timed region; the timed region is the whole oracle
+    forward (router, experts, combine).  Returns (tokens/s, seconds, experts)."""
+    import oracle
     inp = inputs.make_inputs(cfg, device="cuda")
     c = inp["cfg"]
-    x_bits, W = inputs.bits(inp["x"]), inputs.bits(inp["W_gate"])
+    x_bits = inputs.bits(inp["x"])[:n_tokens]
+    W = inputs.bits(inp["W_gate"])
     b = None if inp["bias"] is None else inputs.bits(inp["bias"])
-    gu, dn = Lazy(inp["W_gu"]), Lazy(inp["W_dn"])
-    n = 0
+    touched = np.unique(oracle.route(x_bits, W, c["k"], inp["scale"], b).idx)
+    gu, dn = _host_experts(inp["W_gu"], touched), _host_experts(inp["W_dn"], touched)
+    del inp
+    torch.cuda.empty_cache()
     t0 = time.perf_counter()
-    chunk = 4
-    while n < c["T"] and time.perf_counter() - t0 < max_seconds:
-        toks = np.arange(n, min(n + chunk, c["T"]))
-        oracle.forward_tokens(toks, x_bits, W, gu, dn, c["k"], inputs.ROUTER_SCALE, b)
-        n += len(toks)
+    oracle.forward(x_bits, W, gu, dn, c["k"], inputs.ROUTER_SCALE, b)
     el = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": round(n / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of the {c['T']} decode tokens, oracle.forward_tokens in chunks of "
-                      f"{chunk} (NumPy float64, OpenBLAS), {el:.1f} s"}
+    return n_tokens / el, el, len(touched)
+
+
+def _routing_vs_oracle(rt):
+    """The GPU's routing of one workload against oracle.route on every token."""
+    import oracle
+    x = rt["x"]
+    if rt["norm_w"] is not None:
+        x = oracle.rms_norm_bf16(x, rt["norm_w"], ROUTE_NORM_EPS)
+    r = oracle.route(x, rt["W_gate"], rt["k"], rt["scale"], rt["bias"], score_bias=rt["score_bias"])
+    idx = rt["idx"].astype(np.int64)
+    set_eq = np.all(np.sort(idx, axis=1) == np.sort(r.idx, axis=1), axis=1)
+    slot_eq = np.all(idx == r.idx, axis=1)
+    return {"tokens": int(idx.shape[0]), "near_tie": int(r.near_tie.sum()),
+            "order_tie": int(r.order_tie.sum()), "set_diff": int((~set_eq).sum()),
+            "slot_diff": int((~slot_eq).sum()),
+            "set_diff_unflagged": int((~set_eq & ~r.near_tie).sum()),
+            "slot_diff_unflagged": int((~slot_eq & ~r.order_tie).sum())}
+
+
+def cpu_baseline_leg(routings):
+    """The oracle on the host cores: the decode batch whole, and a 1024-token
+    sample of the prefill batch; then the routing check of every workload."""
+    from threadpoolctl import threadpool_info
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] + [1])
+    vendor = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in blas) or "unknown"
+    dec, dec_s, dec_e = _time_oracle(1, 64)
+    pre, pre_s, pre_e = _time_oracle(2, 1024)
+    base = {"value": round(dec, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole 64-token decode batch (hy3_decode_T64, {dec_e} experts), oracle.forward in "
+                      f"NumPy float64 on {threads} BLAS threads ({vendor}), {dec_s:.1f} s; expert weights copied "
+                      "to the host and decoded to float64 before the timed region",
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "prefill": {"value": round(pre, 2), "unit": "tokens/s",
+                        "sample": f"the first 1024 of the 8192 prefill tokens (hy3_prefill_T8192, {pre_e} experts), "
+                                  f"{pre_s:.1f} s, same method"}}
+    checks = {rt["name"]: _routing_vs_oracle(rt) for rt in routings}
+    return base, checks
 
 
 def shares(steps, warmup):
@@ -270,9 +284,6 @@ def main():
     ap.add_argument("--profile-workload", metavar="NAME",
                     help="run only the named workload (a profiler pass: one workload per run), "
                          "print its stage times and exit")
-    ap.add_argument("--clock-probe", type=float, default=2.5, metavar="SECONDS",
-                    help="after the timed prefill steps, run them back to back this long while amd-smi "
-                         "samples the graphics clock (0: skip)")
     ap.add_argument("--shares", action="store_true",
                     help="print one JSON line with the expert GEMMs at one GPU's share of an 8-way expert-parallel "
                          "or 8- / 4-way d_ff-parallel layer, and exit")
@@ -309,6 +320,7 @@ def main():
         return
 
     dec, _ = run_workload(1, args.steps, args.warmup)
+    routings = [dec.pop("routing")]
     line = {
         "metric": "MoE-layer tokens/s at T=64 & T=8192; % of HBM BW / % of MFMA peak",
         "value": round(dec["tokens_per_s"], 1),
@@ -330,7 +342,8 @@ def main():
         "layer_tflops": round(dec["layer_tflops"], 3),
     }
     if not args.no_prefill:
-        pre, _ = run_workload(2, max(5, args.steps // 5), args.warmup, clock_probe_s=args.clock_probe)
+        pre, _ = run_workload(2, max(5, args.steps // 5), args.warmup)
+        routings.append(pre.pop("routing"))
         line["prefill"] = {
             "workload": pre["cfg"]["name"], "tokens_per_s": round(pre["tokens_per_s"], 1),
             "ms_per_step": round(pre["ms_per_step"], 4),
@@ -341,18 +354,6 @@ def main():
             "kernel_ms": {k: round(v, 5) for k, v in pre["stage_ms"].items()},
             "step_gpu_ms": pre["step_gpu_ms"],
         }
-        # the same fractions against the dense bf16 peak at the graphics clock
-        # the GPU held while running this layer back to back (amd-smi)
-        if pre["sclk_ghz"]:
-            peak = BF16_PEAK_TFLOPS * pre["sclk_ghz"] / NOMINAL_SCLK_GHZ
-            gu = line["prefill"]["roofline"]["achieved"]
-            line["prefill"]["at_measured_clock"] = {
-                "sclk_ghz": pre["sclk_ghz"], "bf16_peak_tflops": round(peak, 1),
-                "gate_up_frac": round(gu / peak, 4),
-                "down_frac": round(line["prefill"]["roofline_down"]["achieved"] / peak, 4),
-                "layer_frac": round(pre["layer_tflops"] / peak, 4)}
-        else:
-            line["prefill"]["at_measured_clock"] = None
     if not args.no_extra:
         for key, cfg, bound in (("skewed", 3, "mfma"), ("fp8", 4, "mfma"), ("fp8_decode", 7, "hbm"),
                                 ("block_decode", 5, "hbm"), ("block_prefill", 6, "mfma"),
@@ -360,6 +361,7 @@ def main():
                                 ("fp8_block128", 10, "mfma"), ("block_residual_prefill", 11, "mfma")):
             n = args.steps if bound == "hbm" else max(3, args.steps // 10)
             res, _ = run_workload(cfg, n, min(args.warmup, 2))
+            routings.append(res.pop("routing"))
             line[key] = {
                 "workload": res["cfg"]["name"], "tokens_per_s": round(res["tokens_per_s"], 1),
                 "ms_per_step": round(res["ms_per_step"], 4),
@@ -371,7 +373,7 @@ def main():
                 "step_gpu_ms": res["step_gpu_ms"],
             }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(1)
+        line["cpu_baseline"], line["routing_vs_oracle"] = cpu_baseline_leg(routings)
     print(json.dumps(line), flush=True)
 
 
