@@ -1,10 +1,12 @@
 """Build libhy3moe.so (gfx950) in-tree with hipcc.
 
-    python -m sparse_moe_layer_wave_amd.build      # or __graft_entry__.build()
+    python -m sparse_moe_layer_wave_amd.build [--sanitize]   # or __graft_entry__.build()
 
 Every .hip file under csrc/ is compiled to an object in csrc/_build/ and the
 objects are linked into sparse_moe_layer_wave_amd/libhy3moe.so.  Always
-recompiles (a build is a few seconds per file)."""
+recompiles (a build is a few seconds per file).  --sanitize builds a separate
+copy with host-side AddressSanitizer and UndefinedBehaviorSanitizer into
+csrc/_build/san/ for the CPU tests of the C ABI."""
 
 import concurrent.futures
 import glob
@@ -29,9 +31,22 @@ CFLAGS = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(OBJDIR, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+# Host-only AddressSanitizer + UndefinedBehaviorSanitizer (argument checks,
+# workspace carving, launch set-up).  Each -fsanitize= sits right after
+# -Xarch_host, so device code is built exactly as in the product library.
+SAN_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+SAN_DIR = os.path.join(OBJDIR, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libhy3moe_san.so")
+
+
+def _compile(src, objdir=OBJDIR, extra=()):
+    obj = os.path.join(objdir, os.path.basename(src).replace(".hip", ".o"))
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -40,25 +55,42 @@ def _compile(src):
     return obj, warn
 
 
-def build(verbose=True):
+def build(verbose=True, sanitize=False):
+    """Build the library; with sanitize=True, a copy whose host code carries
+    the sanitizers (SAN_LIB, outside the package; load it with the
+    sanitizer runtime preloaded, see sanitizer_runtime())."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError("no HIP sources found")
-    os.makedirs(OBJDIR, exist_ok=True)
+    objdir = SAN_DIR if sanitize else OBJDIR
+    lib = SAN_LIB if sanitize else LIB
+    extra = SAN_FLAGS if sanitize else []
+    os.makedirs(objdir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        results = list(ex.map(_compile, srcs))
+        results = list(ex.map(lambda src: _compile(src, objdir, extra), srcs))
     for _, warn in results:
         if warn and verbose:
             print(warn, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[o for o, _ in results], "-o", tmp]
+    tmp = lib + ".tmp"
+    link_extra = [*SAN_FLAGS, "-shared-libsan"] if sanitize else []
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[o for o, _ in results], *link_extra,
+           "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
+
+
+def sanitizer_runtime():
+    """Path of the clang AddressSanitizer runtime (it carries the
+    UndefinedBehaviorSanitizer handlers too) that a process loading SAN_LIB
+    must preload."""
+    r = subprocess.run([HIPCC, "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                       text=True, check=True)
+    return r.stdout.strip()
 
 
 def clean():
@@ -66,4 +98,4 @@ def clean():
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--sanitize" in sys.argv)

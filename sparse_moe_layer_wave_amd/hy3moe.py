@@ -13,7 +13,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhy3moe.so")
+# HY3MOE_LIBRARY names another build of the same library (the sanitized one
+# the C ABI's CPU tests load); by default the in-tree build.
+LIB_PATH = os.environ.get("HY3MOE_LIBRARY") or os.path.join(_PKG, "libhy3moe.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 WEIGHTS_BF16, WEIGHTS_FP8_E4M3 = 0, 1

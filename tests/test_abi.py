@@ -238,8 +238,11 @@ int main(void) {{
 }}
 """)
     exe = tmp_path / "use_abi"
+    # a sanitized build of the library (tests/test_abi_sanitized.py) needs the
+    # preloaded sanitizer runtime on the link line as well
+    san_rt = [p for p in os.environ.get("LD_PRELOAD", "").split() if "libclang_rt.asan" in p]
     subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
-                    str(src), hy3moe.LIB_PATH, f"-Wl,-rpath,{os.path.dirname(hy3moe.LIB_PATH)}",
+                    str(src), hy3moe.LIB_PATH, *san_rt, f"-Wl,-rpath,{os.path.dirname(hy3moe.LIB_PATH)}",
                     "-o", str(exe)], check=True, capture_output=True, text=True)
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert res.returncode == 0, res.stdout + res.stderr
