@@ -59,7 +59,8 @@ typedef enum {
     HY3MOE_ERR_UNSUPPORTED = -3, /* outside the supported shapes listed above, or unknown dtype */
     HY3MOE_ERR_WORKSPACE = -4,   /* workspace smaller than required */
     HY3MOE_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned */
-    HY3MOE_ERR_HIP = -6          /* a HIP launch failed; see hy3moe_last_hip_error() */
+    HY3MOE_ERR_HIP = -6,         /* a HIP launch failed; see hy3moe_last_hip_error() */
+    HY3MOE_ERR_SCRATCH = -7      /* hy3moe_forward_noalloc: sizes need more than its static scratch */
 } hy3moe_status;
 
 enum { HY3MOE_WEIGHTS_BF16 = 0, HY3MOE_WEIGHTS_FP8_E4M3 = 1 };
@@ -120,6 +121,26 @@ int hy3moe_forward(const uint16_t* x, const float* W_gate,
                    int T, int d, int E, int k, int d_ff, float scale, void* stream,
                    const float* logit_bias, int32_t* topk_idx, float* topk_w,
                    void* workspace, size_t workspace_bytes);
+
+/* hy3moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument; the scratch is a static device array inside the
+ * library, HY3MOE_NOALLOC_SCRATCH_BYTES (64 MiB) on every GPU the library
+ * runs on, held until the process ends.  The call allocates nothing and
+ * enqueues the same kernels as hy3moe_forward, so the results are the same
+ * bit for bit.  Sizes whose hy3moe_workspace_size (BF16) exceeds the scratch
+ * return HY3MOE_ERR_SCRATCH with nothing enqueued (at the Hy3 sizes d = 4096,
+ * E = 192, k = 8, d_ff = 1536 that is T > 603).  All calls on one GPU share
+ * its scratch array: calls that may overlap on a GPU (other streams, other
+ * threads) race and must be ordered by the caller.  The first call on a
+ * device looks the array's address up once (hipGetSymbolAddress); a failure
+ * there returns HY3MOE_ERR_HIP.  Other arguments and errors as for
+ * hy3moe_forward. */
+#define HY3MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int hy3moe_forward_noalloc(const uint16_t* x, const float* W_gate,
+                           const uint16_t* W_gate_up, const uint16_t* W_down, float* out,
+                           int T, int d, int E, int k, int d_ff, float scale, void* stream,
+                           const float* logit_bias, int32_t* topk_idx, float* topk_w);
 
 /* hy3moe_forward with instrumentation: stage_events is a HOST array of 6
  * hipEvent_t handles (any may be NULL) recorded on `stream` before the router,

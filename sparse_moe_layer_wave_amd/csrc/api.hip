@@ -119,6 +119,34 @@ int hip_status(hipError_t e) {
     return HY3MOE_ERR_HIP;
 }
 
+// ---- the static scratch of hy3moe_forward_noalloc ----
+// Device memory of the code object, one copy per GPU, held until the process
+// ends.  Host code never uses the array's name as an address (on the host it
+// is a stand-in, not device memory): each device's address is fetched once,
+// with hipGetSymbolAddress while that device is current, and kept here.
+constexpr size_t kScratchBytes = size_t(HY3MOE_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];   // nullptr: not fetched yet
+
+// The scratch array's address on the current device (first call per device:
+// hipGetSymbolAddress; concurrent first calls fetch and store the same value).
+hipError_t scratch_address(void** addr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+    *addr = p;
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -212,31 +240,41 @@ namespace {
 // norm_w (route_norm), score_bias (selection-only bias), Ws_gu/Ws_dn (the
 // shared expert, both or neither).  With out_bf16 instead of out, the
 // output is bf16 with the residual (if any) added in the combine.
+// With use_scratch, the workspace is the library's static scratch array
+// (hy3moe_forward_noalloc) and the workspace arguments are ignored.
 static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_eps,
                         const float* W_gate, const float* logit_bias, const float* score_bias,
                         const uint16_t* W_gate_up, const uint16_t* W_down, const uint16_t* Ws_gu,
                         const uint16_t* Ws_dn, float* out, int T, int d, int E, int k, int d_ff,
                         float scale, void* stream, int32_t* topk_idx, float* topk_w,
                         void* workspace, size_t workspace_bytes, void* const* ev,
-                        const uint16_t* resid = nullptr, uint16_t* out_bf16 = nullptr) {
+                        const uint16_t* resid = nullptr, uint16_t* out_bf16 = nullptr,
+                        bool use_scratch = false) {
     const bool shared = Ws_gu != nullptr;
     int st = check_shape(T, d, E, k, d_ff);
     if (st != HY3MOE_OK) return st;
     if (shared && E > 1023) return HY3MOE_ERR_UNSUPPORTED;
     if (!(norm_eps >= 0.f)) return HY3MOE_ERR_SHAPE;
     if (T == 0) return HY3MOE_OK;
-    if (!x || !W_gate || !W_gate_up || !W_down || !(out || out_bf16) || !workspace)
+    if (!x || !W_gate || !W_gate_up || !W_down || !(out || out_bf16) || (!workspace && !use_scratch))
         return HY3MOE_ERR_NULL;
     if ((Ws_gu == nullptr) != (Ws_dn == nullptr)) return HY3MOE_ERR_NULL;
     if (!aligned16(x) || !aligned16(W_gate) || !aligned16(W_gate_up) || !aligned16(W_down) ||
-        !aligned16(out ? static_cast<const void*>(out) : out_bf16) || !aligned16(workspace) ||
+        !aligned16(out ? static_cast<const void*>(out) : out_bf16) ||
+        (!use_scratch && !aligned16(workspace)) ||
         (resid && !aligned16(resid)) || (logit_bias && !aligned16(logit_bias)) ||
         (score_bias && !aligned16(score_bias)) || (norm_w && !aligned16(norm_w)) ||
         (Ws_gu && !aligned16(Ws_gu)) || (Ws_dn && !aligned16(Ws_dn)) ||
         (topk_idx && !aligned16(topk_idx)) || (topk_w && !aligned16(topk_w)))
         return HY3MOE_ERR_ALIGN;
     const Layout L = make_layout(T, d, E, k, d_ff, HY3MOE_WEIGHTS_BF16, shared, norm_w != nullptr);
-    if (workspace_bytes < L.total) return HY3MOE_ERR_WORKSPACE;
+    if (use_scratch) {
+        if (L.total > kScratchBytes) return HY3MOE_ERR_SCRATCH;
+        const hipError_t e = scratch_address(&workspace);
+        if (e != hipSuccess) return hip_status(e);
+    } else if (workspace_bytes < L.total) {
+        return HY3MOE_ERR_WORKSPACE;
+    }
     char* ws = static_cast<char*>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws + L.idx);
@@ -417,6 +455,15 @@ int hy3moe_forward_timed(const uint16_t* x, const float* W_gate, const uint16_t*
                         workspace_bytes, stage_events);
 }
 
+int hy3moe_forward_noalloc(const uint16_t* x, const float* W_gate, const uint16_t* W_gate_up,
+                           const uint16_t* W_down, float* out, int T, int d, int E, int k, int d_ff,
+                           float scale, void* stream, const float* logit_bias, int32_t* topk_idx,
+                           float* topk_w) {
+    return forward_bf16(x, nullptr, 0.f, W_gate, logit_bias, nullptr, W_gate_up, W_down, nullptr,
+                        nullptr, out, T, d, E, k, d_ff, scale, stream, topk_idx, topk_w, nullptr, 0,
+                        nullptr, nullptr, nullptr, true);
+}
+
 int hy3moe_block_workspace_size(int T, int d, int E, int k, int d_ff, size_t* bytes) {
     if (!bytes) return HY3MOE_ERR_NULL;
     const int st = check_shape(T, d, E, k, d_ff);
@@ -538,6 +585,10 @@ const char* hy3moe_status_string(int status) {
         case HY3MOE_ERR_WORKSPACE: return "workspace smaller than hy3moe_workspace_size reports";
         case HY3MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case HY3MOE_ERR_HIP: return "a HIP launch failed (see hy3moe_last_hip_error)";
+        case HY3MOE_ERR_SCRATCH:
+            return "hy3moe_forward_noalloc: these sizes need more scratch than the library's static "
+                   "scratch array holds (HY3MOE_NOALLOC_SCRATCH_BYTES, 64 MiB; use hy3moe_forward "
+                   "with a workspace)";
         default: return "unknown status";
     }
 }

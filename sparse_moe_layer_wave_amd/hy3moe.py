@@ -17,12 +17,13 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 # the C ABI's CPU tests load); by default the in-tree build.
 LIB_PATH = os.environ.get("HY3MOE_LIBRARY") or os.path.join(_PKG, "libhy3moe.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
+NOALLOC_SCRATCH_BYTES = 64 << 20
 WEIGHTS_BF16, WEIGHTS_FP8_E4M3 = 0, 1
 
 EXPORTS = (
     "hy3moe_workspace_size", "hy3moe_route", "hy3moe_permute", "hy3moe_forward",
-    "hy3moe_forward_timed", "hy3moe_forward_fp8", "hy3moe_forward_fp8_timed",
+    "hy3moe_forward_timed", "hy3moe_forward_noalloc", "hy3moe_forward_fp8", "hy3moe_forward_fp8_timed",
     "hy3moe_forward_fp8_block128", "hy3moe_forward_fp8_block128_timed",
     "hy3moe_block_workspace_size", "hy3moe_route_ex", "hy3moe_block_forward",
     "hy3moe_block_forward_timed", "hy3moe_block_forward_bf16", "hy3moe_block_forward_bf16_timed",
@@ -57,6 +58,7 @@ def lib():
     L.hy3moe_permute.argtypes = [P, I, I, I, P, P, P, P, P, Z, S]
     L.hy3moe_forward.argtypes = [P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z]
     L.hy3moe_forward_timed.argtypes = [P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z, P]
+    L.hy3moe_forward_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, S, P, P, P]
     L.hy3moe_forward_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z]
     L.hy3moe_forward_fp8_timed.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, S, P, P, P, P, Z, P]
     L.hy3moe_forward_fp8_block128.argtypes = L.hy3moe_forward_fp8.argtypes
@@ -187,6 +189,32 @@ def forward(x, W_gate, W_gate_up, W_down, k, scale, bias=None, out=None, workspa
         _check(lib().hy3moe_forward(*args), "hy3moe_forward")
     else:
         _check(lib().hy3moe_forward_timed(*args, _event_array(stage_events)), "hy3moe_forward_timed")
+    return (out, idx, w) if return_routing else out
+
+
+def forward_noalloc(x, W_gate, W_gate_up, W_down, k, scale, bias=None, out=None, return_routing=False):
+    """hy3moe_forward_noalloc: hy3moe_forward with the library's static
+    scratch instead of a workspace (allocates nothing in the library; this
+    wrapper allocates out / the routing outputs only when not given)."""
+    T, d = x.shape
+    E = W_gate.shape[0]
+    F = W_down.shape[2]
+    _need(x, torch.bfloat16, (T, d), "x")
+    _need(W_gate, torch.float32, (E, d), "W_gate")
+    _need(W_gate_up, torch.bfloat16, (E, 2 * F, d), "W_gate_up")
+    _need(W_down, torch.bfloat16, (E, d, F), "W_down")
+    if bias is not None:
+        _need(bias, torch.float32, (E,), "bias")
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    _need(out, torch.float32, (T, d), "out")
+    idx = w = None
+    if return_routing:
+        idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    _check(lib().hy3moe_forward_noalloc(_ptr(x), _ptr(W_gate), _ptr(W_gate_up), _ptr(W_down), _ptr(out), T, d,
+                                        E, k, F, float(scale), _stream(), _ptr(bias), _ptr(idx), _ptr(w)),
+           "hy3moe_forward_noalloc")
     return (out, idx, w) if return_routing else out
 
 

@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported(L):
 
 
 def test_status_strings(L):
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert len(L.hy3moe_status_string(code)) > 0
     assert L.hy3moe_status_string(-99) == b"unknown status"
     assert L.hy3moe_last_hip_error() == 0
@@ -85,6 +85,27 @@ def test_forward_argument_checks(L):
     assert _fwd(L, nws=need - 1) == hy3moe.ERR_WORKSPACE
     # T == 0 is a no-op that needs no pointers at all
     assert _fwd(L, T=0, x=NUL, wg=NUL, gu=NUL, dn=NUL, out=NUL, ws=NUL, nws=0) == hy3moe.OK
+
+
+def _fwd_na(L, T=16, d=512, E=32, k=8, F=128, x=A, wg=A, gu=A, dn=A, out=A, bias=NUL, idx=NUL, w=NUL):
+    return L.hy3moe_forward_noalloc(x, wg, gu, dn, out, T, d, E, k, F, 2.826, NUL, bias, idx, w)
+
+
+def test_forward_noalloc_argument_checks(L):
+    """Checked on the host before the scratch is looked up: bad arguments,
+    and sizes beyond the static scratch (64 MiB) with a status of their own."""
+    assert _fwd_na(L, T=-1) == hy3moe.ERR_SHAPE
+    assert _fwd_na(L, k=17, E=64) == hy3moe.ERR_UNSUPPORTED
+    assert _fwd_na(L, x=NUL) == hy3moe.ERR_NULL
+    assert _fwd_na(L, out=NUL) == hy3moe.ERR_NULL
+    assert _fwd_na(L, gu=MIS) == hy3moe.ERR_ALIGN
+    assert _fwd_na(L, idx=MIS) == hy3moe.ERR_ALIGN
+    assert _fwd_na(L, T=0, x=NUL) == hy3moe.OK
+    assert hy3moe.workspace_size(603, 4096, 192, 8, 1536) <= hy3moe.NOALLOC_SCRATCH_BYTES
+    assert hy3moe.workspace_size(604, 4096, 192, 8, 1536) > hy3moe.NOALLOC_SCRATCH_BYTES
+    assert _fwd_na(L, T=604, d=4096, E=192, k=8, F=1536) == hy3moe.ERR_SCRATCH
+    assert _fwd_na(L, T=8192, d=4096, E=192, k=8, F=1536) == hy3moe.ERR_SCRATCH
+    assert b"static scratch" in L.hy3moe_status_string(hy3moe.ERR_SCRATCH)
 
 
 def test_forward_fp8_argument_checks(L):
