@@ -14,11 +14,11 @@ Fractions of peak are against MI355X's published dense peaks (bf16 2.5
 PFLOP/s, fp8 5.0 PFLOP/s, HBM 8 TB/s).
 
 The cpu_baseline leg (skip with --no-cpu-baseline) runs the CPU oracle on the
-host after the GPU work: its throughput on the whole decode batch and on a
-1024-token sample of the prefill batch (expert weights copied to the host and
-decoded to float64 before the timed region), and, per workload, the GPU's
-routing against the oracle's on every token (near-tie tokens flagged, chosen
-sets and slot orders that differ) under "routing_vs_oracle".
+host after the GPU work: its throughput on the whole decode batch (repeated
+for at least 10 s) and on the whole prefill batch (expert weights copied to
+the host and decoded to float64 before the timed region), and, per workload,
+the GPU's routing against the oracle's on every token (near-tie tokens
+flagged, chosen sets and slot orders that differ) under "routing_vs_oracle".
 
 Prints one JSON line.  Only one GPU is used; --gpus N > 1 exits with a message.
 """
@@ -191,11 +191,12 @@ def _host_experts(t, experts):
     return {int(e): oracle.bf16_bits_to_f64(inputs.bits(t[int(e)])) for e in experts}
 
 
-def _time_oracle(cfg, n_tokens):
-    """oracle.forward on the first n_tokens of a bf16 workload: the expert
-    weights the sample touches are copied to the host and decoded to float64
-    first, outside the timed region; the timed region is the whole oracle
-    forward (router, experts, combine).  Returns (tokens/s, seconds, experts)."""
+def _time_oracle(cfg, n_tokens, min_seconds=0.0):
+    """oracle.forward on the first n_tokens of a bf16 workload, repeated until
+    min_seconds have passed (at least once): the expert weights the batch
+    touches are copied to the host and decoded to float64 first, outside the
+    timed region; the timed region is the whole oracle forward (router,
+    experts, combine).  Returns (tokens/s, seconds, experts, repeats)."""
     import oracle
     inp = inputs.make_inputs(cfg, device="cuda")
     c = inp["cfg"]
@@ -206,10 +207,13 @@ def _time_oracle(cfg, n_tokens):
     gu, dn = _host_experts(inp["W_gu"], touched), _host_experts(inp["W_dn"], touched)
     del inp
     torch.cuda.empty_cache()
+    reps = 0
     t0 = time.perf_counter()
-    oracle.forward(x_bits, W, gu, dn, c["k"], inputs.ROUTER_SCALE, b)
+    while reps == 0 or time.perf_counter() - t0 < min_seconds:
+        oracle.forward(x_bits, W, gu, dn, c["k"], inputs.ROUTER_SCALE, b)
+        reps += 1
     el = time.perf_counter() - t0
-    return n_tokens / el, el, len(touched)
+    return n_tokens * reps / el, el, len(touched), reps
 
 
 def _routing_vs_oracle(rt):
@@ -230,21 +234,22 @@ def _routing_vs_oracle(rt):
 
 
 def cpu_baseline_leg(routings):
-    """The oracle on the host cores: the decode batch whole, and a 1024-token
-    sample of the prefill batch; then the routing check of every workload."""
+    """The oracle on the host cores: the whole decode batch (repeated for at
+    least 10 s) and the whole prefill batch; then the routing check of every
+    workload."""
     from threadpoolctl import threadpool_info
     blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
     threads = max([p.get("num_threads", 1) for p in blas] + [1])
     vendor = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in blas) or "unknown"
-    dec, dec_s, dec_e = _time_oracle(1, 64)
-    pre, pre_s, pre_e = _time_oracle(2, 1024)
+    dec, dec_s, dec_e, dec_n = _time_oracle(1, 64, min_seconds=10.0)
+    pre, pre_s, pre_e, _ = _time_oracle(2, 8192)
     base = {"value": round(dec, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole 64-token decode batch (hy3_decode_T64, {dec_e} experts), oracle.forward in "
-                      f"NumPy float64 on {threads} BLAS threads ({vendor}), {dec_s:.1f} s; expert weights copied "
-                      "to the host and decoded to float64 before the timed region",
+            "sample": f"the whole 64-token decode batch (hy3_decode_T64, {dec_e} experts) {dec_n} times, "
+                      f"oracle.forward in NumPy float64 on {threads} BLAS threads ({vendor}), {dec_s:.1f} s; "
+                      "expert weights copied to the host and decoded to float64 before the timed region",
             "host_cpus": len(os.sched_getaffinity(0)),
             "prefill": {"value": round(pre, 2), "unit": "tokens/s",
-                        "sample": f"the first 1024 of the 8192 prefill tokens (hy3_prefill_T8192, {pre_e} experts), "
+                        "sample": f"the whole 8192-token prefill batch (hy3_prefill_T8192, {pre_e} experts) once, "
                                   f"{pre_s:.1f} s, same method"}}
     checks = {rt["name"]: _routing_vs_oracle(rt) for rt in routings}
     return base, checks
