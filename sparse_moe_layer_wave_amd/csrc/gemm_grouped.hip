@@ -58,9 +58,7 @@
 // into 8 contiguous ranges, one per XCD, which that XCD's workgroups take
 // round-robin.
 
-#include <algorithm>
-
-#include "internal.h"
+#include "grouped_order.h"
 
 namespace hy3 {
 namespace {
@@ -70,20 +68,6 @@ enum Mode { GU_BF16 = 0, DN_BF16 = 1, GU_FP8 = 2, DN_FP8 = 3 };
 constexpr int kRowB = 128;                     // bytes per LDS row (one K slice)
 constexpr int kLdsBytes = 160 * 1024;          // the whole LDS of a CU
 constexpr int kSlots = 2;                      // LDS ring depth
-constexpr int kXcds = 8;
-constexpr int kChunkBlocks = 8;                // row blocks of 128 per chunk (see work order)
-
-struct Unit {
-    int e, row0, rows, n;                          // n: column tile index of this shape
-};
-
-__device__ __forceinline__ int lane_id() {
-    // opaque (asm volatile): recomputed where used rather than hoisted out of
-    // the persistent unit loop and kept live across the MFMA loop
-    int lane;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
-    return lane;
-}
 
 struct Args {
     const uint8_t* A;                              // gate_up: x [T, K]; down: h [rows, K]
@@ -99,11 +83,6 @@ struct Args {
     uint32_t* amax;                                // e4m3 gate_up: [rows] bits of max |h|
     int K, N, E, npanel;                           // K in elements; npanel: 512-row panels per expert
 };
-
-// LDS rows of one slice are 128 bytes: logical 16-byte chunk c of row r sits
-// at physical chunk c ^ ((r >> 1) & 7).  A fragment read phase (16 rows at
-// one logical chunk) then touches 16 distinct 4-bank groups.
-__device__ __forceinline__ int pchunk8(int row, int c) { return c ^ ((row >> 1) & 7); }
 
 // One tile.  SQUARE: 256 rows x 256 weight rows; else 128 x 512.
 template <int MODE, bool SQUARE>
@@ -422,55 +401,6 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
     }
 }
 
-// Unit L -> tile.  Returns false for the second column tile of a partial
-// last panel (nothing to compute).
-template <int MODE>
-__device__ __forceinline__ bool unit_of(const Args& g, int L, Unit& u, bool& square) {
-    constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8;
-    const int E = g.E, npanel = g.npanel;
-    int lo = 0, hi = E - 1;                        // expert: last e with tile_off[e] * npanel <= L
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (g.tile_off[mid] * npanel <= L) lo = mid;
-        else hi = mid - 1;
-    }
-    u.e = lo;
-    // the table values are uniform: kept in scalar registers, so the unit
-    // arithmetic below runs on the scalar unit
-    const int t0 = __builtin_amdgcn_readfirstlane(g.tile_off[lo]);
-    const int nb_e = __builtin_amdgcn_readfirstlane(g.tile_off[lo + 1]) - t0;
-    int v = L - t0 * npanel;
-    // chunks of kChunkBlocks row blocks; a chunk of m blocks has m * npanel
-    // units: for each weight panel, its square tiles (two column tiles per
-    // panel, pairs of blocks) and then its wide tile (odd last block)
-    const int full = nb_e / kChunkBlocks;
-    int c, m;
-    if (v < full * kChunkBlocks * npanel) {
-        c = v / (kChunkBlocks * npanel);
-        m = kChunkBlocks;
-    } else {
-        c = full;
-        m = nb_e - full * kChunkBlocks;
-    }
-    v -= c * kChunkBlocks * npanel;
-    const int pairs = m >> 1;
-    const int panel = v / m;
-    const int w = v - panel * m;
-    int blk;
-    square = w < 2 * pairs;
-    if (square) {
-        u.n = 2 * panel + w / pairs;
-        blk = c * kChunkBlocks + 2 * (w % pairs);
-    } else {
-        u.n = panel;
-        blk = c * kChunkBlocks + 2 * pairs;
-    }
-    u.row0 = __builtin_amdgcn_readfirstlane(g.offsets[lo]) + blk * 128;
-    u.rows = min(square ? 256 : 128, __builtin_amdgcn_readfirstlane(g.offsets[lo + 1]) - u.row0);
-    const int cols_sq = GATE_UP ? 128 : 256;       // output columns of a square tile
-    return !(square && u.n * cols_sq >= g.N);
-}
-
 // Persistent: one workgroup per CU, workgroup b on XCD b % 8 (the dispatcher
 // deals workgroups round-robin over the XCDs).  The units are split into 8
 // contiguous ranges, one per XCD, and the XCD's workgroups take its range
@@ -490,7 +420,9 @@ __global__ __launch_bounds__(256, 1) void k_grouped(Args g) {
     for (int L = x * per_xcd + j; L < end; L += per_wg) {
         Unit u;
         bool square;
-        if (!unit_of<MODE>(g, L, u, square)) continue;
+        if (!unit_of<MODE == GU_BF16 || MODE == GU_FP8>(g.tile_off, g.offsets, g.E, g.npanel, g.N, L, u,
+                                                        square))
+            continue;
         if (square) tile<MODE, true>(g, lds, u, wave);
         else tile<MODE, false>(g, lds, u, wave);
         lds_barrier();                             // every wave has read its staged output back
@@ -506,8 +438,7 @@ hipError_t launch(Args g, int max_blocks, hipStream_t s) {
     int cus = 0;
     const hipError_t err = device_cu_count(&cus);
     if (err != hipSuccess) return err;
-    const long long cap = std::max(kXcds, cus / kXcds * kXcds);    // one workgroup per CU
-    const int grid = static_cast<int>(std::min(cap, (units + kXcds - 1) / kXcds * kXcds));
+    const int grid = persistent_grid(units, cus);
     hipLaunchKernelGGL(k_grouped<MODE>, dim3(grid), dim3(256), 0, s, g);
     return hipGetLastError();
 }
