@@ -44,9 +44,17 @@ SAN_DIR = os.path.join(OBJDIR, "san")
 SAN_LIB = os.path.join(SAN_DIR, "libhy3moe_san.so")
 
 
+# Flags of single files.  gemm_blockscale.hip: its accumulators are rescaled
+# by VALU multiplies between MFMAs, so its MFMAs read and write them in VGPRs
+# rather than AGPRs (which would take a copy out and back per multiply).
+FILE_FLAGS = {
+    "gemm_blockscale.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src, objdir=OBJDIR, extra=()):
     obj = os.path.join(objdir, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

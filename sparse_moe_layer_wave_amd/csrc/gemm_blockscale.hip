@@ -11,30 +11,37 @@
 //
 // Tiles and work order are those of the grouped GEMMs (grouped_order.h): a
 // persistent grid of one workgroup per CU, 256 x 256 square tiles and
-// 128 x 512 wide tiles, four waves each owning 128 x 128 outputs (4 x 4
-// blocks of 32 x 32).  K advances in slices of 128
-// e4m3 values, exactly one k-block, and a wave's weight rows lie in one
-// 128-row block (down) or are 64 gate rows and 64 up rows, each in one block
+// 128 x 512 wide tiles.  A workgroup has eight waves (two per SIMD), each
+// owning 128 token rows x 64 weight rows (4 x 2 blocks of 32 x 32): 128 fp32
+// accumulators per lane, so they stay in VGPRs next to the fragments and the
+// rescale below is one multiply per element (with four waves of 128 x 128
+// the accumulators alone fill the VGPR file and every rescale moves them in
+// and out of AGPRs).  K advances in slices of 128 e4m3 values, exactly one
+// k-block, and a wave's weight rows lie in one 128-row block (down) or are
+// 32 gate rows and the 32 up rows of the same h columns, each in one block
 // (gate_up), so every slice has one scale per wave (down) or two (gate_up).
-// A block's product over the slice is accumulated from zero by two
-// v_mfma_scale_f32_32x32x64_f8f6f4 steps (unit hardware scales) into a
-// temporary, which is multiplied by its scale and added to the block's
-// accumulator during the next block's MFMAs, so the adds do not wait on
-// theirs.  Per slice and wave that is 32 MFMAs and 256 fused multiply-adds.  A lane keeps
-// the scales of k-blocks l and 64 + l of each of its wave's row blocks and
-// reads the slice's with readlane (K <= 16384).
+// Each scale is split as s = m * 2^e with |m| in [1, 2).  The two
+// v_mfma_scale_f32_32x32x64_f8f6f4 steps of a slice apply 2^e themselves,
+// through the E8M0 scale of their B operand (exact), relative to the largest
+// exponent of the row block, and accumulate straight into the block's fp32
+// accumulator, which is kept divided by the current mantissa: before a
+// slice's MFMAs it is multiplied by m_prev / m (a ratio in (1/2, 2)), and
+// after the last slice by m_last * 2^E.  Per slice and wave that is 16 MFMAs
+// and 128 multiplies, the multiplies of a block two MFMAs after its last
+// MFMA of the slice.  A lane keeps the scales of k-blocks l and 64 + l of
+// each of its wave's row blocks and reads the slice's with readlane
+// (K <= 16384).
 //
 // Copies are global_load_lds_dwordx4 into LDS rings laid out as in the
 // grouped GEMMs (square: token rows 2 slots, weight rows 3 slots of 32 KB;
-// wide: 2 slots of 80 KB).  Slice schedule: every fragment of slice kt is in
-// registers before its first MFMA -- it was read while slice kt - 1 ran.
-// While slice kt runs, the fragments of slice kt + 1 take the registers of
-// those of slice kt as soon as their last MFMA has issued (the token-row
-// fragments after each row of blocks, the weight-row fragments during the
-// last row), and the copies of slice kt + 2 (square tiles: token rows; wide
-// tiles: everything) and kt + 3 (square tiles: weight rows) refill the slots
-// slice kt came from.  One wait and one barrier per slice, at its end: slice
-// kt + 2 has landed and every wave is done reading slice kt + 1.
+// wide: 2 slots of 80 KB).  A slice runs k step 0 of its 8 blocks, then a
+// barrier, then k step 1.  Registers hold one k step of token fragments and
+// both k steps of weight fragments: during k step 0 the k-step-1 fragments
+// of the same slice replace the retiring ones, during k step 1 those of the
+// next slice's k step 0.  The barrier marks the slice's slot as read by
+// every wave (and the next slice as landed), so the copies of slice kt + 2
+// (square tiles: token rows; wide tiles: everything) and kt + 3 (square
+// tiles: weight rows) go out into it during k step 1.
 //
 // LDS rows are 128 bytes with 16-byte chunk c of row r at c ^ ((r >> 1) & 7).
 // MFMA lane layout: A lane l holds row l % 32 and bytes 32 (l / 32)..+32 of
@@ -63,21 +70,55 @@ struct BlkArgs {
     int K, N, E, npanel;         // K in elements (= bytes per row); npanel: 512-row panels per expert
 };
 
-__device__ __forceinline__ f32x16_t mfma_f8(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// fp8 MFMA whose B operand is scaled by 2^(sb - 127) (an E8M0 exponent,
+// exact), A unscaled.
+__device__ __forceinline__ f32x16_t mfma_f8(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
-// One tile.  SQUARE: 256 rows x 256 weight rows; else 128 x 512.
+// Per-slice scale of one weight row block, split as s = m * 2^e with |m| in
+// [1, 2): the MFMAs apply 2^(e - E) through their B-operand scale (E: the
+// largest exponent among the block's k-blocks, so the shift is <= 0 and
+// clamped at 2^-127), and the accumulator is kept divided by the current m,
+// so it is multiplied by r = m_prev / m before the slice's products are
+// added.  After the last k-block the accumulator times m_last * 2^E is the
+// scaled sum: acc_kb = (1 / m_kb) sum_{j <= kb} m_j 2^(e_j - E) P_j.
+// A zero scale keeps r = 1 and m_prev and gets the smallest B scale, 2^-127:
+// its products (at most 2^25 in magnitude) then stay more than 2^100 below
+// anything they are added to.
+struct SliceScale {
+    float r;                                   // multiplier of the accumulator before this slice
+    int sb;                                    // E8M0 byte of the MFMA B scale
+};
+
+__device__ __forceinline__ SliceScale slice_scale(float s, int E, float& m_prev) {
+    int ex;
+    const float f = frexpf(s, &ex);            // s = f 2^ex, |f| in [0.5, 1)
+    const bool live = s != 0.f;
+    const float m = 2.f * f;
+    SliceScale o;
+    o.r = live ? m_prev / m : 1.f;
+    o.sb = live ? max(0, 127 + (ex - 1) - E) : 0;
+    if (live) m_prev = m;
+    return o;
+}
+
+constexpr int kWaves = 8;                      // waves per workgroup (two per SIMD)
+
+// One tile.  SQUARE: 256 token rows x 256 weight rows, waves 2 x 4; else
+// 128 x 512, waves 1 x 8.  A wave owns 128 token rows x 64 weight rows (gate_up:
+// 32 gate rows and the 32 up rows of the same h columns).
 template <bool GATE_UP, bool SQUARE>
 __device__ __forceinline__ void tile_blk(const BlkArgs& g, uint8_t* lds, const Unit& u, int wave) {
     constexpr int RA = SQUARE ? 256 : 128;         // token rows of a slice
-    constexpr int WCOLS = SQUARE ? 128 : 256;      // gate_up: h columns of the tile
-    constexpr int NCOLS = SQUARE ? 256 : 512;      // down: output columns of the tile
-    constexpr int ROWS = RA + NCOLS;
-    constexpr int NPW = SQUARE ? 16 : 20;          // 1 KB copies per wave per slice
+    constexpr int NB = SQUARE ? 256 : 512;         // weight rows of a slice
+    constexpr int WCOLS = NB / 2;                  // gate_up: h columns of the tile
+    constexpr int ROWS = RA + NB;
+    constexpr int NPW = ROWS / 8 / kWaves;         // 1 KB copies per wave per slice (8; 10)
     constexpr int kASlot = RA * kRowB;             // square: token ring slot (32 KB)
-    constexpr int kBSlot = NCOLS * kRowB;          // square: weight ring slot (32 KB)
+    constexpr int kBSlot = NB * kRowB;             // square: weight ring slot (32 KB)
     constexpr int kSlotBytes = ROWS * kRowB;       // wide: ring slot (80 KB)
+    constexpr int WN = SQUARE ? 4 : 8;             // waves along the weight rows
     static_assert(SQUARE ? 2 * kASlot + 3 * kBSlot <= kLdsBytes : 2 * kSlotBytes <= kLdsBytes, "LDS");
     const int N = g.N, K = g.K;
     const int nk = K / kRowB;
@@ -88,11 +129,13 @@ __device__ __forceinline__ void tile_blk(const BlkArgs& g, uint8_t* lds, const U
 
     // ---- copy sources: a copy fills 8 LDS rows of 128 bytes (lane -> row
     // + lane / 8, physical chunk lane % 8); the lane keeps the 32-bit index
-    // of its source row per copy.  Square: copy j < 8 of a wave fills token
-    // row group 8 wave + j, copy 8 + j weight row group 8 wave + j; wide:
-    // copy j fills row group 20 wave + j of the single ring.
-    auto is_a = [&](int j) { return SQUARE ? j < 8 : 8 * (wave * NPW + j) < RA; };
-    auto group = [&](int j) { return SQUARE ? 8 * wave + (j & 7) : wave * NPW + j; };
+    // of its source row per copy.  Square: copy j < 4 of a wave fills token
+    // row group 4 wave + j, copy 4 + j weight row group 4 wave + j; wide:
+    // copy j fills row group 10 wave + j of the single ring (token rows
+    // first).  Weight panel row p of a gate_up tile is, in groups of 64, 32
+    // gate rows and the 32 up rows of the same h columns.
+    auto is_a = [&](int j) { return SQUARE ? j < 4 : NPW * wave + j < RA / 8; };
+    auto group = [&](int j) { return SQUARE ? 4 * wave + (j & 3) : NPW * wave + j; };
     const uint8_t* We = g.W + static_cast<size_t>(u.e) * (GATE_UP ? 2 * N : N) * K;
     int srow_of[NPW];
 #pragma unroll
@@ -105,10 +148,10 @@ __device__ __forceinline__ void tile_blk(const BlkArgs& g, uint8_t* lds, const U
             const int p = SQUARE ? row : row - RA;             // weight panel row
             int wr;
             if (GATE_UP) {
-                const int col = u.n * WCOLS + (p >> 7) * 64 + (p & 63);
-                wr = col < N ? ((p & 64) ? N + col : col) : 0;
+                const int col = u.n * WCOLS + (p >> 6) * 32 + (p & 31);
+                wr = col < N ? ((p & 32) ? N + col : col) : 0;
             } else {
-                wr = u.n * NCOLS + p;
+                wr = u.n * NB + p;
                 wr = wr < N ? wr : 0;
             }
             srow_of[j] = wr;
@@ -128,7 +171,7 @@ __device__ __forceinline__ void tile_blk(const BlkArgs& g, uint8_t* lds, const U
     // ---- block scales of the wave's weight rows (gate and up row blocks;
     // down: one row block).  A wave whose columns lie past N (a partial
     // panel) gets scale 0 and contributes nothing.
-    const int cw = GATE_UP ? u.n * WCOLS + wn * 64 : u.n * NCOLS + wn * 128;
+    const int cw = GATE_UP ? u.n * WCOLS + wn * 32 : u.n * NB + wn * 64;
     const int KB = nk;
     const int nrb = (GATE_UP ? 2 * N : N) >> 7;
     const float* se = g.w_scale + static_cast<size_t>(u.e) * nrb * KB;
@@ -148,6 +191,18 @@ __device__ __forceinline__ void tile_blk(const BlkArgs& g, uint8_t* lds, const U
         const float v = kt < 64 ? lo : hi;
         return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kt & 63));
     };
+    // largest exponent among the nonzero scales of each row block (0 if none)
+    auto emax = [&](float lo, float hi) {
+        int e = -1000, ex;
+        if (lo != 0.f) { frexpf(lo, &ex); e = max(e, ex - 1); }
+        if (hi != 0.f) { frexpf(hi, &ex); e = max(e, ex - 1); }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) e = max(e, __shfl_xor(e, o));
+        return e == -1000 ? 0 : e;
+    };
+    const int E0 = emax(sa_lo, sa_hi);
+    const int E1 = GATE_UP ? emax(sb_lo, sb_hi) : E0;
+    float m0 = 1.f, m1 = 1.f;                          // current mantissas (row block 0, 1)
 
     // ---- fragments: token rows a0 + 32 mb + l32 and weight rows b0 + 32 nb
     // + l32 of their slots; k step s of a slice is chunks 4 s..4 s + 3, the
@@ -155,7 +210,7 @@ __device__ __forceinline__ void tile_blk(const BlkArgs& g, uint8_t* lds, const U
     const int l32 = lane & 31;
     const int khalf = lane >> 5;
     const int a0 = wm * 128;
-    const int b0 = (SQUARE ? 0 : RA) + wn * 128;
+    const int b0 = (SQUARE ? 0 : RA) + wn * 64;
     int off[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -167,100 +222,120 @@ __device__ __forceinline__ void tile_blk(const BlkArgs& g, uint8_t* lds, const U
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x16_t{};
-    i32x8_t fa[4][2], fb[4][2];                        // [block][k step] of the current slice
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16_t{};
+    // token fragments of one k step (they roll from k step 0 to 1 and on to
+    // the next slice's k step 0 as they retire), weight fragments of both
+    i32x8_t fa[4], fb[2][2];
 
-    // The 16 blocks of a slice, in row order.  Block b's product goes to
-    // P[b % 2]; its scaled add runs during the next block, half after each of
-    // that block's two MFMAs (the MFMA it reads issued before them), so the
-    // adds share the issue slots with MFMAs in flight.  The adds of a slice's
-    // last block run in the first block of the next slice, with the scales
-    // it carries (pm_lo, pm_hi).  Fragments of slice kt + 1 are read from
-    // (na, nb_) as the current ones retire; copy(b) issues the copies that
-    // follow block b.
-    f32x16_t P[2];
+    // A slice: k step 0 of its 8 blocks (row-major), a barrier, k step 1.
+    //  - k step 0 reads slice kt's k-step-1 token fragments (a row's after
+    //    its last k-step-0 MFMA) and weight fragments (first thing) from its
+    //    slot; the barrier after it (slice kt + 1 has landed, every wave is
+    //    done reading slice kt) frees the slot;
+    //  - k step 1 reads slice kt + 1's k-step-0 fragments from its slot (the
+    //    weight ones first, the token ones as a row retires) and copy(i)
+    //    issues copies into the freed slot after MFMA 8 + i.
+    // Rescales: block b = 2 mb + nb is multiplied by the next slice's ratio
+    // after MFMA 10 + b (two MFMAs after its last one): blocks 0..5 during k
+    // step 1 with qn; blocks 6 and 7 after MFMAs 0 and 1 of the next slice,
+    // with that slice's ratio, qc (in slice 0 they are still zero).
+    auto rescale = [&](int b, float r) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) P[i] = f32x16_t{};
-    float pm_lo = 0.f, pm_hi = 0.f;                    // scales of the previous slice
-    auto add_half = [&](int blk, int half, float lo, float hi) {
-        const int pm = blk >> 2, pn = blk & 3;
-        const float sc = pn < 2 ? lo : hi;             // gate_up: gate rows, then up rows
-#pragma unroll
-        for (int q = 8 * half; q < 8 * half + 8; ++q) acc[pm][pn][q] = __builtin_fmaf(P[blk & 1][q], sc, acc[pm][pn][q]);
+        for (int e = 0; e < 16; ++e) acc[b >> 1][b & 1][e] *= r;
     };
-    auto run_slice = [&](int kt, const uint8_t* na, const uint8_t* nb_, auto copy) {
-        const float s_lo = scale_of(sa_lo, sa_hi, kt);           // down; gate_up: gate rows
-        const float s_hi = GATE_UP ? scale_of(sb_lo, sb_hi, kt) : s_lo;   // gate_up: up rows
+    auto ratio = [&](int b, const SliceScale& q0, const SliceScale& q1) { return (GATE_UP && (b & 1)) ? q1.r : q0.r; };
+    auto run_slice = [&](const SliceScale& qc0, const SliceScale& qc1, const SliceScale& qn0,
+                         const SliceScale& qn1, const uint8_t* ca, const uint8_t* cb, const uint8_t* na,
+                         const uint8_t* nb_, auto mid_wait, auto copy) {
 #pragma unroll
-        for (int b = 0; b < 16; ++b) {
-            const int mb = b >> 2, nb = b & 3;
-            const int pend = (b + 15) & 15;            // block b - 1 (of this slice or the last)
-            P[b & 1] = mfma_f8(fa[mb][0], fb[nb][0], f32x16_t{});
-            __builtin_amdgcn_sched_barrier(0);
-            add_half(pend, 0, b < 1 ? pm_lo : s_lo, b < 1 ? pm_hi : s_hi);
-            __builtin_amdgcn_sched_barrier(0);
-            P[b & 1] = mfma_f8(fa[mb][1], fb[nb][1], P[b & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            add_half(pend, 1, b < 1 ? pm_lo : s_lo, b < 1 ? pm_hi : s_hi);
-            if (nb == 3) {
-                fa[mb][0] = frag(na, a0 + 32 * mb, 0);
-                fa[mb][1] = frag(na, a0 + 32 * mb, 1);
+        for (int p = 0; p < 8; ++p) {
+            const int mb = p >> 1, nb = p & 1;
+            acc[mb][nb] = mfma_f8(fa[mb], fb[nb][0], acc[mb][nb], (GATE_UP && nb) ? qc1.sb : qc0.sb);
+            if (p == 0) {
+                fb[0][1] = frag(cb, b0, 1);
+                fb[1][1] = frag(cb, b0 + 32, 1);
             }
-            if (mb == 3) {
-                fb[nb][0] = frag(nb_, b0 + 32 * nb, 0);
-                fb[nb][1] = frag(nb_, b0 + 32 * nb, 1);
-            }
-            copy(b);
+            if (p < 2) rescale(6 + p, ratio(6 + p, qc0, qc1));
+            if (nb == 1) fa[mb] = frag(ca, a0 + 32 * mb, 1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        pm_lo = s_lo;
-        pm_hi = s_hi;
+        mid_wait();
+        lds_barrier();
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int mb = p >> 1, nb = p & 1;
+            acc[mb][nb] = mfma_f8(fa[mb], fb[nb][1], acc[mb][nb], (GATE_UP && nb) ? qc1.sb : qc0.sb);
+            if (p == 0) {
+                fb[0][0] = frag(nb_, b0, 0);
+                fb[1][0] = frag(nb_, b0 + 32, 0);
+            }
+            if (p >= 2) rescale(p - 2, ratio(p - 2, qn0, qn1));
+            if (nb == 1) fa[mb] = frag(na, a0 + 32 * mb, 0);
+            copy(p);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // this slice's scales (kt) and the next one's (kt + 1; none past the last)
+    auto scales_of = [&](int kt, SliceScale& q0, SliceScale& q1) {
+        const float s0 = kt < nk ? scale_of(sa_lo, sa_hi, kt) : 0.f;
+        q0 = slice_scale(s0, E0, m0);                              // down; gate_up: gate rows
+        if (GATE_UP) {
+            const float s1 = kt < nk ? scale_of(sb_lo, sb_hi, kt) : 0.f;
+            q1 = slice_scale(s1, E1, m1);                          // up rows
+        } else {
+            q1 = q0;
+        }
+    };
+    SliceScale qc0, qc1, qn0, qn1;
+    scales_of(0, qc0, qc1);
+    auto first_frags = [&](const uint8_t* ca, const uint8_t* cb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = frag(ca, a0 + 32 * i, 0);
+        fb[0][0] = frag(cb, b0, 0);
+        fb[1][0] = frag(cb, b0 + 32, 0);
     };
 
     if constexpr (SQUARE) {
         // token ring (2 slots) at 0, weight ring (3 slots) after it.  Issue
-        // order per wave: B(0) A(0) B(1) A(1) B(2), then per slice kt: A(kt+2)
-        // B(kt+3), so "slice kt+2 landed" is vmcnt(8) at the end of slice kt.
+        // order per wave: B(0) A(0) B(1) A(1) B(2), then in slice kt: A(kt+2)
+        // B(kt+3) into the slots slice kt came from, so "slice kt+1 landed"
+        // is vmcnt(4) at the middle of slice kt.
         const uint32_t abase0 = lds0, bbase0 = lds0 + 2 * kASlot;
         const uint8_t* abuf = lds;
         const uint8_t* bbuf = lds + 2 * kASlot;
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
 #pragma unroll
-            for (int j = 8; j < 16; ++j) issue_copy(j, s, bbase0 + s * kBSlot);
+            for (int j = 4; j < 8; ++j) issue_copy(j, s, bbase0 + s * kBSlot);
             if (s < 2) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) issue_copy(j, s, abase0 + s * kASlot);
+                for (int j = 0; j < 4; ++j) issue_copy(j, s, abase0 + s * kASlot);
             }
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(24));     // slice 0 landed
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));     // slice 0 landed
         lds_barrier();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            fa[i][0] = frag(abuf, a0 + 32 * i, 0);
-            fa[i][1] = frag(abuf, a0 + 32 * i, 1);
-            fb[i][0] = frag(bbuf, b0 + 32 * i, 0);
-            fb[i][1] = frag(bbuf, b0 + 32 * i, 1);
-        }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));      // slice 1 landed
-        lds_barrier();
+        first_frags(abuf, bbuf);
         for (int kt = 0; kt < nk; ++kt) {
             const uint32_t afill = abase0 + (kt & 1) * kASlot;
             const uint32_t bfill = bbase0 + (kt % 3) * kBSlot;
-            run_slice(kt, abuf + ((kt + 1) & 1) * kASlot, bbuf + ((kt + 1) % 3) * kBSlot, [&](int b) {
-                if (b < 8) issue_copy(b, kt + 2, afill);
-                else issue_copy(b, kt + 3, bfill);
-            });
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));  // slice kt + 2 landed
-            lds_barrier();                             // and every wave has read slice kt + 1
+            scales_of(kt + 1, qn0, qn1);
+            run_slice(qc0, qc1, qn0, qn1, abuf + (kt & 1) * kASlot, bbuf + (kt % 3) * kBSlot,
+                      abuf + ((kt + 1) & 1) * kASlot, bbuf + ((kt + 1) % 3) * kBSlot,
+                      [&] { __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); },   // slice kt + 1 landed
+                      [&](int i) {
+                          if (i < 4) issue_copy(i, kt + 2, afill);
+                          else issue_copy(i, kt + 3, bfill);
+                      });
+            qc0 = qn0;
+            qc1 = qn1;
         }
     } else {
-        // one ring of 2 slots; the copies of slice kt + 2 go out over the
-        // first 10 blocks of slice kt
+        // one ring of 2 slots; the copies of slice kt + 2 go out in k step 1
+        // of slice kt, so "slice kt+1 landed" is vmcnt(0) at its middle
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -268,41 +343,39 @@ __device__ __forceinline__ void tile_blk(const BlkArgs& g, uint8_t* lds, const U
         }
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(NPW));    // slice 0 landed
         lds_barrier();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            fa[i][0] = frag(lds, a0 + 32 * i, 0);
-            fa[i][1] = frag(lds, a0 + 32 * i, 1);
-            fb[i][0] = frag(lds, b0 + 32 * i, 0);
-            fb[i][1] = frag(lds, b0 + 32 * i, 1);
-        }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));      // slice 1 landed
-        lds_barrier();
+        first_frags(lds, lds);
         for (int kt = 0; kt < nk; ++kt) {
             const uint32_t fill = lds0 + (kt & 1) * kSlotBytes;
+            const uint8_t* cur = lds + (kt & 1) * kSlotBytes;
             const uint8_t* nxt = lds + ((kt + 1) & 1) * kSlotBytes;
-            run_slice(kt, nxt, nxt, [&](int b) {
-                if (b < NPW / 2) {
-                    issue_copy(2 * b, kt + 2, fill);
-                    issue_copy(2 * b + 1, kt + 2, fill);
-                }
-            });
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // slice kt + 2 landed
-            lds_barrier();                             // and every wave has read slice kt + 1
+            scales_of(kt + 1, qn0, qn1);
+            run_slice(qc0, qc1, qn0, qn1, cur, cur, nxt, nxt,
+                      [&] { __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); },   // slice kt + 1 landed
+                      [&](int i) {
+                          issue_copy(i, kt + 2, fill);
+                          if (i + 8 < NPW) issue_copy(i + 8, kt + 2, fill);
+                      });
+            qc0 = qn0;
+            qc1 = qn1;
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));          // no copy may land after the tile ends
-    add_half(15, 0, pm_lo, pm_hi);                     // the last slice's last block
-    add_half(15, 1, pm_lo, pm_hi);
+    // the accumulators are the sums divided by m_last * 2^E: fold that back
+    // (row 3 already carries the ratio of the slice past the last, 1)
+    const float c0 = ldexpf(m0, E0), c1 = GATE_UP ? ldexpf(m1, E1) : c0;
 
-    // ---- epilogue: each wave stages its output block in LDS (rows padded
-    // by 16 bytes) and stores it as 16-byte chunks, whole rows per group of
-    // lanes; the tile's activation row scales are staged in LDS too.
-    constexpr int OCOLS = GATE_UP ? 64 : 128;          // output columns per wave
+    // ---- epilogue: each wave stages its 128 x 128-byte output block in LDS
+    // (rows padded by 16 bytes) and stores it as 16-byte chunks, whole rows
+    // per group of lanes; the tile's activation row scales are staged in LDS
+    // too, and (gate_up) each wave's per-row max |h|, so that one atomic per
+    // row and tile folds the tile's maximum into amax.
+    constexpr int OCOLS = GATE_UP ? 32 : 64;           // output columns per wave
     constexpr int OESZ = GATE_UP ? 4 : 2;              // bytes per output element
     constexpr int OPITCH = OCOLS * OESZ + 16;
-    static_assert(4 * 128 * OPITCH + RA * 4 <= kLdsBytes, "LDS");
+    static_assert(kWaves * 128 * OPITCH + RA * 4 + RA * WN * 4 <= kLdsBytes, "LDS");
     uint8_t* ow = lds + wave * (128 * OPITCH);
-    float* srow = reinterpret_cast<float*>(lds + 4 * 128 * OPITCH);
+    float* srow = reinterpret_cast<float*>(lds + kWaves * 128 * OPITCH);
+    float* hm = srow + RA;                             // gate_up: [RA][WN] max |h| per wave
     lds_barrier();                                     // every wave is done with the rings
     if (tid < RA) {
         const int r = min(tid, u.rows - 1);
@@ -317,27 +390,31 @@ __device__ __forceinline__ void tile_blk(const BlkArgs& g, uint8_t* lds, const U
             uint8_t* orow = ow + rl * OPITCH;
             const float sr = srow[a0 + rl];
             if constexpr (GATE_UP) {
-                float hmax = 0.f;
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const float hv = silu_mul(acc[mb][nb][j] * sr, acc[mb][nb + 2][j] * sr);
-                    *reinterpret_cast<float*>(orow + (32 * nb + l32) * 4) = hv;
-                    hmax = fmaxf(hmax, fabsf(hv));
-                }
+                const float hv = silu_mul(acc[mb][0][j] * c0 * sr, acc[mb][1][j] * c1 * sr);
+                *reinterpret_cast<float*>(orow + l32 * 4) = hv;
+                float hmax = fabsf(hv);
 #pragma unroll
                 for (int o = 16; o >= 1; o >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, o, 32));
-                if (l32 == 0 && a0 + rl < u.rows && cw < N)
-                    atomicMax(&g.amax[u.row0 + a0 + rl], __float_as_uint(hmax));
+                if (l32 == 0) hm[(a0 + rl) * WN + wn] = cw < N ? hmax : 0.f;
             } else {
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
-                    *reinterpret_cast<uint16_t*>(orow + (32 * nb + l32) * 2) = f32_to_bf16(acc[mb][nb][j] * sr);
+                for (int nb = 0; nb < 2; ++nb)
+                    *reinterpret_cast<uint16_t*>(orow + (32 * nb + l32) * 2) = f32_to_bf16(acc[mb][nb][j] * c0 * sr);
             }
+        }
+    }
+    if constexpr (GATE_UP) {
+        __syncthreads();
+        if (tid < RA && tid < u.rows) {
+            float m = 0.f;
+#pragma unroll
+            for (int w = 0; w < WN; ++w) m = fmaxf(m, hm[tid * WN + w]);
+            atomicMax(&g.amax[u.row0 + tid], __float_as_uint(m));
         }
     }
     // a wave's LDS accesses complete in order: it reads its block back
     // without a barrier
-    constexpr int CPR = OCOLS * OESZ / 16;             // 16-byte chunks per row
+    constexpr int CPR = OCOLS * OESZ / 16;             // 16-byte chunks per row (8)
     constexpr int EPC = 16 / OESZ;                     // elements per chunk
 #pragma unroll
     for (int it = 0; it < 128 * CPR / 64; ++it) {
@@ -355,7 +432,7 @@ __device__ __forceinline__ void tile_blk(const BlkArgs& g, uint8_t* lds, const U
 }
 
 template <bool GATE_UP>
-__global__ __launch_bounds__(256, 1) void k_grouped_blk(BlkArgs g) {
+__global__ __launch_bounds__(64 * kWaves, 1) void k_grouped_blk(BlkArgs g) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
     const int U = g.tile_off[g.E] * g.npanel;
     const int per_wg = gridDim.x / kXcds;          // workgroups per XCD (grid: a multiple of kXcds)
@@ -382,8 +459,8 @@ hipError_t launch_blk(BlkArgs g, bool gate_up, int max_blocks, hipStream_t s) {
     const hipError_t err = device_cu_count(&cus);
     if (err != hipSuccess) return err;
     const dim3 grid(persistent_grid(units, cus));
-    if (gate_up) hipLaunchKernelGGL(k_grouped_blk<true>, grid, dim3(256), 0, s, g);
-    else hipLaunchKernelGGL(k_grouped_blk<false>, grid, dim3(256), 0, s, g);
+    if (gate_up) hipLaunchKernelGGL(k_grouped_blk<true>, grid, dim3(64 * kWaves), 0, s, g);
+    else hipLaunchKernelGGL(k_grouped_blk<false>, grid, dim3(64 * kWaves), 0, s, g);
     return hipGetLastError();
 }
 
