@@ -44,11 +44,11 @@ SAN_DIR = os.path.join(OBJDIR, "san")
 SAN_LIB = os.path.join(SAN_DIR, "libhy3moe_san.so")
 
 
-# Flags of single files.  gemm_blockscale.hip: its accumulators are rescaled
+# Flags of single files.  gemm_grouped.hip: block-scale accumulators are rescaled
 # by VALU multiplies between MFMAs, so its MFMAs read and write them in VGPRs
 # rather than AGPRs (which would take a copy out and back per multiply).
 FILE_FLAGS = {
-    "gemm_blockscale.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "gemm_grouped.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
