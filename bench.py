@@ -171,15 +171,17 @@ def roofline(res, kernel, bound):
 
 
 def traffic(kernel, res):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, when
-    it was taken on the current kernel source; otherwise null."""
+    """HBM bytes per launch of the stage's kernels (summed: the e4m3 gate_up
+    stage is three) from the committed rocprofv3 counter summary, when it was
+    taken on the current kernel sources; otherwise null."""
     path = os.path.join(ROOT, "profiles", f"counters_{kernel}_{res['cfg']['name']}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "sparse_moe_layer_wave_amd", "csrc", rec["source"])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if sha != rec.get("source_sha"):
+    h = hashlib.sha256()
+    for src in [rec["source"]] if isinstance(rec["source"], str) else rec["source"]:
+        h.update(open(os.path.join(ROOT, "sparse_moe_layer_wave_amd", "csrc", src), "rb").read())
+    if h.hexdigest()[:16] != rec.get("source_sha"):
         return None
     return rec.get("bytes_per_launch")
 

@@ -11,7 +11,10 @@
 they read for the run's first device copy (bench.py --copy-calibration copies
 1 GiB before anything else), so "bytes" means bytes as a plain copy of known
 size counts them.  The traffic JSON is what bench.py reports as
-roofline.traffic while the kernel's source file is unchanged (sha256 prefix).
+roofline.traffic while the kernels' source files are unchanged (sha256
+prefix of their contents, in order).  --kernel and --source may repeat: a
+stage of several kernels (the e4m3 gate_up stage: x quantiser, GEMM, h
+quantiser) gets the sum of their per-call traffic.
 """
 
 import argparse
@@ -68,10 +71,10 @@ def main():
     ap.add_argument("--command", required=True, help="the command lines that produced the inputs")
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic-json")
-    ap.add_argument("--kernel", help="kernel name (substring) for the traffic JSON")
+    ap.add_argument("--kernel", action="append", help="kernel name for the traffic JSON (repeat: summed)")
     ap.add_argument("--grid-x", type=int, help="grid of that kernel's launch (default: any)")
     ap.add_argument("--grid-y", type=int)
-    ap.add_argument("--source", help="source file (under csrc/) of that kernel")
+    ap.add_argument("--source", action="append", help="source file (under csrc/) of those kernels (repeatable)")
     ap.add_argument("--workload", default="hy3_decode_T64")
     args = ap.parse_args()
 
@@ -90,7 +93,8 @@ def main():
     lines.append("| kernel | grid (threads) | block | calls | avg us | min us | fetch MB/call | write MB/call |")
     lines.append("|---|---|---|---|---|---|---|---|")
     rows = sorted(trace.items(), key=lambda kv: -sum(kv[1]))
-    traffic = None
+    kernels = args.kernel or []
+    part = {}
     for (name, gx, gy, gz, bx), durs in rows:
         if "hy3" not in name and "k_" not in name:
             continue
@@ -103,20 +107,22 @@ def main():
                 fmb = f"{sum(fv) / len(fv) * 1024 * fscale / 1e6:.1f}"
             if wv and wscale:
                 wmb = f"{sum(wv) / len(wv) * 1024 * wscale / 1e6:.1f}"
-            if (args.kernel and args.kernel == name
-                    and args.grid_x in (None, gx) and args.grid_y in (None, gy)
+            if (name in kernels and (len(kernels) > 1 or (args.grid_x in (None, gx) and args.grid_y in (None, gy)))
                     and fv and wv and fscale and wscale):
-                traffic = (sum(fv) / len(fv) * 1024 * fscale + sum(wv) / len(wv) * 1024 * wscale)
+                part[name] = (sum(fv) / len(fv) * 1024 * fscale + sum(wv) / len(wv) * 1024 * wscale)
         lines.append(f"| {name} | ({gx},{gy},{gz}) | {bx} | {len(durs)} | "
                      f"{sum(durs) / len(durs) / 1e3:.1f} | {min(durs) / 1e3:.1f} | {fmb} | {wmb} |")
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
     open(args.out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
-    if args.traffic_json and traffic is not None:
-        src = os.path.join(PKG, "csrc", args.source)
-        rec = {"kernel": args.kernel, "workload": args.workload, "source": args.source,
-               "source_sha": hashlib.sha256(open(src, "rb").read()).hexdigest()[:16],
-               "bytes_per_launch": round(traffic),
+    if args.traffic_json and kernels and all(k in part for k in kernels):
+        h = hashlib.sha256()
+        for src in args.source:
+            h.update(open(os.path.join(PKG, "csrc", src), "rb").read())
+        one = lambda v: v[0] if len(v) == 1 else v
+        rec = {"kernel": one(kernels), "workload": args.workload, "source": one(args.source),
+               "source_sha": h.hexdigest()[:16],
+               "bytes_per_launch": round(sum(part.values())),
                "how": "FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by a 1 GiB copy"}
         json.dump(rec, open(args.traffic_json, "w"), indent=1)
         print("traffic", rec)
