@@ -46,9 +46,10 @@
 // weight fragments: during k step 0 the k-step-1 fragments of the same
 // slice replace the retiring ones, during k step 1 those of the next slice's
 // k step 0.  The barrier marks the slice's slot as read by every wave (and
-// the next slice as landed), so the copies of slice kt + 2 (square tiles:
-// token rows; wide tiles: everything) and kt + 3 (square tiles: weight rows)
-// go out into it during k step 1.
+// the next slice as landed), so the copies of slice kt + 2 go out into it
+// during k step 1 (square tiles: token rows; wide tiles: everything); a
+// square tile's weight rows of slice kt + 2 go out during k step 0, into
+// the third weight slot, freed by the barrier of slice kt - 1.
 //
 // Block scales: each scale is split as s = m * 2^e with |m| in [1, 2).  The
 // MFMAs apply 2^e themselves, through the E8M0 scale of their B operand
@@ -283,8 +284,8 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
     //    slot; the barrier after it (slice kt + 1 has landed, every wave is
     //    done reading slice kt) frees the slot;
     //  - k step 1 reads slice kt + 1's k-step-0 fragments from its slot (the
-    //    weight ones first, the token ones as a row retires) and copy(i)
-    //    issues copies into the freed slot after block i.
+    //    weight ones first, the token ones as a row retires).
+    // copy0(i) / copy1(i) issue the copies that follow block i of k step 0 / 1.
     // Block scales: block b = 2 mb + nb is multiplied by the next slice's
     // ratio after block 2 + b of k step 1 (two blocks after its last MFMA):
     // blocks 0..5 during k step 1 with qn; blocks 6 and 7 after blocks 0 and
@@ -302,7 +303,7 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
     };
     auto run_slice = [&](const SliceScale& qc0, const SliceScale& qc1, const SliceScale& qn0,
                          const SliceScale& qn1, const uint8_t* ca, const uint8_t* cb, const uint8_t* na,
-                         const uint8_t* nb_, auto mid_wait, auto copy) {
+                         const uint8_t* nb_, auto mid_wait, auto copy0, auto copy1) {
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
             const int mb = p >> 1, nb = p & 1;
@@ -313,6 +314,7 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
             }
             if (BLK && p < 2) rescale(6 + p, ratio(6 + p, qc0, qc1));
             if (nb == 1) fa[mb] = frag(ca, a0 + 32 * mb, 1);
+            copy0(p);
             __builtin_amdgcn_sched_barrier(0);
         }
         mid_wait();
@@ -327,7 +329,7 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
             }
             if (BLK && p >= 2) rescale(p - 2, ratio(p - 2, qn0, qn1));
             if (nb == 1) fa[mb] = frag(na, a0 + 32 * mb, 0);
-            copy(p);
+            copy1(p);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -357,34 +359,36 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
 
     if constexpr (SQUARE) {
         // token ring (2 slots) at 0, weight ring (3 slots) after it.  Issue
-        // order per wave: B(0) A(0) B(1) A(1) B(2), then in slice kt: A(kt+2)
-        // B(kt+3) into the slots slice kt came from, so "slice kt+1 landed"
-        // is vmcnt(4) at the middle of slice kt.
+        // order per wave: B(0) A(0) B(1) A(1), then in slice kt: B(kt+2)
+        // during k step 0, into the weight slot slice kt - 1 came from (free
+        // since the middle of slice kt - 1), and A(kt+2) during k step 1,
+        // into the token slot of slice kt; so "slice kt+1 landed" is vmcnt(4)
+        // at the middle of slice kt, and the copies are spread over the slice.
         const uint32_t abase0 = lds0, bbase0 = lds0 + 2 * kASlot;
         const uint8_t* abuf = lds;
         const uint8_t* bbuf = lds + 2 * kASlot;
 #pragma unroll
-        for (int s = 0; s < 3; ++s) {
+        for (int s = 0; s < 2; ++s) {
 #pragma unroll
             for (int j = 4; j < 8; ++j) issue_copy(j, s, bbase0 + s * kBSlot);
-            if (s < 2) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) issue_copy(j, s, abase0 + s * kASlot);
-            }
+            for (int j = 0; j < 4; ++j) issue_copy(j, s, abase0 + s * kASlot);
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));     // slice 0 landed
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));      // slice 0 landed
         lds_barrier();
         first_frags(abuf, bbuf);
         for (int kt = 0; kt < nk; ++kt) {
             const uint32_t afill = abase0 + (kt & 1) * kASlot;
-            const uint32_t bfill = bbase0 + (kt % 3) * kBSlot;
+            const uint32_t bfill = bbase0 + ((kt + 2) % 3) * kBSlot;
             scales_of(kt + 1, qn0, qn1);
             run_slice(qc0, qc1, qn0, qn1, abuf + (kt & 1) * kASlot, bbuf + (kt % 3) * kBSlot,
                       abuf + ((kt + 1) & 1) * kASlot, bbuf + ((kt + 1) % 3) * kBSlot,
                       [&] { __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); },   // slice kt + 1 landed
                       [&](int i) {
-                          if (i < 4) issue_copy(i, kt + 2, afill);
-                          else issue_copy(i, kt + 3, bfill);
+                          if (i & 1) issue_copy(4 + (i >> 1), kt + 2, bfill);
+                      },
+                      [&](int i) {
+                          if (i & 1) issue_copy(i >> 1, kt + 2, afill);
                       });
             qc0 = qn0;
             qc1 = qn1;
@@ -407,6 +411,7 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
             scales_of(kt + 1, qn0, qn1);
             run_slice(qc0, qc1, qn0, qn1, cur, cur, nxt, nxt,
                       [&] { __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); },   // slice kt + 1 landed
+                      [](int) {},
                       [&](int i) {
                           issue_copy(i, kt + 2, fill);
                           if (i + 8 < NPW) issue_copy(i + 8, kt + 2, fill);
