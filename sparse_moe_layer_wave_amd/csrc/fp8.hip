@@ -24,61 +24,102 @@ __device__ float block_max(float v, float* lds) {
     return v;
 }
 
-// One workgroup per row of bf16 input.
+// Four codes of one 8-byte group of bf16 pairs (p = two bf16 values).
+__device__ __forceinline__ uint32_t quant_pair2(uint32_t p0, uint32_t p1, float r) {
+    return static_cast<uint32_t>(f32_to_e4m3(__uint_as_float(p0 << 16) * r)) |
+           (static_cast<uint32_t>(f32_to_e4m3(__uint_as_float(p0 & 0xffff0000u) * r)) << 8) |
+           (static_cast<uint32_t>(f32_to_e4m3(__uint_as_float(p1 << 16) * r)) << 16) |
+           (static_cast<uint32_t>(f32_to_e4m3(__uint_as_float(p1 & 0xffff0000u) * r)) << 24);
+}
+
+__device__ __forceinline__ float amax8(const uint4& v, float m) {
+    const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m = fmaxf(m, fabsf(__uint_as_float(p[i] << 16)));
+        m = fmaxf(m, fabsf(__uint_as_float(p[i] & 0xffff0000u)));
+    }
+    return m;
+}
+
+// One workgroup per row of bf16 input; a thread takes 8 values per step of
+// kQThreads * 8 columns.  Rows of at most NV steps are read once, into
+// registers (NV > 0); longer rows (NV = 0) are read twice, for the max and
+// for the codes.
+template <int NV>
 __global__ __launch_bounds__(kQThreads) void k_quant_rows_bf16(const uint16_t* __restrict__ x,
                                                               int cols, uint8_t* __restrict__ q,
                                                               float* __restrict__ s) {
     __shared__ float lds[kQThreads / 64];
     const size_t row = blockIdx.x;
     const uint16_t* xr = x + row * cols;
+    uint8_t* qr = q + row * cols;
     float amax = 0.f;
-    for (int c = threadIdx.x * 8; c < cols; c += kQThreads * 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
-        const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (NV > 0) {
+        uint4 v[NV];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            amax = fmaxf(amax, fabsf(__uint_as_float(p[i] << 16)));
-            amax = fmaxf(amax, fabsf(__uint_as_float(p[i] & 0xffff0000u)));
+        for (int i = 0; i < NV; ++i) {
+            const int c = (i * kQThreads + threadIdx.x) * 8;
+            v[i] = c < cols ? *reinterpret_cast<const uint4*>(xr + c) : make_uint4(0, 0, 0, 0);
         }
-    }
-    amax = block_max(amax, lds);
-    const float r = amax > 0.f ? 448.0f / amax : 0.f;
-    for (int c = threadIdx.x * 8; c < cols; c += kQThreads * 8) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
-        const uint32_t p[4] = {v.x, v.y, v.z, v.w};
-        uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t c0 = f32_to_e4m3(__uint_as_float(p[i] << 16) * r);
-            const uint32_t c1 = f32_to_e4m3(__uint_as_float(p[i] & 0xffff0000u) * r);
-            const uint32_t pair = c0 | (c1 << 8);
-            if (i < 2) lo |= pair << (16 * i);
-            else hi |= pair << (16 * (i - 2));
+        for (int i = 0; i < NV; ++i) amax = amax8(v[i], amax);
+        amax = block_max(amax, lds);
+        const float r = amax > 0.f ? 448.0f / amax : 0.f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int c = (i * kQThreads + threadIdx.x) * 8;
+            if (c < cols)
+                *reinterpret_cast<uint2*>(qr + c) = make_uint2(quant_pair2(v[i].x, v[i].y, r), quant_pair2(v[i].z, v[i].w, r));
         }
-        *reinterpret_cast<uint2*>(q + row * cols + c) = make_uint2(lo, hi);
+    } else {
+        for (int c = threadIdx.x * 8; c < cols; c += kQThreads * 8)
+            amax = amax8(*reinterpret_cast<const uint4*>(xr + c), amax);
+        amax = block_max(amax, lds);
+        const float r = amax > 0.f ? 448.0f / amax : 0.f;
+        for (int c = threadIdx.x * 8; c < cols; c += kQThreads * 8) {
+            const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
+            *reinterpret_cast<uint2*>(qr + c) = make_uint2(quant_pair2(v.x, v.y, r), quant_pair2(v.z, v.w, r));
+        }
     }
     if (threadIdx.x == 0) s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
 }
 
 // h rows (fp32) with their max |h| already reduced into amax (bit patterns):
-// the same quantiser as above, one workgroup per row.
+// the same quantiser as above, one wave per row (kQThreads / 64 rows per
+// workgroup); a lane takes 4 values per step of 256 columns and keeps up to
+// 8 steps' loads in flight.
+constexpr int kRowsPerWg = kQThreads / 64;
+
 __global__ __launch_bounds__(kQThreads) void k_quant_rows_f32(const float* __restrict__ h,
                                                              const uint32_t* __restrict__ amax_bits,
-                                                             int cols, uint8_t* __restrict__ q,
+                                                             int rows, int cols, uint8_t* __restrict__ q,
                                                              float* __restrict__ s) {
-    const size_t row = blockIdx.x;
+    const size_t row = static_cast<size_t>(blockIdx.x) * kRowsPerWg + (threadIdx.x >> 6);
+    if (row >= static_cast<size_t>(rows)) return;
+    const int lane = threadIdx.x & 63;
     const float amax = __uint_as_float(amax_bits[row]);
     const float r = amax > 0.f ? 448.0f / amax : 0.f;
     const float* hr = h + row * cols;
-    for (int c = threadIdx.x * 4; c < cols; c += kQThreads * 4) {
-        const float4 v = *reinterpret_cast<const float4*>(hr + c);
-        const uint32_t packed = static_cast<uint32_t>(f32_to_e4m3(v.x * r)) |
-                                (static_cast<uint32_t>(f32_to_e4m3(v.y * r)) << 8) |
-                                (static_cast<uint32_t>(f32_to_e4m3(v.z * r)) << 16) |
-                                (static_cast<uint32_t>(f32_to_e4m3(v.w * r)) << 24);
-        *reinterpret_cast<uint32_t*>(q + row * cols + c) = packed;
+    uint8_t* qr = q + row * cols;
+    for (int base = 0; base < cols; base += 8 * 256) {
+        float4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = base + (i * 64 + lane) * 4;
+            v[i] = c < cols ? *reinterpret_cast<const float4*>(hr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = base + (i * 64 + lane) * 4;
+            if (c < cols)
+                *reinterpret_cast<uint32_t*>(qr + c) = static_cast<uint32_t>(f32_to_e4m3(v[i].x * r)) |
+                                                       (static_cast<uint32_t>(f32_to_e4m3(v[i].y * r)) << 8) |
+                                                       (static_cast<uint32_t>(f32_to_e4m3(v[i].z * r)) << 16) |
+                                                       (static_cast<uint32_t>(f32_to_e4m3(v[i].w * r)) << 24);
+        }
     }
-    if (threadIdx.x == 0) s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+    if (lane == 0) s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
 }
 
 __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, size_t n, uint32_t v) {
@@ -91,7 +132,9 @@ __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, size
 
 hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, int rows, int cols,
                                  uint8_t* q, float* s, hipStream_t st) {
-    hipLaunchKernelGGL(k_quant_rows_f32, dim3(rows), dim3(kQThreads), 0, st, h, amax_bits, cols, q, s);
+    if (rows == 0) return hipSuccess;
+    const unsigned wgs = static_cast<unsigned>((static_cast<long long>(rows) + kRowsPerWg - 1) / kRowsPerWg);
+    hipLaunchKernelGGL(k_quant_rows_f32, dim3(wgs), dim3(kQThreads), 0, st, h, amax_bits, rows, cols, q, s);
     return hipGetLastError();
 }
 
@@ -103,7 +146,12 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
 
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,
                              hipStream_t st) {
-    hipLaunchKernelGGL(k_quant_rows_bf16, dim3(rows), dim3(kQThreads), 0, st, x, cols, q, s);
+    if (rows == 0) return hipSuccess;
+    const int steps = (cols + kQThreads * 8 - 1) / (kQThreads * 8);
+    if (steps <= 1) hipLaunchKernelGGL(k_quant_rows_bf16<1>, dim3(rows), dim3(kQThreads), 0, st, x, cols, q, s);
+    else if (steps <= 2) hipLaunchKernelGGL(k_quant_rows_bf16<2>, dim3(rows), dim3(kQThreads), 0, st, x, cols, q, s);
+    else if (steps <= 4) hipLaunchKernelGGL(k_quant_rows_bf16<4>, dim3(rows), dim3(kQThreads), 0, st, x, cols, q, s);
+    else hipLaunchKernelGGL(k_quant_rows_bf16<0>, dim3(rows), dim3(kQThreads), 0, st, x, cols, q, s);
     return hipGetLastError();
 }
 
