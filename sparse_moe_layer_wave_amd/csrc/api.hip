@@ -79,7 +79,9 @@ Layout make_layout(int T, int d, int E, int k, int F, int dtype, bool shared = f
         L.h = take(Tk * F * sizeof(float));            // fp32 SwiGLU activations
         L.hq = take(Tk * F);                           // their e4m3 codes
         L.hs = take(Tk * sizeof(float));               // per-row scale
-        L.amax = take(Tk * sizeof(uint32_t));          // per-row max |h| (bit pattern)
+        // per-row max |h|: [Tk] bit patterns (weight-streaming gate_up, atomics)
+        // or [F / 128][Tk] partial maxima (grouped gate_up)
+        L.amax = take(Tk * ((F + 127) / 128) * sizeof(float));
         L.xq = take(static_cast<size_t>(T) * d);
         L.xs = take(static_cast<size_t>(T) * sizeof(float));
     } else {
@@ -375,19 +377,23 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
                                  decode ? hy3::decode_bm(rg) : hy3::prefill_bm(), row_of, tok_of, 0, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
     if (e == hipSuccess) e = hy3::launch_quant_rows(x, T, d, xq, xs, s);
-    if (e == hipSuccess) e = hy3::launch_fill_u32(amax, Tk, 0u, s);
+    float* hmax = reinterpret_cast<float*>(amax);
+    const int nblk = (d_ff + 127) / 128;
+    if (e == hipSuccess && decode) e = hy3::launch_fill_u32(amax, Tk, 0u, s);
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_gate_up_decode_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, max_slices,
                                                h32, amax, E, d, d_ff, rg, block, s);
         else if (block)
             e = hy3::launch_gate_up_fp8_block(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off,
-                                              L.max_mtiles, h32, amax, E, d, d_ff, s);
+                                              L.max_mtiles, h32, hmax, static_cast<int>(Tk), E, d, d_ff, s);
         else
             e = hy3::launch_gate_up_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, L.max_mtiles,
-                                        h32, amax, E, d, d_ff, s);
+                                        h32, hmax, static_cast<int>(Tk), E, d, d_ff, s);
     }
-    if (e == hipSuccess) e = hy3::launch_quant_rows_f32(h32, amax, static_cast<int>(Tk), d_ff, hq, hs, s);
+    if (e == hipSuccess)
+        e = hy3::launch_quant_rows_f32(h32, decode ? amax : nullptr, decode ? nullptr : hmax, nblk,
+                                       static_cast<int>(Tk), d_ff, hq, hs, s);
     if (e == hipSuccess) e = mark(ev, 3, s);
     if (e == hipSuccess) {
         if (decode)

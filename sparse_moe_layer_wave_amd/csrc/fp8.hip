@@ -85,20 +85,31 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_bf16(const uint16_t* _
     if (threadIdx.x == 0) s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
 }
 
-// h rows (fp32) with their max |h| already reduced into amax (bit patterns):
-// the same quantiser as above, one wave per row (kQThreads / 64 rows per
-// workgroup); a lane takes 4 values per step of 256 columns and keeps up to
-// 8 steps' loads in flight.
+// h rows (fp32) with their max |h| already reduced into amax (bit patterns),
+// or (amax_bits NULL) given as nblk partial maxima per row, hmax[blk * rows +
+// row]: the same quantiser as above, one wave per row (kQThreads / 64 rows
+// per workgroup); a lane takes 4 values per step of 256 columns and keeps up
+// to 8 steps' loads in flight.
 constexpr int kRowsPerWg = kQThreads / 64;
 
 __global__ __launch_bounds__(kQThreads) void k_quant_rows_f32(const float* __restrict__ h,
                                                              const uint32_t* __restrict__ amax_bits,
+                                                             const float* __restrict__ hmax, int nblk,
                                                              int rows, int cols, uint8_t* __restrict__ q,
                                                              float* __restrict__ s) {
     const size_t row = static_cast<size_t>(blockIdx.x) * kRowsPerWg + (threadIdx.x >> 6);
     if (row >= static_cast<size_t>(rows)) return;
     const int lane = threadIdx.x & 63;
-    const float amax = __uint_as_float(amax_bits[row]);
+    float amax;
+    if (amax_bits) {
+        amax = __uint_as_float(amax_bits[row]);
+    } else {
+        float m = 0.f;
+        for (int b = lane; b < nblk; b += 64) m = fmaxf(m, hmax[static_cast<size_t>(b) * rows + row]);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        amax = m;
+    }
     const float r = amax > 0.f ? 448.0f / amax : 0.f;
     const float* hr = h + row * cols;
     uint8_t* qr = q + row * cols;
@@ -130,11 +141,12 @@ __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, size
 
 }  // namespace
 
-hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, int rows, int cols,
-                                 uint8_t* q, float* s, hipStream_t st) {
+hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, const float* hmax, int nblk,
+                                 int rows, int cols, uint8_t* q, float* s, hipStream_t st) {
     if (rows == 0) return hipSuccess;
     const unsigned wgs = static_cast<unsigned>((static_cast<long long>(rows) + kRowsPerWg - 1) / kRowsPerWg);
-    hipLaunchKernelGGL(k_quant_rows_f32, dim3(wgs), dim3(kQThreads), 0, st, h, amax_bits, rows, cols, q, s);
+    hipLaunchKernelGGL(k_quant_rows_f32, dim3(wgs), dim3(kQThreads), 0, st, h, amax_bits, hmax, nblk, rows, cols,
+                       q, s);
     return hipGetLastError();
 }
 

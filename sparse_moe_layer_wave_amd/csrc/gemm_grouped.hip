@@ -7,9 +7,10 @@
 //            architecture teardown", section 2.3: the fused gate_up
 //            projection, gate rows first).  bf16: h stored as bf16.  e4m3:
 //            the two products are rescaled by the token's activation scale
-//            and the weights' scales, h is stored as fp32 and the row's max
-//            |h| is folded into amax[r] (an integer atomic max on the bit
-//            pattern of |h|) for the per-row quantisation of h that follows;
+//            and the weights' scales, h is stored as fp32, and each tile
+//            stores its rows' max |h| over each 128-column block it covers
+//            into hmax[block][r], for the per-row quantisation of h that
+//            follows (which takes the max over the blocks);
 //   down:    y[r, n] = h[r] . Wd[e][n] (e4m3: rescaled by the row's and the
 //            weights' scales), stored as bf16.
 //
@@ -92,7 +93,8 @@ struct Args {
     const float* a_scale;                          // e4m3: per token (gate_up) or per row (down)
     const float* w_scale;                          // per channel: [E, 2N] or [E, N]; block: [E, rows_w/128, K/128]
     float* h32;                                    // e4m3 gate_up: h [rows, N] fp32
-    uint32_t* amax;                                // e4m3 gate_up: [rows] bits of max |h|
+    float* hmax;                                   // e4m3 gate_up: [N / 128][rows] max |h| per 128-column block
+    int rows;                                      // e4m3 gate_up: rows of h (the stride of hmax)
     int K, N, E, npanel;                           // K in elements; npanel: weight panels per expert
 };
 
@@ -427,8 +429,9 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
     // lanes: 8x fewer store instructions than storing the MFMA layout (one
     // column per lane) directly.  e4m3: the tile's activation row scales are
     // staged in LDS too (one load per thread, all in flight together), and
-    // (gate_up) each wave's per-row max |h|, so that one atomic per row and
-    // tile folds the tile's maximum into amax.
+    // (gate_up) each wave's per-row max |h|, combined into one max per row
+    // and 128-column block of the tile and stored (no atomics: each block of
+    // a row belongs to one tile).
     constexpr int OCOLS = GATE_UP ? 32 : 64;           // output columns per wave
     constexpr int OESZ = (GATE_UP && FP8) ? 4 : 2;     // bytes per output element
     constexpr int OPITCH = OCOLS * OESZ + 16;
@@ -473,13 +476,8 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
                     *reinterpret_cast<uint16_t*>(orow + (32 * nb + l32) * 2) = f32_to_bf16(acc[mb][nb][j]);
             } else if constexpr (GATE_UP) {
                 const float sr = srow[a0 + rl];
-                const float hv = silu_mul(acc[mb][0][j] * cs[0] * sr, acc[mb][1][j] * cs[1] * sr);
-                *reinterpret_cast<float*>(orow + l32 * 4) = hv;
-                float hmax = fabsf(hv);
-                // row max over the 32 lanes that share this row (same khalf)
-#pragma unroll
-                for (int o = 16; o >= 1; o >>= 1) hmax = fmaxf(hmax, __shfl_xor(hmax, o, 32));
-                if (l32 == 0) hm[(a0 + rl) * WN + wn] = cw < N ? hmax : 0.f;
+                *reinterpret_cast<float*>(orow + l32 * 4) =
+                    silu_mul(acc[mb][0][j] * cs[0] * sr, acc[mb][1][j] * cs[1] * sr);
             } else {
                 const float sr = srow[a0 + rl];
 #pragma unroll
@@ -489,12 +487,34 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
         }
     }
     if constexpr (GATE_UP && FP8) {
-        __syncthreads();
-        if (tid < RA && tid < u.rows) {
+        // each row's max |h| over the wave's 32 columns, read back from the
+        // staged block (a wave's LDS accesses complete in order): two rows
+        // per lane, instead of a 5-step cross-lane reduction per row
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int rl = lane + 64 * q;
             float m = 0.f;
 #pragma unroll
-            for (int w = 0; w < WN; ++w) m = fmaxf(m, hm[tid * WN + w]);
-            atomicMax(&g.amax[u.row0 + tid], __float_as_uint(m));
+            for (int c = 0; c < 32; c += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(ow + rl * OPITCH + c * 4);
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
+            hm[(a0 + rl) * WN + wn] = cw < N ? m : 0.f;
+        }
+        // a 128-column block is 4 waves' columns: square tiles have one,
+        // wide tiles two (the second may lie past N)
+        __syncthreads();
+        if (tid < RA && tid < u.rows) {
+#pragma unroll
+            for (int cb = 0; cb < WN / 4; ++cb) {
+                const int blk = u.n * (WCOLS / 128) + cb;
+                if (blk * 128 < N) {
+                    float m = 0.f;
+#pragma unroll
+                    for (int w = 4 * cb; w < 4 * cb + 4; ++w) m = fmaxf(m, hm[tid * WN + w]);
+                    g.hmax[static_cast<size_t>(blk) * g.rows + u.row0 + tid] = m;
+                }
+            }
         }
     }
     // a wave's LDS accesses complete in order: it reads its block back
@@ -567,7 +587,7 @@ hipError_t launch_gate_up_grouped(const uint16_t* x, const int32_t* tok_of, cons
                                   int F, hipStream_t s) {
     Args g{reinterpret_cast<const uint8_t*>(x), tok_of, reinterpret_cast<const uint8_t*>(W_gu),
            reinterpret_cast<const uint8_t*>(W_last), offsets, tile_off, h, nullptr, nullptr, nullptr,
-           nullptr, d, F, E, 0};
+           nullptr, 0, d, F, E, 0};
     return launch<GU_BF16>(g, max_blocks, s);
 }
 
@@ -576,37 +596,37 @@ hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const ui
                                uint16_t* y, int E, int d, int F, hipStream_t s) {
     Args g{reinterpret_cast<const uint8_t*>(h), nullptr, reinterpret_cast<const uint8_t*>(W_dn),
            reinterpret_cast<const uint8_t*>(W_last), offsets, tile_off, y, nullptr, nullptr, nullptr,
-           nullptr, F, d, E, 0};
+           nullptr, 0, F, d, E, 0};
     return launch<DN_BF16>(g, max_blocks, s);
 }
 
 hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                               const uint8_t* Wq, const float* ws, const int32_t* offsets,
-                              const int32_t* tile_off, int max_blocks, float* h32, uint32_t* amax,
-                              int E, int d, int F, hipStream_t s) {
-    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, xs, ws, h32, amax, d, F, E, 0};
+                              const int32_t* tile_off, int max_blocks, float* h32, float* hmax,
+                              int rows, int E, int d, int F, hipStream_t s) {
+    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, xs, ws, h32, hmax, rows, d, F, E, 0};
     return launch<GU_FP8>(g, max_blocks, s);
 }
 
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq, const float* ws,
                            const int32_t* offsets, const int32_t* tile_off, int max_blocks,
                            uint16_t* y, int E, int d, int F, hipStream_t s) {
-    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, ws, nullptr, nullptr, F, d, E, 0};
+    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, ws, nullptr, nullptr, 0, F, d, E, 0};
     return launch<DN_FP8>(g, max_blocks, s);
 }
 
 hipError_t launch_gate_up_fp8_block(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                                     const uint8_t* Wq, const float* sb, const int32_t* offsets,
                                     const int32_t* tile_off, int max_mtiles, float* h32,
-                                    uint32_t* amax, int E, int d, int F, hipStream_t s) {
-    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, xs, sb, h32, amax, d, F, E, 0};
+                                    float* hmax, int rows, int E, int d, int F, hipStream_t s) {
+    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, xs, sb, h32, hmax, rows, d, F, E, 0};
     return launch<GU_BLK>(g, max_mtiles, s);
 }
 
 hipError_t launch_down_fp8_block(const uint8_t* hq, const float* hs, const uint8_t* Wq,
                                  const float* sb, const int32_t* offsets, const int32_t* tile_off,
                                  int max_mtiles, uint16_t* y, int E, int d, int F, hipStream_t s) {
-    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, sb, nullptr, nullptr, F, d, E, 0};
+    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, sb, nullptr, nullptr, 0, F, d, E, 0};
     return launch<DN_BLK>(g, max_mtiles, s);
 }
 

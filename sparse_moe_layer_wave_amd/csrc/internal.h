@@ -182,13 +182,16 @@ hipError_t launch_block_counts(const int32_t* idx, int T, int E, int k, int nb,
                                int32_t* blk_counts, hipStream_t s);
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,
                              hipStream_t st);
-hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, int rows, int cols,
-                                 uint8_t* q, float* s, hipStream_t st);
+// h rows' max |h|: amax_bits [rows] (bit patterns; the weight-streaming
+// gate_up folds them in with atomics), or, with amax_bits NULL, the max over
+// the nblk partial maxima hmax[blk * rows + row] (the grouped gate_up's).
+hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, const float* hmax, int nblk,
+                                 int rows, int cols, uint8_t* q, float* s, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
 hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                               const uint8_t* Wq, const float* ws, const int32_t* offsets,
-                              const int32_t* tile_off, int max_mtiles, float* h32, uint32_t* amax,
-                              int E, int d, int F, hipStream_t s);
+                              const int32_t* tile_off, int max_mtiles, float* h32, float* hmax,
+                              int rows, int E, int d, int F, hipStream_t s);
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq, const float* ws,
                            const int32_t* offsets, const int32_t* tile_off, int max_mtiles,
                            uint16_t* y, int E, int d, int F, hipStream_t s);
@@ -211,7 +214,7 @@ hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint
 hipError_t launch_gate_up_fp8_block(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                                     const uint8_t* Wq, const float* sb, const int32_t* offsets,
                                     const int32_t* tile_off, int max_mtiles, float* h32,
-                                    uint32_t* amax, int E, int d, int F, hipStream_t s);
+                                    float* hmax, int rows, int E, int d, int F, hipStream_t s);
 hipError_t launch_down_fp8_block(const uint8_t* hq, const float* hs, const uint8_t* Wq,
                                  const float* sb, const int32_t* offsets, const int32_t* tile_off,
                                  int max_mtiles, uint16_t* y, int E, int d, int F, hipStream_t s);
