@@ -89,6 +89,7 @@ Layout make_layout(int T, int d, int E, int k, int F, int dtype, bool shared = f
         L.hq = L.hs = L.xq = L.xs = L.amax = 0;
     }
     L.y = take(R * d * sizeof(uint16_t));
+    L.sched = take(hy3::kSchedInts * sizeof(int));    // the grouped GEMMs' work counters
     L.total = off;
     return L;
 }
@@ -313,13 +314,16 @@ static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_ep
                                  decode ? hy3::decode_bm(rg) : hy3::prefill_bm(), row_of, tok_of,
                                  shared ? 1 : 0, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
+    int* sched = reinterpret_cast<int*>(ws + L.sched);
+    if (e == hipSuccess && !decode)
+        e = hy3::launch_fill_u32(reinterpret_cast<uint32_t*>(sched), hy3::kSchedInts, 0u, s);
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_gate_up_decode(x, tok_of, W_gate_up, Ws_gu, offsets, tile_off, max_slices,
                                            h, Eg, d, d_ff, rg, s);
         else
             e = hy3::launch_gate_up_grouped(x, tok_of, W_gate_up, Ws_gu, offsets, tile_off,
-                                            L.max_mtiles, h, Eg, d, d_ff, s);
+                                            L.max_mtiles, h, sched, Eg, d, d_ff, s);
     }
     if (e == hipSuccess) e = mark(ev, 3, s);
     if (e == hipSuccess) {
@@ -327,8 +331,8 @@ static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_ep
             e = hy3::launch_down_decode(h, W_down, Ws_dn, offsets, tile_off, max_slices, y, Eg, d,
                                         d_ff, rg, s);
         else
-            e = hy3::launch_down_grouped(h, W_down, Ws_dn, offsets, tile_off, L.max_mtiles, y, Eg, d,
-                                         d_ff, s);
+            e = hy3::launch_down_grouped(h, W_down, Ws_dn, offsets, tile_off, L.max_mtiles, y, sched, Eg,
+                                         d, d_ff, s);
     }
     if (e == hipSuccess) e = mark(ev, 4, s);
     if (e == hipSuccess) {
@@ -379,17 +383,20 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
     if (e == hipSuccess) e = hy3::launch_quant_rows(x, T, d, xq, xs, s);
     float* hmax = reinterpret_cast<float*>(amax);
     const int nblk = (d_ff + 127) / 128;
+    int* sched = reinterpret_cast<int*>(ws + L.sched);
     if (e == hipSuccess && decode) e = hy3::launch_fill_u32(amax, Tk, 0u, s);
+    if (e == hipSuccess && !decode)
+        e = hy3::launch_fill_u32(reinterpret_cast<uint32_t*>(sched), hy3::kSchedInts, 0u, s);
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_gate_up_decode_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, max_slices,
                                                h32, amax, E, d, d_ff, rg, block, s);
         else if (block)
             e = hy3::launch_gate_up_fp8_block(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off,
-                                              L.max_mtiles, h32, hmax, static_cast<int>(Tk), E, d, d_ff, s);
+                                              L.max_mtiles, h32, hmax, static_cast<int>(Tk), sched, E, d, d_ff, s);
         else
             e = hy3::launch_gate_up_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, L.max_mtiles,
-                                        h32, hmax, static_cast<int>(Tk), E, d, d_ff, s);
+                                        h32, hmax, static_cast<int>(Tk), sched, E, d, d_ff, s);
     }
     if (e == hipSuccess)
         e = hy3::launch_quant_rows_f32(h32, decode ? amax : nullptr, decode ? nullptr : hmax, nblk,
@@ -400,11 +407,11 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
             e = hy3::launch_down_decode_fp8(hq, hs, Wq_dn, s_dn, offsets, tile_off, max_slices, y, E, d,
                                             d_ff, rg, block, s);
         else if (block)
-            e = hy3::launch_down_fp8_block(hq, hs, Wq_dn, s_dn, offsets, tile_off, L.max_mtiles, y, E,
-                                           d, d_ff, s);
+            e = hy3::launch_down_fp8_block(hq, hs, Wq_dn, s_dn, offsets, tile_off, L.max_mtiles, y, sched,
+                                           E, d, d_ff, s);
         else
-            e = hy3::launch_down_fp8(hq, hs, Wq_dn, s_dn, offsets, tile_off, L.max_mtiles, y, E, d,
-                                     d_ff, s);
+            e = hy3::launch_down_fp8(hq, hs, Wq_dn, s_dn, offsets, tile_off, L.max_mtiles, y, sched, E,
+                                     d, d_ff, s);
     }
     if (e == hipSuccess) e = mark(ev, 4, s);
     if (e == hipSuccess) e = hy3::launch_combine(y, row_of, w, out, T, d, k, -1, s);

@@ -95,8 +95,13 @@ struct Args {
     float* h32;                                    // e4m3 gate_up: h [rows, N] fp32
     float* hmax;                                   // e4m3 gate_up: [N / 128][rows] max |h| per 128-column block
     int rows;                                      // e4m3 gate_up: rows of h (the stride of hmax)
+    int* sched;                                    // [kXcds] unit counters, zero at launch
     int K, N, E, npanel;                           // K in elements; npanel: weight panels per expert
 };
+
+// The last 64 bytes of LDS: the word through which a claimed unit is
+// broadcast (clear of the epilogue's staging).
+constexpr int kClaimOff = kLdsBytes - 64;
 
 // e4m3 MFMA whose B operand is scaled by 2^(sb - 127) (an E8M0 exponent,
 // exact), A unscaled.
@@ -138,9 +143,11 @@ __device__ __forceinline__ SliceScale slice_scale(float s, int E, float& m_prev)
     return o;
 }
 
-// One tile.  SQUARE: 256 rows x 256 weight rows; else 128 x 512.
+// One tile.  SQUARE: 256 rows x 256 weight rows; else 128 x 512.  claim, if
+// not NULL, is a unit counter: thread 0 takes the next unit from it during
+// the epilogue and leaves the value in LDS (kClaimOff).
 template <int MODE, bool SQUARE>
-__device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u, int wave) {
+__device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u, int wave, int* claim) {
     constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8 || MODE == GU_BLK;
     constexpr bool FP8 = MODE >= GU_FP8;
     constexpr bool BLK = MODE >= GU_BLK;
@@ -435,11 +442,13 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
     constexpr int OCOLS = GATE_UP ? 32 : 64;           // output columns per wave
     constexpr int OESZ = (GATE_UP && FP8) ? 4 : 2;     // bytes per output element
     constexpr int OPITCH = OCOLS * OESZ + 16;
-    static_assert(kWaves * 128 * OPITCH + RA * 4 + RA * WN * 4 <= kLdsBytes, "LDS");
+    static_assert(kWaves * 128 * OPITCH + RA * 4 + RA * WN * 4 <= kClaimOff, "LDS");
     uint8_t* ow = lds + wave * (128 * OPITCH);
     float* srow = reinterpret_cast<float*>(lds + kWaves * 128 * OPITCH);
     float* hm = srow + RA;                             // e4m3 gate_up: [RA][WN] max |h| per wave
     lds_barrier();                                     // every wave is done with the rings
+    int claimed = 0;
+    if (claim && tid == 0) claimed = atomicAdd(claim, 1);
     if constexpr (FP8) {
         if (tid < RA) {
             const int r = min(tid, u.rows - 1);
@@ -534,32 +543,69 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
             else *reinterpret_cast<i32x4_t*>(g.C + grow * N + c) = v;
         }
     }
+    if (claim && tid == 0) *reinterpret_cast<int*>(lds + kClaimOff) = claimed;
 }
 
 // Persistent: one workgroup per CU, workgroup b on XCD b % 8 (the dispatcher
 // deals workgroups round-robin over the XCDs).  The units are split into 8
-// contiguous ranges, one per XCD, and the XCD's workgroups take its range
-// round-robin, so at any time an XCD works on consecutive units (one
-// expert's tiles, reading the same weight panels and token rows through its
-// L2).
+// contiguous ranges, one per XCD, so at any time an XCD works on consecutive
+// units (one expert's tiles, reading the same weight panels and token rows
+// through its L2).  A workgroup takes the unit of its XCD's range at its own
+// index, then claims the next ones from the XCD's counter (g.sched[x]),
+// each during the epilogue of the tile before, so the claim's latency is
+// hidden; once its XCD's range is used up, it claims from the other XCDs'
+// counters in turn.  Tile times vary with how much of each tile's data hits
+// L2, and claiming keeps the workgroups finishing together (a static
+// round-robin left 9-10% of workgroup time idle at the end).
 template <int MODE>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_grouped(Args g) {
     constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8 || MODE == GU_BLK;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+    int* cl = reinterpret_cast<int*>(lds + kClaimOff);
     const int U = g.tile_off[g.E] * g.npanel;
     const int per_wg = gridDim.x / kXcds;          // workgroups per XCD (grid: a multiple of kXcds)
     const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
     const int per_xcd = (U + kXcds - 1) / kXcds;
     int wave;                                      // opaque: not recomputed from the thread index later
     asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(wave) : "v"(static_cast<int>(threadIdx.x) >> 6));
-    const int end = min((x + 1) * per_xcd, U);
-    for (int L = x * per_xcd + j; L < end; L += per_wg) {
-        Unit u;
-        bool square;
-        if (!unit_of<GATE_UP>(g.tile_off, g.offsets, g.E, g.npanel, g.N, L, u, square)) continue;
-        if (square) tile<MODE, true>(g, lds, u, wave);
-        else tile<MODE, false>(g, lds, u, wave);
-        lds_barrier();                             // every wave has read its staged output back
+    int src = x;                                   // XCD whose counter the claims go to
+    int tried = 0;                                 // ranges found used up
+    Unit u;                                        // the unit being decoded (its expert is the next hint)
+    u.e = -1;
+    bool square = false;
+    auto decode = [&](int L) {
+        return unit_of<GATE_UP>(g.tile_off, g.offsets, g.E, g.npanel, g.N, L, u, square, u.e);
+    };
+    // value v taken from counter src -> a unit with work, decoded into u
+    // (-1: none left), claiming again while the unit is empty or src's range
+    // is used up (uniform control flow: every thread runs the same iterations)
+    auto resolve = [&](int v) {
+        for (;;) {
+            const int L = src * per_xcd + per_wg + v;
+            if (L < min((src + 1) * per_xcd, U)) {
+                if (decode(L)) return L;
+            } else {
+                if (++tried >= kXcds) return -1;
+                src = (src + 1) % kXcds;
+            }
+            __syncthreads();                       // every thread has read *cl
+            if (threadIdx.x == 0) *cl = atomicAdd(g.sched + src, 1);
+            __syncthreads();
+            v = __builtin_amdgcn_readfirstlane(*cl);
+        }
+    };
+    int cur = x * per_xcd + j;
+    if (!(cur < min((x + 1) * per_xcd, U) && decode(cur))) {
+        if (threadIdx.x == 0) *cl = atomicAdd(g.sched + src, 1);
+        __syncthreads();
+        cur = resolve(__builtin_amdgcn_readfirstlane(*cl));
+    }
+    while (cur >= 0) {
+        int* claim = tried < kXcds ? g.sched + src : nullptr;
+        if (square) tile<MODE, true>(g, lds, u, wave, claim);
+        else tile<MODE, false>(g, lds, u, wave, claim);
+        lds_barrier();                             // staged output read back, *cl written
+        cur = claim ? resolve(__builtin_amdgcn_readfirstlane(*cl)) : -1;
     }
 }
 
@@ -573,6 +619,7 @@ hipError_t launch(Args g, int max_blocks, hipStream_t s) {
     const hipError_t err = device_cu_count(&cus);
     if (err != hipSuccess) return err;
     const int grid = persistent_grid(units, cus);
+    g.sched += GATE_UP ? 0 : kXcds;                // gate_up and down each have their own counters
     hipLaunchKernelGGL(k_grouped<MODE>, dim3(grid), dim3(64 * kWaves), 0, s, g);
     return hipGetLastError();
 }
@@ -583,50 +630,50 @@ int prefill_bm() { return 128; }
 
 hipError_t launch_gate_up_grouped(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
                                   const uint16_t* W_last, const int32_t* offsets,
-                                  const int32_t* tile_off, int max_blocks, uint16_t* h, int E, int d,
-                                  int F, hipStream_t s) {
+                                  const int32_t* tile_off, int max_blocks, uint16_t* h, int* sched, int E,
+                                  int d, int F, hipStream_t s) {
     Args g{reinterpret_cast<const uint8_t*>(x), tok_of, reinterpret_cast<const uint8_t*>(W_gu),
            reinterpret_cast<const uint8_t*>(W_last), offsets, tile_off, h, nullptr, nullptr, nullptr,
-           nullptr, 0, d, F, E, 0};
+           nullptr, 0, sched, d, F, E, 0};
     return launch<GU_BF16>(g, max_blocks, s);
 }
 
 hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const uint16_t* W_last,
                                const int32_t* offsets, const int32_t* tile_off, int max_blocks,
-                               uint16_t* y, int E, int d, int F, hipStream_t s) {
+                               uint16_t* y, int* sched, int E, int d, int F, hipStream_t s) {
     Args g{reinterpret_cast<const uint8_t*>(h), nullptr, reinterpret_cast<const uint8_t*>(W_dn),
            reinterpret_cast<const uint8_t*>(W_last), offsets, tile_off, y, nullptr, nullptr, nullptr,
-           nullptr, 0, F, d, E, 0};
+           nullptr, 0, sched, F, d, E, 0};
     return launch<DN_BF16>(g, max_blocks, s);
 }
 
 hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                               const uint8_t* Wq, const float* ws, const int32_t* offsets,
                               const int32_t* tile_off, int max_blocks, float* h32, float* hmax,
-                              int rows, int E, int d, int F, hipStream_t s) {
-    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, xs, ws, h32, hmax, rows, d, F, E, 0};
+                              int rows, int* sched, int E, int d, int F, hipStream_t s) {
+    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, xs, ws, h32, hmax, rows, sched, d, F, E, 0};
     return launch<GU_FP8>(g, max_blocks, s);
 }
 
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq, const float* ws,
                            const int32_t* offsets, const int32_t* tile_off, int max_blocks,
-                           uint16_t* y, int E, int d, int F, hipStream_t s) {
-    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, ws, nullptr, nullptr, 0, F, d, E, 0};
+                           uint16_t* y, int* sched, int E, int d, int F, hipStream_t s) {
+    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, ws, nullptr, nullptr, 0, sched, F, d, E, 0};
     return launch<DN_FP8>(g, max_blocks, s);
 }
 
 hipError_t launch_gate_up_fp8_block(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                                     const uint8_t* Wq, const float* sb, const int32_t* offsets,
                                     const int32_t* tile_off, int max_mtiles, float* h32,
-                                    float* hmax, int rows, int E, int d, int F, hipStream_t s) {
-    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, xs, sb, h32, hmax, rows, d, F, E, 0};
+                                    float* hmax, int rows, int* sched, int E, int d, int F, hipStream_t s) {
+    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, xs, sb, h32, hmax, rows, sched, d, F, E, 0};
     return launch<GU_BLK>(g, max_mtiles, s);
 }
 
 hipError_t launch_down_fp8_block(const uint8_t* hq, const float* hs, const uint8_t* Wq,
                                  const float* sb, const int32_t* offsets, const int32_t* tile_off,
-                                 int max_mtiles, uint16_t* y, int E, int d, int F, hipStream_t s) {
-    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, sb, nullptr, nullptr, 0, F, d, E, 0};
+                                 int max_mtiles, uint16_t* y, int* sched, int E, int d, int F, hipStream_t s) {
+    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, sb, nullptr, nullptr, 0, sched, F, d, E, 0};
     return launch<DN_BLK>(g, max_mtiles, s);
 }
 

@@ -42,8 +42,18 @@ __device__ __forceinline__ int pchunk8(int row, int c) { return c ^ ((row >> 1) 
 // column tile of a partial last panel (nothing to compute).
 template <bool GATE_UP>
 __device__ __forceinline__ bool unit_of(const int32_t* tile_off, const int32_t* offsets, int E,
-                                        int npanel, int N, int L, Unit& u, bool& square) {
-    int lo = 0, hi = E - 1;                    // expert: last e with tile_off[e] * npanel <= L
+                                        int npanel, int N, int L, Unit& u, bool& square, int hint = -1) {
+    // expert: last e with tile_off[e] * npanel <= L; the hint (the expert of
+    // the previous unit) is tried first, then the expert after it, with
+    // independent loads, before a binary search
+    int lo = 0, hi = E - 1;
+    if (hint >= 0 && hint + 1 < E) {
+        const int a = __builtin_amdgcn_readfirstlane(tile_off[hint]) * npanel;
+        const int b = __builtin_amdgcn_readfirstlane(tile_off[hint + 1]) * npanel;
+        const int c = hint + 2 <= E ? __builtin_amdgcn_readfirstlane(tile_off[hint + 2]) * npanel : b;
+        if (a <= L && L < b) lo = hi = hint;
+        else if (b <= L && L < c) lo = hi = hint + 1;
+    }
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (tile_off[mid] * npanel <= L) lo = mid;

@@ -82,7 +82,7 @@ hipError_t device_cu_count(int* cus);
 // Workspace carving, computed identically on the host for every entry point.
 struct Layout {
     size_t planes, partial, scores, blk_counts, blk_base, counts, offsets, tile_off, idx, w,
-        row_of, tok_of, h, y, xq, xs, hq, hs, amax, xn, total;
+        row_of, tok_of, h, y, xq, xs, hq, hs, amax, xn, sched, total;
     int nb;              // routing blocks
     int nsplit;          // router d-chunks
     int max_mtiles;      // upper bound on row blocks of the grouped GEMMs
@@ -121,15 +121,18 @@ hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
 // prefill-sized batches: MFMA grouped GEMMs over row blocks of prefill_bm() rows
 // (max_blocks bounds the number of row blocks, tile_off[E]).  E counts the
 // experts of offsets/tile_off; with W_last non-NULL the last of them is the
-// shared expert, whose weights are W_last instead of W[E - 1].
+// shared expert, whose weights are W_last instead of W[E - 1].  sched: the
+// work counters, kSchedInts ints, zero before the gate_up launch (gate_up and
+// down use halves of their own).
+constexpr int kSchedInts = 16;
 int prefill_bm();
 hipError_t launch_gate_up_grouped(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
                                   const uint16_t* W_last, const int32_t* offsets,
-                                  const int32_t* tile_off, int max_blocks, uint16_t* h, int E, int d,
-                                  int F, hipStream_t s);
+                                  const int32_t* tile_off, int max_blocks, uint16_t* h, int* sched, int E,
+                                  int d, int F, hipStream_t s);
 hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const uint16_t* W_last,
                                const int32_t* offsets, const int32_t* tile_off, int max_blocks,
-                               uint16_t* y, int E, int d, int F, hipStream_t s);
+                               uint16_t* y, int* sched, int E, int d, int F, hipStream_t s);
 
 // decode-sized batches: weight streaming, one workgroup per (expert, weight
 // slice); E and W_last as for the grouped GEMMs
@@ -191,10 +194,10 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
 hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                               const uint8_t* Wq, const float* ws, const int32_t* offsets,
                               const int32_t* tile_off, int max_mtiles, float* h32, float* hmax,
-                              int rows, int E, int d, int F, hipStream_t s);
+                              int rows, int* sched, int E, int d, int F, hipStream_t s);
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq, const float* ws,
                            const int32_t* offsets, const int32_t* tile_off, int max_mtiles,
-                           uint16_t* y, int E, int d, int F, hipStream_t s);
+                           uint16_t* y, int* sched, int E, int d, int F, hipStream_t s);
 // decode-sized batches with e4m3 experts (weight streaming, as the bf16 ones).
 // block: ws holds one fp32 scale per 128 x 128 weight block, [E, rows/128,
 // K/128] (rows = 2F for gate_up, d for down; K = d, F), instead of one per
@@ -214,9 +217,9 @@ hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint
 hipError_t launch_gate_up_fp8_block(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                                     const uint8_t* Wq, const float* sb, const int32_t* offsets,
                                     const int32_t* tile_off, int max_mtiles, float* h32,
-                                    float* hmax, int rows, int E, int d, int F, hipStream_t s);
+                                    float* hmax, int rows, int* sched, int E, int d, int F, hipStream_t s);
 hipError_t launch_down_fp8_block(const uint8_t* hq, const float* hs, const uint8_t* Wq,
                                  const float* sb, const int32_t* offsets, const int32_t* tile_off,
-                                 int max_mtiles, uint16_t* y, int E, int d, int F, hipStream_t s);
+                                 int max_mtiles, uint16_t* y, int* sched, int E, int d, int F, hipStream_t s);
 
 }  // namespace hy3
