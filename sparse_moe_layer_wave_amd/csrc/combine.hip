@@ -5,7 +5,7 @@
 // "DeepSeek V4-Flash architecture Q&A", Q8.4).  With the full block's shared
 // expert ("Tencent Hy3-Flash Q&A", Q4.7) its output row for the token is
 // added last, with weight 1.  Memory-bound: k (+1) bf16 rows in, one fp32 row
-// out per token.
+// out per token; the k row loads of a column chunk are issued together.
 //
 // The bf16-output form also ends the decoder layer's residual branch (the
 // same blog: the residual add of section 3.2, done as section 2.3 describes
@@ -20,26 +20,33 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <bool BF16_OUT>
+// K: the number of routed slots (compile time, so that all of a column
+// chunk's K row loads are in flight before the sums, which keep slot order).
+template <bool BF16_OUT, int K>
 __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict__ y,
                                                      const int32_t* __restrict__ row_of,
                                                      const float* __restrict__ w,
-                                                     const uint16_t* resid, void* out, int d, int k,
+                                                     const uint16_t* resid, void* out, int d,
                                                      int shared_row0) {
     const int t = blockIdx.x;
     __shared__ int s_row[16];
     __shared__ float s_w[16];
-    if (static_cast<int>(threadIdx.x) < k) {
-        s_row[threadIdx.x] = row_of[static_cast<size_t>(t) * k + threadIdx.x];
-        s_w[threadIdx.x] = w[static_cast<size_t>(t) * k + threadIdx.x];
+    if (static_cast<int>(threadIdx.x) < K) {
+        s_row[threadIdx.x] = row_of[static_cast<size_t>(t) * K + threadIdx.x];
+        s_w[threadIdx.x] = w[static_cast<size_t>(t) * K + threadIdx.x];
     }
     __syncthreads();
     for (int c = threadIdx.x * 8; c < d; c += kThreads * 8) {
+        uint4 v[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = *reinterpret_cast<const uint4*>(y + static_cast<size_t>(s_row[j]) * d + c);
+        uint4 vs = make_uint4(0, 0, 0, 0);
+        if (shared_row0 >= 0) vs = *reinterpret_cast<const uint4*>(y + (static_cast<size_t>(shared_row0) + t) * d + c);
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < k; ++j) {
-            const uint4 v = *reinterpret_cast<const uint4*>(y + static_cast<size_t>(s_row[j]) * d + c);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
             const float wj = s_w[j];
-            const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+            const uint32_t p[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 acc[2 * i] = fmaf(wj, __uint_as_float(p[i] << 16), acc[2 * i]);
@@ -47,8 +54,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
             }
         }
         if (shared_row0 >= 0) {
-            const uint4 v = *reinterpret_cast<const uint4*>(y + (static_cast<size_t>(shared_row0) + t) * d + c);
-            const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+            const uint32_t p[4] = {vs.x, vs.y, vs.z, vs.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 acc[2 * i] += __uint_as_float(p[i] << 16);
@@ -58,8 +64,8 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
         if constexpr (BF16_OUT) {
             const size_t at = static_cast<size_t>(t) * d + c;
             if (resid) {
-                const uint4 v = *reinterpret_cast<const uint4*>(resid + at);
-                const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+                const uint4 r = *reinterpret_cast<const uint4*>(resid + at);
+                const uint32_t p[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     acc[2 * i] += __uint_as_float(p[i] << 16);
@@ -80,21 +86,36 @@ __global__ __launch_bounds__(kThreads) void k_combine(const uint16_t* __restrict
     }
 }
 
+template <bool BF16_OUT>
+hipError_t launch_k(const uint16_t* y, const int32_t* row_of, const float* w, const uint16_t* resid,
+                    void* out, int T, int d, int k, int shared_row0, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+#define HY3_COMBINE_K(KK)                                                                                    \
+    case KK:                                                                                                 \
+        hipLaunchKernelGGL((k_combine<BF16_OUT, KK>), dim3(T), dim3(kThreads), 0, s, y, row_of, w, resid, out, d, \
+                           shared_row0);                                                                    \
+        break;
+    switch (k) {
+        HY3_COMBINE_K(1) HY3_COMBINE_K(2) HY3_COMBINE_K(3) HY3_COMBINE_K(4) HY3_COMBINE_K(5) HY3_COMBINE_K(6)
+        HY3_COMBINE_K(7) HY3_COMBINE_K(8) HY3_COMBINE_K(9) HY3_COMBINE_K(10) HY3_COMBINE_K(11) HY3_COMBINE_K(12)
+        HY3_COMBINE_K(13) HY3_COMBINE_K(14) HY3_COMBINE_K(15) HY3_COMBINE_K(16)
+        default: return hipErrorInvalidValue;
+    }
+#undef HY3_COMBINE_K
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* row_of, const float* w, float* out,
                           int T, int d, int k, int shared_row0, hipStream_t s) {
-    hipLaunchKernelGGL(k_combine<false>, dim3(T), dim3(kThreads), 0, s, y, row_of, w, nullptr,
-                       static_cast<void*>(out), d, k, shared_row0);
-    return hipGetLastError();
+    return launch_k<false>(y, row_of, w, nullptr, static_cast<void*>(out), T, d, k, shared_row0, s);
 }
 
 hipError_t launch_combine_bf16(const uint16_t* y, const int32_t* row_of, const float* w,
                                const uint16_t* resid, uint16_t* out, int T, int d, int k,
                                int shared_row0, hipStream_t s) {
-    hipLaunchKernelGGL(k_combine<true>, dim3(T), dim3(kThreads), 0, s, y, row_of, w, resid,
-                       static_cast<void*>(out), d, k, shared_row0);
-    return hipGetLastError();
+    return launch_k<true>(y, row_of, w, resid, static_cast<void*>(out), T, d, k, shared_row0, s);
 }
 
 }  // namespace hy3
