@@ -1,5 +1,5 @@
-// Work order of the persistent grouped GEMMs (gemm_grouped.hip and
-// gemm_blockscale.hip): which tile a workgroup computes next.
+// Work order of the persistent grouped GEMMs (gemm_grouped.hip): which tile
+// a unit index stands for.
 //
 // An expert's rows are split into 128-row blocks; pairs of blocks run as
 // square tiles (256 rows x 256 weight rows) and an odd last block as a wide
@@ -8,7 +8,7 @@
 // that read the same weight panel are adjacent, so the panel streams into L2
 // once for all of them.  The grid is one workgroup per CU; the sequence is
 // cut into 8 contiguous ranges, one per XCD (the dispatcher deals workgroup b
-// to XCD b % 8), which that XCD's workgroups take round-robin.
+// to XCD b % 8), whose units that XCD's workgroups claim in order.
 #pragma once
 
 #include "internal.h"
