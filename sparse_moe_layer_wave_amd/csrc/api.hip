@@ -380,7 +380,10 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
                                  reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
                                  decode ? hy3::decode_bm(rg) : hy3::prefill_bm(), row_of, tok_of, 0, s);
     if (e == hipSuccess) e = mark(ev, 2, s);
-    if (e == hipSuccess) e = hy3::launch_quant_rows(x, T, d, xq, xs, s);
+    // the grouped gate_up reads its rows' activation scales per dispatch row,
+    // from hs, which the h quantiser overwrites after it
+    if (e == hipSuccess)
+        e = hy3::launch_quant_rows(x, T, d, xq, xs, s, decode ? nullptr : row_of, k, decode ? nullptr : hs);
     float* hmax = reinterpret_cast<float*>(amax);
     const int nblk = (d_ff + 127) / 128;
     int* sched = reinterpret_cast<int*>(ws + L.sched);
@@ -392,10 +395,10 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
             e = hy3::launch_gate_up_decode_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, max_slices,
                                                h32, amax, E, d, d_ff, rg, block, s);
         else if (block)
-            e = hy3::launch_gate_up_fp8_block(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off,
+            e = hy3::launch_gate_up_fp8_block(xq, hs, tok_of, Wq_gu, s_gu, offsets, tile_off,
                                               L.max_mtiles, h32, hmax, static_cast<int>(Tk), sched, E, d, d_ff, s);
         else
-            e = hy3::launch_gate_up_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, L.max_mtiles,
+            e = hy3::launch_gate_up_fp8(xq, hs, tok_of, Wq_gu, s_gu, offsets, tile_off, L.max_mtiles,
                                         h32, hmax, static_cast<int>(Tk), sched, E, d, d_ff, s);
     }
     if (e == hipSuccess)

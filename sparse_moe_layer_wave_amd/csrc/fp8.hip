@@ -45,11 +45,15 @@ __device__ __forceinline__ float amax8(const uint4& v, float m) {
 // One workgroup per row of bf16 input; a thread takes 8 values per step of
 // kQThreads * 8 columns.  Rows of at most NV steps are read once, into
 // registers (NV > 0); longer rows (NV = 0) are read twice, for the max and
-// for the codes.
+// for the codes.  rs, if not NULL, also receives the row's scale at each of
+// its k dispatch rows (row_of[row * k + j], skipped where negative), so that
+// the grouped gate_up reads a row scale without going through the token.
 template <int NV>
 __global__ __launch_bounds__(kQThreads) void k_quant_rows_bf16(const uint16_t* __restrict__ x,
                                                               int cols, uint8_t* __restrict__ q,
-                                                              float* __restrict__ s) {
+                                                              float* __restrict__ s,
+                                                              const int32_t* __restrict__ row_of, int k,
+                                                              float* __restrict__ rs) {
     __shared__ float lds[kQThreads / 64];
     const size_t row = blockIdx.x;
     const uint16_t* xr = x + row * cols;
@@ -82,7 +86,12 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_bf16(const uint16_t* _
             *reinterpret_cast<uint2*>(qr + c) = make_uint2(quant_pair2(v.x, v.y, r), quant_pair2(v.z, v.w, r));
         }
     }
-    if (threadIdx.x == 0) s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+    if (threadIdx.x == 0) s[row] = scale;
+    if (rs && static_cast<int>(threadIdx.x) < k) {
+        const int r = row_of[row * k + threadIdx.x];
+        if (r >= 0) rs[r] = scale;
+    }
 }
 
 // h rows (fp32) with their max |h| already reduced into amax (bit patterns),
@@ -157,13 +166,17 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
 }
 
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,
-                             hipStream_t st) {
+                             hipStream_t st, const int32_t* row_of, int k, float* rs) {
     if (rows == 0) return hipSuccess;
+    if (k > kQThreads) return hipErrorInvalidValue;
     const int steps = (cols + kQThreads * 8 - 1) / (kQThreads * 8);
-    if (steps <= 1) hipLaunchKernelGGL(k_quant_rows_bf16<1>, dim3(rows), dim3(kQThreads), 0, st, x, cols, q, s);
-    else if (steps <= 2) hipLaunchKernelGGL(k_quant_rows_bf16<2>, dim3(rows), dim3(kQThreads), 0, st, x, cols, q, s);
-    else if (steps <= 4) hipLaunchKernelGGL(k_quant_rows_bf16<4>, dim3(rows), dim3(kQThreads), 0, st, x, cols, q, s);
-    else hipLaunchKernelGGL(k_quant_rows_bf16<0>, dim3(rows), dim3(kQThreads), 0, st, x, cols, q, s);
+#define HY3_QROWS(NV) \
+    hipLaunchKernelGGL(k_quant_rows_bf16<NV>, dim3(rows), dim3(kQThreads), 0, st, x, cols, q, s, row_of, k, rs)
+    if (steps <= 1) HY3_QROWS(1);
+    else if (steps <= 2) HY3_QROWS(2);
+    else if (steps <= 4) HY3_QROWS(4);
+    else HY3_QROWS(0);
+#undef HY3_QROWS
     return hipGetLastError();
 }
 

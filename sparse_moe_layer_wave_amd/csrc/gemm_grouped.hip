@@ -90,7 +90,7 @@ struct Args {
     const int32_t* offsets;                        // [E+1] row offsets
     const int32_t* tile_off;                       // [E+1] offsets in 128-row blocks
     uint16_t* C;                                   // bf16 out: gate_up h (bf16 mode) or y [rows, N]
-    const float* a_scale;                          // e4m3: per token (gate_up) or per row (down)
+    const float* a_scale;                          // e4m3: activation scale per row (gate_up: its token's)
     const float* w_scale;                          // per channel: [E, 2N] or [E, N]; block: [E, rows_w/128, K/128]
     float* h32;                                    // e4m3 gate_up: h [rows, N] fp32
     float* hmax;                                   // e4m3 gate_up: [N / 128][rows] max |h| per 128-column block
@@ -218,6 +218,24 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
 
     // the wave's first output column (gate_up: h column)
     const int cw = GATE_UP ? u.n * WCOLS + wn * 32 : u.n * NB + wn * 64;
+
+    // e4m3: the epilogue's row scale (thread tid < RA: row tid) and, per
+    // channel, the lane's column scales (gate_up: gate, up), loaded before the
+    // first copy so that their latency passes under the K loop; the compiler
+    // waits for them where the epilogue uses them, after every copy has landed
+    float srow_pre = 0.f;
+    float cs[2] = {1.f, 1.f};
+    if constexpr (FP8) {
+        if (tid < RA) srow_pre = g.a_scale[u.row0 + min(tid, u.rows - 1)];
+        if constexpr (!BLK) {
+            const float* ws_e = g.w_scale + static_cast<size_t>(u.e) * (GATE_UP ? 2 * N : N);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const int c = GATE_UP ? cw + (lane & 31) : cw + 32 * nb + (lane & 31);
+                cs[nb] = c < N ? ws_e[(GATE_UP && nb) ? N + c : c] : 0.f;
+            }
+        }
+    }
 
     // ---- block scales of the wave's weight rows (gate and up row blocks;
     // down: one row block).  A wave whose columns lie past N (a partial
@@ -450,26 +468,15 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
     int claimed = 0;
     if (claim && tid == 0) claimed = atomicAdd(claim, 1);
     if constexpr (FP8) {
-        if (tid < RA) {
-            const int r = min(tid, u.rows - 1);
-            srow[tid] = GATE_UP ? g.a_scale[g.tok_of[u.row0 + r]] : g.a_scale[u.row0 + r];
-        }
+        if (tid < RA) srow[tid] = srow_pre;
         __syncthreads();
     }
     // the output's column factors: per channel, the lane's columns' scales
-    // (gate_up: gate, up); block scales: m_last * 2^E of each row block (the
+    // (loaded above); block scales: m_last * 2^E of each row block (the
     // accumulators are the sums divided by it)
-    float cs[2] = {1.f, 1.f};
     if constexpr (BLK) {
         cs[0] = ldexpf(m0, E0);
         cs[1] = GATE_UP ? ldexpf(m1, E1) : cs[0];
-    } else if constexpr (FP8) {
-        const float* ws_e = g.w_scale + static_cast<size_t>(u.e) * (GATE_UP ? 2 * N : N);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const int c = GATE_UP ? cw + l32 : cw + 32 * nb + l32;
-            cs[nb] = c < N ? ws_e[(GATE_UP && nb) ? N + c : c] : 0.f;
-        }
     }
     // bf16 down: lanes 2i and 2i + 1 (columns 2i, 2i + 1) swap one value of
     // rows r, r + 1 (adjacent j), so each writes both columns of one row as a
@@ -661,11 +668,11 @@ hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const ui
     return launch<DN_BF16>(g, max_blocks, s);
 }
 
-hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
+hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* rs, const int32_t* tok_of,
                               const uint8_t* Wq, const float* ws, const int32_t* offsets,
                               const int32_t* tile_off, int max_blocks, float* h32, float* hmax,
                               int rows, int* sched, int E, int d, int F, hipStream_t s) {
-    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, xs, ws, h32, hmax, rows, sched, d, F, E, 0};
+    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, rs, ws, h32, hmax, rows, sched, d, F, E, 0};
     return launch<GU_FP8>(g, max_blocks, s);
 }
 
@@ -676,11 +683,11 @@ hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq
     return launch<DN_FP8>(g, max_blocks, s);
 }
 
-hipError_t launch_gate_up_fp8_block(const uint8_t* xq, const float* xs, const int32_t* tok_of,
+hipError_t launch_gate_up_fp8_block(const uint8_t* xq, const float* rs, const int32_t* tok_of,
                                     const uint8_t* Wq, const float* sb, const int32_t* offsets,
                                     const int32_t* tile_off, int max_mtiles, float* h32,
                                     float* hmax, int rows, int* sched, int E, int d, int F, hipStream_t s) {
-    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, xs, sb, h32, hmax, rows, sched, d, F, E, 0};
+    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, rs, sb, h32, hmax, rows, sched, d, F, E, 0};
     return launch<GU_BLK>(g, max_mtiles, s);
 }
 

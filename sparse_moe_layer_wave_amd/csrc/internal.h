@@ -185,15 +185,18 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
 
 hipError_t launch_block_counts(const int32_t* idx, int T, int E, int k, int nb,
                                int32_t* blk_counts, hipStream_t s);
+// rs (optional): each row's scale also written at its k dispatch rows row_of[row * k + j]
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,
-                             hipStream_t st);
+                             hipStream_t st, const int32_t* row_of = nullptr, int k = 0,
+                             float* rs = nullptr);
 // h rows' max |h|: amax_bits [rows] (bit patterns; the weight-streaming
 // gate_up folds them in with atomics), or, with amax_bits NULL, the max over
 // the nblk partial maxima hmax[blk * rows + row] (the grouped gate_up's).
 hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, const float* hmax, int nblk,
                                  int rows, int cols, uint8_t* q, float* s, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
-hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
+// rs: the tokens' activation scales per dispatch row (launch_quant_rows' rs)
+hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* rs, const int32_t* tok_of,
                               const uint8_t* Wq, const float* ws, const int32_t* offsets,
                               const int32_t* tile_off, int max_mtiles, float* h32, float* hmax,
                               int rows, int* sched, int E, int d, int F, hipStream_t s);
@@ -216,7 +219,7 @@ hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint
 
 // prefill-sized batches with e4m3 weights in 128 x 128 blocks (one fp32
 // scale each, sb [E, rows/128, K/128]); K <= 16384, tile_off in 128-row blocks
-hipError_t launch_gate_up_fp8_block(const uint8_t* xq, const float* xs, const int32_t* tok_of,
+hipError_t launch_gate_up_fp8_block(const uint8_t* xq, const float* rs, const int32_t* tok_of,
                                     const uint8_t* Wq, const float* sb, const int32_t* offsets,
                                     const int32_t* tile_off, int max_mtiles, float* h32,
                                     float* hmax, int rows, int* sched, int E, int d, int F, hipStream_t s);
