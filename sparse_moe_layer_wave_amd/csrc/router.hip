@@ -477,7 +477,7 @@ hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bi
         hipLaunchKernelGGL(k_router_reduce, dim3(static_cast<unsigned>((te + 255) / 256)), dim3(256),
                            0, s, rw.partial, bias, rw.scores, T, E, rw.nsplit);
     }
-    // keys per lane: E / 16 rounded up to a power of two (E <= 1024)
+    // keys per lane: E / 16 rounded up to a power of two or 12 (E <= 1024)
     const int nq = (E + 15) / 16;
 #define HY3_SELECT(NQ)                                                                             \
     hipLaunchKernelGGL(k_router_select<NQ>, dim3(nb), dim3(kSelThreads), 0, s, rw.scores, score_bias, \
@@ -486,6 +486,7 @@ hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bi
     else if (nq <= 2) HY3_SELECT(2);
     else if (nq <= 4) HY3_SELECT(4);
     else if (nq <= 8) HY3_SELECT(8);
+    else if (nq <= 12) HY3_SELECT(12);                     // E = 192: no empty key slots
     else if (nq <= 16) HY3_SELECT(16);
     else if (nq <= 32) HY3_SELECT(32);
     else HY3_SELECT(64);
