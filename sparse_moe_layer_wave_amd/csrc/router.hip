@@ -367,6 +367,46 @@ __device__ __forceinline__ uint32_t order_key(float v) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// The k rounds of one token's top-k: 16 lanes (one DPP row) per token, lane
+// j holding the order keys of experts j, j + 16, ... (NQ of them), clamped to
+// at least 1 so that 0 can mark "taken or absent".  A round takes each lane's
+// largest key (the lowest index among equals), the row's maximum of (key <<
+// 32 | ~expert) by DPP, and clears the winner's key.  Returns, in lane j < k,
+// the expert of slot j.
+template <int NQ>
+__device__ __forceinline__ int select_rounds(uint32_t (&key)[NQ], int j, int k) {
+    int my_e = 0;
+    for (int r = 0; r < k; ++r) {
+        uint32_t bk = 0u;
+        int bq = 0;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const bool better = key[q] > bk;
+            bk = better ? key[q] : bk;
+            bq = better ? q : bq;
+        }
+        unsigned long long best =
+            bk ? (static_cast<unsigned long long>(bk) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(j + 16 * bq))
+               : 0ull;
+        best = row16_max(best);
+        const int e_win = static_cast<int>(~static_cast<uint32_t>(best & 0xffffffffull));
+        const bool mine = (e_win & 15) == j;
+        const int qw = e_win >> 4;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) key[q] = (mine && q == qw) ? 0u : key[q];
+        if (r == j) my_e = e_win;
+    }
+    return my_e;
+}
+
+// The weights of a token's k slots (lane j < k holds slot j and its score):
+// scale * s_j / (sum of the k scores, in slot order).
+__device__ __forceinline__ float slot_weight(float my_s, int lane, int k, float scale) {
+    float sum = 0.f;
+    for (int r = 0; r < k; ++r) sum += __shfl(my_s, (lane & ~15) | r, 64);   // slot order
+    return scale * (my_s / sum);
+}
+
 // One 64-token routing block per workgroup, 16 lanes (one DPP row) per
 // token.  Lane j keeps the order keys of experts j, j + 16, ... (NQ of them)
 // in registers, clamped to at least 1 so that 0 can mark "taken or absent".
@@ -399,42 +439,108 @@ __global__ __launch_bounds__(kSelThreads) void k_router_select(
             key[q] = max(order_key(v), 1u);
         }
     }
-    int my_e = 0;
-    for (int r = 0; r < k; ++r) {
-        uint32_t bk = 0u;
-        int bq = 0;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const bool better = key[q] > bk;
-            bk = better ? key[q] : bk;
-            bq = better ? q : bq;
-        }
-        unsigned long long best =
-            bk ? (static_cast<unsigned long long>(bk) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(j + 16 * bq))
-               : 0ull;
-        best = row16_max(best);
-        const int e_win = static_cast<int>(~static_cast<uint32_t>(best & 0xffffffffull));
-        const bool mine = (e_win & 15) == j;
-        const int qw = e_win >> 4;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) key[q] = (mine && q == qw) ? 0u : key[q];
-        if (r == j) my_e = e_win;
-    }
+    const int my_e = select_rounds<NQ>(key, j, k);
     __syncthreads();                                      // mask cleared
     // lane j < k holds slot j; the weights use the scores themselves
     const float my_s = (active && j < k) ? srow[my_e] : 0.f;
-    float sum = 0.f;
-    for (int r = 0; r < k; ++r) sum += __shfl(my_s, (lane & ~15) | r, 64);   // slot order
+    const float my_w = slot_weight(my_s, lane, k, scale);
     if (active && j < k) {
         const size_t pair = static_cast<size_t>(t) * k + j;
         idx[pair] = my_e;
-        wout[pair] = scale * (my_s / sum);
+        wout[pair] = my_w;
         atomicOr(&mask[my_e], 1ull << ts);
     }
     if (blk_counts) {
         __syncthreads();
         for (int e = tid; e < E; e += kSelThreads)
             blk_counts[static_cast<size_t>(e) * nb + blockIdx.x] = __popcll(mask[e]);
+    }
+}
+
+// A batch of one routing block (T <= 64), whose dispatch (k_dispatch_one)
+// rebuilds its token masks from idx and needs no per-block counts: one wave
+// per 4 tokens, each wave a workgroup of its own, so the tokens spread over
+// as many CUs.  The wave also does k_router_reduce's work for its tokens: the
+// d-chunks' partial logits summed in the order s = 0..nsplit-1, then
+// sigmoid(z + bias), the same arithmetic and so the same bits (nsplit == 1:
+// the logits kernel wrote the scores).  The scores stay in LDS for the
+// weights; the selection is k_router_select's.
+template <int NQ>
+__global__ __launch_bounds__(64) void k_router_select_wave(
+    const float* __restrict__ partial, const float* __restrict__ scores, int nsplit,
+    const float* __restrict__ bias, const float* __restrict__ score_bias, int T, int E, int k,
+    float scale, int32_t* __restrict__ idx, float* __restrict__ wout) {
+    __shared__ float s_sc[4][16 * NQ];
+    const int lane = threadIdx.x;
+    const int j = lane & 15;                              // lane within the token's row
+    const int ts = lane >> 4;                             // token of the wave
+    const int t = blockIdx.x * 4 + ts;
+    const bool active = t < T;
+    const size_t n = static_cast<size_t>(T) * E;
+    const size_t row = static_cast<size_t>(active ? t : 0) * E;
+    // the lane's scores: U d-chunks' partials of all its experts are loaded
+    // together, then added chunk by chunk (zeros past nsplit are added last,
+    // which changes nothing)
+    constexpr int U = NQ <= 12 ? 8 : NQ <= 16 ? 4 : NQ <= 32 ? 2 : 1;
+    // the biases first, all in flight with the partials
+    float bq[NQ], sbq[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int e = j + 16 * q;
+        bq[q] = (bias && e < E) ? bias[e] : 0.f;
+        sbq[q] = (score_bias && e < E) ? score_bias[e] : 0.f;
+    }
+    float sc[NQ];
+    if (nsplit > 1) {
+        float z[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) z[q] = 0.f;
+        for (int sp0 = 0; sp0 < nsplit; sp0 += U) {
+            float pv[U][NQ];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    const int e = j + 16 * q;
+                    pv[u][q] = (active && e < E && sp0 + u < nsplit) ? partial[(sp0 + u) * n + row + e] : 0.f;
+                }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) z[q] += pv[u][q];
+        }
+        // sigmoid_bias, with the bias loaded above
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const float zb = bias ? z[q] + bq[q] : z[q];
+            sc[q] = 1.0f / (1.0f + expf(-zb));
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int e = j + 16 * q;
+            sc[q] = (active && e < E) ? scores[row + e] : 0.f;
+        }
+    }
+    uint32_t key[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int e = j + 16 * q;
+        key[q] = 0u;
+        if (active && e < E) {
+            const float v = score_bias ? sc[q] + sbq[q] : sc[q];
+            key[q] = max(order_key(v), 1u);
+        }
+        s_sc[ts][e] = sc[q];
+    }
+    const int my_e = select_rounds<NQ>(key, j, k);
+    // a wave's LDS accesses complete in order: the stores above precede this read
+    const float my_s = (active && j < k) ? s_sc[ts][my_e] : 0.f;
+    const float my_w = slot_weight(my_s, lane, k, scale);
+    if (active && j < k) {
+        const size_t pair = static_cast<size_t>(t) * k + j;
+        idx[pair] = my_e;
+        wout[pair] = my_w;
     }
 }
 
@@ -472,16 +578,26 @@ hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bi
         hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, s, x, W_gate, bias, rw.partial,
                            rw.scores, T, d, E, d / rw.nsplit, rw.nsplit);
     }
-    if (rw.nsplit > 1) {
+    // keys per lane: E / 16 rounded up to a power of two or 12 (E <= 1024)
+    const int nq = (E + 15) / 16;
+    // one routing block: the wave-per-4-tokens select, which also reduces the
+    // d-chunks; more blocks: the reduce, then one workgroup per block, which
+    // also counts each block's pairs per expert for the dispatch
+    const bool one_block = nb == 1;
+    if (!one_block && rw.nsplit > 1) {
         const size_t te = static_cast<size_t>(T) * E;
         hipLaunchKernelGGL(k_router_reduce, dim3(static_cast<unsigned>((te + 255) / 256)), dim3(256),
                            0, s, rw.partial, bias, rw.scores, T, E, rw.nsplit);
     }
-    // keys per lane: E / 16 rounded up to a power of two or 12 (E <= 1024)
-    const int nq = (E + 15) / 16;
-#define HY3_SELECT(NQ)                                                                             \
-    hipLaunchKernelGGL(k_router_select<NQ>, dim3(nb), dim3(kSelThreads), 0, s, rw.scores, score_bias, \
-                       T, E, k, scale, idx, w, blk_counts, nb)
+#define HY3_SELECT(NQ)                                                                                      \
+    do {                                                                                                    \
+        if (one_block)                                                                                      \
+            hipLaunchKernelGGL(k_router_select_wave<NQ>, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(64), 0, \
+                               s, rw.partial, rw.scores, rw.nsplit, bias, score_bias, T, E, k, scale, idx, w); \
+        else                                                                                                \
+            hipLaunchKernelGGL(k_router_select<NQ>, dim3(nb), dim3(kSelThreads), 0, s, rw.scores, score_bias, \
+                               T, E, k, scale, idx, w, blk_counts, nb);                                     \
+    } while (0)
     if (nq <= 1) HY3_SELECT(1);
     else if (nq <= 2) HY3_SELECT(2);
     else if (nq <= 4) HY3_SELECT(4);
