@@ -107,12 +107,17 @@ __global__ __launch_bounds__(256) void k_router_logits(
     const uint16_t* __restrict__ x, const float* __restrict__ W,
     const float* __restrict__ bias, float* __restrict__ partial, float* __restrict__ scores,
     int T, int d, int E, int kchunk, int nsplit) {
+    __shared__ f32x16_t red[3][2][64];                // kwaves: waves 1-3's sums
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * kLogitTokens + wave * 64;
+    // One wave of tokens (T <= 64): the four waves take a quarter of the
+    // chunk each instead of idling, and their sums are added in wave order.
+    const bool kwaves = T <= 64 && kchunk % 64 == 0;
+    const int t0 = blockIdx.x * kLogitTokens + (kwaves ? 0 : wave * 64);
     if (t0 >= T) return;                            // whole wave past the batch
     const int e0 = blockIdx.y * kLogitExperts;
-    const int k0 = blockIdx.z * kchunk;
+    const int k0 = blockIdx.z * kchunk + (kwaves ? wave * (kchunk / 4) : 0);
+    const int kc = kwaves ? kchunk / 4 : kchunk;      // this wave's share of the chunk
     const int l32 = lane & 31;
     const int kh = (lane >> 5) * 8;
 
@@ -126,11 +131,11 @@ __global__ __launch_bounds__(256) void k_router_logits(
     const float* wb = W + static_cast<size_t>(eb) * d + k0 + kh;
 
     f32x16_t acc[2] = {{}, {}};
-    for (int kb = 0; kb < kchunk; kb += 16 * kUnroll) {
+    for (int kb = 0; kb < kc; kb += 16 * kUnroll) {
         i32x4_t av[kUnroll][2], bv[kUnroll][3];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int kk = min(kb + 16 * u, kchunk - 16);  // kchunk is a multiple of 32
+            const int kk = min(kb + 16 * u, kc - 16);      // kc is a multiple of 16
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) av[u][mb] = *reinterpret_cast<const i32x4_t*>(xa[mb] + kk);
             split_planes(*reinterpret_cast<const float4*>(wb + kk), *reinterpret_cast<const float4*>(wb + kk + 4),
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(256) void k_router_logits(
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            if (kb + 16 * u < kchunk) {
+            if (kb + 16 * u < kc) {
 #pragma unroll
                 for (int p = 0; p < 3; ++p) {
                     Frag b;
@@ -154,6 +159,18 @@ __global__ __launch_bounds__(256) void k_router_logits(
         }
     }
 
+    if (kwaves) {
+        if (wave > 0) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) red[wave - 1][mb][lane] = acc[mb];
+        }
+        __syncthreads();
+        if (wave > 0) return;
+#pragma unroll
+        for (int w = 0; w < 3; ++w)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) acc[mb] += red[w][mb][lane];
+    }
     const int e = e0 + l32;
     if (e >= E) return;
     float* out = nsplit == 1 ? scores : partial + static_cast<size_t>(blockIdx.z) * T * E;
