@@ -305,7 +305,7 @@ static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_ep
     // decode-sized batches: tile_off holds 16-row slice offsets for the
     // weight-streaming kernels, else 128-row block offsets for the grouped GEMMs
     const bool decode = hy3::use_decode_path(T, d, d_ff, E, k, 2, shared);
-    const int rg = hy3::decode_row_groups(T, k, E, shared);
+    const int rg = hy3::decode_row_groups(T, k, E, 2, shared);
     const int max_slices = (L.rows + hy3::decode_bm(rg) - 1) / hy3::decode_bm(rg) + Eg;
     if (e == hipSuccess)
         e = hy3::launch_dispatch(idx, T, E, k, L.nb, blk_counts,
@@ -372,7 +372,7 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
                                idx, w, reinterpret_cast<int32_t*>(ws + L.blk_counts), L.nb, s);
     if (e == hipSuccess) e = mark(ev, 1, s);
     const bool decode = hy3::use_decode_path(T, d, d_ff, E, k, 1, false);
-    const int rg = hy3::decode_row_groups(T, k, E, false);
+    const int rg = hy3::decode_row_groups(T, k, E, 1, false);
     const int max_slices = (L.rows + hy3::decode_bm(rg) - 1) / hy3::decode_bm(rg) + E;
     if (e == hipSuccess)
         e = hy3::launch_dispatch(idx, T, E, k, L.nb, reinterpret_cast<int32_t*>(ws + L.blk_counts),

@@ -76,8 +76,16 @@ struct DecodeArgs {
     int E;                              // experts, the shared one included
 };
 
+// Waves per SIMD the register allocation is held to (more waves, more weight
+// batches in flight): every one-group kernel fits four (bf16 five, unbounded),
+// two groups four (bf16) or three (e4m3 down) without spilling; the e4m3
+// gate_up with two groups is left unbounded (two waves).
+constexpr int decode_min_waves(int mode, int rg) {
+    return rg == 1 ? 4 : mode <= DN_BF16 ? 4 : (mode == DN_FP8 || mode == DN_FP8B) ? 3 : 1;
+}
+
 template <int MODE, int SUBS, int RG>
-__global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
+__global__ __launch_bounds__(256, decode_min_waves(MODE, RG)) void k_decode_gemm(DecodeArgs g) {
     constexpr bool GATE_UP = MODE == GU_BF16 || MODE == GU_FP8 || MODE == GU_FP8B;
     constexpr bool BLK = MODE == GU_FP8B || MODE == DN_FP8B;
     constexpr bool FP8 = MODE >= GU_FP8;
@@ -104,7 +112,7 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
     const int K = g.K, N = g.N;
     const size_t rowbytes = static_cast<size_t>(K) * ESZ;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int r16 = lane & 15;
     const int kq = lane >> 4;                          // quarter of the lane group
     uint8_t* slab = lds + wave * kSlabB;
@@ -120,10 +128,13 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
     };
     const int colb = GATE_UP ? blockIdx.y * 64 * SUBS + wave * 16 : blockIdx.y * 128 * SUBS + wave * 32;
     const size_t sub_stride = static_cast<size_t>(SUBROWS) * rowbytes;
-    // load instruction i (0..7) of a batch: slab rows 4i + lane/16, bytes (lane%16)*16
+    // load instruction i (0..7) of a batch: slab rows 4i + lane/16, bytes
+    // (lane%16)*16.  Its address is a wave-uniform base (weight row
+    // wrow_of(4i), kept in scalar registers) plus the lane's 32-bit offset.
     const uint8_t* wsrc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) wsrc[i] = We + static_cast<size_t>(wrow_of(4 * i + kq)) * rowbytes + r16 * 16;
+    for (int i = 0; i < 8; ++i) wsrc[i] = We + static_cast<size_t>(wrow_of(4 * i)) * rowbytes;
+    const uint32_t wlane = static_cast<uint32_t>(kq * rowbytes) + r16 * 16;
     int wdst[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) wdst[i] = slab_off(4 * i + kq, r16);
@@ -159,17 +170,17 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
 
     const int nb = static_cast<int>(rowbytes / kBatchB);
     for (int p0 = rbeg; p0 < rend; p0 += 16 * RG) {
-        // row group q of the pass: rows p0 + 16 q .. + 16; this lane loads A row p0 + 16 q + r16
-        bool va[RG];
-        const uint8_t* a[RG];
+        // row group q of the pass: rows p0 + 16 q .. + 16; this lane loads A
+        // row p0 + 16 q + r16, or the pass's last row past its end (rows of
+        // the MFMA are independent, and those outputs are not stored).  The
+        // lane's offset into A is 32-bit (A holds at most a few thousand rows).
+        uint32_t a[RG];
 #pragma unroll
         for (int q = 0; q < RG; ++q) {
-            const int prow = p0 + 16 * q + r16;
-            va[q] = prow < rend;
-            const size_t arow = GATE_UP ? static_cast<size_t>(va[q] ? g.tok_of[prow] : 0)
-                                        : static_cast<size_t>(va[q] ? prow : 0);
+            const int prow = min(p0 + 16 * q + r16, rend - 1);
+            const uint32_t arow = static_cast<uint32_t>(GATE_UP ? g.tok_of[prow] : prow);
             // this lane's A bytes within a batch start at kq * (FP8 ? 32 : 16)
-            a[q] = g.A + arow * rowbytes + kq * (FP8 ? 32 : 16);
+            a[q] = arow * static_cast<uint32_t>(rowbytes) + kq * (FP8 ? 32 : 16);
         }
 
         f32x4_t acc0[RG], acc1[RG];
@@ -178,9 +189,13 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
             acc0[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             acc1[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        i32x4_t cur[8], nxt[8];
+        // One weight batch is in flight per wave: batch bt + 1 is loaded into
+        // the registers that batch bt leaves once it is in the slab.  Each
+        // batch's A fragments are loaded before that (loads return in order,
+        // so the wait for them does not include the weight batch behind them).
+        i32x4_t wb[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) cur[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(wsrc[i]));
+        for (int i = 0; i < 8; ++i) wb[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(wsrc[i] + wlane));
         const int nbt = nb * SUBS;
         for (int bt = 0; bt < nbt; ++bt) {
             const int sb = bt / nb, b = bt - sb * nb;
@@ -188,22 +203,23 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
             const int btn = bt + 1 < nbt ? bt + 1 : bt;      // last batch re-reads itself
             const int sbn = btn / nb;
             const size_t kn = sbn * sub_stride + static_cast<size_t>(btn - sbn * nb) * kBatchB;
+            // A: e4m3 2 k-steps of 128, the lane's 32 bytes of step s at
+            // 128 s (j = 2 s + half); bf16 4 k-steps of 32, 16 bytes at 64 j
+            i32x4_t av[RG][4];
+#pragma unroll
+            for (int q = 0; q < RG; ++q)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    av[q][j] = *reinterpret_cast<const i32x4_t*>(g.A + kb + a[q] +
+                                                                 (FP8 ? 128 * (j >> 1) + 16 * (j & 1) : 64 * j));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) *reinterpret_cast<i32x4_t*>(slab + wdst[i]) = wb[i];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                nxt[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(wsrc[i] + kn));
-#pragma unroll
-            for (int i = 0; i < 8; ++i) *reinterpret_cast<i32x4_t*>(slab + wdst[i]) = cur[i];
+                wb[i] = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(wsrc[i] + kn + wlane));
+            __builtin_amdgcn_sched_barrier(0);                // the batch goes out before the MFMAs wait on A
             if constexpr (FP8) {
                 // 2 k-steps of 128: lane's 32 bytes = chunks 8 s + 2 kq, +1
-                i32x4_t av[RG][2][2];
-#pragma unroll
-                for (int q = 0; q < RG; ++q)
-#pragma unroll
-                    for (int s = 0; s < 2; ++s)
-#pragma unroll
-                        for (int h = 0; h < 2; ++h)
-                            av[q][s][h] = va[q] ? *reinterpret_cast<const i32x4_t*>(a[q] + kb + 128 * s + 16 * h)
-                                                : i32x4_t{0, 0, 0, 0};
                 // block scales of this batch's two k-blocks (2b, 2b + 1)
                 float sc0[2] = {1.f, 1.f}, sc1[2] = {1.f, 1.f};
                 if constexpr (BLK) {
@@ -233,7 +249,7 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
                     const i32x8_t f1 = __builtin_shufflevector(b10, b11, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                     for (int q = 0; q < RG; ++q) {
-                        const i32x8_t fa = __builtin_shufflevector(av[q][s][0], av[q][s][1], 0, 1, 2, 3, 4, 5, 6, 7);
+                        const i32x8_t fa = __builtin_shufflevector(av[q][2 * s], av[q][2 * s + 1], 0, 1, 2, 3, 4, 5, 6, 7);
                         if constexpr (BLK) {
                             // one k-step is one 128-wide k-block: its product
                             // is scaled by the block's scale and added in fp32
@@ -253,12 +269,6 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
                 }
             } else {
                 // 4 k-steps of 32: lane's 16 bytes = chunk 4 s + kq
-                i32x4_t av[RG][4];
-#pragma unroll
-                for (int q = 0; q < RG; ++q)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        av[q][s] = va[q] ? *reinterpret_cast<const i32x4_t*>(a[q] + kb + 64 * s) : i32x4_t{0, 0, 0, 0};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const i32x4_t f0 = *reinterpret_cast<const i32x4_t*>(slab + slab_off(r16, 4 * s + kq));
@@ -272,8 +282,6 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
                     }
                 }
             }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
             if (b != nb - 1) continue;
             // end of block sb: C lane l: column l%16, rows 4*(l/16)+i of each row group
             const int col0 = colb + sb * SUBROWS;
@@ -325,26 +333,28 @@ __global__ __launch_bounds__(256) void k_decode_gemm(DecodeArgs g) {
 
 // Rows per pass: a workgroup takes up to 16 rows (one MFMA row group) or 32
 // (two groups sharing every weight batch).  Two groups stream an expert with
-// 17-32 rows once instead of twice, but hold 26 more registers (3 waves per
-// SIMD instead of 4), so they are used where experts get 8 or more rows on
-// average.  At fewer (T = 64, 192 experts: 2.7 rows each) one group is 1%
-// faster; the full block's shared expert (all T rows) gained nothing from two.
-int decode_row_groups(int T, int k, int E, bool shared) {
+// 17-32 rows once instead of twice, but hold more registers (bf16: four waves
+// per SIMD instead of five; e4m3 gate_up: two instead of four).  Measured on
+// the whole layer at d = 4096, E = 192, k = 8, d_ff = 1536 (one group / two):
+// bf16 T = 64 1.065 / 1.094 ms, T = 96 1.132 / 1.136, T = 128 1.167 / 1.149,
+// T = 160 1.191 / 1.170, T = 192 1.260 / 1.183; e4m3 T = 128 0.664 / 0.668,
+// T = 160 0.685 / 0.691, T = 192 0.735 / 0.702.  So two groups from 5 rows
+// per expert on average with bf16 weights (esz 2), from 8 with e4m3.
+int decode_row_groups(int T, int k, int E, int esz, bool shared) {
     (void)shared;
-    return static_cast<long long>(T) * k >= 8LL * E ? 2 : 1;
+    return static_cast<long long>(T) * k >= (esz == 2 ? 5LL : 8LL) * E ? 2 : 1;
 }
 
 // Decode path up to about 11 rows per expert on average with one row group
 // and 20 with two; rows of d and d_ff elements of esz bytes must be whole
-// 256-byte batches.  Measured on the whole layer at d = 4096, E = 192, k = 8,
-// d_ff = 1536 (grouped GEMMs vs this path): T = 128 1.17 vs 1.17 ms (one
-// group); with two groups T = 192 1.26 vs 1.19, T = 256 1.32 vs 1.24,
-// T = 320 1.38 vs 1.26, T = 384 1.37 vs 1.31, T = 448 1.38 vs 1.34,
-// T = 512 1.39 vs 1.51 ms.  The full block's shared expert adds T rows,
-// counted twice: each of its slices streams a whole expert's weights.
+// 256-byte batches.  Measured on the whole layer at the same dims (this path
+// vs the grouped GEMMs): bf16 T = 384 1.302 vs 1.360 ms, T = 448 1.341 vs
+// 1.367, T = 512 1.489 vs 1.373; e4m3 T = 384 0.781 vs 0.810, T = 448 0.812
+// vs 0.818, T = 512 0.891 vs 0.825.  The full block's shared expert adds T
+// rows, counted twice: each of its slices streams a whole expert's weights.
 bool use_decode_path(int T, int d, int F, int E, int k, int esz, bool shared) {
     const long long rows = static_cast<long long>(T) * k + (shared ? 2LL * T : 0);
-    const int rg = decode_row_groups(T, k, E, shared);
+    const int rg = decode_row_groups(T, k, E, esz, shared);
     return rows <= (rg == 2 ? 20LL : 11LL) * E && (d * esz) % kBatchB == 0 && (F * esz) % kBatchB == 0;
 }
 

@@ -143,7 +143,7 @@ bool use_decode_path(int T, int d, int F, int E, int k, int esz, bool shared);  
 // 2, from decode_row_groups); slice_off: [E+1] offsets of the experts' slices
 // of decode_bm(rg) rows (the dispatch's block offsets with that block size);
 // max_slices: an upper bound on slice_off[E], the grid's column count.
-int decode_row_groups(int T, int k, int E, bool shared);
+int decode_row_groups(int T, int k, int E, int esz, bool shared);
 int decode_bm(int rg);
 hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const uint16_t* W_gu,
                                  const uint16_t* W_last, const int32_t* offsets,
