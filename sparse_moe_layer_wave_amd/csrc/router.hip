@@ -191,44 +191,53 @@ __global__ __launch_bounds__(256) void k_router_logits(
 // with all three planes, d-chunk s.  K advances in slices of 32 values (64
 // bytes per row) through a 3-slot LDS ring of 832 rows (256 token rows, then
 // the 192 expert rows of each plane), filled with direct-to-LDS copies two
-// slices ahead; every wave issues 13 of the 52 one-kilobyte copies of a
-// slice.  Wave (wm, wn) owns tokens 128 wm.. x experts 96 wn.. as 4 x 3
-// blocks of 32 x 32: a 16-wide k step reads 4 token and 9 plane fragments
-// and issues 36 MFMAs.  Every accumulator takes each step's planes in the
-// order hi, mid, lo, steps in increasing k, as in k_router_logits, so both
-// kernels give the same bits for the same d-chunks.  A slice's first half
-// runs on fragments read during the previous slice; the barrier between the
-// halves (the next slice landed, every read of this slice done) frees this
-// slice's slot for the refill issued during the second half.
+// slices ahead; waves 0-3 each issue 13 of the 52 one-kilobyte copies of a
+// slice.  Eight waves, two per SIMD, so that one wave's MFMAs run while the
+// other stalls issuing copies or waits: wave (wm, wn) owns tokens 64 wm.. x
+// experts 96 wn.. as 2 x 3 blocks of 32 x 32, and a 16-wide k step reads 2
+// token and 9 plane fragments and issues 18 MFMAs.  Every accumulator takes
+// each step's planes in the order hi, mid, lo, steps in increasing k, as in
+// k_router_logits, so both kernels give the same bits for the same
+// d-chunks.  A slice's first half runs on fragments read during the previous
+// slice; the barrier between the halves (the next slice landed, every read
+// of this slice done) frees this slice's slot for the refill issued during
+// the second half.
 constexpr int kTiledTokens = 256;
 constexpr int kTiledExperts = 192;
 constexpr int kTiledRows = kTiledTokens + 3 * kTiledExperts;    // 832 LDS rows per slice
 constexpr int kTiledSlotB = kTiledRows * 64;                     // 53,248 bytes
 constexpr int kTiledSlots = 3;
-constexpr int kTiledNpw = kTiledRows / 16 / 4;                   // 13 copies per wave and slice
+constexpr int kTiledWaves = 8;
+constexpr int kTiledCopyWaves = 4;
+constexpr int kTiledNpw = kTiledRows / 16 / kTiledCopyWaves;     // 13 copies per copying wave and slice
+constexpr int kTiledFrags = 2 + 9;                               // fragments per k step and wave
+constexpr int kTiledMfmas = 2 * 3 * 3;                           // MFMAs per k step and wave
 constexpr int kTiledMinT = 4096;                                 // smaller batches: k_router_logits
 
-__global__ __launch_bounds__(256, 1) void k_router_logits_tiled(
+__global__ __launch_bounds__(64 * kTiledWaves, 1) void k_router_logits_tiled(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
     const float* __restrict__ bias, float* __restrict__ partial, float* __restrict__ scores,
     int T, int d, int E, int kchunk, int nsplit) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kTiledSlots * kTiledSlotB];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave & 3, wn = wave >> 2;
+    const bool copier = wave < kTiledCopyWaves;
     const int t0 = blockIdx.x * kTiledTokens;
     const int e0 = blockIdx.y * kTiledExperts;
     const int k0 = blockIdx.z * kchunk;
     const int nk = kchunk / 32;
     const size_t plane = static_cast<size_t>(E) * d;
 
-    // copy j of this wave fills LDS rows 16 (13 wave + j) .. +15; lane ->
+    // copy j of copying wave c fills LDS rows 16 (13 c + j) .. +15; lane ->
     // row + lane / 4, physical chunk lane % 4.  Rows past T or E repeat the
-    // last valid one.
+    // last valid one.  (The other waves compute the same sources for c =
+    // wave - 4 and never use them.)
+    const int cw = wave & (kTiledCopyWaves - 1);
     const uint8_t* src[kTiledNpw];
 #pragma unroll
     for (int j = 0; j < kTiledNpw; ++j) {
-        const int row = 16 * (wave * kTiledNpw + j) + (lane >> 2);
+        const int row = 16 * (cw * kTiledNpw + j) + (lane >> 2);
         const int lc = pchunk(row, lane & 3);
         const uint16_t* base;
         if (row < kTiledTokens) {
@@ -241,9 +250,9 @@ __global__ __launch_bounds__(256, 1) void k_router_logits_tiled(
         src[j] = reinterpret_cast<const uint8_t*>(base + k0) + lc * 16;
     }
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-    const uint32_t my_copies = lds0 + static_cast<uint32_t>(wave * kTiledNpw) * 1024u;
+    const uint32_t my_copies = lds0 + static_cast<uint32_t>(cw * kTiledNpw) * 1024u;
 
-    // fragment rows: token block mb at 128 wm + 32 mb; plane p, expert block
+    // fragment rows: token block mb at 64 wm + 32 mb; plane p, expert block
     // eb at 256 + 192 p + 96 wn + 32 eb; k step h of a slice: chunk 2 h + khalf
     const int l32 = lane & 31;
     const int khalf = lane >> 5;
@@ -251,35 +260,38 @@ __global__ __launch_bounds__(256, 1) void k_router_logits_tiled(
 #pragma unroll
     for (int h = 0; h < 2; ++h) off[h] = l32 * 64 + pchunk(l32, 2 * h + khalf) * 16;
 
-    f32x16_t acc[4][3];
+    f32x16_t acc[2][3];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int eb = 0; eb < 3; ++eb) acc[mb][eb] = f32x16_t{};
-    // fragment r of a set: r < 4 token block r; else plane (r - 4) / 3, expert block (r - 4) % 3
-    i32x4_t fr[2][13];
+    // fragment r of a set: r < 2 token block r; else plane (r - 2) / 3, expert block (r - 2) % 3
+    i32x4_t fr[2][kTiledFrags];
     auto read_frag = [&](int set, const uint8_t* base, int h, int r) {
-        const int row = r < 4 ? 128 * wm + 32 * r
-                              : kTiledTokens + kTiledExperts * ((r - 4) / 3) + 96 * wn + 32 * ((r - 4) % 3);
+        const int row = r < 2 ? 64 * wm + 32 * r
+                              : kTiledTokens + kTiledExperts * ((r - 2) / 3) + 96 * wn + 32 * ((r - 2) % 3);
         fr[set][r] = *reinterpret_cast<const i32x4_t*>(base + row * 64 + off[h]);
     };
+    // MFMA i of a k step: plane i / 6, expert block (i / 2) % 3, token block i % 2
     auto mfma = [&](int set, int i) {
-        const int p = i / 12, eb = (i >> 2) % 3, mb = i & 3;
+        const int p = i / 6, eb = (i >> 1) % 3, mb = i & 1;
         acc[mb][eb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, fr[set][mb]), __builtin_bit_cast(bf16x8_t, fr[set][4 + 3 * p + eb]),
+            __builtin_bit_cast(bf16x8_t, fr[set][mb]), __builtin_bit_cast(bf16x8_t, fr[set][2 + 3 * p + eb]),
             acc[mb][eb], 0, 0, 0);
     };
 
+    if (copier) {
 #pragma unroll
-    for (int s = 0; s < kTiledSlots; ++s) {
-        const int kt = min(s, nk - 1);
+        for (int s = 0; s < kTiledSlots; ++s) {
+            const int kt = min(s, nk - 1);
 #pragma unroll
-        for (int j = 0; j < kTiledNpw; ++j) copy_to_lds(src[j] + kt * 64, my_copies + s * kTiledSlotB + j * 1024);
+            for (int j = 0; j < kTiledNpw; ++j) copy_to_lds(src[j] + kt * 64, my_copies + s * kTiledSlotB + j * 1024);
+        }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((kTiledSlots - 1) * kTiledNpw));
     lds_barrier();
 #pragma unroll
-    for (int r = 0; r < 13; ++r) read_frag(0, lds, 0, r);
+    for (int r = 0; r < kTiledFrags; ++r) read_frag(0, lds, 0, r);
 
     for (int kt = 0; kt < nk; ++kt) {
         const int sc = kt % kTiledSlots;
@@ -288,11 +300,11 @@ __global__ __launch_bounds__(256, 1) void k_router_logits_tiled(
         const uint8_t* nxt = lds + sn * kTiledSlotB;
         // first half: step 0 of slice kt; read step 1 of slice kt
 #pragma unroll
-        for (int i = 0; i < 36; ++i) {
+        for (int i = 0; i < kTiledMfmas; ++i) {
             mfma(0, i);
 #pragma unroll
-            for (int r = 0; r < 13; ++r)
-                if (i == r * 36 / 13) read_frag(1, cur, 1, r);
+            for (int r = 0; r < kTiledFrags; ++r)
+                if (i == r * kTiledMfmas / kTiledFrags) read_frag(1, cur, 1, r);
             __builtin_amdgcn_sched_barrier(0);
         }
         // slice kt + 1 landed (at most the copies of kt + 2 in flight), and
@@ -302,17 +314,16 @@ __global__ __launch_bounds__(256, 1) void k_router_logits_tiled(
         const int kin = min(kt + kTiledSlots, nk - 1);
         const uint32_t islot = my_copies + sc * kTiledSlotB;
         // second half: step 1 of slice kt; read step 0 of slice kt + 1;
-        // refill this slot with slice kt + 3
+        // the copying waves refill this slot with slice kt + 3
 #pragma unroll
-        for (int i = 0; i < 36; ++i) {
+        for (int i = 0; i < kTiledMfmas; ++i) {
             mfma(1, i);
 #pragma unroll
-            for (int r = 0; r < 13; ++r) {
-                if (i == r * 36 / 13) {
-                    read_frag(0, nxt, 0, r);
-                    copy_to_lds(src[r] + kin * 64, islot + r * 1024);
-                }
-            }
+            for (int r = 0; r < kTiledFrags; ++r)
+                if (i == r * kTiledMfmas / kTiledFrags) read_frag(0, nxt, 0, r);
+#pragma unroll
+            for (int r = 0; r < kTiledNpw; ++r)
+                if (i == r * kTiledMfmas / kTiledNpw && copier) copy_to_lds(src[r] + kin * 64, islot + r * 1024);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -324,10 +335,10 @@ __global__ __launch_bounds__(256, 1) void k_router_logits_tiled(
         const int e = e0 + 96 * wn + 32 * eb + l32;
         if (e >= E) continue;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int t = t0 + 128 * wm + 32 * mb + 8 * (j >> 2) + 4 * khalf + (j & 3);
+                const int t = t0 + 64 * wm + 32 * mb + 8 * (j >> 2) + 4 * khalf + (j & 3);
                 if (t < T) {
                     const float v = acc[mb][eb][j];
                     out[static_cast<size_t>(t) * E + e] = nsplit == 1 ? sigmoid_bias(v, bias, e) : v;
@@ -587,7 +598,7 @@ hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bi
         hipLaunchKernelGGL(k_router_prep, dim3(static_cast<unsigned>((n / 4 + 255) / 256)), dim3(256), 0,
                            s, W_gate, rw.planes, n);
         dim3 g1((T + kTiledTokens - 1) / kTiledTokens, (E + kTiledExperts - 1) / kTiledExperts, rw.nsplit);
-        hipLaunchKernelGGL(k_router_logits_tiled, g1, dim3(256), 0, s, x, rw.planes, bias, rw.partial,
+        hipLaunchKernelGGL(k_router_logits_tiled, g1, dim3(64 * kTiledWaves), 0, s, x, rw.planes, bias, rw.partial,
                            rw.scores, T, d, E, d / rw.nsplit, rw.nsplit);
     } else {
         dim3 g1((T + kLogitTokens - 1) / kLogitTokens, (E + kLogitExperts - 1) / kLogitExperts,
