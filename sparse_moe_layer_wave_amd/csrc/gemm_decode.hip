@@ -46,11 +46,15 @@ enum Mode { GU_BF16 = 0, DN_BF16 = 1, GU_FP8 = 2, DN_FP8 = 3, GU_FP8B = 4, DN_FP
 // Column blocks per workgroup, taken one after the other with the weight
 // stream running on across the boundary.  An e4m3 block moves half the bytes
 // of a bf16 one, so two of them halve the per-workgroup start and end costs
-// (measured at T = 64: gate_up 0.400 -> 0.393 ms, down 0.197 -> 0.186 ms); a
-// second bf16 block gained nothing, and four e4m3 blocks cost occupancy.
-// The e4m3 path needs d and d_ff in whole 256-byte batches, so the halved
-// grids divide evenly.
+// (measured at T = 64: gate_up 0.400 -> 0.393 ms, down 0.197 -> 0.186 ms);
+// four e4m3 blocks cost occupancy.  A bf16 down block (128 rows of d_ff) is
+// short too: two per workgroup where d allows, down 0.363 -> 0.355 ms at
+// T = 64.  The bf16 gate_up keeps one: two gained 0.6% at T = 64 but cost 3%
+// with skewed routing, where fewer, longer workgroups balance worse.  The
+// e4m3 path needs d and d_ff in whole 256-byte batches, so the halved grids
+// divide evenly.
 constexpr int kSubsBf16 = 1;
+constexpr int kSubsBf16Down = 2;        // where d is a multiple of 256
 constexpr int kSubsFp8 = 2;
 
 constexpr int kBatchB = 256;            // bytes of k per row and batch
@@ -381,9 +385,15 @@ hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uin
                  reinterpret_cast<const uint8_t*>(W_last), offsets, slice_off, y, nullptr, nullptr,
                  nullptr, nullptr, F, d, E};
     if (max_slices == 0) return hipSuccess;
-    const dim3 grid(max_slices, d / (128 * kSubsBf16));
-    if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<DN_BF16, kSubsBf16, 2>), grid, dim3(256), 0, s, g);
-    else hipLaunchKernelGGL((k_decode_gemm<DN_BF16, kSubsBf16, 1>), grid, dim3(256), 0, s, g);
+    if (d % (128 * kSubsBf16Down) == 0) {
+        const dim3 grid(max_slices, d / (128 * kSubsBf16Down));
+        if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<DN_BF16, kSubsBf16Down, 2>), grid, dim3(256), 0, s, g);
+        else hipLaunchKernelGGL((k_decode_gemm<DN_BF16, kSubsBf16Down, 1>), grid, dim3(256), 0, s, g);
+    } else {
+        const dim3 grid(max_slices, d / (128 * kSubsBf16));
+        if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<DN_BF16, kSubsBf16, 2>), grid, dim3(256), 0, s, g);
+        else hipLaunchKernelGGL((k_decode_gemm<DN_BF16, kSubsBf16, 1>), grid, dim3(256), 0, s, g);
+    }
     return hipGetLastError();
 }
 
