@@ -47,15 +47,17 @@ enum Mode { GU_BF16 = 0, DN_BF16 = 1, GU_FP8 = 2, DN_FP8 = 3, GU_FP8B = 4, DN_FP
 // stream running on across the boundary.  An e4m3 block moves half the bytes
 // of a bf16 one, so two of them halve the per-workgroup start and end costs
 // (measured at T = 64: gate_up 0.400 -> 0.393 ms, down 0.197 -> 0.186 ms);
-// four e4m3 blocks cost occupancy.  A bf16 down block (128 rows of d_ff) is
-// short too: two per workgroup where d allows, down 0.363 -> 0.355 ms at
-// T = 64.  The bf16 gate_up keeps one: two gained 0.6% at T = 64 but cost 3%
-// with skewed routing, where fewer, longer workgroups balance worse.  The
-// e4m3 path needs d and d_ff in whole 256-byte batches, so the halved grids
-// divide evenly.
+// four e4m3 gate_up blocks cost occupancy.  Down blocks (128 rows of d_ff)
+// are short: e4m3 takes four per workgroup where d allows (T = 64 down
+// 0.191 -> 0.187 ms), bf16 two (0.363 -> 0.355 ms; four gained under 1% and
+// lost as much with skewed routing).  The bf16 gate_up keeps one: two gained
+// 0.6% at T = 64 but cost 3% with skewed routing, where fewer, longer
+// workgroups balance worse.  The e4m3 path needs d and d_ff in whole 256-byte
+// batches, so the halved grids divide evenly.
 constexpr int kSubsBf16 = 1;
 constexpr int kSubsBf16Down = 2;        // where d is a multiple of 256
 constexpr int kSubsFp8 = 2;
+constexpr int kSubsFp8Down = 4;         // where d is a multiple of 512
 
 constexpr int kBatchB = 256;            // bytes of k per row and batch
 constexpr int kSlabB = 32 * kBatchB;    // bytes of one wave's LDS slab (8 KB)
@@ -421,14 +423,20 @@ hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint
                                   hipStream_t s) {
     DecodeArgs g{hq, nullptr, Wq, nullptr, offsets, slice_off, y, hs, ws, nullptr, nullptr, F, d, E};
     if (max_slices == 0) return hipSuccess;
-    const dim3 grid(max_slices, d / (128 * kSubsFp8));
-    if (block) {
-        if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<DN_FP8B, kSubsFp8, 2>), grid, dim3(256), 0, s, g);
-        else hipLaunchKernelGGL((k_decode_gemm<DN_FP8B, kSubsFp8, 1>), grid, dim3(256), 0, s, g);
-    } else {
-        if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<DN_FP8, kSubsFp8, 2>), grid, dim3(256), 0, s, g);
-        else hipLaunchKernelGGL((k_decode_gemm<DN_FP8, kSubsFp8, 1>), grid, dim3(256), 0, s, g);
-    }
+#define HY3_DN_FP8(SUBS)                                                                                   \
+    do {                                                                                                   \
+        const dim3 grid(max_slices, d / (128 * (SUBS)));                                                   \
+        if (block) {                                                                                       \
+            if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<DN_FP8B, SUBS, 2>), grid, dim3(256), 0, s, g);  \
+            else hipLaunchKernelGGL((k_decode_gemm<DN_FP8B, SUBS, 1>), grid, dim3(256), 0, s, g);          \
+        } else {                                                                                           \
+            if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<DN_FP8, SUBS, 2>), grid, dim3(256), 0, s, g);   \
+            else hipLaunchKernelGGL((k_decode_gemm<DN_FP8, SUBS, 1>), grid, dim3(256), 0, s, g);           \
+        }                                                                                                  \
+    } while (0)
+    if (d % (128 * kSubsFp8Down) == 0) HY3_DN_FP8(kSubsFp8Down);
+    else HY3_DN_FP8(kSubsFp8);
+#undef HY3_DN_FP8
     return hipGetLastError();
 }
 
