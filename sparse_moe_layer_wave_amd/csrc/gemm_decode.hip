@@ -358,10 +358,14 @@ int decode_row_groups(int T, int k, int E, int esz, bool shared) {
 // 1.367, T = 512 1.489 vs 1.373; e4m3 T = 384 0.781 vs 0.810, T = 448 0.812
 // vs 0.818, T = 512 0.891 vs 0.825.  The full block's shared expert adds T
 // rows, counted twice: each of its slices streams a whole expert's weights.
+// The kernels address their A operand (x [T, d] or h [rows, d_ff], esz bytes
+// per element as the weights) with 32-bit byte offsets, so both must stay
+// under 4 GiB.
 bool use_decode_path(int T, int d, int F, int E, int k, int esz, bool shared) {
     const long long rows = static_cast<long long>(T) * k + (shared ? 2LL * T : 0);
     const int rg = decode_row_groups(T, k, E, esz, shared);
-    return rows <= (rg == 2 ? 20LL : 11LL) * E && (d * esz) % kBatchB == 0 && (F * esz) % kBatchB == 0;
+    const bool a32 = static_cast<long long>(T) * d * esz < (1LL << 32) && rows * F * esz < (1LL << 32);
+    return rows <= (rg == 2 ? 20LL : 11LL) * E && (d * esz) % kBatchB == 0 && (F * esz) % kBatchB == 0 && a32;
 }
 
 int decode_bm(int rg) { return 16 * rg; }
