@@ -279,6 +279,75 @@ def shares(steps, warmup):
     return out
 
 
+def _graph_ms(fn, reps):
+    """Median time of fn's GPU work over reps replays of a HIP graph that
+    captures it (launch overhead excluded)."""
+    fn()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    del graph
+    return float(np.median(times))
+
+
+def vendor_gemm(steps, warmup):
+    """The T=8192 prefill expert GEMMs on the vendor GEMM library (torch.mm,
+    which calls hipBLASLt / rocBLAS), beside this library's grouped kernels on
+    the same workload: (a) one dense GEMM of all T*k rows against one expert's
+    weights, the same FLOPs with every weight reused by every row; (b) one GEMM
+    per expert on that expert's rows of the prefill routing, all launches
+    captured in one HIP graph.  bf16 operands, fp32 accumulation, random data."""
+    c = dict(inputs.CONFIGS[2])
+    res, _ = run_workload(c, steps, warmup)
+    T, d, E, k, F = c["T"], c["d"], c["E"], c["k"], c["F"]
+    counts = np.bincount(res["routing"]["idx"].reshape(-1), minlength=E)
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    R = int(offs[-1])
+    g = torch.Generator(device="cuda").manual_seed(0)
+
+    def rnd(*shape):
+        return torch.randn(*shape, device="cuda", generator=g).to(torch.bfloat16)
+
+    X, H = rnd(R, d), rnd(R, F)
+    W_gu, W_dn = rnd(E, 2 * F, d), rnd(E, d, F)
+    G, Y = torch.empty(R, 2 * F, dtype=torch.bfloat16, device="cuda"), torch.empty(R, d, dtype=torch.bfloat16, device="cuda")
+    reps = max(steps, 10)
+    sl = [(int(offs[e]), int(offs[e + 1])) for e in range(E) if counts[e] > 0]
+    cases = {
+        "dense_gate_up": (lambda: torch.mm(X, W_gu[0].t(), out=G), 2.0 * R * d * 2 * F),
+        "per_expert_gate_up": (lambda: [torch.mm(X[a:b], W_gu[e].t(), out=G[a:b])
+                                        for e, (a, b) in zip(np.nonzero(counts)[0], sl)], 2.0 * R * d * 2 * F),
+        "dense_down": (lambda: torch.mm(H, W_dn[0].t(), out=Y), 2.0 * R * F * d),
+        "per_expert_down": (lambda: [torch.mm(H[a:b], W_dn[e].t(), out=Y[a:b])
+                                     for e, (a, b) in zip(np.nonzero(counts)[0], sl)], 2.0 * R * F * d),
+    }
+    out = {"vendor_gemm": "T=8192 prefill expert GEMMs: torch.mm (hipBLASLt / rocBLAS) against this library's "
+                          "grouped kernels on the same routing", "rows": R, "experts": len(sl),
+           "rows_per_expert": {"min": int(counts[counts > 0].min()), "mean": round(float(R / len(sl)), 1),
+                               "max": int(counts.max())}}
+    for name, (fn, flops) in cases.items():
+        ms = _graph_ms(fn, reps)
+        out[name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1), "frac": round(flops / ms / 1e9 / 2500.0, 4)}
+    for st in ("gate_up", "down"):
+        rf = roofline(res, st, "mfma")
+        out["grouped_" + st] = {"ms": rf["avg_kernel_ms"], "tflops": rf["achieved"], "frac": rf["frac"]}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,13 +363,16 @@ def main():
     ap.add_argument("--shares", action="store_true",
                     help="print one JSON line with the expert GEMMs at one GPU's share of an 8-way expert-parallel "
                          "or 8- / 4-way d_ff-parallel layer, and exit")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="print one JSON line comparing the T=8192 prefill expert GEMMs with torch.mm "
+                         "(hipBLASLt / rocBLAS), dense and per expert, and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 1 GiB device-to-device copy (outside every timed region), "
                          "a known byte count for scaling HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); the layer is not sharded "
-              "across GPUs in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for {args.gpus}): the layer is not sharded "
+              "across GPUs", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     if args.copy_calibration:
@@ -313,6 +385,9 @@ def main():
 
     if args.shares:
         print(json.dumps(shares(args.steps, args.warmup)), flush=True)
+        return
+    if args.vendor_gemm:
+        print(json.dumps(vendor_gemm(args.steps, args.warmup)), flush=True)
         return
 
     if args.profile_workload:
