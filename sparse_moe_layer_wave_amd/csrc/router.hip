@@ -572,6 +572,98 @@ __global__ __launch_bounds__(64) void k_router_select_wave(
     }
 }
 
+// The same for E <= 192 (NQ <= 12) with four waves per 4 tokens: each wave
+// loads a quarter of the d-chunks' partials (all its loads in flight at
+// once) into LDS, and wave 0 adds them up in the order s = 0..nsplit-1, so
+// the scores are bit-identical to the one-wave kernel's.  (One wave alone
+// takes two rounds of loads: 16 chunks x 12 experts exceed what a wave keeps
+// in flight.)
+template <int NQ>
+__global__ __launch_bounds__(256) void k_router_select_wave4(
+    const float* __restrict__ partial, const float* __restrict__ scores, int nsplit,
+    const float* __restrict__ bias, const float* __restrict__ score_bias, int T, int E, int k,
+    float scale, int32_t* __restrict__ idx, float* __restrict__ wout) {
+    static_assert(NQ <= 12, "LDS holds kMaxSplit x 12 partials per lane");
+    __shared__ float s_p[kMaxSplit][NQ][64];
+    __shared__ float s_sc[4][16 * NQ];
+    const int wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15;                              // lane within the token's row
+    const int ts = lane >> 4;                             // token of the workgroup
+    const int t = blockIdx.x * 4 + ts;
+    const bool active = t < T;
+    const size_t n = static_cast<size_t>(T) * E;
+    const size_t row = static_cast<size_t>(active ? t : 0) * E;
+    // the biases first, in flight with the partials
+    float bq[NQ], sbq[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int e = j + 16 * q;
+        bq[q] = (bias && e < E) ? bias[e] : 0.f;
+        sbq[q] = (score_bias && e < E) ? score_bias[e] : 0.f;
+    }
+    float sc[NQ];
+    if (nsplit > 1) {
+        constexpr int CMAX = kMaxSplit / 4;
+        const int c = (nsplit + 3) / 4;                   // chunks per wave
+        const int s0 = wv * c;
+        float pv[CMAX][NQ];
+#pragma unroll
+        for (int u = 0; u < CMAX; ++u)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int e = j + 16 * q;
+                const int sp = s0 + u;
+                pv[u][q] = (u < c && sp < nsplit && active && e < E) ? partial[sp * n + row + e] : 0.f;
+            }
+#pragma unroll
+        for (int u = 0; u < CMAX; ++u)
+            if (u < c && s0 + u < nsplit)
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) s_p[s0 + u][q][lane] = pv[u][q];
+        __syncthreads();
+        if (wv != 0) return;
+        float z[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) z[q] = 0.f;
+        for (int sp = 0; sp < nsplit; ++sp)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) z[q] += s_p[sp][q][lane];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const float zb = bias ? z[q] + bq[q] : z[q];
+            sc[q] = 1.0f / (1.0f + expf(-zb));
+        }
+    } else {
+        if (wv != 0) return;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int e = j + 16 * q;
+            sc[q] = (active && e < E) ? scores[row + e] : 0.f;
+        }
+    }
+    uint32_t key[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int e = j + 16 * q;
+        key[q] = 0u;
+        if (active && e < E) {
+            const float v = score_bias ? sc[q] + sbq[q] : sc[q];
+            key[q] = max(order_key(v), 1u);
+        }
+        s_sc[ts][e] = sc[q];
+    }
+    const int my_e = select_rounds<NQ>(key, j, k);
+    // a wave's LDS accesses complete in order: the stores above precede this read
+    const float my_s = (active && j < k) ? s_sc[ts][my_e] : 0.f;
+    const float my_w = slot_weight(my_s, lane, k, scale);
+    if (active && j < k) {
+        const size_t pair = static_cast<size_t>(t) * k + j;
+        idx[pair] = my_e;
+        wout[pair] = my_w;
+    }
+}
+
 }  // namespace
 
 int router_nsplit(int T, int d, int E) {
@@ -619,7 +711,11 @@ hipError_t launch_router(const uint16_t* x, const float* W_gate, const float* bi
     }
 #define HY3_SELECT(NQ)                                                                                      \
     do {                                                                                                    \
-        if (one_block)                                                                                      \
+        if (one_block && (NQ) <= 12)                                                                        \
+            hipLaunchKernelGGL(k_router_select_wave4<((NQ) <= 12 ? (NQ) : 12)>,                             \
+                               dim3(static_cast<unsigned>((T + 3) / 4)), dim3(256), 0, s, rw.partial,       \
+                               rw.scores, rw.nsplit, bias, score_bias, T, E, k, scale, idx, w);             \
+        else if (one_block)                                                                                 \
             hipLaunchKernelGGL(k_router_select_wave<NQ>, dim3(static_cast<unsigned>((T + 3) / 4)), dim3(64), 0, \
                                s, rw.partial, rw.scores, rw.nsplit, bias, score_bias, T, E, k, scale, idx, w); \
         else                                                                                                \
