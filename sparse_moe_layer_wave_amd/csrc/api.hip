@@ -307,16 +307,16 @@ static int forward_bf16(const uint16_t* x, const uint16_t* norm_w, float norm_ep
     const bool decode = hy3::use_decode_path(T, d, d_ff, E, k, 2, shared);
     const int rg = hy3::decode_row_groups(T, k, E, 2, shared);
     const int max_slices = (L.rows + hy3::decode_bm(rg) - 1) / hy3::decode_bm(rg) + Eg;
+    int* sched = reinterpret_cast<int*>(ws + L.sched);
+    // the dispatch also zeroes the grouped GEMMs' work counters
     if (e == hipSuccess)
         e = hy3::launch_dispatch(idx, T, E, k, L.nb, blk_counts,
                                  reinterpret_cast<int32_t*>(ws + L.blk_base),
                                  reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
                                  decode ? hy3::decode_bm(rg) : hy3::prefill_bm(), row_of, tok_of,
-                                 shared ? 1 : 0, s);
+                                 shared ? 1 : 0, s, false, decode ? nullptr : sched,
+                                 decode ? 0 : hy3::kSchedInts);
     if (e == hipSuccess) e = mark(ev, 2, s);
-    int* sched = reinterpret_cast<int*>(ws + L.sched);
-    if (e == hipSuccess && !decode)
-        e = hy3::launch_fill_u32(reinterpret_cast<uint32_t*>(sched), hy3::kSchedInts, 0u, s);
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_gate_up_decode(x, tok_of, W_gate_up, Ws_gu, offsets, tile_off, max_slices,
@@ -374,11 +374,16 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
     const bool decode = hy3::use_decode_path(T, d, d_ff, E, k, 1, false);
     const int rg = hy3::decode_row_groups(T, k, E, 1, false);
     const int max_slices = (L.rows + hy3::decode_bm(rg) - 1) / hy3::decode_bm(rg) + E;
+    int* sched = reinterpret_cast<int*>(ws + L.sched);
+    // the dispatch also zeroes the weight-streaming gate_up's row maxima
+    // (decode) or the grouped GEMMs' work counters
     if (e == hipSuccess)
         e = hy3::launch_dispatch(idx, T, E, k, L.nb, reinterpret_cast<int32_t*>(ws + L.blk_counts),
                                  reinterpret_cast<int32_t*>(ws + L.blk_base),
                                  reinterpret_cast<int32_t*>(ws + L.counts), offsets, tile_off,
-                                 decode ? hy3::decode_bm(rg) : hy3::prefill_bm(), row_of, tok_of, 0, s);
+                                 decode ? hy3::decode_bm(rg) : hy3::prefill_bm(), row_of, tok_of, 0, s,
+                                 false, decode ? reinterpret_cast<int32_t*>(amax) : sched,
+                                 decode ? static_cast<int>(Tk) : hy3::kSchedInts);
     if (e == hipSuccess) e = mark(ev, 2, s);
     // the grouped gate_up reads its rows' activation scales per dispatch row,
     // from hs, which the h quantiser overwrites after it
@@ -386,10 +391,6 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
         e = hy3::launch_quant_rows(x, T, d, xq, xs, s, decode ? nullptr : row_of, k, decode ? nullptr : hs);
     float* hmax = reinterpret_cast<float*>(amax);
     const int nblk = (d_ff + 127) / 128;
-    int* sched = reinterpret_cast<int*>(ws + L.sched);
-    if (e == hipSuccess && decode) e = hy3::launch_fill_u32(amax, Tk, 0u, s);
-    if (e == hipSuccess && !decode)
-        e = hy3::launch_fill_u32(reinterpret_cast<uint32_t*>(sched), hy3::kSchedInts, 0u, s);
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_gate_up_decode_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, max_slices,

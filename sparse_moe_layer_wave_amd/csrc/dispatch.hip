@@ -97,10 +97,12 @@ __global__ __launch_bounds__(256) void k_block_scan(const int32_t* __restrict__ 
 // GEMMs.
 __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ counts, int E,
                                                   int extra, int32_t* __restrict__ offsets,
-                                                  int32_t* __restrict__ tile_off, int bm) {
+                                                  int32_t* __restrict__ tile_off, int bm,
+                                                  int32_t* __restrict__ zero, int nzero) {
     __shared__ int s_cnt[1024];
     __shared__ int s_til[1024];
     const int tid = threadIdx.x;
+    for (int i = tid; i < nzero; i += 1024) zero[i] = 0;
     const int n = E + (extra > 0 ? 1 : 0);
     const int c = tid < E ? counts[tid] : (tid < n ? extra : 0);
     const int nt = (c + bm - 1) / bm;
@@ -184,12 +186,14 @@ __global__ __launch_bounds__(1024) void k_dispatch_one(const int32_t* __restrict
                                                       int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ tile_off,
                                                       int32_t* __restrict__ row_of,
-                                                      int32_t* __restrict__ tok_of, int shared_row0) {
+                                                      int32_t* __restrict__ tok_of, int shared_row0,
+                                                      int32_t* __restrict__ zero, int nzero) {
     __shared__ unsigned long long mask[1024];
     __shared__ int s_cnt[1024];
     __shared__ int s_til[1024];
     __shared__ int s_off[1024];
     const int tid = threadIdx.x;
+    for (int i = tid; i < nzero; i += 1024) zero[i] = 0;
     mask[tid] = 0ull;
     __syncthreads();
     const int npairs = T * k;
@@ -274,16 +278,18 @@ hipError_t launch_block_counts(const int32_t* idx, int T, int E, int k, int nb,
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
                            const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,
                            int32_t* offsets, int32_t* tile_off, int bm, int32_t* row_of,
-                           int32_t* tok_of, int shared, hipStream_t s, bool checked) {
+                           int32_t* tok_of, int shared, hipStream_t s, bool checked,
+                           int32_t* zero, int nzero) {
     if (nb == 1) {
         auto kern = checked ? k_dispatch_one<true> : k_dispatch_one<false>;
         hipLaunchKernelGGL(kern, dim3(1), dim3(1024), 0, s, idx, T, E, k, shared ? T : 0, bm,
-                           blk_base, counts, offsets, tile_off, row_of, tok_of, shared ? T * k : -1);
+                           blk_base, counts, offsets, tile_off, row_of, tok_of, shared ? T * k : -1,
+                           zero, nzero);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(k_block_scan, dim3(E), dim3(256), 0, s, blk_counts, blk_base, counts, nb);
     hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, s, counts, E, shared ? T : 0, offsets,
-                       tile_off, bm);
+                       tile_off, bm, zero, nzero);
     auto scatter = checked ? k_scatter<true> : k_scatter<false>;
     hipLaunchKernelGGL(scatter, dim3(nb), dim3(256), 0, s, idx, T, E, k, nb, blk_base, offsets,
                        row_of, tok_of, shared ? T * k : -1);

@@ -142,12 +142,6 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_f32(const float* __res
     if (lane == 0) s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
 }
 
-__global__ __launch_bounds__(256) void k_fill_u32(uint32_t* __restrict__ p, size_t n, uint32_t v) {
-    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-         i += static_cast<size_t>(gridDim.x) * 256)
-        p[i] = v;
-}
-
 }  // namespace
 
 hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, const float* hmax, int nblk,
@@ -156,12 +150,6 @@ hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, cons
     const unsigned wgs = static_cast<unsigned>((static_cast<long long>(rows) + kRowsPerWg - 1) / kRowsPerWg);
     hipLaunchKernelGGL(k_quant_rows_f32, dim3(wgs), dim3(kQThreads), 0, st, h, amax_bits, hmax, nblk, rows, cols,
                        q, s);
-    return hipGetLastError();
-}
-
-hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
-    const unsigned blocks = static_cast<unsigned>(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096);
-    hipLaunchKernelGGL(k_fill_u32, dim3(blocks), dim3(256), 0, st, p, n, v);
     return hipGetLastError();
 }
 

@@ -115,10 +115,14 @@ hipError_t launch_rms_norm(const uint16_t* x, const uint16_t* w, int T, int d, f
 // so offsets and tile_off then hold E + 2 entries.  checked: the routing is
 // the caller's; pairs with an expert outside [0, E) or repeated within the
 // token's row take no row (row_of = -1) and are counted for no expert.
+// zero, nzero: ints the dispatch also sets to 0 for the kernels after it (the
+// grouped GEMMs' work counters, the e4m3 decode gate_up's row maxima), or
+// NULL, 0; its single-workgroup kernel clears them, so no fill launch is needed.
 hipError_t launch_dispatch(const int32_t* idx, int T, int E, int k, int nb,
                            const int32_t* blk_counts, int32_t* blk_base, int32_t* counts,
                            int32_t* offsets, int32_t* tile_off, int bm, int32_t* row_of,
-                           int32_t* tok_of, int shared, hipStream_t s, bool checked = false);
+                           int32_t* tok_of, int shared, hipStream_t s, bool checked = false,
+                           int32_t* zero = nullptr, int nzero = 0);
 
 // prefill-sized batches: MFMA grouped GEMMs over row blocks of prefill_bm() rows
 // (max_blocks bounds the number of row blocks, tile_off[E]).  E counts the
@@ -194,7 +198,6 @@ hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, uint8_t* q, 
 // the nblk partial maxima hmax[blk * rows + row] (the grouped gate_up's).
 hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, const float* hmax, int nblk,
                                  int rows, int cols, uint8_t* q, float* s, hipStream_t st);
-hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t st);
 // rs: the tokens' activation scales per dispatch row (launch_quant_rows' rs)
 hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* rs, const int32_t* tok_of,
                               const uint8_t* Wq, const float* ws, const int32_t* offsets,
