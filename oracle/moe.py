@@ -16,6 +16,8 @@ except where the pages fix a precision:
 * The FP8 variant quantises activations to e4m3 with one float32 scale per row
   ("DeepSeek V4-Flash architecture Q&A", Q7.2 for the format, Q7.4 for
   per-channel scales), computing the scale and the scaled values in float32.
+  The SwiGLU activation is a stored activation there too: it is rounded to
+  bf16 (from float64, as above) and its bf16 values are quantised.
 """
 
 from collections import namedtuple
@@ -308,7 +310,8 @@ def forward_fp8(x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale, logit_bias=N
     Routing is the float32 router of
     ``route``.  Each token's bf16 row is quantised with quant_row_e4m3 before
     the gate_up product; each (token, slot) SwiGLU activation row, rounded to
-    float32, is quantised the same way before the down product.  Products use
+    bf16 where the layer stores it, is quantised the same way before the down
+    product.  Products use
     the dequantised operands in float64; each expert output row is rounded to
     bf16 (as in ``forward``) and the combine is as in ``forward``."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
@@ -320,7 +323,7 @@ def forward_fp8(x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale, logit_bias=N
     xd = _dequant_x_e4m3(x_bits)
     for e in np.unique(r.idx):
         t, j = np.nonzero(r.idx == e)
-        y_pre = _fp8_expert_parts(xd[t], Wq_gu[e], s_gu[e], Wq_dn[e], s_dn[e])[3]
+        y_pre = _fp8_expert_parts(xd[t], Wq_gu[e], s_gu[e], Wq_dn[e], s_dn[e])[4]
         out[t] += r.w[t, j][:, None] * round_to_bf16(y_pre)
     return out, r
 
@@ -335,22 +338,24 @@ def _dequant_x_e4m3(x_bits):
 def _fp8_expert_parts(xd, Wq_gu_e, s_gu_e, Wq_dn_e, s_dn_e):
     """One e4m3 expert on dequantised x rows xd [n, d] (float64).
 
-    a = SiLU(xd Wg^T) * (xd Wu^T) with the dequantised weights; each row of
-    float32(a) is quantised with quant_row_e4m3 and dequantised; the expert
-    output before its bf16 rounding is y_pre = dequant(a) Wd^T.  Returns
-    (scaled float32 [n, F], the values quant_row_e4m3 rounds to e4m3;
-    s_a float32 [n], the rows' scales; a_deq float64 [n, F]; y_pre float64
-    [n, d])."""
+    a = SiLU(xd Wg^T) * (xd Wu^T) with the dequantised weights, rounded to
+    bf16 where the layer stores it; each row of bf16(a) (exact in float32) is
+    quantised with quant_row_e4m3 and dequantised; the expert output before
+    its bf16 rounding is y_pre = dequant(a) Wd^T.  Returns (a float64 [n, F]
+    before its bf16 rounding; scaled float32 [n, F], the values
+    quant_row_e4m3 rounds to e4m3; s_a float32 [n], the rows' scales; a_deq
+    float64 [n, F]; y_pre float64 [n, d])."""
     Wdn = dequant_e4m3(Wq_dn_e, s_dn_e)
     a = _swiglu_act(xd, dequant_e4m3(Wq_gu_e, s_gu_e), Wdn.shape[1])
+    a16 = round_to_bf16(a).astype(np.float32)
     n, F = a.shape
     qa = np.empty((n, F), np.uint8)
     sa = np.empty(n, np.float32)
     scaled = np.empty((n, F), np.float32)
     for i in range(n):
-        qa[i], sa[i], scaled[i] = quant_row_e4m3_parts(a[i].astype(np.float32))
+        qa[i], sa[i], scaled[i] = quant_row_e4m3_parts(a16[i])
     ad = e4m3_bits_to_f64(qa) * sa.astype(np.float64)[:, None]
-    return scaled, sa, ad, ad @ Wdn.T
+    return a, scaled, sa, ad, ad @ Wdn.T
 
 
 def forward_fp8_tokens(tokens, x_bits, W_gate, Wq_gu, s_gu, Wq_dn, s_dn, k, scale, logit_bias=None):
@@ -403,8 +408,9 @@ def forward_fp8_detail(tokens, x_bits, r, Wq_gu, s_gu, Wq_dn, s_dn):
     """The per-slot terms of ``forward_fp8`` for the listed tokens (r:
     ``route``'s result for the whole batch; slot j is expert r.idx[t, j]).
 
-    Returns Detail(tokens, expert [n, k], w [n, k], None, y float64 [n, k, d],
-    scaled float32 [n, k, F], s_a float32 [n, k], a_deq float64 [n, k, F]):
+    Returns Detail(tokens, expert [n, k], w [n, k], h float64 [n, k, F],
+    y float64 [n, k, d], scaled float32 [n, k, F], s_a float32 [n, k], a_deq
+    float64 [n, k, F]): h is the SwiGLU activation before its bf16 rounding,
     scaled holds the values the activation quantiser rounds to e4m3, s_a the
     activation rows' scales, a_deq the dequantised activations and y the
     expert outputs before their bf16 rounding."""
@@ -415,14 +421,15 @@ def forward_fp8_detail(tokens, x_bits, r, Wq_gu, s_gu, Wq_dn, s_dn):
     F = np.asarray(Wq_dn[int(idx[0, 0])]).shape[-1] if n else 0
     d = xd.shape[1]
     y = np.zeros((n, k, d))
+    h = np.zeros((n, k, F))
     scaled = np.zeros((n, k, F), np.float32)
     s_a = np.zeros((n, k), np.float32)
     a_deq = np.zeros((n, k, F))
     for e in np.unique(idx):
         ti, j = np.nonzero(idx == e)
-        scaled[ti, j], s_a[ti, j], a_deq[ti, j], y[ti, j] = _fp8_expert_parts(
+        h[ti, j], scaled[ti, j], s_a[ti, j], a_deq[ti, j], y[ti, j] = _fp8_expert_parts(
             xd[ti], Wq_gu[e], s_gu[e], Wq_dn[e], s_dn[e])
-    return Detail(tokens, idx.astype(np.int64), r.w[tokens].copy(), None, y, scaled, s_a, a_deq)
+    return Detail(tokens, idx.astype(np.int64), r.w[tokens].copy(), h, y, scaled, s_a, a_deq)
 
 
 # ----------------------------------------------------------------------------- accounting

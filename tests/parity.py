@@ -99,9 +99,14 @@ class LazyExperts:
 #   h (bf16 experts):  flippable if within ETA_H steps of a bf16 boundary, or
 #       within ETA_HA * max|h of its row| (the float32 error of a small h
 #       made of cancelling terms).  A flip moves y_c by |Wd[c, f]| * step.
-#   h (e4m3):  the value quantised, v = a * r, flippable if within ETA_Q steps
-#       of an e4m3 boundary or within ETA_QA * 448 (the row's largest v).  A
-#       flip moves y_c by |Wd[c, f]| * step * s_a, and the element may take it.
+#   h (e4m3):  h is rounded to bf16, and v = bf16(h) * r is quantised.  v
+#       is flippable where h's bf16 rounding may flip (as above) and v lies
+#       within that bf16 step (REL_BF16 * |v|) of an e4m3 boundary; every v
+#       of a row is, where an element next to the row's maximum may flip (the
+#       row's scale moves by up to REL_BF16, and the dequantised row with it:
+#       REL_BF16 * sum_f |Wd[c, f] * a_deq_f|); and, for the float32
+#       arithmetic, within ETA_Q steps or ETA_QA * 448.  A code flip moves
+#       y_c by |Wd[c, f]| * step * s_a.
 #   y:  the GPU's float32 y may be off the oracle's pre-rounding y by D_c =
 #       the h flips above + ETA_Y * sum_f |Wd[c, f] * h_f| (float32 sums of F
 #       products and the scale multiplications); y flips if it lies within D_c
@@ -118,6 +123,7 @@ ETA_HA = 2.0 ** -18
 ETA_Q = 2.0 ** -10
 ETA_QA = 2.0 ** -16
 ETA_Y = 2.0 ** -20
+REL_BF16 = 2.0 ** -7          # a bf16 step relative to the value, at most
 
 
 def bf16_boundary(v):
@@ -169,11 +175,26 @@ def flip_allowance(det, W_dn_of, fp8):
         ti, j = np.nonzero(det.expert == e)
         Wd = np.abs(W_dn_of(int(e)))                  # [d, F]
         if fp8:
+            # h is stored in bf16 and its bf16 values are quantised: where the
+            # GPU's and the oracle's bf16(h) agree, and so do the row's
+            # maxima, both compute v = float32(bf16(h) * r) with the same
+            # float32 operations and get the same codes.  An element whose
+            # bf16 rounding may flip moves its v by at most one bf16 step
+            # (REL_BF16 of v); one next to the row's maximum moves the row's
+            # scale by as much, hence every v of the row and the dequantised
+            # row itself.
+            h = det.h[ti, j]
+            hd, hstep = bf16_boundary(h)
+            hmax = np.max(np.abs(h), axis=1, keepdims=True)
+            hflag = (hd <= ETA_H * hstep) | (hd <= ETA_HA * hmax)
+            rflag = np.any(hflag & (np.abs(h) >= hmax * (1.0 - 2.0 ** -6)), axis=1, keepdims=True)
             v = det.scaled[ti, j].astype(np.float64)
             dist, step = e4m3_boundary(v)
-            flag = (dist <= ETA_Q * step) | (dist <= ETA_QA * 448.0)
-            C = (flag * step * det.s_a[ti, j].astype(np.float64)[:, None]) @ Wd.T
-            D = C + ETA_Y * (np.abs(det.a_deq[ti, j]) @ Wd.T)
+            moved = (hflag.astype(np.float64) + rflag) * REL_BF16 * np.abs(v)
+            flag = (dist <= ETA_Q * step) | (dist <= ETA_QA * 448.0) | (dist <= moved + ETA_Q * step)
+            ad = np.abs(det.a_deq[ti, j]) @ Wd.T
+            C = (flag * step * det.s_a[ti, j].astype(np.float64)[:, None]) @ Wd.T + rflag * REL_BF16 * ad
+            D = C + ETA_Y * ad
         else:
             h = det.h[ti, j]
             dist, step = bf16_boundary(h)

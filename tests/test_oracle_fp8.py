@@ -158,7 +158,8 @@ def test_block_dequantisation_element_by_element():
 # picks one activation column, fd[e, c], so y_c = dequant(a)[fd] * w_d
 # exactly.  The expected output is then written with torch's e4m3 cast and
 # scipy's sigmoid, independently of the oracle's codecs: x quantised per
-# token row, the float32 activation a quantised per (token, slot) row,
+# token row, the activation a rounded to bf16 (where the layer stores it) and
+# its bf16 values quantised per (token, slot) row,
 # r = float32(448 / amax), codes = e4m3(float32(a * r)), scale
 # float32(amax / 448), dequantised as codes * scale ("DeepSeek V4-Flash
 # architecture Q&A", Q7.2 and Q7.4).  Mutant copies of the oracle that move
@@ -233,8 +234,8 @@ def _one_hot_fp8_layer(seed, x_exact):
     wd = _torch_e4m3_value(cd) * s_dn
     g = xd[:, ig] * wg[None]                                 # [T, E, F], exact
     u = xd[:, iu] * wu[None]
-    a32 = (g * expit(g) * u).astype(np.float32)
-    ad = _torch_quant_rows(a32.reshape(T * E, F)).reshape(T, E, F)
+    a16 = _bf16_nearest(g * expit(g) * u).astype(np.float32)          # exact in float32
+    ad = _torch_quant_rows(a16.reshape(T * E, F)).reshape(T, E, F)
     y = np.take_along_axis(ad, np.broadcast_to(fd[None], (T, E, d)), axis=2) * wd[None]   # exact
     s = expit(x64 @ Wg.astype(np.float64).T).astype(np.float32).astype(np.float64)
     w = np.float64(np.float32(SCALE)) * s / s.sum(axis=1, keepdims=True)
@@ -250,8 +251,9 @@ def _fp8_closed_form_holds(forward_fp8, seed, x_exact):
 
 def _mutant_fp8(kind):
     """A scratch copy of the oracle's FP8 layer with one deliberate change:
-    no_h_quant (the down product takes float64 a), h_bf16_first (a rounded to
-    bf16 before its quantisation), h_per_token (one scale over a token's k
+    no_h_quant (the down product takes float64 a), h_fp32 (a quantised from
+    its float32 value, without the bf16 rounding), h_per_token (one scale over
+    a token's k
     activation rows), no_x_quant (the gate_up product takes x itself).  The
     scale's exact float32 value is pinned by the quantiser tests above: a
     one-ulp change of it does not survive the bf16 rounding of y."""
@@ -273,9 +275,10 @@ def _mutant_fp8(kind):
         if kind == "no_h_quant":
             ad = a
         elif kind == "h_per_token":
-            ad = np.stack([_oracle_deq_rows(a[t].reshape(1, -1)).reshape(k, F) for t in range(T)])
+            ad = np.stack([_oracle_deq_rows(codecs.round_to_bf16(a[t]).reshape(1, -1)).reshape(k, F)
+                           for t in range(T)])
         else:
-            src = codecs.round_to_bf16(a) if kind == "h_bf16_first" else a
+            src = a if kind == "h_fp32" else codecs.round_to_bf16(a)
             ad = _oracle_deq_rows(src.reshape(T * k, F)).reshape(T, k, F)
         out = np.zeros(x.shape)
         for e in np.unique(r.idx):
@@ -303,7 +306,7 @@ def test_fp8_quantisation_placement_closed_form():
 def test_fp8_closed_form_rejects_moved_quantisations():
     """Each mutant fails the closed-form check: the check is sharp enough to
     catch a dropped or moved quantisation of either operand."""
-    for kind in ("no_h_quant", "h_bf16_first", "h_per_token"):
+    for kind in ("no_h_quant", "h_fp32", "h_per_token"):
         assert not _fp8_closed_form_holds(_mutant_fp8(kind), 90, x_exact=True), kind
     # x itself is exact in the first form, so dropping its quantisation needs the second
     assert _fp8_closed_form_holds(_mutant_fp8("no_x_quant"), 90, x_exact=True)

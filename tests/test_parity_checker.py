@@ -82,7 +82,7 @@ def _torch_fp32_fp8_layer(x, qgu, sgu, qdn, sdn, r, F, per_token_h=False):
         t, j = np.nonzero(r.idx == e)
         Wgu = torch.from_numpy(oracle.dequant_e4m3(qgu[e], sgu[e]).astype(np.float32))
         g, u = xt[t] @ Wgu[:F].T, xt[t] @ Wgu[F:].T
-        hs[t, j] = g * torch.sigmoid(g) * u
+        hs[t, j] = (g * torch.sigmoid(g) * u).to(torch.bfloat16).float()     # h is stored in bf16
     hq = q_rows(hs.reshape(T, k * F)).reshape(T, k, F) if per_token_h else q_rows(hs.reshape(T * k, F)).reshape(T, k, F)
     for e in np.unique(r.idx):
         t, j = np.nonzero(r.idx == e)
