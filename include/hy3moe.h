@@ -159,7 +159,8 @@ int hy3moe_forward_timed(const uint16_t* x, const float* W_gate,
  *   Wq_down    e4m3 [E, d, d_ff],   s_down    fp32 [E, d]
  * Routing is the fp32 router above.  Each token's x row and each (token, slot)
  * SwiGLU activation row are quantised to e4m3 with one fp32 scale per row, as
- * hy3moe_quantize_rows_e4m3 does (the activation row from its fp32 value);
+ * hy3moe_quantize_rows_e4m3 does (the activation row as stored: rounded to
+ * bf16);
  * the products run on fp8 MFMA with fp32 accumulation and are rescaled by row
  * scale * channel scale; expert outputs are stored as bf16 and combined in
  * fp32 as in hy3moe_forward.  d and d_ff must be multiples of 128 here

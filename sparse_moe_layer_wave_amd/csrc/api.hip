@@ -76,7 +76,7 @@ Layout make_layout(int T, int d, int E, int k, int F, int dtype, bool shared = f
     L.row_of = take(Tk * sizeof(int32_t));
     L.tok_of = take(R * sizeof(int32_t));
     if (dtype == HY3MOE_WEIGHTS_FP8_E4M3) {
-        L.h = take(Tk * F * sizeof(float));            // fp32 SwiGLU activations
+        L.h = take(Tk * F * sizeof(uint16_t));         // bf16 SwiGLU activations
         L.hq = take(Tk * F);                           // their e4m3 codes
         L.hs = take(Tk * sizeof(float));               // per-row scale
         // per-row max |h|: [Tk] bit patterns (weight-streaming gate_up, atomics)
@@ -358,7 +358,7 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
     int32_t* tile_off = reinterpret_cast<int32_t*>(ws + L.tile_off);
     int32_t* row_of = reinterpret_cast<int32_t*>(ws + L.row_of);
     int32_t* tok_of = reinterpret_cast<int32_t*>(ws + L.tok_of);
-    float* h32 = reinterpret_cast<float*>(ws + L.h);
+    uint16_t* h16 = reinterpret_cast<uint16_t*>(ws + L.h);
     uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
     float* hs = reinterpret_cast<float*>(ws + L.hs);
     uint32_t* amax = reinterpret_cast<uint32_t*>(ws + L.amax);
@@ -394,16 +394,16 @@ int forward_fp8(const uint16_t* x, const float* W_gate, const uint8_t* Wq_gu, co
     if (e == hipSuccess) {
         if (decode)
             e = hy3::launch_gate_up_decode_fp8(xq, xs, tok_of, Wq_gu, s_gu, offsets, tile_off, max_slices,
-                                               h32, amax, E, d, d_ff, rg, block, s);
+                                               h16, amax, E, d, d_ff, rg, block, s);
         else if (block)
             e = hy3::launch_gate_up_fp8_block(xq, hs, tok_of, Wq_gu, s_gu, offsets, tile_off,
-                                              L.max_mtiles, h32, hmax, static_cast<int>(Tk), sched, E, d, d_ff, s);
+                                              L.max_mtiles, h16, hmax, static_cast<int>(Tk), sched, E, d, d_ff, s);
         else
             e = hy3::launch_gate_up_fp8(xq, hs, tok_of, Wq_gu, s_gu, offsets, tile_off, L.max_mtiles,
-                                        h32, hmax, static_cast<int>(Tk), sched, E, d, d_ff, s);
+                                        h16, hmax, static_cast<int>(Tk), sched, E, d, d_ff, s);
     }
     if (e == hipSuccess)
-        e = hy3::launch_quant_rows_f32(h32, decode ? amax : nullptr, decode ? nullptr : hmax, nblk,
+        e = hy3::launch_quant_rows_h(h16, decode ? amax : nullptr, decode ? nullptr : hmax, nblk,
                                        static_cast<int>(Tk), d_ff, hq, hs, s);
     if (e == hipSuccess) e = mark(ev, 3, s);
     if (e == hipSuccess) {

@@ -94,18 +94,18 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_bf16(const uint16_t* _
     }
 }
 
-// h rows (fp32) with their max |h| already reduced into amax (bit patterns),
-// or (amax_bits NULL) given as nblk partial maxima per row, hmax[blk * rows +
-// row]: the same quantiser as above, one wave per row (kQThreads / 64 rows
-// per workgroup); a lane takes 4 values per step of 256 columns and keeps up
-// to 8 steps' loads in flight.
+// h rows (bf16) with their max |h| already reduced into amax (bit patterns
+// of the float), or (amax_bits NULL) given as nblk partial maxima per row,
+// hmax[blk * rows + row]: the same quantiser as above, one wave per row
+// (kQThreads / 64 rows per workgroup); a lane takes 8 values per step of 512
+// columns and keeps up to 8 steps' loads in flight.
 constexpr int kRowsPerWg = kQThreads / 64;
 
-__global__ __launch_bounds__(kQThreads) void k_quant_rows_f32(const float* __restrict__ h,
-                                                             const uint32_t* __restrict__ amax_bits,
-                                                             const float* __restrict__ hmax, int nblk,
-                                                             int rows, int cols, uint8_t* __restrict__ q,
-                                                             float* __restrict__ s) {
+__global__ __launch_bounds__(kQThreads) void k_quant_rows_h(const uint16_t* __restrict__ h,
+                                                           const uint32_t* __restrict__ amax_bits,
+                                                           const float* __restrict__ hmax, int nblk,
+                                                           int rows, int cols, uint8_t* __restrict__ q,
+                                                           float* __restrict__ s) {
     const size_t row = static_cast<size_t>(blockIdx.x) * kRowsPerWg + (threadIdx.x >> 6);
     if (row >= static_cast<size_t>(rows)) return;
     const int lane = threadIdx.x & 63;
@@ -120,23 +120,20 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_f32(const float* __res
         amax = m;
     }
     const float r = amax > 0.f ? 448.0f / amax : 0.f;
-    const float* hr = h + row * cols;
+    const uint16_t* hr = h + row * cols;
     uint8_t* qr = q + row * cols;
-    for (int base = 0; base < cols; base += 8 * 256) {
-        float4 v[8];
+    for (int base = 0; base < cols; base += 8 * 512) {
+        uint4 v[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int c = base + (i * 64 + lane) * 4;
-            v[i] = c < cols ? *reinterpret_cast<const float4*>(hr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int c = base + (i * 64 + lane) * 8;
+            v[i] = c < cols ? *reinterpret_cast<const uint4*>(hr + c) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int c = base + (i * 64 + lane) * 4;
+            const int c = base + (i * 64 + lane) * 8;
             if (c < cols)
-                *reinterpret_cast<uint32_t*>(qr + c) = static_cast<uint32_t>(f32_to_e4m3(v[i].x * r)) |
-                                                       (static_cast<uint32_t>(f32_to_e4m3(v[i].y * r)) << 8) |
-                                                       (static_cast<uint32_t>(f32_to_e4m3(v[i].z * r)) << 16) |
-                                                       (static_cast<uint32_t>(f32_to_e4m3(v[i].w * r)) << 24);
+                *reinterpret_cast<uint2*>(qr + c) = make_uint2(quant_pair2(v[i].x, v[i].y, r), quant_pair2(v[i].z, v[i].w, r));
         }
     }
     if (lane == 0) s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
@@ -144,11 +141,11 @@ __global__ __launch_bounds__(kQThreads) void k_quant_rows_f32(const float* __res
 
 }  // namespace
 
-hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, const float* hmax, int nblk,
-                                 int rows, int cols, uint8_t* q, float* s, hipStream_t st) {
+hipError_t launch_quant_rows_h(const uint16_t* h, const uint32_t* amax_bits, const float* hmax, int nblk,
+                               int rows, int cols, uint8_t* q, float* s, hipStream_t st) {
     if (rows == 0) return hipSuccess;
     const unsigned wgs = static_cast<unsigned>((static_cast<long long>(rows) + kRowsPerWg - 1) / kRowsPerWg);
-    hipLaunchKernelGGL(k_quant_rows_f32, dim3(wgs), dim3(kQThreads), 0, st, h, amax_bits, hmax, nblk, rows, cols,
+    hipLaunchKernelGGL(k_quant_rows_h, dim3(wgs), dim3(kQThreads), 0, st, h, amax_bits, hmax, nblk, rows, cols,
                        q, s);
     return hipGetLastError();
 }

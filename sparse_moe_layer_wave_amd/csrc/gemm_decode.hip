@@ -23,9 +23,9 @@
 //          SiLU on the gate branch).  bf16: h[r, c] = bf16(SiLU(g) * u).
 //          e4m3: g and u are rescaled by the token's activation scale and the
 //          channel's weight scale (Q7.4: one scale per output channel), h is
-//          stored as fp32 and the row's max |h| folded into amax[r] (integer
-//          atomic max on the bit pattern of |h|) for the row quantiser that
-//          follows.
+//          stored as bf16 and the row's max |bf16(h)| folded into amax[r]
+//          (integer atomic max on the bit pattern of the float) for the row
+//          quantiser that follows.
 // down:    wave w of block (e, n0) owns W_down rows n0+32w..+32 and writes
 //          y[r, n] = bf16(h[r] . W_down[e][n]) (e4m3: rescaled by the row's
 //          and the channel's scales first).
@@ -73,10 +73,9 @@ struct DecodeArgs {
     const uint8_t* W_last;              // non-NULL: weights of expert E - 1 (shared)
     const int32_t* offsets;
     const int32_t* slice_off;           // [E+1] offsets in 16-row slices (one workgroup column each)
-    uint16_t* C;                        // bf16 out: gate_up h (bf16 mode) or y [rows, N]
+    uint16_t* C;                        // bf16 out: gate_up h or down y [rows, N]
     const float* a_scale;               // e4m3: per token (gate_up) or per row (down)
     const float* w_scale;               // e4m3: [E, 2N] (gate_up) or [E, N] (down)
-    float* h32;                         // e4m3 gate_up: h [rows, N] fp32
     uint32_t* amax;                     // e4m3 gate_up: [rows] bits of max |h|
     int K, N;                           // K in elements
     int E;                              // experts, the shared one included
@@ -310,10 +309,10 @@ __global__ __launch_bounds__(256, decode_min_waves(MODE, RG)) void k_decode_gemm
                         }
                     } else if constexpr (MODE == GU_FP8 || MODE == GU_FP8B) {
                         const float sx = g.a_scale[g.tok_of[crow]];
-                        const float hv = silu_mul(acc0[q][i] * sx * w0, acc1[q][i] * sx * w1);
-                        if (vr) g.h32[crow * N + col0 + r16] = hv;
+                        const uint16_t hv = f32_to_bf16(silu_mul(acc0[q][i] * sx * w0, acc1[q][i] * sx * w1));
+                        if (vr) g.C[crow * N + col0 + r16] = hv;
                         // row max over the 16 lanes that share this row
-                        float m = fabsf(hv);
+                        float m = fabsf(bf16_to_f32(hv));
 #pragma unroll
                         for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
                         if (vr && r16 == 0) atomicMax(&g.amax[crow], __float_as_uint(m));
@@ -376,7 +375,7 @@ hipError_t launch_gate_up_decode(const uint16_t* x, const int32_t* tok_of, const
                                  int F, int rg, hipStream_t s) {
     DecodeArgs g{reinterpret_cast<const uint8_t*>(x), tok_of, reinterpret_cast<const uint8_t*>(W_gu),
                  reinterpret_cast<const uint8_t*>(W_last), offsets, slice_off, h, nullptr, nullptr,
-                 nullptr, nullptr, d, F, E};
+                 nullptr, d, F, E};
     if (max_slices == 0) return hipSuccess;
     const dim3 grid(max_slices, F / (64 * kSubsBf16));
     if (rg == 2) hipLaunchKernelGGL((k_decode_gemm<GU_BF16, kSubsBf16, 2>), grid, dim3(256), 0, s, g);
@@ -389,7 +388,7 @@ hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uin
                               uint16_t* y, int E, int d, int F, int rg, hipStream_t s) {
     DecodeArgs g{reinterpret_cast<const uint8_t*>(h), nullptr, reinterpret_cast<const uint8_t*>(W_dn),
                  reinterpret_cast<const uint8_t*>(W_last), offsets, slice_off, y, nullptr, nullptr,
-                 nullptr, nullptr, F, d, E};
+                 nullptr, F, d, E};
     if (max_slices == 0) return hipSuccess;
     if (d % (128 * kSubsBf16Down) == 0) {
         const dim3 grid(max_slices, d / (128 * kSubsBf16Down));
@@ -405,10 +404,10 @@ hipError_t launch_down_decode(const uint16_t* h, const uint16_t* W_dn, const uin
 
 hipError_t launch_gate_up_decode_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                                      const uint8_t* Wq, const float* ws, const int32_t* offsets,
-                                     const int32_t* slice_off, int max_slices, float* h32,
+                                     const int32_t* slice_off, int max_slices, uint16_t* h,
                                      uint32_t* amax, int E, int d, int F, int rg, bool block,
                                      hipStream_t s) {
-    DecodeArgs g{xq, tok_of, Wq, nullptr, offsets, slice_off, nullptr, xs, ws, h32, amax, d, F, E};
+    DecodeArgs g{xq, tok_of, Wq, nullptr, offsets, slice_off, h, xs, ws, amax, d, F, E};
     if (max_slices == 0) return hipSuccess;
     const dim3 grid(max_slices, F / (64 * kSubsFp8));
     if (block) {
@@ -425,7 +424,7 @@ hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint
                                   const float* ws, const int32_t* offsets, const int32_t* slice_off,
                                   int max_slices, uint16_t* y, int E, int d, int F, int rg, bool block,
                                   hipStream_t s) {
-    DecodeArgs g{hq, nullptr, Wq, nullptr, offsets, slice_off, y, hs, ws, nullptr, nullptr, F, d, E};
+    DecodeArgs g{hq, nullptr, Wq, nullptr, offsets, slice_off, y, hs, ws, nullptr, F, d, E};
     if (max_slices == 0) return hipSuccess;
 #define HY3_DN_FP8(SUBS)                                                                                   \
     do {                                                                                                   \

@@ -7,10 +7,10 @@
 //            architecture teardown", section 2.3: the fused gate_up
 //            projection, gate rows first).  bf16: h stored as bf16.  e4m3:
 //            the two products are rescaled by the token's activation scale
-//            and the weights' scales, h is stored as fp32, and each tile
-//            stores its rows' max |h| over each 128-column block it covers
-//            into hmax[block][r], for the per-row quantisation of h that
-//            follows (which takes the max over the blocks);
+//            and the weights' scales, h is stored as bf16, and each tile
+//            stores its rows' max |bf16(h)| over each 128-column block it
+//            covers into hmax[block][r], for the per-row quantisation of the
+//            bf16 h that follows (which takes the max over the blocks);
 //   down:    y[r, n] = h[r] . Wd[e][n] (e4m3: rescaled by the row's and the
 //            weights' scales), stored as bf16.
 //
@@ -89,10 +89,9 @@ struct Args {
     const uint8_t* W_last;                         // non-NULL: weights of expert E - 1 (shared)
     const int32_t* offsets;                        // [E+1] row offsets
     const int32_t* tile_off;                       // [E+1] offsets in 128-row blocks
-    uint16_t* C;                                   // bf16 out: gate_up h (bf16 mode) or y [rows, N]
+    uint16_t* C;                                   // bf16 out: gate_up h or down y [rows, N]
     const float* a_scale;                          // e4m3: activation scale per row (gate_up: its token's)
     const float* w_scale;                          // per channel: [E, 2N] or [E, N]; block: [E, rows_w/128, K/128]
-    float* h32;                                    // e4m3 gate_up: h [rows, N] fp32
     float* hmax;                                   // e4m3 gate_up: [N / 128][rows] max |h| per 128-column block
     int rows;                                      // e4m3 gate_up: rows of h (the stride of hmax)
     int* sched;                                    // [kXcds] unit counters, zero at launch
@@ -458,7 +457,7 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
     // and 128-column block of the tile and stored (no atomics: each block of
     // a row belongs to one tile).
     constexpr int OCOLS = GATE_UP ? 32 : 64;           // output columns per wave
-    constexpr int OESZ = (GATE_UP && FP8) ? 4 : 2;     // bytes per output element
+    constexpr int OESZ = 2;                            // bytes per output element (bf16)
     constexpr int OPITCH = OCOLS * OESZ + 16;
     static_assert(kWaves * 128 * OPITCH + RA * 4 + RA * WN * 4 <= kClaimOff, "LDS");
     uint8_t* ow = lds + wave * (128 * OPITCH);
@@ -506,8 +505,8 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
                     if (j & 1) put_pair(rl - 1, 32 * nb + l32, acc[mb][nb][j - 1], acc[mb][nb][j]);
             } else if constexpr (GATE_UP) {
                 const float sr = srow[a0 + rl];
-                *reinterpret_cast<float*>(orow + l32 * 4) =
-                    silu_mul(acc[mb][0][j] * cs[0] * sr, acc[mb][1][j] * cs[1] * sr);
+                *reinterpret_cast<uint16_t*>(orow + l32 * 2) =
+                    f32_to_bf16(silu_mul(acc[mb][0][j] * cs[0] * sr, acc[mb][1][j] * cs[1] * sr));
             } else {
                 const float sr = srow[a0 + rl];
 #pragma unroll
@@ -517,17 +516,20 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
         }
     }
     if constexpr (GATE_UP && FP8) {
-        // each row's max |h| over the wave's 32 columns, read back from the
-        // staged block (a wave's LDS accesses complete in order): two rows
-        // per lane, instead of a 5-step cross-lane reduction per row
+        // each row's max |h| over the wave's 32 bf16 columns, read back from
+        // the staged block (a wave's LDS accesses complete in order): two
+        // rows per lane, instead of a 5-step cross-lane reduction per row
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int rl = lane + 64 * q;
             float m = 0.f;
 #pragma unroll
-            for (int c = 0; c < 32; c += 4) {
-                const float4 v = *reinterpret_cast<const float4*>(ow + rl * OPITCH + c * 4);
-                m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            for (int c = 0; c < 32; c += 8) {
+                const uint4 v = *reinterpret_cast<const uint4*>(ow + rl * OPITCH + c * 2);
+                const uint32_t p[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    m = fmaxf(m, fmaxf(fabsf(__uint_as_float(p[i] << 16)), fabsf(__uint_as_float(p[i] & 0xffff0000u))));
             }
             hm[(a0 + rl) * WN + wn] = cw < N ? m : 0.f;
         }
@@ -560,8 +562,7 @@ __device__ __forceinline__ void tile(const Args& g, uint8_t* lds, const Unit& u,
         const i32x4_t v = *reinterpret_cast<const i32x4_t*>(ow + rl * OPITCH + cc * 16);
         if (r < u.rows && c < N) {
             const size_t grow = static_cast<size_t>(u.row0 + r);
-            if constexpr (GATE_UP && FP8) *reinterpret_cast<i32x4_t*>(g.h32 + grow * N + c) = v;
-            else *reinterpret_cast<i32x4_t*>(g.C + grow * N + c) = v;
+            *reinterpret_cast<i32x4_t*>(g.C + grow * N + c) = v;
         }
     }
     if (claim && tid == 0) *reinterpret_cast<int*>(lds + kClaimOff) = claimed;
@@ -654,7 +655,7 @@ hipError_t launch_gate_up_grouped(const uint16_t* x, const int32_t* tok_of, cons
                                   const int32_t* tile_off, int max_blocks, uint16_t* h, int* sched, int E,
                                   int d, int F, hipStream_t s) {
     Args g{reinterpret_cast<const uint8_t*>(x), tok_of, reinterpret_cast<const uint8_t*>(W_gu),
-           reinterpret_cast<const uint8_t*>(W_last), offsets, tile_off, h, nullptr, nullptr, nullptr,
+           reinterpret_cast<const uint8_t*>(W_last), offsets, tile_off, h, nullptr, nullptr,
            nullptr, 0, sched, d, F, E, 0};
     return launch<GU_BF16>(g, max_blocks, s);
 }
@@ -663,38 +664,38 @@ hipError_t launch_down_grouped(const uint16_t* h, const uint16_t* W_dn, const ui
                                const int32_t* offsets, const int32_t* tile_off, int max_blocks,
                                uint16_t* y, int* sched, int E, int d, int F, hipStream_t s) {
     Args g{reinterpret_cast<const uint8_t*>(h), nullptr, reinterpret_cast<const uint8_t*>(W_dn),
-           reinterpret_cast<const uint8_t*>(W_last), offsets, tile_off, y, nullptr, nullptr, nullptr,
+           reinterpret_cast<const uint8_t*>(W_last), offsets, tile_off, y, nullptr, nullptr,
            nullptr, 0, sched, F, d, E, 0};
     return launch<DN_BF16>(g, max_blocks, s);
 }
 
 hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* rs, const int32_t* tok_of,
                               const uint8_t* Wq, const float* ws, const int32_t* offsets,
-                              const int32_t* tile_off, int max_blocks, float* h32, float* hmax,
+                              const int32_t* tile_off, int max_blocks, uint16_t* h, float* hmax,
                               int rows, int* sched, int E, int d, int F, hipStream_t s) {
-    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, rs, ws, h32, hmax, rows, sched, d, F, E, 0};
+    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, h, rs, ws, hmax, rows, sched, d, F, E, 0};
     return launch<GU_FP8>(g, max_blocks, s);
 }
 
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq, const float* ws,
                            const int32_t* offsets, const int32_t* tile_off, int max_blocks,
                            uint16_t* y, int* sched, int E, int d, int F, hipStream_t s) {
-    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, ws, nullptr, nullptr, 0, sched, F, d, E, 0};
+    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, ws, nullptr, 0, sched, F, d, E, 0};
     return launch<DN_FP8>(g, max_blocks, s);
 }
 
 hipError_t launch_gate_up_fp8_block(const uint8_t* xq, const float* rs, const int32_t* tok_of,
                                     const uint8_t* Wq, const float* sb, const int32_t* offsets,
-                                    const int32_t* tile_off, int max_mtiles, float* h32,
+                                    const int32_t* tile_off, int max_mtiles, uint16_t* h,
                                     float* hmax, int rows, int* sched, int E, int d, int F, hipStream_t s) {
-    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, nullptr, rs, sb, h32, hmax, rows, sched, d, F, E, 0};
+    Args g{xq, tok_of, Wq, nullptr, offsets, tile_off, h, rs, sb, hmax, rows, sched, d, F, E, 0};
     return launch<GU_BLK>(g, max_mtiles, s);
 }
 
 hipError_t launch_down_fp8_block(const uint8_t* hq, const float* hs, const uint8_t* Wq,
                                  const float* sb, const int32_t* offsets, const int32_t* tile_off,
                                  int max_mtiles, uint16_t* y, int* sched, int E, int d, int F, hipStream_t s) {
-    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, sb, nullptr, nullptr, 0, sched, F, d, E, 0};
+    Args g{hq, nullptr, Wq, nullptr, offsets, tile_off, y, hs, sb, nullptr, 0, sched, F, d, E, 0};
     return launch<DN_BLK>(g, max_mtiles, s);
 }
 

@@ -193,15 +193,16 @@ hipError_t launch_block_counts(const int32_t* idx, int T, int E, int k, int nb,
 hipError_t launch_quant_rows(const uint16_t* x, int rows, int cols, uint8_t* q, float* s,
                              hipStream_t st, const int32_t* row_of = nullptr, int k = 0,
                              float* rs = nullptr);
-// h rows' max |h|: amax_bits [rows] (bit patterns; the weight-streaming
-// gate_up folds them in with atomics), or, with amax_bits NULL, the max over
-// the nblk partial maxima hmax[blk * rows + row] (the grouped gate_up's).
-hipError_t launch_quant_rows_f32(const float* h, const uint32_t* amax_bits, const float* hmax, int nblk,
-                                 int rows, int cols, uint8_t* q, float* s, hipStream_t st);
+// bf16 h rows, their max |h|: amax_bits [rows] (bit patterns of the float;
+// the weight-streaming gate_up folds them in with atomics), or, with
+// amax_bits NULL, the max over the nblk partial maxima hmax[blk * rows + row]
+// (the grouped gate_up's).
+hipError_t launch_quant_rows_h(const uint16_t* h, const uint32_t* amax_bits, const float* hmax, int nblk,
+                               int rows, int cols, uint8_t* q, float* s, hipStream_t st);
 // rs: the tokens' activation scales per dispatch row (launch_quant_rows' rs)
 hipError_t launch_gate_up_fp8(const uint8_t* xq, const float* rs, const int32_t* tok_of,
                               const uint8_t* Wq, const float* ws, const int32_t* offsets,
-                              const int32_t* tile_off, int max_mtiles, float* h32, float* hmax,
+                              const int32_t* tile_off, int max_mtiles, uint16_t* h, float* hmax,
                               int rows, int* sched, int E, int d, int F, hipStream_t s);
 hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq, const float* ws,
                            const int32_t* offsets, const int32_t* tile_off, int max_mtiles,
@@ -212,7 +213,7 @@ hipError_t launch_down_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq
 // output channel; K <= 16384.
 hipError_t launch_gate_up_decode_fp8(const uint8_t* xq, const float* xs, const int32_t* tok_of,
                                      const uint8_t* Wq, const float* ws, const int32_t* offsets,
-                                     const int32_t* slice_off, int max_slices, float* h32,
+                                     const int32_t* slice_off, int max_slices, uint16_t* h,
                                      uint32_t* amax, int E, int d, int F, int rg, bool block,
                                      hipStream_t s);
 hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint8_t* Wq,
@@ -224,7 +225,7 @@ hipError_t launch_down_decode_fp8(const uint8_t* hq, const float* hs, const uint
 // scale each, sb [E, rows/128, K/128]); K <= 16384, tile_off in 128-row blocks
 hipError_t launch_gate_up_fp8_block(const uint8_t* xq, const float* rs, const int32_t* tok_of,
                                     const uint8_t* Wq, const float* sb, const int32_t* offsets,
-                                    const int32_t* tile_off, int max_mtiles, float* h32,
+                                    const int32_t* tile_off, int max_mtiles, uint16_t* h,
                                     float* hmax, int rows, int* sched, int E, int d, int F, hipStream_t s);
 hipError_t launch_down_fp8_block(const uint8_t* hq, const float* hs, const uint8_t* Wq,
                                  const float* sb, const int32_t* offsets, const int32_t* tile_off,

@@ -99,8 +99,10 @@ class LazyExperts:
 #   h (bf16 experts):  flippable if within ETA_H steps of a bf16 boundary, or
 #       within ETA_HA * max|h of its row| (the float32 error of a small h
 #       made of cancelling terms).  A flip moves y_c by |Wd[c, f]| * step.
-#   h (e4m3):  h is rounded to bf16, and v = bf16(h) * r is quantised.  v
-#       is flippable where h's bf16 rounding may flip (as above) and v lies
+#   h (e4m3):  h is rounded to bf16, and v = bf16(h) * r is quantised.  h's
+#       bf16 rounding may flip within ETA_QR * |h| or ETA_QA * max|h of its
+#       row| of a bf16 boundary (the e4m3 path's float32 margins below, now
+#       on h).  v is flippable where h's bf16 rounding may flip and v lies
 #       within that bf16 step (REL_BF16 * |v|) of an e4m3 boundary; every v
 #       of a row is, where an element next to the row's maximum may flip (the
 #       row's scale moves by up to REL_BF16, and the dequantised row with it:
@@ -124,6 +126,7 @@ ETA_Q = 2.0 ** -10
 ETA_QA = 2.0 ** -16
 ETA_Y = 2.0 ** -20
 REL_BF16 = 2.0 ** -7          # a bf16 step relative to the value, at most
+ETA_QR = ETA_Q * 2.0 ** -4     # ETA_Q steps of e4m3 relative to the value, at least
 
 
 def bf16_boundary(v):
@@ -183,10 +186,15 @@ def flip_allowance(det, W_dn_of, fp8):
             # (REL_BF16 of v); one next to the row's maximum moves the row's
             # scale by as much, hence every v of the row and the dequantised
             # row itself.
+            # The e4m3 path's fp32 h carries the error the ETA_Q / ETA_QA
+            # margins allow for v (at least 2^-14 of |v|, or 2^-16 of the
+            # row's largest): the block-scale accumulation rescales its sums
+            # once per k-block.  The same margins, on h, decide where h's
+            # bf16 rounding may flip.
             h = det.h[ti, j]
             hd, hstep = bf16_boundary(h)
             hmax = np.max(np.abs(h), axis=1, keepdims=True)
-            hflag = (hd <= ETA_H * hstep) | (hd <= ETA_HA * hmax)
+            hflag = (hd <= ETA_QR * np.abs(h)) | (hd <= ETA_QA * hmax)
             rflag = np.any(hflag & (np.abs(h) >= hmax * (1.0 - 2.0 ** -6)), axis=1, keepdims=True)
             v = det.scaled[ti, j].astype(np.float64)
             dist, step = e4m3_boundary(v)
