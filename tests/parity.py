@@ -100,15 +100,14 @@ class LazyExperts:
 #       within ETA_HA * max|h of its row| (the float32 error of a small h
 #       made of cancelling terms).  A flip moves y_c by |Wd[c, f]| * step.
 #   h (e4m3):  h is rounded to bf16, and v = bf16(h) * r is quantised.  h's
-#       bf16 rounding may flip within ETA_QR * |h| or ETA_QA * max|h of its
-#       row| of a bf16 boundary (the e4m3 path's float32 margins below, now
-#       on h).  v is flippable where h's bf16 rounding may flip and v lies
-#       within that bf16 step (REL_BF16 * |v|) of an e4m3 boundary; every v
-#       of a row is, where an element next to the row's maximum may flip (the
-#       row's scale moves by up to REL_BF16, and the dequantised row with it:
-#       REL_BF16 * sum_f |Wd[c, f] * a_deq_f|); and, for the float32
-#       arithmetic, within ETA_Q steps or ETA_QA * 448.  A code flip moves
-#       y_c by |Wd[c, f]| * step * s_a.
+#       bf16 rounding may flip within ETA_HQ * max|h of its row| of a bf16
+#       boundary (the e4m3 path's error is absolute at its row's scale).  v
+#       is flippable where h's bf16 rounding may flip and v lies within that
+#       bf16 step (REL_BF16 * |v|) of an e4m3 boundary; every v of a row is,
+#       where an element next to the row's maximum may flip (the row's scale
+#       moves by up to REL_BF16, and y with it: REL_BF16 * |y_c|); and, for
+#       the float32 arithmetic, within ETA_Q steps or ETA_QA * 448.  A code
+#       flip moves y_c by |Wd[c, f]| * step * s_a.
 #   y:  the GPU's float32 y may be off the oracle's pre-rounding y by D_c =
 #       the h flips above + ETA_Y * sum_f |Wd[c, f] * h_f| (float32 sums of F
 #       products and the scale multiplications); y flips if it lies within D_c
@@ -126,7 +125,7 @@ ETA_Q = 2.0 ** -10
 ETA_QA = 2.0 ** -16
 ETA_Y = 2.0 ** -20
 REL_BF16 = 2.0 ** -7          # a bf16 step relative to the value, at most
-ETA_QR = ETA_Q * 2.0 ** -4     # ETA_Q steps of e4m3 relative to the value, at least
+ETA_HQ = ETA_Q * 32.0 / 448.0  # ETA_Q e4m3 steps at the row's largest v (448, step 32), relative to it
 
 
 def bf16_boundary(v):
@@ -186,22 +185,26 @@ def flip_allowance(det, W_dn_of, fp8):
             # (REL_BF16 of v); one next to the row's maximum moves the row's
             # scale by as much, hence every v of the row and the dequantised
             # row itself.
-            # The e4m3 path's fp32 h carries the error the ETA_Q / ETA_QA
-            # margins allow for v (at least 2^-14 of |v|, or 2^-16 of the
-            # row's largest): the block-scale accumulation rescales its sums
-            # once per k-block.  The same margins, on h, decide where h's
-            # bf16 rounding may flip.
+            # The e4m3 path's h carries an absolute error at the scale of its
+            # row (fp8 MFMA sums): up to 2^-14.5 of the row's largest |h| was
+            # measured.  ETA_HQ of the row's largest |h| -- the margin ETA_Q
+            # gives v at the row's largest value (448, e4m3 step 32) --
+            # decides where h's bf16 rounding may flip.
             h = det.h[ti, j]
             hd, hstep = bf16_boundary(h)
             hmax = np.max(np.abs(h), axis=1, keepdims=True)
-            hflag = (hd <= ETA_QR * np.abs(h)) | (hd <= ETA_QA * hmax)
+            hflag = hd <= ETA_HQ * hmax
             rflag = np.any(hflag & (np.abs(h) >= hmax * (1.0 - 2.0 ** -6)), axis=1, keepdims=True)
             v = det.scaled[ti, j].astype(np.float64)
             dist, step = e4m3_boundary(v)
             moved = (hflag.astype(np.float64) + rflag) * REL_BF16 * np.abs(v)
             flag = (dist <= ETA_Q * step) | (dist <= ETA_QA * 448.0) | (dist <= moved + ETA_Q * step)
             ad = np.abs(det.a_deq[ti, j]) @ Wd.T
-            C = (flag * step * det.s_a[ti, j].astype(np.float64)[:, None]) @ Wd.T + rflag * REL_BF16 * ad
+            # a row scale that moves by a factor (1 + delta) multiplies every
+            # dequantised value of the row, so y moves by delta * y (code
+            # flips are counted separately)
+            C = (flag * step * det.s_a[ti, j].astype(np.float64)[:, None]) @ Wd.T + \
+                rflag * REL_BF16 * np.abs(det.y[ti, j])
             D = C + ETA_Y * ad
         else:
             h = det.h[ti, j]
