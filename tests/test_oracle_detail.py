@@ -81,6 +81,9 @@ def test_fp8_detail_recombines_and_matches_the_closed_form():
         det = oracle.forward_fp8_detail(np.arange(T), L["x"], r, L["Wq_gu"], L["s_gu"], L["Wq_dn"], L["s_dn"])
         np.testing.assert_allclose(_recombine(det), out, rtol=0, atol=1e-13 * np.abs(out).max())
         assert np.max(np.abs(_recombine(det) - expect)) <= 1e-12 * np.abs(expect).max()
+        # h is the activation before its bf16 rounding: the closed form's, slot j being expert r.idx[t, j]
+        a = L["a"][np.arange(T)[:, None], r.idx]
+        np.testing.assert_allclose(det.h, a, rtol=1e-12, atol=0)
         # the dequantised activations are torch's e4m3 cast of the scaled values times the row scale
         _, vals = _torch_e4m3(det.scaled)
         assert np.array_equal(det.a_deq, vals * det.s_a.astype(np.float64)[..., None])

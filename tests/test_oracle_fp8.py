@@ -225,6 +225,7 @@ def _one_hot_fp8_layer(seed, x_exact):
     s_gu = np.concatenate([np.ldexp(1.0, pg.astype(int)), np.ldexp(1.0, pu.astype(int))], axis=1).astype(np.float32)
     s_dn = np.ldexp(1.0, pd.astype(int)).astype(np.float32)
     layer = dict(x=x, Wg=Wg, Wq_gu=Wq_gu, s_gu=s_gu, Wq_dn=Wq_dn, s_dn=s_dn, k=E)
+    # the closed form's activation before its bf16 rounding, [T, E, F] by expert
     # ---- the closed form
     from scipy.special import expit
     x64 = codecs.bf16_bits_to_f64(x)
@@ -234,7 +235,8 @@ def _one_hot_fp8_layer(seed, x_exact):
     wd = _torch_e4m3_value(cd) * s_dn
     g = xd[:, ig] * wg[None]                                 # [T, E, F], exact
     u = xd[:, iu] * wu[None]
-    a16 = _bf16_nearest(g * expit(g) * u).astype(np.float32)          # exact in float32
+    layer["a"] = g * expit(g) * u
+    a16 = _bf16_nearest(layer["a"]).astype(np.float32)                # exact in float32
     ad = _torch_quant_rows(a16.reshape(T * E, F)).reshape(T, E, F)
     y = np.take_along_axis(ad, np.broadcast_to(fd[None], (T, E, d)), axis=2) * wd[None]   # exact
     s = expit(x64 @ Wg.astype(np.float64).T).astype(np.float32).astype(np.float64)
