@@ -110,8 +110,11 @@ class LazyExperts:
 #       flip moves y_c by |Wd[c, f]| * step * s_a.
 #   y:  the GPU's float32 y may be off the oracle's pre-rounding y by D_c =
 #       the h flips above + ETA_Y * sum_f |Wd[c, f] * h_f| (float32 sums of F
-#       products and the scale multiplications); y flips if it lies within D_c
-#       of a bf16 boundary, moving the element by w * step(y).
+#       products and the scale multiplications).  Where y lies within D_c of
+#       a bf16 boundary, the stored y may differ from the oracle's rounding by
+#       up to D_c plus one bf16 step (D_c can span several steps when several
+#       h values of the row may flip); elsewhere both round alike.  The
+#       element may move by the weighted sum of that over its slots.
 #
 # The ETA values are chosen from the GPU's float32 error with margin: the
 # gate and up sums over d terms carry about 2^-18 relative error, so h and v
@@ -165,14 +168,14 @@ def e4m3_boundary(v):
     return dist, np.maximum(hi - lo, lo - prev)
 
 
-def flip_allowance(det, W_dn_of, fp8):
-    """Per element of the detail's tokens [n, d]: how far the GPU's output may
-    move from the oracle's through predicted rounding-boundary flips.
-    W_dn_of(e) gives expert e's down matrix as float64 [d, F] (e = -1: the
-    shared expert)."""
-    n, S = det.expert.shape
+def slot_flip_terms(det, W_dn_of, fp8):
+    """For each expert of the detail: (ti, j, C, D) with the (token, slot)
+    pairs (ti, j) it serves, C [len(ti), d] the move of each expert output
+    element through e4m3 code flips and row-scale moves (zero for bf16
+    experts), and D [len(ti), d] how far the GPU's float32 y may lie from the
+    oracle's before its bf16 rounding.  W_dn_of(e) gives expert e's down
+    matrix as float64 [d, F] (e = -1: the shared expert)."""
     d = det.y.shape[2]
-    A = np.zeros((n, d))
     for e in np.unique(det.expert):
         ti, j = np.nonzero(det.expert == e)
         Wd = np.abs(W_dn_of(int(e)))                  # [d, F]
@@ -213,8 +216,27 @@ def flip_allowance(det, W_dn_of, fp8):
             C = np.zeros((len(ti), d))
             from oracle import codecs
             D = (flag * step) @ Wd.T + ETA_Y * (np.abs(codecs.round_to_bf16(h)) @ Wd.T)
-        ydist, ystep = bf16_boundary(det.y[ti, j])
-        np.add.at(A, ti, det.w[ti, j][:, None] * (C + ystep * (ydist <= D)))
+        yield ti, j, C, D
+
+
+def y_allowance(y, D):
+    """How far a stored bf16 expert output may lie from the oracle's rounding
+    of y when the GPU's float32 y lies within D of the oracle's y: nothing
+    where y is farther than D from a bf16 boundary (both round alike),
+    otherwise D plus one bf16 step at |y| + D (each rounding moves a value by
+    at most half a step)."""
+    ydist, _ = bf16_boundary(y)
+    _, step_hi = bf16_boundary(np.abs(y) + D)
+    return (ydist <= D) * (D + step_hi)
+
+
+def flip_allowance(det, W_dn_of, fp8):
+    """Per element of the detail's tokens [n, d]: how far the GPU's output may
+    move from the oracle's through predicted rounding-boundary flips: the
+    weighted sum over the token's slots of y_allowance."""
+    A = np.zeros((det.expert.shape[0], det.y.shape[2]))
+    for ti, j, C, D in slot_flip_terms(det, W_dn_of, fp8):
+        np.add.at(A, ti, det.w[ti, j][:, None] * y_allowance(det.y[ti, j], D))
     return A
 
 

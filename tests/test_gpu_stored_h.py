@@ -1,8 +1,12 @@
-"""The premise of the output check (parity.check_output_flips), on the GPU's
-own intermediate values: the SwiGLU activation h the layer stores in bf16
-lands on the other bf16 neighbour than the oracle's rounding only where the
-oracle's h lies within the check's stated distance of a bf16 rounding
-boundary.  h and the row map are read back from the caller's workspace; the
+"""The premises of the output check (parity.check_output_flips), on the
+GPU's own intermediate values:
+* the SwiGLU activation h the layer stores in bf16 lands on the other bf16
+  neighbour than the oracle's rounding only where the oracle's h lies within
+  the check's stated distance of a bf16 rounding boundary;
+* each stored expert output y differs from the oracle's bf16 rounding by no
+  more than the check's per-slot y_allowance: nothing where y lies farther
+  than D from a bf16 boundary, else D plus one bf16 step.
+h, y and the row map are read back from the caller's workspace; the
 workspace carving is mirrored here and must reproduce hy3moe_workspace_size,
 so a change of the library's layout fails these tests instead of misreading
 them."""
@@ -13,7 +17,7 @@ import torch
 
 import oracle
 from oracle import codecs
-from parity import ETA_H, ETA_HA, ETA_HQ, bf16_boundary
+from parity import ETA_H, ETA_HA, ETA_HQ, bf16_boundary, slot_flip_terms, y_allowance
 from sparse_moe_layer_wave_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -54,11 +58,29 @@ def _layout(T, d, E, k, F, fp8):
     return found[0]
 
 
-def _stored_h(ws, L, T, k, F):
+def _stored(ws, L, T, k, F, d):
+    """The stored h [T, k, F] and y [T, k, d] of each (token, slot), as float64."""
     R = T * k
+    row_of = ws[L["row_of"]:L["row_of"] + R * 4].cpu().numpy().view(np.int32).reshape(-1)
     h = ws[L["h"]:L["h"] + R * F * 2].cpu().numpy().view(np.uint16).reshape(R, F)
-    row_of = ws[L["row_of"]:L["row_of"] + R * 4].cpu().numpy().view(np.int32).reshape(T, k)
-    return codecs.bf16_bits_to_f64(h[row_of.reshape(-1)]).reshape(T, k, F)
+    y = ws[L["y"]:L["y"] + R * d * 2].cpu().numpy().view(np.uint16).reshape(R, d)
+    return (codecs.bf16_bits_to_f64(h[row_of]).reshape(T, k, F),
+            codecs.bf16_bits_to_f64(y[row_of]).reshape(T, k, d))
+
+
+def _check_y(gpu_y, det, W_dn_of, fp8):
+    """Each stored y element lies within the check's y_allowance of the
+    oracle's bf16 rounding."""
+    n_other = 0
+    for ti, j, C, D in slot_flip_terms(det, W_dn_of, fp8):
+        y = det.y[ti, j]
+        diff = np.abs(gpu_y[ti, j] - codecs.round_to_bf16(y))
+        allow = y_allowance(y, D)
+        bad = diff > allow * (1 + 1e-9)
+        assert not bad.any(), (f"{int(bad.sum())} stored y values beyond the per-slot allowance "
+                               f"(worst excess {float((diff - allow)[bad].max()):.3e})")
+        n_other += int((diff > 0).sum())
+    return n_other
 
 
 def _check(gpu_h, det_h, fp8):
@@ -94,8 +116,11 @@ def test_stored_h_bf16_grouped(gpu_lib):
                      None if inp["bias"] is None else inp["bias"].numpy())
     assert np.array_equal(idx.cpu().numpy(), r.idx)
     det = oracle.forward_detail(np.arange(T), xb, r, inputs.bits(inp["W_gu"]), inputs.bits(inp["W_dn"]))
-    n = _check(_stored_h(ws, L, T, k, F), det.h, fp8=False)
-    print("bf16: stored h on the other neighbour:", n)
+    gh, gy = _stored(ws, L, T, k, F, d)
+    n = _check(gh, det.h, fp8=False)
+    W_dn = inputs.bits(inp["W_dn"])
+    ny = _check_y(gy, det, lambda e: oracle.bf16_bits_to_f64(W_dn[e]), fp8=False)
+    print("bf16: stored h on the other neighbour:", n, "; y off the oracle's rounding:", ny)
 
 
 @pytest.mark.parametrize("case", ["per_channel_decode", "block128_grouped"])
@@ -121,7 +146,9 @@ def test_stored_h_e4m3(gpu_lib, case):
     r = oracle.route(xb, inp["W_gate"].numpy(), k, inp["scale"],
                      None if inp["bias"] is None else inp["bias"].numpy())
     assert np.array_equal(idx.cpu().numpy(), r.idx)
-    det = oracle.forward_fp8_detail(np.arange(T), xb, r, inputs.bits(inp["Wq_gu"]), inp["s_gu"].numpy(),
-                                    inputs.bits(inp["Wq_dn"]), inp["s_dn"].numpy())
-    n = _check(_stored_h(ws, L, T, k, F), det.h, fp8=True)
-    print(case, ": stored h on the other neighbour:", n)
+    qdn, sdn = inputs.bits(inp["Wq_dn"]), inp["s_dn"].numpy()
+    det = oracle.forward_fp8_detail(np.arange(T), xb, r, inputs.bits(inp["Wq_gu"]), inp["s_gu"].numpy(), qdn, sdn)
+    gh, gy = _stored(ws, L, T, k, F, d)
+    n = _check(gh, det.h, fp8=True)
+    ny = _check_y(gy, det, lambda e: oracle.dequant_e4m3(qdn[e], sdn[e]), fp8=True)
+    print(case, ": stored h on the other neighbour:", n, "; y off the oracle's rounding:", ny)
