@@ -168,6 +168,23 @@ def e4m3_boundary(v):
     return dist, np.maximum(hi - lo, lo - prev)
 
 
+def e4m3_flip_flags(h, scaled):
+    """For e4m3 activation rows h [n, F] (the oracle's, before their bf16
+    rounding) and the values the quantiser rounds, scaled [n, F]: (flag
+    [n, F], where the GPU's code may differ from the oracle's; rflag [n, 1],
+    where the GPU's row scale may differ; step [n, F], the e4m3 step beside
+    each value)."""
+    hd, _ = bf16_boundary(h)
+    hmax = np.max(np.abs(h), axis=1, keepdims=True)
+    hflag = hd <= ETA_HQ * hmax
+    rflag = np.any(hflag & (np.abs(h) >= hmax * (1.0 - 2.0 ** -6)), axis=1, keepdims=True)
+    v = np.asarray(scaled, dtype=np.float64)
+    dist, step = e4m3_boundary(v)
+    moved = (hflag.astype(np.float64) + rflag) * REL_BF16 * np.abs(v)
+    flag = (dist <= ETA_Q * step) | (dist <= ETA_QA * 448.0) | (dist <= moved + ETA_Q * step)
+    return flag, rflag, step
+
+
 def slot_flip_terms(det, W_dn_of, fp8):
     """For each expert of the detail: (ti, j, C, D) with the (token, slot)
     pairs (ti, j) it serves, C [len(ti), d] the move of each expert output
@@ -193,15 +210,7 @@ def slot_flip_terms(det, W_dn_of, fp8):
             # measured.  ETA_HQ of the row's largest |h| -- the margin ETA_Q
             # gives v at the row's largest value (448, e4m3 step 32) --
             # decides where h's bf16 rounding may flip.
-            h = det.h[ti, j]
-            hd, hstep = bf16_boundary(h)
-            hmax = np.max(np.abs(h), axis=1, keepdims=True)
-            hflag = hd <= ETA_HQ * hmax
-            rflag = np.any(hflag & (np.abs(h) >= hmax * (1.0 - 2.0 ** -6)), axis=1, keepdims=True)
-            v = det.scaled[ti, j].astype(np.float64)
-            dist, step = e4m3_boundary(v)
-            moved = (hflag.astype(np.float64) + rflag) * REL_BF16 * np.abs(v)
-            flag = (dist <= ETA_Q * step) | (dist <= ETA_QA * 448.0) | (dist <= moved + ETA_Q * step)
+            flag, rflag, step = e4m3_flip_flags(det.h[ti, j], det.scaled[ti, j])
             ad = np.abs(det.a_deq[ti, j]) @ Wd.T
             # a row scale that moves by a factor (1 + delta) multiplies every
             # dequantised value of the row, so y moves by delta * y (code

@@ -3,6 +3,9 @@ GPU's own intermediate values:
 * the SwiGLU activation h the layer stores in bf16 lands on the other bf16
   neighbour than the oracle's rounding only where the oracle's h lies within
   the check's stated distance of a bf16 rounding boundary;
+* with e4m3 experts, a stored activation code differs from the oracle's only
+  where the check lets it flip, and a row scale only where the check lets
+  the row's largest value flip;
 * each stored expert output y differs from the oracle's bf16 rounding by no
   more than the check's per-slot y_allowance: nothing where y lies farther
   than D from a bf16 boundary, else D plus one bf16 step.
@@ -17,7 +20,7 @@ import torch
 
 import oracle
 from oracle import codecs
-from parity import ETA_H, ETA_HA, ETA_HQ, bf16_boundary, slot_flip_terms, y_allowance
+from parity import ETA_H, ETA_HA, ETA_HQ, bf16_boundary, e4m3_flip_flags, slot_flip_terms, y_allowance
 from sparse_moe_layer_wave_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -81,6 +84,25 @@ def _check_y(gpu_y, det, W_dn_of, fp8):
                                f"(worst excess {float((diff - allow)[bad].max()):.3e})")
         n_other += int((diff > 0).sum())
     return n_other
+
+
+def _stored_codes(ws, L, T, k, F):
+    """The stored e4m3 codes [T, k, F] and row scales [T, k] of h."""
+    R = T * k
+    row_of = ws[L["row_of"]:L["row_of"] + R * 4].cpu().numpy().view(np.int32).reshape(-1)
+    q = ws[L["hq"]:L["hq"] + R * F].cpu().numpy().reshape(R, F)
+    s = ws[L["hs"]:L["hs"] + R * 4].cpu().numpy().view(np.float32)
+    return q[row_of].reshape(T, k, F), s[row_of].reshape(T, k)
+
+
+def _check_codes(gpu_q, gpu_s, det):
+    flag, rflag, _ = e4m3_flip_flags(det.h.reshape(-1, det.h.shape[2]), det.scaled.reshape(-1, det.h.shape[2]))
+    q_ref = codecs.f32_to_e4m3_bits(det.scaled)
+    other_q = (gpu_q != q_ref).reshape(flag.shape)
+    other_s = (gpu_s != det.s_a).reshape(-1, 1)
+    assert not (other_q & ~flag).any(), f"{int((other_q & ~flag).sum())} codes differ where no flip was allowed"
+    assert not (other_s & ~rflag).any(), f"{int((other_s & ~rflag).sum())} row scales differ where none may"
+    return int(other_q.sum()), int(other_s.sum())
 
 
 def _check(gpu_h, det_h, fp8):
@@ -150,5 +172,7 @@ def test_stored_h_e4m3(gpu_lib, case):
     det = oracle.forward_fp8_detail(np.arange(T), xb, r, inputs.bits(inp["Wq_gu"]), inp["s_gu"].numpy(), qdn, sdn)
     gh, gy = _stored(ws, L, T, k, F, d)
     n = _check(gh, det.h, fp8=True)
+    nq, ns = _check_codes(*_stored_codes(ws, L, T, k, F), det)
     ny = _check_y(gy, det, lambda e: oracle.dequant_e4m3(qdn[e], sdn[e]), fp8=True)
-    print(case, ": stored h on the other neighbour:", n, "; y off the oracle's rounding:", ny)
+    print(case, ": stored h on the other neighbour:", n, "; codes / row scales differing:", nq, ns,
+          "; y off the oracle's rounding:", ny)
