@@ -94,6 +94,18 @@ def test_maximum_sizes(gpu_lib, T, k, E, F, d):
     print(T, k, E, F, d, stats)
 
 
+@pytest.mark.parametrize("T,k,E", [(1, 1, 1), (16, 1, 1), (300, 1, 1), (16, 4, 4), (500, 4, 4)])
+def test_degenerate_expert_counts(gpu_lib, T, k, E):
+    """One expert (every token's only slot, weight 2.826) and k = E (every
+    token takes every expert, in score order), each on the weight-streaming
+    (small T) and the grouped (larger T) GEMMs; every token compared."""
+    c = dict(inputs.CONFIGS[0], T=T, k=k, E=E, seed=170 + T + E)
+    stats, _, idx = _full_compare(_cpu_case(c))
+    idx = idx.cpu().numpy()
+    assert all(sorted(row) == list(range(E)) for row in idx.tolist())
+    print(T, k, E, stats)
+
+
 def test_route_entry_matches_forward_routing(gpu_lib):
     from sparse_moe_layer_wave_amd import hy3moe as hy
     inp = _to("cuda", _cpu_case(0, T=300, seed=7))
