@@ -155,6 +155,15 @@ def test_block_decode_path_shapes(gpu_lib, T):
     print(T, _compare_full(_case(T, 1024, 192, 8, 256, seed=80 + T)))
 
 
+@pytest.mark.parametrize("T,k,E", [(1, 1, 1), (16, 1, 1), (300, 1, 1), (4, 4, 4), (500, 4, 4)])
+def test_block_degenerate_expert_counts(gpu_lib, T, k, E):
+    """One routed expert and k = E beside the shared expert, with route_norm
+    and the score bias, on the weight-streaming (T = 1 and T = 4: the shared
+    expert's rows count twice, so T = 16 already takes the grouped GEMMs) and
+    the grouped GEMMs, every token."""
+    print(T, k, E, _compare_full(_case(T, 512, E, k, 256, seed=210 + T + E)))
+
+
 def test_block_maximum_experts(gpu_lib):
     """E = 1023 routed experts plus the shared one: 1024 experts in the
     dispatch order, the most it takes."""

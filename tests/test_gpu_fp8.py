@@ -84,6 +84,22 @@ def test_fp8_decode_path_full_parity(gpu_lib, T, E, k, F, d):
     print(T, E, k, F, d, stats)
 
 
+@pytest.mark.parametrize("block128", [False, True], ids=["per_channel", "block128"])
+@pytest.mark.parametrize("T,k,E", [(1, 1, 1), (16, 1, 1), (300, 1, 1), (16, 4, 4), (500, 4, 4)])
+def test_fp8_degenerate_expert_counts(gpu_lib, T, k, E, block128):
+    """One expert and k = E with e4m3 experts, on the weight-streaming (T <= 16)
+    and the grouped GEMMs, every token."""
+    from sparse_moe_layer_wave_amd import hy3moe as hy
+    c = dict(inputs.CONFIGS[9 if block128 else 4], T=T, d=512, E=E, k=k, F=256, seed=190 + T + E)
+    inp = inputs.make_inputs(c, device="cpu")
+    dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
+    out, idx, w = hy.forward_fp8(dev["x"], dev["W_gate"], dev["Wq_gu"], dev["s_gu"], dev["Wq_dn"], dev["s_dn"],
+                                 k, inp["scale"], bias=dev["bias"], return_routing=True, block128=block128)
+    torch.cuda.synchronize()
+    assert all(sorted(row) == list(range(E)) for row in idx.cpu().numpy().tolist())
+    print(T, k, E, block128, _compare_cpu_case(inp, out, idx, w))
+
+
 def test_fp8_deterministic(gpu_lib):
     inp = _cpu_fp8_case(500, 32, 8, 128, seed=41)
     a = _run_fp8(inp)
