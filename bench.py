@@ -243,8 +243,8 @@ def cpu_baseline_leg(routings):
     blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
     threads = max([p.get("num_threads", 1) for p in blas] + [1])
     vendor = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in blas) or "unknown"
-    dec, dec_s, dec_e, dec_n = _time_oracle(1, 64, min_seconds=10.0)
-    pre, pre_s, pre_e, _ = _time_oracle(2, 8192)
+    dec, dec_s, dec_e, dec_n = _time_oracle("hy3_decode_T64", 64, min_seconds=10.0)
+    pre, pre_s, pre_e, _ = _time_oracle("hy3_prefill_T8192", 8192)
     base = {"value": round(dec, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole 64-token decode batch (hy3_decode_T64, {dec_e} experts) {dec_n} times, "
                       f"oracle.forward in NumPy float64 on {threads} BLAS threads ({vendor}), {dec_s:.1f} s; "
@@ -264,7 +264,7 @@ def shares(steps, warmup):
     24-expert layer with k = 8 over T/8 tokens has the same expert GEMMs
     (its router and combine are not the sharded ones).  d_ff parallelism gives
     each GPU all experts with d_ff/8 (192) or d_ff/4 (384) columns."""
-    base = dict(inputs.CONFIGS[1])
+    base = dict(inputs.CONFIGS["hy3_decode_T64"])
     cases = [("ep8_prefill_T8192", dict(base, T=1024, E=24, seed=11), "mfma"),
              ("ep8_decode_T64x8", dict(base, T=64, E=24, seed=12), "hbm"),
              ("tp8_decode_T64", dict(base, T=64, F=192, seed=13), "hbm"),
@@ -311,7 +311,7 @@ def vendor_gemm(steps, warmup):
     weights, the same FLOPs with every weight reused by every row; (b) one GEMM
     per expert on that expert's rows of the prefill routing, all launches
     captured in one HIP graph.  bf16 operands, fp32 accumulation, random data."""
-    c = dict(inputs.CONFIGS[2])
+    c = dict(inputs.CONFIGS["hy3_prefill_T8192"])
     res, _ = run_workload(c, steps, warmup)
     T, d, E, k, F = c["T"], c["d"], c["E"], c["k"], c["F"]
     counts = np.bincount(res["routing"]["idx"].reshape(-1), minlength=E)
@@ -391,17 +391,16 @@ def main():
         return
 
     if args.profile_workload:
-        names = {c["name"]: i for i, c in inputs.CONFIGS.items()}
-        if args.profile_workload not in names:
-            print(f"unknown workload {args.profile_workload!r}; one of {sorted(names)}", file=sys.stderr)
+        if args.profile_workload not in inputs.CONFIGS:
+            print(f"unknown workload {args.profile_workload!r}; one of {sorted(inputs.CONFIGS)}", file=sys.stderr)
             sys.exit(2)
-        res, _ = run_workload(names[args.profile_workload], args.steps, args.warmup)
+        res, _ = run_workload(args.profile_workload, args.steps, args.warmup)
         print(json.dumps({"workload": args.profile_workload, "ms_per_step": round(res["ms_per_step"], 4),
                           "kernel_ms": {k: round(v, 5) for k, v in res["stage_ms"].items()},
                           "step_gpu_ms": res["step_gpu_ms"]}), flush=True)
         return
 
-    dec, _ = run_workload(1, args.steps, args.warmup)
+    dec, _ = run_workload("hy3_decode_T64", args.steps, args.warmup)
     routings = [dec.pop("routing")]
     line = {
         "metric": "MoE-layer tokens/s at T=64 & T=8192; % of HBM BW / % of MFMA peak",
@@ -424,7 +423,7 @@ def main():
         "layer_tflops": round(dec["layer_tflops"], 3),
     }
     if not args.no_prefill:
-        pre, _ = run_workload(2, max(5, args.steps // 5), args.warmup)
+        pre, _ = run_workload("hy3_prefill_T8192", max(5, args.steps // 5), args.warmup)
         routings.append(pre.pop("routing"))
         line["prefill"] = {
             "workload": pre["cfg"]["name"], "tokens_per_s": round(pre["tokens_per_s"], 1),
@@ -437,10 +436,14 @@ def main():
             "step_gpu_ms": pre["step_gpu_ms"],
         }
     if not args.no_extra:
-        for key, cfg, bound in (("skewed", 3, "mfma"), ("fp8", 4, "mfma"), ("fp8_decode", 7, "hbm"),
-                                ("block_decode", 5, "hbm"), ("block_prefill", 6, "mfma"),
-                                ("skewed_decode", 8, "hbm"), ("fp8_block128_decode", 9, "hbm"),
-                                ("fp8_block128", 10, "mfma"), ("block_residual_prefill", 11, "mfma")):
+        for key, cfg, bound in (("skewed", "hy3_long_skewed_T65536", "mfma"), ("fp8", "hy3_fp8_T8192", "mfma"),
+                                ("fp8_decode", "hy3_fp8_decode_T64", "hbm"),
+                                ("block_decode", "hy3_block_decode_T64", "hbm"),
+                                ("block_prefill", "hy3_block_prefill_T8192", "mfma"),
+                                ("skewed_decode", "hy3_skewed_decode_T64", "hbm"),
+                                ("fp8_block128_decode", "hy3_fp8_block128_decode_T64", "hbm"),
+                                ("fp8_block128", "hy3_fp8_block128_T8192", "mfma"),
+                                ("block_residual_prefill", "hy3_block_residual_T8192", "mfma")):
             n = args.steps if bound == "hbm" else max(3, args.steps // 10)
             res, _ = run_workload(cfg, n, min(args.warmup, 2))
             routings.append(res.pop("routing"))

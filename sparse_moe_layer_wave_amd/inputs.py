@@ -42,39 +42,42 @@ ROUTER_SCALE = float(np.float32(2.826))   # router_scaling_factor, as a float32 
 # 15x the mean load; the fit is tests/golden/fit_skew_tau.py.
 SKEW_TAU = 0.5467
 
-# name, T, d, E, k, d_ff, seed, expert weight format, skewed routing
-CONFIGS = {
-    0: dict(name="tiny_T128_d512_E32_F128", T=128, d=512, E=32, k=8, F=128, seed=0,
-            weights="bf16", skew=False),
-    1: dict(name="hy3_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=1,
-            weights="bf16", skew=False),
-    2: dict(name="hy3_prefill_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=2,
-            weights="bf16", skew=False),
-    3: dict(name="hy3_long_skewed_T65536", T=65536, d=4096, E=192, k=8, F=1536, seed=3,
-            weights="bf16", skew=True),
-    4: dict(name="hy3_fp8_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=4,
-            weights="fp8", skew=False),
+# Seeded workloads by name: T, d, E, k, d_ff, seed, expert weight format,
+# skewed routing.  The seed is a field of its own, so a workload's inputs do
+# not depend on where it stands in this table.
+_WORKLOADS = (
+    dict(name="tiny_T128_d512_E32_F128", T=128, d=512, E=32, k=8, F=128, seed=0,
+         weights="bf16", skew=False),
+    dict(name="hy3_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=1,
+         weights="bf16", skew=False),
+    dict(name="hy3_prefill_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=2,
+         weights="bf16", skew=False),
+    dict(name="hy3_long_skewed_T65536", T=65536, d=4096, E=192, k=8, F=1536, seed=3,
+         weights="bf16", skew=True),
+    dict(name="hy3_fp8_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=4,
+         weights="fp8", skew=False),
     # the full block (shared expert, route_norm, selection-only score bias)
-    5: dict(name="hy3_block_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=5,
-            weights="bf16", skew=False, block=True),
-    6: dict(name="hy3_block_prefill_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=6,
-            weights="bf16", skew=False, block=True),
+    dict(name="hy3_block_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=5,
+         weights="bf16", skew=False, block=True),
+    dict(name="hy3_block_prefill_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=6,
+         weights="bf16", skew=False, block=True),
     # e4m3 experts at the decode batch
-    7: dict(name="hy3_fp8_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=7,
-            weights="fp8", skew=False),
-    # the skewed routing of workload 3 at the decode batch (hot experts get
+    dict(name="hy3_fp8_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=7,
+         weights="fp8", skew=False),
+    # the skewed routing of hy3_long_skewed_T65536 at the decode batch (hot experts get
     # tens of rows)
-    8: dict(name="hy3_skewed_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=8,
-            weights="bf16", skew=True),
+    dict(name="hy3_skewed_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=8,
+         weights="bf16", skew=True),
     # e4m3 experts with one scale per 128 x 128 weight block
-    9: dict(name="hy3_fp8_block128_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=9,
-            weights="fp8_block128", skew=False),
-    10: dict(name="hy3_fp8_block128_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=10,
-             weights="fp8_block128", skew=False),
+    dict(name="hy3_fp8_block128_decode_T64", T=64, d=4096, E=192, k=8, F=1536, seed=9,
+         weights="fp8_block128", skew=False),
+    dict(name="hy3_fp8_block128_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=10,
+         weights="fp8_block128", skew=False),
     # the full block ending the residual branch: bf16 output, residual added
-    11: dict(name="hy3_block_residual_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=11,
-             weights="bf16", skew=False, block=True, residual=True),
-}
+    dict(name="hy3_block_residual_T8192", T=8192, d=4096, E=192, k=8, F=1536, seed=11,
+         weights="bf16", skew=False, block=True, residual=True),
+)
+CONFIGS = {c["name"]: c for c in _WORKLOADS}
 
 (_STREAM_X, _STREAM_WG, _STREAM_BIAS, _STREAM_WGU, _STREAM_WDN, _STREAM_NORM, _STREAM_SBIAS,
  _STREAM_SGU, _STREAM_SDN, _STREAM_RESID) = range(10)
@@ -187,10 +190,13 @@ def make_block_extras(d, E, F, seed, device="cpu"):
 def make_inputs(cfg, device="cpu", T=None, with_experts=True):
     """All inputs of one workload as torch tensors on ``device``.
 
-    ``cfg`` is a CONFIGS key or a dict with the same fields; ``T`` overrides
+    ``cfg`` is a workload name (a CONFIGS key) or a dict with the same
+    fields; ``T`` overrides
     the token count (the rows are the first T rows the seed would give only if
     the generator's draw order allows it -- treat each T as its own input)."""
-    c = dict(CONFIGS[cfg]) if not isinstance(cfg, dict) else dict(cfg)
+    if not isinstance(cfg, (str, dict)):
+        raise TypeError(f"workload must be a name or a dict, not {cfg!r}")
+    c = dict(CONFIGS[cfg]) if isinstance(cfg, str) else dict(cfg)
     if T is not None:
         c["T"] = T
     out = dict(cfg=c, scale=ROUTER_SCALE)

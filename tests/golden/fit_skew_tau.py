@@ -31,7 +31,7 @@ def hot_ratio(x_bits, W, rank, tau, k, scale):
 
 
 def main():
-    c = inputs.CONFIGS[3]
+    c = inputs.CONFIGS["hy3_long_skewed_T65536"]
     T = 8192
     x = inputs.bits(inputs.make_x(T, c["d"], c["seed"], "cpu"))
     W, _ = inputs.make_router(c["E"], c["d"], c["seed"], "cpu", skew=False)

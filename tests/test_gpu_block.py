@@ -22,7 +22,7 @@ EPS = float(np.float32(1e-6))     # the library takes eps as a float32
 
 
 def _case(T, d, E, k, F, seed, **over):
-    c = dict(inputs.CONFIGS[5], T=T, d=d, E=E, k=k, F=F, seed=seed)
+    c = dict(inputs.CONFIGS["hy3_block_decode_T64"], T=T, d=d, E=E, k=k, F=F, seed=seed)
     c.update(over)
     return inputs.make_inputs(c, device="cpu")
 
@@ -203,11 +203,11 @@ def _hy3_block_case(cfg):
 
 
 def test_hy3_block_decode_T64(gpu_lib):
-    print("block decode", _hy3_block_case(5))
+    print("block decode", _hy3_block_case("hy3_block_decode_T64"))
 
 
 def test_hy3_block_prefill_T8192(gpu_lib):
-    print("block prefill", _hy3_block_case(6))
+    print("block prefill", _hy3_block_case("hy3_block_prefill_T8192"))
 
 
 # ----------------------------------------------------------------------------- bf16 output + residual
@@ -258,7 +258,7 @@ def test_hy3_block_residual_T8192(gpu_lib):
     bit for bit against the fp32 block output plus the residual rounded once
     to bf16."""
     from sparse_moe_layer_wave_amd import hy3moe as hy
-    inp = inputs.make_inputs(11, device="cuda")
+    inp = inputs.make_inputs("hy3_block_residual_T8192", device="cuda")
     c = inp["cfg"]
     k = c["k"]
     kw = dict(norm_weight=inp["norm_w"], norm_eps=EPS, score_bias=inp["score_bias"])

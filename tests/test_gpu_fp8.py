@@ -32,7 +32,7 @@ def test_quantize_rows_bit_exact(gpu_lib):
 
 
 def _cpu_fp8_case(T, E, k, F, d=512, seed=40):
-    c = dict(inputs.CONFIGS[4], T=T, d=d, E=E, k=k, F=F, seed=seed)
+    c = dict(inputs.CONFIGS["hy3_fp8_T8192"], T=T, d=d, E=E, k=k, F=F, seed=seed)
     return inputs.make_inputs(c, device="cpu")
 
 
@@ -90,7 +90,7 @@ def test_fp8_degenerate_expert_counts(gpu_lib, T, k, E, block128):
     """One expert and k = E with e4m3 experts, on the weight-streaming (T <= 16)
     and the grouped GEMMs, every token."""
     from sparse_moe_layer_wave_amd import hy3moe as hy
-    c = dict(inputs.CONFIGS[9 if block128 else 4], T=T, d=512, E=E, k=k, F=256, seed=190 + T + E)
+    c = dict(inputs.CONFIGS["hy3_fp8_block128_decode_T64" if block128 else "hy3_fp8_T8192"], T=T, d=512, E=E, k=k, F=256, seed=190 + T + E)
     inp = inputs.make_inputs(c, device="cpu")
     dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
     out, idx, w = hy.forward_fp8(dev["x"], dev["W_gate"], dev["Wq_gu"], dev["s_gu"], dev["Wq_dn"], dev["s_dn"],
@@ -108,9 +108,10 @@ def test_fp8_deterministic(gpu_lib):
         assert torch.equal(u, v)
 
 
-@pytest.mark.parametrize("cfg", [4, 7, 9, 10])
+@pytest.mark.parametrize("cfg", ["hy3_fp8_T8192", "hy3_fp8_decode_T64", "hy3_fp8_block128_decode_T64",
+                                 "hy3_fp8_block128_T8192"])
 def test_hy3_fp8(gpu_lib, cfg):
-    """Per-channel scales (workloads 4, 7) and 128 x 128 block scales (9, 10),
+    """Per-channel and 128 x 128 block scales, at T=8192 and T=64,
     every token."""
     from sparse_moe_layer_wave_amd import hy3moe as hy
     inp = inputs.make_inputs(cfg, device="cuda")
@@ -133,7 +134,7 @@ def test_hy3_fp8(gpu_lib, cfg):
 # ----------------------------------------------------------------------------- 128 x 128 block scales
 
 def _cpu_fp8_block_case(T, E, k, F, d, seed):
-    c = dict(inputs.CONFIGS[9], T=T, d=d, E=E, k=k, F=F, seed=seed)
+    c = dict(inputs.CONFIGS["hy3_fp8_block128_decode_T64"], T=T, d=d, E=E, k=k, F=F, seed=seed)
     return inputs.make_inputs(c, device="cpu")
 
 

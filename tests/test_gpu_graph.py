@@ -37,7 +37,7 @@ def _replays_match(run, n=3):
 
 @pytest.mark.parametrize("T,E,k,F", [(64, 32, 8, 128), (1000, 32, 8, 128)])
 def test_forward_bf16_graph(gpu_lib, T, E, k, F):
-    c = dict(inputs.CONFIGS[0], T=T, E=E, k=k, F=F, seed=400 + T)
+    c = dict(inputs.CONFIGS["tiny_T128_d512_E32_F128"], T=T, E=E, k=k, F=F, seed=400 + T)
     inp = inputs.make_inputs(c, device="cuda")
     ws = hy.alloc_workspace(T, c["d"], E, k, F, hy.WEIGHTS_BF16)
     out = torch.empty((T, c["d"]), dtype=torch.float32, device="cuda")
@@ -46,7 +46,7 @@ def test_forward_bf16_graph(gpu_lib, T, E, k, F):
 
 
 def test_forward_fp8_graph(gpu_lib):
-    c = dict(inputs.CONFIGS[4], T=300, d=512, E=32, F=256, seed=410)
+    c = dict(inputs.CONFIGS["hy3_fp8_T8192"], T=300, d=512, E=32, F=256, seed=410)
     inp = inputs.make_inputs(c, device="cuda")
     ws = hy.alloc_workspace(300, 512, 32, 8, 256, hy.WEIGHTS_FP8_E4M3)
     out = torch.empty((300, 512), dtype=torch.float32, device="cuda")
@@ -55,7 +55,7 @@ def test_forward_fp8_graph(gpu_lib):
 
 
 def test_block_forward_graph(gpu_lib):
-    c = dict(inputs.CONFIGS[5], T=64, d=512, E=32, F=128, seed=420)
+    c = dict(inputs.CONFIGS["hy3_block_decode_T64"], T=64, d=512, E=32, F=128, seed=420)
     inp = inputs.make_inputs(c, device="cuda")
     ws = torch.empty(hy.block_workspace_size(64, 512, 32, 8, 128), dtype=torch.uint8, device="cuda")
     out = torch.empty((64, 512), dtype=torch.float32, device="cuda")
@@ -67,7 +67,7 @@ def test_block_forward_graph(gpu_lib):
 
 @pytest.mark.parametrize("T", [40, 600], ids=["decode-kernels", "grouped-kernels"])
 def test_forward_fp8_block128_graph(gpu_lib, T):
-    c = dict(inputs.CONFIGS[9], T=T, d=512, E=32, F=256, seed=430 + T)
+    c = dict(inputs.CONFIGS["hy3_fp8_block128_decode_T64"], T=T, d=512, E=32, F=256, seed=430 + T)
     inp = inputs.make_inputs(c, device="cuda")
     ws = hy.alloc_workspace(T, 512, 32, 8, 256, hy.WEIGHTS_FP8_E4M3)
     out = torch.empty((T, 512), dtype=torch.float32, device="cuda")
@@ -77,7 +77,7 @@ def test_forward_fp8_block128_graph(gpu_lib, T):
 
 
 def test_block_forward_bf16_graph(gpu_lib):
-    c = dict(inputs.CONFIGS[5], T=64, d=512, E=32, F=128, seed=440)
+    c = dict(inputs.CONFIGS["hy3_block_decode_T64"], T=64, d=512, E=32, F=128, seed=440)
     inp = inputs.make_inputs(c, device="cuda")
     res = inputs.make_residual(64, 512, 440, device="cuda")
     ws = torch.empty(hy.block_workspace_size(64, 512, 32, 8, 128), dtype=torch.uint8, device="cuda")

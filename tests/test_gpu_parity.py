@@ -64,7 +64,7 @@ def _full_compare(inp_cpu, tol=TOL_BF16):
 
 
 def test_tiny_workload_full_parity(gpu_lib):
-    stats, inp, idx = _full_compare(_cpu_case(0))
+    stats, inp, idx = _full_compare(_cpu_case("tiny_T128_d512_E32_F128"))
     print("tiny", stats)
     from sparse_moe_layer_wave_amd import hy3moe as hy
     counts, offsets, row_of, token_of = hy.permute(idx, inp["cfg"]["E"])
@@ -75,7 +75,7 @@ def test_tiny_workload_full_parity(gpu_lib):
 @pytest.mark.parametrize("T,k,E,F", [(1, 8, 32, 128), (37, 8, 32, 128), (200, 1, 32, 128),
                                      (333, 4, 48, 192), (1000, 8, 32, 64), (130, 16, 64, 128)])
 def test_ragged_and_small_shapes(gpu_lib, T, k, E, F):
-    c = dict(inputs.CONFIGS[0], T=T, k=k, E=E, F=F, seed=100 + T)
+    c = dict(inputs.CONFIGS["tiny_T128_d512_E32_F128"], T=T, k=k, E=E, F=F, seed=100 + T)
     stats, _, _ = _full_compare(_cpu_case(c))
     print(T, k, E, F, stats)
 
@@ -89,7 +89,7 @@ def test_maximum_sizes(gpu_lib, T, k, E, F, d):
     GEMMs' work order).  Every token is compared; with k = 2 the weights are
     near 1.4, so a rounding-boundary flip of a large |y| is above 1e-2 * rms
     and the flip check has work to do there."""
-    c = dict(inputs.CONFIGS[0], T=T, k=k, E=E, F=F, d=d, seed=150 + k)
+    c = dict(inputs.CONFIGS["tiny_T128_d512_E32_F128"], T=T, k=k, E=E, F=F, d=d, seed=150 + k)
     stats, _, _ = _full_compare(_cpu_case(c))
     print(T, k, E, F, d, stats)
 
@@ -99,7 +99,7 @@ def test_degenerate_expert_counts(gpu_lib, T, k, E):
     """One expert (every token's only slot, weight 2.826) and k = E (every
     token takes every expert, in score order), each on the weight-streaming
     (small T) and the grouped (larger T) GEMMs; every token compared."""
-    c = dict(inputs.CONFIGS[0], T=T, k=k, E=E, seed=170 + T + E)
+    c = dict(inputs.CONFIGS["tiny_T128_d512_E32_F128"], T=T, k=k, E=E, seed=170 + T + E)
     stats, _, idx = _full_compare(_cpu_case(c))
     idx = idx.cpu().numpy()
     assert all(sorted(row) == list(range(E)) for row in idx.tolist())
@@ -108,7 +108,7 @@ def test_degenerate_expert_counts(gpu_lib, T, k, E):
 
 def test_route_entry_matches_forward_routing(gpu_lib):
     from sparse_moe_layer_wave_amd import hy3moe as hy
-    inp = _to("cuda", _cpu_case(0, T=300, seed=7))
+    inp = _to("cuda", _cpu_case("tiny_T128_d512_E32_F128", T=300, seed=7))
     c = inp["cfg"]
     idx_r, w_r = hy.route(inp["x"], inp["W_gate"], c["k"], inp["scale"])
     _, idx_f, w_f = _run_bf16(hy, inp)
@@ -121,7 +121,7 @@ def test_router_large_batch_shapes(gpu_lib, T, E, k, d):
     token tiles of 256 with a ragged last one, expert groups of 192 with a
     partial last one (E = 200, 1024) or a single short one (E = 7)."""
     from sparse_moe_layer_wave_amd import hy3moe as hy
-    c = dict(inputs.CONFIGS[0], T=T, E=E, k=k, d=d, F=64, seed=300 + E)
+    c = dict(inputs.CONFIGS["tiny_T128_d512_E32_F128"], T=T, E=E, k=k, d=d, F=64, seed=300 + E)
     inp_cpu = _cpu_case(c)
     inp = _to("cuda", inp_cpu)
     idx, w = hy.route(inp["x"], inp["W_gate"], k, inp["scale"])
@@ -131,7 +131,7 @@ def test_router_large_batch_shapes(gpu_lib, T, E, k, d):
 
 
 def test_zero_tokens_tie_to_lowest_experts(gpu_lib):
-    inp = _cpu_case(0, T=64, seed=8)
+    inp = _cpu_case("tiny_T128_d512_E32_F128", T=64, seed=8)
     inp["x"][5] = 0
     inp["x"][40] = 0
     stats, _, idx = _full_compare(inp)
@@ -140,7 +140,7 @@ def test_zero_tokens_tie_to_lowest_experts(gpu_lib):
 
 
 def test_duplicated_gate_rows_lower_index_wins(gpu_lib):
-    inp = _cpu_case(0, T=256, seed=9)
+    inp = _cpu_case("tiny_T128_d512_E32_F128", T=256, seed=9)
     inp["W_gate"][17] = inp["W_gate"][4]
     stats, _, idx = _full_compare(inp)
     for row in idx.cpu().numpy().tolist():
@@ -150,7 +150,7 @@ def test_duplicated_gate_rows_lower_index_wins(gpu_lib):
 
 def test_all_tokens_one_expert(gpu_lib):
     """Maximum skew: a large logit bias sends every token to expert 5 first."""
-    inp = _cpu_case(0, T=500, seed=10)
+    inp = _cpu_case("tiny_T128_d512_E32_F128", T=500, seed=10)
     b = torch.zeros(inp["cfg"]["E"], dtype=torch.float32)
     b[5] = 30.0
     inp["bias"] = b
@@ -168,7 +168,7 @@ def test_decode_path_shapes(gpu_lib, T, E, k, hot):
     the last four cases, the second with a 56-row hot expert cut into two
     slices, the last at 6 rows per expert).  A hot expert with more rows than
     a slice is cut into several slices."""
-    c = dict(inputs.CONFIGS[0], T=T, E=E, k=k, F=128, seed=200 + T)
+    c = dict(inputs.CONFIGS["tiny_T128_d512_E32_F128"], T=T, E=E, k=k, F=128, seed=200 + T)
     inp = _cpu_case(c)
     if hot:
         b = torch.zeros(E, dtype=torch.float32)
@@ -180,7 +180,7 @@ def test_decode_path_shapes(gpu_lib, T, E, k, hot):
 
 def test_empty_batch(gpu_lib):
     from sparse_moe_layer_wave_amd import hy3moe as hy
-    inp = _to("cuda", _cpu_case(0, T=0))
+    inp = _to("cuda", _cpu_case("tiny_T128_d512_E32_F128", T=0))
     out = hy.forward(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], 8, inp["scale"])
     assert out.shape == (0, 512)
 
@@ -190,21 +190,21 @@ def test_empty_batch_every_entry(gpu_lib):
     no output is written (outputs of fixed size, such as permute's counts, keep
     whatever they held), so only the shapes are checked."""
     from sparse_moe_layer_wave_amd import hy3moe as hy
-    c = dict(inputs.CONFIGS[0], T=0)
+    c = dict(inputs.CONFIGS["tiny_T128_d512_E32_F128"], T=0)
     inp = _to("cuda", _cpu_case(c))
     idx, w = hy.route(inp["x"], inp["W_gate"], 8, inp["scale"])
     assert idx.shape == (0, 8) and w.shape == (0, 8)
     counts, offsets, row_of, token_of = hy.permute(idx, c["E"])
     assert counts.shape == (c["E"],) and offsets.shape == (c["E"] + 1,)
     assert row_of.numel() == 0 and token_of.numel() == 0
-    blk = inputs.make_inputs(dict(inputs.CONFIGS[5], T=0, d=512, E=32, F=128), device="cuda")
+    blk = inputs.make_inputs(dict(inputs.CONFIGS["hy3_block_decode_T64"], T=0, d=512, E=32, F=128), device="cuda")
     idx, w = hy.route_ex(blk["x"], blk["W_gate"], 8, blk["scale"], norm_weight=blk["norm_w"],
                          score_bias=blk["score_bias"])
     assert idx.shape == (0, 8)
     out = hy.block_forward(blk["x"], blk["W_gate"], blk["W_gu"], blk["W_dn"], blk["Ws_gu"], blk["Ws_dn"], 8,
                            blk["scale"], norm_weight=blk["norm_w"], score_bias=blk["score_bias"])
     assert out.shape == (0, 512)
-    f8 = inputs.make_inputs(dict(inputs.CONFIGS[4], T=0, d=512, E=32, F=256), device="cuda")
+    f8 = inputs.make_inputs(dict(inputs.CONFIGS["hy3_fp8_T8192"], T=0, d=512, E=32, F=256), device="cuda")
     out = hy.forward_fp8(f8["x"], f8["W_gate"], f8["Wq_gu"], f8["s_gu"], f8["Wq_dn"], f8["s_dn"], 8, f8["scale"])
     assert out.shape == (0, 512)
     torch.cuda.synchronize()
@@ -212,7 +212,7 @@ def test_empty_batch_every_entry(gpu_lib):
 
 def test_deterministic(gpu_lib):
     from sparse_moe_layer_wave_amd import hy3moe as hy
-    inp = _to("cuda", _cpu_case(0, T=777, seed=11))
+    inp = _to("cuda", _cpu_case("tiny_T128_d512_E32_F128", T=777, seed=11))
     a = _run_bf16(hy, inp)
     b = _run_bf16(hy, inp)
     for u, v in zip(a, b):
@@ -280,22 +280,22 @@ def _hy3_case(cfg):
 
 
 def test_hy3_decode_T64(gpu_lib):
-    print("decode", _hy3_case(1))
+    print("decode", _hy3_case("hy3_decode_T64"))
 
 
 def test_hy3_skewed_decode_T64(gpu_lib):
     """Decode batch with the skewed routing: hot experts get tens of rows,
     each cut into several 16-row slices of the weight-streaming kernels."""
-    stats = _hy3_case(8)
+    stats = _hy3_case("hy3_skewed_decode_T64")
     print("skewed decode", stats)
     assert stats["hottest_over_mean"] > 8
 
 
 def test_hy3_prefill_T8192(gpu_lib):
-    print("prefill", _hy3_case(2))
+    print("prefill", _hy3_case("hy3_prefill_T8192"))
 
 
 def test_hy3_long_skewed_T65536(gpu_lib):
-    stats = _hy3_case(3)
+    stats = _hy3_case("hy3_long_skewed_T65536")
     print("skewed", stats)
     assert stats["hottest_over_mean"] > 10 and stats["compared"] > 4000

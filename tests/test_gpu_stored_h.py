@@ -125,7 +125,7 @@ def test_stored_h_bf16_grouped(gpu_lib):
     """bf16 experts at Hy3 dims, T=512 (the grouped GEMMs)."""
     from sparse_moe_layer_wave_amd import hy3moe as hy
     T, d, E, k, F = 512, 4096, 192, 8, 1536
-    c = dict(inputs.CONFIGS[2], T=T, seed=4242)
+    c = dict(inputs.CONFIGS["hy3_prefill_T8192"], T=T, seed=4242)
     inp = inputs.make_inputs(c, device="cpu")
     dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
     L = _layout(T, d, E, k, F, fp8=False)
@@ -152,10 +152,10 @@ def test_stored_h_e4m3(gpu_lib, case):
     from sparse_moe_layer_wave_amd import hy3moe as hy
     if case == "per_channel_decode":
         T, d, E, k, F = 128, 4096, 192, 8, 1536
-        c = dict(inputs.CONFIGS[4], T=T, seed=4243)
+        c = dict(inputs.CONFIGS["hy3_fp8_T8192"], T=T, seed=4243)
     else:
         T, d, E, k, F = 393, 512, 31, 2, 256
-        c = dict(inputs.CONFIGS[9], T=T, d=d, E=E, k=k, F=F, seed=800 + T)
+        c = dict(inputs.CONFIGS["hy3_fp8_block128_decode_T64"], T=T, d=d, E=E, k=k, F=F, seed=800 + T)
     inp = inputs.make_inputs(c, device="cpu")
     dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
     L = _layout(T, d, E, k, F, fp8=True)

@@ -68,7 +68,7 @@ def _set_eq(idx, r):
 def test_sweep_bf16(gpu_lib, T, d, E, k, F):
     from sparse_moe_layer_wave_amd import hy3moe as hy
     skew = (T + E) % 3 == 0                           # a third of the cases with the skewed logit bias
-    c = dict(inputs.CONFIGS[0], T=T, d=d, E=E, k=k, F=F, seed=500 + T, skew=skew)
+    c = dict(inputs.CONFIGS["tiny_T128_d512_E32_F128"], T=T, d=d, E=E, k=k, F=F, seed=500 + T, skew=skew)
     inp = inputs.make_inputs(c, device="cpu")
     dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
     out, idx, w = hy.forward(dev["x"], dev["W_gate"], dev["W_gu"], dev["W_dn"], k, inp["scale"],
@@ -88,7 +88,7 @@ def test_sweep_bf16(gpu_lib, T, d, E, k, F):
 @pytest.mark.parametrize("T,d,E,k,F", FP8_CASES, ids=_ids(FP8_CASES))
 def test_sweep_fp8(gpu_lib, T, d, E, k, F):
     from sparse_moe_layer_wave_amd import hy3moe as hy
-    c = dict(inputs.CONFIGS[4], T=T, d=d, E=E, k=k, F=F, seed=600 + T)
+    c = dict(inputs.CONFIGS["hy3_fp8_T8192"], T=T, d=d, E=E, k=k, F=F, seed=600 + T)
     inp = inputs.make_inputs(c, device="cpu")
     dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
     out, idx, w = hy.forward_fp8(dev["x"], dev["W_gate"], dev["Wq_gu"], dev["s_gu"], dev["Wq_dn"],
@@ -109,7 +109,7 @@ def test_sweep_fp8(gpu_lib, T, d, E, k, F):
 @pytest.mark.parametrize("T,d,E,k,F", BLOCK_CASES, ids=_ids(BLOCK_CASES))
 def test_sweep_block(gpu_lib, T, d, E, k, F):
     from sparse_moe_layer_wave_amd import hy3moe as hy
-    c = dict(inputs.CONFIGS[5], T=T, d=d, E=E, k=k, F=F, seed=700 + T)
+    c = dict(inputs.CONFIGS["hy3_block_decode_T64"], T=T, d=d, E=E, k=k, F=F, seed=700 + T)
     inp = inputs.make_inputs(c, device="cpu")
     dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
     out, idx, w = hy.block_forward(dev["x"], dev["W_gate"], dev["W_gu"], dev["W_dn"], dev["Ws_gu"],
@@ -132,7 +132,7 @@ def test_sweep_block(gpu_lib, T, d, E, k, F):
 @pytest.mark.parametrize("T,d,E,k,F", BLK128_CASES, ids=_ids(BLK128_CASES))
 def test_sweep_fp8_block128(gpu_lib, T, d, E, k, F):
     from sparse_moe_layer_wave_amd import hy3moe as hy
-    c = dict(inputs.CONFIGS[9], T=T, d=d, E=E, k=k, F=F, seed=800 + T)
+    c = dict(inputs.CONFIGS["hy3_fp8_block128_decode_T64"], T=T, d=d, E=E, k=k, F=F, seed=800 + T)
     inp = inputs.make_inputs(c, device="cpu")
     dev = {kk: (v.cuda() if torch.is_tensor(v) else v) for kk, v in inp.items()}
     out, idx, w = hy.forward_fp8_block128(dev["x"], dev["W_gate"], dev["Wq_gu"], dev["s_gu"], dev["Wq_dn"],

@@ -10,8 +10,8 @@ from sparse_moe_layer_wave_amd import inputs
 
 
 def test_tiny_config_shapes_and_determinism():
-    a = inputs.make_inputs(0)
-    b = inputs.make_inputs(0)
+    a = inputs.make_inputs("tiny_T128_d512_E32_F128")
+    b = inputs.make_inputs("tiny_T128_d512_E32_F128")
     c = a["cfg"]
     assert a["x"].shape == (c["T"], c["d"]) and a["x"].dtype == torch.bfloat16
     assert a["W_gate"].shape == (c["E"], c["d"]) and a["W_gate"].dtype == torch.float32
@@ -23,7 +23,7 @@ def test_tiny_config_shapes_and_determinism():
 
 
 def test_distributions():
-    a = inputs.make_inputs(0)
+    a = inputs.make_inputs("tiny_T128_d512_E32_F128")
     c = a["cfg"]
     assert abs(a["x"].float().std().item() - 1.0) < 0.02
     assert abs(a["W_gate"].std().item() * np.sqrt(c["d"]) - 1.0) < 0.03
@@ -32,7 +32,7 @@ def test_distributions():
 
 
 def test_fp8_weights_have_per_row_scales():
-    c = dict(inputs.CONFIGS[4], T=8, d=128, E=4, F=64)
+    c = dict(inputs.CONFIGS["hy3_fp8_T8192"], T=8, d=128, E=4, F=64)
     a = inputs.make_inputs(c)
     q = a["Wq_gu"].view(torch.float8_e4m3fn).float()
     assert a["Wq_gu"].dtype == torch.uint8 and a["s_gu"].shape == (4, 128)
@@ -41,7 +41,7 @@ def test_fp8_weights_have_per_row_scales():
 
 
 def test_skew_bias_gives_about_15x_hottest_load():
-    c = inputs.CONFIGS[3]
+    c = inputs.CONFIGS["hy3_long_skewed_T65536"]
     T = 2048
     x = inputs.bits(inputs.make_x(T, c["d"], c["seed"] + 100, "cpu"))
     W, b = inputs.make_router(c["E"], c["d"], c["seed"], "cpu", skew=True)

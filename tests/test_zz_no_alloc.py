@@ -25,8 +25,9 @@ def _same(inp, T):
     return got[0]
 
 
-@pytest.mark.parametrize("cfg,T1,T2", [(1, 64, 16), (dict(inputs.CONFIGS[0], T=1000, seed=31), 1000, 300),
-                                       (8, 64, 40)],
+@pytest.mark.parametrize("cfg,T1,T2", [("hy3_decode_T64", 64, 16),
+                                       (dict(inputs.CONFIGS["tiny_T128_d512_E32_F128"], T=1000, seed=31), 1000, 300),
+                                       ("hy3_skewed_decode_T64", 64, 40)],
                          ids=["hy3-decode", "grouped", "hy3-skewed-decode"])
 def test_noalloc_matches_forward(gpu_lib, cfg, T1, T2):
     inp = inputs.make_inputs(cfg, device="cuda")
@@ -38,7 +39,7 @@ def test_noalloc_matches_forward(gpu_lib, cfg, T1, T2):
 
 def test_noalloc_rejects_sizes_beyond_its_scratch(gpu_lib):
     from sparse_moe_layer_wave_amd import hy3moe as hy
-    inp = inputs.make_inputs(dict(inputs.CONFIGS[1], T=700), device="cuda")
+    inp = inputs.make_inputs(dict(inputs.CONFIGS["hy3_decode_T64"], T=700), device="cuda")
     c = inp["cfg"]
     with pytest.raises(hy.Hy3MoeError, match="static scratch"):
         hy.forward_noalloc(inp["x"], inp["W_gate"], inp["W_gu"], inp["W_dn"], c["k"], inp["scale"])
