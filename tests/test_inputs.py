@@ -3,6 +3,7 @@ distributions the workloads specify; the skewed workload's load ratio under
 the oracle's router."""
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -20,6 +21,16 @@ def test_tiny_config_shapes_and_determinism():
     for key in ("x", "W_gate", "W_gu", "W_dn"):
         assert torch.equal(a[key], b[key])
     assert a["bias"] is None
+
+
+def test_workloads_are_looked_up_by_name():
+    """Each workload's key is its name; seeds are distinct, so no two
+    workloads draw the same inputs; a bare number is refused."""
+    assert all(k == c["name"] for k, c in inputs.CONFIGS.items())
+    seeds = [c["seed"] for c in inputs.CONFIGS.values()]
+    assert len(set(seeds)) == len(seeds)
+    with pytest.raises(TypeError):
+        inputs.make_inputs(0)
 
 
 def test_distributions():
